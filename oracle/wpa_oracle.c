@@ -1,0 +1,272 @@
+/*
+ * wpa_oracle.c -- plain, slow, fp64 CPU oracle for per-RoPE-wavelength windowed
+ * causal attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or call
+ * this file; only the tests, the package smoke check and the bench's CPU-baseline
+ * leg do.  It shares no code, header, table or helper with the HIP library.
+ *
+ * What it computes (ATFlash abstract, "Per-RoPE-Wavelength Attention Windows",
+ * and WavePrune, "One period is often enough for RoPE", original abstract):
+ *   - the RoPE attention score is an exact sum over 2-D rotation frequency
+ *     pairs (ATFlash abstract, first sentence);
+ *   - pair i has wavelength lambda_i = 2*pi*base^(2i/d), one full rotation
+ *     period (WavePrune abstract: "restricts each channel to its first rotation
+ *     period"); its query-key term is kept only while the query-key distance
+ *     is at most alpha*lambda_i (ATFlash abstract: "prunes the query--key
+ *     inner-product terms beyond a wavelength-proportional distance");
+ *   - a pruned term contributes zero but the key stays in the softmax
+ *     (ATFlash abstract: "every key remains reachable");
+ *   - the softmax over the windowed logits is ordinary (ATFlash abstract:
+ *     "leaving the online-softmax recurrences untouched").
+ *
+ * Readings taken where the pages are silent (each is listed in the design notes):
+ *   - pair i is made of head dims i and i + d/2 ("half-split" layout);
+ *   - the window edge is inclusive: |dt| <= alpha*lambda_i keeps the term;
+ *   - alpha*lambda_i is evaluated in IEEE double as
+ *       alpha * ((2.0*M_PI) * pow(base, (2.0*i)/d));
+ *   - logits are scaled by `scale` (1/sqrt(d) by default) after the windowed sum;
+ *   - causality is by token index: key c is visible to query r iff c <= r;
+ *   - q head h reads kv head h / (Hq/Hkv);
+ *   - rotation: x'_i = x_i cos(t th_i) - x_{i+P} sin(t th_i),
+ *               x'_{i+P} = x_{i+P} cos(t th_i) + x_i sin(t th_i),
+ *     th_i = base^(-2i/d), angle formed in double, libm cos/sin;
+ *   - decode: the one query sits at token index kv_len-1 (its own key included).
+ *
+ * Inputs are the exact values the GPU consumes (bf16 bit patterns as uint16, or
+ * fp32); step 1 upcasts them to double.  All arithmetic is double.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_BF16 0
+#define ORC_FP32 1
+
+/* Step 1: exact upcast of one input element. */
+static double orc_load(const void* base_ptr, int dtype, int64_t idx) {
+    if (dtype == ORC_FP32) return (double)((const float*)base_ptr)[idx];
+    uint32_t bits = ((uint32_t)((const uint16_t*)base_ptr)[idx]) << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* Step 2: per-pair window thresholds alpha*lambda_i (may be +inf). */
+void orc_thresholds(int d, double base, double alpha, double* thr) {
+    for (int i = 0; i < d / 2; ++i) {
+        double lam = (2.0 * M_PI) * pow(base, (2.0 * i) / (double)d);
+        thr[i] = alpha * lam;
+    }
+}
+
+/* Rotation frequencies th_i = base^(-2i/d). */
+static void orc_freqs(int d, double base, double* th) {
+    for (int i = 0; i < d / 2; ++i) th[i] = pow(base, -(2.0 * i) / (double)d);
+}
+
+/* Step 3: rotate n_tok tokens x[n_tok][H][d] at positions pos[n_tok] (half-split). */
+void orc_rope(const void* x, int dtype, int64_t n_tok, int H, int d,
+              const int64_t* pos, double base, double* out) {
+    int P = d / 2;
+    double* th = (double*)malloc(sizeof(double) * P);
+    orc_freqs(d, base, th);
+    #pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < n_tok; ++t) {
+        for (int h = 0; h < H; ++h) {
+            int64_t row = (t * H + h) * (int64_t)d;
+            for (int i = 0; i < P; ++i) {
+                double a = (double)pos[t] * th[i];
+                double c = cos(a), s = sin(a);
+                double x0 = orc_load(x, dtype, row + i);
+                double x1 = orc_load(x, dtype, row + i + P);
+                out[row + i] = x0 * c - x1 * s;
+                out[row + i + P] = x1 * c + x0 * s;
+            }
+        }
+    }
+    free(th);
+}
+
+/* Steps 4-5 for one query row: windowed logits over visible keys 0..last,
+ * ordinary softmax, out = sum p v, lse = log sum exp(logit).
+ *   qr  : rotated query [d]          kr : rotated keys [n_k][Hkv][d]
+ *   v   : raw values (dtype)         g  : kv head
+ *   logit: scratch of length last+1
+ * Returns the number of kept (key, pair) terms for this row. */
+static int64_t orc_row(const double* qr, int64_t qpos, const double* kr, const int64_t* kpos,
+                       const void* v, int dtype, int64_t last, int Hkv, int g, int d,
+                       const double* thr, double scale, double* logit, double* out, double* lse) {
+    int P = d / 2;
+    int64_t kept = 0;
+    double m = -INFINITY;
+    for (int64_t c = 0; c <= last; ++c) {
+        const double* k = kr + (c * Hkv + g) * (int64_t)d;
+        double dist = fabs((double)(qpos - kpos[c]));
+        double s = 0.0;
+        for (int i = 0; i < P; ++i) {
+            if (dist <= thr[i]) {
+                s += qr[i] * k[i] + qr[i + P] * k[i + P];
+                ++kept;
+            }
+        }
+        logit[c] = scale * s;
+        if (logit[c] > m) m = logit[c];
+    }
+    double den = 0.0;
+    for (int e = 0; e < d; ++e) out[e] = 0.0;
+    for (int64_t c = 0; c <= last; ++c) {
+        double p = exp(logit[c] - m);
+        den += p;
+        int64_t vrow = (c * Hkv + g) * (int64_t)d;
+        for (int e = 0; e < d; ++e) out[e] += p * orc_load(v, dtype, vrow + e);
+    }
+    for (int e = 0; e < d; ++e) out[e] /= den;
+    *lse = m + log(den);
+    return kept;
+}
+
+/*
+ * Causal prefill.
+ *   q [B][N][Hq][d], k, v [B][N][Hkv][d] (pre-RoPE, dtype), pos [B][N] (NULL -> 0..N-1)
+ *   rows[n_rows]: query token indices to evaluate (NULL -> all N rows, n_rows = N)
+ *   out [B][n_rows][Hq][d], lse [B][Hq][n_rows]  (double)
+ *   kept_out (nullable): total kept (query, key, pair) terms over all evaluated rows/heads.
+ * Returns 0, or -1 on bad arguments.
+ */
+int orc_prefill(const void* q, const void* k, const void* v, int dtype, const int32_t* pos,
+                int B, int64_t N, int Hq, int Hkv, int d, double base, double alpha,
+                double scale, const int64_t* rows, int64_t n_rows,
+                double* out, double* lse, int64_t* kept_out, int nthreads) {
+    if (B < 1 || N < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || d < 2 || d % 2 != 0)
+        return -1;
+    if (!rows) n_rows = N;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#endif
+    int G = Hq / Hkv;
+    int P = d / 2;
+    double* thr = (double*)malloc(sizeof(double) * P);
+    orc_thresholds(d, base, alpha, thr);
+    int64_t* p64 = (int64_t*)malloc(sizeof(int64_t) * N);
+    double* kr = (double*)malloc(sizeof(double) * N * Hkv * d);
+    double* qr = (double*)malloc(sizeof(double) * n_rows * Hq * d);
+    int64_t* qp = (int64_t*)malloc(sizeof(int64_t) * n_rows);
+    int64_t kept_total = 0;
+    for (int b = 0; b < B; ++b) {
+        for (int64_t t = 0; t < N; ++t) p64[t] = pos ? (int64_t)pos[(int64_t)b * N + t] : t;
+        orc_rope((const char*)k + (dtype == ORC_FP32 ? 4 : 2) * (int64_t)b * N * Hkv * d, dtype,
+                 N, Hkv, d, p64, base, kr);
+        /* gather the evaluated query rows, then rotate them at their own positions */
+        const char* qb = (const char*)q + (dtype == ORC_FP32 ? 4 : 2) * (int64_t)b * N * Hq * d;
+        int esz = dtype == ORC_FP32 ? 4 : 2;
+        char* qsel = (char*)malloc((size_t)esz * n_rows * Hq * d);
+        for (int64_t j = 0; j < n_rows; ++j) {
+            int64_t r = rows ? rows[j] : j;
+            memcpy(qsel + (size_t)esz * j * Hq * d, qb + (size_t)esz * r * Hq * d, (size_t)esz * Hq * d);
+            qp[j] = p64[r];
+        }
+        orc_rope(qsel, dtype, n_rows, Hq, d, qp, base, qr);
+        free(qsel);
+        const char* vb = (const char*)v + (size_t)esz * b * N * Hkv * d;
+        int64_t kept_b = 0;
+        #pragma omp parallel reduction(+:kept_b)
+        {
+            double* logit = (double*)malloc(sizeof(double) * N);
+            #pragma omp for schedule(dynamic, 1) collapse(2)
+            for (int64_t j = 0; j < n_rows; ++j) {
+                for (int h = 0; h < Hq; ++h) {
+                    int64_t r = rows ? rows[j] : j;
+                    double* o = out + (((int64_t)b * n_rows + j) * Hq + h) * d;
+                    double* l = lse + ((int64_t)b * Hq + h) * n_rows + j;
+                    kept_b += orc_row(qr + (j * Hq + h) * (int64_t)d, qp[j], kr, p64, vb, dtype,
+                                      r, Hkv, h / G, d, thr, scale, logit, o, l);
+                }
+            }
+            free(logit);
+        }
+        kept_total += kept_b;
+    }
+    if (kept_out) *kept_out = kept_total;
+    free(thr); free(p64); free(kr); free(qr); free(qp);
+    return 0;
+}
+
+/*
+ * One decode step per sequence.
+ *   q [B][Hq][d] pre-RoPE; k, v [B][Lmax][Hkv][d] pre-RoPE cache contents, key c at position c;
+ *   kv_len[B] (1..Lmax); q_pos[B] (NULL -> kv_len-1); the query sees keys 0..kv_len-1.
+ *   out [B][Hq][d], lse [B][Hq] (double).
+ */
+int orc_decode(const void* q, const void* k, const void* v, int dtype, const int32_t* kv_len,
+               const int32_t* q_pos, int B, int64_t Lmax, int Hq, int Hkv, int d, double base,
+               double alpha, double scale, double* out, double* lse, int64_t* kept_out, int nthreads) {
+    if (B < 1 || Lmax < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || d < 2 || d % 2 != 0)
+        return -1;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#endif
+    int G = Hq / Hkv, P = d / 2;
+    int esz = dtype == ORC_FP32 ? 4 : 2;
+    double* thr = (double*)malloc(sizeof(double) * P);
+    orc_thresholds(d, base, alpha, thr);
+    int64_t kept_total = 0;
+    for (int b = 0; b < B; ++b) {
+        int64_t L = kv_len[b];
+        if (L < 1 || L > Lmax) { free(thr); return -1; }
+        int64_t qp = q_pos ? (int64_t)q_pos[b] : L - 1;
+        int64_t* kp = (int64_t*)malloc(sizeof(int64_t) * L);
+        for (int64_t c = 0; c < L; ++c) kp[c] = c;
+        double* kr = (double*)malloc(sizeof(double) * L * Hkv * d);
+        orc_rope((const char*)k + (size_t)esz * b * Lmax * Hkv * d, dtype, L, Hkv, d, kp, base, kr);
+        double* qr = (double*)malloc(sizeof(double) * Hq * d);
+        orc_rope((const char*)q + (size_t)esz * b * Hq * d, dtype, 1, Hq, d, &qp, base, qr);
+        const char* vb = (const char*)v + (size_t)esz * b * Lmax * Hkv * d;
+        int64_t kept_b = 0;
+        #pragma omp parallel reduction(+:kept_b)
+        {
+            double* logit = (double*)malloc(sizeof(double) * L);
+            #pragma omp for schedule(dynamic, 1)
+            for (int h = 0; h < Hq; ++h)
+                kept_b += orc_row(qr + (int64_t)h * d, qp, kr, kp, vb, dtype, L - 1, Hkv, h / G, d,
+                                  thr, scale, logit, out + ((int64_t)b * Hq + h) * d,
+                                  lse + (int64_t)b * Hq + h);
+            free(logit);
+        }
+        kept_total += kept_b;
+        free(kp); free(kr); free(qr);
+    }
+    if (kept_out) *kept_out = kept_total;
+    free(thr);
+    return 0;
+}
+
+/*
+ * Kept-term count by enumeration (no closed form): queries at token indices
+ * q_idx0 .. q_idx0+n_q-1 with positions equal to their indices, keys 0..n_k-1,
+ * key c visible to query r iff c <= r; counts (r, c, i) with |r-c| <= alpha*lambda_i.
+ * total = (d/2) * #visible (r, c).  O(n_q * n_k * d/2).
+ */
+void orc_count_enumerate(int d, double base, double alpha, int64_t n_q, int64_t q_idx0,
+                         int64_t n_k, int64_t* kept, int64_t* total) {
+    int P = d / 2;
+    double* thr = (double*)malloc(sizeof(double) * P);
+    orc_thresholds(d, base, alpha, thr);
+    int64_t kk = 0, tt = 0;
+    #pragma omp parallel for reduction(+:kk, tt) schedule(dynamic, 16)
+    for (int64_t j = 0; j < n_q; ++j) {
+        int64_t r = q_idx0 + j;
+        for (int64_t c = 0; c < n_k && c <= r; ++c) {
+            double dist = (double)(r - c);
+            tt += P;
+            for (int i = 0; i < P; ++i) kk += (dist <= thr[i]);
+        }
+    }
+    *kept = kk;
+    *total = tt;
+    free(thr);
+}

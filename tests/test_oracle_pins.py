@@ -1,0 +1,325 @@
+"""Pins of the fp64 oracle against facts the pages and the mathematics fix.
+
+None of these re-types the oracle's own loop: each compares it with an independent
+formulation (complex-number rotation, library softmax attention, closed forms,
+invariants, hand-derived tiny cases, three separate count enumerations).
+
+Sources:
+  ATFlash abstract ("Per-RoPE-Wavelength Attention Windows for Compute/Memory-Efficient
+  LLM Inference"): exact decomposition over 2-D rotation pairs; pruning beyond a
+  wavelength-proportional distance; every key reachable through low-frequency pairs;
+  closed-form reduction rate logarithmic in N; online softmax untouched.
+  WavePrune original abstract ("One period is often enough for RoPE"): alpha=1 is the
+  first rotation period.
+  "The Heterogeneous Feature of RoPE-based Attention", Explanation: the critical
+  dimension (pairs completing a full period inside the context).
+"""
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+import torch.nn.functional as F
+
+import oracle
+import synth
+
+
+def _complex_rope(x, pos, base):
+    """Independent rotation: pair i of a half-split vector as the complex number
+    x_i + 1j*x_{i+P}, multiplied by exp(1j*pos*theta_i)."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    P = d // 2
+    theta = np.power(float(base), -np.arange(P) * 2.0 / d)
+    z = x[..., :P] + 1j * x[..., P:]
+    ang = np.asarray(pos, dtype=np.float64).reshape((-1,) + (1,) * (x.ndim - 1)) * theta
+    zr = z * np.exp(1j * ang)
+    return np.concatenate([zr.real, zr.imag], axis=-1)
+
+
+def _f64(t):
+    return t.double().numpy()
+
+
+def test_rope_is_complex_multiplication():
+    q, _, _ = synth.prefill_inputs(1, 37, 3, 3, 16, "fp32", seed=11)
+    pos = np.arange(37) * 101 + 5
+    got = oracle.rope(synth.to_oracle(q[0]), pos, 1e4)
+    ref = _complex_rope(_f64(q[0]), pos, 1e4)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_full_window_equals_library_sdpa(dtype):
+    """alpha = inf is ordinary causal RoPE attention."""
+    B, N, Hq, Hkv, d, base = 2, 45, 4, 2, 16, 1e4
+    q, k, v = synth.prefill_inputs(B, N, Hq, Hkv, d, dtype, seed=3)
+    out, lse, kept = oracle.prefill(synth.to_oracle(q), synth.to_oracle(k), synth.to_oracle(v),
+                                    base, math.inf)
+    pos = np.arange(N)
+    qr = torch.from_numpy(np.stack([_complex_rope(_f64(q[b]), pos, base) for b in range(B)]))
+    kr = torch.from_numpy(np.stack([_complex_rope(_f64(k[b]), pos, base) for b in range(B)]))
+    vv = v.double()
+    G = Hq // Hkv
+    kr = kr.repeat_interleave(G, dim=2)
+    vv = vv.repeat_interleave(G, dim=2)
+    ref = F.scaled_dot_product_attention(qr.transpose(1, 2), kr.transpose(1, 2),
+                                         vv.transpose(1, 2), is_causal=True)
+    np.testing.assert_allclose(out, ref.transpose(1, 2).numpy(), rtol=0, atol=1e-12)
+    s = (qr.transpose(1, 2) @ kr.transpose(1, 2).transpose(-1, -2)) / math.sqrt(d)
+    s = s.masked_fill(torch.ones(N, N, dtype=torch.bool).triu(1), -math.inf)
+    np.testing.assert_allclose(lse, torch.logsumexp(s, -1).numpy(), rtol=0, atol=1e-12)
+    assert kept == B * Hq * (d // 2) * N * (N + 1) // 2
+
+
+def test_huge_alpha_is_bitwise_full_window():
+    q, k, v = synth.prefill_inputs(1, 60, 2, 1, 32, "bf16", seed=4)
+    a = [synth.to_oracle(t) for t in (q, k, v)]
+    o1, l1, _ = oracle.prefill(*a, 1e4, math.inf)
+    o2, l2, _ = oracle.prefill(*a, 1e4, 1e9)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def _relative_form(q, k, v, qpos, kpos, base, alpha, scale):
+    """Windowed attention written with the relative (complex) form of each pair's term:
+    Term_i = Re( zq_i * conj(zk_i) * exp(1j*(tq - tk)*theta_i) ), computed on pre-RoPE
+    vectors; softmax from scipy.  q [Nq][d], k, v [Nk][d]; causal by token index."""
+    d = q.shape[-1]
+    P = d // 2
+    theta = np.power(float(base), -np.arange(P) * 2.0 / d)
+    lam = 2.0 * np.pi * np.power(float(base), np.arange(P) * 2.0 / d)
+    zq = q[:, :P] + 1j * q[:, P:]
+    zk = k[:, :P] + 1j * k[:, P:]
+    dt = (np.asarray(qpos, np.float64)[:, None] - np.asarray(kpos, np.float64)[None, :])
+    terms = np.real(zq[:, None, :] * np.conj(zk[None, :, :]) * np.exp(1j * dt[..., None] * theta))
+    keep = np.abs(dt)[..., None] <= alpha * lam
+    logits = scale * np.where(keep, terms, 0.0).sum(-1)
+    Nq, Nk = logits.shape
+    causal = np.arange(Nk)[None, :] <= np.arange(Nq)[:, None]
+    logits = np.where(causal, logits, -np.inf)
+    p = scipy.special.softmax(logits, axis=-1)
+    return p @ v, scipy.special.logsumexp(logits, axis=-1)
+
+
+@pytest.mark.parametrize("alpha", [0.0, 0.5, 1.0, 2.0, 8.0])
+@pytest.mark.parametrize("positions", ["default", "gapped", "nonmonotone"])
+def test_windowed_equals_relative_form(alpha, positions):
+    N, H, d, base = 40, 1, 16, 100.0
+    q, k, v = synth.prefill_inputs(1, N, H, H, d, "fp32", seed=7)
+    rng = np.random.default_rng(5)
+    if positions == "default":
+        pos = np.arange(N)
+    elif positions == "gapped":
+        pos = np.cumsum(rng.integers(0, 9, N))
+    else:
+        pos = rng.integers(0, 200, N)
+    out, lse, _ = oracle.prefill(synth.to_oracle(q), synth.to_oracle(k), synth.to_oracle(v),
+                                 base, alpha, pos=pos)
+    ref_o, ref_l = _relative_form(_f64(q[0, :, 0]), _f64(k[0, :, 0]), _f64(v[0, :, 0]),
+                                  pos, pos, base, alpha, 1.0 / math.sqrt(d))
+    np.testing.assert_allclose(out[0, :, 0], ref_o, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse[0, 0], ref_l, rtol=0, atol=1e-12)
+
+
+def test_alpha_zero_closed_form():
+    """alpha = 0 keeps terms only at distance 0: row r has logit s*q_r.k_r on the diagonal
+    (rotation by the same angle preserves the dot product) and 0 elsewhere, so
+    out_r = (e^l v_r + sum_{c<r} v_c) / (e^l + r),  lse_r = log(e^l + r)."""
+    N, d = 50, 32
+    q, k, v = synth.prefill_inputs(1, N, 1, 1, d, "fp32", seed=9)
+    out, lse, kept = oracle.prefill(synth.to_oracle(q), synth.to_oracle(k), synth.to_oracle(v),
+                                    1e4, 0.0)
+    qq, kk, vv = _f64(q[0, :, 0]), _f64(k[0, :, 0]), _f64(v[0, :, 0])
+    ell = (qq * kk).sum(-1) / math.sqrt(d)
+    csum = np.cumsum(vv, axis=0) - vv
+    r = np.arange(N)[:, None]
+    ref = (np.exp(ell)[:, None] * vv + csum) / (np.exp(ell)[:, None] + r)
+    np.testing.assert_allclose(out[0, :, 0], ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse[0, 0], np.log(np.exp(ell) + np.arange(N)), rtol=0, atol=1e-12)
+    assert kept == N * d // 2
+
+
+@pytest.mark.parametrize("tk, alpha_steps, kept_far", [(6, 0, True), (7, 0, False),
+                                                       (7, +7, True), (7, -1, False)])
+def test_two_token_window_edge(tk, alpha_steps, kept_far):
+    """Hand-derived d=2 case (one pair, theta_0 = 1, lambda_0 = 2*pi).  q = k = (1, 0) for
+    both tokens, v_0 = (1, 0), v_1 = (0, 1).  Row 1 sees key 1 at distance 0 (term 1) and
+    key 0 at distance tk (term cos(tk) if tk <= alpha*2*pi, else 0)."""
+    alpha = 1.0
+    if alpha_steps:
+        alpha = 7.0 / (2.0 * math.pi)          # alpha*2*pi lands within an ulp of 7
+        for _ in range(abs(alpha_steps)):
+            alpha = float(np.nextafter(alpha, np.inf if alpha_steps > 0 else -np.inf))
+    thr = oracle.thresholds(2, 1e4, alpha)[0]
+    assert (tk <= thr) == kept_far
+    q = np.array([[[[1.0, 0.0]], [[1.0, 0.0]]]], dtype=np.float32)
+    v = np.array([[[[1.0, 0.0]], [[0.0, 1.0]]]], dtype=np.float32)
+    out, lse, _ = oracle.prefill(q, q, v, 1e4, alpha, pos=np.array([0, tk]))
+    s = 1.0 / math.sqrt(2.0)
+    l0 = s * math.cos(tk) if kept_far else 0.0
+    l1 = s * 1.0
+    w0 = math.exp(l0) / (math.exp(l0) + math.exp(l1))
+    np.testing.assert_allclose(out[0, 1, 0], [w0, 1.0 - w0], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(out[0, 0, 0], [1.0, 0.0], rtol=0, atol=1e-15)
+    assert abs(lse[0, 0, 1] - math.log(math.exp(l0) + math.exp(l1))) < 1e-15
+
+
+def test_shift_invariance():
+    """RoPE scores depend on positions only through differences (WavePrune abstract:
+    'invariant to a common shift of positions'); the window does too."""
+    N = 64
+    q, k, v = synth.prefill_inputs(1, N, 2, 2, 32, "fp32", seed=12)
+    a = [synth.to_oracle(t) for t in (q, k, v)]
+    pos = np.cumsum(np.random.default_rng(1).integers(0, 5, N))
+    o1, l1, c1 = oracle.prefill(*a, 1e4, 1.0, pos=pos)
+    o2, l2, c2 = oracle.prefill(*a, 1e4, 1.0, pos=pos + 123457)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-9)
+    np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-9)
+    assert c1 == c2
+
+
+def test_gqa_equals_repeated_kv():
+    q, k, v = synth.prefill_inputs(1, 33, 6, 2, 16, "fp32", seed=13)
+    a = oracle.prefill(synth.to_oracle(q), synth.to_oracle(k), synth.to_oracle(v), 1e4, 1.0)
+    kr = k.repeat_interleave(3, dim=2)
+    vr = v.repeat_interleave(3, dim=2)
+    b = oracle.prefill(synth.to_oracle(q), synth.to_oracle(kr), synth.to_oracle(vr), 1e4, 1.0)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and a[2] == b[2]
+
+
+def test_sampled_rows_equal_full():
+    q, k, v = synth.prefill_inputs(2, 70, 4, 2, 16, "bf16", seed=14)
+    a = [synth.to_oracle(t) for t in (q, k, v)]
+    full_o, full_l, _ = oracle.prefill(*a, 1e4, 1.0)
+    rows = np.array([0, 3, 31, 32, 69])
+    o, l, _ = oracle.prefill(*a, 1e4, 1.0, rows=rows)
+    assert np.array_equal(o, full_o[:, rows]) and np.array_equal(l, full_l[:, :, rows])
+
+
+def test_decode_equals_last_prefill_row():
+    B, L, Hq, Hkv, d = 3, 57, 4, 2, 32
+    q, k, v = synth.prefill_inputs(B, L, Hq, Hkv, d, "bf16", seed=15)
+    a = [synth.to_oracle(t) for t in (q, k, v)]
+    po, pl, _ = oracle.prefill(*a, 1e4, 1.0)
+    lens = np.array([L, 20, 1], dtype=np.int32)
+    for b in range(B):
+        n = int(lens[b])
+        qd = synth.to_oracle(q[:, n - 1])                  # [B][Hq][d]
+        o, l, kept = oracle.decode(qd, a[1], a[2], lens, 1e4, 1.0)
+        if n == L:
+            np.testing.assert_allclose(o[b], po[b, L - 1], rtol=0, atol=1e-13)
+            np.testing.assert_allclose(l[b], pl[b, :, L - 1], rtol=0, atol=1e-13)
+        pb, plb, _ = oracle.prefill(a[0][b:b + 1, :n], a[1][b:b + 1, :n], a[2][b:b + 1, :n],
+                                    1e4, 1.0)
+        np.testing.assert_allclose(o[b], pb[0, n - 1], rtol=0, atol=1e-13)
+
+
+def test_decode_explicit_query_position():
+    """q_pos = kv_len-1 is the default; an explicit q_pos shifts every distance."""
+    B, L, H, d = 1, 40, 2, 16
+    q, k, v, _ = synth.decode_inputs(B, L, H, H, d, "fp32", seed=16, len_lo=L)
+    lens = np.array([L], np.int32)
+    a = [synth.to_oracle(t) for t in (q, k, v)]
+    o1, _, _ = oracle.decode(*a, lens, 100.0, 1.0)
+    o2, _, _ = oracle.decode(*a, lens, 100.0, 1.0, q_pos=np.array([L - 1], np.int32))
+    assert np.array_equal(o1, o2)
+    o3, l3, _ = oracle.decode(*a, lens, 100.0, 1.0, q_pos=np.array([L + 30], np.int32))
+    # a query past its keys sees all of them: all-visible softmax of the relative form
+    d2 = d // 2
+    theta = np.power(100.0, -np.arange(d2) * 2.0 / d)
+    lam = 2.0 * np.pi * np.power(100.0, np.arange(d2) * 2.0 / d)
+    qq, kk, vv = _f64(q[0, 0]), _f64(k[0, :, 0]), _f64(v[0, :, 0])
+    zq = qq[:d2] + 1j * qq[d2:]
+    zk = kk[:, :d2] + 1j * kk[:, d2:]
+    dt = (L + 30) - np.arange(L, dtype=np.float64)
+    terms = np.real(zq[None] * np.conj(zk) * np.exp(1j * dt[:, None] * theta))
+    logit = np.where(np.abs(dt)[:, None] <= lam, terms, 0.0).sum(-1) / math.sqrt(d)
+    p = scipy.special.softmax(logit)
+    np.testing.assert_allclose(o3[0, 0], p @ vv, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l3[0, 0], scipy.special.logsumexp(logit), rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------------------------- counts
+
+GRID = [(d, base, alpha) for d in (2, 4, 16, 64, 128) for base in (10.0, 1e4, 1e6)
+        for alpha in (0.0, 0.5, 1.0, 2.0, 8.0, math.inf)]
+
+
+@pytest.mark.parametrize("d,base,alpha", GRID)
+def test_count_three_enumerations_agree(d, base, alpha):
+    for N in (1, 2, 7, 64, 300):
+        a = oracle.count_enumerate(d, base, alpha, N, 0, N)
+        b = oracle.count_bruteforce(d, base, alpha, N, 0, N)
+        c = oracle.count_by_distance(d, base, alpha, N, 0, N)
+        assert a == b == c
+        assert a[1] == (d // 2) * N * (N + 1) // 2
+    for L in (1, 5, 300):                                  # decode: one query at L-1
+        a = oracle.count_enumerate(d, base, alpha, 1, L - 1, L)
+        assert a == oracle.count_bruteforce(d, base, alpha, 1, L - 1, L)
+        assert a == oracle.count_by_distance(d, base, alpha, 1, L - 1, L)
+    a = oracle.count_enumerate(d, base, alpha, 37, 250, 260)   # chunk of queries
+    assert a == oracle.count_bruteforce(d, base, alpha, 37, 250, 260)
+    assert a == oracle.count_by_distance(d, base, alpha, 37, 250, 260)
+
+
+def test_count_matches_attention_tally():
+    """The kept-term tally of the attention oracle equals the enumerated count."""
+    q, k, v = synth.prefill_inputs(1, 256, 2, 2, 64, "fp32", seed=1)
+    _, _, kept = oracle.prefill(synth.to_oracle(q), synth.to_oracle(k), synth.to_oracle(v),
+                                1e4, 1.0)
+    assert kept == 2 * oracle.count_enumerate(64, 1e4, 1.0, 256, 0, 256)[0]
+
+
+@pytest.mark.parametrize("d,base", [(128, 5e5), (64, 1e6), (128, 1e7)])
+def test_pruned_fraction_grows_logarithmically(d, base):
+    """ATFlash abstract: the reduction rate has a closed form logarithmic in N.  Once
+    every short-wavelength pair is well inside N, doubling N adds ln 2 / ln base to the
+    pruned fraction (pairs are spaced ln(base)*2/d apart in ln(lambda))."""
+    slope = math.log(2.0) / math.log(base)
+    frac = {}
+    for k in range(12, 21):
+        N = 1 << k
+        kept, total = oracle.count_by_distance(d, base, 1.0, N, 0, N)
+        frac[k] = 1.0 - kept / total
+    diffs = [frac[k + 1] - frac[k] for k in range(12, 20)]
+    assert all(dd > 0 for dd in diffs)
+    # the per-doubling increment oscillates around the slope with the pair spacing
+    assert abs(np.mean(diffs) - slope) < 0.1 * slope
+    assert all(abs(dd - slope) < 0.45 * slope for dd in diffs)
+
+
+@pytest.mark.parametrize("N,alpha", [(256, 1.0), (300, 0.001), (300, 0.0), (1000, 0.01)])
+def test_reachability(N, alpha):
+    """ATFlash abstract: every key remains reachable through the low-frequency pairs.
+    A (query, key) pair has no active term iff its distance exceeds the largest
+    threshold; there are C(N - W, 2) such pairs, W = min(floor(alpha*lambda_max), N-1),
+    which is zero whenever alpha*lambda_max >= N-1."""
+    d, base = 64, 1e4
+    thr = oracle.thresholds(d, base, alpha)
+    r = np.arange(N)[:, None]
+    c = np.arange(N)[None, :]
+    dist = (r - c).astype(np.float64)
+    visible = c <= r
+    zero_terms = int(np.count_nonzero(visible & ~(dist[..., None] <= thr).any(-1)))
+    W = min(math.floor(thr[-1]), N - 1)
+    assert zero_terms == (N - W) * (N - W - 1) // 2
+    if thr[-1] >= N - 1:
+        assert zero_terms == 0
+
+
+@pytest.mark.parametrize("d,base,N", [(64, 1e4, 256), (64, 1e6, 32768), (128, 5e5, 131072),
+                                      (128, 1e7, 1 << 20)])
+def test_critical_dimension(d, base, N):
+    """'Heterogeneous Feature' talk, Explanation: the critical dimension counts the dims
+    whose RoPE period completes inside the context.  At alpha = 1 those are exactly the
+    pairs that ever lose a term inside N (a pair loses a term iff some visible distance
+    exceeds its period)."""
+    thr = oracle.thresholds(d, base, 1.0)
+    ever_pruned = 0
+    for t in thr:
+        kept_i = int(np.sum((N - np.arange(N))[np.arange(N) <= t]))
+        ever_pruned += kept_i < N * (N + 1) // 2
+    periods = 2.0 * np.pi * np.power(base, np.arange(d // 2) * 2.0 / d)
+    assert ever_pruned == int(np.count_nonzero(periods < N - 1))
