@@ -1,0 +1,152 @@
+/*
+ * wpa.h -- C ABI of libwpa: per-RoPE-wavelength windowed causal attention on MI355X.
+ *
+ * The operation (ATFlash, "Per-RoPE-Wavelength Attention Windows for Compute/Memory-
+ * Efficient LLM Inference", abstract; WavePrune, "One period is often enough for RoPE",
+ * original abstract):
+ *   The RoPE attention score of query token r and key token c is an exact sum over the
+ *   d/2 two-dimensional rotation ("frequency") pairs.  Pair i has wavelength
+ *   lambda_i = 2*pi*base^(2i/d) and keeps its term only while the query-key distance
+ *   |t_r - t_c| <= alpha*lambda_i; a pruned term contributes zero and the key stays in
+ *   the softmax.  alpha = 1 is WavePrune's "first rotation period"; alpha = +INFINITY is
+ *   ordinary (full-window) causal RoPE attention in the same kernels.  Softmax and the
+ *   P*V product are unchanged.
+ *
+ * Conventions shared by every entry point
+ *   - Pair layout is half-split: pair i of a head vector is (x[i], x[i + d/2]); rotation
+ *     x'[i] = x[i]cos(t th_i) - x[i+d/2] sin(t th_i), x'[i+d/2] = x[i+d/2]cos + x[i]sin,
+ *     th_i = base^(-2i/d).
+ *   - The window test uses alpha*lambda_i evaluated in IEEE double as
+ *       alpha * ((2.0*M_PI) * pow(base, (2.0*i)/d))
+ *     and keeps pair i at integer distance D iff D <= that value.
+ *   - Logits are scale * (windowed sum); scale <= 0 selects 1/sqrt(d).
+ *   - Causality is by token index (key c visible to query r iff c <= r).
+ *   - GQA: q head h reads kv head h / (Hq/Hkv).
+ *   - dtype (WPA_BF16 or WPA_FP32) is the element type of q, k and v; out_dtype that of
+ *     out.  fp32 inputs are rounded to bf16 (round-to-nearest-even) on load; every matrix
+ *     product runs in bf16 with fp32 accumulation; softmax statistics are fp32.  A bf16
+ *     out is the fp32 result rounded to nearest even.
+ *   - All pointers except those documented as host pointers are device pointers.  Device
+ *     buffers must be 16-byte aligned.  The caller owns every buffer (including workspace
+ *     and caches); the library allocates nothing and keeps no per-call state.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued and the call
+ *     returns without waiting; faults inside kernels surface at the caller's next
+ *     synchronisation.
+ *   - Return value: WPA_OK, or a negative status.  Every argument is checked before any
+ *     work is enqueued; a failing call enqueues nothing and wpa_last_error() describes it.
+ *
+ * Supported: d in {64, 128}; Hq % Hkv == 0; base > 1; alpha >= 0 (not NaN; +inf allowed);
+ * B, N, heads >= 1; token counts and positions below 2^31.
+ */
+#ifndef WPA_H
+#define WPA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    WPA_OK = 0,
+    WPA_ERR_INVALID = -1,      /* argument out of range, null or misaligned pointer */
+    WPA_ERR_UNSUPPORTED = -2,  /* valid request this build does not implement (e.g. d) */
+    WPA_ERR_WORKSPACE = -3,    /* workspace smaller than the matching *_bytes() query */
+    WPA_ERR_HIP = -4           /* the HIP runtime reported an error while enqueueing */
+};
+
+enum { WPA_BF16 = 0, WPA_FP32 = 1 };
+
+/*
+ * Kept-term count, host only, exact (ATFlash abstract: the reduction rate is
+ * input-independent with a closed form logarithmic in N).  A term is one pair's
+ * contribution to one (query, key) score.  Queries sit at positions q_pos0 ..
+ * q_pos0+n_q-1, keys at 0 .. n_k-1, key c visible to query r iff c <= r.
+ *   *kept  = #{(r, c, i) visible : r - c <= alpha*lambda_i}
+ *   *total = (d/2) * #{(r, c) visible}
+ * Prefill of N tokens: (n_q = n_k = N, q_pos0 = 0).  Decode at length L: (1, L-1, L).
+ * Counts are per head.  Any even d >= 2 is accepted here.  O(d) time.
+ */
+int wpa_count_terms(int32_t d, double base, double alpha, int64_t n_q, int64_t q_pos0,
+                    int64_t n_k, int64_t* kept, int64_t* total);
+
+/*
+ * Integer window table the kernels use: W[i] = floor(alpha*lambda_i), or INT32_MAX when
+ * that is +inf or exceeds INT32_MAX-1 (every representable distance is then inside).
+ * W is a host array of d/2 entries.  Any even d in [2, 128].
+ */
+int wpa_thresholds(int32_t d, double base, double alpha, int32_t* W);
+
+/* Workspace bytes wpa_prefill needs: the rotated, pair-blocked K and the transposed V
+ * of all B*Hkv heads, padded to 64 tokens (2 * B*Hkv*roundup(N,64)*d*2 bytes). */
+size_t wpa_prefill_workspace_bytes(int32_t B, int64_t N, int32_t Hkv, int32_t d);
+
+/*
+ * Causal windowed prefill.
+ *   q         [B][N][Hq][d]  pre-RoPE queries (dtype)
+ *   k, v      [B][N][Hkv][d] pre-RoPE keys, values (dtype)
+ *   out       [B][N][Hq][d]  attention output (out_dtype)
+ *   lse       [B][Hq][N] fp32 natural-log sum of exp(logits), or NULL
+ *   positions [B][N] int32 token positions, non-decreasing within each sequence and in
+ *             [0, 2^31); NULL means 0..N-1.  (Non-decreasing order is a precondition
+ *             the kernels rely on; it is not checked.)
+ *   term_count  NULL, or a device counter to which the number of kept (query, key, pair)
+ *             terms summed over all heads is added (atomically).  It is not cleared.
+ *   workspace at least wpa_prefill_workspace_bytes(B, N, Hkv, d) bytes, device.
+ */
+int wpa_prefill(const void* q, const void* k, const void* v, void* out, float* lse,
+                const int32_t* positions, int32_t B, int64_t N, int32_t Hq, int32_t Hkv,
+                int32_t d, double base, double alpha, float scale, int32_t dtype,
+                int32_t out_dtype, unsigned long long* term_count, void* workspace,
+                size_t ws_bytes, void* stream);
+
+/* Bytes of the decode K cache (opaque: rotated keys, pair-blocked) and of the V cache
+ * ([B][Hkv][Lmax][d] bf16) for B sequences of up to Lmax tokens. */
+size_t wpa_kcache_bytes(int32_t B, int64_t Lmax, int32_t Hkv, int32_t d);
+size_t wpa_vcache_bytes(int32_t B, int64_t Lmax, int32_t Hkv, int32_t d);
+
+/*
+ * Append n tokens (token indices start .. start+n-1, which are also their positions) of
+ * every sequence to the decode caches.  k, v are pre-RoPE [B][n][Hkv][d] (dtype).  Keys
+ * are rotated once here and stored as bf16; values are stored as bf16.
+ * Requires 0 <= start, n >= 1, start + n <= Lmax.
+ */
+int wpa_kv_write(const void* k, const void* v, int64_t start, int64_t n, void* k_cache,
+                 void* v_cache, int32_t B, int64_t Lmax, int32_t Hkv, int32_t d, double base,
+                 int32_t dtype, void* stream);
+
+/* Workspace bytes wpa_decode needs for split-KV partial results (chunk_keys as passed to
+ * wpa_decode; 0 = the library's choice for this shape). */
+size_t wpa_decode_workspace_bytes(int32_t B, int64_t Lmax, int32_t Hq, int32_t Hkv,
+                                  int32_t d, int32_t chunk_keys);
+
+/*
+ * One decode step per sequence (ATFlash abstract: the window ported into a decode
+ * kernel; far keys read only the pairs still active).
+ *   q        [B][Hq][d] pre-RoPE query (dtype)
+ *   k_cache, v_cache  written by wpa_kv_write for the same B, Lmax, Hkv, d, base
+ *   kv_len   [B] int32 device, each in [1, Lmax]: the query sees keys 0 .. kv_len-1
+ *   q_pos    [B] int32 device query positions, or NULL for kv_len-1 (the query's own
+ *            token is then the last cached key)
+ *   out      [B][Hq][d] (out_dtype);  lse [B][Hq] fp32 or NULL
+ *   chunk_keys  keys per split-KV work item: a multiple of 256, or 0 for the library's
+ *            choice.  The result does not depend on it beyond fp32 rounding.
+ *   workspace at least wpa_decode_workspace_bytes(B, Lmax, Hq, Hkv, d, chunk_keys).
+ * kv_len values outside [1, Lmax] are a precondition violation (not checked: they live
+ * on the device).
+ */
+int wpa_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* kv_len,
+               const int32_t* q_pos, void* out, float* lse, int32_t B, int64_t Lmax,
+               int32_t Hq, int32_t Hkv, int32_t d, double base, double alpha, float scale,
+               int32_t dtype, int32_t out_dtype, unsigned long long* term_count,
+               int32_t chunk_keys, void* workspace, size_t ws_bytes, void* stream);
+
+/* Message for the last non-OK status returned on the calling thread ("" if none). */
+const char* wpa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WPA_H */

@@ -1,0 +1,240 @@
+"""Per-RoPE-wavelength windowed causal attention on MI355X (gfx950).
+
+Thin ctypes binding over ``libwpa.so`` (C ABI in ``include/wpa.h``).  This module only
+marshals arguments: it checks tensor shapes/dtypes/devices, allocates outputs and
+workspace with torch when the caller does not pass them, and forwards raw device
+pointers and the current HIP stream.  Every step of the computation runs in the HIP
+kernels behind the C ABI; there is no CPU or PyTorch fallback.  If the library is not
+built, every entry point raises.
+
+Method (ATFlash abstract, "Per-RoPE-Wavelength Attention Windows"; WavePrune original
+abstract): pair i of the half-split head vector, with wavelength 2*pi*base^(2i/d),
+contributes its q.k term only while the query-key distance is <= alpha*wavelength;
+alpha = 1 is the first rotation period, alpha = inf is full causal RoPE attention.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libwpa.so")
+
+WPA_OK, WPA_ERR_INVALID, WPA_ERR_UNSUPPORTED, WPA_ERR_WORKSPACE, WPA_ERR_HIP = 0, -1, -2, -3, -4
+WPA_BF16, WPA_FP32 = 0, 1
+
+# every symbol include/wpa.h declares
+EXPORTS = ("wpa_count_terms", "wpa_thresholds", "wpa_prefill_workspace_bytes", "wpa_prefill",
+           "wpa_kcache_bytes", "wpa_vcache_bytes", "wpa_kv_write", "wpa_decode_workspace_bytes",
+           "wpa_decode", "wpa_last_error")
+
+
+class WpaError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__("wpa error %d: %s" % (code, msg))
+        self.code = code
+
+
+_lib = None
+
+
+def lib():
+    """Load libwpa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libwpa.so is not built: run `python -m rope_wavelength_sparsity_amd.build` "
+                           "(or __graft_entry__.build()) first")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, D, F, SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double,
+                             ctypes.c_float, ctypes.c_size_t)
+    L.wpa_count_terms.argtypes = [I32, D, D, I64, I64, I64, P, P]
+    L.wpa_count_terms.restype = ctypes.c_int
+    L.wpa_thresholds.argtypes = [I32, D, D, P]
+    L.wpa_thresholds.restype = ctypes.c_int
+    L.wpa_prefill_workspace_bytes.argtypes = [I32, I64, I32, I32]
+    L.wpa_prefill_workspace_bytes.restype = SZ
+    L.wpa_prefill.argtypes = [P, P, P, P, P, P, I32, I64, I32, I32, I32, D, D, F, I32, I32, P, P, SZ,
+                              P]
+    L.wpa_prefill.restype = ctypes.c_int
+    L.wpa_kcache_bytes.argtypes = [I32, I64, I32, I32]
+    L.wpa_kcache_bytes.restype = SZ
+    L.wpa_vcache_bytes.argtypes = [I32, I64, I32, I32]
+    L.wpa_vcache_bytes.restype = SZ
+    L.wpa_kv_write.argtypes = [P, P, I64, I64, P, P, I32, I64, I32, I32, D, I32, P]
+    L.wpa_kv_write.restype = ctypes.c_int
+    L.wpa_decode_workspace_bytes.argtypes = [I32, I64, I32, I32, I32, I32]
+    L.wpa_decode_workspace_bytes.restype = SZ
+    L.wpa_decode.argtypes = [P, P, P, P, P, P, P, I32, I64, I32, I32, I32, D, D, F, I32, I32, P,
+                             I32, P, SZ, P]
+    L.wpa_decode.restype = ctypes.c_int
+    L.wpa_last_error.argtypes = []
+    L.wpa_last_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(rc: int):
+    if rc != WPA_OK:
+        raise WpaError(rc, lib().wpa_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return WPA_BF16
+    if t.dtype == torch.float32:
+        return WPA_FP32
+    raise TypeError("q, k, v must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _dev(t, name):
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous device tensor" % name)
+
+
+# ------------------------------------------------------------------------------ host-only
+
+def count_terms(d: int, base: float, alpha: float, n_q: int, q_pos0: int, n_k: int):
+    """(kept, total) (query, key, pair) terms per head; exact closed form, host only."""
+    kept, total = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().wpa_count_terms(d, float(base), float(alpha), n_q, q_pos0, n_k,
+                                 ctypes.byref(kept), ctypes.byref(total)))
+    return kept.value, total.value
+
+
+def thresholds(d: int, base: float, alpha: float):
+    """Integer window table W_i = floor(alpha * 2*pi * base^(2i/d)) (INT32_MAX if unbounded)."""
+    W = (ctypes.c_int32 * (d // 2))()
+    _check(lib().wpa_thresholds(d, float(base), float(alpha), W))
+    return list(W)
+
+
+def prefill_workspace_bytes(B, N, Hkv, d) -> int:
+    return lib().wpa_prefill_workspace_bytes(B, N, Hkv, d)
+
+
+def kcache_bytes(B, Lmax, Hkv, d) -> int:
+    return lib().wpa_kcache_bytes(B, Lmax, Hkv, d)
+
+
+def vcache_bytes(B, Lmax, Hkv, d) -> int:
+    return lib().wpa_vcache_bytes(B, Lmax, Hkv, d)
+
+
+def decode_workspace_bytes(B, Lmax, Hq, Hkv, d, chunk_keys=0) -> int:
+    return lib().wpa_decode_workspace_bytes(B, Lmax, Hq, Hkv, d, chunk_keys)
+
+
+# ------------------------------------------------------------------------------ device ops
+
+def prefill(q, k, v, base: float, alpha: float, *, scale: float | None = None, positions=None,
+            out=None, out_dtype=None, lse=None, want_lse: bool = False, term_count=None,
+            workspace=None, stream=None):
+    """Causal windowed prefill.  q [B][N][Hq][d], k/v [B][N][Hkv][d] (bf16 or fp32, pre-RoPE).
+
+    Returns out [B][N][Hq][d] (out_dtype, default q's dtype), or (out, lse [B][Hq][N] fp32)
+    when want_lse or an lse buffer is passed.  term_count: optional int64 device tensor of
+    one element to which the kept-term count is added.
+    """
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n)
+    if q.dim() != 4 or k.shape != v.shape or k.dim() != 4:
+        raise ValueError("q [B][N][Hq][d], k, v [B][N][Hkv][d] expected")
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if k.shape[0] != B or k.shape[1] != N or k.shape[3] != d or not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v shapes/dtypes disagree")
+    if out is None:
+        out = torch.empty(q.shape, device=q.device, dtype=out_dtype or q.dtype)
+    _dev(out, "out")
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq, N), device=q.device, dtype=torch.float32)
+    if positions is not None:
+        _dev(positions, "positions")
+        if positions.dtype != torch.int32 or positions.numel() != B * N:
+            raise ValueError("positions must be int32 [B][N]")
+    if term_count is not None and (term_count.dtype != torch.int64 or not term_count.is_cuda):
+        raise ValueError("term_count must be an int64 device tensor")
+    need = prefill_workspace_bytes(B, N, Hkv, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), device=q.device, dtype=torch.uint8)
+    _check(lib().wpa_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(positions),
+                             B, N, Hq, Hkv, d, float(base), float(alpha),
+                             float(scale) if scale is not None else 0.0, _dtype_code(q),
+                             _dtype_code(out), _ptr(term_count), _ptr(workspace),
+                             workspace.numel(),
+                             _stream(stream)))
+    return (out, lse) if lse is not None else out
+
+
+class KVCache:
+    """Decode caches for B sequences of up to Lmax tokens (library-owned K layout)."""
+
+    def __init__(self, B, Lmax, Hkv, d, base, device="cuda"):
+        self.B, self.Lmax, self.Hkv, self.d, self.base = B, Lmax, Hkv, d, float(base)
+        self.k = torch.empty(kcache_bytes(B, Lmax, Hkv, d), device=device, dtype=torch.uint8)
+        self.v = torch.empty(vcache_bytes(B, Lmax, Hkv, d), device=device, dtype=torch.uint8)
+
+    def write(self, k, v, start: int, stream=None):
+        """Append pre-RoPE k, v [B][n][Hkv][d] at token indices start .. start+n-1."""
+        _dev(k, "k")
+        _dev(v, "v")
+        if k.shape != v.shape or k.dim() != 4 or k.shape[0] != self.B or k.shape[2] != self.Hkv \
+                or k.shape[3] != self.d or k.dtype != v.dtype:
+            raise ValueError("k, v must be [B][n][Hkv][d] of one dtype")
+        _check(lib().wpa_kv_write(_ptr(k), _ptr(v), int(start), k.shape[1], _ptr(self.k),
+                                  _ptr(self.v), self.B, self.Lmax, self.Hkv, self.d, self.base,
+                                  _dtype_code(k), _stream(stream)))
+
+    def v_view(self):
+        """The V cache as bf16 [B][Hkv][Lmax][d]."""
+        return self.v.view(torch.bfloat16).view(self.B, self.Hkv, self.Lmax, self.d)
+
+
+def decode(q, cache: KVCache, kv_len, alpha: float, *, q_pos=None, scale: float | None = None,
+           out=None, out_dtype=None, lse=None, want_lse: bool = False, term_count=None,
+           chunk_keys: int = 0, workspace=None, stream=None):
+    """One decode step.  q [B][Hq][d] pre-RoPE; kv_len int32 device [B]."""
+    _dev(q, "q")
+    _dev(kv_len, "kv_len")
+    B, Hq, d = q.shape
+    if B != cache.B or d != cache.d or kv_len.dtype != torch.int32 or kv_len.numel() != B:
+        raise ValueError("q [B][Hq][d] and kv_len int32 [B] must match the cache")
+    if q_pos is not None:
+        _dev(q_pos, "q_pos")
+        if q_pos.dtype != torch.int32 or q_pos.numel() != B:
+            raise ValueError("q_pos must be int32 [B]")
+    if out is None:
+        out = torch.empty(q.shape, device=q.device, dtype=out_dtype or q.dtype)
+    _dev(out, "out")
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq), device=q.device, dtype=torch.float32)
+    need = decode_workspace_bytes(B, cache.Lmax, Hq, cache.Hkv, d, chunk_keys)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), device=q.device, dtype=torch.uint8)
+    _check(lib().wpa_decode(_ptr(q), _ptr(cache.k), _ptr(cache.v), _ptr(kv_len), _ptr(q_pos),
+                            _ptr(out), _ptr(lse), B, cache.Lmax, Hq, cache.Hkv, d, cache.base,
+                            float(alpha), float(scale) if scale is not None else 0.0,
+                            _dtype_code(q), _dtype_code(out), _ptr(term_count), int(chunk_keys),
+                            _ptr(workspace),
+                            workspace.numel(), _stream(stream)))
+    return (out, lse) if lse is not None else out
+
+
+def full_window() -> float:
+    """alpha for the full-window (dense) mode of the same kernels."""
+    return math.inf

@@ -1,0 +1,345 @@
+// Causal prefill with a per-RoPE-wavelength window (ATFlash abstract; WavePrune
+// original abstract), bf16 MFMA on gfx950.
+//
+// Work decomposition
+//   A workgroup owns one (sequence b, kv head g, chunk of Gc q heads of that kv head) and
+//   32*R consecutive query rows; wave w handles q head (w % Gc) and the 32 rows of row
+//   group (w / Gc).  All waves share each K/V tile staged in LDS (GQA reuse).
+//   Key tiles of 64 tokens are walked from the diagonal outward.
+//
+// Per 32x32 (query x key) sub-tile
+//   Distance band: dmin/dmax over the sub-tile's visible elements.  With the window table
+//   W (non-decreasing in the pair index), pairs split into dead (W < dmin), straddling
+//   (dmin <= W < dmax) and fully active (W >= dmax).  Because the active pairs at any
+//   distance are a suffix of the pair axis (ATFlash abstract: "a slice of the
+//   query--key contraction axis"), fully active pairs occupy a suffix of 16-dim blocks:
+//     * S^T = K'_blk * Q'_blk^T on v_mfma_f32_32x32x16_bf16 over those blocks only; the
+//       leading pairs of the first such block are zeroed in the Q operand;
+//     * straddling pairs are added per element on VALU with the exact test D <= W_i.
+//   Then causal mask, online softmax (fp32, exp2 domain; the running max is only moved
+//   when it grows by more than 2^8, which leaves the result exact) and O^T += V^T P^T on
+//   MFMA.
+//
+// Register layouts (32x32x16 MFMA: A row m and B column n live in lane m%32 / n%32, the
+// 16-deep contraction is split 8+8 between lane halves; C element (row 8(r/4)+4(l/32)+r%4,
+// column l%32) is register r of lane l):
+//   Q operand (B): lane = query row, half h holds the first-half (h=0) or second-half
+//     (h=1) components of the block's 8 pairs.
+//   K operand (A): lane m%32 reads key row perm(m) = m with bits 2 and 3 swapped, so S^T
+//     register r of half h holds key 16(r/8) + 8h + (r%8).  Registers 8c..8c+7 are then
+//     exactly the 8 keys that half h must supply as the B operand of the P*V step over
+//     keys 16c..16c+15, and the P^T operand needs no data movement.
+//   V operand (A of the P*V step): V^T rows (dims) from LDS, key-contiguous.
+//   O^T accumulator: lane = query row, so the softmax rescale is a per-lane scalar.
+#include "wpa_device.hpp"
+#include "wpa_internal.hpp"
+
+namespace wpa {
+
+namespace {
+
+constexpr int BN = kTileKeys;     // keys per tile
+constexpr int VSTR = BN + 8;      // LDS row stride of V^T (elements), padded against bank conflicts
+constexpr float kTau = 8.0f;      // lazy-rescale threshold (log2 units)
+
+__device__ inline int perm_row(int m) {
+    return (m & ~0xC) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+__device__ inline int key_of_reg(int r, int h) {
+    return 16 * (r >> 3) + 8 * h + (r & 7);
+}
+
+__device__ inline uint32_t sel4(u32x4 v, int i) {
+    uint32_t a = (i & 1) ? v[1] : v[0];
+    uint32_t b = (i & 1) ? v[3] : v[2];
+    return (i & 2) ? b : a;
+}
+
+struct Launch {
+    int Gc, R, nhc, n_rb;
+};
+
+template <int D, bool F32, bool HASPOS, bool COUNT>
+__global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
+    constexpr int NB = D / 16;
+    constexpr int P = D / 2;
+    constexpr int NDB = D / 32;
+    __shared__ __attribute__((aligned(16))) uint16_t sK[NB * BN * 16];
+    __shared__ __attribute__((aligned(16))) uint16_t sV[D * VSTR];
+    __shared__ int32_t sPos[BN];
+
+    const int tid = threadIdx.x;
+    const int T = blockDim.x;
+    const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
+    const int G = p.Hq / p.Hkv;
+    const int U = p.B * p.Hkv * L.nhc;
+    const int u = blockIdx.x % U;
+    const int rb = L.n_rb - 1 - (int)(blockIdx.x / U);     // longest rows first
+    const int hc = u % L.nhc;
+    const int g = (u / L.nhc) % p.Hkv;
+    const int b = u / (L.nhc * p.Hkv);
+    const int hin = hc * L.Gc + (w % L.Gc);
+    const int rg = w / L.Gc;
+    const bool head_ok = hin < G;
+    const int hq = g * G + (head_ok ? hin : 0);
+    const int64_t N = p.N;
+    const int64_t qs = (int64_t)rb * 32 * L.R;
+    const int64_t q0 = qs + 32 * rg;
+    const bool wave_ok = head_ok && q0 < N;
+    const int64_t qrow = q0 + l32;
+    const bool row_ok = qrow < N;
+    const int64_t qrow_c = row_ok ? qrow : N - 1;
+    const int32_t* posb = p.pos + (HASPOS ? (int64_t)b * N : 0);
+    auto POS = [&](int64_t t) -> int64_t { return HASPOS ? (int64_t)posb[t] : t; };
+    const int64_t pq = POS(qrow_c);
+
+    // ---- Q: load, round to bf16, rotate at its own position, round to bf16 (B operand)
+    u32x4 Qf[NB];
+    {
+        const int64_t qb = (((int64_t)b * N + qrow_c) * p.Hq + hq) * D;
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            // pairs 8j..8j+7, one at a time (rolled loop: one sincos instance per block);
+            // each bf16 result enters at the top of the 128-bit block value, which shifts
+            // down by 16 bits, so after 8 steps pair 8j+e sits in element e.
+            u32x4 acc = {0u, 0u, 0u, 0u};
+#pragma unroll 1
+            for (int e = 0; e < 8; ++e) {
+                float x, y;
+                if constexpr (F32) {
+                    x = round_bf16(static_cast<const float*>(p.q)[qb + 8 * j + e]);
+                    y = round_bf16(static_cast<const float*>(p.q)[qb + P + 8 * j + e]);
+                } else {
+                    x = bf16_bits_to_f32(static_cast<const uint16_t*>(p.q)[qb + 8 * j + e]);
+                    y = bf16_bits_to_f32(static_cast<const uint16_t*>(p.q)[qb + P + 8 * j + e]);
+                }
+                float sn, cs;
+                rope_sincos(pq, tab.theta[8 * j + e], &sn, &cs);
+                const uint32_t bits = f32_to_bf16_bits(h ? (y * cs + x * sn) : (x * cs - y * sn));
+                acc[0] = (acc[0] >> 16) | (acc[1] << 16);
+                acc[1] = (acc[1] >> 16) | (acc[2] << 16);
+                acc[2] = (acc[2] >> 16) | (acc[3] << 16);
+                acc[3] = (acc[3] >> 16) | (bits << 16);
+            }
+            Qf[j] = acc;
+        }
+    }
+
+    const uint16_t* kpg = p.kp + ((int64_t)b * p.Hkv + g) * NB * p.Np * 16;
+    const uint16_t* vtg = p.vt + ((int64_t)b * p.Hkv + g) * D * p.Np;
+    const int64_t row_end = (qs + 32 * L.R < N ? qs + 32 * L.R : N) - 1;
+    const int kt_last = (int)(row_end / BN);
+    const int64_t pq_wg = POS(qs < N ? qs : N - 1);
+    const int64_t pq_lo = POS(q0 < N ? q0 : N - 1);
+    const int64_t pq_hi = POS(q0 + 31 < N ? q0 + 31 : N - 1);
+    const float sl2 = p.scale * 1.4426950408889634f;
+
+    f32x16 O[NDB];
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) O[i] = f32x16{};
+    float m = -INFINITY, lsum = 0.f;
+    uint64_t cnt = 0;
+
+    for (int kt = kt_last; kt >= 0; --kt) {
+        const int64_t ks = (int64_t)kt * BN;
+        const int64_t kend = (ks + BN < N ? ks + BN : N) - 1;
+        const int64_t dmin_wg = pq_wg - POS(kend) > 0 ? pq_wg - POS(kend) : 0;
+        const int jlo = first_at_least(tab.W, P, dmin_wg) >> 3;
+
+        __syncthreads();
+        {
+            const int nK = (NB - jlo) * (BN * 2);
+            for (int c = tid; c < nK; c += T) {
+                const int jj = jlo + c / (BN * 2), off = c % (BN * 2);
+                const u32x4 val = *reinterpret_cast<const u32x4*>(
+                    kpg + ((int64_t)jj * p.Np + ks) * 16 + off * 8);
+                *reinterpret_cast<u32x4*>(&sK[jj * BN * 16 + off * 8]) = val;
+            }
+            for (int c = tid; c < D * (BN / 8); c += T) {
+                const int e = c / (BN / 8), part = c % (BN / 8);
+                const u32x4 val =
+                    *reinterpret_cast<const u32x4*>(vtg + (int64_t)e * p.Np + ks + part * 8);
+                *reinterpret_cast<u32x4*>(&sV[e * VSTR + part * 8]) = val;
+            }
+            if (HASPOS)
+                for (int c = tid; c < BN; c += T) sPos[c] = posb[ks + c < N ? ks + c : N - 1];
+        }
+        __syncthreads();
+        if (!wave_ok) continue;
+
+#pragma unroll 1
+        for (int sub = 0; sub < 2; ++sub) {
+            const int64_t k0 = ks + 32 * sub;
+            if (k0 > q0 + 31 || k0 >= N) continue;     // whole sub-tile above the diagonal
+            const int64_t k_last = k0 + 31 < N ? k0 + 31 : N - 1;
+            const int64_t dmin = pq_lo - POS(k_last) > 0 ? pq_lo - POS(k_last) : 0;
+            const int64_t dmax = pq_hi - POS(k0);
+            const int plo = first_at_least(tab.W, P, dmin);
+            const int pfull = first_at_least(tab.W, P, dmax);
+            const int jf = pfull >> 3;
+            f32x16 S = f32x16{};
+
+            // fully active blocks on MFMA
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                if (j < jf) continue;
+                u32x4 qv = Qf[j];
+                if (j == jf) {
+                    const int nz = pfull - 8 * j;      // leading pairs of the block to drop
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const uint32_t lo = (2 * t >= nz) ? 0xffffu : 0u;
+                        const uint32_t hi = (2 * t + 1 >= nz) ? 0xffff0000u : 0u;
+                        qv[t] &= (lo | hi);
+                    }
+                }
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                    &sK[(j * BN + 32 * sub + perm_row(l32)) * 16 + 8 * h]);
+                S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, qv), S,
+                                                            0, 0, 0);
+            }
+
+            if (COUNT && row_ok) {
+                int nv = 0;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) nv += (k0 + key_of_reg(r, h) <= qrow);
+                cnt += (uint64_t)nv * (uint64_t)(P - pfull);
+            }
+
+            // straddling pairs on VALU, per element
+            if (plo < pfull) {
+#pragma unroll
+                for (int j = 0; j < NB; ++j) {
+                    const int e_lo = plo - 8 * j > 0 ? plo - 8 * j : 0;
+                    const int e_hi = pfull - 8 * j < 8 ? pfull - 8 * j : 8;
+                    if (e_lo >= e_hi) continue;
+                    const u32x4 mine = Qf[j];
+                    u32x4 oth;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) oth[t] = (uint32_t)__shfl_xor((int)mine[t], 32);
+                    const u32x4 qx = h ? oth : mine;
+                    const u32x4 qy = h ? mine : oth;
+                    for (int e = e_lo; e < e_hi; ++e) {
+                        const int sh = (e & 1) * 16;
+                        const float fqx = bf16_bits_to_f32((sel4(qx, e >> 1) >> sh) & 0xffffu);
+                        const float fqy = bf16_bits_to_f32((sel4(qy, e >> 1) >> sh) & 0xffffu);
+                        const int64_t Wi = tab.W[8 * j + e];
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int kl = 32 * sub + key_of_reg(r, h);
+                            const int64_t dist = pq - (HASPOS ? (int64_t)sPos[kl] : ks + kl);
+                            const uint16_t* kr = &sK[(j * BN + kl) * 16];
+                            const float kx = bf16_bits_to_f32(kr[e]);
+                            const float ky = bf16_bits_to_f32(kr[8 + e]);
+                            const bool on = dist <= Wi;
+                            S[r] += on ? (fqx * kx + fqy * ky) : 0.f;
+                            if (COUNT) cnt += (on && row_ok && ks + kl <= qrow) ? 1 : 0;
+                        }
+                    }
+                }
+            }
+
+            // scale into log2 units, causal mask, sub-tile max
+            const bool diag = k0 + 31 > q0;
+            float mx = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float t = S[r] * sl2;
+                if (diag && k0 + key_of_reg(r, h) > qrow) t = -INFINITY;
+                S[r] = t;
+                mx = fmaxf(mx, t);
+            }
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float m_new = fmaxf(m, mx);
+            if (__any(m_new > m + kTau)) {
+                const float alpha = exp2f(m - m_new);
+                lsum *= alpha;
+#pragma unroll
+                for (int i = 0; i < NDB; ++i) O[i] *= alpha;
+                m = m_new;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) S[r] = exp2f(S[r] - m);
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const u32x4 pb = u32x4{pack_bf16x2(S[8 * c + 0], S[8 * c + 1]),
+                                       pack_bf16x2(S[8 * c + 2], S[8 * c + 3]),
+                                       pack_bf16x2(S[8 * c + 4], S[8 * c + 5]),
+                                       pack_bf16x2(S[8 * c + 6], S[8 * c + 7])};
+                // the row sum takes the same bf16-rounded weights the P*V product uses, so
+                // out = sum(w v) / sum(w) is an exact weighted mean of the rounded weights
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    lsum += __builtin_bit_cast(float, pb[t] << 16) +
+                            __builtin_bit_cast(float, pb[t] & 0xffff0000u);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                        &sV[(32 * db + l32) * VSTR + 32 * sub + 16 * c + 8 * h]);
+                    O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        a, __builtin_bit_cast(bf16x8, pb), O[db], 0, 0, 0);
+                }
+            }
+        }
+    }
+
+    if (COUNT) {
+        uint64_t tot = cnt;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) tot += __shfl_xor(tot, o);
+        if (lane == 0 && wave_ok && tot) atomicAdd(p.counter, (unsigned long long)tot);
+    }
+    if (!wave_ok) return;
+    const float l_tot = lsum + __shfl_xor(lsum, 32);
+    if (!row_ok) return;
+    const float inv = 1.0f / l_tot;
+    const int64_t ob = (((int64_t)b * N + qrow) * p.Hq + hq) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp) {
+            const int dim = 32 * db + 8 * grp + 4 * h;
+            const float o0 = O[db][4 * grp + 0] * inv, o1 = O[db][4 * grp + 1] * inv;
+            const float o2 = O[db][4 * grp + 2] * inv, o3 = O[db][4 * grp + 3] * inv;
+            if (p.out_f32) {
+                *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + ob + dim) =
+                    f32x4{o0, o1, o2, o3};
+            } else {
+                uint32_t* dst = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p.out) + ob + dim);
+                dst[0] = pack_bf16x2(o0, o1);
+                dst[1] = pack_bf16x2(o2, o3);
+            }
+        }
+    }
+    if (p.lse && h == 0)
+        p.lse[((int64_t)b * p.Hq + hq) * N + qrow] = (m + log2f(l_tot)) * 0.6931471805599453f;
+}
+
+template <int D, bool F32>
+hipError_t launch_d(const PrefillParams& p, const Tables& t, hipStream_t s) {
+    const int G = p.Hq / p.Hkv;
+    Launch L;
+    L.Gc = G < 8 ? G : 8;
+    L.nhc = (G + L.Gc - 1) / L.Gc;
+    L.R = 8 / L.Gc > 1 ? 8 / L.Gc : 1;
+    L.n_rb = (int)((p.N + 32 * L.R - 1) / (32 * L.R));
+    const int waves = L.Gc * L.R;
+    const int64_t nblk = (int64_t)L.n_rb * p.B * p.Hkv * L.nhc;
+    dim3 grid((unsigned)nblk), block(64 * waves);
+    const bool hp = p.pos != nullptr, cn = p.counter != nullptr;
+    if (hp && cn) prefill_kernel<D, F32, true, true><<<grid, block, 0, s>>>(p, t, L);
+    else if (hp) prefill_kernel<D, F32, true, false><<<grid, block, 0, s>>>(p, t, L);
+    else if (cn) prefill_kernel<D, F32, false, true><<<grid, block, 0, s>>>(p, t, L);
+    else prefill_kernel<D, F32, false, false><<<grid, block, 0, s>>>(p, t, L);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillParams& p, const Tables& t, hipStream_t s) {
+    if (p.d == 64) return p.in_f32 ? launch_d<64, true>(p, t, s) : launch_d<64, false>(p, t, s);
+    return p.in_f32 ? launch_d<128, true>(p, t, s) : launch_d<128, false>(p, t, s);
+}
+
+}  // namespace wpa

@@ -1,0 +1,147 @@
+// Key rotation and K/V relayout.
+//
+// Keys are rotated once, at their own position (ATFlash abstract: the RoPE score is a
+// sum over 2-D rotation pairs), and stored pair-blocked: block j of a head holds pairs
+// 8j..8j+7, as the 8 first-half components followed by the 8 second-half components,
+// [B][Hkv][d/16][tokens][16] in bf16.  One 16-element block is one bf16 MFMA K-step, so
+// "contract only the active blocks" (pairs form a contiguous slice of the contraction
+// axis at every distance) reads contiguous memory for every token range.
+//
+// Values: for prefill they are transposed to [B][Hkv][d][tokens] so the P*V product can
+// read key-contiguous MFMA operands; for the decode cache they keep [B][Hkv][tokens][d].
+#include "wpa_device.hpp"
+#include "wpa_internal.hpp"
+
+namespace wpa {
+
+template <bool F32>
+__global__ __launch_bounds__(256) void rope_keys_kernel(RopeParams p, Tables tab) {
+    const int NB = p.d / 16;
+    const int P = p.d / 2;
+    const int64_t ntok = p.pad_to > p.n ? p.pad_to : p.n;
+    const int64_t total = (int64_t)p.B * p.Hkv * NB * ntok;
+    int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (id >= total) return;
+    const int64_t t = id % ntok;
+    int64_t rest = id / ntok;
+    const int j = (int)(rest % NB);
+    rest /= NB;
+    const int g = (int)(rest % p.Hkv);
+    const int b = (int)(rest / p.Hkv);
+
+    uint16_t* dst = p.kp + ((((int64_t)b * p.Hkv + g) * NB + j) * p.ld + p.t0 + t) * 16;
+    u32x4* d4 = reinterpret_cast<u32x4*>(dst);
+    if (t >= p.n) {
+        u32x4 z = {0u, 0u, 0u, 0u};
+        d4[0] = z;
+        d4[1] = z;
+        return;
+    }
+    const int64_t row = (((int64_t)b * p.n + t) * p.Hkv + g) * p.d;
+    float x[8], y[8];
+    load8<F32>(p.k, row + 8 * j, x);
+    load8<F32>(p.k, row + P + 8 * j, y);
+    const int64_t pos = p.pos ? (int64_t)p.pos[(int64_t)b * p.n + t] : p.t0 + t;
+    uint32_t ox[4], oy[4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+        float s0, c0, s1, c1;
+        rope_sincos(pos, tab.theta[8 * j + e], &s0, &c0);
+        rope_sincos(pos, tab.theta[8 * j + e + 1], &s1, &c1);
+        float x0 = round_bf16(x[e]), y0 = round_bf16(y[e]);
+        float x1 = round_bf16(x[e + 1]), y1 = round_bf16(y[e + 1]);
+        ox[e / 2] = pack_bf16x2(x0 * c0 - y0 * s0, x1 * c1 - y1 * s1);
+        oy[e / 2] = pack_bf16x2(y0 * c0 + x0 * s0, y1 * c1 + x1 * s1);
+    }
+    d4[0] = u32x4{ox[0], ox[1], ox[2], ox[3]};
+    d4[1] = u32x4{oy[0], oy[1], oy[2], oy[3]};
+}
+
+// V transpose for prefill: one block = 64 tokens x d dims of one (b, kv head).
+template <bool F32, int D>
+__global__ __launch_bounds__(256) void v_transpose_kernel(RopeParams p) {
+    __shared__ uint16_t tile[64][D + 2];
+    const int64_t ntok = p.pad_to > p.n ? p.pad_to : p.n;
+    const int64_t ntiles = (ntok + 63) / 64;
+    const int64_t tile_id = blockIdx.x % ntiles;
+    const int bg = blockIdx.x / ntiles;
+    const int g = bg % p.Hkv, b = bg / p.Hkv;
+    const int64_t t0 = tile_id * 64;
+    // load: each thread 8 elements of one token row
+    for (int c = threadIdx.x; c < 64 * (D / 8); c += blockDim.x) {
+        const int tt = c / (D / 8), e8 = (c % (D / 8)) * 8;
+        const int64_t t = t0 + tt;
+        float x[8];
+        if (t < p.n) {
+            load8<F32>(p.v, (((int64_t)b * p.n + t) * p.Hkv + g) * D + e8, x);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) tile[tt][e8 + i] = f32_to_bf16_bits(x[i]);
+    }
+    __syncthreads();
+    // store: each thread 8 consecutive tokens of one dim
+    for (int c = threadIdx.x; c < D * 8; c += blockDim.x) {
+        const int e = c / 8, t8 = (c % 8) * 8;
+        const int64_t t = t0 + t8;
+        if (t >= ntok) continue;
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            w[i] = (uint32_t)tile[t8 + 2 * i][e] | ((uint32_t)tile[t8 + 2 * i + 1][e] << 16);
+        uint16_t* dst = p.vout + (((int64_t)b * p.Hkv + g) * D + e) * p.ld + p.t0 + t;
+        *reinterpret_cast<u32x4*>(dst) = u32x4{w[0], w[1], w[2], w[3]};
+    }
+}
+
+// V copy into the decode cache [B][Hkv][Lmax][d] (bf16).
+template <bool F32>
+__global__ __launch_bounds__(256) void v_copy_kernel(RopeParams p) {
+    const int per_row = p.d / 8;
+    const int64_t total = (int64_t)p.B * p.n * p.Hkv * per_row;
+    int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (id >= total) return;
+    const int e8 = (int)(id % per_row) * 8;
+    int64_t rest = id / per_row;
+    const int g = (int)(rest % p.Hkv);
+    rest /= p.Hkv;
+    const int64_t t = rest % p.n;
+    const int b = (int)(rest / p.n);
+    float x[8];
+    load8<F32>(p.v, (((int64_t)b * p.n + t) * p.Hkv + g) * p.d + e8, x);
+    uint16_t* dst = p.vout + (((int64_t)b * p.Hkv + g) * p.ld + p.t0 + t) * p.d + e8;
+    *reinterpret_cast<u32x4*>(dst) = u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                                           pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
+}
+
+hipError_t launch_rope_relayout(const RopeParams& p, hipStream_t s) {
+    const int NB = p.d / 16;
+    const int64_t ntok = p.pad_to > p.n ? p.pad_to : p.n;
+    const int64_t nk = (int64_t)p.B * p.Hkv * NB * ntok;
+    dim3 blk(256);
+    if (p.in_f32)
+        rope_keys_kernel<true><<<dim3((unsigned)((nk + 255) / 256)), blk, 0, s>>>(p, *p.tab);
+    else
+        rope_keys_kernel<false><<<dim3((unsigned)((nk + 255) / 256)), blk, 0, s>>>(p, *p.tab);
+    if (p.v_transposed) {
+        const int64_t nt = (ntok + 63) / 64;
+        dim3 grid((unsigned)(nt * p.B * p.Hkv));
+        if (p.d == 64) {
+            if (p.in_f32) v_transpose_kernel<true, 64><<<grid, blk, 0, s>>>(p);
+            else v_transpose_kernel<false, 64><<<grid, blk, 0, s>>>(p);
+        } else {
+            if (p.in_f32) v_transpose_kernel<true, 128><<<grid, blk, 0, s>>>(p);
+            else v_transpose_kernel<false, 128><<<grid, blk, 0, s>>>(p);
+        }
+    } else {
+        const int64_t nv = (int64_t)p.B * p.n * p.Hkv * (p.d / 8);
+        dim3 grid((unsigned)((nv + 255) / 256));
+        if (p.in_f32) v_copy_kernel<true><<<grid, blk, 0, s>>>(p);
+        else v_copy_kernel<false><<<grid, blk, 0, s>>>(p);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace wpa

@@ -1,0 +1,286 @@
+// C ABI of libwpa (declared in include/wpa.h): argument checks, the window and rotation
+// tables, the closed-form kept-term count, workspace sizing and kernel launches.
+#include "wpa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "wpa_internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = 0;
+    return WPA_OK;
+}
+
+// alpha*lambda_i, lambda_i = 2*pi*base^(2i/d): one full rotation period of pair i
+// (WavePrune original abstract: each channel keeps its first rotation period at alpha=1;
+// ATFlash abstract: the distance window is proportional to the wavelength).
+double window_value(int d, double base, double alpha, int i) {
+    const double lam = (2.0 * M_PI) * std::pow(base, (2.0 * i) / (double)d);
+    return alpha * lam;
+}
+
+// Integer form used by the kernels: distance D (an integer) is inside iff D <= floor(t).
+int32_t window_int(double t) {
+    if (!(t < (double)INT32_MAX)) return INT32_MAX;
+    return (int32_t)std::floor(t);
+}
+
+int check_common(int32_t d, double base, double alpha) {
+    if (d != 64 && d != 128) return fail(WPA_ERR_UNSUPPORTED, "head dim d=%d unsupported (64 or 128)", d);
+    if (!(base > 1.0) || !std::isfinite(base)) return fail(WPA_ERR_INVALID, "rope base must be finite and > 1");
+    if (!(alpha >= 0.0)) return fail(WPA_ERR_INVALID, "alpha must be >= 0 (got %g)", alpha);
+    return WPA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+void make_tables(int32_t d, double base, double alpha, wpa::Tables* t) {
+    std::memset(t, 0, sizeof *t);
+    for (int i = 0; i < d / 2; ++i) {
+        t->W[i] = window_int(window_value(d, base, alpha, i));
+        t->theta[i] = std::pow(base, -(2.0 * i) / (double)d);
+    }
+}
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+int default_chunk(int32_t B, int64_t Lmax, int32_t Hkv) {
+    // aim for ~4096 work items (>= 16 per CU) and at least 256 keys per item
+    const int64_t keys = (int64_t)B * Hkv * Lmax;
+    int64_t c = 256;
+    while (c < 8192 && keys / c > 4096) c <<= 1;
+    return (int)c;
+}
+
+// sum over integer r in [a, b] of max(0, hi(r) - lo(r) + 1) for the visible-window count,
+// evaluated piecewise (each piece linear in r).  Used by the closed form below.
+__int128 sum_linear(int64_t a, int64_t b, int64_t c0, int64_t c1) {
+    // sum_{r=a}^{b} (c1*r + c0); requires a <= b
+    const __int128 n = (__int128)b - a + 1;
+    const __int128 sr = ((__int128)a + b) * n / 2;
+    return (__int128)c1 * sr + (__int128)c0 * n;
+}
+
+// kept terms of one pair with integer threshold Wi (>= 0, possibly huge): queries r in
+// [q0, q0+nq), keys c in [0, nk), visible iff c <= r, kept iff r - c <= Wi.
+// For query r the kept keys are c in [max(0, r - Wi), min(r, nk - 1)].
+__int128 pair_kept(int64_t q0, int64_t nq, int64_t nk, int64_t Wi) {
+    const int64_t r_lo = q0, r_hi = q0 + nq - 1;
+    // breakpoints: r = Wi (lower end leaves 0), r = nk - 1 (upper end saturates)
+    int64_t cuts[4] = {r_lo, r_hi + 1, 0, 0};
+    int nc = 2;
+    if (Wi + 1 > r_lo && Wi + 1 <= r_hi) cuts[nc++] = Wi + 1;
+    if (nk > r_lo && nk <= r_hi) cuts[nc++] = nk;
+    for (int i = 0; i < nc; ++i)
+        for (int j = i + 1; j < nc; ++j)
+            if (cuts[j] < cuts[i]) { int64_t t = cuts[i]; cuts[i] = cuts[j]; cuts[j] = t; }
+    __int128 total = 0;
+    for (int s = 0; s + 1 < nc; ++s) {
+        const int64_t a = cuts[s], b = cuts[s + 1] - 1;
+        if (a > b) continue;
+        // on [a, b] both ends are linear: lo = (a > Wi ? r - Wi : 0), hi = (a >= nk ? nk-1 : r)
+        const bool lo_shift = a > Wi;
+        const bool hi_sat = a >= nk;
+        // count(r) = hi - lo + 1 ; may be <= 0 only if hi_sat && lo_shift and r - Wi > nk - 1
+        if (hi_sat && lo_shift) {
+            // count = nk - 1 - (r - Wi) + 1 = (nk + Wi) - r, positive while r < nk + Wi
+            const int64_t b2 = (b < nk + Wi - 1) ? b : nk + Wi - 1;
+            if (a <= b2) total += sum_linear(a, b2, nk + Wi, -1);
+        } else if (hi_sat) {
+            total += (__int128)nk * ((__int128)b - a + 1);          // keys 0..nk-1
+        } else if (lo_shift) {
+            total += (__int128)(Wi + 1) * ((__int128)b - a + 1);    // keys r-Wi..r
+        } else {
+            total += sum_linear(a, b, 1, 1);                         // keys 0..r
+        }
+    }
+    return total;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* wpa_last_error(void) { return g_err; }
+
+int wpa_thresholds(int32_t d, double base, double alpha, int32_t* W) {
+    if (d < 2 || d > 128 || (d & 1)) return fail(WPA_ERR_INVALID, "d must be even and in [2, 128]");
+    if (!(base > 1.0) || !std::isfinite(base)) return fail(WPA_ERR_INVALID, "rope base must be finite and > 1");
+    if (!(alpha >= 0.0)) return fail(WPA_ERR_INVALID, "alpha must be >= 0");
+    if (!W) return fail(WPA_ERR_INVALID, "W is null");
+    for (int i = 0; i < d / 2; ++i) W[i] = window_int(window_value(d, base, alpha, i));
+    return ok();
+}
+
+int wpa_count_terms(int32_t d, double base, double alpha, int64_t n_q, int64_t q_pos0,
+                    int64_t n_k, int64_t* kept, int64_t* total) {
+    if (d < 2 || (d & 1)) return fail(WPA_ERR_INVALID, "d must be even and >= 2");
+    if (!(base > 1.0) || !std::isfinite(base)) return fail(WPA_ERR_INVALID, "rope base must be finite and > 1");
+    if (!(alpha >= 0.0)) return fail(WPA_ERR_INVALID, "alpha must be >= 0");
+    if (n_q < 0 || n_k < 0 || q_pos0 < 0) return fail(WPA_ERR_INVALID, "negative count or position");
+    if (!kept || !total) return fail(WPA_ERR_INVALID, "null output pointer");
+    __int128 k = 0, vis = 0;
+    if (n_q > 0 && n_k > 0) {
+        vis = pair_kept(q_pos0, n_q, n_k, INT64_MAX / 4);
+        for (int i = 0; i < d / 2; ++i) {
+            const double t = window_value(d, base, alpha, i);
+            const int64_t Wi = (t < 9.0e18) ? (int64_t)std::floor(t) : INT64_MAX / 4;
+            k += pair_kept(q_pos0, n_q, n_k, Wi);
+        }
+    }
+    const __int128 tot = vis * (d / 2);
+    if (tot > (__int128)INT64_MAX) return fail(WPA_ERR_INVALID, "count overflows int64");
+    *kept = (int64_t)k;
+    *total = (int64_t)tot;
+    return ok();
+}
+
+size_t wpa_prefill_workspace_bytes(int32_t B, int64_t N, int32_t Hkv, int32_t d) {
+    if (B < 1 || N < 1 || Hkv < 1 || d < 1) return 0;
+    return (size_t)2 * B * Hkv * round_up(N, wpa::kTileKeys) * d * 2;
+}
+
+int wpa_prefill(const void* q, const void* k, const void* v, void* out, float* lse,
+                const int32_t* positions, int32_t B, int64_t N, int32_t Hq, int32_t Hkv,
+                int32_t d, double base, double alpha, float scale, int32_t dtype,
+                int32_t out_dtype, unsigned long long* term_count, void* workspace,
+                size_t ws_bytes, void* stream) {
+    int rc = check_common(d, base, alpha);
+    if (rc) return rc;
+    if (B < 1 || N < 1 || Hq < 1 || Hkv < 1) return fail(WPA_ERR_INVALID, "B, N, Hq, Hkv must be >= 1");
+    if (Hq % Hkv) return fail(WPA_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+    if (N >= (int64_t)INT32_MAX - wpa::kTileKeys) return fail(WPA_ERR_INVALID, "N too large");
+    if (dtype != WPA_BF16 && dtype != WPA_FP32) return fail(WPA_ERR_INVALID, "dtype must be WPA_BF16 or WPA_FP32");
+    if (out_dtype != WPA_BF16 && out_dtype != WPA_FP32) return fail(WPA_ERR_INVALID, "out_dtype must be WPA_BF16 or WPA_FP32");
+    if (std::isnan(scale)) return fail(WPA_ERR_INVALID, "scale is NaN");
+    if (!q || !k || !v || !out || !workspace) return fail(WPA_ERR_INVALID, "null q, k, v, out or workspace");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(workspace))
+        return fail(WPA_ERR_INVALID, "q, k, v, out and workspace must be 16-byte aligned");
+    if ((lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) || (positions && (reinterpret_cast<uintptr_t>(positions) & 3u)))
+        return fail(WPA_ERR_INVALID, "lse and positions must be 4-byte aligned");
+    if (term_count && (reinterpret_cast<uintptr_t>(term_count) & 7u)) return fail(WPA_ERR_INVALID, "term_count must be 8-byte aligned");
+    const size_t need = wpa_prefill_workspace_bytes(B, N, Hkv, d);
+    if (ws_bytes < need) return fail(WPA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+
+    wpa::Tables tab;
+    make_tables(d, base, alpha, &tab);
+    const int64_t Np = round_up(N, wpa::kTileKeys);
+    uint16_t* kp = static_cast<uint16_t*>(workspace);
+    uint16_t* vt = kp + (size_t)B * Hkv * Np * d;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    wpa::RopeParams rp{};
+    rp.k = k; rp.v = v; rp.pos = positions; rp.kp = kp; rp.vout = vt;
+    rp.n = N; rp.t0 = 0; rp.ld = Np; rp.pad_to = Np;
+    rp.B = B; rp.Hkv = Hkv; rp.d = d; rp.in_f32 = dtype == WPA_FP32; rp.v_transposed = 1;
+    rp.tab = &tab;
+    hipError_t e = wpa::launch_rope_relayout(rp, s);
+    if (e != hipSuccess) return fail(WPA_ERR_HIP, "rope relayout launch: %s", hipGetErrorString(e));
+
+    wpa::PrefillParams pp{};
+    pp.q = q; pp.kp = kp; pp.vt = vt; pp.out = out; pp.lse = lse; pp.pos = positions;
+    pp.counter = term_count; pp.N = N; pp.Np = Np; pp.B = B; pp.Hq = Hq; pp.Hkv = Hkv; pp.d = d;
+    pp.in_f32 = dtype == WPA_FP32;
+    pp.out_f32 = out_dtype == WPA_FP32;
+    pp.scale = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)d));
+    e = wpa::launch_prefill(pp, tab, s);
+    if (e != hipSuccess) return fail(WPA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+size_t wpa_kcache_bytes(int32_t B, int64_t Lmax, int32_t Hkv, int32_t d) {
+    if (B < 1 || Lmax < 1 || Hkv < 1 || d < 1) return 0;
+    return (size_t)B * Hkv * Lmax * d * 2;
+}
+
+size_t wpa_vcache_bytes(int32_t B, int64_t Lmax, int32_t Hkv, int32_t d) {
+    return wpa_kcache_bytes(B, Lmax, Hkv, d);
+}
+
+int wpa_kv_write(const void* k, const void* v, int64_t start, int64_t n, void* k_cache,
+                 void* v_cache, int32_t B, int64_t Lmax, int32_t Hkv, int32_t d, double base,
+                 int32_t dtype, void* stream) {
+    int rc = check_common(d, base, 1.0);
+    if (rc) return rc;
+    if (B < 1 || Hkv < 1 || Lmax < 1 || n < 1 || start < 0 || start + n > Lmax)
+        return fail(WPA_ERR_INVALID, "need B, Hkv, n >= 1 and 0 <= start, start + n <= Lmax");
+    if (Lmax >= (int64_t)INT32_MAX) return fail(WPA_ERR_INVALID, "Lmax too large");
+    if (dtype != WPA_BF16 && dtype != WPA_FP32) return fail(WPA_ERR_INVALID, "dtype must be WPA_BF16 or WPA_FP32");
+    if (!k || !v || !k_cache || !v_cache) return fail(WPA_ERR_INVALID, "null pointer");
+    if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
+        return fail(WPA_ERR_INVALID, "pointers must be 16-byte aligned");
+    wpa::Tables tab;
+    make_tables(d, base, 1.0, &tab);
+    wpa::RopeParams rp{};
+    rp.k = k; rp.v = v; rp.pos = nullptr;
+    rp.kp = static_cast<uint16_t*>(k_cache); rp.vout = static_cast<uint16_t*>(v_cache);
+    rp.n = n; rp.t0 = start; rp.ld = Lmax; rp.pad_to = 0;
+    rp.B = B; rp.Hkv = Hkv; rp.d = d; rp.in_f32 = dtype == WPA_FP32; rp.v_transposed = 0;
+    rp.tab = &tab;
+    hipError_t e = wpa::launch_rope_relayout(rp, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(WPA_ERR_HIP, "kv write launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+size_t wpa_decode_workspace_bytes(int32_t B, int64_t Lmax, int32_t Hq, int32_t Hkv, int32_t d,
+                                  int32_t chunk_keys) {
+    if (B < 1 || Lmax < 1 || Hq < 1 || Hkv < 1 || d < 1 || Hq % Hkv) return 0;
+    const int ch = chunk_keys > 0 ? chunk_keys : default_chunk(B, Lmax, Hkv);
+    const int64_t nc = (Lmax + ch - 1) / ch;
+    return (size_t)B * Hkv * nc * (Hq / Hkv) * (d + 2) * sizeof(float);
+}
+
+int wpa_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* kv_len,
+               const int32_t* q_pos, void* out, float* lse, int32_t B, int64_t Lmax,
+               int32_t Hq, int32_t Hkv, int32_t d, double base, double alpha, float scale,
+               int32_t dtype, int32_t out_dtype, unsigned long long* term_count,
+               int32_t chunk_keys, void* workspace, size_t ws_bytes, void* stream) {
+    int rc = check_common(d, base, alpha);
+    if (rc) return rc;
+    if (B < 1 || Lmax < 1 || Hq < 1 || Hkv < 1) return fail(WPA_ERR_INVALID, "B, Lmax, Hq, Hkv must be >= 1");
+    if (Hq % Hkv) return fail(WPA_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+    if (Hq / Hkv > 16) return fail(WPA_ERR_UNSUPPORTED, "decode supports up to 16 q heads per kv head");
+    if (Lmax >= (int64_t)INT32_MAX) return fail(WPA_ERR_INVALID, "Lmax too large");
+    if (dtype != WPA_BF16 && dtype != WPA_FP32) return fail(WPA_ERR_INVALID, "dtype must be WPA_BF16 or WPA_FP32");
+    if (out_dtype != WPA_BF16 && out_dtype != WPA_FP32) return fail(WPA_ERR_INVALID, "out_dtype must be WPA_BF16 or WPA_FP32");
+    if (std::isnan(scale)) return fail(WPA_ERR_INVALID, "scale is NaN");
+    if (chunk_keys < 0 || (chunk_keys % 256)) return fail(WPA_ERR_INVALID, "chunk_keys must be 0 or a positive multiple of 256");
+    if (!q || !k_cache || !v_cache || !kv_len || !out || !workspace) return fail(WPA_ERR_INVALID, "null pointer");
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) || !aligned16(workspace))
+        return fail(WPA_ERR_INVALID, "q, caches, out and workspace must be 16-byte aligned");
+    if (term_count && (reinterpret_cast<uintptr_t>(term_count) & 7u)) return fail(WPA_ERR_INVALID, "term_count must be 8-byte aligned");
+    const int ch = chunk_keys > 0 ? chunk_keys : default_chunk(B, Lmax, Hkv);
+    const size_t need = wpa_decode_workspace_bytes(B, Lmax, Hq, Hkv, d, ch);
+    if (ws_bytes < need) return fail(WPA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    wpa::Tables tab;
+    make_tables(d, base, alpha, &tab);
+    wpa::DecodeParams dp{};
+    dp.q = q; dp.kp = static_cast<const uint16_t*>(k_cache); dp.v = static_cast<const uint16_t*>(v_cache);
+    dp.kv_len = kv_len; dp.q_pos = q_pos; dp.out = out; dp.lse = lse; dp.counter = term_count;
+    dp.partial = static_cast<float*>(workspace); dp.Lmax = Lmax; dp.B = B; dp.Hq = Hq; dp.Hkv = Hkv;
+    dp.d = d; dp.in_f32 = dtype == WPA_FP32; dp.out_f32 = out_dtype == WPA_FP32; dp.chunk = ch; dp.n_chunks = (int)((Lmax + ch - 1) / ch);
+    dp.scale = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)d));
+    hipError_t e = wpa::launch_decode(dp, tab, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(WPA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,66 @@
+// Internal launch interface between the C-ABI layer (wpa_api.cpp) and the HIP kernels.
+// Host-visible plain structs only; no HIP types beyond hipStream_t.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wpa {
+
+constexpr int kMaxPairs = 64;     // d <= 128
+constexpr int kTileKeys = 64;     // prefill key tile and the token padding of the workspace
+
+// Window and rotation tables, computed once on the host in double.
+struct Tables {
+    int32_t W[kMaxPairs];         // floor(alpha*lambda_i), INT32_MAX when unbounded
+    double theta[kMaxPairs];      // base^(-2i/d)
+};
+
+// Rotate keys into the pair-blocked layout [B][Hkv][d/16][ld][16] (bf16) and, for
+// prefill, write V transposed to [B][Hkv][d][ld]; for the decode cache, V is copied to
+// [B][Hkv][ld][d].  Tokens t0 .. t0+n-1 of the destination receive source rows 0 .. n-1;
+// tokens n .. pad_to-1 (prefill only) are zero-filled.
+struct RopeParams {
+    const void* k;                // [B][n][Hkv][d]
+    const void* v;                // [B][n][Hkv][d]
+    const int32_t* pos;           // [B][n] or null (positions t0 + row)
+    uint16_t* kp;                 // pair-blocked rotated keys
+    uint16_t* vout;               // transposed (prefill) or row-major (cache) values
+    int64_t n, t0, ld, pad_to;
+    int32_t B, Hkv, d, in_f32, v_transposed;
+    const Tables* tab;            // host pointer; copied into kernel arguments
+};
+
+struct PrefillParams {
+    const void* q;                // [B][N][Hq][d]
+    const uint16_t* kp;           // [B][Hkv][d/16][Np][16]
+    const uint16_t* vt;           // [B][Hkv][d][Np]
+    void* out;                    // [B][N][Hq][d]
+    float* lse;                   // [B][Hq][N] or null
+    const int32_t* pos;           // [B][N] or null
+    unsigned long long* counter;  // or null
+    int64_t N, Np;
+    int32_t B, Hq, Hkv, d, in_f32, out_f32;
+    float scale;
+};
+
+struct DecodeParams {
+    const void* q;                // [B][Hq][d]
+    const uint16_t* kp;           // [B][Hkv][d/16][Lmax][16]
+    const uint16_t* v;            // [B][Hkv][Lmax][d]
+    const int32_t* kv_len;        // [B]
+    const int32_t* q_pos;         // [B] or null
+    void* out;                    // [B][Hq][d]
+    float* lse;                   // [B][Hq] or null
+    unsigned long long* counter;
+    float* partial;               // [B][Hkv][n_chunks][G][d+2]
+    int64_t Lmax;
+    int32_t B, Hq, Hkv, d, in_f32, out_f32, chunk, n_chunks;
+    float scale;
+};
+
+hipError_t launch_rope_relayout(const RopeParams& p, hipStream_t s);
+hipError_t launch_prefill(const PrefillParams& p, const Tables& t, hipStream_t s);
+hipError_t launch_decode(const DecodeParams& p, const Tables& t, hipStream_t s);
+
+}  // namespace wpa

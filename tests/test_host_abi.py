@@ -1,0 +1,160 @@
+"""Host-side checks of libwpa that need no GPU: exported symbols, the closed-form kept-term
+count against the oracle's enumerations, the window table, and argument validation (every
+rejected call returns before any HIP call)."""
+import ctypes
+import json
+import math
+import os
+import re
+
+import pytest
+
+import oracle
+import rope_wavelength_sparsity_amd as wpa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    text = open(os.path.join(ROOT, "include", "wpa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(wpa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = wpa.lib()
+    declared = _declared_symbols()
+    assert declared, "no declarations parsed"
+    assert set(declared) == set(wpa.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+GRID = [(d, base, alpha) for d in (2, 8, 64, 128) for base in (10.0, 1e4, 5e5, 1e7)
+        for alpha in (0.0, 0.3, 1.0, 2.0, 8.0, math.inf)]
+
+
+@pytest.mark.parametrize("d,base,alpha", GRID)
+def test_closed_form_count_matches_enumeration(d, base, alpha):
+    for (n_q, q0, n_k) in [(1, 0, 1), (5, 0, 5), (64, 0, 64), (300, 0, 300), (1, 299, 300),
+                           (1, 0, 300), (37, 250, 260), (10, 400, 300), (50, 3, 20)]:
+        got = wpa.count_terms(d, base, alpha, n_q, q0, n_k)
+        assert got == oracle.count_enumerate(d, base, alpha, n_q, q0, n_k), (n_q, q0, n_k)
+
+
+def test_closed_form_count_matches_golden_large():
+    """Workload-sized counts written by tests/golden/make_counts.py (oracle only)."""
+    data = json.load(open(os.path.join(ROOT, "tests", "golden", "counts.json")))
+    for c in data["cases"]:
+        alpha = math.inf if c["alpha"] == "inf" else c["alpha"]
+        got = wpa.count_terms(c["d"], c["base"], alpha, c["n_q"], c["q0"], c["n_k"])
+        assert got == (c["kept"], c["total"]), c["name"]
+
+
+@pytest.mark.parametrize("N", [1000, 4097, 65536, 1 << 20])
+def test_closed_form_count_matches_distance_histogram(N):
+    for d, base in ((64, 1e6), (128, 5e5), (128, 1e7)):
+        for alpha in (1.0, 2.0, 0.25):
+            assert wpa.count_terms(d, base, alpha, N, 0, N) == \
+                oracle.count_by_distance(d, base, alpha, N, 0, N)
+    assert wpa.count_terms(128, 5e5, 1.0, 1, N - 1, N) == \
+        oracle.count_by_distance(128, 5e5, 1.0, 1, N - 1, N)
+
+
+@pytest.mark.parametrize("d,base,alpha", [(64, 1e4, 1.0), (128, 5e5, 2.0), (128, 1e7, 0.5),
+                                          (64, 1e6, math.inf), (16, 10.0, 1e12)])
+def test_window_table_is_floor_of_oracle_threshold(d, base, alpha):
+    W = wpa.thresholds(d, base, alpha)
+    thr = oracle.thresholds(d, base, alpha)
+    for w, t in zip(W, thr):
+        if t >= 2 ** 31 - 1:
+            assert w == 2 ** 31 - 1
+        else:
+            assert w == math.floor(t)
+    assert all(a <= b for a, b in zip(W, W[1:]))       # non-decreasing: a suffix is active
+
+
+FAKE = ctypes.c_void_p(1 << 20)        # aligned, never dereferenced: validation fails first
+
+
+def _prefill_rc(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, pos=None, B=1, N=128, Hq=4, Hkv=2, d=64,
+             base=1e4, alpha=1.0, scale=0.0, dtype=0, odt=0, cnt=None, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    L = wpa.lib()
+    return L.wpa_prefill(a["q"], a["k"], a["v"], a["out"], a["lse"], a["pos"], a["B"], a["N"],
+                         a["Hq"], a["Hkv"], a["d"], a["base"], a["alpha"], a["scale"], a["dtype"],
+                         a["odt"], a["cnt"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=96), wpa.WPA_ERR_UNSUPPORTED),
+    (dict(d=32), wpa.WPA_ERR_UNSUPPORTED),
+    (dict(Hq=3, Hkv=2), wpa.WPA_ERR_INVALID),
+    (dict(alpha=float("nan")), wpa.WPA_ERR_INVALID),
+    (dict(alpha=-1.0), wpa.WPA_ERR_INVALID),
+    (dict(base=1.0), wpa.WPA_ERR_INVALID),
+    (dict(base=float("inf")), wpa.WPA_ERR_INVALID),
+    (dict(N=0), wpa.WPA_ERR_INVALID),
+    (dict(B=0), wpa.WPA_ERR_INVALID),
+    (dict(dtype=7), wpa.WPA_ERR_INVALID),
+    (dict(odt=2), wpa.WPA_ERR_INVALID),
+    (dict(scale=float("nan")), wpa.WPA_ERR_INVALID),
+    (dict(q=None), wpa.WPA_ERR_INVALID),
+    (dict(ws=None), wpa.WPA_ERR_INVALID),
+    (dict(k=ctypes.c_void_p((1 << 20) + 8)), wpa.WPA_ERR_INVALID),
+    (dict(cnt=ctypes.c_void_p((1 << 20) + 4)), wpa.WPA_ERR_INVALID),
+    (dict(ws_bytes=100), wpa.WPA_ERR_WORKSPACE),
+])
+def test_prefill_rejects_bad_arguments(kw, code):
+    assert _prefill_rc(**kw) == code
+    assert wpa.lib().wpa_last_error().decode() != ""
+
+
+def _decode_rc(**kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, lens=FAKE, qpos=None, out=FAKE, lse=None, B=2, Lmax=4096,
+             Hq=8, Hkv=2, d=128, base=5e5, alpha=1.0, scale=0.0, dtype=0, odt=1, cnt=None,
+             chunk=0, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    return wpa.lib().wpa_decode(a["q"], a["kc"], a["vc"], a["lens"], a["qpos"], a["out"],
+                                a["lse"], a["B"], a["Lmax"], a["Hq"], a["Hkv"], a["d"], a["base"],
+                                a["alpha"], a["scale"], a["dtype"], a["odt"], a["cnt"], a["chunk"],
+                                a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=80), wpa.WPA_ERR_UNSUPPORTED),
+    (dict(Hq=34, Hkv=2), wpa.WPA_ERR_UNSUPPORTED),
+    (dict(Hq=6, Hkv=4), wpa.WPA_ERR_INVALID),
+    (dict(chunk=100), wpa.WPA_ERR_INVALID),
+    (dict(odt=-1), wpa.WPA_ERR_INVALID),
+    (dict(chunk=-256), wpa.WPA_ERR_INVALID),
+    (dict(lens=None), wpa.WPA_ERR_INVALID),
+    (dict(alpha=float("nan")), wpa.WPA_ERR_INVALID),
+    (dict(ws_bytes=64), wpa.WPA_ERR_WORKSPACE),
+])
+def test_decode_rejects_bad_arguments(kw, code):
+    assert _decode_rc(**kw) == code
+
+
+def test_kv_write_rejects_out_of_range():
+    L = wpa.lib()
+    rc = L.wpa_kv_write(FAKE, FAKE, 4000, 200, FAKE, FAKE, 1, 4096, 2, 64, 1e4, 0, None)
+    assert rc == wpa.WPA_ERR_INVALID
+    rc = L.wpa_kv_write(FAKE, FAKE, -1, 1, FAKE, FAKE, 1, 4096, 2, 64, 1e4, 0, None)
+    assert rc == wpa.WPA_ERR_INVALID
+
+
+def test_workspace_sizes():
+    assert wpa.prefill_workspace_bytes(1, 100, 2, 64) == 2 * 1 * 2 * 128 * 64 * 2
+    assert wpa.kcache_bytes(2, 1000, 4, 128) == 2 * 4 * 1000 * 128 * 2
+    ws = wpa.decode_workspace_bytes(16, 131072, 24, 8, 128, 4096)
+    assert ws == 16 * 8 * 32 * 3 * 130 * 4
+
+
+def test_count_rejects_bad_arguments():
+    kept, total = ctypes.c_int64(), ctypes.c_int64()
+    L = wpa.lib()
+    assert L.wpa_count_terms(3, 1e4, 1.0, 1, 0, 1, ctypes.byref(kept), ctypes.byref(total)) == -1
+    assert L.wpa_count_terms(64, 0.5, 1.0, 1, 0, 1, ctypes.byref(kept), ctypes.byref(total)) == -1
+    assert L.wpa_count_terms(64, 1e4, -1.0, 1, 0, 1, ctypes.byref(kept), ctypes.byref(total)) == -1
