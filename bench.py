@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Benchmark of per-RoPE-wavelength windowed attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Headline (`value`): windowed causal prefill of the Qwen2.5-0.5B-shaped layer (B=1, 14 q /
+2 kv heads, d=64, base 1e6, N=32768, alpha=1, bf16 synthetic inputs).  One step = the
+whole prefill path: key rotation/relayout + the attention kernel.  `value` is the
+algorithmic (active-term) TFLOP/s of that step, inputs resident in HBM:
+    flops = B*Hq*(4*kept + 2*d*N(N+1)/2)
+where kept (per head) is the exact kept-term count and P*V stays full.
+
+Also reported on the same line:
+  roofline       the attention kernel alone (HIP events around its launch) vs bf16 MFMA peak
+  decode         one decode step of the Llama-3.2-3B-shaped batch (B=16, 24/8 heads, d=128,
+                 kv_len ~ U{8192..131072}), algorithmic KV bytes per second vs HBM peak
+  speedup_vs_full_window   the same kernels with alpha = inf, prefill and decode
+  cpu_baseline   the fp64 CPU oracle on a bounded sample of query rows of the same prefill
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("prefill active-term TFLOP/s + decode KV GB/s vs roofline; "
+          "speedup over α=∞")
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+
+
+def _parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen05b", help="prefill workload (synth.WORKLOADS)")
+    ap.add_argument("--alpha", type=float, default=None, help="override the workload's alpha")
+    ap.add_argument("--decode-workload", default="llama3b_decode")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-full-window", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def _events(n):
+    import torch
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def bench_prefill(w, alpha, steps, warmup):
+    """Times `steps` prefill steps (prepare + attend).  Returns dict of timings."""
+    import torch
+    import rope_wavelength_sparsity_amd as wpa
+    import synth
+    q, k, v = synth.workload_inputs(w, device="cuda")
+    ws = torch.empty(wpa.prefill_workspace_bytes(w.B, w.N, w.Hkv, w.d), device="cuda",
+                     dtype=torch.uint8)
+    out = torch.empty_like(q)
+    ka, kb = _events(steps), _events(steps)
+
+    def step(i=None):
+        wpa.prefill_prepare(k, v, w.base, workspace=ws)
+        if i is not None:
+            ka[i].record()
+        wpa.prefill_attend(q, ws, w.Hkv, w.base, alpha, out=out)
+        if i is not None:
+            kb[i].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0, t1 = _events(2)
+    w0 = time.perf_counter()
+    t0.record()
+    for i in range(steps):
+        step(i)
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    step_ms = t0.elapsed_time(t1) / steps
+    kern_ms = sum(a.elapsed_time(b) for a, b in zip(ka, kb)) / steps
+    kept, _ = wpa.count_terms(w.d, w.base, alpha, w.N, 0, w.N)
+    flops = w.B * w.Hq * (4 * kept + 2 * w.d * w.N * (w.N + 1) // 2)
+    del q, k, v, ws, out
+    torch.cuda.empty_cache()
+    return {"step_ms": step_ms, "kernel_ms": kern_ms, "wall_s": wall, "flops": flops,
+            "kept_per_head": kept}
+
+
+def bench_decode(w, alpha, steps, warmup):
+    import torch
+    import rope_wavelength_sparsity_amd as wpa
+    import synth
+    q, k, v, lens = synth.workload_inputs(w, device="cuda")
+    cache = wpa.KVCache(w.B, w.N, w.Hkv, w.d, w.base)
+    cache.write(k, v, 0)
+    del k, v
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    ws = torch.empty(max(wpa.decode_workspace_bytes(w.B, w.N, w.Hq, w.Hkv, w.d), 16),
+                     device="cuda", dtype=torch.uint8)
+    out = torch.empty_like(q)
+    for _ in range(warmup):
+        wpa.decode(q, cache, lens, alpha, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    t0, t1 = _events(2)
+    t0.record()
+    for _ in range(steps):
+        wpa.decode(q, cache, lens, alpha, out=out, workspace=ws)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    lens_h = [int(x) for x in lens.cpu().tolist()]
+    nbytes = 0
+    for L in lens_h:
+        kept, _ = wpa.count_terms(w.d, w.base, alpha, 1, L - 1, L)
+        nbytes += w.Hkv * (4 * kept + 2 * w.d * L)
+    nbytes += 2 * 2 * w.B * w.Hq * w.d                 # q in, out
+    del q, cache, ws, out
+    torch.cuda.empty_cache()
+    return {"ms": ms, "bytes": nbytes, "kv_len_mean": sum(lens_h) / len(lens_h)}
+
+
+def cpu_baseline(w, alpha, target_s):
+    """The fp64 oracle on sampled query rows of the same prefill (all heads)."""
+    import numpy as np
+    import oracle
+    import rope_wavelength_sparsity_amd as wpa
+    import synth
+    q, k, v = synth.workload_inputs(w, device="cpu")
+    qa, ka, va = synth.to_oracle(q), synth.to_oracle(k), synth.to_oracle(v)
+
+    def run(rows):
+        t = time.perf_counter()
+        oracle.prefill(qa, ka, va, w.base, alpha, rows=rows)
+        return time.perf_counter() - t
+
+    rng = np.random.default_rng(12345)
+    cal = np.sort(rng.integers(0, w.N, 8))
+    tc = run(cal)
+    n = int(max(8, min(4096, 8 * target_s / max(tc, 1e-3))))
+    rows = np.sort(rng.integers(0, w.N, n))
+    dt = run(rows)
+    flops = 0
+    for r in rows.tolist():
+        kept, _ = wpa.count_terms(w.d, w.base, alpha, 1, r, r + 1)
+        flops += w.B * w.Hq * (4 * kept + 2 * w.d * (r + 1))
+    cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": "%d random query rows x %d heads of %s (N=%d), fp64, %.1f s" % (
+                n, w.Hq, w.name, w.N, dt)}
+
+
+def _traffic(kernel_file, workload, alpha):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if the kernel source is
+    unchanged since they were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    src = os.path.join(ROOT, "rope_wavelength_sparsity_amd", "csrc", kernel_file)
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    for e in json.load(open(path)).get("entries", []):
+        if e.get("source_sha256") == sha and e.get("workload") == workload and e.get("alpha") == alpha:
+            return e["hbm_bytes_per_launch"]
+    return None
+
+
+def main():
+    args = _parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print("bench.py runs on one GPU only: the windowed attention kernels here are single-GPU; "
+              "the multi-GPU sharding is a design note, not an implemented path. Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synth
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = synth.WORKLOADS[args.workload]
+    assert w.kind == "prefill"
+    alpha = args.alpha if args.alpha is not None else w.alphas[0]
+    print("# prefill %s alpha=%g" % (w.name, alpha), file=sys.stderr, flush=True)
+    pre = bench_prefill(w, alpha, args.steps, args.warmup)
+    res = {
+        "metric": METRIC,
+        "value": pre["flops"] / (pre["step_ms"] * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": pre["step_ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) tensors at the layer's shapes; no weights or datasets)",
+        "config": {"workload": "%s prefill: B=%d N=%d Hq=%d Hkv=%d d=%d base=%g alpha=%g" % (
+            w.name, w.B, w.N, w.Hq, w.Hkv, w.d, w.base, alpha),
+            "step": "prefill_prepare (key rotation + relayout) + prefill_attend",
+            "algorithmic_flops_per_step": pre["flops"],
+            "kept_terms_per_head": pre["kept_per_head"]},
+    }
+    achieved = pre["flops"] / (pre["kernel_ms"] * 1e-3) / 1e12
+    res["roofline"] = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                       "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                       "traffic": _traffic("prefill_kernel.hip", w.name, alpha),
+                       "kernel": "prefill_kernel (attend)", "kernel_ms": pre["kernel_ms"]}
+    print("# prefill %.3f ms/step, attend %.3f ms, %.1f TFLOP/s" % (
+        pre["step_ms"], pre["kernel_ms"], achieved), file=sys.stderr, flush=True)
+    speed = {}
+    if not args.no_full_window and not math.isinf(alpha):
+        print("# prefill full window", file=sys.stderr, flush=True)
+        full = bench_prefill(w, math.inf, args.steps, args.warmup)
+        speed["prefill_attend"] = full["kernel_ms"] / pre["kernel_ms"]
+        speed["prefill_step"] = full["step_ms"] / pre["step_ms"]
+        speed["prefill_full_window_kernel_ms"] = full["kernel_ms"]
+        speed["prefill_full_window_tflops_dense"] = full["flops"] / (full["kernel_ms"] * 1e-3) / 1e12
+    if not args.no_decode:
+        wd = synth.WORKLOADS[args.decode_workload]
+        print("# decode %s" % wd.name, file=sys.stderr, flush=True)
+        dec = bench_decode(wd, 1.0, args.steps, args.warmup)
+        gbs = dec["bytes"] / (dec["ms"] * 1e-3) / 1e9
+        res["decode"] = {"workload": "%s: B=%d Lmax=%d Hq=%d Hkv=%d d=%d base=%g alpha=1, "
+                                     "kv_len ~ U{%d..%d} (mean %.0f)" % (
+                                         wd.name, wd.B, wd.N, wd.Hq, wd.Hkv, wd.d, wd.base,
+                                         wd.len_lo, wd.N, dec["kv_len_mean"]),
+                         "value": gbs, "unit": "GB/s", "ms_per_step": dec["ms"],
+                         "algorithmic_bytes": dec["bytes"],
+                         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
+                                      "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                                      "kernel": "decode_partial + decode_combine"}}
+        print("# decode %.3f ms, %.0f GB/s" % (dec["ms"], gbs), file=sys.stderr, flush=True)
+        if not args.no_full_window:
+            decf = bench_decode(wd, math.inf, args.steps, args.warmup)
+            speed["decode"] = decf["ms"] / dec["ms"]
+            speed["decode_full_window_ms"] = decf["ms"]
+    if speed:
+        res["speedup_vs_full_window"] = speed
+    if not args.no_cpu_baseline:
+        print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w, alpha, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -79,7 +79,7 @@ int wpa_count_terms(int32_t d, double base, double alpha, int64_t n_q, int64_t q
 int wpa_thresholds(int32_t d, double base, double alpha, int32_t* W);
 
 /* Workspace bytes wpa_prefill needs: the rotated, pair-blocked K and the transposed V
- * of all B*Hkv heads, padded to 64 tokens (2 * B*Hkv*roundup(N,64)*d*2 bytes). */
+ * of all B*Hkv heads, padded to 128 tokens (2 * B*Hkv*roundup(N,128)*d*2 bytes). */
 size_t wpa_prefill_workspace_bytes(int32_t B, int64_t N, int32_t Hkv, int32_t d);
 
 /*
@@ -100,6 +100,25 @@ int wpa_prefill(const void* q, const void* k, const void* v, void* out, float* l
                 int32_t d, double base, double alpha, float scale, int32_t dtype,
                 int32_t out_dtype, unsigned long long* term_count, void* workspace,
                 size_t ws_bytes, void* stream);
+
+/*
+ * The two halves of wpa_prefill, for callers that time them apart or reuse the prepared
+ * keys and values for several query launches.  wpa_prefill(...) is exactly
+ * wpa_prefill_prepare(...) followed by wpa_prefill_attend(...) on the same stream.
+ *   prepare: rotate k at its positions into the workspace (pair-blocked bf16) and store v
+ *            transposed there; q is not read.
+ *   attend:  the windowed attention of q against a workspace prepared for the same
+ *            B, N, Hkv, d, base, positions (the workspace is only read).
+ * Arguments have the meaning given for wpa_prefill.
+ */
+int wpa_prefill_prepare(const void* k, const void* v, const int32_t* positions, int32_t B,
+                        int64_t N, int32_t Hkv, int32_t d, double base, int32_t dtype,
+                        void* workspace, size_t ws_bytes, void* stream);
+int wpa_prefill_attend(const void* q, void* out, float* lse, const int32_t* positions,
+                       int32_t B, int64_t N, int32_t Hq, int32_t Hkv, int32_t d, double base,
+                       double alpha, float scale, int32_t dtype, int32_t out_dtype,
+                       unsigned long long* term_count, const void* workspace, size_t ws_bytes,
+                       void* stream);
 
 /* Bytes of the decode K cache (opaque: rotated keys, pair-blocked) and of the V cache
  * ([B][Hkv][Lmax][d] bf16) for B sequences of up to Lmax tokens. */

@@ -28,7 +28,7 @@ WPA_BF16, WPA_FP32 = 0, 1
 
 # every symbol include/wpa.h declares
 EXPORTS = ("wpa_count_terms", "wpa_thresholds", "wpa_prefill_workspace_bytes", "wpa_prefill",
-           "wpa_kcache_bytes", "wpa_vcache_bytes", "wpa_kv_write", "wpa_decode_workspace_bytes",
+           "wpa_prefill_prepare", "wpa_prefill_attend", "wpa_kcache_bytes", "wpa_vcache_bytes", "wpa_kv_write", "wpa_decode_workspace_bytes",
            "wpa_decode", "wpa_last_error")
 
 
@@ -61,6 +61,11 @@ def lib():
     L.wpa_prefill.argtypes = [P, P, P, P, P, P, I32, I64, I32, I32, I32, D, D, F, I32, I32, P, P, SZ,
                               P]
     L.wpa_prefill.restype = ctypes.c_int
+    L.wpa_prefill_prepare.argtypes = [P, P, P, I32, I64, I32, I32, D, I32, P, SZ, P]
+    L.wpa_prefill_prepare.restype = ctypes.c_int
+    L.wpa_prefill_attend.argtypes = [P, P, P, P, I32, I64, I32, I32, I32, D, D, F, I32, I32, P, P,
+                                     SZ, P]
+    L.wpa_prefill_attend.restype = ctypes.c_int
     L.wpa_kcache_bytes.argtypes = [I32, I64, I32, I32]
     L.wpa_kcache_bytes.restype = SZ
     L.wpa_vcache_bytes.argtypes = [I32, I64, I32, I32]
@@ -178,6 +183,48 @@ def prefill(q, k, v, base: float, alpha: float, *, scale: float | None = None, p
                              _dtype_code(out), _ptr(term_count), _ptr(workspace),
                              workspace.numel(),
                              _stream(stream)))
+    return (out, lse) if lse is not None else out
+
+
+def prefill_prepare(k, v, base: float, *, positions=None, workspace=None, stream=None):
+    """First half of prefill: rotate k, transpose v into a workspace (returned)."""
+    _dev(k, "k")
+    _dev(v, "v")
+    if k.dim() != 4 or k.shape != v.shape or k.dtype != v.dtype:
+        raise ValueError("k, v must be [B][N][Hkv][d] of one dtype")
+    B, N, Hkv, d = k.shape
+    if positions is not None:
+        _dev(positions, "positions")
+        if positions.dtype != torch.int32 or positions.numel() != B * N:
+            raise ValueError("positions must be int32 [B][N]")
+    need = prefill_workspace_bytes(B, N, Hkv, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), device=k.device, dtype=torch.uint8)
+    _check(lib().wpa_prefill_prepare(_ptr(k), _ptr(v), _ptr(positions), B, N, Hkv, d, float(base),
+                                     _dtype_code(k), _ptr(workspace), workspace.numel(),
+                                     _stream(stream)))
+    return workspace
+
+
+def prefill_attend(q, workspace, Hkv: int, base: float, alpha: float, *, scale=None,
+                   positions=None, out=None, out_dtype=None, lse=None, want_lse=False,
+                   term_count=None, stream=None):
+    """Second half of prefill: windowed attention of q against a prepared workspace."""
+    _dev(q, "q")
+    _dev(workspace, "workspace")
+    B, N, Hq, d = q.shape
+    if out is None:
+        out = torch.empty(q.shape, device=q.device, dtype=out_dtype or q.dtype)
+    _dev(out, "out")
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq, N), device=q.device, dtype=torch.float32)
+    if positions is not None:
+        _dev(positions, "positions")
+    _check(lib().wpa_prefill_attend(_ptr(q), _ptr(out), _ptr(lse), _ptr(positions), B, N, Hq, Hkv,
+                                    d, float(base), float(alpha),
+                                    float(scale) if scale is not None else 0.0, _dtype_code(q),
+                                    _dtype_code(out), _ptr(term_count), _ptr(workspace),
+                                    workspace.numel(), _stream(stream)))
     return (out, lse) if lse is not None else out
 
 

@@ -4,8 +4,9 @@
 // Work decomposition
 //   A workgroup owns one (sequence b, kv head g, chunk of Gc q heads of that kv head) and
 //   32*R consecutive query rows; wave w handles q head (w % Gc) and the 32 rows of row
-//   group (w / Gc).  All waves share each K/V tile staged in LDS (GQA reuse).
-//   Key tiles of 64 tokens are walked from the diagonal outward.
+//   group (w / Gc).  All waves share each K/V tile staged in LDS (GQA reuse).  Key tiles
+//   (BN keys) are walked from the diagonal outward through a two-stage LDS ring filled by
+//   direct global->LDS loads: tile t+1 streams in while tile t is computed.
 //
 // Per 32x32 (query x key) sub-tile
 //   Distance band: dmin/dmax over the sub-tile's visible elements.  With the window table
@@ -16,9 +17,11 @@
 //     * S^T = K'_blk * Q'_blk^T on v_mfma_f32_32x32x16_bf16 over those blocks only; the
 //       leading pairs of the first such block are zeroed in the Q operand;
 //     * straddling pairs are added per element on VALU with the exact test D <= W_i.
-//   Then causal mask, online softmax (fp32, exp2 domain; the running max is only moved
-//   when it grows by more than 2^8, which leaves the result exact) and O^T += V^T P^T on
-//   MFMA.
+//   Sub-tiles are visited in order of growing distance, so both band edges only move
+//   forward along the pair axis: they are tracked with running indices, not searched.
+//   Then causal mask, online softmax (fp32, exp2 domain with the scale folded into one
+//   FMA; the running max is only moved when it grows by more than 2^8, which leaves the
+//   result exact) and O^T += V^T P^T on MFMA.
 //
 // Register layouts (32x32x16 MFMA: A row m and B column n live in lane m%32 / n%32, the
 // 16-deep contraction is split 8+8 between lane halves; C element (row 8(r/4)+4(l/32)+r%4,
@@ -29,7 +32,8 @@
 //     register r of half h holds key 16(r/8) + 8h + (r%8).  Registers 8c..8c+7 are then
 //     exactly the 8 keys that half h must supply as the B operand of the P*V step over
 //     keys 16c..16c+15, and the P^T operand needs no data movement.
-//   V operand (A of the P*V step): V^T rows (dims) from LDS, key-contiguous.
+//   V operand (A of the P*V step): V^T rows (dims) from LDS, key-contiguous, 16-byte
+//     chunks XOR-swizzled by the row index against bank conflicts.
 //   O^T accumulator: lane = query row, so the softmax rescale is a per-lane scalar.
 #include "wpa_device.hpp"
 #include "wpa_internal.hpp"
@@ -38,9 +42,9 @@ namespace wpa {
 
 namespace {
 
-constexpr int BN = kTileKeys;     // keys per tile
-constexpr int VSTR = BN + 8;      // LDS row stride of V^T (elements), padded against bank conflicts
 constexpr float kTau = 8.0f;      // lazy-rescale threshold (log2 units)
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
 
 __device__ inline int perm_row(int m) {
     return (m & ~0xC) | ((m & 4) << 1) | ((m & 8) >> 1);
@@ -56,8 +60,31 @@ __device__ inline uint32_t sel4(u32x4 v, int i) {
     return (i & 2) ? b : a;
 }
 
+// value of lane l ^ 32
+__device__ inline uint32_t partner32(uint32_t v, int h) {
+    (void)h;
+    return (uint32_t)__shfl_xor((int)v, 32);
+}
+
+__device__ inline float max_with_partner(float v) { return fmaxf(v, __shfl_xor(v, 32)); }
+
+__device__ inline float sum_with_partner(float v) { return v + __shfl_xor(v, 32); }
+
+__device__ inline int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 struct Launch {
     int Gc, R, nhc, n_rb;
+};
+
+template <int D>
+struct Tile {
+    static constexpr int BN = D == 64 ? 128 : 64;   // keys per tile
+    static constexpr int NSUB = BN / 32;
+    static constexpr int KI = BN * 32 / 1024;       // wave loads per K block
+    static constexpr int VI = D * BN * 2 / 1024;    // wave loads for V^T
+    static constexpr int PI = BN * 4 / 256;         // wave loads for positions
+    static constexpr int CPR = BN / 8;              // 16-byte chunks per V^T row
+    static constexpr int RPI = 64 / CPR;            // V^T rows per wave load
 };
 
 template <int D, bool F32, bool HASPOS, bool COUNT>
@@ -65,12 +92,14 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p, Tables ta
     constexpr int NB = D / 16;
     constexpr int P = D / 2;
     constexpr int NDB = D / 32;
-    __shared__ __attribute__((aligned(16))) uint16_t sK[NB * BN * 16];
-    __shared__ __attribute__((aligned(16))) uint16_t sV[D * VSTR];
-    __shared__ int32_t sPos[BN];
+    constexpr int BN = Tile<D>::BN;
+    constexpr int NSUB = Tile<D>::NSUB;
+    __shared__ __attribute__((aligned(16))) uint16_t sK2[2][NB * BN * 16];
+    __shared__ __attribute__((aligned(16))) uint16_t sV2[2][D * BN];
+    __shared__ __attribute__((aligned(16))) int32_t sPos2[2][HASPOS ? BN : 1];
 
     const int tid = threadIdx.x;
-    const int T = blockDim.x;
+    const int nw = blockDim.x >> 6;
     const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
     const int G = p.Hq / p.Hkv;
     const int U = p.B * p.Hkv * L.nhc;
@@ -83,16 +112,16 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p, Tables ta
     const int rg = w / L.Gc;
     const bool head_ok = hin < G;
     const int hq = g * G + (head_ok ? hin : 0);
-    const int64_t N = p.N;
-    const int64_t qs = (int64_t)rb * 32 * L.R;
-    const int64_t q0 = qs + 32 * rg;
+    const int N = (int)p.N;
+    const int qs = rb * 32 * L.R;
+    const int q0 = qs + 32 * rg;
     const bool wave_ok = head_ok && q0 < N;
-    const int64_t qrow = q0 + l32;
+    const int qrow = q0 + l32;
     const bool row_ok = qrow < N;
-    const int64_t qrow_c = row_ok ? qrow : N - 1;
+    const int qrow_c = row_ok ? qrow : N - 1;
     const int32_t* posb = p.pos + (HASPOS ? (int64_t)b * N : 0);
-    auto POS = [&](int64_t t) -> int64_t { return HASPOS ? (int64_t)posb[t] : t; };
-    const int64_t pq = POS(qrow_c);
+    auto POS = [&](int t) -> int { return HASPOS ? posb[t] : t; };
+    const int pq = POS(qrow_c);
 
     // ---- Q: load, round to bf16, rotate at its own position, round to bf16 (B operand)
     u32x4 Qf[NB];
@@ -128,11 +157,11 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p, Tables ta
 
     const uint16_t* kpg = p.kp + ((int64_t)b * p.Hkv + g) * NB * p.Np * 16;
     const uint16_t* vtg = p.vt + ((int64_t)b * p.Hkv + g) * D * p.Np;
-    const int64_t row_end = (qs + 32 * L.R < N ? qs + 32 * L.R : N) - 1;
-    const int kt_last = (int)(row_end / BN);
-    const int64_t pq_wg = POS(qs < N ? qs : N - 1);
-    const int64_t pq_lo = POS(q0 < N ? q0 : N - 1);
-    const int64_t pq_hi = POS(q0 + 31 < N ? q0 + 31 : N - 1);
+    const int row_end = (qs + 32 * L.R < N ? qs + 32 * L.R : N) - 1;
+    const int kt_last = row_end / BN;
+    const int pq_wg = POS(qs < N ? qs : N - 1);
+    const int pq_lo = POS(q0 < N ? q0 : N - 1);
+    const int pq_hi = POS(q0 + 31 < N ? q0 + 31 : N - 1);
     const float sl2 = p.scale * 1.4426950408889634f;
 
     f32x16 O[NDB];
@@ -140,70 +169,109 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p, Tables ta
     for (int i = 0; i < NDB; ++i) O[i] = f32x16{};
     float m = -INFINITY, lsum = 0.f;
     uint64_t cnt = 0;
+    int plo = 0, pfull = 0, plo_wg = 0;     // running band edges (distances only grow)
+    int q_key = -1;                          // pfull for which qm holds the masked block
+    u32x4 qm = {0u, 0u, 0u, 0u};
 
-    for (int kt = kt_last; kt >= 0; --kt) {
-        const int64_t ks = (int64_t)kt * BN;
-        const int64_t kend = (ks + BN < N ? ks + BN : N) - 1;
-        const int64_t dmin_wg = pq_wg - POS(kend) > 0 ? pq_wg - POS(kend) : 0;
-        const int jlo = first_at_least(tab.W, P, dmin_wg) >> 3;
-
-        __syncthreads();
-        {
-            const int nK = (NB - jlo) * (BN * 2);
-            for (int c = tid; c < nK; c += T) {
-                const int jj = jlo + c / (BN * 2), off = c % (BN * 2);
-                const u32x4 val = *reinterpret_cast<const u32x4*>(
-                    kpg + ((int64_t)jj * p.Np + ks) * 16 + off * 8);
-                *reinterpret_cast<u32x4*>(&sK[jj * BN * 16 + off * 8]) = val;
+    // Stream key tile kt into `stage` with direct global->LDS loads (one wave instruction
+    // fills 1 KB of LDS: lane l's bytes land at base + size*l).  Only the pair blocks that
+    // can be active anywhere in the tile (from the workgroup's smallest distance) are read.
+    auto issue = [&](int kt, int stage) {
+        const int ks = kt * BN;
+        const int kend = (ks + BN < N ? ks + BN : N) - 1;
+        const int dmin_wg = pq_wg - POS(kend) > 0 ? pq_wg - POS(kend) : 0;
+        while (plo_wg < P && tab.W[plo_wg] < dmin_wg) ++plo_wg;
+        const int jlo = uniform(plo_wg) >> 3;
+        const int nK = Tile<D>::KI * (NB - jlo);
+        const int nI = nK + Tile<D>::VI + (HASPOS ? Tile<D>::PI : 0);
+        for (int i = w; i < nI; i += nw) {
+            if (i < nK) {
+                const int j = jlo + i / Tile<D>::KI, part = i % Tile<D>::KI;
+                const uint16_t* src = kpg + ((int64_t)j * p.Np + ks) * 16 + (part * 64 + lane) * 8;
+                __builtin_amdgcn_global_load_lds(src, (lds_ptr)&sK2[stage][j * BN * 16 + part * 512],
+                                                 16, 0, 0);
+            } else if (i < nK + Tile<D>::VI) {
+                // V^T rows e; the 16-byte chunk c of row e sits in slot c ^ (e & 7)
+                const int r = i - nK;
+                const int e = r * Tile<D>::RPI + lane / Tile<D>::CPR;
+                const int c = (lane % Tile<D>::CPR) ^ (e & 7);
+                const uint16_t* src = vtg + (int64_t)e * p.Np + ks + 8 * c;
+                __builtin_amdgcn_global_load_lds(src, (lds_ptr)&sV2[stage][r * Tile<D>::RPI * BN],
+                                                 16, 0, 0);
+            } else if (HASPOS) {
+                const int pi = i - nK - Tile<D>::VI;
+                const int t = ks + 64 * pi + lane;
+                const int32_t* src = posb + (t < N ? t : N - 1);
+                __builtin_amdgcn_global_load_lds(src, (lds_ptr)&sPos2[stage][64 * pi], 4, 0, 0);
             }
-            for (int c = tid; c < D * (BN / 8); c += T) {
-                const int e = c / (BN / 8), part = c % (BN / 8);
-                const u32x4 val =
-                    *reinterpret_cast<const u32x4*>(vtg + (int64_t)e * p.Np + ks + part * 8);
-                *reinterpret_cast<u32x4*>(&sV[e * VSTR + part * 8]) = val;
-            }
-            if (HASPOS)
-                for (int c = tid; c < BN; c += T) sPos[c] = posb[ks + c < N ? ks + c : N - 1];
         }
-        __syncthreads();
+    };
+
+    issue(kt_last, 0);
+    for (int kt = kt_last, it = 0; kt >= 0; --kt, ++it) {
+        const int ks = kt * BN;
+        const int stage = it & 1;
+        __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): this thread's loads landed
+        __syncthreads();                     // ... and everyone's; the other stage is free again
+        if (kt > 0) issue(kt - 1, stage ^ 1);
         if (!wave_ok) continue;
+        const uint16_t* sK = sK2[stage];
+        const uint16_t* sV = sV2[stage];
+        const int32_t* sPos = sPos2[stage];
 
 #pragma unroll 1
-        for (int sub = 0; sub < 2; ++sub) {
-            const int64_t k0 = ks + 32 * sub;
+        for (int sub = NSUB - 1; sub >= 0; --sub) {      // nearest keys first
+            const int k0 = ks + 32 * sub;
             if (k0 > q0 + 31 || k0 >= N) continue;     // whole sub-tile above the diagonal
-            const int64_t k_last = k0 + 31 < N ? k0 + 31 : N - 1;
-            const int64_t dmin = pq_lo - POS(k_last) > 0 ? pq_lo - POS(k_last) : 0;
-            const int64_t dmax = pq_hi - POS(k0);
-            const int plo = first_at_least(tab.W, P, dmin);
-            const int pfull = first_at_least(tab.W, P, dmax);
+            const int k_last = k0 + 31 < N ? k0 + 31 : N - 1;
+            const int dmin = pq_lo - POS(k_last) > 0 ? pq_lo - POS(k_last) : 0;
+            const int dmax = pq_hi - POS(k0);
+            while (plo < P && tab.W[plo] < dmin) ++plo;
+            while (pfull < P && tab.W[pfull] < dmax) ++pfull;
+            plo = uniform(plo);
+            pfull = uniform(pfull);
             const int jf = pfull >> 3;
+            if (pfull != q_key && pfull < P) {
+                // first fully-active block with its leading (not fully active) pairs zeroed
+                u32x4 src = Qf[0];
+#pragma unroll
+                for (int j = 1; j < NB; ++j)
+                    if (j == jf) src = Qf[j];
+                const int nz = pfull - 8 * jf;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const uint32_t lo = (2 * t >= nz) ? 0xffffu : 0u;
+                    const uint32_t hi = (2 * t + 1 >= nz) ? 0xffff0000u : 0u;
+                    qm[t] = src[t] & (lo | hi);
+                }
+                q_key = pfull;
+            }
             f32x16 S = f32x16{};
 
             // fully active blocks on MFMA
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
                 if (j < jf) continue;
-                u32x4 qv = Qf[j];
-                if (j == jf) {
-                    const int nz = pfull - 8 * j;      // leading pairs of the block to drop
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        const uint32_t lo = (2 * t >= nz) ? 0xffffu : 0u;
-                        const uint32_t hi = (2 * t + 1 >= nz) ? 0xffff0000u : 0u;
-                        qv[t] &= (lo | hi);
-                    }
-                }
                 const bf16x8 a = *reinterpret_cast<const bf16x8*>(
                     &sK[(j * BN + 32 * sub + perm_row(l32)) * 16 + 8 * h]);
-                S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, qv), S,
-                                                            0, 0, 0);
+                if (j == jf)
+                    S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, qm),
+                                                                S, 0, 0, 0);
+                else
+                    S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        a, __builtin_bit_cast(bf16x8, Qf[j]), S, 0, 0, 0);
             }
 
+            const bool diag = k0 + 31 > q0;
+            // register r of half h holds key k0 + 16(r/8) + (r%8) + 8h: causal iff that <= qrow
+            const int lim = qrow - k0 - 8 * h;
             if (COUNT && row_ok) {
-                int nv = 0;
+                int nv = 16;
+                if (diag) {
+                    nv = 0;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) nv += (k0 + key_of_reg(r, h) <= qrow);
+                    for (int r = 0; r < 16; ++r) nv += (16 * (r >> 3) + (r & 7) <= lim);
+                }
                 cnt += (uint64_t)nv * (uint64_t)(P - pfull);
             }
 
@@ -217,66 +285,64 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p, Tables ta
                     const u32x4 mine = Qf[j];
                     u32x4 oth;
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) oth[t] = (uint32_t)__shfl_xor((int)mine[t], 32);
+                    for (int t = 0; t < 4; ++t) oth[t] = partner32(mine[t], h);
                     const u32x4 qx = h ? oth : mine;
                     const u32x4 qy = h ? mine : oth;
                     for (int e = e_lo; e < e_hi; ++e) {
                         const int sh = (e & 1) * 16;
                         const float fqx = bf16_bits_to_f32((sel4(qx, e >> 1) >> sh) & 0xffffu);
                         const float fqy = bf16_bits_to_f32((sel4(qy, e >> 1) >> sh) & 0xffffu);
-                        const int64_t Wi = tab.W[8 * j + e];
+                        const int Wi = tab.W[8 * j + e];
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
                             const int kl = 32 * sub + key_of_reg(r, h);
-                            const int64_t dist = pq - (HASPOS ? (int64_t)sPos[kl] : ks + kl);
+                            const int dist = pq - (HASPOS ? sPos[kl] : ks + kl);
                             const uint16_t* kr = &sK[(j * BN + kl) * 16];
                             const float kx = bf16_bits_to_f32(kr[e]);
                             const float ky = bf16_bits_to_f32(kr[8 + e]);
                             const bool on = dist <= Wi;
                             S[r] += on ? (fqx * kx + fqy * ky) : 0.f;
-                            if (COUNT) cnt += (on && row_ok && ks + kl <= qrow) ? 1 : 0;
+                            if (COUNT)
+                                cnt += (on && row_ok && 16 * (r >> 3) + (r & 7) <= lim) ? 1 : 0;
                         }
                     }
                 }
             }
 
-            // scale into log2 units, causal mask, sub-tile max
-            const bool diag = k0 + 31 > q0;
-            float mx = -INFINITY;
+            // causal mask, sub-tile max (raw scores; the scale is folded into the exponent)
+            if (diag) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float t = S[r] * sl2;
-                if (diag && k0 + key_of_reg(r, h) > qrow) t = -INFINITY;
-                S[r] = t;
-                mx = fmaxf(mx, t);
+                for (int r = 0; r < 16; ++r)
+                    if (16 * (r >> 3) + (r & 7) > lim) S[r] = -INFINITY;
             }
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            float mx = S[0];
+#pragma unroll
+            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
+            mx = max_with_partner(mx) * sl2;
             const float m_new = fmaxf(m, mx);
             if (__any(m_new > m + kTau)) {
-                const float alpha = exp2f(m - m_new);
+                const float alpha = __builtin_amdgcn_exp2f(m - m_new);
                 lsum *= alpha;
 #pragma unroll
                 for (int i = 0; i < NDB; ++i) O[i] *= alpha;
                 m = m_new;
             }
 #pragma unroll
-            for (int r = 0; r < 16; ++r) S[r] = exp2f(S[r] - m);
+            for (int r = 0; r < 16; ++r) {
+                S[r] = __builtin_amdgcn_exp2f(fmaf(S[r], sl2, -m));
+                lsum += S[r];
+            }
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
                 const u32x4 pb = u32x4{pack_bf16x2(S[8 * c + 0], S[8 * c + 1]),
                                        pack_bf16x2(S[8 * c + 2], S[8 * c + 3]),
                                        pack_bf16x2(S[8 * c + 4], S[8 * c + 5]),
                                        pack_bf16x2(S[8 * c + 6], S[8 * c + 7])};
-                // the row sum takes the same bf16-rounded weights the P*V product uses, so
-                // out = sum(w v) / sum(w) is an exact weighted mean of the rounded weights
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    lsum += __builtin_bit_cast(float, pb[t] << 16) +
-                            __builtin_bit_cast(float, pb[t] & 0xffff0000u);
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
+                    const int e = 32 * db + l32, ch = 4 * sub + 2 * c + h;
                     const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                        &sV[(32 * db + l32) * VSTR + 32 * sub + 16 * c + 8 * h]);
+                        &sV[e * BN + ((ch ^ (e & 7)) << 3)]);
                     O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                         a, __builtin_bit_cast(bf16x8, pb), O[db], 0, 0, 0);
                 }
@@ -291,7 +357,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p, Tables ta
         if (lane == 0 && wave_ok && tot) atomicAdd(p.counter, (unsigned long long)tot);
     }
     if (!wave_ok) return;
-    const float l_tot = lsum + __shfl_xor(lsum, 32);
+    const float l_tot = sum_with_partner(lsum);
     if (!row_ok) return;
     const float inv = 1.0f / l_tot;
     const int64_t ob = (((int64_t)b * N + qrow) * p.Hq + hq) * D;
@@ -338,6 +404,7 @@ hipError_t launch_d(const PrefillParams& p, const Tables& t, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_prefill(const PrefillParams& p, const Tables& t, hipStream_t s) {
+    if (p.Np % Tile<64>::BN || p.Np % Tile<128>::BN) return hipErrorInvalidValue;
     if (p.d == 64) return p.in_f32 ? launch_d<64, true>(p, t, s) : launch_d<64, false>(p, t, s);
     return p.in_f32 ? launch_d<128, true>(p, t, s) : launch_d<128, false>(p, t, s);
 }

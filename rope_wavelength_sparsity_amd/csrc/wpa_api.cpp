@@ -158,52 +158,101 @@ size_t wpa_prefill_workspace_bytes(int32_t B, int64_t N, int32_t Hkv, int32_t d)
     return (size_t)2 * B * Hkv * round_up(N, wpa::kTileKeys) * d * 2;
 }
 
+namespace {
+
+int check_prefill_shape(int64_t N, int32_t B, int32_t Hkv, int32_t dtype, const int32_t* positions,
+                        const void* workspace, size_t ws_bytes, int32_t d) {
+    if (B < 1 || N < 1 || Hkv < 1) return fail(WPA_ERR_INVALID, "B, N, Hkv must be >= 1");
+    if (N >= (int64_t)INT32_MAX - wpa::kTileKeys) return fail(WPA_ERR_INVALID, "N too large");
+    if (dtype != WPA_BF16 && dtype != WPA_FP32) return fail(WPA_ERR_INVALID, "dtype must be WPA_BF16 or WPA_FP32");
+    if (!workspace) return fail(WPA_ERR_INVALID, "null workspace");
+    if (!aligned16(workspace)) return fail(WPA_ERR_INVALID, "workspace must be 16-byte aligned");
+    if (positions && (reinterpret_cast<uintptr_t>(positions) & 3u))
+        return fail(WPA_ERR_INVALID, "positions must be 4-byte aligned");
+    const size_t need = wpa_prefill_workspace_bytes(B, N, Hkv, d);
+    if (ws_bytes < need) return fail(WPA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    return WPA_OK;
+}
+
+}  // namespace
+
+int wpa_prefill_prepare(const void* k, const void* v, const int32_t* positions, int32_t B,
+                        int64_t N, int32_t Hkv, int32_t d, double base, int32_t dtype,
+                        void* workspace, size_t ws_bytes, void* stream) {
+    int rc = check_common(d, base, 1.0);
+    if (rc) return rc;
+    rc = check_prefill_shape(N, B, Hkv, dtype, positions, workspace, ws_bytes, d);
+    if (rc) return rc;
+    if (!k || !v) return fail(WPA_ERR_INVALID, "null k or v");
+    if (!aligned16(k) || !aligned16(v)) return fail(WPA_ERR_INVALID, "k and v must be 16-byte aligned");
+    wpa::Tables tab;
+    make_tables(d, base, 1.0, &tab);
+    const int64_t Np = round_up(N, wpa::kTileKeys);
+    uint16_t* kp = static_cast<uint16_t*>(workspace);
+    wpa::RopeParams rp{};
+    rp.k = k; rp.v = v; rp.pos = positions; rp.kp = kp; rp.vout = kp + (size_t)B * Hkv * Np * d;
+    rp.n = N; rp.t0 = 0; rp.ld = Np; rp.pad_to = Np;
+    rp.B = B; rp.Hkv = Hkv; rp.d = d; rp.in_f32 = dtype == WPA_FP32; rp.v_transposed = 1;
+    rp.tab = &tab;
+    hipError_t e = wpa::launch_rope_relayout(rp, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(WPA_ERR_HIP, "rope relayout launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int wpa_prefill_attend(const void* q, void* out, float* lse, const int32_t* positions,
+                       int32_t B, int64_t N, int32_t Hq, int32_t Hkv, int32_t d, double base,
+                       double alpha, float scale, int32_t dtype, int32_t out_dtype,
+                       unsigned long long* term_count, const void* workspace, size_t ws_bytes,
+                       void* stream) {
+    int rc = check_common(d, base, alpha);
+    if (rc) return rc;
+    rc = check_prefill_shape(N, B, Hkv, dtype, positions, workspace, ws_bytes, d);
+    if (rc) return rc;
+    if (Hq < 1) return fail(WPA_ERR_INVALID, "Hq must be >= 1");
+    if (Hq % Hkv) return fail(WPA_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+    if (out_dtype != WPA_BF16 && out_dtype != WPA_FP32) return fail(WPA_ERR_INVALID, "out_dtype must be WPA_BF16 or WPA_FP32");
+    if (std::isnan(scale)) return fail(WPA_ERR_INVALID, "scale is NaN");
+    if (!q || !out) return fail(WPA_ERR_INVALID, "null q or out");
+    if (!aligned16(q) || !aligned16(out)) return fail(WPA_ERR_INVALID, "q and out must be 16-byte aligned");
+    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(WPA_ERR_INVALID, "lse must be 4-byte aligned");
+    if (term_count && (reinterpret_cast<uintptr_t>(term_count) & 7u)) return fail(WPA_ERR_INVALID, "term_count must be 8-byte aligned");
+    wpa::Tables tab;
+    make_tables(d, base, alpha, &tab);
+    const int64_t Np = round_up(N, wpa::kTileKeys);
+    const uint16_t* kp = static_cast<const uint16_t*>(workspace);
+    wpa::PrefillParams pp{};
+    pp.q = q; pp.kp = kp; pp.vt = kp + (size_t)B * Hkv * Np * d; pp.out = out; pp.lse = lse;
+    pp.pos = positions; pp.counter = term_count; pp.N = N; pp.Np = Np; pp.B = B; pp.Hq = Hq;
+    pp.Hkv = Hkv; pp.d = d; pp.in_f32 = dtype == WPA_FP32; pp.out_f32 = out_dtype == WPA_FP32;
+    pp.scale = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)d));
+    hipError_t e = wpa::launch_prefill(pp, tab, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(WPA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
 int wpa_prefill(const void* q, const void* k, const void* v, void* out, float* lse,
                 const int32_t* positions, int32_t B, int64_t N, int32_t Hq, int32_t Hkv,
                 int32_t d, double base, double alpha, float scale, int32_t dtype,
                 int32_t out_dtype, unsigned long long* term_count, void* workspace,
                 size_t ws_bytes, void* stream) {
+    // check everything before enqueueing anything
     int rc = check_common(d, base, alpha);
     if (rc) return rc;
     if (B < 1 || N < 1 || Hq < 1 || Hkv < 1) return fail(WPA_ERR_INVALID, "B, N, Hq, Hkv must be >= 1");
     if (Hq % Hkv) return fail(WPA_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
-    if (N >= (int64_t)INT32_MAX - wpa::kTileKeys) return fail(WPA_ERR_INVALID, "N too large");
-    if (dtype != WPA_BF16 && dtype != WPA_FP32) return fail(WPA_ERR_INVALID, "dtype must be WPA_BF16 or WPA_FP32");
-    if (out_dtype != WPA_BF16 && out_dtype != WPA_FP32) return fail(WPA_ERR_INVALID, "out_dtype must be WPA_BF16 or WPA_FP32");
     if (std::isnan(scale)) return fail(WPA_ERR_INVALID, "scale is NaN");
-    if (!q || !k || !v || !out || !workspace) return fail(WPA_ERR_INVALID, "null q, k, v, out or workspace");
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(workspace))
-        return fail(WPA_ERR_INVALID, "q, k, v, out and workspace must be 16-byte aligned");
-    if ((lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) || (positions && (reinterpret_cast<uintptr_t>(positions) & 3u)))
-        return fail(WPA_ERR_INVALID, "lse and positions must be 4-byte aligned");
+    if (out_dtype != WPA_BF16 && out_dtype != WPA_FP32) return fail(WPA_ERR_INVALID, "out_dtype must be WPA_BF16 or WPA_FP32");
+    if (!q || !k || !v || !out) return fail(WPA_ERR_INVALID, "null q, k, v or out");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(WPA_ERR_INVALID, "q, k, v and out must be 16-byte aligned");
+    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(WPA_ERR_INVALID, "lse must be 4-byte aligned");
     if (term_count && (reinterpret_cast<uintptr_t>(term_count) & 7u)) return fail(WPA_ERR_INVALID, "term_count must be 8-byte aligned");
-    const size_t need = wpa_prefill_workspace_bytes(B, N, Hkv, d);
-    if (ws_bytes < need) return fail(WPA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
-
-    wpa::Tables tab;
-    make_tables(d, base, alpha, &tab);
-    const int64_t Np = round_up(N, wpa::kTileKeys);
-    uint16_t* kp = static_cast<uint16_t*>(workspace);
-    uint16_t* vt = kp + (size_t)B * Hkv * Np * d;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-
-    wpa::RopeParams rp{};
-    rp.k = k; rp.v = v; rp.pos = positions; rp.kp = kp; rp.vout = vt;
-    rp.n = N; rp.t0 = 0; rp.ld = Np; rp.pad_to = Np;
-    rp.B = B; rp.Hkv = Hkv; rp.d = d; rp.in_f32 = dtype == WPA_FP32; rp.v_transposed = 1;
-    rp.tab = &tab;
-    hipError_t e = wpa::launch_rope_relayout(rp, s);
-    if (e != hipSuccess) return fail(WPA_ERR_HIP, "rope relayout launch: %s", hipGetErrorString(e));
-
-    wpa::PrefillParams pp{};
-    pp.q = q; pp.kp = kp; pp.vt = vt; pp.out = out; pp.lse = lse; pp.pos = positions;
-    pp.counter = term_count; pp.N = N; pp.Np = Np; pp.B = B; pp.Hq = Hq; pp.Hkv = Hkv; pp.d = d;
-    pp.in_f32 = dtype == WPA_FP32;
-    pp.out_f32 = out_dtype == WPA_FP32;
-    pp.scale = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)d));
-    e = wpa::launch_prefill(pp, tab, s);
-    if (e != hipSuccess) return fail(WPA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
-    return ok();
+    rc = check_prefill_shape(N, B, Hkv, dtype, positions, workspace, ws_bytes, d);
+    if (rc) return rc;
+    rc = wpa_prefill_prepare(k, v, positions, B, N, Hkv, d, base, dtype, workspace, ws_bytes, stream);
+    if (rc) return rc;
+    return wpa_prefill_attend(q, out, lse, positions, B, N, Hq, Hkv, d, base, alpha, scale, dtype,
+                              out_dtype, term_count, workspace, ws_bytes, stream);
 }
 
 size_t wpa_kcache_bytes(int32_t B, int64_t Lmax, int32_t Hkv, int32_t d) {

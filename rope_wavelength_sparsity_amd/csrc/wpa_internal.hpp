@@ -8,7 +8,7 @@
 namespace wpa {
 
 constexpr int kMaxPairs = 64;     // d <= 128
-constexpr int kTileKeys = 64;     // prefill key tile and the token padding of the workspace
+constexpr int kTileKeys = 128;    // token padding of the prefill workspace (a multiple of every key tile)
 
 // Window and rotation tables, computed once on the host in double.
 struct Tables {
