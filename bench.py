@@ -49,6 +49,9 @@ def _parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="first run a plain device copy of this many MiB (twice), as the "
+                         "reference kernel for scaling FETCH_SIZE/WRITE_SIZE counters")
     return ap.parse_args()
 
 
@@ -186,6 +189,15 @@ def main():
     import torch
     import synth
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print("# copy calibration: %d bytes per copy" % n, file=sys.stderr, flush=True)
+        del src, dst
     w = synth.WORKLOADS[args.workload]
     assert w.kind == "prefill"
     alpha = args.alpha if args.alpha is not None else w.alphas[0]

@@ -60,15 +60,18 @@ __device__ inline uint32_t sel4(u32x4 v, int i) {
     return (i & 2) ? b : a;
 }
 
-// value of lane l ^ 32
-__device__ inline uint32_t partner32(uint32_t v, int h) {
-    (void)h;
-    return (uint32_t)__shfl_xor((int)v, 32);
+// Exchange with lane l ^ 32 through ds_bpermute; `xaddr` = 4 * (lane ^ 32), computed once.
+__device__ inline uint32_t partner32(uint32_t v, int xaddr) {
+    return (uint32_t)__builtin_amdgcn_ds_bpermute(xaddr, (int)v);
 }
 
-__device__ inline float max_with_partner(float v) { return fmaxf(v, __shfl_xor(v, 32)); }
+__device__ inline float max_with_partner(float v, int xaddr) {
+    return fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(xaddr, __builtin_bit_cast(int, v))));
+}
 
-__device__ inline float sum_with_partner(float v) { return v + __shfl_xor(v, 32); }
+__device__ inline float sum_with_partner(float v, int xaddr) {
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(xaddr, __builtin_bit_cast(int, v)));
+}
 
 __device__ inline int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
@@ -87,8 +90,14 @@ struct Tile {
     static constexpr int RPI = 64 / CPR;            // V^T rows per wave load
 };
 
+template <int D>
+struct Occupancy {
+    static constexpr int waves_per_eu = 2;
+};
+
 template <int D, bool F32, bool HASPOS, bool COUNT>
-__global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(Occupancy<D>::waves_per_eu)))
+void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
     constexpr int NB = D / 16;
     constexpr int P = D / 2;
     constexpr int NDB = D / 32;
@@ -101,6 +110,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p, Tables ta
     const int tid = threadIdx.x;
     const int nw = blockDim.x >> 6;
     const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
+    const int xaddr = (lane ^ 32) << 2;
     const int G = p.Hq / p.Hkv;
     const int U = p.B * p.Hkv * L.nhc;
     const int u = blockIdx.x % U;
@@ -248,18 +258,22 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p, Tables ta
             }
             f32x16 S = f32x16{};
 
-            // fully active blocks on MFMA
+            // fully active blocks on MFMA: the blocks above jf with the plain Q operand, then
+            // block jf with its leading pairs zeroed (one in-place accumulator chain)
 #pragma unroll
-            for (int j = 0; j < NB; ++j) {
-                if (j < jf) continue;
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                    &sK[(j * BN + 32 * sub + perm_row(l32)) * 16 + 8 * h]);
-                if (j == jf)
-                    S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, qm),
-                                                                S, 0, 0, 0);
-                else
+            for (int j = NB - 1; j > 0; --j) {
+                if (j > jf) {
+                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                        &sK[(j * BN + 32 * sub + perm_row(l32)) * 16 + 8 * h]);
                     S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                         a, __builtin_bit_cast(bf16x8, Qf[j]), S, 0, 0, 0);
+                }
+            }
+            if (jf < NB) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                    &sK[(jf * BN + 32 * sub + perm_row(l32)) * 16 + 8 * h]);
+                S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, qm), S,
+                                                            0, 0, 0);
             }
 
             const bool diag = k0 + 31 > q0;
@@ -285,7 +299,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p, Tables ta
                     const u32x4 mine = Qf[j];
                     u32x4 oth;
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) oth[t] = partner32(mine[t], h);
+                    for (int t = 0; t < 4; ++t) oth[t] = partner32(mine[t], xaddr);
                     const u32x4 qx = h ? oth : mine;
                     const u32x4 qy = h ? mine : oth;
                     for (int e = e_lo; e < e_hi; ++e) {
@@ -318,7 +332,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p, Tables ta
             float mx = S[0];
 #pragma unroll
             for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
-            mx = max_with_partner(mx) * sl2;
+            mx = max_with_partner(mx, xaddr) * sl2;
             const float m_new = fmaxf(m, mx);
             if (__any(m_new > m + kTau)) {
                 const float alpha = __builtin_amdgcn_exp2f(m - m_new);
@@ -357,7 +371,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p, Tables ta
         if (lane == 0 && wave_ok && tot) atomicAdd(p.counter, (unsigned long long)tot);
     }
     if (!wave_ok) return;
-    const float l_tot = sum_with_partner(lsum);
+    const float l_tot = sum_with_partner(lsum, xaddr);
     if (!row_ok) return;
     const float inv = 1.0f / l_tot;
     const int64_t ob = (((int64_t)b * N + qrow) * p.Hq + hq) * D;
