@@ -120,8 +120,10 @@ int wpa_prefill_attend(const void* q, void* out, float* lse, const int32_t* posi
                        unsigned long long* term_count, const void* workspace, size_t ws_bytes,
                        void* stream);
 
-/* Bytes of the decode K cache (opaque: rotated keys, pair-blocked) and of the V cache
- * ([B][Hkv][Lmax][d] bf16) for B sequences of up to Lmax tokens. */
+/* Bytes of the decode caches for B sequences of up to Lmax tokens.  Both layouts belong to
+ * the library (K: rotated keys, pair-blocked [B][Hkv][d/16][Lmax][16] bf16; V: blocked by
+ * 8 consecutive tokens, [B][Hkv][ceil(Lmax/8)][d][8] bf16); callers only size, allocate
+ * and pass them. */
 size_t wpa_kcache_bytes(int32_t B, int64_t Lmax, int32_t Hkv, int32_t d);
 size_t wpa_vcache_bytes(int32_t B, int64_t Lmax, int32_t Hkv, int32_t d);
 
@@ -150,7 +152,8 @@ size_t wpa_decode_workspace_bytes(int32_t B, int64_t Lmax, int32_t Hq, int32_t H
  *            token is then the last cached key)
  *   out      [B][Hq][d] (out_dtype);  lse [B][Hq] fp32 or NULL
  *   chunk_keys  keys per split-KV work item: a multiple of 256, or 0 for the library's
- *            choice.  The result does not depend on it beyond fp32 rounding.
+ *            choice.  The result depends on it only through rounding (probabilities
+ *            enter the P*V product as bf16 relative to each split's running maximum).
  *   workspace at least wpa_decode_workspace_bytes(B, Lmax, Hq, Hkv, d, chunk_keys).
  * kv_len values outside [1, Lmax] are a precondition violation (not checked: they live
  * on the device).

@@ -247,9 +247,12 @@ class KVCache:
                                   _ptr(self.v), self.B, self.Lmax, self.Hkv, self.d, self.base,
                                   _dtype_code(k), _stream(stream)))
 
-    def v_view(self):
-        """The V cache as bf16 [B][Hkv][Lmax][d]."""
-        return self.v.view(torch.bfloat16).view(self.B, self.Hkv, self.Lmax, self.d)
+    def v_tokens(self):
+        """A copy of the V cache as bf16 [B][Hkv][Lmax][d] (the cache itself is blocked by
+        8 consecutive tokens: [B][Hkv][ceil(Lmax/8)][d][8])."""
+        L8 = (self.Lmax + 7) // 8
+        v = self.v.view(torch.bfloat16).view(self.B, self.Hkv, L8, self.d, 8)
+        return v.permute(0, 1, 2, 4, 3).reshape(self.B, self.Hkv, L8 * 8, self.d)[:, :, :self.Lmax]
 
 
 def decode(q, cache: KVCache, kv_len, alpha: float, *, q_pos=None, scale: float | None = None,

@@ -1,20 +1,23 @@
 // One decode step with the per-RoPE-wavelength window (ATFlash abstract: the window
-// ported into a decode kernel), split over the KV sequence.
+// ported into a decode kernel), split over the KV sequence, on bf16 MFMA.
 //
 // Work item = (sequence b, kv head g, chunk of `chunk` keys); items past kv_len exit.
 // Each item serves all G q heads of its kv head, so every K/V byte is read once per step.
+// The 4 waves take interleaved 32-key tiles of the chunk, each with its own online-softmax
+// state, merged in LDS at the end.
 //
-// The keys of a wave (64 consecutive cache entries, lane = key) span a distance band
-// [dlo, dhi]; pairs with W_i < dlo are inactive for all of them, so the 16-dim blocks
-// below the first pair with W_i >= dlo are never read: far keys load only the blocks of
-// the long-wavelength pairs still inside their window (the K cache is pair-blocked, so
-// each block of 64 keys is one contiguous 2 KB run).  Blocks holding a pair whose
-// threshold falls inside the band are masked per key and pair; the test is D <= W_i.
-//
-// QK: VALU dot products, lane = key, q' broadcast from LDS.  Softmax: wavefront max
-// reductions, exp2 domain, lazy rescale (exact).  P*V: lane = (key group, 8-dim group),
-// coalesced 16-byte V loads.  Partials (O, m, l) per (item, q head) are merged in LDS
-// across the 4 waves and written out; the combine kernel merges chunks.
+// Per 32-key tile (one v_mfma_f32_32x32x16_bf16 row block):
+//   S^T[32 keys x 32 cols] = K'[keys x 16 dims] * Q'^T, one MFMA per active 16-dim pair
+//   block; columns are the G q heads (padded to 32).  With a single query position the
+//   window test depends on the key alone, so straddling pairs are handled exactly by
+//   zeroing them in the key's A-operand row (lane = key): no per-element fixup.  Blocks
+//   below the first pair active anywhere in the tile are neither read nor multiplied: far
+//   keys stream only the blocks of the long-wavelength pairs still inside their window.
+//   Softmax runs per column (lane = q head) over the keys held in registers, exp2 domain
+//   (q' is pre-scaled by scale*log2 e), lazy rescale.  The key rows of the A operand are
+//   permuted (bits 2 and 3 swapped) so the S^T registers are directly the P^T operand of
+//   O^T[32 dims x 32 cols] += V^T[32 dims x 16 keys] * P^T, whose V^T operand is one
+//   16-byte load per lane from the key-octet-blocked V cache.
 #include "wpa_device.hpp"
 #include "wpa_internal.hpp"
 
@@ -25,186 +28,213 @@ namespace {
 constexpr int kWaves = 4;
 constexpr float kTau = 8.0f;
 
-template <int D, int GM>
-__global__ __launch_bounds__(256) void decode_partial_kernel(DecodeParams p, Tables tab) {
+__device__ inline int perm_row(int m) {
+    return (m & ~0xC) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+__device__ inline float xchg32(float v, int xaddr) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(xaddr, __builtin_bit_cast(int, v)));
+}
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_partial_kernel(DecodeParams p, Tables tab) {
     constexpr int NB = D / 16;
     constexpr int P = D / 2;
-    constexpr int LPK = D / 8;            // lanes per key row in the P*V phase
-    constexpr int KPL = 64 / LPK;         // keys per wave-wide V load
-    __shared__ __attribute__((aligned(16))) float sQ[GM][D];
-    __shared__ float sP[kWaves][GM][64];
-    __shared__ float sM[kWaves][GM], sL[kWaves][GM];
-    __shared__ __attribute__((aligned(16))) float sO[kWaves][GM][D];
+    constexpr int NDB = D / 32;
+    constexpr int GMAX = 16;                        // q heads per kv head (columns used)
+    __shared__ __attribute__((aligned(16))) uint16_t sQ[32][D];      // pair-blocked, bf16
+    __shared__ float sO[kWaves][GMAX][D + 2];
 
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
+    const int xaddr = (lane ^ 32) << 2;
     const int G = p.Hq / p.Hkv;
     const int chunk = blockIdx.x % p.n_chunks;
     const int bg = blockIdx.x / p.n_chunks;
     const int g = bg % p.Hkv, b = bg / p.Hkv;
-    const int64_t Lb = p.kv_len[b];
-    const int64_t c0 = (int64_t)chunk * p.chunk;
+    const int Lb = __builtin_amdgcn_readfirstlane(p.kv_len[b]);
+    const int c0 = chunk * p.chunk;
     if (c0 >= Lb) return;
-    const int64_t c1 = c0 + p.chunk < Lb ? c0 + p.chunk : Lb;
-    const int64_t qpos = p.q_pos ? (int64_t)p.q_pos[b] : Lb - 1;
+    const int c1 = c0 + p.chunk < Lb ? c0 + p.chunk : Lb;
+    const int64_t qpos = __builtin_amdgcn_readfirstlane(p.q_pos ? p.q_pos[b] : Lb - 1);
+    const float sl2 = p.scale * 1.4426950408889634f;
 
-    // rotate the G query heads of this kv head into pair-blocked fp32 in LDS
-    for (int i = tid; i < GM * P; i += blockDim.x) {
+    // rotated q of the G heads (pre-scaled into log2 units), pair-blocked bf16 rows; rows
+    // >= G are zero
+    for (int i = tid; i < 32 * P; i += blockDim.x) {
         const int hh = i / P, pr = i % P;
-        if (hh >= G) continue;
-        const int64_t qb = ((int64_t)b * p.Hq + g * G + hh) * D;
-        float x, y;
-        if (p.in_f32) {
-            x = round_bf16(static_cast<const float*>(p.q)[qb + pr]);
-            y = round_bf16(static_cast<const float*>(p.q)[qb + P + pr]);
-        } else {
-            x = bf16_bits_to_f32(static_cast<const uint16_t*>(p.q)[qb + pr]);
-            y = bf16_bits_to_f32(static_cast<const uint16_t*>(p.q)[qb + P + pr]);
-        }
-        float s, c;
-        rope_sincos(qpos, tab.theta[pr], &s, &c);
         const int j = pr >> 3, e = pr & 7;
-        sQ[hh][16 * j + e] = round_bf16(x * c - y * s);
-        sQ[hh][16 * j + 8 + e] = round_bf16(y * c + x * s);
+        float xo = 0.f, yo = 0.f;
+        if (hh < G) {
+            const int64_t qb = ((int64_t)b * p.Hq + g * G + hh) * D;
+            float x, y;
+            if (p.in_f32) {
+                x = round_bf16(static_cast<const float*>(p.q)[qb + pr]);
+                y = round_bf16(static_cast<const float*>(p.q)[qb + P + pr]);
+            } else {
+                x = bf16_bits_to_f32(static_cast<const uint16_t*>(p.q)[qb + pr]);
+                y = bf16_bits_to_f32(static_cast<const uint16_t*>(p.q)[qb + P + pr]);
+            }
+            float sn, cs;
+            rope_sincos(qpos, tab.theta[pr], &sn, &cs);
+            xo = (x * cs - y * sn) * sl2;
+            yo = (y * cs + x * sn) * sl2;
+        }
+        sQ[hh][16 * j + e] = f32_to_bf16_bits(xo);
+        sQ[hh][16 * j + 8 + e] = f32_to_bf16_bits(yo);
     }
     __syncthreads();
+    // B operand of QK: column l32 = q head, half h = first/second halves of the block's pairs
+    u32x4 qB[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) qB[j] = *reinterpret_cast<const u32x4*>(&sQ[l32][16 * j + 8 * h]);
 
     const uint16_t* kpg = p.kp + ((int64_t)b * p.Hkv + g) * NB * p.Lmax * 16;
-    const uint16_t* vg = p.v + ((int64_t)b * p.Hkv + g) * p.Lmax * D;
-    const float sl2 = p.scale * 1.4426950408889634f;
-    const int kg = lane / LPK, dg = lane % LPK;
+    const int64_t L8 = (p.Lmax + 7) / 8;
+    const uint16_t* vg = p.v + ((int64_t)b * p.Hkv + g) * L8 * D * 8;
 
-    float m[GM], l[GM], acc[GM][8];
+    f32x16 O[NDB];
 #pragma unroll
-    for (int hh = 0; hh < GM; ++hh) {
-        m[hh] = -INFINITY;
-        l[hh] = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[hh][i] = 0.f;
-    }
+    for (int i = 0; i < NDB; ++i) O[i] = f32x16{};
+    float m = -INFINITY, lsum = 0.f;
     uint64_t cnt = 0;
+    const int arow = perm_row(l32);                  // key row this lane feeds to the A operand
 
-    for (int64_t kw0 = c0 + 64 * w; kw0 < c1; kw0 += 64 * kWaves) {
-        const int64_t key = kw0 + lane;
-        const bool kvalid = key < c1;
-        const int64_t kmax = (kw0 + 63 < c1 ? kw0 + 63 : c1 - 1);
-        const int64_t dist = qpos - key >= 0 ? qpos - key : key - qpos;
+    const char* kbytes = reinterpret_cast<const char*>(kpg);
+    const char* vbytes = reinterpret_cast<const char*>(vg);
+    const int64_t kblk = (int64_t)p.Lmax * 32;           // bytes of one pair block
+    const uint32_t voff0 = (uint32_t)((h * D + l32) * 16);
+    int plo = 0, pfull = 0;                          // band edges, moved incrementally
+    for (int k0 = c0 + 32 * w; k0 < c1; k0 += 32 * kWaves) {
+        const int kmax = k0 + 31 < c1 ? k0 + 31 : c1 - 1;
         int64_t dlo, dhi;
-        if (qpos >= kmax) { dlo = qpos - kmax; dhi = qpos - kw0; }
-        else if (qpos <= kw0) { dlo = kw0 - qpos; dhi = kmax - qpos; }
-        else { dlo = 0; dhi = (qpos - kw0 > kmax - qpos) ? qpos - kw0 : kmax - qpos; }
-        const int plo = first_at_least(tab.W, P, dlo);
-        const int pfull = first_at_least(tab.W, P, dhi);
+        if (qpos >= kmax) { dlo = qpos - kmax; dhi = qpos - k0; }
+        else if (qpos <= k0) { dlo = k0 - qpos; dhi = kmax - qpos; }
+        else { dlo = 0; dhi = (qpos - k0 > kmax - qpos) ? qpos - k0 : kmax - qpos; }
+        const int dl = __builtin_amdgcn_readfirstlane((int)(dlo < INT32_MAX ? dlo : INT32_MAX));
+        const int dh = __builtin_amdgcn_readfirstlane((int)(dhi < INT32_MAX ? dhi : INT32_MAX));
+        // first pair with W >= dl (resp. dh); consecutive tiles of a wave move these by a
+        // step or two, so walk from the previous value instead of searching
+        while (plo > 0 && tab.W[plo - 1] >= dl) --plo;
+        while (plo < P && tab.W[plo] < dl) ++plo;
+        while (pfull > 0 && tab.W[pfull - 1] >= dh) --pfull;
+        while (pfull < P && tab.W[pfull] < dh) ++pfull;
+        plo = __builtin_amdgcn_readfirstlane(plo);
+        pfull = __builtin_amdgcn_readfirstlane(pfull);
+        const int jlo = plo >> 3;
+        const bool tail = k0 + 32 > c1;             // tile runs past the chunk's last key
 
-        float s[GM];
+        // issue every load of the tile before using any: active K blocks (lane = key row
+        // arow, half h) and the V^T operands (lane = dim, half h = key octet); uniform
+        // 64-bit bases with 32-bit lane offsets
+        const int key = k0 + arow;
+        const int keyc = key < c1 ? key : c1 - 1;
+        const uint32_t koff = (uint32_t)(keyc * 32 + 16 * h);
+        u32x4 ka[NB];
 #pragma unroll
-        for (int hh = 0; hh < GM; ++hh) s[hh] = 0.f;
-        for (int j = plo >> 3; j < NB; ++j) {
-            u32x4 wx = {0u, 0u, 0u, 0u}, wy = {0u, 0u, 0u, 0u};
-            if (kvalid) {
-                const u32x4* src = reinterpret_cast<const u32x4*>(kpg + ((int64_t)j * p.Lmax + key) * 16);
-                wx = src[0];
-                wy = src[1];
-            }
-            float kx[8], ky[8];
+        for (int j = 0; j < NB; ++j) {
+            if (j < jlo) continue;
+            ka[j] = *reinterpret_cast<const u32x4*>(kbytes + j * kblk + koff);
+        }
+        u32x4 va[2][NDB];
+        const int64_t oct0 = k0 >> 3;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                kx[2 * t] = bf16_bits_to_f32(wx[t] & 0xffffu);
-                kx[2 * t + 1] = bf16_bits_to_f32(wx[t] >> 16);
-                ky[2 * t] = bf16_bits_to_f32(wy[t] & 0xffffu);
-                ky[2 * t + 1] = bf16_bits_to_f32(wy[t] >> 16);
-            }
-            if (8 * j < pfull) {       // block holds a pair not active for every key
-                int on_count = 0;
+        for (int c = 0; c < 2; ++c) {
+            // octet oct0 + 2c + h; the last octet of the cache stands in past its end
+            const int64_t ob = oct0 + 2 * c + 1 < L8 ? oct0 + 2 * c : L8 - 1 - h;
+            const char* vb = vbytes + ob * (D * 16);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const bool on = dist <= (int64_t)tab.W[8 * j + e];
-                    on_count += on;
-                    kx[e] = on ? kx[e] : 0.f;
-                    ky[e] = on ? ky[e] : 0.f;
+            for (int db = 0; db < NDB; ++db)
+                va[c][db] = *reinterpret_cast<const u32x4*>(vb + voff0 + db * 512);
+        }
+
+        // S^T over the active blocks; pairs not active for this lane's key are zeroed
+        const int64_t dist = qpos - key >= 0 ? qpos - key : key - qpos;
+        f32x16 S = f32x16{};
+#pragma unroll
+        for (int j = NB - 1; j >= 0; --j) {
+            if (j < jlo) continue;
+            u32x4 a = ka[j];
+            int on = 8;
+            if (8 * j < pfull) {                      // block holds a straddling pair
+                on = 0;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const bool e0 = dist <= (int64_t)tab.W[8 * j + 2 * t];
+                    const bool e1 = dist <= (int64_t)tab.W[8 * j + 2 * t + 1];
+                    on += e0 + e1;
+                    a[t] &= (e0 ? 0xffffu : 0u) | (e1 ? 0xffff0000u : 0u);
                 }
-                if (kvalid) cnt += on_count;
-            } else if (kvalid) {
-                cnt += 8;
             }
-#pragma unroll
-            for (int hh = 0; hh < GM; ++hh) {
-                if (hh >= G) continue;
-                const f32x4* qx = reinterpret_cast<const f32x4*>(&sQ[hh][16 * j]);
-                const f32x4 a0 = qx[0], a1 = qx[1], b0 = qx[2], b1 = qx[3];
-                float t = s[hh];
-                t += a0[0] * kx[0] + a0[1] * kx[1] + a0[2] * kx[2] + a0[3] * kx[3];
-                t += a1[0] * kx[4] + a1[1] * kx[5] + a1[2] * kx[6] + a1[3] * kx[7];
-                t += b0[0] * ky[0] + b0[1] * ky[1] + b0[2] * ky[2] + b0[3] * ky[3];
-                t += b1[0] * ky[4] + b1[1] * ky[5] + b1[2] * ky[6] + b1[3] * ky[7];
-                s[hh] = t;
-            }
+            if (p.counter && h == 0 && key < c1) cnt += on;
+            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                        __builtin_bit_cast(bf16x8, qB[j]), S,
+                                                        0, 0, 0);
         }
 
+        // register r of half h holds key k0 + 16(r/8) + 8h + (r%8) for column l32
+        if (tail) {
 #pragma unroll
-        for (int hh = 0; hh < GM; ++hh) {
-            if (hh >= G) continue;
-            const float t = kvalid ? s[hh] * sl2 : -INFINITY;
-            const float mx = wave_max(t);
-            const float m_new = fmaxf(m[hh], mx);
-            if (m_new > m[hh] + kTau) {          // uniform: m and mx are wave-wide
-                const float alpha = exp2f(m[hh] - m_new);
-                l[hh] *= alpha;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) acc[hh][i] *= alpha;
-                m[hh] = m_new;
-            }
-            const float pr = exp2f(t - m[hh]);
-            l[hh] += pr;
-            sP[w][hh][lane] = pr;
+            for (int r = 0; r < 16; ++r)
+                if (k0 + 16 * (r >> 3) + 8 * h + (r & 7) >= c1) S[r] = -INFINITY;
         }
-        __builtin_amdgcn_s_waitcnt(0xc07f);      // lgkmcnt(0): own LDS writes done
-        __builtin_amdgcn_wave_barrier();
-
-        // P*V: lane = (key group kg, dims 8*dg .. 8*dg+7)
-#pragma unroll 4
-        for (int it = 0; it < 64 / KPL; ++it) {
-            const int kl = it * KPL + kg;
-            const int64_t kk = kw0 + kl;
-            if (kk >= c1) continue;
-            float vv[8];
-            load8<false>(vg, kk * D + 8 * dg, vv);
+        float mx = S[0];
 #pragma unroll
-            for (int hh = 0; hh < GM; ++hh) {
-                if (hh >= G) continue;
-                const float pw = sP[w][hh][kl];
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
+        mx = fmaxf(mx, xchg32(mx, xaddr));
+        const float m_new = fmaxf(m, mx);
+        if (__any(m_new > m + kTau)) {
+            const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+            lsum *= alpha;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) acc[hh][i] += pw * vv[i];
+            for (int i = 0; i < NDB; ++i) O[i] *= alpha;
+            m = m_new;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            S[r] = __builtin_amdgcn_exp2f(S[r] - m);
+            lsum += S[r];
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const u32x4 pb = u32x4{pack_bf16x2(S[8 * c + 0], S[8 * c + 1]),
+                                   pack_bf16x2(S[8 * c + 2], S[8 * c + 3]),
+                                   pack_bf16x2(S[8 * c + 4], S[8 * c + 5]),
+                                   pack_bf16x2(S[8 * c + 6], S[8 * c + 7])};
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                u32x4 a = va[c][db];
+                if (tail) {                           // cache slots past kv_len: zero them
+                    const int kb = k0 + 16 * c + 8 * h;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        a[t] &= (kb + 2 * t < c1 ? 0xffffu : 0u) | (kb + 2 * t + 1 < c1 ? 0xffff0000u : 0u);
+                }
+                O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, pb), O[db], 0, 0, 0);
             }
         }
-        __builtin_amdgcn_wave_barrier();
     }
 
-    // merge the key groups of this wave (same dims, same running max)
-#pragma unroll
-    for (int hh = 0; hh < GM; ++hh) {
-        if (hh >= G) continue;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            float v = acc[hh][i];
-#pragma unroll
-            for (int o = LPK; o < 64; o <<= 1) v += __shfl_xor(v, o);
-            acc[hh][i] = v;
-        }
-        const float lw = wave_sum(l[hh]);
-        if (lane < LPK) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) sO[w][hh][8 * lane + i] = acc[hh][i];
-        }
-        if (lane == 0) {
-            sM[w][hh] = m[hh];
-            sL[w][hh] = lw;
-        }
-    }
     if (p.counter) {
         uint64_t tot = cnt;
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) tot += __shfl_xor(tot, o);
         if (lane == 0 && tot) atomicAdd(p.counter, (unsigned long long)(tot * (uint64_t)G));
+    }
+    // this wave's (O^T, m, l) for its columns (q heads) into LDS: lane = column l32,
+    // register r of dim block db is dim 32db + 8(r/4) + 4h + (r%4)
+    const float l_tot = lsum + xchg32(lsum, xaddr);
+    if (l32 < G) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                sO[w][l32][32 * db + 8 * (r >> 2) + 4 * h + (r & 3)] = O[db][r];
+        if (h == 0) {
+            sO[w][l32][D] = m;
+            sO[w][l32][D + 1] = l_tot;
+        }
     }
     __syncthreads();
 
@@ -214,13 +244,13 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeParams p, Tab
         const int hh = i / D, e = i % D;
         float M = -INFINITY;
 #pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sM[ww][hh]);
+        for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sO[ww][hh][D]);
         float o = 0.f, ls = 0.f;
 #pragma unroll
         for (int ww = 0; ww < kWaves; ++ww) {
-            const float f = exp2f(sM[ww][hh] - M);
+            const float f = __builtin_amdgcn_exp2f(sO[ww][hh][D] - M);
             o += f * sO[ww][hh][e];
-            ls += f * sL[ww][hh];
+            ls += f * sO[ww][hh][D + 1];
         }
         dst[hh * (D + 2) + e] = o;
         if (e == 0) {
@@ -241,7 +271,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
     const int b = bh / p.Hq, hq = bh % p.Hq;
     const int G = p.Hq / p.Hkv;
     const int g = hq / G, hh = hq % G;
-    const int64_t Lb = p.kv_len[b];
+    const int64_t Lb = __builtin_amdgcn_readfirstlane(p.kv_len[b]);
     const int nc = (int)((Lb + p.chunk - 1) / p.chunk);
     const float* base = p.partial + ((int64_t)(b * p.Hkv + g) * p.n_chunks) * G * (D + 2) + hh * (D + 2);
     const int64_t cstride = (int64_t)G * (D + 2);
@@ -285,24 +315,14 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
     }
 }
 
-template <int D, int GM>
-void launch_partial(const DecodeParams& p, const Tables& t, hipStream_t s) {
-    dim3 grid((unsigned)((int64_t)p.n_chunks * p.B * p.Hkv)), block(64 * kWaves);
-    decode_partial_kernel<D, GM><<<grid, block, 0, s>>>(p, t);
-}
-
 template <int D>
 hipError_t launch_decode_d(const DecodeParams& p, const Tables& t, hipStream_t s) {
-    const int G = p.Hq / p.Hkv;
-    if (G <= 1) launch_partial<D, 1>(p, t, s);
-    else if (G <= 2) launch_partial<D, 2>(p, t, s);
-    else if (G <= 4) launch_partial<D, 4>(p, t, s);
-    else if (G <= 8) launch_partial<D, 8>(p, t, s);
-    else launch_partial<D, 16>(p, t, s);
+    dim3 grid((unsigned)((int64_t)p.n_chunks * p.B * p.Hkv)), block(64 * kWaves);
+    decode_partial_kernel<D><<<grid, block, 0, s>>>(p, t);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    dim3 grid((unsigned)(p.B * p.Hq), D / 32), block(256);
-    decode_combine_kernel<D><<<grid, block, 0, s>>>(p);
+    dim3 grid2((unsigned)(p.B * p.Hq), D / 32), block2(256);
+    decode_combine_kernel<D><<<grid2, block2, 0, s>>>(p);
     return hipGetLastError();
 }
 

@@ -189,7 +189,7 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
     auto issue = [&](int kt, int stage) {
         const int ks = kt * BN;
         const int kend = (ks + BN < N ? ks + BN : N) - 1;
-        const int dmin_wg = pq_wg - POS(kend) > 0 ? pq_wg - POS(kend) : 0;
+        const int dmin_wg = uniform(pq_wg - POS(kend) > 0 ? pq_wg - POS(kend) : 0);
         while (plo_wg < P && tab.W[plo_wg] < dmin_wg) ++plo_wg;
         const int jlo = uniform(plo_wg) >> 3;
         const int nK = Tile<D>::KI * (NB - jlo);
@@ -234,8 +234,8 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
             const int k0 = ks + 32 * sub;
             if (k0 > q0 + 31 || k0 >= N) continue;     // whole sub-tile above the diagonal
             const int k_last = k0 + 31 < N ? k0 + 31 : N - 1;
-            const int dmin = pq_lo - POS(k_last) > 0 ? pq_lo - POS(k_last) : 0;
-            const int dmax = pq_hi - POS(k0);
+            const int dmin = uniform(pq_lo - POS(k_last) > 0 ? pq_lo - POS(k_last) : 0);
+            const int dmax = uniform(pq_hi - POS(k0));
             while (plo < P && tab.W[plo] < dmin) ++plo;
             while (pfull < P && tab.W[pfull] < dmax) ++pfull;
             plo = uniform(plo);

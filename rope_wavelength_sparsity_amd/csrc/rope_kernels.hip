@@ -7,8 +7,9 @@
 // "contract only the active blocks" (pairs form a contiguous slice of the contraction
 // axis at every distance) reads contiguous memory for every token range.
 //
-// Values: for prefill they are transposed to [B][Hkv][d][tokens] so the P*V product can
-// read key-contiguous MFMA operands; for the decode cache they keep [B][Hkv][tokens][d].
+// Values: for prefill they are transposed to [B][Hkv][d][tokens] and for the decode cache
+// blocked by key octets, [B][Hkv][tokens/8][d][8]: in both, the P*V matrix product (a
+// contraction over keys) reads key-contiguous MFMA operands.
 #include "wpa_device.hpp"
 #include "wpa_internal.hpp"
 
@@ -96,24 +97,57 @@ __global__ __launch_bounds__(256) void v_transpose_kernel(RopeParams p) {
     }
 }
 
-// V copy into the decode cache [B][Hkv][Lmax][d] (bf16).
+// V into the decode cache, key-octet blocked: [B][Hkv][ceil(Lmax/8)][d][8] bf16, i.e. for
+// every 8 consecutive tokens each dim's 8 values are contiguous (16 bytes).  That is the
+// operand layout of the P*V matrix product in decode (contraction over keys).  One thread
+// handles one (sequence, kv head, octet, 8 dims): an 8x8 transpose in registers; tokens of a
+// partially written octet keep their previous cache contents.
 template <bool F32>
-__global__ __launch_bounds__(256) void v_copy_kernel(RopeParams p) {
-    const int per_row = p.d / 8;
-    const int64_t total = (int64_t)p.B * p.n * p.Hkv * per_row;
+__global__ __launch_bounds__(256) void v_cache_kernel(RopeParams p) {
+    const int d8 = p.d / 8;
+    const int64_t o_first = p.t0 / 8, o_last = (p.t0 + p.n - 1) / 8;
+    const int64_t n_oct = o_last - o_first + 1;
+    const int64_t total = (int64_t)p.B * p.Hkv * n_oct * d8;
     int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (id >= total) return;
-    const int e8 = (int)(id % per_row) * 8;
-    int64_t rest = id / per_row;
+    const int e8 = (int)(id % d8) * 8;
+    int64_t rest = id / d8;
+    const int64_t o = o_first + rest % n_oct;
+    rest /= n_oct;
     const int g = (int)(rest % p.Hkv);
-    rest /= p.Hkv;
-    const int64_t t = rest % p.n;
-    const int b = (int)(rest / p.n);
-    float x[8];
-    load8<F32>(p.v, (((int64_t)b * p.n + t) * p.Hkv + g) * p.d + e8, x);
-    uint16_t* dst = p.vout + (((int64_t)b * p.Hkv + g) * p.ld + p.t0 + t) * p.d + e8;
-    *reinterpret_cast<u32x4*>(dst) = u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
-                                           pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
+    const int b = (int)(rest / p.Hkv);
+    const int64_t L8 = (p.ld + 7) / 8;
+    uint16_t* dst = p.vout + ((((int64_t)b * p.Hkv + g) * L8 + o) * p.d + e8) * 8;
+    uint16_t cell[8][8];                 // [dim][token in octet]
+    const bool partial = o * 8 < p.t0 || o * 8 + 8 > p.t0 + p.n;
+    if (partial) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const u32x4 w = reinterpret_cast<const u32x4*>(dst)[e];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                cell[e][2 * i] = (uint16_t)(w[i] & 0xffffu);
+                cell[e][2 * i + 1] = (uint16_t)(w[i] >> 16);
+            }
+        }
+    }
+#pragma unroll
+    for (int t8 = 0; t8 < 8; ++t8) {
+        const int64_t t = o * 8 + t8 - p.t0;            // source row
+        if (t < 0 || t >= p.n) continue;
+        float x[8];
+        load8<F32>(p.v, (((int64_t)b * p.n + t) * p.Hkv + g) * p.d + e8, x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cell[e][t8] = f32_to_bf16_bits(x[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        u32x4 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            w[i] = (uint32_t)cell[e][2 * i] | ((uint32_t)cell[e][2 * i + 1] << 16);
+        reinterpret_cast<u32x4*>(dst)[e] = w;
+    }
 }
 
 hipError_t launch_rope_relayout(const RopeParams& p, hipStream_t s) {
@@ -136,10 +170,11 @@ hipError_t launch_rope_relayout(const RopeParams& p, hipStream_t s) {
             else v_transpose_kernel<false, 128><<<grid, blk, 0, s>>>(p);
         }
     } else {
-        const int64_t nv = (int64_t)p.B * p.n * p.Hkv * (p.d / 8);
+        const int64_t n_oct = (p.t0 + p.n - 1) / 8 - p.t0 / 8 + 1;
+        const int64_t nv = (int64_t)p.B * p.Hkv * n_oct * (p.d / 8);
         dim3 grid((unsigned)((nv + 255) / 256));
-        if (p.in_f32) v_copy_kernel<true><<<grid, blk, 0, s>>>(p);
-        else v_copy_kernel<false><<<grid, blk, 0, s>>>(p);
+        if (p.in_f32) v_cache_kernel<true><<<grid, blk, 0, s>>>(p);
+        else v_cache_kernel<false><<<grid, blk, 0, s>>>(p);
     }
     return hipGetLastError();
 }

@@ -261,7 +261,8 @@ size_t wpa_kcache_bytes(int32_t B, int64_t Lmax, int32_t Hkv, int32_t d) {
 }
 
 size_t wpa_vcache_bytes(int32_t B, int64_t Lmax, int32_t Hkv, int32_t d) {
-    return wpa_kcache_bytes(B, Lmax, Hkv, d);
+    if (B < 1 || Lmax < 1 || Hkv < 1 || d < 1) return 0;
+    return (size_t)B * Hkv * ((Lmax + 7) / 8) * 8 * d * 2;
 }
 
 int wpa_kv_write(const void* k, const void* v, int64_t start, int64_t n, void* k_cache,

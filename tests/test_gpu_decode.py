@@ -23,14 +23,15 @@ def _cache_from(k, v, base, Lmax=None):
 @pytest.mark.parametrize("d,base", [(64, 1e4), (128, 5e5), (128, 1e7)])
 def test_kv_write_rotation(d, base):
     """The K cache holds the keys rotated at their token index, rounded to bf16, in the
-    pair-blocked layout [B][Hkv][d/16][Lmax][16]; the V cache holds V as bf16."""
+    pair-blocked layout [B][Hkv][d/16][Lmax][16]; the V cache holds V as bf16 (blocked by 8
+    tokens).  Two appends, the second starting inside an 8-token block."""
     need_gpu()
     B, L, Hkv = 2, 300, 3
     k, v = synth.prefill_inputs(B, L, Hkv, Hkv, d, "bf16", seed=5)[1:]
     say("kv_write", d, base)
     cache = wpa.KVCache(B, L + 17, Hkv, d, base)
-    cache.write(k[:, :100].cuda().contiguous(), v[:, :100].cuda().contiguous(), 0)
-    cache.write(k[:, 100:].cuda().contiguous(), v[:, 100:].cuda().contiguous(), 100)
+    cache.write(k[:, :101].cuda().contiguous(), v[:, :101].cuda().contiguous(), 0)
+    cache.write(k[:, 101:].cuda().contiguous(), v[:, 101:].cuda().contiguous(), 101)
     torch.cuda.synchronize()
     kb = cache.k.view(torch.bfloat16).view(B, Hkv, d // 16, L + 17, 16)[:, :, :, :L].float().cpu()
     P = d // 2
@@ -41,7 +42,7 @@ def test_kv_write_rotation(d, base):
         ref = oracle.rope(synth.to_oracle(k[b]), np.arange(L), base)
         # bf16 rounding of the rotated value (relative 2^-8) plus fp32 sincos
         assert np.abs(got[b] - ref).max() <= 2 ** -8 * (np.abs(ref).max() + 1e-3) * 1.01
-    vb = cache.v_view()[:, :, :L].float().cpu().permute(0, 2, 1, 3)
+    vb = cache.v_tokens()[:, :, :L].float().cpu().permute(0, 2, 1, 3)
     assert torch.equal(vb, v.float())
 
 
@@ -104,6 +105,9 @@ def test_decode_equals_last_prefill_row():
 
 
 def test_decode_chunking_invariance():
+    """The split of the keys into work items changes only rounding: the probabilities enter
+    the P*V product as bf16 relative to each split's running max, so outputs may move by a
+    few bf16 ulps of p (bound 2e-3, a fifth of the parity tolerance); LSE by fp32 rounding."""
     need_gpu()
     B, Lmax, Hq, Hkv, d, base = 2, 5000, 24, 8, 128, 5e5
     q, k, v, lens = synth.decode_inputs(B, Lmax, Hq, Hkv, d, "bf16", seed=11, len_lo=3000)
@@ -116,7 +120,7 @@ def test_decode_chunking_invariance():
         outs.append((o.cpu(), l.cpu()))
     torch.cuda.synchronize()
     for o, l in outs[1:]:
-        assert (o - outs[0][0]).abs().max() <= 1e-4
+        assert (o - outs[0][0]).abs().max() <= 2e-3
         assert (l - outs[0][1]).abs().max() <= 1e-4
 
 
