@@ -88,15 +88,16 @@ struct Tile {
     static constexpr int PI = BN * 4 / 256;         // wave loads for positions
     static constexpr int CPR = BN / 8;              // 16-byte chunks per V^T row
     static constexpr int RPI = 64 / CPR;            // V^T rows per wave load
-};
-
-template <int D>
-struct Occupancy {
-    static constexpr int waves_per_eu = 2;
+    // Compute waves per workgroup (plus one producer wave) and the waves per SIMD that the
+    // register budget must allow: a 9-wave workgroup needs 3 per SIMD (<= 168 VGPRs), and
+    // the d=128 kernel, at up to 256 VGPRs, runs 2 per SIMD, so at most 8 waves per CU.
+    static constexpr int MAXW = D == 64 ? 8 : 7;
+    static constexpr int WAVES_PER_EU = D == 64 ? 3 : 2;
 };
 
 template <int D, bool F32, bool HASPOS, bool COUNT>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(Occupancy<D>::waves_per_eu)))
+__global__ __launch_bounds__(64 * (Tile<D>::MAXW + 1))
+__attribute__((amdgpu_waves_per_eu(Tile<D>::WAVES_PER_EU)))
 void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
     constexpr int NB = D / 16;
     constexpr int P = D / 2;
@@ -108,8 +109,10 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
     __shared__ __attribute__((aligned(16))) int32_t sPos2[2][HASPOS ? BN : 1];
 
     const int tid = threadIdx.x;
-    const int nw = blockDim.x >> 6;
-    const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
+    // wave index through readfirstlane: everything derived from it (head, rows, band
+    // edges, branches on them) is then known to be wave-uniform and stays scalar
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l32 = lane & 31, h = lane >> 5;
     const int xaddr = (lane ^ 32) << 2;
     const int G = p.Hq / p.Hkv;
     const int U = p.B * p.Hkv * L.nhc;
@@ -125,7 +128,8 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
     const int N = (int)p.N;
     const int qs = rb * 32 * L.R;
     const int q0 = qs + 32 * rg;
-    const bool wave_ok = head_ok && q0 < N;
+    const bool producer = w == L.Gc * L.R;                 // the extra, loading wave
+    const bool wave_ok = !producer && head_ok && q0 < N;
     const int qrow = q0 + l32;
     const bool row_ok = qrow < N;
     const int qrow_c = row_ok ? qrow : N - 1;
@@ -180,6 +184,7 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
     float m = -INFINITY, lsum = 0.f;
     uint64_t cnt = 0;
     int plo = 0, pfull = 0, plo_wg = 0;     // running band edges (distances only grow)
+    int w_lo = tab.W[0], w_full = tab.W[0];  // W at the two edges (INT32_MAX past the end)
     int q_key = -1;                          // pfull for which qm holds the masked block
     u32x4 qm = {0u, 0u, 0u, 0u};
 
@@ -194,7 +199,7 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
         const int jlo = uniform(plo_wg) >> 3;
         const int nK = Tile<D>::KI * (NB - jlo);
         const int nI = nK + Tile<D>::VI + (HASPOS ? Tile<D>::PI : 0);
-        for (int i = w; i < nI; i += nw) {
+        for (int i = 0; i < nI; ++i) {
             if (i < nK) {
                 const int j = jlo + i / Tile<D>::KI, part = i % Tile<D>::KI;
                 const uint16_t* src = kpg + ((int64_t)j * p.Np + ks) * 16 + (part * 64 + lane) * 8;
@@ -217,29 +222,26 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
         }
     };
 
-    issue(kt_last, 0);
-    for (int kt = kt_last, it = 0; kt >= 0; --kt, ++it) {
+    // One key tile from LDS: its 32-key sub-tiles, nearest keys first.
+    auto compute = [&](int kt, const uint16_t* sK, const uint16_t* sV, const int32_t* sPos) {
         const int ks = kt * BN;
-        const int stage = it & 1;
-        __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): this thread's loads landed
-        __syncthreads();                     // ... and everyone's; the other stage is free again
-        if (kt > 0) issue(kt - 1, stage ^ 1);
-        if (!wave_ok) continue;
-        const uint16_t* sK = sK2[stage];
-        const uint16_t* sV = sV2[stage];
-        const int32_t* sPos = sPos2[stage];
-
 #pragma unroll 1
         for (int sub = NSUB - 1; sub >= 0; --sub) {      // nearest keys first
             const int k0 = ks + 32 * sub;
             if (k0 > q0 + 31 || k0 >= N) continue;     // whole sub-tile above the diagonal
             const int k_last = k0 + 31 < N ? k0 + 31 : N - 1;
-            const int dmin = uniform(pq_lo - POS(k_last) > 0 ? pq_lo - POS(k_last) : 0);
-            const int dmax = uniform(pq_hi - POS(k0));
-            while (plo < P && tab.W[plo] < dmin) ++plo;
-            while (pfull < P && tab.W[pfull] < dmax) ++pfull;
-            plo = uniform(plo);
-            pfull = uniform(pfull);
+            const int p_first = uniform(HASPOS ? sPos[k0 - ks] : k0);
+            const int p_last = uniform(HASPOS ? sPos[k_last - ks] : k_last);
+            const int dmin = pq_lo - p_last > 0 ? pq_lo - p_last : 0;
+            const int dmax = pq_hi - p_first;
+            while (w_lo < dmin) {
+                ++plo;
+                w_lo = plo < P ? tab.W[plo] : INT32_MAX;
+            }
+            while (w_full < dmax) {
+                ++pfull;
+                w_full = pfull < P ? tab.W[pfull] : INT32_MAX;
+            }
             const int jf = pfull >> 3;
             if (pfull != q_key && pfull < P) {
                 // first fully-active block with its leading (not fully active) pairs zeroed
@@ -362,6 +364,26 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
                 }
             }
         }
+    };
+
+    // The producer wave streams tile kt-1 into one stage while the others compute tile kt
+    // from the other stage; it waits for its own loads before the barrier that hands the
+    // stage over, so no compute wave ever has a direct load in flight (the compiler would
+    // otherwise hold every LDS read of a compute wave until such loads land).
+    if (producer) {
+        issue(kt_last, 0);
+        __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+    }
+    for (int kt = kt_last, it = 0; kt >= 0; --kt, ++it) {
+        __syncthreads();          // tile kt is in stage it&1; stage (it+1)&1 is free again
+        if (producer) {
+            if (kt > 0) {
+                issue(kt - 1, (it & 1) ^ 1);
+                __builtin_amdgcn_s_waitcnt(0x0070);
+            }
+        } else if (wave_ok) {
+            compute(kt, sK2[it & 1], sV2[it & 1], sPos2[it & 1]);
+        }
     }
 
     if (COUNT) {
@@ -399,12 +421,13 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
 template <int D, bool F32>
 hipError_t launch_d(const PrefillParams& p, const Tables& t, hipStream_t s) {
     const int G = p.Hq / p.Hkv;
+    constexpr int MAXW = Tile<D>::MAXW;
     Launch L;
-    L.Gc = G < 8 ? G : 8;
-    L.nhc = (G + L.Gc - 1) / L.Gc;
-    L.R = 8 / L.Gc > 1 ? 8 / L.Gc : 1;
+    L.nhc = (G + MAXW - 1) / MAXW;                  // head chunks, as even as possible
+    L.Gc = (G + L.nhc - 1) / L.nhc;
+    L.R = MAXW / L.Gc > 1 ? MAXW / L.Gc : 1;
     L.n_rb = (int)((p.N + 32 * L.R - 1) / (32 * L.R));
-    const int waves = L.Gc * L.R;
+    const int waves = L.Gc * L.R + 1;               // + the producer wave
     const int64_t nblk = (int64_t)L.n_rb * p.B * p.Hkv * L.nhc;
     dim3 grid((unsigned)nblk), block(64 * waves);
     const bool hp = p.pos != nullptr, cn = p.counter != nullptr;
