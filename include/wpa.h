@@ -23,9 +23,13 @@
  *   - Causality is by token index (key c visible to query r iff c <= r).
  *   - GQA: q head h reads kv head h / (Hq/Hkv).
  *   - dtype (WPA_BF16 or WPA_FP32) is the element type of q, k and v; out_dtype that of
- *     out.  fp32 inputs are rounded to bf16 (round-to-nearest-even) on load; every matrix
- *     product runs in bf16 with fp32 accumulation; softmax statistics are fp32.  A bf16
- *     out is the fp32 result rounded to nearest even.
+ *     out.  fp32 inputs are rounded to bf16 (round-to-nearest-even) on load.  Rotated
+ *     queries (times scale*log2 e) and rotated keys are rounded to IEEE half precision
+ *     for the q.k product; probabilities and values enter the P*V product as bf16; both
+ *     products accumulate in fp32 and softmax statistics are fp32.  Rotated key components
+ *     and scaled rotated query components must stay below 65504 in magnitude (larger ones
+ *     overflow to infinity and the affected outputs are not finite).  A bf16 out is the
+ *     fp32 result rounded to nearest even.
  *   - All pointers except those documented as host pointers are device pointers.  Device
  *     buffers must be 16-byte aligned.  The caller owns every buffer (including workspace
  *     and caches); the library allocates nothing and keeps no per-call state.
@@ -105,7 +109,7 @@ int wpa_prefill(const void* q, const void* k, const void* v, void* out, float* l
  * The two halves of wpa_prefill, for callers that time them apart or reuse the prepared
  * keys and values for several query launches.  wpa_prefill(...) is exactly
  * wpa_prefill_prepare(...) followed by wpa_prefill_attend(...) on the same stream.
- *   prepare: rotate k at its positions into the workspace (pair-blocked bf16) and store v
+ *   prepare: rotate k at its positions into the workspace (pair-blocked half) and store v
  *            transposed there; q is not read.
  *   attend:  the windowed attention of q against a workspace prepared for the same
  *            B, N, Hkv, d, base, positions (the workspace is only read).
@@ -121,7 +125,7 @@ int wpa_prefill_attend(const void* q, void* out, float* lse, const int32_t* posi
                        void* stream);
 
 /* Bytes of the decode caches for B sequences of up to Lmax tokens.  Both layouts belong to
- * the library (K: rotated keys, pair-blocked [B][Hkv][d/16][Lmax][16] bf16; V: blocked by
+ * the library (K: rotated keys, pair-blocked [B][Hkv][d/16][Lmax][16] half; V: blocked by
  * 8 consecutive tokens, [B][Hkv][ceil(Lmax/8)][d][8] bf16); callers only size, allocate
  * and pass them. */
 size_t wpa_kcache_bytes(int32_t B, int64_t Lmax, int32_t Hkv, int32_t d);
@@ -130,7 +134,7 @@ size_t wpa_vcache_bytes(int32_t B, int64_t Lmax, int32_t Hkv, int32_t d);
 /*
  * Append n tokens (token indices start .. start+n-1, which are also their positions) of
  * every sequence to the decode caches.  k, v are pre-RoPE [B][n][Hkv][d] (dtype).  Keys
- * are rotated once here and stored as bf16; values are stored as bf16.
+ * are rotated once here and stored as IEEE half; values are stored as bf16.
  * Requires 0 <= start, n >= 1, start + n <= Lmax.
  */
 int wpa_kv_write(const void* k, const void* v, int64_t start, int64_t n, void* k_cache,

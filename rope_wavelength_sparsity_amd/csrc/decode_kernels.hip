@@ -1,12 +1,13 @@
 // One decode step with the per-RoPE-wavelength window (ATFlash abstract: the window
-// ported into a decode kernel), split over the KV sequence, on bf16 MFMA.
+// ported into a decode kernel), split over the KV sequence, on MFMA (q.k in half
+// precision, P*V in bf16).
 //
 // Work item = (sequence b, kv head g, chunk of `chunk` keys); items past kv_len exit.
 // Each item serves all G q heads of its kv head, so every K/V byte is read once per step.
 // The 4 waves take interleaved 32-key tiles of the chunk, each with its own online-softmax
 // state, merged in LDS at the end.
 //
-// Per 32-key tile (one v_mfma_f32_32x32x16_bf16 row block):
+// Per 32-key tile (one 32x32x16 MFMA row block):
 //   S^T[32 keys x 32 cols] = K'[keys x 16 dims] * Q'^T, one MFMA per active 16-dim pair
 //   block; columns are the G q heads (padded to 32).  With a single query position the
 //   window test depends on the key alone, so straddling pairs are handled exactly by
@@ -43,7 +44,7 @@ void decode_partial_kernel(DecodeParams p, Tables tab) {
     constexpr int P = D / 2;
     constexpr int NDB = D / 32;
     constexpr int GMAX = 16;                        // q heads per kv head (columns used)
-    __shared__ __attribute__((aligned(16))) uint16_t sQ[32][D];      // pair-blocked, bf16
+    __shared__ __attribute__((aligned(16))) uint16_t sQ[32][D];      // pair-blocked, half
     __shared__ float sO[kWaves][GMAX][D + 2];
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
@@ -59,8 +60,8 @@ void decode_partial_kernel(DecodeParams p, Tables tab) {
     const int64_t qpos = __builtin_amdgcn_readfirstlane(p.q_pos ? p.q_pos[b] : Lb - 1);
     const float sl2 = p.scale * 1.4426950408889634f;
 
-    // rotated q of the G heads (pre-scaled into log2 units), pair-blocked bf16 rows; rows
-    // >= G are zero
+    // rotated q of the G heads (pre-scaled into log2 units), pair-blocked half-precision
+    // rows; rows >= G are zero
     for (int i = tid; i < 32 * P; i += blockDim.x) {
         const int hh = i / P, pr = i % P;
         const int j = pr >> 3, e = pr & 7;
@@ -80,8 +81,8 @@ void decode_partial_kernel(DecodeParams p, Tables tab) {
             xo = (x * cs - y * sn) * sl2;
             yo = (y * cs + x * sn) * sl2;
         }
-        sQ[hh][16 * j + e] = f32_to_bf16_bits(xo);
-        sQ[hh][16 * j + 8 + e] = f32_to_bf16_bits(yo);
+        sQ[hh][16 * j + e] = f32_to_f16_bits(xo);
+        sQ[hh][16 * j + 8 + e] = f32_to_f16_bits(yo);
     }
     __syncthreads();
     // B operand of QK: column l32 = q head, half h = first/second halves of the block's pairs
@@ -167,9 +168,9 @@ void decode_partial_kernel(DecodeParams p, Tables tab) {
                 }
             }
             if (p.counter && h == 0 && key < c1) cnt += on;
-            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                        __builtin_bit_cast(bf16x8, qB[j]), S,
-                                                        0, 0, 0);
+            S = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                       __builtin_bit_cast(f16x8, qB[j]), S,
+                                                       0, 0, 0);
         }
 
         // register r of half h holds key k0 + 16(r/8) + 8h + (r%8) for column l32

@@ -1,5 +1,5 @@
 // Causal prefill with a per-RoPE-wavelength window (ATFlash abstract; WavePrune
-// original abstract), bf16 MFMA on gfx950.
+// original abstract), on gfx950 MFMA: q.k in half precision, P*V in bf16.
 //
 // Work decomposition
 //   A workgroup owns one (sequence b, kv head g, chunk of Gc q heads of that kv head) and
@@ -14,7 +14,7 @@
 //   (dmin <= W < dmax) and fully active (W >= dmax).  Because the active pairs at any
 //   distance are a suffix of the pair axis (ATFlash abstract: "a slice of the
 //   query--key contraction axis"), fully active pairs occupy a suffix of 16-dim blocks:
-//     * S^T = K'_blk * Q'_blk^T on v_mfma_f32_32x32x16_bf16 over those blocks only; the
+//     * S^T = K'_blk * Q'_blk^T on v_mfma_f32_32x32x16_f16 over those blocks only; the
 //       leading pairs of the first such block are zeroed in the Q operand;
 //     * straddling pairs are added per element on VALU with the exact test D <= W_i.
 //   Sub-tiles are visited in order of growing distance, so both band edges only move
@@ -137,14 +137,18 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
     auto POS = [&](int t) -> int { return HASPOS ? posb[t] : t; };
     const int pq = POS(qrow_c);
 
-    // ---- Q: load, round to bf16, rotate at its own position, round to bf16 (B operand)
+    // Scores are kept in log2 units: the softmax scale times log2(e) is folded into Q.
+    const float sl2 = p.scale * 1.4426950408889634f;
+
+    // ---- Q: load, round to bf16, rotate at its own position, scale, round to half (the
+    // B operand of the q.k product)
     u32x4 Qf[NB];
     {
         const int64_t qb = (((int64_t)b * N + qrow_c) * p.Hq + hq) * D;
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
             // pairs 8j..8j+7, one at a time (rolled loop: one sincos instance per block);
-            // each bf16 result enters at the top of the 128-bit block value, which shifts
+            // each 16-bit result enters at the top of the 128-bit block value, which shifts
             // down by 16 bits, so after 8 steps pair 8j+e sits in element e.
             u32x4 acc = {0u, 0u, 0u, 0u};
 #pragma unroll 1
@@ -159,7 +163,8 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
                 }
                 float sn, cs;
                 rope_sincos(pq, tab.theta[8 * j + e], &sn, &cs);
-                const uint32_t bits = f32_to_bf16_bits(h ? (y * cs + x * sn) : (x * cs - y * sn));
+                const float rot = h ? (y * cs + x * sn) : (x * cs - y * sn);
+                const uint32_t bits = f32_to_f16_bits(rot * sl2);
                 acc[0] = (acc[0] >> 16) | (acc[1] << 16);
                 acc[1] = (acc[1] >> 16) | (acc[2] << 16);
                 acc[2] = (acc[2] >> 16) | (acc[3] << 16);
@@ -176,17 +181,18 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
     const int pq_wg = POS(qs < N ? qs : N - 1);
     const int pq_lo = POS(q0 < N ? q0 : N - 1);
     const int pq_hi = POS(q0 + 31 < N ? q0 + 31 : N - 1);
-    const float sl2 = p.scale * 1.4426950408889634f;
 
     f32x16 O[NDB];
 #pragma unroll
     for (int i = 0; i < NDB; ++i) O[i] = f32x16{};
-    float m = -INFINITY, lsum = 0.f;
+    // Running row max m (log2 units) and sum.  The first sub-tile a wave visits holds the
+    // diagonal of all its rows, so m is finite from then on and later score accumulators
+    // start at -m: the MFMA then yields the exponent of exp2 directly.
+    float m = 0.f, lsum = 0.f;
+    bool started = false;
     uint64_t cnt = 0;
     int plo = 0, pfull = 0, plo_wg = 0;     // running band edges (distances only grow)
     int w_lo = tab.W[0], w_full = tab.W[0];  // W at the two edges (INT32_MAX past the end)
-    int q_key = -1;                          // pfull for which qm holds the masked block
-    u32x4 qm = {0u, 0u, 0u, 0u};
 
     // Stream key tile kt into `stage` with direct global->LDS loads (one wave instruction
     // fills 1 KB of LDS: lane l's bytes land at base + size*l).  Only the pair blocks that
@@ -243,39 +249,27 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
                 w_full = pfull < P ? tab.W[pfull] : INT32_MAX;
             }
             const int jf = pfull >> 3;
-            if (pfull != q_key && pfull < P) {
-                // first fully-active block with its leading (not fully active) pairs zeroed
-                u32x4 src = Qf[0];
+            // block jf enters with its leading nz pairs (not fully active) zeroed
+            const int nz = pfull - 8 * jf;
+            u32x4 qmask;
 #pragma unroll
-                for (int j = 1; j < NB; ++j)
-                    if (j == jf) src = Qf[j];
-                const int nz = pfull - 8 * jf;
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const uint32_t lo = (2 * t >= nz) ? 0xffffu : 0u;
-                    const uint32_t hi = (2 * t + 1 >= nz) ? 0xffff0000u : 0u;
-                    qm[t] = src[t] & (lo | hi);
-                }
-                q_key = pfull;
-            }
-            f32x16 S = f32x16{};
+            for (int t = 0; t < 4; ++t)
+                qmask[t] = ((2 * t >= nz) ? 0xffffu : 0u) | ((2 * t + 1 >= nz) ? 0xffff0000u : 0u);
 
-            // fully active blocks on MFMA: the blocks above jf with the plain Q operand, then
-            // block jf with its leading pairs zeroed (one in-place accumulator chain)
+            // fully active blocks on MFMA, top block first, accumulating onto -m
+            f32x16 S;
+            const float c0 = started ? -m : 0.f;
 #pragma unroll
-            for (int j = NB - 1; j > 0; --j) {
-                if (j > jf) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+            for (int r = 0; r < 16; ++r) S[r] = c0;
+#pragma unroll
+            for (int j = NB - 1; j >= 0; --j) {
+                if (j >= jf) {
+                    const f16x8 a = *reinterpret_cast<const f16x8*>(
                         &sK[(j * BN + 32 * sub + perm_row(l32)) * 16 + 8 * h]);
-                    S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        a, __builtin_bit_cast(bf16x8, Qf[j]), S, 0, 0, 0);
+                    const u32x4 qb = j == jf ? (Qf[j] & qmask) : Qf[j];
+                    S = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(f16x8, qb), S,
+                                                               0, 0, 0);
                 }
-            }
-            if (jf < NB) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                    &sK[(jf * BN + 32 * sub + perm_row(l32)) * 16 + 8 * h]);
-                S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, qm), S,
-                                                            0, 0, 0);
             }
 
             const bool diag = k0 + 31 > q0;
@@ -306,16 +300,16 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
                     const u32x4 qy = h ? mine : oth;
                     for (int e = e_lo; e < e_hi; ++e) {
                         const int sh = (e & 1) * 16;
-                        const float fqx = bf16_bits_to_f32((sel4(qx, e >> 1) >> sh) & 0xffffu);
-                        const float fqy = bf16_bits_to_f32((sel4(qy, e >> 1) >> sh) & 0xffffu);
+                        const float fqx = f16_bits_to_f32((sel4(qx, e >> 1) >> sh) & 0xffffu);
+                        const float fqy = f16_bits_to_f32((sel4(qy, e >> 1) >> sh) & 0xffffu);
                         const int Wi = tab.W[8 * j + e];
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
                             const int kl = 32 * sub + key_of_reg(r, h);
                             const int dist = pq - (HASPOS ? sPos[kl] : ks + kl);
                             const uint16_t* kr = &sK[(j * BN + kl) * 16];
-                            const float kx = bf16_bits_to_f32(kr[e]);
-                            const float ky = bf16_bits_to_f32(kr[8 + e]);
+                            const float kx = f16_bits_to_f32(kr[e]);
+                            const float ky = f16_bits_to_f32(kr[8 + e]);
                             const bool on = dist <= Wi;
                             S[r] += on ? (fqx * kx + fqy * ky) : 0.f;
                             if (COUNT)
@@ -331,21 +325,30 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
                 for (int r = 0; r < 16; ++r)
                     if (16 * (r >> 3) + (r & 7) > lim) S[r] = -INFINITY;
             }
+            // sub-tile max relative to m (absolute on the first sub-tile)
             float mx = S[0];
 #pragma unroll
             for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
-            mx = max_with_partner(mx, xaddr) * sl2;
-            const float m_new = fmaxf(m, mx);
-            if (__any(m_new > m + kTau)) {
-                const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+            mx = max_with_partner(mx, xaddr);
+            if (!started) {
+                m = mx;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) S[r] -= mx;
+                started = true;
+            } else if (__any(mx > kTau)) {
+                // move the max only when it grew by more than 2^kTau
+                const float shift = fmaxf(mx, 0.f);
+                const float alpha = __builtin_amdgcn_exp2f(-shift);
                 lsum *= alpha;
 #pragma unroll
                 for (int i = 0; i < NDB; ++i) O[i] *= alpha;
-                m = m_new;
+                m += shift;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) S[r] -= shift;
             }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                S[r] = __builtin_amdgcn_exp2f(fmaf(S[r], sl2, -m));
+                S[r] = __builtin_amdgcn_exp2f(S[r]);
                 lsum += S[r];
             }
 #pragma unroll

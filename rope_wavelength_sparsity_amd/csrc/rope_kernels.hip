@@ -3,7 +3,9 @@
 // Keys are rotated once, at their own position (ATFlash abstract: the RoPE score is a
 // sum over 2-D rotation pairs), and stored pair-blocked: block j of a head holds pairs
 // 8j..8j+7, as the 8 first-half components followed by the 8 second-half components,
-// [B][Hkv][d/16][tokens][16] in bf16.  One 16-element block is one bf16 MFMA K-step, so
+// [B][Hkv][d/16][tokens][16] in IEEE half precision (the rotated value of a bf16 input
+// needs more than bf16's 8 significant bits; half keeps 11, at the same MFMA rate, for
+// rotated components below 65504 in magnitude).  One 16-element block is one MFMA K-step, so
 // "contract only the active blocks" (pairs form a contiguous slice of the contraction
 // axis at every distance) reads contiguous memory for every token range.
 //
@@ -51,8 +53,8 @@ __global__ __launch_bounds__(256) void rope_keys_kernel(RopeParams p, Tables tab
         rope_sincos(pos, tab.theta[8 * j + e + 1], &s1, &c1);
         float x0 = round_bf16(x[e]), y0 = round_bf16(y[e]);
         float x1 = round_bf16(x[e + 1]), y1 = round_bf16(y[e + 1]);
-        ox[e / 2] = pack_bf16x2(x0 * c0 - y0 * s0, x1 * c1 - y1 * s1);
-        oy[e / 2] = pack_bf16x2(y0 * c0 + x0 * s0, y1 * c1 + x1 * s1);
+        ox[e / 2] = pack_f16x2(x0 * c0 - y0 * s0, x1 * c1 - y1 * s1);
+        oy[e / 2] = pack_f16x2(y0 * c0 + x0 * s0, y1 * c1 + x1 * s1);
     }
     d4[0] = u32x4{ox[0], ox[1], ox[2], ox[3]};
     d4[1] = u32x4{oy[0], oy[1], oy[2], oy[3]};

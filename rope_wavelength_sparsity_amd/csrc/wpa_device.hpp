@@ -8,6 +8,8 @@
 namespace wpa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -43,6 +45,21 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ inline uint16_t f32_to_bf16_bits(float x) {
     return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+// IEEE half precision (rotated keys and queries, the operands of the q.k product).
+__device__ inline float f16_bits_to_f32(uint32_t bits16) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+__device__ inline uint16_t f32_to_f16_bits(float x) {
+    return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+// Two floats -> packed halves (round to nearest even), `lo` in the low half.
+__device__ inline uint32_t pack_f16x2(float lo, float hi) {
+    f16x2 v = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 // Load 8 consecutive input elements (bf16 or fp32) as floats.

@@ -76,19 +76,19 @@ def test_prefill_shapes_match_oracle(shape, alpha):
 @pytest.mark.parametrize("alpha", [1.0, 2.0])
 def test_prefill_scaled_inputs(alpha):
     """Qwen2.5-0.5B-shaped inputs with the per-dim log-uniform [0.5, 2] scale on q and k at a
-    short length (1000 tokens, where rows see few keys and attention is peaked).  Rounding
-    the rotated q and k to bf16 (the MFMA operand precision) is by itself worth 1.02e-2
-    max-abs on this input (measured by emulating only that rounding in fp64 on the CPU), so
-    the max-abs bound here is 2e-2 (out and lse); the mean-abs bar stays 1e-3.  The same distribution at
-    the full 32768-token size meets 1e-2 (test_full_size_sampled_rows)."""
+    short length (1000 tokens, where rows see few keys and attention is peaked): the input
+    most sensitive to the rounding of the rotated q and k.  Rounded to bf16 they would by
+    themselves cost 1.02e-2 max-abs here (emulated in fp64 on the CPU); the kernels round
+    them to IEEE half (11 significant bits), which keeps this case inside the standard
+    bounds."""
     need_gpu()
     B, N, Hq, Hkv, d, base = 1, 1000, 14, 2, 64, 1e6
     q, k, v = synth.prefill_inputs(B, N, Hq, Hkv, d, "bf16", seed=100 + N, dim_scale=True)
     say("prefill scaled inputs", alpha)
     out, lse, cnt = _run(q, k, v, base, alpha, count=True)
     ro, rl, kept = _oracle(q, k, v, base, alpha)
-    check_close(out, ro, "out", 2e-2, 1e-3)
-    check_close(lse, rl, "lse", 2e-2, LSE_MAX)     # the same logit rounding, unattenuated
+    check_close(out, ro, "out")
+    check_close(lse, rl, "lse", LSE_MAX, LSE_MAX)
     assert cnt == kept
 
 
