@@ -75,6 +75,39 @@ __device__ inline float sum_with_partner(float v, int xaddr) {
 
 __device__ inline int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+template <int V>
+struct IntC {
+    static constexpr int value = V;
+};
+
+// f(IntC<v>{}) for a run-time v in [I, N] (a chain of scalar compares).
+template <int I, int N, class F>
+__device__ __attribute__((always_inline)) inline void dispatch(int v, F& f) {
+    if constexpr (I < N) {
+        if (v == I) f(IntC<I>{});
+        else dispatch<I + 1, N>(v, f);
+    } else {
+        f(IntC<N>{});
+    }
+}
+
+// x in all 16 registers, written as 64-bit moves.
+__device__ inline f32x16 splat16(float x) {
+    typedef uint64_t u64x8 __attribute__((ext_vector_type(8)));
+    const uint64_t x2 = ((uint64_t)__float_as_uint(x) << 32) | __float_as_uint(x);
+    const u64x8 v = {x2, x2, x2, x2, x2, x2, x2, x2};
+    return __builtin_bit_cast(f32x16, v);
+}
+
+// Leading nz pairs of an 8-pair block zeroed, as a mask on the packed block.
+__device__ inline u32x4 lead_mask(int nz) {
+    u32x4 q;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+        q[t] = ((2 * t >= nz) ? 0xffffu : 0u) | ((2 * t + 1 >= nz) ? 0xffff0000u : 0u);
+    return q;
+}
+
 struct Launch {
     int Gc, R, nhc, n_rb;
 };
@@ -88,11 +121,12 @@ struct Tile {
     static constexpr int PI = BN * 4 / 256;         // wave loads for positions
     static constexpr int CPR = BN / 8;              // 16-byte chunks per V^T row
     static constexpr int RPI = 64 / CPR;            // V^T rows per wave load
-    // Compute waves per workgroup (plus one producer wave) and the waves per SIMD that the
-    // register budget must allow: a 9-wave workgroup needs 3 per SIMD (<= 168 VGPRs), and
-    // the d=128 kernel, at up to 256 VGPRs, runs 2 per SIMD, so at most 8 waves per CU.
-    static constexpr int MAXW = D == 64 ? 8 : 7;
-    static constexpr int WAVES_PER_EU = D == 64 ? 3 : 2;
+    // Compute waves per workgroup (plus one producer wave) and the waves per SIMD the
+    // register budget must allow.  d=64 fits 128 VGPRs: 4 waves per SIMD, two 8-wave
+    // workgroups per CU (64 KB of LDS each).  d=128 needs up to 256: 2 per SIMD, one
+    // workgroup per CU.
+    static constexpr int MAXW = 7;
+    static constexpr int WAVES_PER_EU = D == 64 ? 4 : 2;
 };
 
 template <int D, bool F32, bool HASPOS, bool COUNT>
@@ -142,7 +176,11 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
 
     // ---- Q: load, round to bf16, rotate at its own position, scale, round to half (the
     // B operand of the q.k product)
-    u32x4 Qf[NB];
+    // All NB blocks as one vector value (not an array): a run-time block index then reads
+    // registers, where an array would be moved to scratch memory.
+    typedef uint32_t u32xQ __attribute__((ext_vector_type(4 * NB)));
+    u32xQ Qv;
+    auto Qf = [&](int j) -> u32x4 { return u32x4{Qv[4 * j], Qv[4 * j + 1], Qv[4 * j + 2], Qv[4 * j + 3]}; };
     {
         const int64_t qb = (((int64_t)b * N + qrow_c) * p.Hq + hq) * D;
 #pragma unroll
@@ -170,7 +208,8 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
                 acc[2] = (acc[2] >> 16) | (acc[3] << 16);
                 acc[3] = (acc[3] >> 16) | (bits << 16);
             }
-            Qf[j] = acc;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) Qv[4 * j + t] = acc[t];
         }
     }
 
@@ -193,6 +232,10 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
     uint64_t cnt = 0;
     int plo = 0, pfull = 0, plo_wg = 0;     // running band edges (distances only grow)
     int w_lo = tab.W[0], w_full = tab.W[0];  // W at the two edges (INT32_MAX past the end)
+    // Block jf = pfull/8 of Q with its leading (not fully active) pairs zeroed, valid for
+    // the band edge pfull == q_key; rebuilt only when that edge moves.
+    u32x4 qm = {0u, 0u, 0u, 0u};
+    int q_key = -1;
 
     // Stream key tile kt into `stage` with direct global->LDS loads (one wave instruction
     // fills 1 KB of LDS: lane l's bytes land at base + size*l).  Only the pair blocks that
@@ -249,25 +292,30 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
                 w_full = pfull < P ? tab.W[pfull] : INT32_MAX;
             }
             const int jf = pfull >> 3;
-            // block jf enters with its leading nz pairs (not fully active) zeroed
-            const int nz = pfull - 8 * jf;
-            u32x4 qmask;
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-                qmask[t] = ((2 * t >= nz) ? 0xffffu : 0u) | ((2 * t + 1 >= nz) ? 0xffff0000u : 0u);
+            if (pfull != q_key && jf < NB) {
+                qm = Qf(jf) & lead_mask(pfull - 8 * jf);
+                q_key = pfull;
+            }
 
-            // fully active blocks on MFMA, top block first, accumulating onto -m
-            f32x16 S;
-            const float c0 = started ? -m : 0.f;
+            // fully active blocks on MFMA, accumulating onto -m: block jf (masked) first,
+            // then the blocks above it
+            const int kbase = (32 * sub + perm_row(l32)) * 16 + 8 * h;
+            constexpr bool kHoistK = D == 64;      // read every K block up front
+            f16x8 ka[NB];
+            if constexpr (kHoistK) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) S[r] = c0;
+                for (int j = 1; j < NB; ++j) ka[j] = *reinterpret_cast<const f16x8*>(&sK[j * BN * 16 + kbase]);
+            }
+            const f16x8 kjf = *reinterpret_cast<const f16x8*>(&sK[(jf < NB ? jf : 0) * BN * 16 + kbase]);
+            f32x16 S = splat16(started ? -m : 0.f);
+            if (jf < NB)
+                S = __builtin_amdgcn_mfma_f32_32x32x16_f16(kjf, __builtin_bit_cast(f16x8, qm), S, 0, 0, 0);
 #pragma unroll
-            for (int j = NB - 1; j >= 0; --j) {
-                if (j >= jf) {
-                    const f16x8 a = *reinterpret_cast<const f16x8*>(
-                        &sK[(j * BN + 32 * sub + perm_row(l32)) * 16 + 8 * h]);
-                    const u32x4 qb = j == jf ? (Qf[j] & qmask) : Qf[j];
-                    S = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(f16x8, qb), S,
+            for (int j = NB - 1; j >= 1; --j) {
+                if (j > jf) {
+                    if constexpr (!kHoistK)
+                        ka[j] = *reinterpret_cast<const f16x8*>(&sK[j * BN * 16 + kbase]);
+                    S = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[j], __builtin_bit_cast(f16x8, Qf(j)), S,
                                                                0, 0, 0);
                 }
             }
@@ -292,7 +340,7 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
                     const int e_lo = plo - 8 * j > 0 ? plo - 8 * j : 0;
                     const int e_hi = pfull - 8 * j < 8 ? pfull - 8 * j : 8;
                     if (e_lo >= e_hi) continue;
-                    const u32x4 mine = Qf[j];
+                    const u32x4 mine = Qf(j);
                     u32x4 oth;
 #pragma unroll
                     for (int t = 0; t < 4; ++t) oth[t] = partner32(mine[t], xaddr);
@@ -347,16 +395,20 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
                 for (int r = 0; r < 16; ++r) S[r] -= shift;
             }
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                S[r] = __builtin_amdgcn_exp2f(S[r]);
-                lsum += S[r];
-            }
+            for (int r = 0; r < 16; ++r) S[r] = __builtin_amdgcn_exp2f(S[r]);
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
-                const u32x4 pb = u32x4{pack_bf16x2(S[8 * c + 0], S[8 * c + 1]),
-                                       pack_bf16x2(S[8 * c + 2], S[8 * c + 3]),
-                                       pack_bf16x2(S[8 * c + 4], S[8 * c + 5]),
-                                       pack_bf16x2(S[8 * c + 6], S[8 * c + 7])};
+                // the packed words, and the row sum of the probabilities as they enter P*V
+                // (bf16), two per instruction; the dot products take the words as scalars
+                // (taken back out of a vector, the compiler fed them one same register)
+                uint32_t wd[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    wd[t] = pack_bf16x2(S[8 * c + 2 * t], S[8 * c + 2 * t + 1]);
+                    lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wd[t]),
+                                                           __builtin_bit_cast(bf16x2, 0x3f803f80u), lsum, false);
+                }
+                const u32x4 pb = u32x4{wd[0], wd[1], wd[2], wd[3]};
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
                     const int e = 32 * db + l32, ch = 4 * sub + 2 * c + h;
