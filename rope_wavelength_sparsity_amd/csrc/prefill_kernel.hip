@@ -3,10 +3,11 @@
 //
 // Work decomposition
 //   A workgroup owns one (sequence b, kv head g, chunk of Gc q heads of that kv head) and
-//   32*R consecutive query rows; wave w handles q head (w % Gc) and the 32 rows of row
-//   group (w / Gc).  All waves share each K/V tile staged in LDS (GQA reuse).  Key tiles
-//   (BN keys) are walked from the diagonal outward through a two-stage LDS ring filled by
-//   direct global->LDS loads: tile t+1 streams in while tile t is computed.
+//   32*R consecutive query rows; compute wave w handles q head (w % Gc) and the 32 rows of
+//   row group (w / Gc).  One more wave, the producer, streams key tiles (BN keys) into a
+//   two-stage LDS ring with direct global->LDS loads, walking from the diagonal outward:
+//   tile t+1 streams in while the compute waves, sharing each tile (GQA reuse), work on
+//   tile t.  At d=64 a compute wave fits 128 VGPRs, so a CU runs two workgroups.
 //
 // Per 32x32 (query x key) sub-tile
 //   Distance band: dmin/dmax over the sub-tile's visible elements.  With the window table
@@ -19,9 +20,12 @@
 //     * straddling pairs are added per element on VALU with the exact test D <= W_i.
 //   Sub-tiles are visited in order of growing distance, so both band edges only move
 //   forward along the pair axis: they are tracked with running indices, not searched.
-//   Then causal mask, online softmax (fp32, exp2 domain with the scale folded into one
-//   FMA; the running max is only moved when it grows by more than 2^8, which leaves the
-//   result exact) and O^T += V^T P^T on MFMA.
+//   Scores are in log2 units (scale*log2 e is folded into Q), and the chain starts from
+//   -m, the running row max, supplied by one more MFMA step, so the MFMA yields the
+//   exponent of exp2 directly.  m only moves when a sub-tile exceeds it by more than 2^8
+//   (a wave-wide vote on per-lane maxima; the row max across lane halves is formed only
+//   then), which leaves the result exact.  Then causal mask, exp2, the row sum of the
+//   bf16 probabilities (two per v_dot2) and O^T += V^T P^T on MFMA.
 //
 // Register layouts (32x32x16 MFMA: A row m and B column n live in lane m%32 / n%32, the
 // 16-deep contraction is split 8+8 between lane halves; C element (row 8(r/4)+4(l/32)+r%4,
@@ -74,30 +78,6 @@ __device__ inline float sum_with_partner(float v, int xaddr) {
 }
 
 __device__ inline int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
-
-template <int V>
-struct IntC {
-    static constexpr int value = V;
-};
-
-// f(IntC<v>{}) for a run-time v in [I, N] (a chain of scalar compares).
-template <int I, int N, class F>
-__device__ __attribute__((always_inline)) inline void dispatch(int v, F& f) {
-    if constexpr (I < N) {
-        if (v == I) f(IntC<I>{});
-        else dispatch<I + 1, N>(v, f);
-    } else {
-        f(IntC<N>{});
-    }
-}
-
-// x in all 16 registers, written as 64-bit moves.
-__device__ inline f32x16 splat16(float x) {
-    typedef uint64_t u64x8 __attribute__((ext_vector_type(8)));
-    const uint64_t x2 = ((uint64_t)__float_as_uint(x) << 32) | __float_as_uint(x);
-    const u64x8 v = {x2, x2, x2, x2, x2, x2, x2, x2};
-    return __builtin_bit_cast(f32x16, v);
-}
 
 // Leading nz pairs of an 8-pair block zeroed, as a mask on the packed block.
 __device__ inline u32x4 lead_mask(int nz) {
@@ -225,10 +205,23 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
 #pragma unroll
     for (int i = 0; i < NDB; ++i) O[i] = f32x16{};
     // Running row max m (log2 units) and sum.  The first sub-tile a wave visits holds the
-    // diagonal of all its rows, so m is finite from then on and later score accumulators
-    // start at -m: the MFMA then yields the exponent of exp2 directly.
+    // diagonal of all its rows, so m is finite from then on; later score accumulators
+    // start at -m, so the MFMA yields the exponent of exp2 directly.  The -m start is one
+    // more MFMA step: a constant A block with 1 and 2048 in its first two columns (lanes of
+    // half 0) against a B block holding -lo and -hi per query, m = 2048*hi + lo with hi, lo
+    // half-precision values (m is kept at exactly that value; |m| < 1.3e8).
     float m = 0.f, lsum = 0.f;
     bool started = false;
+    const u32x4 ones_blk = h ? u32x4{0u, 0u, 0u, 0u} : u32x4{0x68003c00u, 0u, 0u, 0u};   // (1, 2048)
+    u32x4 negm_blk = {0u, 0u, 0u, 0u};
+    auto set_m = [&](float mv) {
+        const _Float16 hi = (_Float16)(mv * (1.0f / 2048.0f));
+        const _Float16 lo = (_Float16)(mv - 2048.0f * (float)hi);
+        m = 2048.0f * (float)hi + (float)lo;
+        const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)-lo) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)-hi) << 16);
+        negm_blk[0] = h ? 0u : w0;
+    };
     uint64_t cnt = 0;
     int plo = 0, pfull = 0, plo_wg = 0;     // running band edges (distances only grow)
     int w_lo = tab.W[0], w_full = tab.W[0];  // W at the two edges (INT32_MAX past the end)
@@ -300,23 +293,18 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
             // fully active blocks on MFMA, accumulating onto -m: block jf (masked) first,
             // then the blocks above it
             const int kbase = (32 * sub + perm_row(l32)) * 16 + 8 * h;
-            constexpr bool kHoistK = D == 64;      // read every K block up front
-            f16x8 ka[NB];
-            if constexpr (kHoistK) {
-#pragma unroll
-                for (int j = 1; j < NB; ++j) ka[j] = *reinterpret_cast<const f16x8*>(&sK[j * BN * 16 + kbase]);
-            }
+            // (K fragments are read next to their MFMA: reading every block up front costs the
+            // d=64 kernel its fourth wave per SIMD, which hides more latency than it saves)
             const f16x8 kjf = *reinterpret_cast<const f16x8*>(&sK[(jf < NB ? jf : 0) * BN * 16 + kbase]);
-            f32x16 S = splat16(started ? -m : 0.f);
+            f32x16 S = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                __builtin_bit_cast(f16x8, ones_blk), __builtin_bit_cast(f16x8, negm_blk), f32x16{}, 0, 0, 0);
             if (jf < NB)
                 S = __builtin_amdgcn_mfma_f32_32x32x16_f16(kjf, __builtin_bit_cast(f16x8, qm), S, 0, 0, 0);
 #pragma unroll
             for (int j = NB - 1; j >= 1; --j) {
                 if (j > jf) {
-                    if constexpr (!kHoistK)
-                        ka[j] = *reinterpret_cast<const f16x8*>(&sK[j * BN * 16 + kbase]);
-                    S = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[j], __builtin_bit_cast(f16x8, Qf(j)), S,
-                                                               0, 0, 0);
+                    const f16x8 a = *reinterpret_cast<const f16x8*>(&sK[j * BN * 16 + kbase]);
+                    S = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(f16x8, Qf(j)), S, 0, 0, 0);
                 }
             }
 
@@ -373,24 +361,27 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
                 for (int r = 0; r < 16; ++r)
                     if (16 * (r >> 3) + (r & 7) > lim) S[r] = -INFINITY;
             }
-            // sub-tile max relative to m (absolute on the first sub-tile)
+            // sub-tile max relative to m (absolute on the first sub-tile) over this half's
+            // keys; the row max (both halves) is only formed when m moves
             float mx = S[0];
 #pragma unroll
             for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
-            mx = max_with_partner(mx, xaddr);
             if (!started) {
-                m = mx;
+                mx = max_with_partner(mx, xaddr);
+                set_m(mx);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) S[r] -= mx;
+                for (int r = 0; r < 16; ++r) S[r] -= m;
                 started = true;
             } else if (__any(mx > kTau)) {
                 // move the max only when it grew by more than 2^kTau
-                const float shift = fmaxf(mx, 0.f);
+                mx = max_with_partner(mx, xaddr);
+                const float m_old = m;
+                set_m(m + fmaxf(mx, 0.f));
+                const float shift = m - m_old;
                 const float alpha = __builtin_amdgcn_exp2f(-shift);
                 lsum *= alpha;
 #pragma unroll
                 for (int i = 0; i < NDB; ++i) O[i] *= alpha;
-                m += shift;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) S[r] -= shift;
             }
