@@ -49,6 +49,11 @@ def _parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the headline line: the speedup sweep over alpha in {1, 2, inf} "
+                         "at N = 32K..1M for the Llama-3.2-3B and Qwen2.5-7B-1M shapes, prefill "
+                         "and decode (B=1 and B=16), printed as one JSON line")
+    ap.add_argument("--sweep-max", type=int, default=1 << 20, help="largest N of the sweep")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (twice), as the "
                          "reference kernel for scaling FETCH_SIZE/WRITE_SIZE counters")
@@ -164,6 +169,121 @@ def cpu_baseline(w, alpha, target_s):
                 n, w.Hq, w.name, w.N, dt)}
 
 
+def _log(*a):
+    print("#", *a, file=sys.stderr, flush=True)
+
+
+def sweep_prefill(w, N, alphas, reps):
+    """Prefill at length N for each alpha: prepare + attend timed per rep (HIP events), the
+    attend kernel alone as well.  Returns a list of result dicts."""
+    import torch
+    import rope_wavelength_sparsity_amd as wpa
+    import synth
+    q, k, v = synth.workload_inputs(w, device="cuda", N=N)
+    ws = torch.empty(wpa.prefill_workspace_bytes(w.B, N, w.Hkv, w.d), device="cuda",
+                     dtype=torch.uint8)
+    out = torch.empty_like(q)
+    res = []
+    for alpha in alphas:
+        wpa.prefill_prepare(k, v, w.base, workspace=ws)          # warm-up
+        wpa.prefill_attend(q, ws, w.Hkv, w.base, alpha, out=out)
+        torch.cuda.synchronize()
+        ev = _events(3 * reps)
+        for i in range(reps):
+            ev[3 * i].record()
+            wpa.prefill_prepare(k, v, w.base, workspace=ws)
+            ev[3 * i + 1].record()
+            wpa.prefill_attend(q, ws, w.Hkv, w.base, alpha, out=out)
+            ev[3 * i + 2].record()
+        torch.cuda.synchronize()
+        step = sorted(ev[3 * i].elapsed_time(ev[3 * i + 2]) for i in range(reps))[reps // 2]
+        kern = sorted(ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) for i in range(reps))[reps // 2]
+        kept, total = wpa.count_terms(w.d, w.base, alpha, N, 0, N)
+        flops = w.B * w.Hq * (4 * kept + 2 * w.d * N * (N + 1) // 2)
+        r = {"kind": "prefill", "shape": w.name, "N": N, "alpha": alpha, "reps": reps,
+             "attend_ms": kern, "step_ms": step, "flops": flops,
+             "kept_fraction": kept / total, "attend_tflops": flops / (kern * 1e-3) / 1e12}
+        _log("prefill %s N=%d alpha=%g: attend %.2f ms (%.0f TFLOP/s), step %.2f ms" % (
+            w.name, N, alpha, kern, r["attend_tflops"], step))
+        res.append(r)
+    del q, k, v, ws, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def sweep_decode(w, B, L, alphas, reps):
+    """One decode step of B sequences all at kv_len L, for each alpha; the 256 MB last-level
+    cache is flushed by a 1 GB write before every timed call."""
+    import torch
+    import rope_wavelength_sparsity_amd as wpa
+    import synth
+    cache = wpa.KVCache(B, L, w.Hkv, w.d, w.base)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(w.seed)
+    chunk = max(1, min(L, (1 << 30) // (B * w.Hkv * w.d * 4)))
+    for t0 in range(0, L, chunk):                 # fill the caches chunk by chunk
+        n = min(chunk, L - t0)
+        k = torch.randn((B, n, w.Hkv, w.d), generator=g, device="cuda").to(torch.bfloat16)
+        v = torch.randn((B, n, w.Hkv, w.d), generator=g, device="cuda").to(torch.bfloat16)
+        cache.write(k, v, t0)
+        del k, v
+    q = torch.randn((B, w.Hq, w.d), generator=g, device="cuda").to(torch.bfloat16)
+    lens = torch.full((B,), L, dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(wpa.decode_workspace_bytes(B, L, w.Hq, w.Hkv, w.d), 16), device="cuda",
+                     dtype=torch.uint8)
+    out = torch.empty_like(q)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    res = []
+    for alpha in alphas:
+        wpa.decode(q, cache, lens, alpha, out=out, workspace=ws)
+        ts = []
+        for _ in range(reps):
+            flush.zero_()
+            a, b = _events(2)
+            a.record()
+            wpa.decode(q, cache, lens, alpha, out=out, workspace=ws)
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        ms = sorted(ts)[reps // 2]
+        kept, _ = wpa.count_terms(w.d, w.base, alpha, 1, L - 1, L)
+        nbytes = B * w.Hkv * (4 * kept + 2 * w.d * L) + 2 * 2 * B * w.Hq * w.d
+        r = {"kind": "decode", "shape": w.name, "B": B, "L": L, "alpha": alpha, "reps": reps,
+             "ms": ms, "bytes": nbytes, "gbs": nbytes / (ms * 1e-3) / 1e9}
+        _log("decode %s B=%d L=%d alpha=%g: %.3f ms (%.0f GB/s)" % (w.name, B, L, alpha, ms, r["gbs"]))
+        res.append(r)
+    del cache, q, ws, out, flush
+    torch.cuda.empty_cache()
+    return res
+
+
+def sweep(max_n):
+    """Speedup over the full window (alpha = inf) across lengths, prefill and decode."""
+    import synth
+    alphas = (1.0, 2.0, math.inf)
+    lengths = [n for n in (1 << 15, 1 << 16, 1 << 17, 1 << 18, 1 << 19, 1 << 20) if n <= max_n]
+    rows = []
+    for name in ("llama3b", "qwen7b1m"):
+        w = synth.WORKLOADS[name]
+        for N in lengths:
+            rows += sweep_prefill(w, N, alphas, 3 if N >= (1 << 19) else 5)
+        for B in (1, 16):
+            for L in lengths:
+                rows += sweep_decode(w, B, L, alphas, 10)
+    speed = []
+    key = lambda r: (r["kind"], r["shape"], r.get("B", 1), r.get("N", r.get("L")))
+    for r in rows:
+        if math.isinf(r["alpha"]):
+            continue
+        full = [x for x in rows if key(x) == key(r) and math.isinf(x["alpha"])][0]
+        t, tf = (r["attend_ms"], full["attend_ms"]) if r["kind"] == "prefill" else (r["ms"], full["ms"])
+        speed.append({"kind": r["kind"], "shape": r["shape"], "B": r.get("B", 1),
+                      "N": r.get("N", r.get("L")), "alpha": r["alpha"], "speedup": tf / t})
+    return {"sweep": {"rows": rows, "speedup_vs_full_window": speed,
+                      "timing": "median of reps; HIP events; decode after a 1 GB cache flush",
+                      "data": "synthetic N(0,1) bf16 tensors (seeded)"}}
+
+
 def _traffic(kernel_file, workload, alpha):
     """HBM bytes per launch from committed rocprofv3 counter runs, if the kernel source is
     unchanged since they were taken."""
@@ -189,6 +309,9 @@ def main():
     import torch
     import synth
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.sweep:
+        print(json.dumps(sweep(args.sweep_max)), flush=True)
+        return
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda")
