@@ -168,6 +168,57 @@ int wpa_decode(const void* q, const void* k_cache, const void* v_cache, const in
                int32_t dtype, int32_t out_dtype, unsigned long long* term_count,
                int32_t chunk_keys, void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * RoPE variants.  The pages state the window for RoPE with frequencies base^(-2i/d) on
+ * half-split pairs; models that scale their frequencies (Llama-3-style per-band scaling,
+ * NTK or YaRN variants) or pair adjacent dims use the same window with their own per-pair
+ * wavelength lambda_i = 2*pi/theta_i (ATFlash abstract: the window is proportional to each
+ * pair's wavelength).
+ *   pairs     WPA_PAIRS_HALF: pair i = dims (i, i + d/2); WPA_PAIRS_INTERLEAVED: (2i, 2i + 1).
+ *   inv_freq  host array of the d/2 rotation frequencies theta_i (radians per position),
+ *             finite, > 0 and non-increasing in i (so that the pairs active at a distance
+ *             stay a suffix of the pair axis), or NULL for theta_i = base^(-2i/d).  With a
+ *             table the window test is D <= alpha * ((2.0*M_PI) / theta_i) in IEEE double,
+ *             and `base` is not used.  The table is read during the call only.
+ * Every *_ex entry point below is its namesake with this description added; rope = NULL
+ * means {WPA_PAIRS_HALF, NULL}.  A table that is not positive and non-increasing is
+ * WPA_ERR_UNSUPPORTED; an unknown `pairs` value WPA_ERR_INVALID.  The decode caches hold
+ * keys rotated by the description given to wpa_kv_write_ex; wpa_decode_ex must be given
+ * the same one (q is rotated by it).
+ */
+enum { WPA_PAIRS_HALF = 0, WPA_PAIRS_INTERLEAVED = 1 };
+
+typedef struct wpa_rope {
+    int32_t pairs;
+    const double* inv_freq;
+} wpa_rope_t;
+
+int wpa_count_terms_ex(int32_t d, double base, const wpa_rope_t* rope, double alpha, int64_t n_q,
+                       int64_t q_pos0, int64_t n_k, int64_t* kept, int64_t* total);
+int wpa_thresholds_ex(int32_t d, double base, const wpa_rope_t* rope, double alpha, int32_t* W);
+int wpa_prefill_ex(const void* q, const void* k, const void* v, void* out, float* lse,
+                   const int32_t* positions, int32_t B, int64_t N, int32_t Hq, int32_t Hkv,
+                   int32_t d, double base, const wpa_rope_t* rope, double alpha, float scale,
+                   int32_t dtype, int32_t out_dtype, unsigned long long* term_count,
+                   void* workspace, size_t ws_bytes, void* stream);
+int wpa_prefill_prepare_ex(const void* k, const void* v, const int32_t* positions, int32_t B,
+                           int64_t N, int32_t Hkv, int32_t d, double base, const wpa_rope_t* rope,
+                           int32_t dtype, void* workspace, size_t ws_bytes, void* stream);
+int wpa_prefill_attend_ex(const void* q, void* out, float* lse, const int32_t* positions,
+                          int32_t B, int64_t N, int32_t Hq, int32_t Hkv, int32_t d, double base,
+                          const wpa_rope_t* rope, double alpha, float scale, int32_t dtype,
+                          int32_t out_dtype, unsigned long long* term_count,
+                          const void* workspace, size_t ws_bytes, void* stream);
+int wpa_kv_write_ex(const void* k, const void* v, int64_t start, int64_t n, void* k_cache,
+                    void* v_cache, int32_t B, int64_t Lmax, int32_t Hkv, int32_t d, double base,
+                    const wpa_rope_t* rope, int32_t dtype, void* stream);
+int wpa_decode_ex(const void* q, const void* k_cache, const void* v_cache, const int32_t* kv_len,
+                  const int32_t* q_pos, void* out, float* lse, int32_t B, int64_t Lmax,
+                  int32_t Hq, int32_t Hkv, int32_t d, double base, const wpa_rope_t* rope,
+                  double alpha, float scale, int32_t dtype, int32_t out_dtype,
+                  unsigned long long* term_count, int32_t chunk_keys, void* workspace,
+                  size_t ws_bytes, void* stream);
+
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char* wpa_last_error(void);
 

@@ -13,7 +13,9 @@ the query-key distance is <= alpha*lambda_i.  Online softmax and P.V are unchang
 Parity status of each function (what pins it is listed in the design notes and in
 ``tests/test_oracle_pins.py``):
   prefill / prefill_rows / decode -- pinned (full-window library SDPA, complex relative
-      form, alpha=0 closed form, hand-derived two-token cases, shift invariance, GQA)
+      form, alpha=0 closed form, hand-derived two-token cases, shift invariance, GQA);
+      with a frequency table or the interleaved layout: full-window SDPA on complex-rotated
+      inputs, the complex relative form with the table, and the layout permutation identity
   count_enumerate / count_bruteforce / count_by_distance -- pinned against each other
       (three independent enumerations) and against closed-form asymptotics.
 """
@@ -52,16 +54,17 @@ def _load():
         build()
         lib = ctypes.CDLL(_LIB)
         P, I, I64, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
-        lib.orc_prefill.argtypes = [P, P, P, I, P, I, I64, I, I, I, D, D, D, P, I64, P, P, P, I]
-        lib.orc_prefill.restype = I
-        lib.orc_decode.argtypes = [P, P, P, I, P, P, I, I64, I, I, I, D, D, D, P, P, P, I]
-        lib.orc_decode.restype = I
-        lib.orc_rope.argtypes = [P, I, I64, I, I, P, D, P]
-        lib.orc_rope.restype = None
-        lib.orc_thresholds.argtypes = [I, D, D, P]
-        lib.orc_thresholds.restype = None
-        lib.orc_count_enumerate.argtypes = [I, D, D, I64, I64, I64, P, P]
-        lib.orc_count_enumerate.restype = None
+        lib.orc_prefill_ex.argtypes = [P, P, P, I, P, I, I64, I, I, I, D, P, I, D, D, P, I64, P, P,
+                                       P, I]
+        lib.orc_prefill_ex.restype = I
+        lib.orc_decode_ex.argtypes = [P, P, P, I, P, P, I, I64, I, I, I, D, P, I, D, D, P, P, P, I]
+        lib.orc_decode_ex.restype = I
+        lib.orc_rope_ex.argtypes = [P, I, I64, I, I, P, D, P, I, P]
+        lib.orc_rope_ex.restype = None
+        lib.orc_thresholds_ex.argtypes = [I, D, P, D, P]
+        lib.orc_thresholds_ex.restype = None
+        lib.orc_count_enumerate_ex.argtypes = [I, D, P, D, I64, I64, I64, P, P]
+        lib.orc_count_enumerate_ex.restype = None
         _lib = lib
     return _lib
 
@@ -80,26 +83,42 @@ def _as_input(x):
     raise TypeError("oracle inputs are float32 or uint16 (bf16 bits), got %s" % x.dtype)
 
 
-def thresholds(d: int, base: float, alpha: float) -> np.ndarray:
-    """alpha*lambda_i for i < d/2, in double (may be +inf)."""
+LAYOUTS = {"half": 0, "interleaved": 1}
+
+
+def _freq(inv_freq, d):
+    """Optional per-pair rotation frequencies th_i (a d/2 float64 table), else None."""
+    if inv_freq is None:
+        return None
+    f = np.ascontiguousarray(inv_freq, dtype=np.float64)
+    assert f.shape == (d // 2,)
+    return f
+
+
+def thresholds(d: int, base: float, alpha: float, inv_freq=None) -> np.ndarray:
+    """alpha*lambda_i for i < d/2, in double (may be +inf); lambda_i = 2*pi*base^(2i/d), or
+    2*pi/th_i for a given frequency table."""
     out = np.empty(d // 2, dtype=np.float64)
-    _load().orc_thresholds(d, float(base), float(alpha), _ptr(out))
+    _load().orc_thresholds_ex(d, float(base), _ptr(_freq(inv_freq, d)), float(alpha), _ptr(out))
     return out
 
 
-def rope(x, pos, base: float) -> np.ndarray:
+def rope(x, pos, base: float, inv_freq=None, layout: str = "half") -> np.ndarray:
     """Rotate x [T][H][d] (fp32 or bf16 bits) at positions pos[T]; returns fp64."""
     x, dt = _as_input(x)
     T, H, d = x.shape
     pos = np.ascontiguousarray(pos, dtype=np.int64)
     out = np.empty((T, H, d), dtype=np.float64)
-    _load().orc_rope(_ptr(x), dt, T, H, d, _ptr(pos), float(base), _ptr(out))
+    _load().orc_rope_ex(_ptr(x), dt, T, H, d, _ptr(pos), float(base), _ptr(_freq(inv_freq, d)),
+                        LAYOUTS[layout], _ptr(out))
     return out
 
 
 def prefill(q, k, v, base: float, alpha: float, scale: float | None = None, pos=None,
-            rows=None, nthreads: int = 0):
+            rows=None, nthreads: int = 0, inv_freq=None, layout: str = "half"):
     """Causal windowed prefill.  q [B][N][Hq][d], k/v [B][N][Hkv][d] (same dtype).
+    inv_freq: optional d/2 rotation frequencies (else base^(-2i/d)); layout: "half"
+    (pair i = dims i, i+d/2) or "interleaved" (dims 2i, 2i+1).
 
     Returns (out [B][R][Hq][d], lse [B][Hq][R], kept) in fp64, R = len(rows) or N.
     """
@@ -121,17 +140,19 @@ def prefill(q, k, v, base: float, alpha: float, scale: float | None = None, pos=
     out = np.empty((B, R, Hq, d), dtype=np.float64)
     lse = np.empty((B, Hq, R), dtype=np.float64)
     kept = ctypes.c_int64(0)
-    rc = _load().orc_prefill(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(pos), B, N, Hq, Hkv, d,
-                             float(base), float(alpha), float(scale), _ptr(rows), R,
-                             _ptr(out), _ptr(lse), ctypes.byref(kept), int(nthreads))
+    rc = _load().orc_prefill_ex(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(pos), B, N, Hq, Hkv, d,
+                                float(base), _ptr(_freq(inv_freq, d)), LAYOUTS[layout],
+                                float(alpha), float(scale), _ptr(rows), R,
+                                _ptr(out), _ptr(lse), ctypes.byref(kept), int(nthreads))
     if rc != 0:
         raise ValueError("orc_prefill rejected its arguments")
     return out, lse, kept.value
 
 
 def decode(q, k, v, kv_len, base: float, alpha: float, scale: float | None = None,
-           q_pos=None, nthreads: int = 0):
-    """One decode step.  q [B][Hq][d]; k/v pre-RoPE cache [B][Lmax][Hkv][d]; kv_len [B]."""
+           q_pos=None, nthreads: int = 0, inv_freq=None, layout: str = "half"):
+    """One decode step.  q [B][Hq][d]; k/v pre-RoPE cache [B][Lmax][Hkv][d]; kv_len [B];
+    inv_freq and layout as for prefill."""
     q, dt = _as_input(q)
     k, _ = _as_input(k)
     v, _ = _as_input(v)
@@ -145,9 +166,10 @@ def decode(q, k, v, kv_len, base: float, alpha: float, scale: float | None = Non
     out = np.empty((B, Hq, d), dtype=np.float64)
     lse = np.empty((B, Hq), dtype=np.float64)
     kept = ctypes.c_int64(0)
-    rc = _load().orc_decode(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(kv_len), _ptr(q_pos), B, Lmax,
-                            Hq, Hkv, d, float(base), float(alpha), float(scale), _ptr(out),
-                            _ptr(lse), ctypes.byref(kept), int(nthreads))
+    rc = _load().orc_decode_ex(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(kv_len), _ptr(q_pos), B, Lmax,
+                               Hq, Hkv, d, float(base), _ptr(_freq(inv_freq, d)), LAYOUTS[layout],
+                               float(alpha), float(scale), _ptr(out), _ptr(lse),
+                               ctypes.byref(kept), int(nthreads))
     if rc != 0:
         raise ValueError("orc_decode rejected its arguments")
     return out, lse, kept.value
@@ -159,17 +181,18 @@ def decode(q, k, v, kv_len, base: float, alpha: float, scale: float | None = Non
 # indices, key c visible to query r iff c <= r.  Three independent enumerations.
 # --------------------------------------------------------------------------------------
 
-def count_enumerate(d, base, alpha, n_q, q0, n_k):
+def count_enumerate(d, base, alpha, n_q, q0, n_k, inv_freq=None):
     """C loop over every (r, c, i).  Returns (kept, total)."""
     kept, total = ctypes.c_int64(0), ctypes.c_int64(0)
-    _load().orc_count_enumerate(int(d), float(base), float(alpha), int(n_q), int(q0),
-                                int(n_k), ctypes.byref(kept), ctypes.byref(total))
+    _load().orc_count_enumerate_ex(int(d), float(base), _ptr(_freq(inv_freq, d)), float(alpha),
+                                   int(n_q), int(q0), int(n_k), ctypes.byref(kept),
+                                   ctypes.byref(total))
     return kept.value, total.value
 
 
-def count_bruteforce(d, base, alpha, n_q, q0, n_k):
+def count_bruteforce(d, base, alpha, n_q, q0, n_k, inv_freq=None):
     """numpy: materialise the (r, c) distance matrix and test every pair.  O(n_q*n_k*d/2)."""
-    thr = thresholds(d, base, alpha)
+    thr = thresholds(d, base, alpha, inv_freq)
     r = np.arange(q0, q0 + n_q, dtype=np.int64)[:, None]
     c = np.arange(n_k, dtype=np.int64)[None, :]
     visible = c <= r
@@ -180,11 +203,11 @@ def count_bruteforce(d, base, alpha, n_q, q0, n_k):
     return kept, int(np.count_nonzero(visible)) * (d // 2)
 
 
-def count_by_distance(d, base, alpha, n_q, q0, n_k):
+def count_by_distance(d, base, alpha, n_q, q0, n_k, inv_freq=None):
     """numpy: histogram of distances.  For each distance D, the number of visible (r, c)
     with r - c = D is the size of r in [max(q0, D), min(q0+n_q-1, n_k-1+D)].
     O((q0+n_q) * d/2), exact in int64."""
-    thr = thresholds(d, base, alpha)
+    thr = thresholds(d, base, alpha, inv_freq)
     D = np.arange(0, q0 + n_q, dtype=np.int64)
     lo = np.maximum(q0, D)
     hi = np.minimum(q0 + n_q - 1, n_k - 1 + D)

@@ -33,6 +33,12 @@
  *     th_i = base^(-2i/d), angle formed in double, libm cos/sin;
  *   - decode: the one query sits at token index kv_len-1 (its own key included).
  *
+ * RoPE variants (the `_ex` entry points): a caller-given frequency table th_i
+ * (frequency-scaled RoPE, e.g. Llama-3 style, carries its own per-pair
+ * frequencies), with wavelength lambda_i = 2*pi/th_i evaluated in IEEE double as
+ * alpha * ((2.0*M_PI) / th_i); and the interleaved pair layout, pair i = dims
+ * (2i, 2i+1), rotated by the same formulas.
+ *
  * Inputs are the exact values the GPU consumes (bf16 bit patterns as uint16, or
  * fp32); step 1 upcasts them to double.  All arithmetic is double.
  */
@@ -56,40 +62,56 @@ static double orc_load(const void* base_ptr, int dtype, int64_t idx) {
     return (double)f;
 }
 
-/* Step 2: per-pair window thresholds alpha*lambda_i (may be +inf). */
-void orc_thresholds(int d, double base, double alpha, double* thr) {
+/* The two head dims of pair i: (i, i + d/2) half-split, (2i, 2i + 1) interleaved. */
+static int orc_dim_x(int i, int d, int interleaved) { return interleaved ? 2 * i : i; }
+static int orc_dim_y(int i, int d, int interleaved) { return interleaved ? 2 * i + 1 : i + d / 2; }
+
+/* Step 2: per-pair window thresholds alpha*lambda_i (may be +inf); lambda_i from
+ * base, or 2*pi/th_i for a given frequency table. */
+void orc_thresholds_ex(int d, double base, const double* inv_freq, double alpha, double* thr) {
     for (int i = 0; i < d / 2; ++i) {
-        double lam = (2.0 * M_PI) * pow(base, (2.0 * i) / (double)d);
+        double lam = inv_freq ? (2.0 * M_PI) / inv_freq[i]
+                              : (2.0 * M_PI) * pow(base, (2.0 * i) / (double)d);
         thr[i] = alpha * lam;
     }
 }
 
-/* Rotation frequencies th_i = base^(-2i/d). */
-static void orc_freqs(int d, double base, double* th) {
-    for (int i = 0; i < d / 2; ++i) th[i] = pow(base, -(2.0 * i) / (double)d);
+void orc_thresholds(int d, double base, double alpha, double* thr) {
+    orc_thresholds_ex(d, base, NULL, alpha, thr);
 }
 
-/* Step 3: rotate n_tok tokens x[n_tok][H][d] at positions pos[n_tok] (half-split). */
-void orc_rope(const void* x, int dtype, int64_t n_tok, int H, int d,
-              const int64_t* pos, double base, double* out) {
+/* Rotation frequencies: th_i = base^(-2i/d), or the given table. */
+static void orc_freqs(int d, double base, const double* inv_freq, double* th) {
+    for (int i = 0; i < d / 2; ++i) th[i] = inv_freq ? inv_freq[i] : pow(base, -(2.0 * i) / (double)d);
+}
+
+/* Step 3: rotate n_tok tokens x[n_tok][H][d] at positions pos[n_tok]. */
+void orc_rope_ex(const void* x, int dtype, int64_t n_tok, int H, int d, const int64_t* pos,
+                 double base, const double* inv_freq, int interleaved, double* out) {
     int P = d / 2;
     double* th = (double*)malloc(sizeof(double) * P);
-    orc_freqs(d, base, th);
+    orc_freqs(d, base, inv_freq, th);
     #pragma omp parallel for schedule(static)
     for (int64_t t = 0; t < n_tok; ++t) {
         for (int h = 0; h < H; ++h) {
             int64_t row = (t * H + h) * (int64_t)d;
             for (int i = 0; i < P; ++i) {
+                int ix = orc_dim_x(i, d, interleaved), iy = orc_dim_y(i, d, interleaved);
                 double a = (double)pos[t] * th[i];
                 double c = cos(a), s = sin(a);
-                double x0 = orc_load(x, dtype, row + i);
-                double x1 = orc_load(x, dtype, row + i + P);
-                out[row + i] = x0 * c - x1 * s;
-                out[row + i + P] = x1 * c + x0 * s;
+                double x0 = orc_load(x, dtype, row + ix);
+                double x1 = orc_load(x, dtype, row + iy);
+                out[row + ix] = x0 * c - x1 * s;
+                out[row + iy] = x1 * c + x0 * s;
             }
         }
     }
     free(th);
+}
+
+void orc_rope(const void* x, int dtype, int64_t n_tok, int H, int d,
+              const int64_t* pos, double base, double* out) {
+    orc_rope_ex(x, dtype, n_tok, H, d, pos, base, NULL, 0, out);
 }
 
 /* Steps 4-5 for one query row: windowed logits over visible keys 0..last,
@@ -100,7 +122,8 @@ void orc_rope(const void* x, int dtype, int64_t n_tok, int H, int d,
  * Returns the number of kept (key, pair) terms for this row. */
 static int64_t orc_row(const double* qr, int64_t qpos, const double* kr, const int64_t* kpos,
                        const void* v, int dtype, int64_t last, int Hkv, int g, int d,
-                       const double* thr, double scale, double* logit, double* out, double* lse) {
+                       int interleaved, const double* thr, double scale, double* logit,
+                       double* out, double* lse) {
     int P = d / 2;
     int64_t kept = 0;
     double m = -INFINITY;
@@ -110,7 +133,8 @@ static int64_t orc_row(const double* qr, int64_t qpos, const double* kr, const i
         double s = 0.0;
         for (int i = 0; i < P; ++i) {
             if (dist <= thr[i]) {
-                s += qr[i] * k[i] + qr[i + P] * k[i + P];
+                int ix = orc_dim_x(i, d, interleaved), iy = orc_dim_y(i, d, interleaved);
+                s += qr[ix] * k[ix] + qr[iy] * k[iy];
                 ++kept;
             }
         }
@@ -138,10 +162,11 @@ static int64_t orc_row(const double* qr, int64_t qpos, const double* kr, const i
  *   kept_out (nullable): total kept (query, key, pair) terms over all evaluated rows/heads.
  * Returns 0, or -1 on bad arguments.
  */
-int orc_prefill(const void* q, const void* k, const void* v, int dtype, const int32_t* pos,
-                int B, int64_t N, int Hq, int Hkv, int d, double base, double alpha,
-                double scale, const int64_t* rows, int64_t n_rows,
-                double* out, double* lse, int64_t* kept_out, int nthreads) {
+int orc_prefill_ex(const void* q, const void* k, const void* v, int dtype, const int32_t* pos,
+                   int B, int64_t N, int Hq, int Hkv, int d, double base,
+                   const double* inv_freq, int interleaved, double alpha,
+                   double scale, const int64_t* rows, int64_t n_rows,
+                   double* out, double* lse, int64_t* kept_out, int nthreads) {
     if (B < 1 || N < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || d < 2 || d % 2 != 0)
         return -1;
     if (!rows) n_rows = N;
@@ -151,7 +176,7 @@ int orc_prefill(const void* q, const void* k, const void* v, int dtype, const in
     int G = Hq / Hkv;
     int P = d / 2;
     double* thr = (double*)malloc(sizeof(double) * P);
-    orc_thresholds(d, base, alpha, thr);
+    orc_thresholds_ex(d, base, inv_freq, alpha, thr);
     int64_t* p64 = (int64_t*)malloc(sizeof(int64_t) * N);
     double* kr = (double*)malloc(sizeof(double) * N * Hkv * d);
     double* qr = (double*)malloc(sizeof(double) * n_rows * Hq * d);
@@ -159,8 +184,8 @@ int orc_prefill(const void* q, const void* k, const void* v, int dtype, const in
     int64_t kept_total = 0;
     for (int b = 0; b < B; ++b) {
         for (int64_t t = 0; t < N; ++t) p64[t] = pos ? (int64_t)pos[(int64_t)b * N + t] : t;
-        orc_rope((const char*)k + (dtype == ORC_FP32 ? 4 : 2) * (int64_t)b * N * Hkv * d, dtype,
-                 N, Hkv, d, p64, base, kr);
+        orc_rope_ex((const char*)k + (dtype == ORC_FP32 ? 4 : 2) * (int64_t)b * N * Hkv * d, dtype,
+                    N, Hkv, d, p64, base, inv_freq, interleaved, kr);
         /* gather the evaluated query rows, then rotate them at their own positions */
         const char* qb = (const char*)q + (dtype == ORC_FP32 ? 4 : 2) * (int64_t)b * N * Hq * d;
         int esz = dtype == ORC_FP32 ? 4 : 2;
@@ -170,7 +195,7 @@ int orc_prefill(const void* q, const void* k, const void* v, int dtype, const in
             memcpy(qsel + (size_t)esz * j * Hq * d, qb + (size_t)esz * r * Hq * d, (size_t)esz * Hq * d);
             qp[j] = p64[r];
         }
-        orc_rope(qsel, dtype, n_rows, Hq, d, qp, base, qr);
+        orc_rope_ex(qsel, dtype, n_rows, Hq, d, qp, base, inv_freq, interleaved, qr);
         free(qsel);
         const char* vb = (const char*)v + (size_t)esz * b * N * Hkv * d;
         int64_t kept_b = 0;
@@ -184,7 +209,7 @@ int orc_prefill(const void* q, const void* k, const void* v, int dtype, const in
                     double* o = out + (((int64_t)b * n_rows + j) * Hq + h) * d;
                     double* l = lse + ((int64_t)b * Hq + h) * n_rows + j;
                     kept_b += orc_row(qr + (j * Hq + h) * (int64_t)d, qp[j], kr, p64, vb, dtype,
-                                      r, Hkv, h / G, d, thr, scale, logit, o, l);
+                                      r, Hkv, h / G, d, interleaved, thr, scale, logit, o, l);
                 }
             }
             free(logit);
@@ -196,15 +221,24 @@ int orc_prefill(const void* q, const void* k, const void* v, int dtype, const in
     return 0;
 }
 
+int orc_prefill(const void* q, const void* k, const void* v, int dtype, const int32_t* pos,
+                int B, int64_t N, int Hq, int Hkv, int d, double base, double alpha,
+                double scale, const int64_t* rows, int64_t n_rows,
+                double* out, double* lse, int64_t* kept_out, int nthreads) {
+    return orc_prefill_ex(q, k, v, dtype, pos, B, N, Hq, Hkv, d, base, NULL, 0, alpha, scale,
+                          rows, n_rows, out, lse, kept_out, nthreads);
+}
+
 /*
  * One decode step per sequence.
  *   q [B][Hq][d] pre-RoPE; k, v [B][Lmax][Hkv][d] pre-RoPE cache contents, key c at position c;
  *   kv_len[B] (1..Lmax); q_pos[B] (NULL -> kv_len-1); the query sees keys 0..kv_len-1.
  *   out [B][Hq][d], lse [B][Hq] (double).
  */
-int orc_decode(const void* q, const void* k, const void* v, int dtype, const int32_t* kv_len,
-               const int32_t* q_pos, int B, int64_t Lmax, int Hq, int Hkv, int d, double base,
-               double alpha, double scale, double* out, double* lse, int64_t* kept_out, int nthreads) {
+int orc_decode_ex(const void* q, const void* k, const void* v, int dtype, const int32_t* kv_len,
+                  const int32_t* q_pos, int B, int64_t Lmax, int Hq, int Hkv, int d, double base,
+                  const double* inv_freq, int interleaved, double alpha, double scale,
+                  double* out, double* lse, int64_t* kept_out, int nthreads) {
     if (B < 1 || Lmax < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || d < 2 || d % 2 != 0)
         return -1;
 #ifdef _OPENMP
@@ -213,7 +247,7 @@ int orc_decode(const void* q, const void* k, const void* v, int dtype, const int
     int G = Hq / Hkv, P = d / 2;
     int esz = dtype == ORC_FP32 ? 4 : 2;
     double* thr = (double*)malloc(sizeof(double) * P);
-    orc_thresholds(d, base, alpha, thr);
+    orc_thresholds_ex(d, base, inv_freq, alpha, thr);
     int64_t kept_total = 0;
     for (int b = 0; b < B; ++b) {
         int64_t L = kv_len[b];
@@ -222,9 +256,11 @@ int orc_decode(const void* q, const void* k, const void* v, int dtype, const int
         int64_t* kp = (int64_t*)malloc(sizeof(int64_t) * L);
         for (int64_t c = 0; c < L; ++c) kp[c] = c;
         double* kr = (double*)malloc(sizeof(double) * L * Hkv * d);
-        orc_rope((const char*)k + (size_t)esz * b * Lmax * Hkv * d, dtype, L, Hkv, d, kp, base, kr);
+        orc_rope_ex((const char*)k + (size_t)esz * b * Lmax * Hkv * d, dtype, L, Hkv, d, kp, base,
+                    inv_freq, interleaved, kr);
         double* qr = (double*)malloc(sizeof(double) * Hq * d);
-        orc_rope((const char*)q + (size_t)esz * b * Hq * d, dtype, 1, Hq, d, &qp, base, qr);
+        orc_rope_ex((const char*)q + (size_t)esz * b * Hq * d, dtype, 1, Hq, d, &qp, base,
+                    inv_freq, interleaved, qr);
         const char* vb = (const char*)v + (size_t)esz * b * Lmax * Hkv * d;
         int64_t kept_b = 0;
         #pragma omp parallel reduction(+:kept_b)
@@ -233,7 +269,7 @@ int orc_decode(const void* q, const void* k, const void* v, int dtype, const int
             #pragma omp for schedule(dynamic, 1)
             for (int h = 0; h < Hq; ++h)
                 kept_b += orc_row(qr + (int64_t)h * d, qp, kr, kp, vb, dtype, L - 1, Hkv, h / G, d,
-                                  thr, scale, logit, out + ((int64_t)b * Hq + h) * d,
+                                  interleaved, thr, scale, logit, out + ((int64_t)b * Hq + h) * d,
                                   lse + (int64_t)b * Hq + h);
             free(logit);
         }
@@ -245,17 +281,24 @@ int orc_decode(const void* q, const void* k, const void* v, int dtype, const int
     return 0;
 }
 
+int orc_decode(const void* q, const void* k, const void* v, int dtype, const int32_t* kv_len,
+               const int32_t* q_pos, int B, int64_t Lmax, int Hq, int Hkv, int d, double base,
+               double alpha, double scale, double* out, double* lse, int64_t* kept_out, int nthreads) {
+    return orc_decode_ex(q, k, v, dtype, kv_len, q_pos, B, Lmax, Hq, Hkv, d, base, NULL, 0, alpha,
+                         scale, out, lse, kept_out, nthreads);
+}
+
 /*
  * Kept-term count by enumeration (no closed form): queries at token indices
  * q_idx0 .. q_idx0+n_q-1 with positions equal to their indices, keys 0..n_k-1,
  * key c visible to query r iff c <= r; counts (r, c, i) with |r-c| <= alpha*lambda_i.
  * total = (d/2) * #visible (r, c).  O(n_q * n_k * d/2).
  */
-void orc_count_enumerate(int d, double base, double alpha, int64_t n_q, int64_t q_idx0,
-                         int64_t n_k, int64_t* kept, int64_t* total) {
+void orc_count_enumerate_ex(int d, double base, const double* inv_freq, double alpha,
+                            int64_t n_q, int64_t q_idx0, int64_t n_k, int64_t* kept, int64_t* total) {
     int P = d / 2;
     double* thr = (double*)malloc(sizeof(double) * P);
-    orc_thresholds(d, base, alpha, thr);
+    orc_thresholds_ex(d, base, inv_freq, alpha, thr);
     int64_t kk = 0, tt = 0;
     #pragma omp parallel for reduction(+:kk, tt) schedule(dynamic, 16)
     for (int64_t j = 0; j < n_q; ++j) {
@@ -269,4 +312,9 @@ void orc_count_enumerate(int d, double base, double alpha, int64_t n_q, int64_t 
     *kept = kk;
     *total = tt;
     free(thr);
+}
+
+void orc_count_enumerate(int d, double base, double alpha, int64_t n_q, int64_t q_idx0,
+                         int64_t n_k, int64_t* kept, int64_t* total) {
+    orc_count_enumerate_ex(d, base, NULL, alpha, n_q, q_idx0, n_k, kept, total);
 }

@@ -11,6 +11,10 @@ Method (ATFlash abstract, "Per-RoPE-Wavelength Attention Windows"; WavePrune ori
 abstract): pair i of the half-split head vector, with wavelength 2*pi*base^(2i/d),
 contributes its q.k term only while the query-key distance is <= alpha*wavelength;
 alpha = 1 is the first rotation period, alpha = inf is full causal RoPE attention.
+
+RoPE variants: every op takes ``inv_freq`` (the d/2 per-pair rotation frequencies of a
+frequency-scaled RoPE, e.g. ``llama3_inv_freq(...)``; wavelength 2*pi/theta_i) and
+``pairs`` ("half": dims i, i+d/2; "interleaved": dims 2i, 2i+1).
 """
 from __future__ import annotations
 
@@ -18,6 +22,7 @@ import ctypes
 import math
 import os
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -26,10 +31,53 @@ LIB_PATH = os.path.join(_HERE, "libwpa.so")
 WPA_OK, WPA_ERR_INVALID, WPA_ERR_UNSUPPORTED, WPA_ERR_WORKSPACE, WPA_ERR_HIP = 0, -1, -2, -3, -4
 WPA_BF16, WPA_FP32 = 0, 1
 
+WPA_PAIRS = {"half": 0, "interleaved": 1}
+
 # every symbol include/wpa.h declares
 EXPORTS = ("wpa_count_terms", "wpa_thresholds", "wpa_prefill_workspace_bytes", "wpa_prefill",
-           "wpa_prefill_prepare", "wpa_prefill_attend", "wpa_kcache_bytes", "wpa_vcache_bytes", "wpa_kv_write", "wpa_decode_workspace_bytes",
-           "wpa_decode", "wpa_last_error")
+           "wpa_prefill_prepare", "wpa_prefill_attend", "wpa_kcache_bytes", "wpa_vcache_bytes",
+           "wpa_kv_write", "wpa_decode_workspace_bytes", "wpa_decode", "wpa_count_terms_ex",
+           "wpa_thresholds_ex", "wpa_prefill_ex", "wpa_prefill_prepare_ex", "wpa_prefill_attend_ex",
+           "wpa_kv_write_ex", "wpa_decode_ex", "wpa_last_error")
+
+
+class Rope(ctypes.Structure):
+    """wpa_rope_t: pair layout and optional host table of rotation frequencies."""
+    _fields_ = [("pairs", ctypes.c_int32), ("inv_freq", ctypes.c_void_p)]
+
+
+def _rope(d, inv_freq, pairs):
+    """(pointer to a wpa_rope_t or None, objects that must outlive the call)."""
+    if inv_freq is None and pairs == "half":
+        return None, ()
+    if pairs not in WPA_PAIRS:
+        raise ValueError("pairs must be 'half' or 'interleaved'")
+    tab = None
+    if inv_freq is not None:
+        tab = np.ascontiguousarray(np.asarray(inv_freq, dtype=np.float64))
+        if tab.shape != (d // 2,):
+            raise ValueError("inv_freq must hold d/2 = %d frequencies" % (d // 2))
+    r = Rope(WPA_PAIRS[pairs], None if tab is None else tab.ctypes.data)
+    return ctypes.byref(r), (r, tab)
+
+
+def default_inv_freq(d: int, base: float) -> np.ndarray:
+    """theta_i = base^(-2i/d), i < d/2 (float64)."""
+    return np.power(float(base), -np.arange(d // 2, dtype=np.float64) * 2.0 / d)
+
+
+def llama3_inv_freq(d: int, base: float, factor: float, low_freq_factor: float,
+                    high_freq_factor: float, original_max_position: int) -> np.ndarray:
+    """Rotation frequencies of Llama-3-style frequency-scaled RoPE (float64): pairs whose
+    wavelength is shorter than original_max_position/high_freq_factor keep theta_i, pairs
+    longer than original_max_position/low_freq_factor are slowed by `factor`, and the band
+    in between blends the two linearly in original_max_position/wavelength.  The result is
+    non-increasing in i, as the kernels require."""
+    theta = default_inv_freq(d, base)
+    wavelen = 2.0 * math.pi / theta
+    ratio = original_max_position / wavelen                    # periods within the old context
+    blend = np.clip((ratio - low_freq_factor) / (high_freq_factor - low_freq_factor), 0.0, 1.0)
+    return theta * (blend + (1.0 - blend) / factor)
 
 
 class WpaError(RuntimeError):
@@ -77,6 +125,23 @@ def lib():
     L.wpa_decode.argtypes = [P, P, P, P, P, P, P, I32, I64, I32, I32, I32, D, D, F, I32, I32, P,
                              I32, P, SZ, P]
     L.wpa_decode.restype = ctypes.c_int
+    L.wpa_count_terms_ex.argtypes = [I32, D, P, D, I64, I64, I64, P, P]
+    L.wpa_count_terms_ex.restype = ctypes.c_int
+    L.wpa_thresholds_ex.argtypes = [I32, D, P, D, P]
+    L.wpa_thresholds_ex.restype = ctypes.c_int
+    L.wpa_prefill_ex.argtypes = [P, P, P, P, P, P, I32, I64, I32, I32, I32, D, P, D, F, I32, I32, P,
+                                 P, SZ, P]
+    L.wpa_prefill_ex.restype = ctypes.c_int
+    L.wpa_prefill_prepare_ex.argtypes = [P, P, P, I32, I64, I32, I32, D, P, I32, P, SZ, P]
+    L.wpa_prefill_prepare_ex.restype = ctypes.c_int
+    L.wpa_prefill_attend_ex.argtypes = [P, P, P, P, I32, I64, I32, I32, I32, D, P, D, F, I32, I32, P,
+                                        P, SZ, P]
+    L.wpa_prefill_attend_ex.restype = ctypes.c_int
+    L.wpa_kv_write_ex.argtypes = [P, P, I64, I64, P, P, I32, I64, I32, I32, D, P, I32, P]
+    L.wpa_kv_write_ex.restype = ctypes.c_int
+    L.wpa_decode_ex.argtypes = [P, P, P, P, P, P, P, I32, I64, I32, I32, I32, D, P, D, F, I32, I32,
+                                P, I32, P, SZ, P]
+    L.wpa_decode_ex.restype = ctypes.c_int
     L.wpa_last_error.argtypes = []
     L.wpa_last_error.restype = ctypes.c_char_p
     _lib = L
@@ -113,18 +178,22 @@ def _dev(t, name):
 
 # ------------------------------------------------------------------------------ host-only
 
-def count_terms(d: int, base: float, alpha: float, n_q: int, q_pos0: int, n_k: int):
+def count_terms(d: int, base: float, alpha: float, n_q: int, q_pos0: int, n_k: int, *,
+                inv_freq=None, pairs: str = "half"):
     """(kept, total) (query, key, pair) terms per head; exact closed form, host only."""
     kept, total = ctypes.c_int64(), ctypes.c_int64()
-    _check(lib().wpa_count_terms(d, float(base), float(alpha), n_q, q_pos0, n_k,
-                                 ctypes.byref(kept), ctypes.byref(total)))
+    rope, keep = _rope(d, inv_freq, pairs)
+    _check(lib().wpa_count_terms_ex(d, float(base), rope, float(alpha), n_q, q_pos0, n_k,
+                                    ctypes.byref(kept), ctypes.byref(total)))
     return kept.value, total.value
 
 
-def thresholds(d: int, base: float, alpha: float):
-    """Integer window table W_i = floor(alpha * 2*pi * base^(2i/d)) (INT32_MAX if unbounded)."""
+def thresholds(d: int, base: float, alpha: float, *, inv_freq=None, pairs: str = "half"):
+    """Integer window table W_i = floor(alpha * lambda_i) (INT32_MAX if unbounded), with
+    lambda_i = 2*pi*base^(2i/d) or 2*pi/inv_freq[i]."""
     W = (ctypes.c_int32 * (d // 2))()
-    _check(lib().wpa_thresholds(d, float(base), float(alpha), W))
+    rope, keep = _rope(d, inv_freq, pairs)
+    _check(lib().wpa_thresholds_ex(d, float(base), rope, float(alpha), W))
     return list(W)
 
 
@@ -148,7 +217,7 @@ def decode_workspace_bytes(B, Lmax, Hq, Hkv, d, chunk_keys=0) -> int:
 
 def prefill(q, k, v, base: float, alpha: float, *, scale: float | None = None, positions=None,
             out=None, out_dtype=None, lse=None, want_lse: bool = False, term_count=None,
-            workspace=None, stream=None):
+            workspace=None, stream=None, inv_freq=None, pairs: str = "half"):
     """Causal windowed prefill.  q [B][N][Hq][d], k/v [B][N][Hkv][d] (bf16 or fp32, pre-RoPE).
 
     Returns out [B][N][Hq][d] (out_dtype, default q's dtype), or (out, lse [B][Hq][N] fp32)
@@ -177,16 +246,17 @@ def prefill(q, k, v, base: float, alpha: float, *, scale: float | None = None, p
     need = prefill_workspace_bytes(B, N, Hkv, d)
     if workspace is None:
         workspace = torch.empty(max(need, 16), device=q.device, dtype=torch.uint8)
-    _check(lib().wpa_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(positions),
-                             B, N, Hq, Hkv, d, float(base), float(alpha),
-                             float(scale) if scale is not None else 0.0, _dtype_code(q),
-                             _dtype_code(out), _ptr(term_count), _ptr(workspace),
-                             workspace.numel(),
-                             _stream(stream)))
+    rope, keep = _rope(d, inv_freq, pairs)
+    _check(lib().wpa_prefill_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(positions),
+                                B, N, Hq, Hkv, d, float(base), rope, float(alpha),
+                                float(scale) if scale is not None else 0.0, _dtype_code(q),
+                                _dtype_code(out), _ptr(term_count), _ptr(workspace),
+                                workspace.numel(), _stream(stream)))
     return (out, lse) if lse is not None else out
 
 
-def prefill_prepare(k, v, base: float, *, positions=None, workspace=None, stream=None):
+def prefill_prepare(k, v, base: float, *, positions=None, workspace=None, stream=None,
+                    inv_freq=None, pairs: str = "half"):
     """First half of prefill: rotate k, transpose v into a workspace (returned)."""
     _dev(k, "k")
     _dev(v, "v")
@@ -200,15 +270,16 @@ def prefill_prepare(k, v, base: float, *, positions=None, workspace=None, stream
     need = prefill_workspace_bytes(B, N, Hkv, d)
     if workspace is None:
         workspace = torch.empty(max(need, 16), device=k.device, dtype=torch.uint8)
-    _check(lib().wpa_prefill_prepare(_ptr(k), _ptr(v), _ptr(positions), B, N, Hkv, d, float(base),
-                                     _dtype_code(k), _ptr(workspace), workspace.numel(),
-                                     _stream(stream)))
+    rope, keep = _rope(d, inv_freq, pairs)
+    _check(lib().wpa_prefill_prepare_ex(_ptr(k), _ptr(v), _ptr(positions), B, N, Hkv, d,
+                                        float(base), rope, _dtype_code(k), _ptr(workspace),
+                                        workspace.numel(), _stream(stream)))
     return workspace
 
 
 def prefill_attend(q, workspace, Hkv: int, base: float, alpha: float, *, scale=None,
                    positions=None, out=None, out_dtype=None, lse=None, want_lse=False,
-                   term_count=None, stream=None):
+                   term_count=None, stream=None, inv_freq=None, pairs: str = "half"):
     """Second half of prefill: windowed attention of q against a prepared workspace."""
     _dev(q, "q")
     _dev(workspace, "workspace")
@@ -220,19 +291,25 @@ def prefill_attend(q, workspace, Hkv: int, base: float, alpha: float, *, scale=N
         lse = torch.empty((B, Hq, N), device=q.device, dtype=torch.float32)
     if positions is not None:
         _dev(positions, "positions")
-    _check(lib().wpa_prefill_attend(_ptr(q), _ptr(out), _ptr(lse), _ptr(positions), B, N, Hq, Hkv,
-                                    d, float(base), float(alpha),
-                                    float(scale) if scale is not None else 0.0, _dtype_code(q),
-                                    _dtype_code(out), _ptr(term_count), _ptr(workspace),
-                                    workspace.numel(), _stream(stream)))
+    rope, keep = _rope(d, inv_freq, pairs)
+    _check(lib().wpa_prefill_attend_ex(_ptr(q), _ptr(out), _ptr(lse), _ptr(positions), B, N, Hq,
+                                       Hkv, d, float(base), rope, float(alpha),
+                                       float(scale) if scale is not None else 0.0, _dtype_code(q),
+                                       _dtype_code(out), _ptr(term_count), _ptr(workspace),
+                                       workspace.numel(), _stream(stream)))
     return (out, lse) if lse is not None else out
 
 
 class KVCache:
-    """Decode caches for B sequences of up to Lmax tokens (library-owned K layout)."""
+    """Decode caches for B sequences of up to Lmax tokens (library-owned K layout).  The
+    RoPE description (inv_freq, pairs) given here rotates the keys written and the queries
+    of every decode step against this cache."""
 
-    def __init__(self, B, Lmax, Hkv, d, base, device="cuda"):
+    def __init__(self, B, Lmax, Hkv, d, base, device="cuda", *, inv_freq=None, pairs="half"):
         self.B, self.Lmax, self.Hkv, self.d, self.base = B, Lmax, Hkv, d, float(base)
+        self.inv_freq = None if inv_freq is None else np.asarray(inv_freq, dtype=np.float64).copy()
+        self.pairs = pairs
+        _rope(d, self.inv_freq, pairs)                 # validates the description
         self.k = torch.empty(kcache_bytes(B, Lmax, Hkv, d), device=device, dtype=torch.uint8)
         self.v = torch.empty(vcache_bytes(B, Lmax, Hkv, d), device=device, dtype=torch.uint8)
 
@@ -243,9 +320,10 @@ class KVCache:
         if k.shape != v.shape or k.dim() != 4 or k.shape[0] != self.B or k.shape[2] != self.Hkv \
                 or k.shape[3] != self.d or k.dtype != v.dtype:
             raise ValueError("k, v must be [B][n][Hkv][d] of one dtype")
-        _check(lib().wpa_kv_write(_ptr(k), _ptr(v), int(start), k.shape[1], _ptr(self.k),
-                                  _ptr(self.v), self.B, self.Lmax, self.Hkv, self.d, self.base,
-                                  _dtype_code(k), _stream(stream)))
+        rope, keep = _rope(self.d, self.inv_freq, self.pairs)
+        _check(lib().wpa_kv_write_ex(_ptr(k), _ptr(v), int(start), k.shape[1], _ptr(self.k),
+                                     _ptr(self.v), self.B, self.Lmax, self.Hkv, self.d, self.base,
+                                     rope, _dtype_code(k), _stream(stream)))
 
     def v_tokens(self):
         """A copy of the V cache as bf16 [B][Hkv][Lmax][d] (the cache itself is blocked by
@@ -276,12 +354,13 @@ def decode(q, cache: KVCache, kv_len, alpha: float, *, q_pos=None, scale: float 
     need = decode_workspace_bytes(B, cache.Lmax, Hq, cache.Hkv, d, chunk_keys)
     if workspace is None:
         workspace = torch.empty(max(need, 16), device=q.device, dtype=torch.uint8)
-    _check(lib().wpa_decode(_ptr(q), _ptr(cache.k), _ptr(cache.v), _ptr(kv_len), _ptr(q_pos),
-                            _ptr(out), _ptr(lse), B, cache.Lmax, Hq, cache.Hkv, d, cache.base,
-                            float(alpha), float(scale) if scale is not None else 0.0,
-                            _dtype_code(q), _dtype_code(out), _ptr(term_count), int(chunk_keys),
-                            _ptr(workspace),
-                            workspace.numel(), _stream(stream)))
+    rope, keep = _rope(d, cache.inv_freq, cache.pairs)
+    _check(lib().wpa_decode_ex(_ptr(q), _ptr(cache.k), _ptr(cache.v), _ptr(kv_len), _ptr(q_pos),
+                               _ptr(out), _ptr(lse), B, cache.Lmax, Hq, cache.Hkv, d, cache.base,
+                               rope, float(alpha), float(scale) if scale is not None else 0.0,
+                               _dtype_code(q), _dtype_code(out), _ptr(term_count),
+                               int(chunk_keys), _ptr(workspace), workspace.numel(),
+                               _stream(stream)))
     return (out, lse) if lse is not None else out
 
 

@@ -68,13 +68,16 @@ void decode_partial_kernel(DecodeParams p, Tables tab) {
         float xo = 0.f, yo = 0.f;
         if (hh < G) {
             const int64_t qb = ((int64_t)b * p.Hq + g * G + hh) * D;
+            // the two dims of pair pr: (pr, pr+P) half-split, (2pr, 2pr+1) interleaved
+            const int64_t ix = p.interleaved ? qb + 2 * pr : qb + pr;
+            const int64_t iy = p.interleaved ? ix + 1 : ix + P;
             float x, y;
             if (p.in_f32) {
-                x = round_bf16(static_cast<const float*>(p.q)[qb + pr]);
-                y = round_bf16(static_cast<const float*>(p.q)[qb + P + pr]);
+                x = round_bf16(static_cast<const float*>(p.q)[ix]);
+                y = round_bf16(static_cast<const float*>(p.q)[iy]);
             } else {
-                x = bf16_bits_to_f32(static_cast<const uint16_t*>(p.q)[qb + pr]);
-                y = bf16_bits_to_f32(static_cast<const uint16_t*>(p.q)[qb + P + pr]);
+                x = bf16_bits_to_f32(static_cast<const uint16_t*>(p.q)[ix]);
+                y = bf16_bits_to_f32(static_cast<const uint16_t*>(p.q)[iy]);
             }
             float sn, cs;
             rope_sincos(qpos, tab.theta[pr], &sn, &cs);

@@ -171,13 +171,16 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
             u32x4 acc = {0u, 0u, 0u, 0u};
 #pragma unroll 1
             for (int e = 0; e < 8; ++e) {
+                // the two dims of pair 8j+e: (i, i+P) half-split, (2i, 2i+1) interleaved
+                const int64_t ix = p.interleaved ? qb + 2 * (8 * j + e) : qb + 8 * j + e;
+                const int64_t iy = p.interleaved ? ix + 1 : ix + P;
                 float x, y;
                 if constexpr (F32) {
-                    x = round_bf16(static_cast<const float*>(p.q)[qb + 8 * j + e]);
-                    y = round_bf16(static_cast<const float*>(p.q)[qb + P + 8 * j + e]);
+                    x = round_bf16(static_cast<const float*>(p.q)[ix]);
+                    y = round_bf16(static_cast<const float*>(p.q)[iy]);
                 } else {
-                    x = bf16_bits_to_f32(static_cast<const uint16_t*>(p.q)[qb + 8 * j + e]);
-                    y = bf16_bits_to_f32(static_cast<const uint16_t*>(p.q)[qb + P + 8 * j + e]);
+                    x = bf16_bits_to_f32(static_cast<const uint16_t*>(p.q)[ix]);
+                    y = bf16_bits_to_f32(static_cast<const uint16_t*>(p.q)[iy]);
                 }
                 float sn, cs;
                 rope_sincos(pq, tab.theta[8 * j + e], &sn, &cs);

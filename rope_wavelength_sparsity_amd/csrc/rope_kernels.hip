@@ -42,8 +42,22 @@ __global__ __launch_bounds__(256) void rope_keys_kernel(RopeParams p, Tables tab
     }
     const int64_t row = (((int64_t)b * p.n + t) * p.Hkv + g) * p.d;
     float x[8], y[8];
-    load8<F32>(p.k, row + 8 * j, x);
-    load8<F32>(p.k, row + P + 8 * j, y);
+    if (p.interleaved) {
+        // pairs 8j..8j+7 are dims 16j..16j+15, each pair's two components adjacent
+        float a[8], c[8];
+        load8<F32>(p.k, row + 16 * j, a);
+        load8<F32>(p.k, row + 16 * j + 8, c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[e] = a[2 * e];
+            y[e] = a[2 * e + 1];
+            x[4 + e] = c[2 * e];
+            y[4 + e] = c[2 * e + 1];
+        }
+    } else {
+        load8<F32>(p.k, row + 8 * j, x);
+        load8<F32>(p.k, row + P + 8 * j, y);
+    }
     const int64_t pos = p.pos ? (int64_t)p.pos[(int64_t)b * p.n + t] : p.t0 + t;
     uint32_t ox[4], oy[4];
 #pragma unroll

@@ -31,10 +31,34 @@ int ok() {
 
 // alpha*lambda_i, lambda_i = 2*pi*base^(2i/d): one full rotation period of pair i
 // (WavePrune original abstract: each channel keeps its first rotation period at alpha=1;
-// ATFlash abstract: the distance window is proportional to the wavelength).
-double window_value(int d, double base, double alpha, int i) {
-    const double lam = (2.0 * M_PI) * std::pow(base, (2.0 * i) / (double)d);
+// ATFlash abstract: the distance window is proportional to the wavelength).  With a
+// frequency table, lambda_i = 2*pi/theta_i.
+double window_value(int d, double base, const double* inv_freq, double alpha, int i) {
+    const double lam = inv_freq ? (2.0 * M_PI) / inv_freq[i]
+                                : (2.0 * M_PI) * std::pow(base, (2.0 * i) / (double)d);
     return alpha * lam;
+}
+
+const double* freq_table(const wpa_rope_t* rope) { return rope ? rope->inv_freq : nullptr; }
+int interleaved(const wpa_rope_t* rope) { return rope && rope->pairs == WPA_PAIRS_INTERLEAVED; }
+
+// The RoPE description: a known pair layout; a frequency table positive, finite and
+// non-increasing (the pairs active at a distance must stay a suffix), else a base > 1.
+int check_rope(int32_t d, double base, const wpa_rope_t* rope) {
+    if (rope && rope->pairs != WPA_PAIRS_HALF && rope->pairs != WPA_PAIRS_INTERLEAVED)
+        return fail(WPA_ERR_INVALID, "rope pairs must be WPA_PAIRS_HALF or WPA_PAIRS_INTERLEAVED");
+    const double* f = freq_table(rope);
+    if (!f) {
+        if (!(base > 1.0) || !std::isfinite(base)) return fail(WPA_ERR_INVALID, "rope base must be finite and > 1");
+        return WPA_OK;
+    }
+    for (int i = 0; i < d / 2; ++i) {
+        if (!(f[i] > 0.0) || !std::isfinite(f[i]))
+            return fail(WPA_ERR_UNSUPPORTED, "inv_freq[%d] = %g: rotation frequencies must be finite and > 0", i, f[i]);
+        if (i > 0 && f[i] > f[i - 1])
+            return fail(WPA_ERR_UNSUPPORTED, "inv_freq must be non-increasing (inv_freq[%d] > inv_freq[%d])", i, i - 1);
+    }
+    return WPA_OK;
 }
 
 // Integer form used by the kernels: distance D (an integer) is inside iff D <= floor(t).
@@ -43,20 +67,22 @@ int32_t window_int(double t) {
     return (int32_t)std::floor(t);
 }
 
-int check_common(int32_t d, double base, double alpha) {
+int check_common(int32_t d, double base, const wpa_rope_t* rope, double alpha) {
     if (d != 64 && d != 128) return fail(WPA_ERR_UNSUPPORTED, "head dim d=%d unsupported (64 or 128)", d);
-    if (!(base > 1.0) || !std::isfinite(base)) return fail(WPA_ERR_INVALID, "rope base must be finite and > 1");
+    const int rc = check_rope(d, base, rope);
+    if (rc) return rc;
     if (!(alpha >= 0.0)) return fail(WPA_ERR_INVALID, "alpha must be >= 0 (got %g)", alpha);
     return WPA_OK;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-void make_tables(int32_t d, double base, double alpha, wpa::Tables* t) {
+void make_tables(int32_t d, double base, const wpa_rope_t* rope, double alpha, wpa::Tables* t) {
     std::memset(t, 0, sizeof *t);
+    const double* f = freq_table(rope);
     for (int i = 0; i < d / 2; ++i) {
-        t->W[i] = window_int(window_value(d, base, alpha, i));
-        t->theta[i] = std::pow(base, -(2.0 * i) / (double)d);
+        t->W[i] = window_int(window_value(d, base, f, alpha, i));
+        t->theta[i] = f ? f[i] : std::pow(base, -(2.0 * i) / (double)d);
     }
 }
 
@@ -121,19 +147,30 @@ extern "C" {
 
 const char* wpa_last_error(void) { return g_err; }
 
-int wpa_thresholds(int32_t d, double base, double alpha, int32_t* W) {
+int wpa_thresholds_ex(int32_t d, double base, const wpa_rope_t* rope, double alpha, int32_t* W) {
     if (d < 2 || d > 128 || (d & 1)) return fail(WPA_ERR_INVALID, "d must be even and in [2, 128]");
-    if (!(base > 1.0) || !std::isfinite(base)) return fail(WPA_ERR_INVALID, "rope base must be finite and > 1");
+    const int rc = check_rope(d, base, rope);
+    if (rc) return rc;
     if (!(alpha >= 0.0)) return fail(WPA_ERR_INVALID, "alpha must be >= 0");
     if (!W) return fail(WPA_ERR_INVALID, "W is null");
-    for (int i = 0; i < d / 2; ++i) W[i] = window_int(window_value(d, base, alpha, i));
+    for (int i = 0; i < d / 2; ++i) W[i] = window_int(window_value(d, base, freq_table(rope), alpha, i));
     return ok();
+}
+
+int wpa_thresholds(int32_t d, double base, double alpha, int32_t* W) {
+    return wpa_thresholds_ex(d, base, nullptr, alpha, W);
 }
 
 int wpa_count_terms(int32_t d, double base, double alpha, int64_t n_q, int64_t q_pos0,
                     int64_t n_k, int64_t* kept, int64_t* total) {
+    return wpa_count_terms_ex(d, base, nullptr, alpha, n_q, q_pos0, n_k, kept, total);
+}
+
+int wpa_count_terms_ex(int32_t d, double base, const wpa_rope_t* rope, double alpha, int64_t n_q,
+                       int64_t q_pos0, int64_t n_k, int64_t* kept, int64_t* total) {
     if (d < 2 || (d & 1)) return fail(WPA_ERR_INVALID, "d must be even and >= 2");
-    if (!(base > 1.0) || !std::isfinite(base)) return fail(WPA_ERR_INVALID, "rope base must be finite and > 1");
+    const int rc = check_rope(d, base, rope);
+    if (rc) return rc;
     if (!(alpha >= 0.0)) return fail(WPA_ERR_INVALID, "alpha must be >= 0");
     if (n_q < 0 || n_k < 0 || q_pos0 < 0) return fail(WPA_ERR_INVALID, "negative count or position");
     if (!kept || !total) return fail(WPA_ERR_INVALID, "null output pointer");
@@ -141,7 +178,7 @@ int wpa_count_terms(int32_t d, double base, double alpha, int64_t n_q, int64_t q
     if (n_q > 0 && n_k > 0) {
         vis = pair_kept(q_pos0, n_q, n_k, INT64_MAX / 4);
         for (int i = 0; i < d / 2; ++i) {
-            const double t = window_value(d, base, alpha, i);
+            const double t = window_value(d, base, freq_table(rope), alpha, i);
             const int64_t Wi = (t < 9.0e18) ? (int64_t)std::floor(t) : INT64_MAX / 4;
             k += pair_kept(q_pos0, n_q, n_k, Wi);
         }
@@ -179,20 +216,28 @@ int check_prefill_shape(int64_t N, int32_t B, int32_t Hkv, int32_t dtype, const 
 int wpa_prefill_prepare(const void* k, const void* v, const int32_t* positions, int32_t B,
                         int64_t N, int32_t Hkv, int32_t d, double base, int32_t dtype,
                         void* workspace, size_t ws_bytes, void* stream) {
-    int rc = check_common(d, base, 1.0);
+    return wpa_prefill_prepare_ex(k, v, positions, B, N, Hkv, d, base, nullptr, dtype, workspace,
+                                  ws_bytes, stream);
+}
+
+int wpa_prefill_prepare_ex(const void* k, const void* v, const int32_t* positions, int32_t B,
+                           int64_t N, int32_t Hkv, int32_t d, double base, const wpa_rope_t* rope,
+                           int32_t dtype, void* workspace, size_t ws_bytes, void* stream) {
+    int rc = check_common(d, base, rope, 1.0);
     if (rc) return rc;
     rc = check_prefill_shape(N, B, Hkv, dtype, positions, workspace, ws_bytes, d);
     if (rc) return rc;
     if (!k || !v) return fail(WPA_ERR_INVALID, "null k or v");
     if (!aligned16(k) || !aligned16(v)) return fail(WPA_ERR_INVALID, "k and v must be 16-byte aligned");
     wpa::Tables tab;
-    make_tables(d, base, 1.0, &tab);
+    make_tables(d, base, rope, 1.0, &tab);
     const int64_t Np = round_up(N, wpa::kTileKeys);
     uint16_t* kp = static_cast<uint16_t*>(workspace);
     wpa::RopeParams rp{};
     rp.k = k; rp.v = v; rp.pos = positions; rp.kp = kp; rp.vout = kp + (size_t)B * Hkv * Np * d;
     rp.n = N; rp.t0 = 0; rp.ld = Np; rp.pad_to = Np;
     rp.B = B; rp.Hkv = Hkv; rp.d = d; rp.in_f32 = dtype == WPA_FP32; rp.v_transposed = 1;
+    rp.interleaved = interleaved(rope);
     rp.tab = &tab;
     hipError_t e = wpa::launch_rope_relayout(rp, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(WPA_ERR_HIP, "rope relayout launch: %s", hipGetErrorString(e));
@@ -204,7 +249,16 @@ int wpa_prefill_attend(const void* q, void* out, float* lse, const int32_t* posi
                        double alpha, float scale, int32_t dtype, int32_t out_dtype,
                        unsigned long long* term_count, const void* workspace, size_t ws_bytes,
                        void* stream) {
-    int rc = check_common(d, base, alpha);
+    return wpa_prefill_attend_ex(q, out, lse, positions, B, N, Hq, Hkv, d, base, nullptr, alpha,
+                                 scale, dtype, out_dtype, term_count, workspace, ws_bytes, stream);
+}
+
+int wpa_prefill_attend_ex(const void* q, void* out, float* lse, const int32_t* positions,
+                          int32_t B, int64_t N, int32_t Hq, int32_t Hkv, int32_t d, double base,
+                          const wpa_rope_t* rope, double alpha, float scale, int32_t dtype,
+                          int32_t out_dtype, unsigned long long* term_count,
+                          const void* workspace, size_t ws_bytes, void* stream) {
+    int rc = check_common(d, base, rope, alpha);
     if (rc) return rc;
     rc = check_prefill_shape(N, B, Hkv, dtype, positions, workspace, ws_bytes, d);
     if (rc) return rc;
@@ -217,10 +271,11 @@ int wpa_prefill_attend(const void* q, void* out, float* lse, const int32_t* posi
     if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(WPA_ERR_INVALID, "lse must be 4-byte aligned");
     if (term_count && (reinterpret_cast<uintptr_t>(term_count) & 7u)) return fail(WPA_ERR_INVALID, "term_count must be 8-byte aligned");
     wpa::Tables tab;
-    make_tables(d, base, alpha, &tab);
+    make_tables(d, base, rope, alpha, &tab);
     const int64_t Np = round_up(N, wpa::kTileKeys);
     const uint16_t* kp = static_cast<const uint16_t*>(workspace);
     wpa::PrefillParams pp{};
+    pp.interleaved = interleaved(rope);
     pp.q = q; pp.kp = kp; pp.vt = kp + (size_t)B * Hkv * Np * d; pp.out = out; pp.lse = lse;
     pp.pos = positions; pp.counter = term_count; pp.N = N; pp.Np = Np; pp.B = B; pp.Hq = Hq;
     pp.Hkv = Hkv; pp.d = d; pp.in_f32 = dtype == WPA_FP32; pp.out_f32 = out_dtype == WPA_FP32;
@@ -235,8 +290,17 @@ int wpa_prefill(const void* q, const void* k, const void* v, void* out, float* l
                 int32_t d, double base, double alpha, float scale, int32_t dtype,
                 int32_t out_dtype, unsigned long long* term_count, void* workspace,
                 size_t ws_bytes, void* stream) {
+    return wpa_prefill_ex(q, k, v, out, lse, positions, B, N, Hq, Hkv, d, base, nullptr, alpha,
+                          scale, dtype, out_dtype, term_count, workspace, ws_bytes, stream);
+}
+
+int wpa_prefill_ex(const void* q, const void* k, const void* v, void* out, float* lse,
+                   const int32_t* positions, int32_t B, int64_t N, int32_t Hq, int32_t Hkv,
+                   int32_t d, double base, const wpa_rope_t* rope, double alpha, float scale,
+                   int32_t dtype, int32_t out_dtype, unsigned long long* term_count,
+                   void* workspace, size_t ws_bytes, void* stream) {
     // check everything before enqueueing anything
-    int rc = check_common(d, base, alpha);
+    int rc = check_common(d, base, rope, alpha);
     if (rc) return rc;
     if (B < 1 || N < 1 || Hq < 1 || Hkv < 1) return fail(WPA_ERR_INVALID, "B, N, Hq, Hkv must be >= 1");
     if (Hq % Hkv) return fail(WPA_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
@@ -249,10 +313,11 @@ int wpa_prefill(const void* q, const void* k, const void* v, void* out, float* l
     if (term_count && (reinterpret_cast<uintptr_t>(term_count) & 7u)) return fail(WPA_ERR_INVALID, "term_count must be 8-byte aligned");
     rc = check_prefill_shape(N, B, Hkv, dtype, positions, workspace, ws_bytes, d);
     if (rc) return rc;
-    rc = wpa_prefill_prepare(k, v, positions, B, N, Hkv, d, base, dtype, workspace, ws_bytes, stream);
+    rc = wpa_prefill_prepare_ex(k, v, positions, B, N, Hkv, d, base, rope, dtype, workspace,
+                                ws_bytes, stream);
     if (rc) return rc;
-    return wpa_prefill_attend(q, out, lse, positions, B, N, Hq, Hkv, d, base, alpha, scale, dtype,
-                              out_dtype, term_count, workspace, ws_bytes, stream);
+    return wpa_prefill_attend_ex(q, out, lse, positions, B, N, Hq, Hkv, d, base, rope, alpha, scale,
+                                 dtype, out_dtype, term_count, workspace, ws_bytes, stream);
 }
 
 size_t wpa_kcache_bytes(int32_t B, int64_t Lmax, int32_t Hkv, int32_t d) {
@@ -268,7 +333,14 @@ size_t wpa_vcache_bytes(int32_t B, int64_t Lmax, int32_t Hkv, int32_t d) {
 int wpa_kv_write(const void* k, const void* v, int64_t start, int64_t n, void* k_cache,
                  void* v_cache, int32_t B, int64_t Lmax, int32_t Hkv, int32_t d, double base,
                  int32_t dtype, void* stream) {
-    int rc = check_common(d, base, 1.0);
+    return wpa_kv_write_ex(k, v, start, n, k_cache, v_cache, B, Lmax, Hkv, d, base, nullptr, dtype,
+                           stream);
+}
+
+int wpa_kv_write_ex(const void* k, const void* v, int64_t start, int64_t n, void* k_cache,
+                    void* v_cache, int32_t B, int64_t Lmax, int32_t Hkv, int32_t d, double base,
+                    const wpa_rope_t* rope, int32_t dtype, void* stream) {
+    int rc = check_common(d, base, rope, 1.0);
     if (rc) return rc;
     if (B < 1 || Hkv < 1 || Lmax < 1 || n < 1 || start < 0 || start + n > Lmax)
         return fail(WPA_ERR_INVALID, "need B, Hkv, n >= 1 and 0 <= start, start + n <= Lmax");
@@ -278,8 +350,9 @@ int wpa_kv_write(const void* k, const void* v, int64_t start, int64_t n, void* k
     if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
         return fail(WPA_ERR_INVALID, "pointers must be 16-byte aligned");
     wpa::Tables tab;
-    make_tables(d, base, 1.0, &tab);
+    make_tables(d, base, rope, 1.0, &tab);
     wpa::RopeParams rp{};
+    rp.interleaved = interleaved(rope);
     rp.k = k; rp.v = v; rp.pos = nullptr;
     rp.kp = static_cast<uint16_t*>(k_cache); rp.vout = static_cast<uint16_t*>(v_cache);
     rp.n = n; rp.t0 = start; rp.ld = Lmax; rp.pad_to = 0;
@@ -303,7 +376,18 @@ int wpa_decode(const void* q, const void* k_cache, const void* v_cache, const in
                int32_t Hq, int32_t Hkv, int32_t d, double base, double alpha, float scale,
                int32_t dtype, int32_t out_dtype, unsigned long long* term_count,
                int32_t chunk_keys, void* workspace, size_t ws_bytes, void* stream) {
-    int rc = check_common(d, base, alpha);
+    return wpa_decode_ex(q, k_cache, v_cache, kv_len, q_pos, out, lse, B, Lmax, Hq, Hkv, d, base,
+                         nullptr, alpha, scale, dtype, out_dtype, term_count, chunk_keys, workspace,
+                         ws_bytes, stream);
+}
+
+int wpa_decode_ex(const void* q, const void* k_cache, const void* v_cache, const int32_t* kv_len,
+                  const int32_t* q_pos, void* out, float* lse, int32_t B, int64_t Lmax,
+                  int32_t Hq, int32_t Hkv, int32_t d, double base, const wpa_rope_t* rope,
+                  double alpha, float scale, int32_t dtype, int32_t out_dtype,
+                  unsigned long long* term_count, int32_t chunk_keys, void* workspace,
+                  size_t ws_bytes, void* stream) {
+    int rc = check_common(d, base, rope, alpha);
     if (rc) return rc;
     if (B < 1 || Lmax < 1 || Hq < 1 || Hkv < 1) return fail(WPA_ERR_INVALID, "B, Lmax, Hq, Hkv must be >= 1");
     if (Hq % Hkv) return fail(WPA_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
@@ -321,8 +405,9 @@ int wpa_decode(const void* q, const void* k_cache, const void* v_cache, const in
     const size_t need = wpa_decode_workspace_bytes(B, Lmax, Hq, Hkv, d, ch);
     if (ws_bytes < need) return fail(WPA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
     wpa::Tables tab;
-    make_tables(d, base, alpha, &tab);
+    make_tables(d, base, rope, alpha, &tab);
     wpa::DecodeParams dp{};
+    dp.interleaved = interleaved(rope);
     dp.q = q; dp.kp = static_cast<const uint16_t*>(k_cache); dp.v = static_cast<const uint16_t*>(v_cache);
     dp.kv_len = kv_len; dp.q_pos = q_pos; dp.out = out; dp.lse = lse; dp.counter = term_count;
     dp.partial = static_cast<float*>(workspace); dp.Lmax = Lmax; dp.B = B; dp.Hq = Hq; dp.Hkv = Hkv;

@@ -13,7 +13,7 @@ constexpr int kTileKeys = 128;    // token padding of the prefill workspace (a m
 // Window and rotation tables, computed once on the host in double.
 struct Tables {
     int32_t W[kMaxPairs];         // floor(alpha*lambda_i), INT32_MAX when unbounded
-    double theta[kMaxPairs];      // base^(-2i/d)
+    double theta[kMaxPairs];      // rotation frequency of pair i (base^(-2i/d), or a table)
 };
 
 // Rotate keys into the pair-blocked layout [B][Hkv][d/16][ld][16] (bf16) and, for
@@ -28,6 +28,7 @@ struct RopeParams {
     uint16_t* vout;               // transposed (prefill) or row-major (cache) values
     int64_t n, t0, ld, pad_to;
     int32_t B, Hkv, d, in_f32, v_transposed;
+    int32_t interleaved;          // pair i = dims (2i, 2i+1) instead of (i, i+d/2)
     const Tables* tab;            // host pointer; copied into kernel arguments
 };
 
@@ -41,6 +42,7 @@ struct PrefillParams {
     unsigned long long* counter;  // or null
     int64_t N, Np;
     int32_t B, Hq, Hkv, d, in_f32, out_f32;
+    int32_t interleaved;          // pair i = dims (2i, 2i+1) instead of (i, i+d/2)
     float scale;
 };
 
@@ -56,6 +58,7 @@ struct DecodeParams {
     float* partial;               // [B][Hkv][n_chunks][G][d+2]
     int64_t Lmax;
     int32_t B, Hq, Hkv, d, in_f32, out_f32, chunk, n_chunks;
+    int32_t interleaved;          // pair i = dims (2i, 2i+1) instead of (i, i+d/2)
     float scale;
 };
 

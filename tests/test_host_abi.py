@@ -7,6 +7,7 @@ import math
 import os
 import re
 
+import numpy as np
 import pytest
 
 import oracle
@@ -158,3 +159,62 @@ def test_count_rejects_bad_arguments():
     assert L.wpa_count_terms(3, 1e4, 1.0, 1, 0, 1, ctypes.byref(kept), ctypes.byref(total)) == -1
     assert L.wpa_count_terms(64, 0.5, 1.0, 1, 0, 1, ctypes.byref(kept), ctypes.byref(total)) == -1
     assert L.wpa_count_terms(64, 1e4, -1.0, 1, 0, 1, ctypes.byref(kept), ctypes.byref(total)) == -1
+
+
+# ------------------------------------------------------------------ RoPE variants
+
+def _llama32_table(d=128):
+    return wpa.llama3_inv_freq(d, 5e5, factor=32.0, low_freq_factor=1.0, high_freq_factor=4.0,
+                               original_max_position=8192)
+
+
+def test_llama3_inv_freq_matches_transformers():
+    """The Llama-3 frequency-scaling helper against transformers' own (fp32) computation."""
+    transformers = pytest.importorskip("transformers")
+    from transformers import LlamaConfig
+    from transformers import modeling_rope_utils as mru
+    cfg = LlamaConfig(hidden_size=3072, num_attention_heads=24, num_key_value_heads=8, head_dim=128,
+                      rope_theta=500000.0, max_position_embeddings=131072,
+                      rope_scaling={"rope_type": "llama3", "factor": 32.0, "low_freq_factor": 1.0,
+                                    "high_freq_factor": 4.0, "original_max_position_embeddings": 8192})
+    ref, _ = mru._compute_llama3_parameters(cfg, "cpu")
+    got = _llama32_table()
+    assert np.allclose(got, ref.double().numpy(), rtol=2e-6, atol=0)
+    assert np.all(np.diff(got) <= 0)                     # non-increasing, as the kernels need
+
+
+@pytest.mark.parametrize("alpha", [0.0, 0.5, 1.0, 2.0, math.inf])
+def test_table_count_matches_enumeration(alpha):
+    theta = _llama32_table(64)
+    for (n_q, q0, n_k) in [(1, 0, 1), (300, 0, 300), (1, 9999, 10000), (37, 250, 260)]:
+        ref = oracle.count_by_distance(64, 5e5, alpha, n_q, q0, n_k, inv_freq=theta)
+        assert wpa.count_terms(64, 5e5, alpha, n_q, q0, n_k, inv_freq=theta) == ref
+    W = wpa.thresholds(64, 5e5, alpha, inv_freq=theta)
+    thr = oracle.thresholds(64, 5e5, alpha, inv_freq=theta)
+    assert W == [min(int(math.floor(t)), 2**31 - 1) if math.isfinite(t) else 2**31 - 1 for t in thr]
+
+
+def test_rope_description_is_validated():
+    L = wpa.lib()
+    W = (ctypes.c_int32 * 32)()
+    up = np.linspace(0.1, 1.0, 32)                       # increasing: suffix property broken
+    r = wpa.Rope(0, up.ctypes.data)
+    assert L.wpa_thresholds_ex(64, 1e4, ctypes.byref(r), 1.0, W) == wpa.WPA_ERR_UNSUPPORTED
+    bad = np.full(32, 0.5)
+    bad[3] = float("nan")
+    r = wpa.Rope(0, bad.ctypes.data)
+    assert L.wpa_thresholds_ex(64, 1e4, ctypes.byref(r), 1.0, W) == wpa.WPA_ERR_UNSUPPORTED
+    r = wpa.Rope(7, None)
+    assert L.wpa_thresholds_ex(64, 1e4, ctypes.byref(r), 1.0, W) == wpa.WPA_ERR_INVALID
+    ok = _llama32_table(64)
+    r = wpa.Rope(1, ok.ctypes.data)                      # a table makes `base` irrelevant
+    assert L.wpa_thresholds_ex(64, 1.0, ctypes.byref(r), 1.0, W) == wpa.WPA_OK
+    # the _ex entry points check the description before anything else
+    rc = L.wpa_prefill_ex(FAKE, FAKE, FAKE, FAKE, None, None, 1, 128, 4, 2, 64, 1e4,
+                          ctypes.byref(wpa.Rope(0, up.ctypes.data)), 1.0, 0.0, 0, 0, None, FAKE,
+                          1 << 30, None)
+    assert rc == wpa.WPA_ERR_UNSUPPORTED
+    rc = L.wpa_decode_ex(FAKE, FAKE, FAKE, FAKE, None, FAKE, None, 2, 4096, 8, 2, 128, 1e4,
+                         ctypes.byref(wpa.Rope(3, None)), 1.0, 0.0, 0, 0, None, 0, FAKE, 1 << 30,
+                         None)
+    assert rc == wpa.WPA_ERR_INVALID

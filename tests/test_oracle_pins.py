@@ -323,3 +323,131 @@ def test_critical_dimension(d, base, N):
         ever_pruned += kept_i < N * (N + 1) // 2
     periods = 2.0 * np.pi * np.power(base, np.arange(d // 2) * 2.0 / d)
     assert ever_pruned == int(np.count_nonzero(periods < N - 1))
+
+
+# ------------------------------------------------------------------ RoPE variants
+# A frequency table theta_i (frequency-scaled RoPE) gives pair i the wavelength
+# 2*pi/theta_i; the interleaved layout pairs dims (2i, 2i+1).  Pins: complex rotation,
+# library attention at alpha = inf, the relative complex form, a layout permutation, and
+# hand values of the window table.
+
+def _dims(d, layout):
+    P = d // 2
+    if layout == "interleaved":
+        return np.arange(P) * 2, np.arange(P) * 2 + 1
+    return np.arange(P), np.arange(P) + P
+
+
+def _complex_rope_table(x, pos, theta, layout):
+    """Pair i as the complex number x[dx_i] + 1j*x[dy_i], times exp(1j*pos*theta_i)."""
+    x = np.asarray(x, dtype=np.float64)
+    dx, dy = _dims(x.shape[-1], layout)
+    z = x[..., dx] + 1j * x[..., dy]
+    ang = np.asarray(pos, dtype=np.float64).reshape((-1,) + (1,) * (x.ndim - 1)) * theta
+    zr = z * np.exp(1j * ang)
+    out = np.empty_like(x)
+    out[..., dx] = zr.real
+    out[..., dy] = zr.imag
+    return out
+
+
+def _llama3_table(d, base):
+    """Llama-3.2 style frequency scaling (factor 32, bands 1..4 of an 8192-token context),
+    written out here independently of the package helper."""
+    theta = base ** (-np.arange(d // 2) * 2.0 / d)
+    lam = 2 * np.pi / theta
+    out = theta.copy()
+    for i, l in enumerate(lam):
+        if l > 8192 / 1.0:
+            out[i] = theta[i] / 32.0
+        elif l >= 8192 / 4.0:
+            s = (8192 / l - 1.0) / (4.0 - 1.0)
+            out[i] = (1 - s) * theta[i] / 32.0 + s * theta[i]
+    return out
+
+
+@pytest.mark.parametrize("layout", ["half", "interleaved"])
+def test_rope_variants_are_complex_multiplication(layout):
+    q, _, _ = synth.prefill_inputs(1, 29, 3, 3, 16, "fp32", seed=31)
+    pos = np.arange(29) * 97 + 3
+    theta = np.sort(np.random.default_rng(2).uniform(1e-4, 2.0, 8))[::-1].copy()
+    got = oracle.rope(synth.to_oracle(q[0]), pos, 1e4, inv_freq=theta, layout=layout)
+    np.testing.assert_allclose(got, _complex_rope_table(_f64(q[0]), pos, theta, layout), rtol=0,
+                               atol=1e-12)
+
+
+@pytest.mark.parametrize("layout", ["half", "interleaved"])
+def test_full_window_variant_equals_library_sdpa(layout):
+    B, N, Hq, Hkv, d, base = 1, 41, 4, 2, 32, 5e5
+    q, k, v = synth.prefill_inputs(B, N, Hq, Hkv, d, "bf16", seed=33)
+    theta = _llama3_table(d, base)
+    out, lse, kept = oracle.prefill(synth.to_oracle(q), synth.to_oracle(k), synth.to_oracle(v),
+                                    base, math.inf, inv_freq=theta, layout=layout)
+    pos = np.arange(N)
+    qr = torch.from_numpy(_complex_rope_table(_f64(q[0]), pos, theta, layout))[None]
+    kr = torch.from_numpy(_complex_rope_table(_f64(k[0]), pos, theta, layout))[None]
+    G = Hq // Hkv
+    kr = kr.repeat_interleave(G, dim=2)
+    vv = v.double().repeat_interleave(G, dim=2)
+    ref = F.scaled_dot_product_attention(qr.transpose(1, 2), kr.transpose(1, 2),
+                                         vv.transpose(1, 2), is_causal=True)
+    np.testing.assert_allclose(out, ref.transpose(1, 2).numpy(), rtol=0, atol=1e-12)
+    assert kept == B * Hq * (d // 2) * N * (N + 1) // 2
+
+
+def _relative_form_table(q, k, v, qpos, kpos, theta, layout, alpha, scale):
+    """The relative complex form with a frequency table: Term_i = Re(zq_i conj(zk_i)
+    exp(1j*(tq - tk)*theta_i)), kept iff |tq - tk| <= alpha*2*pi/theta_i."""
+    dx, dy = _dims(q.shape[-1], layout)
+    zq = q[:, dx] + 1j * q[:, dy]
+    zk = k[:, dx] + 1j * k[:, dy]
+    dt = (np.asarray(qpos, np.float64)[:, None] - np.asarray(kpos, np.float64)[None, :])
+    terms = np.real(zq[:, None, :] * np.conj(zk[None, :, :]) * np.exp(1j * dt[..., None] * theta))
+    keep = np.abs(dt)[..., None] <= alpha * (2.0 * np.pi / theta)
+    logits = scale * np.where(keep, terms, 0.0).sum(-1)
+    Nq, Nk = logits.shape
+    logits = np.where(np.arange(Nk)[None, :] <= np.arange(Nq)[:, None], logits, -np.inf)
+    return scipy.special.softmax(logits, axis=-1) @ v, scipy.special.logsumexp(logits, axis=-1)
+
+
+@pytest.mark.parametrize("alpha", [0.5, 1.0, 2.0])
+@pytest.mark.parametrize("layout", ["half", "interleaved"])
+def test_windowed_variant_equals_relative_form(alpha, layout):
+    N, H, d = 40, 1, 16
+    q, k, v = synth.prefill_inputs(1, N, H, H, d, "fp32", seed=35)
+    pos = np.cumsum(np.random.default_rng(7).integers(0, 6, N))
+    theta = np.array([1.3, 0.9, 0.5, 0.31, 0.2, 0.11, 0.05, 0.02])     # decreasing
+    out, lse, _ = oracle.prefill(synth.to_oracle(q), synth.to_oracle(k), synth.to_oracle(v),
+                                 1e4, alpha, pos=pos, inv_freq=theta, layout=layout)
+    ref_o, ref_l = _relative_form_table(_f64(q[0, :, 0]), _f64(k[0, :, 0]), _f64(v[0, :, 0]),
+                                        pos, pos, theta, layout, alpha, 1.0 / math.sqrt(d))
+    np.testing.assert_allclose(out[0, :, 0], ref_o, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse[0, 0], ref_l, rtol=0, atol=1e-12)
+
+
+def test_interleaved_is_half_split_of_permuted_dims():
+    """Moving dims (2i, 2i+1) to (i, i+d/2) in q and k maps the interleaved layout onto the
+    half-split one with identical outputs (v is untouched)."""
+    B, N, Hq, Hkv, d = 1, 33, 2, 1, 16
+    q, k, v = synth.prefill_inputs(B, N, Hq, Hkv, d, "fp32", seed=37)
+    perm = np.concatenate([np.arange(d // 2) * 2, np.arange(d // 2) * 2 + 1])
+    a = oracle.prefill(synth.to_oracle(q), synth.to_oracle(k), synth.to_oracle(v), 100.0, 1.0,
+                       layout="interleaved")
+    b = oracle.prefill(synth.to_oracle(q[..., perm].contiguous()),
+                       synth.to_oracle(k[..., perm].contiguous()), synth.to_oracle(v), 100.0, 1.0)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+    assert a[2] == b[2]
+
+
+def test_table_thresholds_and_counts():
+    """alpha * 2*pi / theta_i by hand, and the three count enumerations agree on a table."""
+    theta = np.array([1.0, 0.5, 0.25, 0.001])
+    np.testing.assert_array_equal(oracle.thresholds(8, 1e4, 1.5, inv_freq=theta),
+                                  1.5 * (2.0 * math.pi / theta))
+    d, theta = 64, _llama3_table(64, 5e5)
+    for n_q, q0, n_k in [(300, 0, 300), (1, 4999, 5000), (70, 200, 250)]:
+        a = oracle.count_enumerate(d, 5e5, 1.0, n_q, q0, n_k, inv_freq=theta)
+        b = oracle.count_bruteforce(d, 5e5, 1.0, n_q, q0, n_k, inv_freq=theta)
+        c = oracle.count_by_distance(d, 5e5, 1.0, n_q, q0, n_k, inv_freq=theta)
+        assert a == b == c
