@@ -127,7 +127,10 @@ int wpa_prefill_attend(const void* q, void* out, float* lse, const int32_t* posi
 /* Bytes of the decode caches for B sequences of up to Lmax tokens.  Both layouts belong to
  * the library (K: rotated keys, pair-blocked [B][Hkv][d/16][Lmax][16] half; V: blocked by
  * 8 consecutive tokens, [B][Hkv][ceil(Lmax/8)][d][8] bf16); callers only size, allocate
- * and pass them. */
+ * and pass them.  Sequence b's part of each cache is one block of
+ * wpa_kcache_bytes(1, Lmax, Hkv, d) (wpa_vcache_bytes(...) for V) bytes at b times that
+ * offset, so a call with B = 1 on those offsets touches that sequence alone (how a ragged
+ * batch appends each sequence at its own start). */
 size_t wpa_kcache_bytes(int32_t B, int64_t Lmax, int32_t Hkv, int32_t d);
 size_t wpa_vcache_bytes(int32_t B, int64_t Lmax, int32_t Hkv, int32_t d);
 
@@ -218,6 +221,29 @@ int wpa_decode_ex(const void* q, const void* k_cache, const void* v_cache, const
                   double alpha, float scale, int32_t dtype, int32_t out_dtype,
                   unsigned long long* term_count, int32_t chunk_keys, void* workspace,
                   size_t ws_bytes, void* stream);
+
+/*
+ * Chunked prefill against the decode caches, with a ragged batch (a cached prefix per
+ * sequence).  Sequence b holds kv_len[b] tokens in the caches, the last Nq of which are
+ * the chunk's queries (tokens kv_len[b]-Nq .. kv_len[b]-1, positions = token indices).
+ * Each query attends causally to keys 0 .. its own token under the same per-pair window
+ * as wpa_prefill (WavePrune original, the pair-wise window; ATFlash abstract: one window
+ * test per pair and distance), so a prompt prefilled in chunks gets the rows a one-shot
+ * wpa_prefill would give it (up to rounding order).
+ *   q        [B][Nq][Hq][d] pre-RoPE (dtype), device; row i is token kv_len[b]-Nq+i
+ *   k_cache, v_cache  as for wpa_decode_ex, with the chunk's keys and values already
+ *            appended (wpa_kv_write_ex) under the same rope description
+ *   kv_len   [B] int32 device, each in [Nq, Lmax] (a precondition: the values live on the
+ *            device; the kernel clamps them into that range so no access leaves the caches)
+ *   out      [B][Nq][Hq][d] (out_dtype); lse [B][Hq][Nq] fp32 or NULL
+ *   term_count  as for wpa_prefill: kept (pair, query, key) terms, added
+ * No workspace: the kernel reads the caches in their own layouts.
+ */
+int wpa_prefill_cached(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* kv_len, void* out, float* lse, int32_t B, int32_t Nq,
+                       int64_t Lmax, int32_t Hq, int32_t Hkv, int32_t d, double base,
+                       const wpa_rope_t* rope, double alpha, float scale, int32_t dtype,
+                       int32_t out_dtype, unsigned long long* term_count, void* stream);
 
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char* wpa_last_error(void);

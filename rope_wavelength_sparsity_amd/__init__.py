@@ -38,7 +38,7 @@ EXPORTS = ("wpa_count_terms", "wpa_thresholds", "wpa_prefill_workspace_bytes", "
            "wpa_prefill_prepare", "wpa_prefill_attend", "wpa_kcache_bytes", "wpa_vcache_bytes",
            "wpa_kv_write", "wpa_decode_workspace_bytes", "wpa_decode", "wpa_count_terms_ex",
            "wpa_thresholds_ex", "wpa_prefill_ex", "wpa_prefill_prepare_ex", "wpa_prefill_attend_ex",
-           "wpa_kv_write_ex", "wpa_decode_ex", "wpa_last_error")
+           "wpa_kv_write_ex", "wpa_decode_ex", "wpa_prefill_cached", "wpa_last_error")
 
 
 class Rope(ctypes.Structure):
@@ -142,6 +142,9 @@ def lib():
     L.wpa_decode_ex.argtypes = [P, P, P, P, P, P, P, I32, I64, I32, I32, I32, D, P, D, F, I32, I32,
                                 P, I32, P, SZ, P]
     L.wpa_decode_ex.restype = ctypes.c_int
+    L.wpa_prefill_cached.argtypes = [P, P, P, P, P, P, I32, I32, I64, I32, I32, I32, D, P, D, F,
+                                     I32, I32, P, P]
+    L.wpa_prefill_cached.restype = ctypes.c_int
     L.wpa_last_error.argtypes = []
     L.wpa_last_error.restype = ctypes.c_char_p
     _lib = L
@@ -313,17 +316,25 @@ class KVCache:
         self.k = torch.empty(kcache_bytes(B, Lmax, Hkv, d), device=device, dtype=torch.uint8)
         self.v = torch.empty(vcache_bytes(B, Lmax, Hkv, d), device=device, dtype=torch.uint8)
 
-    def write(self, k, v, start: int, stream=None):
-        """Append pre-RoPE k, v [B][n][Hkv][d] at token indices start .. start+n-1."""
+    def write(self, k, v, start: int, stream=None, *, seq: int | None = None):
+        """Append pre-RoPE k, v [B][n][Hkv][d] at token indices start .. start+n-1; with
+        `seq`, k and v are [1][n][Hkv][d] and go to sequence `seq` alone (ragged batches)."""
         _dev(k, "k")
         _dev(v, "v")
-        if k.shape != v.shape or k.dim() != 4 or k.shape[0] != self.B or k.shape[2] != self.Hkv \
+        nb = self.B if seq is None else 1
+        if k.shape != v.shape or k.dim() != 4 or k.shape[0] != nb or k.shape[2] != self.Hkv \
                 or k.shape[3] != self.d or k.dtype != v.dtype:
-            raise ValueError("k, v must be [B][n][Hkv][d] of one dtype")
+            raise ValueError("k, v must be [%d][n][Hkv][d] of one dtype" % nb)
+        kc, vc = self.k.data_ptr(), self.v.data_ptr()
+        if seq is not None:
+            if not 0 <= seq < self.B:
+                raise ValueError("seq out of range")
+            kc += seq * kcache_bytes(1, self.Lmax, self.Hkv, self.d)
+            vc += seq * vcache_bytes(1, self.Lmax, self.Hkv, self.d)
         rope, keep = _rope(self.d, self.inv_freq, self.pairs)
-        _check(lib().wpa_kv_write_ex(_ptr(k), _ptr(v), int(start), k.shape[1], _ptr(self.k),
-                                     _ptr(self.v), self.B, self.Lmax, self.Hkv, self.d, self.base,
-                                     rope, _dtype_code(k), _stream(stream)))
+        _check(lib().wpa_kv_write_ex(_ptr(k), _ptr(v), int(start), k.shape[1], kc, vc, nb,
+                                     self.Lmax, self.Hkv, self.d, self.base, rope, _dtype_code(k),
+                                     _stream(stream)))
 
     def v_tokens(self):
         """A copy of the V cache as bf16 [B][Hkv][Lmax][d] (the cache itself is blocked by
@@ -361,6 +372,30 @@ def decode(q, cache: KVCache, kv_len, alpha: float, *, q_pos=None, scale: float 
                                _dtype_code(q), _dtype_code(out), _ptr(term_count),
                                int(chunk_keys), _ptr(workspace), workspace.numel(),
                                _stream(stream)))
+    return (out, lse) if lse is not None else out
+
+
+def prefill_cached(q, cache: KVCache, kv_len, alpha: float, *, scale: float | None = None,
+                   out=None, out_dtype=None, lse=None, want_lse: bool = False, term_count=None,
+                   stream=None):
+    """Chunked prefill: q [B][Nq][Hq][d] pre-RoPE holds the last Nq tokens of each sequence,
+    whose keys and values are already in `cache`; kv_len int32 device [B], each >= Nq."""
+    _dev(q, "q")
+    _dev(kv_len, "kv_len")
+    B, Nq, Hq, d = q.shape
+    if B != cache.B or d != cache.d or kv_len.dtype != torch.int32 or kv_len.numel() != B:
+        raise ValueError("q [B][Nq][Hq][d] and kv_len int32 [B] must match the cache")
+    if out is None:
+        out = torch.empty(q.shape, device=q.device, dtype=out_dtype or q.dtype)
+    _dev(out, "out")
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq, Nq), device=q.device, dtype=torch.float32)
+    rope, keep = _rope(d, cache.inv_freq, cache.pairs)
+    _check(lib().wpa_prefill_cached(_ptr(q), _ptr(cache.k), _ptr(cache.v), _ptr(kv_len),
+                                    _ptr(out), _ptr(lse), B, Nq, cache.Lmax, Hq, cache.Hkv, d,
+                                    cache.base, rope, float(alpha),
+                                    float(scale) if scale is not None else 0.0, _dtype_code(q),
+                                    _dtype_code(out), _ptr(term_count), _stream(stream)))
     return (out, lse) if lse is not None else out
 
 

@@ -109,7 +109,10 @@ struct Tile {
     static constexpr int WAVES_PER_EU = D == 64 ? 4 : 2;
 };
 
-template <int D, bool F32, bool HASPOS, bool COUNT>
+// CACHED: the keys and values are the decode caches (K pair-blocked with row stride
+// ldk = Lmax, V blocked by key octets) and sequence b holds kv_len[b] of them; its Nq
+// queries are its last Nq tokens (chunked prefill).  Positions are token indices.
+template <int D, bool F32, bool HASPOS, bool COUNT, bool CACHED>
 __global__ __launch_bounds__(64 * (Tile<D>::MAXW + 1))
 __attribute__((amdgpu_waves_per_eu(Tile<D>::WAVES_PER_EU)))
 void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
@@ -139,15 +142,26 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
     const int rg = w / L.Gc;
     const bool head_ok = hin < G;
     const int hq = g * G + (head_ok ? hin : 0);
-    const int N = (int)p.N;
-    const int qs = rb * 32 * L.R;
+    // Token geometry: NK keys (tokens 0..NK-1); the NQ rows of q and out are tokens
+    // tq0..NK-1.  Row groups start at multiples of 32 tokens, so the first sub-tile a wave
+    // visits holds the diagonal of all its rows.  (Plain prefill: NK = NQ = N, tq0 = 0.)
+    const int NQ = CACHED ? p.Nq : (int)p.N;
+    int NK = (int)p.N;
+    if constexpr (CACHED) {
+        NK = uniform(p.kv_len[b]);                     // in [Nq, Lmax] by contract; clamped
+        NK = NK < NQ ? NQ : (NK > (int)p.N ? (int)p.N : NK);     // so that no access leaves
+    }                                                  // the caches
+    const int tq0 = NK - NQ;
+    const int qs = (CACHED ? (tq0 & ~31) : 0) + rb * 32 * L.R;
+    if (CACHED && qs >= NK) return;                    // this sequence has fewer rows
     const int q0 = qs + 32 * rg;
     const bool producer = w == L.Gc * L.R;                 // the extra, loading wave
-    const bool wave_ok = !producer && head_ok && q0 < N;
-    const int qrow = q0 + l32;
-    const bool row_ok = qrow < N;
-    const int qrow_c = row_ok ? qrow : N - 1;
-    const int32_t* posb = p.pos + (HASPOS ? (int64_t)b * N : 0);
+    const bool wave_ok = !producer && head_ok && q0 < NK && (!CACHED || q0 + 31 >= tq0);
+    const int qrow = q0 + l32;                             // this lane's row, as a token
+    const bool row_ok = (!CACHED || qrow >= tq0) && qrow < NK;
+    const int qrow_c = row_ok ? qrow : (CACHED && qrow < tq0 ? tq0 : NK - 1);
+    const int qi = qrow_c - tq0;                           // ... and as a row of q / out
+    const int32_t* posb = p.pos + (HASPOS ? (int64_t)b * NK : 0);
     auto POS = [&](int t) -> int { return HASPOS ? posb[t] : t; };
     const int pq = POS(qrow_c);
 
@@ -162,7 +176,7 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
     u32xQ Qv;
     auto Qf = [&](int j) -> u32x4 { return u32x4{Qv[4 * j], Qv[4 * j + 1], Qv[4 * j + 2], Qv[4 * j + 3]}; };
     {
-        const int64_t qb = (((int64_t)b * N + qrow_c) * p.Hq + hq) * D;
+        const int64_t qb = (((int64_t)b * NQ + qi) * p.Hq + hq) * D;
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
             // pairs 8j..8j+7, one at a time (rolled loop: one sincos instance per block);
@@ -196,13 +210,16 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
         }
     }
 
-    const uint16_t* kpg = p.kp + ((int64_t)b * p.Hkv + g) * NB * p.Np * 16;
-    const uint16_t* vtg = p.vt + ((int64_t)b * p.Hkv + g) * D * p.Np;
-    const int row_end = (qs + 32 * L.R < N ? qs + 32 * L.R : N) - 1;
+    const int64_t ldk = CACHED ? p.ldk : p.Np;            // key row stride of kp
+    const uint16_t* kpg = p.kp + ((int64_t)b * p.Hkv + g) * NB * ldk * 16;
+    // V^T [d][Np] per head (plain) or the key-octet cache [ceil(Lmax/8)][d][8] (CACHED)
+    const uint16_t* vtg = p.vt + ((int64_t)b * p.Hkv + g) * D *
+                                     (CACHED ? (p.ldk + 7) / 8 * 8 : p.Np);
+    const int row_end = (qs + 32 * L.R < NK ? qs + 32 * L.R : NK) - 1;
     const int kt_last = row_end / BN;
-    const int pq_wg = POS(qs < N ? qs : N - 1);
-    const int pq_lo = POS(q0 < N ? q0 : N - 1);
-    const int pq_hi = POS(q0 + 31 < N ? q0 + 31 : N - 1);
+    const int pq_wg = POS(qs < NK ? qs : NK - 1);
+    const int pq_lo = POS(q0 < NK ? q0 : NK - 1);
+    const int pq_hi = POS(q0 + 31 < NK ? q0 + 31 : NK - 1);
 
     f32x16 O[NDB];
 #pragma unroll
@@ -238,7 +255,7 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
     // can be active anywhere in the tile (from the workgroup's smallest distance) are read.
     auto issue = [&](int kt, int stage) {
         const int ks = kt * BN;
-        const int kend = (ks + BN < N ? ks + BN : N) - 1;
+        const int kend = (ks + BN < NK ? ks + BN : NK) - 1;
         const int dmin_wg = uniform(pq_wg - POS(kend) > 0 ? pq_wg - POS(kend) : 0);
         while (plo_wg < P && tab.W[plo_wg] < dmin_wg) ++plo_wg;
         const int jlo = uniform(plo_wg) >> 3;
@@ -246,8 +263,18 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
         const int nI = nK + Tile<D>::VI + (HASPOS ? Tile<D>::PI : 0);
         for (int i = 0; i < nI; ++i) {
             if (i < nK) {
+                // 16-byte chunk `ch` of block j: half (ch & 1) of key ks + ch/2 (past the last
+                // key of a cache, the last key stands in: those keys are masked)
                 const int j = jlo + i / Tile<D>::KI, part = i % Tile<D>::KI;
-                const uint16_t* src = kpg + ((int64_t)j * p.Np + ks) * 16 + (part * 64 + lane) * 8;
+                const int ch = part * 64 + lane;
+                const uint16_t* src;
+                if constexpr (CACHED) {
+                    int t = ks + (ch >> 1);
+                    if (t > NK - 1) t = NK - 1;
+                    src = kpg + ((int64_t)j * ldk + t) * 16 + (ch & 1) * 8;
+                } else {
+                    src = kpg + ((int64_t)j * ldk + ks) * 16 + ch * 8;
+                }
                 __builtin_amdgcn_global_load_lds(src, (lds_ptr)&sK2[stage][j * BN * 16 + part * 512],
                                                  16, 0, 0);
             } else if (i < nK + Tile<D>::VI) {
@@ -255,13 +282,21 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
                 const int r = i - nK;
                 const int e = r * Tile<D>::RPI + lane / Tile<D>::CPR;
                 const int c = (lane % Tile<D>::CPR) ^ (e & 7);
-                const uint16_t* src = vtg + (int64_t)e * p.Np + ks + 8 * c;
+                const uint16_t* src;
+                if constexpr (CACHED) {
+                    // keys ks+8c .. ks+8c+7 form octet ks/8 + c of the cache
+                    int o = ks / 8 + c;
+                    if (o > (NK - 1) / 8) o = (NK - 1) / 8;
+                    src = vtg + ((int64_t)o * D + e) * 8;
+                } else {
+                    src = vtg + (int64_t)e * p.Np + ks + 8 * c;
+                }
                 __builtin_amdgcn_global_load_lds(src, (lds_ptr)&sV2[stage][r * Tile<D>::RPI * BN],
                                                  16, 0, 0);
             } else if (HASPOS) {
                 const int pi = i - nK - Tile<D>::VI;
                 const int t = ks + 64 * pi + lane;
-                const int32_t* src = posb + (t < N ? t : N - 1);
+                const int32_t* src = posb + (t < NK ? t : NK - 1);
                 __builtin_amdgcn_global_load_lds(src, (lds_ptr)&sPos2[stage][64 * pi], 4, 0, 0);
             }
         }
@@ -273,8 +308,8 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
 #pragma unroll 1
         for (int sub = NSUB - 1; sub >= 0; --sub) {      // nearest keys first
             const int k0 = ks + 32 * sub;
-            if (k0 > q0 + 31 || k0 >= N) continue;     // whole sub-tile above the diagonal
-            const int k_last = k0 + 31 < N ? k0 + 31 : N - 1;
+            if (k0 > q0 + 31 || k0 >= NK) continue;    // whole sub-tile above the diagonal
+            const int k_last = k0 + 31 < NK ? k0 + 31 : NK - 1;
             const int p_first = uniform(HASPOS ? sPos[k0 - ks] : k0);
             const int p_last = uniform(HASPOS ? sPos[k_last - ks] : k_last);
             const int dmin = pq_lo - p_last > 0 ? pq_lo - p_last : 0;
@@ -406,8 +441,18 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
                     const int e = 32 * db + l32, ch = 4 * sub + 2 * c + h;
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                    bf16x8 a = *reinterpret_cast<const bf16x8*>(
                         &sV[e * BN + ((ch ^ (e & 7)) << 3)]);
+                    if (CACHED && k0 + 32 > NK) {
+                        // cache slots past the last key: zero them (their p is 0, but the
+                        // slots may hold anything)
+                        u32x4 av = __builtin_bit_cast(u32x4, a);
+                        const int kb = k0 + 16 * c + 8 * h;
+#pragma unroll
+                        for (int t = 0; t < 4; ++t)
+                            av[t] &= (kb + 2 * t < NK ? 0xffffu : 0u) | (kb + 2 * t + 1 < NK ? 0xffff0000u : 0u);
+                        a = __builtin_bit_cast(bf16x8, av);
+                    }
                     O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                         a, __builtin_bit_cast(bf16x8, pb), O[db], 0, 0, 0);
                 }
@@ -445,7 +490,7 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
     const float l_tot = sum_with_partner(lsum, xaddr);
     if (!row_ok) return;
     const float inv = 1.0f / l_tot;
-    const int64_t ob = (((int64_t)b * N + qrow) * p.Hq + hq) * D;
+    const int64_t ob = (((int64_t)b * NQ + qi) * p.Hq + hq) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -464,7 +509,7 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
         }
     }
     if (p.lse && h == 0)
-        p.lse[((int64_t)b * p.Hq + hq) * N + qrow] = (m + log2f(l_tot)) * 0.6931471805599453f;
+        p.lse[((int64_t)b * p.Hq + hq) * NQ + qi] = (m + log2f(l_tot)) * 0.6931471805599453f;
 }
 
 template <int D, bool F32>
@@ -475,22 +520,27 @@ hipError_t launch_d(const PrefillParams& p, const Tables& t, hipStream_t s) {
     L.nhc = (G + MAXW - 1) / MAXW;                  // head chunks, as even as possible
     L.Gc = (G + L.nhc - 1) / L.nhc;
     L.R = MAXW / L.Gc > 1 ? MAXW / L.Gc : 1;
-    L.n_rb = (int)((p.N + 32 * L.R - 1) / (32 * L.R));
+    // row blocks per sequence (cached: up to 31 extra rows from aligning the first group)
+    const int64_t rows = p.kv_len ? (int64_t)p.Nq + 31 : p.N;
+    L.n_rb = (int)((rows + 32 * L.R - 1) / (32 * L.R));
     const int waves = L.Gc * L.R + 1;               // + the producer wave
     const int64_t nblk = (int64_t)L.n_rb * p.B * p.Hkv * L.nhc;
     dim3 grid((unsigned)nblk), block(64 * waves);
     const bool hp = p.pos != nullptr, cn = p.counter != nullptr;
-    if (hp && cn) prefill_kernel<D, F32, true, true><<<grid, block, 0, s>>>(p, t, L);
-    else if (hp) prefill_kernel<D, F32, true, false><<<grid, block, 0, s>>>(p, t, L);
-    else if (cn) prefill_kernel<D, F32, false, true><<<grid, block, 0, s>>>(p, t, L);
-    else prefill_kernel<D, F32, false, false><<<grid, block, 0, s>>>(p, t, L);
+    if (p.kv_len) {
+        if (cn) prefill_kernel<D, F32, false, true, true><<<grid, block, 0, s>>>(p, t, L);
+        else prefill_kernel<D, F32, false, false, true><<<grid, block, 0, s>>>(p, t, L);
+    } else if (hp && cn) prefill_kernel<D, F32, true, true, false><<<grid, block, 0, s>>>(p, t, L);
+    else if (hp) prefill_kernel<D, F32, true, false, false><<<grid, block, 0, s>>>(p, t, L);
+    else if (cn) prefill_kernel<D, F32, false, true, false><<<grid, block, 0, s>>>(p, t, L);
+    else prefill_kernel<D, F32, false, false, false><<<grid, block, 0, s>>>(p, t, L);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_prefill(const PrefillParams& p, const Tables& t, hipStream_t s) {
-    if (p.Np % Tile<64>::BN || p.Np % Tile<128>::BN) return hipErrorInvalidValue;
+    if (!p.kv_len && (p.Np % Tile<64>::BN || p.Np % Tile<128>::BN)) return hipErrorInvalidValue;
     if (p.d == 64) return p.in_f32 ? launch_d<64, true>(p, t, s) : launch_d<64, false>(p, t, s);
     return p.in_f32 ? launch_d<128, true>(p, t, s) : launch_d<128, false>(p, t, s);
 }

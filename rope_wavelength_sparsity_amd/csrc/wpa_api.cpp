@@ -277,7 +277,7 @@ int wpa_prefill_attend_ex(const void* q, void* out, float* lse, const int32_t* p
     wpa::PrefillParams pp{};
     pp.interleaved = interleaved(rope);
     pp.q = q; pp.kp = kp; pp.vt = kp + (size_t)B * Hkv * Np * d; pp.out = out; pp.lse = lse;
-    pp.pos = positions; pp.counter = term_count; pp.N = N; pp.Np = Np; pp.B = B; pp.Hq = Hq;
+    pp.pos = positions; pp.counter = term_count; pp.N = N; pp.Np = Np; pp.ldk = Np; pp.B = B; pp.Hq = Hq;
     pp.Hkv = Hkv; pp.d = d; pp.in_f32 = dtype == WPA_FP32; pp.out_f32 = out_dtype == WPA_FP32;
     pp.scale = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)d));
     hipError_t e = wpa::launch_prefill(pp, tab, static_cast<hipStream_t>(stream));
@@ -415,6 +415,40 @@ int wpa_decode_ex(const void* q, const void* k_cache, const void* v_cache, const
     dp.scale = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)d));
     hipError_t e = wpa::launch_decode(dp, tab, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(WPA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int wpa_prefill_cached(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* kv_len, void* out, float* lse, int32_t B, int32_t Nq,
+                       int64_t Lmax, int32_t Hq, int32_t Hkv, int32_t d, double base,
+                       const wpa_rope_t* rope, double alpha, float scale, int32_t dtype,
+                       int32_t out_dtype, unsigned long long* term_count, void* stream) {
+    int rc = check_common(d, base, rope, alpha);
+    if (rc) return rc;
+    if (B < 1 || Nq < 1 || Lmax < 1 || Hq < 1 || Hkv < 1) return fail(WPA_ERR_INVALID, "B, Nq, Lmax, Hq, Hkv must be >= 1");
+    if (Nq > Lmax) return fail(WPA_ERR_INVALID, "Nq (%d) exceeds Lmax (%lld)", Nq, (long long)Lmax);
+    if (Hq % Hkv) return fail(WPA_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+    if (Lmax >= (int64_t)INT32_MAX - 64) return fail(WPA_ERR_INVALID, "Lmax too large");
+    if (dtype != WPA_BF16 && dtype != WPA_FP32) return fail(WPA_ERR_INVALID, "dtype must be WPA_BF16 or WPA_FP32");
+    if (out_dtype != WPA_BF16 && out_dtype != WPA_FP32) return fail(WPA_ERR_INVALID, "out_dtype must be WPA_BF16 or WPA_FP32");
+    if (std::isnan(scale)) return fail(WPA_ERR_INVALID, "scale is NaN");
+    if (!q || !k_cache || !v_cache || !kv_len || !out) return fail(WPA_ERR_INVALID, "null pointer");
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+        return fail(WPA_ERR_INVALID, "q, caches and out must be 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(kv_len) & 3u) return fail(WPA_ERR_INVALID, "kv_len must be 4-byte aligned");
+    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(WPA_ERR_INVALID, "lse must be 4-byte aligned");
+    if (term_count && (reinterpret_cast<uintptr_t>(term_count) & 7u)) return fail(WPA_ERR_INVALID, "term_count must be 8-byte aligned");
+    wpa::Tables tab;
+    make_tables(d, base, rope, alpha, &tab);
+    wpa::PrefillParams pp{};
+    pp.interleaved = interleaved(rope);
+    pp.q = q; pp.kp = static_cast<const uint16_t*>(k_cache); pp.vt = static_cast<const uint16_t*>(v_cache);
+    pp.kv_len = kv_len; pp.out = out; pp.lse = lse; pp.pos = nullptr; pp.counter = term_count;
+    pp.N = Lmax; pp.Np = 0; pp.ldk = Lmax; pp.Nq = Nq; pp.B = B; pp.Hq = Hq;
+    pp.Hkv = Hkv; pp.d = d; pp.in_f32 = dtype == WPA_FP32; pp.out_f32 = out_dtype == WPA_FP32;
+    pp.scale = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)d));
+    hipError_t e = wpa::launch_prefill(pp, tab, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(WPA_ERR_HIP, "cached prefill launch: %s", hipGetErrorString(e));
     return ok();
 }
 

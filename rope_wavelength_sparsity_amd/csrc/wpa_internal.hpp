@@ -33,14 +33,17 @@ struct RopeParams {
 };
 
 struct PrefillParams {
-    const void* q;                // [B][N][Hq][d]
-    const uint16_t* kp;           // [B][Hkv][d/16][Np][16]
-    const uint16_t* vt;           // [B][Hkv][d][Np]
+    const void* q;                // [B][N][Hq][d]  (cached: [B][Nq][Hq][d])
+    const uint16_t* kp;           // [B][Hkv][d/16][ldk][16]
+    const uint16_t* vt;           // [B][Hkv][d][Np]  (cached: V cache [B][Hkv][ceil(ldk/8)][d][8])
+    const int32_t* kv_len;        // cached (chunked) prefill: [B] keys per sequence; else null
+    int64_t ldk;                  // key row stride of kp: Np, or Lmax of the caches
+    int32_t Nq;                   // cached: queries per sequence (its last Nq tokens)
     void* out;                    // [B][N][Hq][d]
     float* lse;                   // [B][Hq][N] or null
     const int32_t* pos;           // [B][N] or null
     unsigned long long* counter;  // or null
-    int64_t N, Np;
+    int64_t N, Np;                // N: tokens (cached: Lmax); Np: workspace padding
     int32_t B, Hq, Hkv, d, in_f32, out_f32;
     int32_t interleaved;          // pair i = dims (2i, 2i+1) instead of (i, i+d/2)
     float scale;

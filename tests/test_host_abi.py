@@ -138,6 +138,36 @@ def test_decode_rejects_bad_arguments(kw, code):
     assert _decode_rc(**kw) == code
 
 
+def _cached_rc(**kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, lens=FAKE, out=FAKE, lse=None, B=2, Nq=64, Lmax=4096,
+             Hq=8, Hkv=2, d=128, base=5e5, rope=None, alpha=1.0, scale=0.0, dtype=0, odt=1,
+             cnt=None)
+    a.update(kw)
+    return wpa.lib().wpa_prefill_cached(a["q"], a["kc"], a["vc"], a["lens"], a["out"], a["lse"],
+                                        a["B"], a["Nq"], a["Lmax"], a["Hq"], a["Hkv"], a["d"],
+                                        a["base"], a["rope"], a["alpha"], a["scale"], a["dtype"],
+                                        a["odt"], a["cnt"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=96), wpa.WPA_ERR_UNSUPPORTED),
+    (dict(Hq=6, Hkv=4), wpa.WPA_ERR_INVALID),
+    (dict(Nq=0), wpa.WPA_ERR_INVALID),
+    (dict(Nq=5000), wpa.WPA_ERR_INVALID),
+    (dict(Lmax=0), wpa.WPA_ERR_INVALID),
+    (dict(lens=None), wpa.WPA_ERR_INVALID),
+    (dict(kc=None), wpa.WPA_ERR_INVALID),
+    (dict(lens=ctypes.c_void_p((1 << 20) + 2)), wpa.WPA_ERR_INVALID),
+    (dict(vc=ctypes.c_void_p((1 << 20) + 8)), wpa.WPA_ERR_INVALID),
+    (dict(odt=3), wpa.WPA_ERR_INVALID),
+    (dict(alpha=-2.0), wpa.WPA_ERR_INVALID),
+    (dict(scale=float("nan")), wpa.WPA_ERR_INVALID),
+])
+def test_prefill_cached_rejects_bad_arguments(kw, code):
+    assert _cached_rc(**kw) == code
+    assert wpa.lib().wpa_last_error().decode() != ""
+
+
 def test_kv_write_rejects_out_of_range():
     L = wpa.lib()
     rc = L.wpa_kv_write(FAKE, FAKE, 4000, 200, FAKE, FAKE, 1, 4096, 2, 64, 1e4, 0, None)
