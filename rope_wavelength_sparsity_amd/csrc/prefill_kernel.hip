@@ -39,6 +39,8 @@
 //   V operand (A of the P*V step): V^T rows (dims) from LDS, key-contiguous, 16-byte
 //     chunks XOR-swizzled by the row index against bank conflicts.
 //   O^T accumulator: lane = query row, so the softmax rescale is a per-lane scalar.
+#include <type_traits>
+
 #include "wpa_device.hpp"
 #include "wpa_internal.hpp"
 
@@ -46,7 +48,7 @@ namespace wpa {
 
 namespace {
 
-constexpr float kTau = 8.0f;      // lazy-rescale threshold (log2 units)
+constexpr float kSumTau = 256.0f;  // lazy rescale: a half-row's probabilities may sum to 2^8
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
@@ -88,6 +90,31 @@ __device__ inline u32x4 lead_mask(int nz) {
     return q;
 }
 
+// The element e of an 8-pair block alone (both halves), as a mask on the packed block.
+__device__ inline u32x4 pair_mask(int e) {
+    u32x4 q;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+        q[t] = (e >> 1) == t ? ((e & 1) ? 0xffff0000u : 0xffffu) : 0u;
+    return q;
+}
+
+// Number of registers r of a sub-tile with off(r) = 16(r/8) + r%8 <= x.
+__device__ inline int n_off_le(int x) {
+    const int a = x + 1 < 0 ? 0 : (x + 1 > 8 ? 8 : x + 1);
+    const int b = x - 15 < 0 ? 0 : (x - 15 > 8 ? 8 : x - 15);
+    return a + b;
+}
+
+// f(std::integral_constant<int, v>{}) for a run-time v in [0, N).
+template <int N, class F>
+__device__ inline void dispatch(int v, F&& f) {
+    if constexpr (N > 0) {
+        if (v == N - 1) f(std::integral_constant<int, N - 1>{});
+        else dispatch<N - 1>(v, f);
+    }
+}
+
 struct Launch {
     int Gc, R, nhc, n_rb;
 };
@@ -103,18 +130,27 @@ struct Tile {
     static constexpr int RPI = 64 / CPR;            // V^T rows per wave load
     // Compute waves per workgroup (plus one producer wave) and the waves per SIMD the
     // register budget must allow.  d=64 fits 128 VGPRs: 4 waves per SIMD, two 8-wave
-    // workgroups per CU (64 KB of LDS each).  d=128 needs up to 256: 2 per SIMD, one
-    // workgroup per CU.
-    static constexpr int MAXW = 7;
-    static constexpr int WAVES_PER_EU = D == 64 ? 4 : 2;
+    // workgroups per CU (64 KB of LDS each).  d=128 fits 168: 3 per SIMD, one 10-wave
+    // workgroup per CU; with explicit positions (more registers) 2 per SIMD, 8 waves.
+    static constexpr int maxw(bool haspos) { return D == 64 || haspos ? 7 : 9; }
+    static constexpr int waves_per_eu(bool haspos) { return D == 64 ? 4 : (haspos ? 2 : 3); }
+    // Slot swizzle of V^T row e (16-byte chunks).  The P*V read has lane l fetch row
+    // e = l%32 (+32db): any 8 consecutive rows, and any 16, must land on distinct
+    // (bank-group) slots.  d=64 rows are 256 bytes (16 slots): e mod 16.  d=128 rows are
+    // 128 bytes, two per 256-byte bank window: e mod 8, with bit 0 flipped for rows 8..15
+    // of each 16.
+    __device__ static int swz(int e) {
+        if constexpr (D == 64) return e & 15;
+        else return (e & 7) ^ ((e >> 3) & 1);
+    }
 };
 
 // CACHED: the keys and values are the decode caches (K pair-blocked with row stride
 // ldk = Lmax, V blocked by key octets) and sequence b holds kv_len[b] of them; its Nq
 // queries are its last Nq tokens (chunked prefill).  Positions are token indices.
 template <int D, bool F32, bool HASPOS, bool COUNT, bool CACHED>
-__global__ __launch_bounds__(64 * (Tile<D>::MAXW + 1))
-__attribute__((amdgpu_waves_per_eu(Tile<D>::WAVES_PER_EU)))
+__global__ __launch_bounds__(64 * (Tile<D>::maxw(HASPOS) + 1))
+__attribute__((amdgpu_waves_per_eu(Tile<D>::waves_per_eu(HASPOS))))
 void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
     constexpr int NB = D / 16;
     constexpr int P = D / 2;
@@ -278,10 +314,10 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
                 __builtin_amdgcn_global_load_lds(src, (lds_ptr)&sK2[stage][j * BN * 16 + part * 512],
                                                  16, 0, 0);
             } else if (i < nK + Tile<D>::VI) {
-                // V^T rows e; the 16-byte chunk c of row e sits in slot c ^ (e & 7)
+                // V^T rows e; the 16-byte chunk c of row e sits in slot c ^ swz(e)
                 const int r = i - nK;
                 const int e = r * Tile<D>::RPI + lane / Tile<D>::CPR;
-                const int c = (lane % Tile<D>::CPR) ^ (e & 7);
+                const int c = (lane % Tile<D>::CPR) ^ Tile<D>::swz(e);
                 const uint16_t* src;
                 if constexpr (CACHED) {
                     // keys ks+8c .. ks+8c+7 form octet ks/8 + c of the cache
@@ -302,161 +338,245 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
         }
     };
 
+    // Softmax step and P*V of one sub-tile (keys k0 .. k0+31, `sub` within its tile) whose
+    // scores come from scores(): probabilities relative to the running max m, packed to bf16
+    // as P*V takes them, and their sum over this half's 16 keys (two per v_dot2).
+    // m moves only when the probabilities would grow past 2^8: every probability is at most
+    // the half-row sum, so a wave-wide vote on that sum replaces a max over the scores.  The
+    // rare sub-tile that fails it (and the first one, which sets m) recomputes its scores
+    // and takes the row max.
+    const int v_row = l32 * BN;                               // V^T row of this lane (db = 0)
+    const int v_x = (h ^ Tile<D>::swz(l32)) << 3;             // its slot swizzle, in elements
+    auto finish = [&](auto&& scores, int sub, int k0, const uint16_t* sV) {
+        uint32_t wd[8];
+        float psum = 0.f;
+        auto probs = [&](const f32x16& S) {
+            psum = 0.f;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                wd[t] = pack_bf16x2(__builtin_amdgcn_exp2f(S[2 * t]), __builtin_amdgcn_exp2f(S[2 * t + 1]));
+                psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wd[t]),
+                                                       __builtin_bit_cast(bf16x2, 0x3f803f80u), psum, false);
+            }
+        };
+        bool redo = !started;
+        if (started) {
+            probs(scores());
+            redo = __any(psum > kSumTau);
+        }
+        if (redo) {
+            f32x16 S = scores();
+            float mx = S[0];
+#pragma unroll
+            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
+            mx = max_with_partner(mx, xaddr);
+            float shift;
+            if (!started) {
+                set_m(mx);
+                shift = m;
+                started = true;
+            } else {
+                const float m_old = m;
+                set_m(m + fmaxf(mx, 0.f));
+                shift = m - m_old;
+                const float alpha = __builtin_amdgcn_exp2f(-shift);
+                lsum *= alpha;
+#pragma unroll
+                for (int i = 0; i < NDB; ++i) O[i] *= alpha;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) S[r] -= shift;
+            probs(S);
+        }
+        lsum += psum;
+
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const u32x4 pb = u32x4{wd[4 * c], wd[4 * c + 1], wd[4 * c + 2], wd[4 * c + 3]};
+            // chunk 4sub + 2c + h of row e sits in slot (4sub + 2c + h) ^ swz(e)
+            const uint16_t* vp = sV + v_row + ((((4 * sub + 2 * c) << 3)) ^ v_x);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                bf16x8 a = *reinterpret_cast<const bf16x8*>(vp + 32 * db * BN);
+                if (CACHED && k0 + 32 > NK) {
+                    // cache slots past the last key: zero them (their p is 0, but the slots
+                    // may hold anything)
+                    u32x4 av = __builtin_bit_cast(u32x4, a);
+                    const int kb = k0 + 16 * c + 8 * h;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        av[t] &= (kb + 2 * t < NK ? 0xffffu : 0u) | (kb + 2 * t + 1 < NK ? 0xffff0000u : 0u);
+                    a = __builtin_bit_cast(bf16x8, av);
+                }
+                O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    a, __builtin_bit_cast(bf16x8, pb), O[db], 0, 0, 0);
+            }
+        }
+    };
+
     // One key tile from LDS: its 32-key sub-tiles, nearest keys first.
     auto compute = [&](int kt, const uint16_t* sK, const uint16_t* sV, const int32_t* sPos) {
         const int ks = kt * BN;
-#pragma unroll 1
-        for (int sub = NSUB - 1; sub >= 0; --sub) {      // nearest keys first
-            const int k0 = ks + 32 * sub;
-            if (k0 > q0 + 31 || k0 >= NK) continue;    // whole sub-tile above the diagonal
-            const int k_last = k0 + 31 < NK ? k0 + 31 : NK - 1;
-            const int p_first = uniform(HASPOS ? sPos[k0 - ks] : k0);
-            const int p_last = uniform(HASPOS ? sPos[k_last - ks] : k_last);
-            const int dmin = pq_lo - p_last > 0 ? pq_lo - p_last : 0;
-            const int dmax = pq_hi - p_first;
-            while (w_lo < dmin) {
+        auto POSL = [&](int t) -> int { return uniform(HASPOS ? sPos[t - ks] : t); };
+
+        // Plain tile: every key precedes every row of the wave (no causal mask), none is past
+        // the last key, and no window edge falls inside the tile's distance range, so every
+        // pair is dead or fully active on the whole tile.  The band is then fixed for the tile
+        // and its sub-tiles run the chain of that block set, known at compile time.  The
+        // tile's smallest distance is its nearest sub-tile's, so moving plo there is the step
+        // that sub-tile would take anyway.
+        bool plain = false;
+        if (started && ks + BN - 1 < q0 && ks + BN <= NK) {
+            const int dmin_t = pq_lo - POSL(ks + BN - 1);
+            const int dmax_t = pq_hi - POSL(ks);
+            while (w_lo < dmin_t) {
                 ++plo;
                 w_lo = plo < P ? tab.W[plo] : INT32_MAX;
             }
-            while (w_full < dmax) {
-                ++pfull;
-                w_full = pfull < P ? tab.W[pfull] : INT32_MAX;
+            if (w_lo >= dmax_t && plo < P) {
+                pfull = plo;                    // no W in [dmin_t, dmax_t): plo is also the
+                w_full = w_lo;                  // first pair active at dmax_t
+                if (COUNT && row_ok) cnt += (uint64_t)(16 * NSUB) * (uint64_t)(P - pfull);
+                plain = true;
+            }
+        }
+        const uint16_t* kl = sK + perm_row(l32) * 16 + 8 * h;   // this lane's K row (sub 0)
+
+#pragma unroll 1
+        for (int sub = NSUB - 1; sub >= 0; --sub) {      // nearest keys first
+            const int k0 = ks + 32 * sub;
+            if (!plain) {
+                if (k0 > q0 + 31 || k0 >= NK) continue;    // whole sub-tile above the diagonal
+                const int k_last = k0 + 31 < NK ? k0 + 31 : NK - 1;
+                const int dmin = pq_lo - POSL(k_last) > 0 ? pq_lo - POSL(k_last) : 0;
+                const int dmax = pq_hi - POSL(k0);
+                while (w_lo < dmin) {
+                    ++plo;
+                    w_lo = plo < P ? tab.W[plo] : INT32_MAX;
+                }
+                while (w_full < dmax) {
+                    ++pfull;
+                    w_full = pfull < P ? tab.W[pfull] : INT32_MAX;
+                }
             }
             const int jf = pfull >> 3;
             if (pfull != q_key && jf < NB) {
                 qm = Qf(jf) & lead_mask(pfull - 8 * jf);
                 q_key = pfull;
             }
-
-            // fully active blocks on MFMA, accumulating onto -m: block jf (masked) first,
-            // then the blocks above it
-            const int kbase = (32 * sub + perm_row(l32)) * 16 + 8 * h;
-            // (K fragments are read next to their MFMA: reading every block up front costs the
-            // d=64 kernel its fourth wave per SIMD, which hides more latency than it saves)
-            const f16x8 kjf = *reinterpret_cast<const f16x8*>(&sK[(jf < NB ? jf : 0) * BN * 16 + kbase]);
-            f32x16 S = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                __builtin_bit_cast(f16x8, ones_blk), __builtin_bit_cast(f16x8, negm_blk), f32x16{}, 0, 0, 0);
-            if (jf < NB)
-                S = __builtin_amdgcn_mfma_f32_32x32x16_f16(kjf, __builtin_bit_cast(f16x8, qm), S, 0, 0, 0);
-#pragma unroll
-            for (int j = NB - 1; j >= 1; --j) {
-                if (j > jf) {
-                    const f16x8 a = *reinterpret_cast<const f16x8*>(&sK[j * BN * 16 + kbase]);
-                    S = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(f16x8, Qf(j)), S, 0, 0, 0);
-                }
-            }
-
+            const uint16_t* ksub = kl + 32 * sub * 16;           // this lane's K row, this sub-tile
+            auto K = [&](int j) { return *reinterpret_cast<const f16x8*>(ksub + j * BN * 16); };
             const bool diag = k0 + 31 > q0;
-            // register r of half h holds key k0 + 16(r/8) + (r%8) + 8h: causal iff that <= qrow
+            // register r of half h holds key k0 + off(r) + 8h, off(r) = 16(r/8) + r%8:
+            // causal iff off(r) <= lim
             const int lim = qrow - k0 - 8 * h;
-            if (COUNT && row_ok) {
-                int nv = 16;
-                if (diag) {
-                    nv = 0;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) nv += (16 * (r >> 3) + (r & 7) <= lim);
-                }
-                cnt += (uint64_t)nv * (uint64_t)(P - pfull);
-            }
 
-            // straddling pairs on VALU, per element
-            if (plo < pfull) {
+            // Scores on one MFMA chain: the fully active blocks and a bias step that adds -m.
+            // With straddling pairs, the chain starts with each of them as its own step (Q
+            // operand holding that pair alone), after which the elements outside its window go
+            // back to zero.  Pair windows grow with the pair index, so an element outside pair
+            // e's window is outside every earlier one's too and still holds zero: the reset
+            // removes exactly pair e's term.  A plain tile runs the chain of its block set
+            // unrolled (no per-block branches).
+            auto full_blocks = [&](f32x16 S) -> f32x16 {
+                if (jf < NB) S = __builtin_amdgcn_mfma_f32_32x32x16_f16(K(jf), __builtin_bit_cast(f16x8, qm), S, 0, 0, 0);
 #pragma unroll
-                for (int j = 0; j < NB; ++j) {
-                    const int e_lo = plo - 8 * j > 0 ? plo - 8 * j : 0;
-                    const int e_hi = pfull - 8 * j < 8 ? pfull - 8 * j : 8;
-                    if (e_lo >= e_hi) continue;
-                    const u32x4 mine = Qf(j);
-                    u32x4 oth;
+                for (int j = NB - 1; j >= 1; --j)
+                    if (j > jf) S = __builtin_amdgcn_mfma_f32_32x32x16_f16(K(j), __builtin_bit_cast(f16x8, Qf(j)), S, 0, 0, 0);
+                return S;
+            };
+            auto bias = [&](const f32x16& S) {
+                return __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                    __builtin_bit_cast(f16x8, ones_blk), __builtin_bit_cast(f16x8, negm_blk), S, 0, 0, 0);
+            };
+            auto scores = [&]() -> f32x16 {
+                f32x16 S;
+                if (plain) {
+                    dispatch<NB>(jf, [&](auto jfc) {
+                        constexpr int JF = decltype(jfc)::value;
+                        f32x16 T = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                            K(JF), __builtin_bit_cast(f16x8, qm), f32x16{}, 0, 0, 0);
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) oth[t] = partner32(mine[t], xaddr);
-                    const u32x4 qx = h ? oth : mine;
-                    const u32x4 qy = h ? mine : oth;
-                    for (int e = e_lo; e < e_hi; ++e) {
-                        const int sh = (e & 1) * 16;
-                        const float fqx = f16_bits_to_f32((sel4(qx, e >> 1) >> sh) & 0xffffu);
-                        const float fqy = f16_bits_to_f32((sel4(qy, e >> 1) >> sh) & 0xffffu);
-                        const int Wi = tab.W[8 * j + e];
+                        for (int j = JF + 1; j < NB; ++j)
+                            T = __builtin_amdgcn_mfma_f32_32x32x16_f16(K(j), __builtin_bit_cast(f16x8, Qf(j)), T, 0, 0, 0);
+                        S = T;
+                    });
+                    return bias(S);
+                }
+                if (!HASPOS && plo < pfull) {
+                    f32x16 T = {};
+#pragma unroll 1
+                    for (int e = plo; e < pfull; ++e) {
+                        const u32x4 qe = Qf(e >> 3) & pair_mask(e & 7);
+                        T = __builtin_amdgcn_mfma_f32_32x32x16_f16(K(e >> 3), __builtin_bit_cast(f16x8, qe), T, 0, 0, 0);
+                        const int t = lim - tab.W[e];              // inside iff off(r) >= t
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int kl = 32 * sub + key_of_reg(r, h);
-                            const int dist = pq - (HASPOS ? sPos[kl] : ks + kl);
-                            const uint16_t* kr = &sK[(j * BN + kl) * 16];
-                            const float kx = f16_bits_to_f32(kr[e]);
-                            const float ky = f16_bits_to_f32(kr[8 + e]);
-                            const bool on = dist <= Wi;
-                            S[r] += on ? (fqx * kx + fqy * ky) : 0.f;
-                            if (COUNT)
-                                cnt += (on && row_ok && 16 * (r >> 3) + (r & 7) <= lim) ? 1 : 0;
+                        for (int r = 0; r < 16; ++r)
+                            if (16 * (r >> 3) + (r & 7) < t) T[r] = 0.f;
+                    }
+                    S = bias(full_blocks(T));
+                } else {
+                    S = full_blocks(bias(f32x16{}));
+                }
+                if constexpr (HASPOS) {
+                    // arbitrary positions: straddling pairs per element on VALU
+                    if (plo < pfull) {
+#pragma unroll
+                        for (int j = 0; j < NB; ++j) {
+                            const int e_lo = plo - 8 * j > 0 ? plo - 8 * j : 0;
+                            const int e_hi = pfull - 8 * j < 8 ? pfull - 8 * j : 8;
+                            if (e_lo >= e_hi) continue;
+                            const u32x4 mine = Qf(j);
+                            u32x4 oth;
+#pragma unroll
+                            for (int t = 0; t < 4; ++t) oth[t] = partner32(mine[t], xaddr);
+                            const u32x4 qx = h ? oth : mine;
+                            const u32x4 qy = h ? mine : oth;
+                            for (int e = e_lo; e < e_hi; ++e) {
+                                const int sh = (e & 1) * 16;
+                                const float fqx = f16_bits_to_f32((sel4(qx, e >> 1) >> sh) & 0xffffu);
+                                const float fqy = f16_bits_to_f32((sel4(qy, e >> 1) >> sh) & 0xffffu);
+                                const int Wi = tab.W[8 * j + e];
+#pragma unroll
+                                for (int r = 0; r < 16; ++r) {
+                                    const int kk = 32 * sub + key_of_reg(r, h);
+                                    const uint16_t* kr = &sK[(j * BN + kk) * 16];
+                                    const float kx = f16_bits_to_f32(kr[e]);
+                                    const float ky = f16_bits_to_f32(kr[8 + e]);
+                                    S[r] += (pq - sPos[kk] <= Wi) ? (fqx * kx + fqy * ky) : 0.f;
+                                }
+                            }
                         }
                     }
                 }
-            }
+                // causal mask (raw scores; the scale is folded into the exponent)
+                if (diag) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (16 * (r >> 3) + (r & 7) > lim) S[r] = -INFINITY;
+                }
+                return S;
+            };
 
-            // causal mask, sub-tile max (raw scores; the scale is folded into the exponent)
-            if (diag) {
+            if (COUNT && row_ok && !plain) {
+                // kept terms of this row: fully active pairs on every causal key, straddling
+                // pairs on the causal keys inside their window
+                const int nv = diag ? n_off_le(lim) : 16;
+                cnt += (uint64_t)nv * (uint64_t)(P - pfull);
+                for (int e = plo; e < pfull; ++e) {
+                    if constexpr (HASPOS) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (16 * (r >> 3) + (r & 7) > lim) S[r] = -INFINITY;
-            }
-            // sub-tile max relative to m (absolute on the first sub-tile) over this half's
-            // keys; the row max (both halves) is only formed when m moves
-            float mx = S[0];
-#pragma unroll
-            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
-            if (!started) {
-                mx = max_with_partner(mx, xaddr);
-                set_m(mx);
-#pragma unroll
-                for (int r = 0; r < 16; ++r) S[r] -= m;
-                started = true;
-            } else if (__any(mx > kTau)) {
-                // move the max only when it grew by more than 2^kTau
-                mx = max_with_partner(mx, xaddr);
-                const float m_old = m;
-                set_m(m + fmaxf(mx, 0.f));
-                const float shift = m - m_old;
-                const float alpha = __builtin_amdgcn_exp2f(-shift);
-                lsum *= alpha;
-#pragma unroll
-                for (int i = 0; i < NDB; ++i) O[i] *= alpha;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) S[r] -= shift;
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) S[r] = __builtin_amdgcn_exp2f(S[r]);
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                // the packed words, and the row sum of the probabilities as they enter P*V
-                // (bf16), two per instruction; the dot products take the words as scalars
-                // (taken back out of a vector, the compiler fed them one same register)
-                uint32_t wd[4];
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    wd[t] = pack_bf16x2(S[8 * c + 2 * t], S[8 * c + 2 * t + 1]);
-                    lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wd[t]),
-                                                           __builtin_bit_cast(bf16x2, 0x3f803f80u), lsum, false);
-                }
-                const u32x4 pb = u32x4{wd[0], wd[1], wd[2], wd[3]};
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    const int e = 32 * db + l32, ch = 4 * sub + 2 * c + h;
-                    bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                        &sV[e * BN + ((ch ^ (e & 7)) << 3)]);
-                    if (CACHED && k0 + 32 > NK) {
-                        // cache slots past the last key: zero them (their p is 0, but the
-                        // slots may hold anything)
-                        u32x4 av = __builtin_bit_cast(u32x4, a);
-                        const int kb = k0 + 16 * c + 8 * h;
-#pragma unroll
-                        for (int t = 0; t < 4; ++t)
-                            av[t] &= (kb + 2 * t < NK ? 0xffffu : 0u) | (kb + 2 * t + 1 < NK ? 0xffff0000u : 0u);
-                        a = __builtin_bit_cast(bf16x8, av);
+                        for (int r = 0; r < 16; ++r) {
+                            const int kk = 32 * sub + key_of_reg(r, h);
+                            cnt += (16 * (r >> 3) + (r & 7) <= lim && pq - sPos[kk] <= tab.W[e]) ? 1 : 0;
+                        }
+                    } else {
+                        const int c = n_off_le(lim) - n_off_le(lim - tab.W[e] - 1);
+                        cnt += c > 0 ? c : 0;
                     }
-                    O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        a, __builtin_bit_cast(bf16x8, pb), O[db], 0, 0, 0);
                 }
             }
+            finish(scores, sub, k0, sV);
         }
     };
 
@@ -515,7 +635,7 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
 template <int D, bool F32>
 hipError_t launch_d(const PrefillParams& p, const Tables& t, hipStream_t s) {
     const int G = p.Hq / p.Hkv;
-    constexpr int MAXW = Tile<D>::MAXW;
+    const int MAXW = Tile<D>::maxw(p.pos != nullptr);
     Launch L;
     L.nhc = (G + MAXW - 1) / MAXW;                  // head chunks, as even as possible
     L.Gc = (G + L.nhc - 1) / L.nhc;
