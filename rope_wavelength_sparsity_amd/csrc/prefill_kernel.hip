@@ -338,58 +338,50 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
         }
     };
 
-    // Softmax step and P*V of one sub-tile (keys k0 .. k0+31, `sub` within its tile) whose
-    // scores come from scores(): probabilities relative to the running max m, packed to bf16
-    // as P*V takes them, and their sum over this half's 16 keys (two per v_dot2).
+    // Softmax step and P*V of one sub-tile (keys k0 .. k0+31, `sub` within its tile):
+    // probabilities relative to the running max m, packed to bf16 as P*V takes them, and
+    // their sum over this half's 16 keys (two per v_dot2).
     // m moves only when the probabilities would grow past 2^8: every probability is at most
     // the half-row sum, so a wave-wide vote on that sum replaces a max over the scores.  The
     // rare sub-tile that fails it (and the first one, which sets m) recomputes its scores
     // and takes the row max.
+    auto probs = [&](const f32x16& S, uint32_t (&wd)[8]) -> float {
+        float ps = 0.f;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            wd[t] = pack_bf16x2(__builtin_amdgcn_exp2f(S[2 * t]), __builtin_amdgcn_exp2f(S[2 * t + 1]));
+            ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wd[t]),
+                                                 __builtin_bit_cast(bf16x2, 0x3f803f80u), ps, false);
+        }
+        return ps;
+    };
+    // scores S (relative to m; absolute before the first sub-tile) -> new m, O and the row
+    // sum rescaled, S made relative to the new m
+    auto remax = [&](f32x16& S) {
+        float mx = S[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
+        mx = max_with_partner(mx, xaddr);
+        float shift;
+        if (!started) {
+            set_m(mx);
+            shift = m;
+            started = true;
+        } else {
+            const float m_old = m;
+            set_m(m + fmaxf(mx, 0.f));
+            shift = m - m_old;
+            const float alpha = __builtin_amdgcn_exp2f(-shift);
+            lsum *= alpha;
+#pragma unroll
+            for (int i = 0; i < NDB; ++i) O[i] *= alpha;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) S[r] -= shift;
+    };
     const int v_row = l32 * BN;                               // V^T row of this lane (db = 0)
     const int v_x = (h ^ Tile<D>::swz(l32)) << 3;             // its slot swizzle, in elements
-    auto finish = [&](auto&& scores, int sub, int k0, const uint16_t* sV) {
-        uint32_t wd[8];
-        float psum = 0.f;
-        auto probs = [&](const f32x16& S) {
-            psum = 0.f;
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                wd[t] = pack_bf16x2(__builtin_amdgcn_exp2f(S[2 * t]), __builtin_amdgcn_exp2f(S[2 * t + 1]));
-                psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wd[t]),
-                                                       __builtin_bit_cast(bf16x2, 0x3f803f80u), psum, false);
-            }
-        };
-        bool redo = !started;
-        if (started) {
-            probs(scores());
-            redo = __any(psum > kSumTau);
-        }
-        if (redo) {
-            f32x16 S = scores();
-            float mx = S[0];
-#pragma unroll
-            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
-            mx = max_with_partner(mx, xaddr);
-            float shift;
-            if (!started) {
-                set_m(mx);
-                shift = m;
-                started = true;
-            } else {
-                const float m_old = m;
-                set_m(m + fmaxf(mx, 0.f));
-                shift = m - m_old;
-                const float alpha = __builtin_amdgcn_exp2f(-shift);
-                lsum *= alpha;
-#pragma unroll
-                for (int i = 0; i < NDB; ++i) O[i] *= alpha;
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) S[r] -= shift;
-            probs(S);
-        }
-        lsum += psum;
-
+    auto pv = [&](int sub, int k0, const uint32_t (&wd)[8], const uint16_t* sV) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             const u32x4 pb = u32x4{wd[4 * c], wd[4 * c + 1], wd[4 * c + 2], wd[4 * c + 3]};
@@ -412,6 +404,10 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
                     a, __builtin_bit_cast(bf16x8, pb), O[db], 0, 0, 0);
             }
         }
+    };
+    auto bias = [&](const f32x16& S) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(
+            __builtin_bit_cast(f16x8, ones_blk), __builtin_bit_cast(f16x8, negm_blk), S, 0, 0, 0);
     };
 
     // One key tile from LDS: its 32-key sub-tiles, nearest keys first.
@@ -436,129 +432,63 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
             if (w_lo >= dmax_t && plo < P) {
                 pfull = plo;                    // no W in [dmin_t, dmax_t): plo is also the
                 w_full = w_lo;                  // first pair active at dmax_t
+                const int jf = pfull >> 3;
+                if (pfull != q_key) {
+                    qm = Qf(jf) & lead_mask(pfull - 8 * jf);
+                    q_key = pfull;
+                }
                 if (COUNT && row_ok) cnt += (uint64_t)(16 * NSUB) * (uint64_t)(P - pfull);
                 plain = true;
             }
         }
         const uint16_t* kl = sK + perm_row(l32) * 16 + 8 * h;   // this lane's K row (sub 0)
 
-#pragma unroll 1
-        for (int sub = NSUB - 1; sub >= 0; --sub) {      // nearest keys first
+        // Scores of sub-tile `sub` without the -m step, on one MFMA chain: the fully active
+        // blocks, preceded, when pairs straddle the window edge, by each such pair as its own
+        // step (Q operand holding that pair alone), after which the elements outside its
+        // window go back to zero.  Pair windows grow with the pair index, so an element
+        // outside pair e's window is outside every earlier one's too and still holds zero:
+        // the reset removes exactly pair e's term.  Then the causal mask.  Moves the band to
+        // this sub-tile (sub-tiles come nearest first, so distances only grow).
+        auto raw = [&](int sub, bool count) -> f32x16 {
             const int k0 = ks + 32 * sub;
-            if (!plain) {
-                if (k0 > q0 + 31 || k0 >= NK) continue;    // whole sub-tile above the diagonal
-                const int k_last = k0 + 31 < NK ? k0 + 31 : NK - 1;
-                const int dmin = pq_lo - POSL(k_last) > 0 ? pq_lo - POSL(k_last) : 0;
-                const int dmax = pq_hi - POSL(k0);
-                while (w_lo < dmin) {
-                    ++plo;
-                    w_lo = plo < P ? tab.W[plo] : INT32_MAX;
-                }
-                while (w_full < dmax) {
-                    ++pfull;
-                    w_full = pfull < P ? tab.W[pfull] : INT32_MAX;
-                }
+            const uint16_t* ksub = kl + 32 * sub * 16;            // this lane's K row, this sub-tile
+            auto K = [&](int j) { return *reinterpret_cast<const f16x8*>(ksub + j * BN * 16); };
+            f32x16 S;
+            if (plain) {
+                // the tile's block set, unrolled for each first block
+                dispatch<NB>(pfull >> 3, [&](auto jfc) {
+                    constexpr int JF = decltype(jfc)::value;
+                    f32x16 T = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                        K(JF), __builtin_bit_cast(f16x8, qm), f32x16{}, 0, 0, 0);
+#pragma unroll
+                    for (int j = JF + 1; j < NB; ++j)
+                        T = __builtin_amdgcn_mfma_f32_32x32x16_f16(K(j), __builtin_bit_cast(f16x8, Qf(j)), T, 0, 0, 0);
+                    S = T;
+                });
+                return S;
+            }
+            const int k_last = k0 + 31 < NK ? k0 + 31 : NK - 1;
+            const int dmin = pq_lo - POSL(k_last) > 0 ? pq_lo - POSL(k_last) : 0;
+            const int dmax = pq_hi - POSL(k0);
+            while (w_lo < dmin) {
+                ++plo;
+                w_lo = plo < P ? tab.W[plo] : INT32_MAX;
+            }
+            while (w_full < dmax) {
+                ++pfull;
+                w_full = pfull < P ? tab.W[pfull] : INT32_MAX;
             }
             const int jf = pfull >> 3;
             if (pfull != q_key && jf < NB) {
                 qm = Qf(jf) & lead_mask(pfull - 8 * jf);
                 q_key = pfull;
             }
-            const uint16_t* ksub = kl + 32 * sub * 16;           // this lane's K row, this sub-tile
-            auto K = [&](int j) { return *reinterpret_cast<const f16x8*>(ksub + j * BN * 16); };
             const bool diag = k0 + 31 > q0;
             // register r of half h holds key k0 + off(r) + 8h, off(r) = 16(r/8) + r%8:
             // causal iff off(r) <= lim
             const int lim = qrow - k0 - 8 * h;
-
-            // Scores on one MFMA chain: the fully active blocks and a bias step that adds -m.
-            // With straddling pairs, the chain starts with each of them as its own step (Q
-            // operand holding that pair alone), after which the elements outside its window go
-            // back to zero.  Pair windows grow with the pair index, so an element outside pair
-            // e's window is outside every earlier one's too and still holds zero: the reset
-            // removes exactly pair e's term.  A plain tile runs the chain of its block set
-            // unrolled (no per-block branches).
-            auto full_blocks = [&](f32x16 S) -> f32x16 {
-                if (jf < NB) S = __builtin_amdgcn_mfma_f32_32x32x16_f16(K(jf), __builtin_bit_cast(f16x8, qm), S, 0, 0, 0);
-#pragma unroll
-                for (int j = NB - 1; j >= 1; --j)
-                    if (j > jf) S = __builtin_amdgcn_mfma_f32_32x32x16_f16(K(j), __builtin_bit_cast(f16x8, Qf(j)), S, 0, 0, 0);
-                return S;
-            };
-            auto bias = [&](const f32x16& S) {
-                return __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                    __builtin_bit_cast(f16x8, ones_blk), __builtin_bit_cast(f16x8, negm_blk), S, 0, 0, 0);
-            };
-            auto scores = [&]() -> f32x16 {
-                f32x16 S;
-                if (plain) {
-                    dispatch<NB>(jf, [&](auto jfc) {
-                        constexpr int JF = decltype(jfc)::value;
-                        f32x16 T = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                            K(JF), __builtin_bit_cast(f16x8, qm), f32x16{}, 0, 0, 0);
-#pragma unroll
-                        for (int j = JF + 1; j < NB; ++j)
-                            T = __builtin_amdgcn_mfma_f32_32x32x16_f16(K(j), __builtin_bit_cast(f16x8, Qf(j)), T, 0, 0, 0);
-                        S = T;
-                    });
-                    return bias(S);
-                }
-                if (!HASPOS && plo < pfull) {
-                    f32x16 T = {};
-#pragma unroll 1
-                    for (int e = plo; e < pfull; ++e) {
-                        const u32x4 qe = Qf(e >> 3) & pair_mask(e & 7);
-                        T = __builtin_amdgcn_mfma_f32_32x32x16_f16(K(e >> 3), __builtin_bit_cast(f16x8, qe), T, 0, 0, 0);
-                        const int t = lim - tab.W[e];              // inside iff off(r) >= t
-#pragma unroll
-                        for (int r = 0; r < 16; ++r)
-                            if (16 * (r >> 3) + (r & 7) < t) T[r] = 0.f;
-                    }
-                    S = bias(full_blocks(T));
-                } else {
-                    S = full_blocks(bias(f32x16{}));
-                }
-                if constexpr (HASPOS) {
-                    // arbitrary positions: straddling pairs per element on VALU
-                    if (plo < pfull) {
-#pragma unroll
-                        for (int j = 0; j < NB; ++j) {
-                            const int e_lo = plo - 8 * j > 0 ? plo - 8 * j : 0;
-                            const int e_hi = pfull - 8 * j < 8 ? pfull - 8 * j : 8;
-                            if (e_lo >= e_hi) continue;
-                            const u32x4 mine = Qf(j);
-                            u32x4 oth;
-#pragma unroll
-                            for (int t = 0; t < 4; ++t) oth[t] = partner32(mine[t], xaddr);
-                            const u32x4 qx = h ? oth : mine;
-                            const u32x4 qy = h ? mine : oth;
-                            for (int e = e_lo; e < e_hi; ++e) {
-                                const int sh = (e & 1) * 16;
-                                const float fqx = f16_bits_to_f32((sel4(qx, e >> 1) >> sh) & 0xffffu);
-                                const float fqy = f16_bits_to_f32((sel4(qy, e >> 1) >> sh) & 0xffffu);
-                                const int Wi = tab.W[8 * j + e];
-#pragma unroll
-                                for (int r = 0; r < 16; ++r) {
-                                    const int kk = 32 * sub + key_of_reg(r, h);
-                                    const uint16_t* kr = &sK[(j * BN + kk) * 16];
-                                    const float kx = f16_bits_to_f32(kr[e]);
-                                    const float ky = f16_bits_to_f32(kr[8 + e]);
-                                    S[r] += (pq - sPos[kk] <= Wi) ? (fqx * kx + fqy * ky) : 0.f;
-                                }
-                            }
-                        }
-                    }
-                }
-                // causal mask (raw scores; the scale is folded into the exponent)
-                if (diag) {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        if (16 * (r >> 3) + (r & 7) > lim) S[r] = -INFINITY;
-                }
-                return S;
-            };
-
-            if (COUNT && row_ok && !plain) {
+            if (COUNT && count && row_ok) {
                 // kept terms of this row: fully active pairs on every causal key, straddling
                 // pairs on the causal keys inside their window
                 const int nv = diag ? n_off_le(lim) : 16;
@@ -576,7 +506,111 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
                     }
                 }
             }
-            finish(scores, sub, k0, sV);
+
+            auto upper = [&](f32x16 A) {        // the fully active blocks above jf
+#pragma unroll
+                for (int j = NB - 1; j >= 1; --j)
+                    if (j > jf) A = __builtin_amdgcn_mfma_f32_32x32x16_f16(K(j), __builtin_bit_cast(f16x8, Qf(j)), A, 0, 0, 0);
+                return A;
+            };
+            if (!HASPOS && plo < pfull) {
+                f32x16 T = {};
+#pragma unroll 1
+                for (int e = plo; e < pfull; ++e) {
+                    const u32x4 qe = Qf(e >> 3) & pair_mask(e & 7);
+                    T = __builtin_amdgcn_mfma_f32_32x32x16_f16(K(e >> 3), __builtin_bit_cast(f16x8, qe), T, 0, 0, 0);
+                    const int t = lim - tab.W[e];              // inside iff off(r) >= t
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (16 * (r >> 3) + (r & 7) < t) T[r] = 0.f;
+                }
+                if (jf < NB) T = __builtin_amdgcn_mfma_f32_32x32x16_f16(K(jf), __builtin_bit_cast(f16x8, qm), T, 0, 0, 0);
+                S = upper(T);
+            } else if (jf < NB) {
+                S = upper(__builtin_amdgcn_mfma_f32_32x32x16_f16(K(jf), __builtin_bit_cast(f16x8, qm), f32x16{}, 0, 0, 0));
+            } else {
+                S = f32x16{};
+            }
+            if constexpr (HASPOS) {
+                // arbitrary positions: straddling pairs per element on VALU
+                if (plo < pfull) {
+#pragma unroll
+                    for (int j = 0; j < NB; ++j) {
+                        const int e_lo = plo - 8 * j > 0 ? plo - 8 * j : 0;
+                        const int e_hi = pfull - 8 * j < 8 ? pfull - 8 * j : 8;
+                        if (e_lo >= e_hi) continue;
+                        const u32x4 mine = Qf(j);
+                        u32x4 oth;
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) oth[t] = partner32(mine[t], xaddr);
+                        const u32x4 qx = h ? oth : mine;
+                        const u32x4 qy = h ? mine : oth;
+                        for (int e = e_lo; e < e_hi; ++e) {
+                            const int sh = (e & 1) * 16;
+                            const float fqx = f16_bits_to_f32((sel4(qx, e >> 1) >> sh) & 0xffffu);
+                            const float fqy = f16_bits_to_f32((sel4(qy, e >> 1) >> sh) & 0xffffu);
+                            const int Wi = tab.W[8 * j + e];
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                const int kk = 32 * sub + key_of_reg(r, h);
+                                const uint16_t* kr = &sK[(j * BN + kk) * 16];
+                                const float kx = f16_bits_to_f32(kr[e]);
+                                const float ky = f16_bits_to_f32(kr[8 + e]);
+                                S[r] += (pq - sPos[kk] <= Wi) ? (fqx * kx + fqy * ky) : 0.f;
+                            }
+                        }
+                    }
+                }
+            }
+            // causal mask (raw scores; the scale is folded into the exponent)
+            if (diag) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (16 * (r >> 3) + (r & 7) > lim) S[r] = -INFINITY;
+            }
+            return S;
+        };
+
+        // Sub-tiles above the diagonal, or past the last key, come first in the visiting
+        // order and are skipped.
+        int sub = NSUB - 1;
+        if (!plain) {
+            const int a = (q0 + 31 - ks) >> 5, c = (NK - 1 - ks) >> 5;
+            sub = a < sub ? a : sub;
+            sub = uniform(c < sub ? c : sub);
+        }
+        if (sub < 0) return;
+        // Software pipeline (d=64, plain tiles): the next sub-tile's chain is issued before
+        // this one's softmax, so the matrix cores work while the vector unit does; its -m
+        // step waits for this sub-tile's vote, which may move m.  (At d=128 the registers for
+        // a second score block would cost a wave per SIMD.)  A sub-tile that fails the vote
+        // recomputes its scores: a plain tile's band is fixed, and elsewhere the band still
+        // sits at this sub-tile.
+        constexpr bool PIPE = D == 64;
+        f32x16 T;
+        bool have = false;                      // T holds sub-tile `sub`'s scores already
+#pragma unroll 1
+        while (true) {
+            if (!have) T = raw(sub, true);
+            f32x16 S = bias(T);
+            have = PIPE && plain && sub > 0;
+            if (have) T = raw(sub - 1, true);
+            uint32_t wd[8];
+            float psum = 0.f;
+            bool redo = !started;
+            if (started) {
+                psum = probs(S, wd);
+                redo = __any(psum > kSumTau);
+            }
+            if (redo) {
+                f32x16 R = bias(raw(sub, false));
+                remax(R);
+                psum = probs(R, wd);
+            }
+            lsum += psum;
+            pv(sub, ks + 32 * sub, wd, sV);
+            if (sub == 0) break;
+            --sub;
         }
     };
 
