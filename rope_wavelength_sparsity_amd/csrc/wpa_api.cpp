@@ -89,10 +89,13 @@ void make_tables(int32_t d, double base, const wpa_rope_t* rope, double alpha, w
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 int default_chunk(int32_t B, int64_t Lmax, int32_t Hkv) {
-    // aim for ~4096 work items (>= 16 per CU) and at least 256 keys per item
+    // About two work items per compute unit (one round of resident workgroups: 256 CUs x
+    // 2), at least 256 keys each.  Fewer, longer items stream the caches faster: measured
+    // on the Llama-3.2-3B (16 x 131072) and Qwen2.5-7B (1 x 1M) decode shapes, 512 items
+    // beat 4096 by 7% and 20%.
     const int64_t keys = (int64_t)B * Hkv * Lmax;
     int64_t c = 256;
-    while (c < 8192 && keys / c > 4096) c <<= 1;
+    while (c < (1 << 20) && keys > 512 * c) c <<= 1;
     return (int)c;
 }
 
