@@ -245,6 +245,40 @@ int wpa_prefill_cached(const void* q, const void* k_cache, const void* v_cache,
                        const wpa_rope_t* rope, double alpha, float scale, int32_t dtype,
                        int32_t out_dtype, unsigned long long* term_count, void* stream);
 
+/*
+ * Windowed decode cache (K-dim eviction).  In decode the query is the newest token, so the
+ * distance to a given key only grows: once it exceeds the window of every pair of a 16-dim
+ * pair block, that block of that key is never read again (WavePrune original abstract:
+ * each pair keeps only its first rotation periods; ATFlash abstract: the window is
+ * proportional to the wavelength, and a decode step reads only the dims still active).  A
+ * windowed K cache keeps pair block j only for the newest W_j + 1 tokens, W_j being the
+ * window of the block's last pair at `cache_alpha` (rounded up to 32 rows; a block whose
+ * window reaches Lmax keeps all Lmax), in rows reused as a ring.  V is kept whole: a key
+ * whose terms are all pruned still enters the softmax, with logit 0.
+ *   cache_alpha  the window the cache is built for: finite, >= 0.  Decodes on it take any
+ *            alpha <= cache_alpha (a larger alpha is WPA_ERR_INVALID).
+ *   wpa_kcache_window_bytes  bytes of such a K cache (0 for invalid arguments); the V cache
+ *            is wpa_vcache_bytes.  Sequence b's part is one block at b times the B = 1 size.
+ *   wpa_kv_write_window  as wpa_kv_write_ex, into a windowed K cache (and the usual V cache).
+ *            Rows are reused: only the newest rows of each block are kept.
+ *   wpa_decode_window  as wpa_decode_ex with q_pos = NULL, on a windowed K cache.  Each
+ *            kv_len[b] must be at least the end (start + n) of the last write to sequence b
+ *            (append-only use: a shorter kv_len would need keys whose rows were reused).
+ * Chunked prefill (wpa_prefill_cached) reads the dense cache only.
+ */
+size_t wpa_kcache_window_bytes(int32_t B, int64_t Lmax, int32_t Hkv, int32_t d, double base,
+                               const wpa_rope_t* rope, double cache_alpha);
+int wpa_kv_write_window(const void* k, const void* v, int64_t start, int64_t n, void* k_cache,
+                        void* v_cache, int32_t B, int64_t Lmax, int32_t Hkv, int32_t d,
+                        double base, const wpa_rope_t* rope, double cache_alpha, int32_t dtype,
+                        void* stream);
+int wpa_decode_window(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* kv_len, void* out, float* lse, int32_t B, int64_t Lmax,
+                      int32_t Hq, int32_t Hkv, int32_t d, double base, const wpa_rope_t* rope,
+                      double cache_alpha, double alpha, float scale, int32_t dtype,
+                      int32_t out_dtype, unsigned long long* term_count, int32_t chunk_keys,
+                      void* workspace, size_t ws_bytes, void* stream);
+
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char* wpa_last_error(void);
 

@@ -38,7 +38,8 @@ EXPORTS = ("wpa_count_terms", "wpa_thresholds", "wpa_prefill_workspace_bytes", "
            "wpa_prefill_prepare", "wpa_prefill_attend", "wpa_kcache_bytes", "wpa_vcache_bytes",
            "wpa_kv_write", "wpa_decode_workspace_bytes", "wpa_decode", "wpa_count_terms_ex",
            "wpa_thresholds_ex", "wpa_prefill_ex", "wpa_prefill_prepare_ex", "wpa_prefill_attend_ex",
-           "wpa_kv_write_ex", "wpa_decode_ex", "wpa_prefill_cached", "wpa_last_error")
+           "wpa_kv_write_ex", "wpa_decode_ex", "wpa_prefill_cached", "wpa_kcache_window_bytes",
+           "wpa_kv_write_window", "wpa_decode_window", "wpa_last_error")
 
 
 class Rope(ctypes.Structure):
@@ -145,6 +146,13 @@ def lib():
     L.wpa_prefill_cached.argtypes = [P, P, P, P, P, P, I32, I32, I64, I32, I32, I32, D, P, D, F,
                                      I32, I32, P, P]
     L.wpa_prefill_cached.restype = ctypes.c_int
+    L.wpa_kcache_window_bytes.argtypes = [I32, I64, I32, I32, D, P, D]
+    L.wpa_kcache_window_bytes.restype = SZ
+    L.wpa_kv_write_window.argtypes = [P, P, I64, I64, P, P, I32, I64, I32, I32, D, P, D, I32, P]
+    L.wpa_kv_write_window.restype = ctypes.c_int
+    L.wpa_decode_window.argtypes = [P, P, P, P, P, P, I32, I64, I32, I32, I32, D, P, D, D, F, I32,
+                                    I32, P, I32, P, SZ, P]
+    L.wpa_decode_window.restype = ctypes.c_int
     L.wpa_last_error.argtypes = []
     L.wpa_last_error.restype = ctypes.c_char_p
     _lib = L
@@ -306,14 +314,27 @@ def prefill_attend(q, workspace, Hkv: int, base: float, alpha: float, *, scale=N
 class KVCache:
     """Decode caches for B sequences of up to Lmax tokens (library-owned K layout).  The
     RoPE description (inv_freq, pairs) given here rotates the keys written and the queries
-    of every decode step against this cache."""
+    of every decode step against this cache.
 
-    def __init__(self, B, Lmax, Hkv, d, base, device="cuda", *, inv_freq=None, pairs="half"):
+    window_alpha: build the windowed K cache, which keeps each 16-dim pair block only for the
+    keys still inside that block's window at this alpha (decodes then take alpha <=
+    window_alpha, with the query at the newest token)."""
+
+    def __init__(self, B, Lmax, Hkv, d, base, device="cuda", *, inv_freq=None, pairs="half",
+                 window_alpha=None):
         self.B, self.Lmax, self.Hkv, self.d, self.base = B, Lmax, Hkv, d, float(base)
         self.inv_freq = None if inv_freq is None else np.asarray(inv_freq, dtype=np.float64).copy()
         self.pairs = pairs
-        _rope(d, self.inv_freq, pairs)                 # validates the description
-        self.k = torch.empty(kcache_bytes(B, Lmax, Hkv, d), device=device, dtype=torch.uint8)
+        rope, keep = _rope(d, self.inv_freq, pairs)    # validates the description
+        self.window_alpha = None if window_alpha is None else float(window_alpha)
+        if self.window_alpha is None:
+            self.k_seq_bytes = kcache_bytes(1, Lmax, Hkv, d)
+        else:
+            self.k_seq_bytes = lib().wpa_kcache_window_bytes(1, Lmax, Hkv, d, self.base, rope,
+                                                             self.window_alpha)
+            if self.k_seq_bytes == 0:
+                raise ValueError("invalid windowed cache arguments")
+        self.k = torch.empty(B * self.k_seq_bytes, device=device, dtype=torch.uint8)
         self.v = torch.empty(vcache_bytes(B, Lmax, Hkv, d), device=device, dtype=torch.uint8)
 
     def write(self, k, v, start: int, stream=None, *, seq: int | None = None):
@@ -329,12 +350,17 @@ class KVCache:
         if seq is not None:
             if not 0 <= seq < self.B:
                 raise ValueError("seq out of range")
-            kc += seq * kcache_bytes(1, self.Lmax, self.Hkv, self.d)
+            kc += seq * self.k_seq_bytes
             vc += seq * vcache_bytes(1, self.Lmax, self.Hkv, self.d)
         rope, keep = _rope(self.d, self.inv_freq, self.pairs)
-        _check(lib().wpa_kv_write_ex(_ptr(k), _ptr(v), int(start), k.shape[1], kc, vc, nb,
-                                     self.Lmax, self.Hkv, self.d, self.base, rope, _dtype_code(k),
-                                     _stream(stream)))
+        if self.window_alpha is None:
+            _check(lib().wpa_kv_write_ex(_ptr(k), _ptr(v), int(start), k.shape[1], kc, vc, nb,
+                                         self.Lmax, self.Hkv, self.d, self.base, rope,
+                                         _dtype_code(k), _stream(stream)))
+        else:
+            _check(lib().wpa_kv_write_window(_ptr(k), _ptr(v), int(start), k.shape[1], kc, vc, nb,
+                                             self.Lmax, self.Hkv, self.d, self.base, rope,
+                                             self.window_alpha, _dtype_code(k), _stream(stream)))
 
     def v_tokens(self):
         """A copy of the V cache as bf16 [B][Hkv][Lmax][d] (the cache itself is blocked by
@@ -366,6 +392,17 @@ def decode(q, cache: KVCache, kv_len, alpha: float, *, q_pos=None, scale: float 
     if workspace is None:
         workspace = torch.empty(max(need, 16), device=q.device, dtype=torch.uint8)
     rope, keep = _rope(d, cache.inv_freq, cache.pairs)
+    if cache.window_alpha is not None:
+        if q_pos is not None:
+            raise ValueError("a windowed cache decodes at the newest token (q_pos must be None)")
+        _check(lib().wpa_decode_window(_ptr(q), _ptr(cache.k), _ptr(cache.v), _ptr(kv_len),
+                                       _ptr(out), _ptr(lse), B, cache.Lmax, Hq, cache.Hkv, d,
+                                       cache.base, rope, cache.window_alpha, float(alpha),
+                                       float(scale) if scale is not None else 0.0,
+                                       _dtype_code(q), _dtype_code(out), _ptr(term_count),
+                                       int(chunk_keys), _ptr(workspace), workspace.numel(),
+                                       _stream(stream)))
+        return (out, lse) if lse is not None else out
     _check(lib().wpa_decode_ex(_ptr(q), _ptr(cache.k), _ptr(cache.v), _ptr(kv_len), _ptr(q_pos),
                                _ptr(out), _ptr(lse), B, cache.Lmax, Hq, cache.Hkv, d, cache.base,
                                rope, float(alpha), float(scale) if scale is not None else 0.0,
@@ -385,6 +422,8 @@ def prefill_cached(q, cache: KVCache, kv_len, alpha: float, *, scale: float | No
     B, Nq, Hq, d = q.shape
     if B != cache.B or d != cache.d or kv_len.dtype != torch.int32 or kv_len.numel() != B:
         raise ValueError("q [B][Nq][Hq][d] and kv_len int32 [B] must match the cache")
+    if cache.window_alpha is not None:
+        raise ValueError("chunked prefill needs the dense cache (window_alpha=None)")
     if out is None:
         out = torch.empty(q.shape, device=q.device, dtype=out_dtype or q.dtype)
     _dev(out, "out")

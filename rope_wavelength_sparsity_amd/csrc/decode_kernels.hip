@@ -93,7 +93,7 @@ void decode_partial_kernel(DecodeParams p, Tables tab) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) qB[j] = *reinterpret_cast<const u32x4*>(&sQ[l32][16 * j + 8 * h]);
 
-    const uint16_t* kpg = p.kp + ((int64_t)b * p.Hkv + g) * NB * p.Lmax * 16;
+    const uint16_t* kpg = p.kp + ((int64_t)b * p.Hkv + g) * p.kl.head * 16;
     const int64_t L8 = (p.Lmax + 7) / 8;
     const uint16_t* vg = p.v + ((int64_t)b * p.Hkv + g) * L8 * D * 8;
 
@@ -106,7 +106,6 @@ void decode_partial_kernel(DecodeParams p, Tables tab) {
 
     const char* kbytes = reinterpret_cast<const char*>(kpg);
     const char* vbytes = reinterpret_cast<const char*>(vg);
-    const int64_t kblk = (int64_t)p.Lmax * 32;           // bytes of one pair block
     const uint32_t voff0 = (uint32_t)((h * D + l32) * 16);
     int plo = 0, pfull = 0;                          // band edges, moved incrementally
     for (int k0 = c0 + 32 * w; k0 < c1; k0 += 32 * kWaves) {
@@ -134,12 +133,16 @@ void decode_partial_kernel(DecodeParams p, Tables tab) {
         // non-temporal loads (a plain read runs markedly closer to the HBM peak with them)
         const int key = k0 + arow;
         const int keyc = key < c1 ? key : c1 - 1;
-        const uint32_t koff = (uint32_t)(keyc * 32 + 16 * h);
         u32x4 ka[NB];
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
             if (j < jlo) continue;
-            ka[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbytes + j * kblk + koff));
+            // row of this key in block j: the key itself, or in a ring block (one holding only
+            // the keys inside its largest window) key mod cap, without wrapping in the tile
+            const int cap = p.kl.cap[j];
+            const int r0 = cap < p.Lmax ? (int)((uint32_t)k0 % (uint32_t)cap) : k0;
+            const int64_t koff = (p.kl.off[j] + r0) * 32 + (int64_t)((keyc - k0) * 32 + 16 * h);
+            ka[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbytes + koff));
         }
         u32x4 va[2][NDB];
         const int64_t oct0 = k0 >> 3;

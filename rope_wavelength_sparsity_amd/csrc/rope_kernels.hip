@@ -1,5 +1,8 @@
 // Key rotation and K/V relayout.
 //
+// (A decode cache may keep a pair block only for the keys still inside that block's
+// largest window: such a block is a ring over tokens, see KLayout.)
+//
 // Keys are rotated once, at their own position (ATFlash abstract: the RoPE score is a
 // sum over 2-D rotation pairs), and stored pair-blocked: block j of a head holds pairs
 // 8j..8j+7, as the 8 first-half components followed by the 8 second-half components,
@@ -32,7 +35,23 @@ __global__ __launch_bounds__(256) void rope_keys_kernel(RopeParams p, Tables tab
     const int g = (int)(rest % p.Hkv);
     const int b = (int)(rest / p.Hkv);
 
-    uint16_t* dst = p.kp + ((((int64_t)b * p.Hkv + g) * NB + j) * p.ld + p.t0 + t) * 16;
+    // block j's rows (layout kl); a ring block takes token tok in row tok mod cap, and only
+    // the newest cap tokens of this write (an older one would share a row with a newer)
+    int64_t off = p.kl.off[0];
+    int cap = p.kl.cap[0];
+#pragma unroll
+    for (int jj = 1; jj < 8; ++jj)
+        if (j == jj) {
+            off = p.kl.off[jj];
+            cap = p.kl.cap[jj];
+        }
+    const int64_t tok = p.t0 + t;
+    int64_t krow = tok;
+    if (cap < p.ld) {
+        if (tok + cap < p.t0 + p.n) return;
+        krow = tok % cap;
+    }
+    uint16_t* dst = p.kp + (((int64_t)b * p.Hkv + g) * p.kl.head + off + krow) * 16;
     u32x4* d4 = reinterpret_cast<u32x4*>(dst);
     if (t >= p.n) {
         u32x4 z = {0u, 0u, 0u, 0u};

@@ -88,6 +88,39 @@ void make_tables(int32_t d, double base, const wpa_rope_t* rope, double alpha, w
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
+// K rows of one (sequence, kv head) when every pair block keeps all `rows` tokens.
+wpa::KLayout dense_layout(int32_t d, int64_t rows) {
+    wpa::KLayout kl{};
+    for (int j = 0; j < d / 16; ++j) {
+        kl.off[j] = j * rows;
+        kl.cap[j] = (int32_t)rows;
+    }
+    kl.head = (int64_t)(d / 16) * rows;
+    return kl;
+}
+
+// The windowed decode cache: pair block j keeps only the keys still inside its largest
+// window W = floor(cache_alpha * lambda) of its last pair (windows grow with the pair index),
+// i.e. the newest W + 1 tokens, rounded up to 32 rows; a block whose window reaches the
+// cache length keeps all Lmax.  In decode the query is the newest token, so a key that has
+// left a block's window never re-enters it: the block's older rows can be reused (a ring).
+wpa::KLayout window_layout(int32_t d, int64_t Lmax, double base, const wpa_rope_t* rope,
+                           double cache_alpha) {
+    wpa::KLayout kl{};
+    int64_t off = 0;
+    for (int j = 0; j < d / 16; ++j) {
+        const double t = window_value(d, base, freq_table(rope), cache_alpha, 8 * j + 7);
+        int64_t cap = Lmax;
+        if (t < (double)(Lmax - 1)) cap = round_up((int64_t)std::floor(t) + 1, 32);
+        if (cap > Lmax) cap = Lmax;
+        kl.off[j] = off;
+        kl.cap[j] = (int32_t)cap;
+        off += cap;
+    }
+    kl.head = off;
+    return kl;
+}
+
 int default_chunk(int32_t B, int64_t Lmax, int32_t Hkv) {
     // About two work items per compute unit (one round of resident workgroups: 256 CUs x
     // 2), at least 256 keys each.  Fewer, longer items stream the caches faster: measured
@@ -238,7 +271,7 @@ int wpa_prefill_prepare_ex(const void* k, const void* v, const int32_t* position
     uint16_t* kp = static_cast<uint16_t*>(workspace);
     wpa::RopeParams rp{};
     rp.k = k; rp.v = v; rp.pos = positions; rp.kp = kp; rp.vout = kp + (size_t)B * Hkv * Np * d;
-    rp.n = N; rp.t0 = 0; rp.ld = Np; rp.pad_to = Np;
+    rp.n = N; rp.t0 = 0; rp.ld = Np; rp.pad_to = Np; rp.kl = dense_layout(d, Np);
     rp.B = B; rp.Hkv = Hkv; rp.d = d; rp.in_f32 = dtype == WPA_FP32; rp.v_transposed = 1;
     rp.interleaved = interleaved(rope);
     rp.tab = &tab;
@@ -340,11 +373,13 @@ int wpa_kv_write(const void* k, const void* v, int64_t start, int64_t n, void* k
                            stream);
 }
 
-int wpa_kv_write_ex(const void* k, const void* v, int64_t start, int64_t n, void* k_cache,
-                    void* v_cache, int32_t B, int64_t Lmax, int32_t Hkv, int32_t d, double base,
-                    const wpa_rope_t* rope, int32_t dtype, void* stream) {
-    int rc = check_common(d, base, rope, 1.0);
-    if (rc) return rc;
+}  // extern "C"
+
+namespace {
+
+int kv_write_impl(const void* k, const void* v, int64_t start, int64_t n, void* k_cache,
+                  void* v_cache, int32_t B, int64_t Lmax, int32_t Hkv, int32_t d, double base,
+                  const wpa_rope_t* rope, const wpa::KLayout& kl, int32_t dtype, void* stream) {
     if (B < 1 || Hkv < 1 || Lmax < 1 || n < 1 || start < 0 || start + n > Lmax)
         return fail(WPA_ERR_INVALID, "need B, Hkv, n >= 1 and 0 <= start, start + n <= Lmax");
     if (Lmax >= (int64_t)INT32_MAX) return fail(WPA_ERR_INVALID, "Lmax too large");
@@ -358,12 +393,106 @@ int wpa_kv_write_ex(const void* k, const void* v, int64_t start, int64_t n, void
     rp.interleaved = interleaved(rope);
     rp.k = k; rp.v = v; rp.pos = nullptr;
     rp.kp = static_cast<uint16_t*>(k_cache); rp.vout = static_cast<uint16_t*>(v_cache);
+    rp.kl = kl;
     rp.n = n; rp.t0 = start; rp.ld = Lmax; rp.pad_to = 0;
     rp.B = B; rp.Hkv = Hkv; rp.d = d; rp.in_f32 = dtype == WPA_FP32; rp.v_transposed = 0;
     rp.tab = &tab;
     hipError_t e = wpa::launch_rope_relayout(rp, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(WPA_ERR_HIP, "kv write launch: %s", hipGetErrorString(e));
     return ok();
+}
+
+int decode_impl(const void* q, const void* k_cache, const void* v_cache, const int32_t* kv_len,
+                const int32_t* q_pos, void* out, float* lse, int32_t B, int64_t Lmax,
+                int32_t Hq, int32_t Hkv, int32_t d, double base, const wpa_rope_t* rope,
+                const wpa::KLayout& kl, double alpha, float scale, int32_t dtype, int32_t out_dtype,
+                unsigned long long* term_count, int32_t chunk_keys, void* workspace,
+                size_t ws_bytes, void* stream) {
+    if (B < 1 || Lmax < 1 || Hq < 1 || Hkv < 1) return fail(WPA_ERR_INVALID, "B, Lmax, Hq, Hkv must be >= 1");
+    if (Hq % Hkv) return fail(WPA_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+    if (Hq / Hkv > 16) return fail(WPA_ERR_UNSUPPORTED, "decode supports up to 16 q heads per kv head");
+    if (Lmax >= (int64_t)INT32_MAX) return fail(WPA_ERR_INVALID, "Lmax too large");
+    if (dtype != WPA_BF16 && dtype != WPA_FP32) return fail(WPA_ERR_INVALID, "dtype must be WPA_BF16 or WPA_FP32");
+    if (out_dtype != WPA_BF16 && out_dtype != WPA_FP32) return fail(WPA_ERR_INVALID, "out_dtype must be WPA_BF16 or WPA_FP32");
+    if (std::isnan(scale)) return fail(WPA_ERR_INVALID, "scale is NaN");
+    if (chunk_keys < 0 || (chunk_keys % 256)) return fail(WPA_ERR_INVALID, "chunk_keys must be 0 or a positive multiple of 256");
+    if (!q || !k_cache || !v_cache || !kv_len || !out || !workspace) return fail(WPA_ERR_INVALID, "null pointer");
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) || !aligned16(workspace))
+        return fail(WPA_ERR_INVALID, "q, caches, out and workspace must be 16-byte aligned");
+    if (term_count && (reinterpret_cast<uintptr_t>(term_count) & 7u)) return fail(WPA_ERR_INVALID, "term_count must be 8-byte aligned");
+    const int ch = chunk_keys > 0 ? chunk_keys : default_chunk(B, Lmax, Hkv);
+    const size_t need = wpa_decode_workspace_bytes(B, Lmax, Hq, Hkv, d, ch);
+    if (ws_bytes < need) return fail(WPA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    wpa::Tables tab;
+    make_tables(d, base, rope, alpha, &tab);
+    wpa::DecodeParams dp{};
+    dp.interleaved = interleaved(rope);
+    dp.q = q; dp.kp = static_cast<const uint16_t*>(k_cache); dp.v = static_cast<const uint16_t*>(v_cache);
+    dp.kl = kl;
+    dp.kv_len = kv_len; dp.q_pos = q_pos; dp.out = out; dp.lse = lse; dp.counter = term_count;
+    dp.partial = static_cast<float*>(workspace); dp.Lmax = Lmax; dp.B = B; dp.Hq = Hq; dp.Hkv = Hkv;
+    dp.d = d; dp.in_f32 = dtype == WPA_FP32; dp.out_f32 = out_dtype == WPA_FP32; dp.chunk = ch; dp.n_chunks = (int)((Lmax + ch - 1) / ch);
+    dp.scale = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)d));
+    hipError_t e = wpa::launch_decode(dp, tab, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(WPA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+// cache_alpha of a windowed cache: finite (a full window keeps every key: use the dense
+// cache), >= 0
+int check_cache_alpha(double cache_alpha) {
+    if (!(cache_alpha >= 0.0) || !std::isfinite(cache_alpha))
+        return fail(WPA_ERR_INVALID, "cache_alpha must be finite and >= 0 (got %g)", cache_alpha);
+    return WPA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int wpa_kv_write_ex(const void* k, const void* v, int64_t start, int64_t n, void* k_cache,
+                    void* v_cache, int32_t B, int64_t Lmax, int32_t Hkv, int32_t d, double base,
+                    const wpa_rope_t* rope, int32_t dtype, void* stream) {
+    int rc = check_common(d, base, rope, 1.0);
+    if (rc) return rc;
+    return kv_write_impl(k, v, start, n, k_cache, v_cache, B, Lmax, Hkv, d, base, rope,
+                         dense_layout(d, Lmax), dtype, stream);
+}
+
+size_t wpa_kcache_window_bytes(int32_t B, int64_t Lmax, int32_t Hkv, int32_t d, double base,
+                               const wpa_rope_t* rope, double cache_alpha) {
+    if (B < 1 || Lmax < 1 || Hkv < 1 || Lmax >= (int64_t)INT32_MAX) return 0;
+    if (check_common(d, base, rope, 1.0) || check_cache_alpha(cache_alpha)) return 0;
+    return (size_t)B * Hkv * window_layout(d, Lmax, base, rope, cache_alpha).head * 32;
+}
+
+int wpa_kv_write_window(const void* k, const void* v, int64_t start, int64_t n, void* k_cache,
+                        void* v_cache, int32_t B, int64_t Lmax, int32_t Hkv, int32_t d,
+                        double base, const wpa_rope_t* rope, double cache_alpha, int32_t dtype,
+                        void* stream) {
+    int rc = check_common(d, base, rope, 1.0);
+    if (rc) return rc;
+    rc = check_cache_alpha(cache_alpha);
+    if (rc) return rc;
+    return kv_write_impl(k, v, start, n, k_cache, v_cache, B, Lmax, Hkv, d, base, rope,
+                         window_layout(d, Lmax, base, rope, cache_alpha), dtype, stream);
+}
+
+int wpa_decode_window(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* kv_len, void* out, float* lse, int32_t B, int64_t Lmax,
+                      int32_t Hq, int32_t Hkv, int32_t d, double base, const wpa_rope_t* rope,
+                      double cache_alpha, double alpha, float scale, int32_t dtype,
+                      int32_t out_dtype, unsigned long long* term_count, int32_t chunk_keys,
+                      void* workspace, size_t ws_bytes, void* stream) {
+    int rc = check_common(d, base, rope, alpha);
+    if (rc) return rc;
+    rc = check_cache_alpha(cache_alpha);
+    if (rc) return rc;
+    if (alpha > cache_alpha)
+        return fail(WPA_ERR_INVALID, "alpha (%g) exceeds the cache's window alpha (%g)", alpha, cache_alpha);
+    return decode_impl(q, k_cache, v_cache, kv_len, nullptr, out, lse, B, Lmax, Hq, Hkv, d, base,
+                       rope, window_layout(d, Lmax, base, rope, cache_alpha), alpha, scale, dtype,
+                       out_dtype, term_count, chunk_keys, workspace, ws_bytes, stream);
 }
 
 size_t wpa_decode_workspace_bytes(int32_t B, int64_t Lmax, int32_t Hq, int32_t Hkv, int32_t d,
@@ -392,33 +521,9 @@ int wpa_decode_ex(const void* q, const void* k_cache, const void* v_cache, const
                   size_t ws_bytes, void* stream) {
     int rc = check_common(d, base, rope, alpha);
     if (rc) return rc;
-    if (B < 1 || Lmax < 1 || Hq < 1 || Hkv < 1) return fail(WPA_ERR_INVALID, "B, Lmax, Hq, Hkv must be >= 1");
-    if (Hq % Hkv) return fail(WPA_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
-    if (Hq / Hkv > 16) return fail(WPA_ERR_UNSUPPORTED, "decode supports up to 16 q heads per kv head");
-    if (Lmax >= (int64_t)INT32_MAX) return fail(WPA_ERR_INVALID, "Lmax too large");
-    if (dtype != WPA_BF16 && dtype != WPA_FP32) return fail(WPA_ERR_INVALID, "dtype must be WPA_BF16 or WPA_FP32");
-    if (out_dtype != WPA_BF16 && out_dtype != WPA_FP32) return fail(WPA_ERR_INVALID, "out_dtype must be WPA_BF16 or WPA_FP32");
-    if (std::isnan(scale)) return fail(WPA_ERR_INVALID, "scale is NaN");
-    if (chunk_keys < 0 || (chunk_keys % 256)) return fail(WPA_ERR_INVALID, "chunk_keys must be 0 or a positive multiple of 256");
-    if (!q || !k_cache || !v_cache || !kv_len || !out || !workspace) return fail(WPA_ERR_INVALID, "null pointer");
-    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) || !aligned16(workspace))
-        return fail(WPA_ERR_INVALID, "q, caches, out and workspace must be 16-byte aligned");
-    if (term_count && (reinterpret_cast<uintptr_t>(term_count) & 7u)) return fail(WPA_ERR_INVALID, "term_count must be 8-byte aligned");
-    const int ch = chunk_keys > 0 ? chunk_keys : default_chunk(B, Lmax, Hkv);
-    const size_t need = wpa_decode_workspace_bytes(B, Lmax, Hq, Hkv, d, ch);
-    if (ws_bytes < need) return fail(WPA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
-    wpa::Tables tab;
-    make_tables(d, base, rope, alpha, &tab);
-    wpa::DecodeParams dp{};
-    dp.interleaved = interleaved(rope);
-    dp.q = q; dp.kp = static_cast<const uint16_t*>(k_cache); dp.v = static_cast<const uint16_t*>(v_cache);
-    dp.kv_len = kv_len; dp.q_pos = q_pos; dp.out = out; dp.lse = lse; dp.counter = term_count;
-    dp.partial = static_cast<float*>(workspace); dp.Lmax = Lmax; dp.B = B; dp.Hq = Hq; dp.Hkv = Hkv;
-    dp.d = d; dp.in_f32 = dtype == WPA_FP32; dp.out_f32 = out_dtype == WPA_FP32; dp.chunk = ch; dp.n_chunks = (int)((Lmax + ch - 1) / ch);
-    dp.scale = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)d));
-    hipError_t e = wpa::launch_decode(dp, tab, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return fail(WPA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
-    return ok();
+    return decode_impl(q, k_cache, v_cache, kv_len, q_pos, out, lse, B, Lmax, Hq, Hkv, d, base,
+                       rope, dense_layout(d, Lmax), alpha, scale, dtype, out_dtype, term_count,
+                       chunk_keys, workspace, ws_bytes, stream);
 }
 
 int wpa_prefill_cached(const void* q, const void* k_cache, const void* v_cache,

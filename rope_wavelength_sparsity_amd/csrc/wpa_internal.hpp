@@ -20,12 +20,23 @@ struct Tables {
 // prefill, write V transposed to [B][Hkv][d][ld]; for the decode cache, V is copied to
 // [B][Hkv][ld][d].  Tokens t0 .. t0+n-1 of the destination receive source rows 0 .. n-1;
 // tokens n .. pad_to-1 (prefill only) are zero-filled.
+// Rows of the pair-blocked K layout of one (sequence, kv head): block j holds cap[j] rows
+// starting at row off[j].  A block with fewer rows than the tokens it serves is a ring:
+// token t sits in row t mod cap[j] (cap[j] a multiple of 32, so a 32-token tile starting at a
+// multiple of 32 never wraps).  Dense layouts have cap[j] = tokens, off[j] = j * tokens.
+struct KLayout {
+    int64_t head;                 // rows per (sequence, kv head)
+    int64_t off[8];
+    int32_t cap[8];
+};
+
 struct RopeParams {
     const void* k;                // [B][n][Hkv][d]
     const void* v;                // [B][n][Hkv][d]
     const int32_t* pos;           // [B][n] or null (positions t0 + row)
-    uint16_t* kp;                 // pair-blocked rotated keys
+    uint16_t* kp;                 // pair-blocked rotated keys, rows as in kl
     uint16_t* vout;               // transposed (prefill) or row-major (cache) values
+    KLayout kl;
     int64_t n, t0, ld, pad_to;
     int32_t B, Hkv, d, in_f32, v_transposed;
     int32_t interleaved;          // pair i = dims (2i, 2i+1) instead of (i, i+d/2)
@@ -51,8 +62,9 @@ struct PrefillParams {
 
 struct DecodeParams {
     const void* q;                // [B][Hq][d]
-    const uint16_t* kp;           // [B][Hkv][d/16][Lmax][16]
-    const uint16_t* v;            // [B][Hkv][Lmax][d]
+    const uint16_t* kp;           // [B][Hkv][rows as in kl][16]
+    const uint16_t* v;            // [B][Hkv][ceil(Lmax/8)][d][8]
+    KLayout kl;
     const int32_t* kv_len;        // [B]
     const int32_t* q_pos;         // [B] or null
     void* out;                    // [B][Hq][d]

@@ -248,3 +248,64 @@ def test_rope_description_is_validated():
                          ctypes.byref(wpa.Rope(3, None)), 1.0, 0.0, 0, 0, None, 0, FAKE, 1 << 30,
                          None)
     assert rc == wpa.WPA_ERR_INVALID
+
+
+def _window_rows_from_oracle(d, base, Lmax, alpha):
+    """Rows per (sequence, kv head) of the windowed K cache, from the oracle's thresholds:
+    block j keeps floor(alpha * lambda of pair 8j+7) + 1 tokens rounded up to 32, at most
+    Lmax (all Lmax once that window reaches Lmax - 1)."""
+    W = oracle.thresholds(d, base, alpha)
+    rows = 0
+    for j in range(d // 16):
+        t = W[8 * j + 7]
+        cap = Lmax if t >= Lmax - 1 else min(Lmax, (int(math.floor(t)) + 1 + 31) // 32 * 32)
+        rows += cap
+    return rows
+
+
+@pytest.mark.parametrize("d,base,Lmax,alpha", [(128, 5e5, 131072, 1.0), (128, 5e5, 131072, 2.0),
+                                               (128, 1e7, 1 << 20, 1.0), (64, 1e6, 32768, 1.0),
+                                               (64, 1e4, 8192, 1.0), (64, 1e4, 100, 0.0),
+                                               (128, 1e4, 5000, 0.25)])
+def test_window_cache_size_matches_oracle_windows(d, base, Lmax, alpha):
+    got = wpa.lib().wpa_kcache_window_bytes(3, Lmax, 2, d, base, None, alpha)
+    assert got == 3 * 2 * _window_rows_from_oracle(d, base, Lmax, alpha) * 32
+    assert got <= wpa.kcache_bytes(3, Lmax, 2, d)
+
+
+def test_window_cache_llama_shape_saving():
+    """Llama-3.2-3B shape at alpha = 1: the K cache shrinks to about a third."""
+    w = wpa.lib().wpa_kcache_window_bytes(16, 131072, 8, 128, 5e5, None, 1.0)
+    assert 0.30 < w / wpa.kcache_bytes(16, 131072, 8, 128) < 0.40
+
+
+@pytest.mark.parametrize("alpha", [math.inf, float("nan"), -1.0])
+def test_window_cache_rejects_bad_cache_alpha(alpha):
+    assert wpa.lib().wpa_kcache_window_bytes(1, 4096, 2, 64, 1e4, None, alpha) == 0
+    rc = wpa.lib().wpa_kv_write_window(FAKE, FAKE, 0, 16, FAKE, FAKE, 1, 4096, 2, 64, 1e4, None,
+                                       alpha, 0, None)
+    assert rc == wpa.WPA_ERR_INVALID
+
+
+def _decode_window_rc(**kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, lens=FAKE, out=FAKE, lse=None, B=2, Lmax=4096, Hq=8,
+             Hkv=2, d=128, base=5e5, rope=None, calpha=1.0, alpha=1.0, scale=0.0, dtype=0,
+             odt=1, cnt=None, chunk=0, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    return wpa.lib().wpa_decode_window(a["q"], a["kc"], a["vc"], a["lens"], a["out"], a["lse"],
+                                       a["B"], a["Lmax"], a["Hq"], a["Hkv"], a["d"], a["base"],
+                                       a["rope"], a["calpha"], a["alpha"], a["scale"], a["dtype"],
+                                       a["odt"], a["cnt"], a["chunk"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(alpha=2.0), wpa.WPA_ERR_INVALID),
+    (dict(alpha=math.inf), wpa.WPA_ERR_INVALID),
+    (dict(calpha=math.inf), wpa.WPA_ERR_INVALID),
+    (dict(calpha=-0.5), wpa.WPA_ERR_INVALID),
+    (dict(d=96), wpa.WPA_ERR_UNSUPPORTED),
+    (dict(lens=None), wpa.WPA_ERR_INVALID),
+    (dict(ws_bytes=64), wpa.WPA_ERR_WORKSPACE),
+])
+def test_decode_window_rejects_bad_arguments(kw, code):
+    assert _decode_window_rc(**kw) == code
