@@ -57,6 +57,9 @@ def _load():
         lib.orc_prefill_ex.argtypes = [P, P, P, I, P, I, I64, I, I, I, D, P, I, D, D, P, I64, P, P,
                                        P, I]
         lib.orc_prefill_ex.restype = I
+        lib.orc_prefill_sparse.argtypes = [P, P, P, I, I, I64, I, I, I, D, P, I, D, D, P, P, I, I,
+                                           P, I64, P, P, P, I]
+        lib.orc_prefill_sparse.restype = I
         lib.orc_decode_ex.argtypes = [P, P, P, I, P, P, I, I64, I, I, I, D, P, I, D, D, P, P, P, I]
         lib.orc_decode_ex.restype = I
         lib.orc_rope_ex.argtypes = [P, I, I64, I, I, P, D, P, I, P]
@@ -146,6 +149,44 @@ def prefill(q, k, v, base: float, alpha: float, scale: float | None = None, pos=
                                 _ptr(out), _ptr(lse), ctypes.byref(kept), int(nthreads))
     if rc != 0:
         raise ValueError("orc_prefill rejected its arguments")
+    return out, lse, kept.value
+
+
+def prefill_sparse(q, k, v, base: float, alpha: float, count, idx, blk: int = 64,
+                   scale: float | None = None, rows=None, nthreads: int = 0, inv_freq=None,
+                   layout: str = "half"):
+    """Causal windowed prefill restricted to listed key blocks: with R = r // blk, row r of
+    head h attends key c <= r iff c // blk == R or c // blk is among the first
+    count[b][h][R] entries of idx[b][h][R]; other keys leave the softmax.  Positions are
+    token indices.  count int32 [B][Hq][nblk], idx int32 [B][Hq][nblk][max_blocks].
+    Returns (out [B][R][Hq][d], lse [B][Hq][R], kept) in fp64 like prefill()."""
+    q, dt = _as_input(q)
+    k, dk = _as_input(k)
+    v, dv = _as_input(v)
+    assert dt == dk == dv
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    nblk = (N + blk - 1) // blk
+    count = np.ascontiguousarray(count, dtype=np.int32)
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    assert count.shape == (B, Hq, nblk) and idx.shape[:3] == (B, Hq, nblk)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        R = rows.shape[0]
+    else:
+        R = N
+    out = np.empty((B, R, Hq, d), dtype=np.float64)
+    lse = np.empty((B, Hq, R), dtype=np.float64)
+    kept = ctypes.c_int64(0)
+    rc = _load().orc_prefill_sparse(_ptr(q), _ptr(k), _ptr(v), dt, B, N, Hq, Hkv, d, float(base),
+                                    _ptr(_freq(inv_freq, d)), LAYOUTS[layout], float(alpha),
+                                    float(scale), _ptr(count), _ptr(idx), idx.shape[3], blk,
+                                    _ptr(rows), R, _ptr(out), _ptr(lse), ctypes.byref(kept),
+                                    int(nthreads))
+    if rc != 0:
+        raise ValueError("orc_prefill_sparse rejected its arguments")
     return out, lse, kept.value
 
 

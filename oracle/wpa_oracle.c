@@ -123,11 +123,13 @@ void orc_rope(const void* x, int dtype, int64_t n_tok, int H, int d,
 static int64_t orc_row(const double* qr, int64_t qpos, const double* kr, const int64_t* kpos,
                        const void* v, int dtype, int64_t last, int Hkv, int g, int d,
                        int interleaved, const double* thr, double scale, double* logit,
-                       double* out, double* lse) {
+                       double* out, double* lse, const unsigned char* vis) {
+    /* vis (nullable): vis[c] == 0 removes key c from this row's softmax altogether */
     int P = d / 2;
     int64_t kept = 0;
     double m = -INFINITY;
     for (int64_t c = 0; c <= last; ++c) {
+        if (vis && !vis[c]) { logit[c] = -INFINITY; continue; }
         const double* k = kr + (c * Hkv + g) * (int64_t)d;
         double dist = fabs((double)(qpos - kpos[c]));
         double s = 0.0;
@@ -144,6 +146,7 @@ static int64_t orc_row(const double* qr, int64_t qpos, const double* kr, const i
     double den = 0.0;
     for (int e = 0; e < d; ++e) out[e] = 0.0;
     for (int64_t c = 0; c <= last; ++c) {
+        if (vis && !vis[c]) continue;
         double p = exp(logit[c] - m);
         den += p;
         int64_t vrow = (c * Hkv + g) * (int64_t)d;
@@ -209,7 +212,8 @@ int orc_prefill_ex(const void* q, const void* k, const void* v, int dtype, const
                     double* o = out + (((int64_t)b * n_rows + j) * Hq + h) * d;
                     double* l = lse + ((int64_t)b * Hq + h) * n_rows + j;
                     kept_b += orc_row(qr + (j * Hq + h) * (int64_t)d, qp[j], kr, p64, vb, dtype,
-                                      r, Hkv, h / G, d, interleaved, thr, scale, logit, o, l);
+                                      r, Hkv, h / G, d, interleaved, thr, scale, logit, o, l,
+                                      NULL);
                 }
             }
             free(logit);
@@ -227,6 +231,88 @@ int orc_prefill(const void* q, const void* k, const void* v, int dtype, const in
                 double* out, double* lse, int64_t* kept_out, int nthreads) {
     return orc_prefill_ex(q, k, v, dtype, pos, B, N, Hq, Hkv, d, base, NULL, 0, alpha, scale,
                           rows, n_rows, out, lse, kept_out, nthreads);
+}
+
+/*
+ * Causal prefill composed with token-level block sparsity (ATFlash abstract: the window
+ * can be applied on top of other sparse attention methods).  Tokens form blocks of
+ * `blk` consecutive indices; the row of query r (block R = r / blk) of head h attends key c
+ * iff c <= r and c's block is R itself or one of the first count[b][h][R] entries of
+ * idx[b][h][R][0 .. max_blocks).  Keys outside the listed blocks leave the softmax
+ * altogether; the listed ones get the windowed logits of orc_prefill_ex.
+ *   count int32 [B][Hq][nblk], idx int32 [B][Hq][nblk][max_blocks], nblk = ceil(N / blk).
+ * Positions are token indices.  Other arguments and outputs as for orc_prefill_ex.
+ */
+int orc_prefill_sparse(const void* q, const void* k, const void* v, int dtype, int B, int64_t N,
+                       int Hq, int Hkv, int d, double base, const double* inv_freq,
+                       int interleaved, double alpha, double scale, const int32_t* count,
+                       const int32_t* idx, int max_blocks, int blk, const int64_t* rows,
+                       int64_t n_rows, double* out, double* lse, int64_t* kept_out,
+                       int nthreads) {
+    if (B < 1 || N < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || d < 2 || d % 2 != 0 || blk < 1 ||
+        max_blocks < 0 || !count || (max_blocks > 0 && !idx))
+        return -1;
+    if (!rows) n_rows = N;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#endif
+    int G = Hq / Hkv, P = d / 2;
+    int esz = dtype == ORC_FP32 ? 4 : 2;
+    int64_t nblk = (N + blk - 1) / blk;
+    double* thr = (double*)malloc(sizeof(double) * P);
+    orc_thresholds_ex(d, base, inv_freq, alpha, thr);
+    int64_t* p64 = (int64_t*)malloc(sizeof(int64_t) * N);
+    for (int64_t t = 0; t < N; ++t) p64[t] = t;
+    double* kr = (double*)malloc(sizeof(double) * N * Hkv * d);
+    double* qr = (double*)malloc(sizeof(double) * n_rows * Hq * d);
+    int64_t* qp = (int64_t*)malloc(sizeof(int64_t) * n_rows);
+    int64_t kept_total = 0;
+    for (int b = 0; b < B; ++b) {
+        orc_rope_ex((const char*)k + (size_t)esz * b * N * Hkv * d, dtype, N, Hkv, d, p64, base,
+                    inv_freq, interleaved, kr);
+        const char* qb = (const char*)q + (size_t)esz * b * N * Hq * d;
+        char* qsel = (char*)malloc((size_t)esz * n_rows * Hq * d);
+        for (int64_t j = 0; j < n_rows; ++j) {
+            int64_t r = rows ? rows[j] : j;
+            memcpy(qsel + (size_t)esz * j * Hq * d, qb + (size_t)esz * r * Hq * d, (size_t)esz * Hq * d);
+            qp[j] = r;
+        }
+        orc_rope_ex(qsel, dtype, n_rows, Hq, d, qp, base, inv_freq, interleaved, qr);
+        free(qsel);
+        const char* vb = (const char*)v + (size_t)esz * b * N * Hkv * d;
+        int64_t kept_b = 0;
+        #pragma omp parallel reduction(+:kept_b)
+        {
+            double* logit = (double*)malloc(sizeof(double) * N);
+            unsigned char* vis = (unsigned char*)malloc((size_t)N);
+            #pragma omp for schedule(dynamic, 1) collapse(2)
+            for (int64_t j = 0; j < n_rows; ++j) {
+                for (int h = 0; h < Hq; ++h) {
+                    int64_t r = rows ? rows[j] : j;
+                    int64_t R = r / blk;
+                    int64_t li = ((int64_t)b * Hq + h) * nblk + R;
+                    memset(vis, 0, (size_t)N);
+                    for (int64_t c = R * blk; c <= r; ++c) vis[c] = 1;
+                    int n = count[li] < max_blocks ? count[li] : max_blocks;
+                    for (int e = 0; e < n; ++e) {
+                        int64_t kb = idx[li * max_blocks + e];
+                        if (kb < 0 || kb > R) continue;
+                        for (int64_t c = kb * blk; c < (kb + 1) * blk && c <= r; ++c) vis[c] = 1;
+                    }
+                    double* o = out + (((int64_t)b * n_rows + j) * Hq + h) * d;
+                    double* l = lse + ((int64_t)b * Hq + h) * n_rows + j;
+                    kept_b += orc_row(qr + (j * Hq + h) * (int64_t)d, qp[j], kr, p64, vb, dtype,
+                                      r, Hkv, h / G, d, interleaved, thr, scale, logit, o, l, vis);
+                }
+            }
+            free(logit);
+            free(vis);
+        }
+        kept_total += kept_b;
+    }
+    if (kept_out) *kept_out = kept_total;
+    free(thr); free(p64); free(kr); free(qr); free(qp);
+    return 0;
 }
 
 /*
@@ -270,7 +356,7 @@ int orc_decode_ex(const void* q, const void* k, const void* v, int dtype, const 
             for (int h = 0; h < Hq; ++h)
                 kept_b += orc_row(qr + (int64_t)h * d, qp, kr, kp, vb, dtype, L - 1, Hkv, h / G, d,
                                   interleaved, thr, scale, logit, out + ((int64_t)b * Hq + h) * d,
-                                  lse + (int64_t)b * Hq + h);
+                                  lse + (int64_t)b * Hq + h, NULL);
             free(logit);
         }
         kept_total += kept_b;

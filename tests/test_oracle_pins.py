@@ -82,10 +82,11 @@ def test_huge_alpha_is_bitwise_full_window():
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
-def _relative_form(q, k, v, qpos, kpos, base, alpha, scale):
+def _relative_form(q, k, v, qpos, kpos, base, alpha, scale, visible=None):
     """Windowed attention written with the relative (complex) form of each pair's term:
     Term_i = Re( zq_i * conj(zk_i) * exp(1j*(tq - tk)*theta_i) ), computed on pre-RoPE
-    vectors; softmax from scipy.  q [Nq][d], k, v [Nk][d]; causal by token index."""
+    vectors; softmax from scipy.  q [Nq][d], k, v [Nk][d]; causal by token index; an
+    optional boolean visible [Nq][Nk] removes keys from the softmax."""
     d = q.shape[-1]
     P = d // 2
     theta = np.power(float(base), -np.arange(P) * 2.0 / d)
@@ -98,6 +99,8 @@ def _relative_form(q, k, v, qpos, kpos, base, alpha, scale):
     logits = scale * np.where(keep, terms, 0.0).sum(-1)
     Nq, Nk = logits.shape
     causal = np.arange(Nk)[None, :] <= np.arange(Nq)[:, None]
+    if visible is not None:
+        causal = causal & visible
     logits = np.where(causal, logits, -np.inf)
     p = scipy.special.softmax(logits, axis=-1)
     return p @ v, scipy.special.logsumexp(logits, axis=-1)
@@ -451,3 +454,86 @@ def test_table_thresholds_and_counts():
         b = oracle.count_bruteforce(d, 5e5, 1.0, n_q, q0, n_k, inv_freq=theta)
         c = oracle.count_by_distance(d, 5e5, 1.0, n_q, q0, n_k, inv_freq=theta)
         assert a == b == c
+
+
+# ---------------------------------------------------------------------------------------
+# Composition with token-level block sparsity: key blocks listed per query block
+
+
+def _random_lists(B, H, nblk, maxb, seed):
+    """Block lists with the quirks the rule must absorb: unsorted, duplicates, entries
+    above the query block or negative, the query block itself listed or not, counts above
+    max_blocks."""
+    rng = np.random.default_rng(seed)
+    count = rng.integers(0, maxb + 3, (B, H, nblk)).astype(np.int32)
+    idx = rng.integers(-2, nblk + 2, (B, H, nblk, maxb)).astype(np.int32)
+    return count, idx
+
+
+def _visible(N, blk, count, idx):
+    """[B][H][N][N] boolean, written from the rule: c <= r and (c//blk == r//blk or c//blk
+    among the first count entries of r//blk's list)."""
+    B, H, nblk = count.shape
+    vis = np.zeros((B, H, N, N), dtype=bool)
+    for b in range(B):
+        for h in range(H):
+            for r in range(N):
+                R = r // blk
+                listed = set(int(x) for x in idx[b, h, R, :min(int(count[b, h, R]), idx.shape[3])])
+                for c in range(r + 1):
+                    vis[b, h, r, c] = (c // blk == R) or (c // blk in listed)
+    return vis
+
+
+@pytest.mark.parametrize("alpha", [0.5, 1.0, math.inf])
+def test_block_sparse_equals_relative_form_with_mask(alpha):
+    B, N, Hq, Hkv, d, base, blk = 2, 45, 4, 2, 16, 100.0, 8
+    q, k, v = synth.prefill_inputs(B, N, Hq, Hkv, d, "fp32", seed=81)
+    nblk = (N + blk - 1) // blk
+    count, idx = _random_lists(B, Hq, nblk, 4, seed=82)
+    out, lse, kept = oracle.prefill_sparse(synth.to_oracle(q), synth.to_oracle(k),
+                                           synth.to_oracle(v), base, alpha, count, idx, blk=blk)
+    vis = _visible(N, blk, count, idx)
+    pos = np.arange(N)
+    G = Hq // Hkv
+    P = d // 2
+    lam = 2.0 * np.pi * np.power(base, np.arange(P) * 2.0 / d)
+    tally = 0
+    for b in range(B):
+        for h in range(Hq):
+            ro, rl = _relative_form(_f64(q[b, :, h]), _f64(k[b, :, h // G]), _f64(v[b, :, h // G]),
+                                    pos, pos, base, alpha, 1.0 / math.sqrt(d), visible=vis[b, h])
+            np.testing.assert_allclose(out[b, :, h], ro, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(lse[b, h], rl, rtol=0, atol=1e-12)
+            dist = pos[:, None] - pos[None, :]
+            tally += int(((np.abs(dist)[..., None] <= alpha * lam) & vis[b, h][..., None]).sum())
+    assert kept == tally
+
+
+def test_block_sparse_with_every_block_is_dense():
+    """Listing every block is the plain causal prefill, bit for bit."""
+    B, N, Hq, Hkv, d, base, blk = 1, 70, 3, 1, 32, 1e4, 16
+    q, k, v = synth.prefill_inputs(B, N, Hq, Hkv, d, "bf16", seed=83)
+    a = [synth.to_oracle(t) for t in (q, k, v)]
+    nblk = (N + blk - 1) // blk
+    count = np.full((B, Hq, nblk), nblk, np.int32)
+    idx = np.broadcast_to(np.arange(nblk, dtype=np.int32), (B, Hq, nblk, nblk)).copy()
+    o1, l1, k1 = oracle.prefill(*a, base, 1.0)
+    o2, l2, k2 = oracle.prefill_sparse(*a, base, 1.0, count, idx, blk=blk)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2) and k1 == k2
+
+
+def test_block_sparse_empty_lists_are_block_local():
+    """With no listed blocks every row sees only its own block: the same rows as a plain
+    prefill of that block alone (positions shifted, which RoPE attention does not see)."""
+    N, d, base, blk = 48, 16, 1e4, 16
+    q, k, v = synth.prefill_inputs(1, N, 1, 1, d, "fp32", seed=84)
+    count = np.zeros((1, 1, N // blk), np.int32)
+    idx = np.zeros((1, 1, N // blk, 1), np.int32)
+    out, _, _ = oracle.prefill_sparse(synth.to_oracle(q), synth.to_oracle(k), synth.to_oracle(v),
+                                      base, 1.0, count, idx, blk=blk)
+    for R in range(N // blk):
+        sl = slice(R * blk, (R + 1) * blk)
+        ref, _, _ = oracle.prefill(synth.to_oracle(q[:, sl]), synth.to_oracle(k[:, sl]),
+                                   synth.to_oracle(v[:, sl]), base, 1.0)
+        np.testing.assert_allclose(out[:, sl], ref, rtol=0, atol=1e-12)
