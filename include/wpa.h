@@ -246,6 +246,26 @@ int wpa_prefill_cached(const void* q, const void* k_cache, const void* v_cache,
                        int32_t out_dtype, unsigned long long* term_count, void* stream);
 
 /*
+ * Prefill composed with token-level block sparsity (ATFlash abstract: the window can be
+ * applied on top of other sparse attention methods).  Tokens form blocks of 64; the query
+ * rows of block R of q head h attend, besides block R itself (always), only the key blocks
+ * listed for (b, h, R), with the per-pair window on every listed key; keys of unlisted blocks
+ * leave the softmax altogether (unlike pruned terms, which keep the key at logit 0).
+ *   blk_count  int32 device [B][Hq][ceil(N/64)]: list lengths (clamped to [0, blk_max])
+ *   blk_idx    int32 device [B][Hq][ceil(N/64)][blk_max]: key blocks in ascending order;
+ *              entries outside [0, R) are ignored (R is always visited).  An unsorted list is a
+ *              precondition violation (some of its blocks may be skipped).
+ *   positions are token indices; other arguments as for wpa_prefill_ex (the workspace is
+ *   prepared here).  term_count adds the kept terms of the visited keys.
+ */
+int wpa_prefill_sparse(const void* q, const void* k, const void* v, void* out, float* lse,
+                       const int32_t* blk_count, const int32_t* blk_idx, int32_t blk_max,
+                       int32_t B, int64_t N, int32_t Hq, int32_t Hkv, int32_t d, double base,
+                       const wpa_rope_t* rope, double alpha, float scale, int32_t dtype,
+                       int32_t out_dtype, unsigned long long* term_count, void* workspace,
+                       size_t ws_bytes, void* stream);
+
+/*
  * Windowed decode cache (K-dim eviction).  In decode the query is the newest token, so the
  * distance to a given key only grows: once it exceeds the window of every pair of a 16-dim
  * pair block, that block of that key is never read again (WavePrune original abstract:

@@ -39,7 +39,7 @@ EXPORTS = ("wpa_count_terms", "wpa_thresholds", "wpa_prefill_workspace_bytes", "
            "wpa_kv_write", "wpa_decode_workspace_bytes", "wpa_decode", "wpa_count_terms_ex",
            "wpa_thresholds_ex", "wpa_prefill_ex", "wpa_prefill_prepare_ex", "wpa_prefill_attend_ex",
            "wpa_kv_write_ex", "wpa_decode_ex", "wpa_prefill_cached", "wpa_kcache_window_bytes",
-           "wpa_kv_write_window", "wpa_decode_window", "wpa_last_error")
+           "wpa_kv_write_window", "wpa_decode_window", "wpa_prefill_sparse", "wpa_last_error")
 
 
 class Rope(ctypes.Structure):
@@ -153,6 +153,9 @@ def lib():
     L.wpa_decode_window.argtypes = [P, P, P, P, P, P, I32, I64, I32, I32, I32, D, P, D, D, F, I32,
                                     I32, P, I32, P, SZ, P]
     L.wpa_decode_window.restype = ctypes.c_int
+    L.wpa_prefill_sparse.argtypes = [P, P, P, P, P, P, P, I32, I32, I64, I32, I32, I32, D, P, D, F,
+                                     I32, I32, P, P, SZ, P]
+    L.wpa_prefill_sparse.restype = ctypes.c_int
     L.wpa_last_error.argtypes = []
     L.wpa_last_error.restype = ctypes.c_char_p
     _lib = L
@@ -228,8 +231,13 @@ def decode_workspace_bytes(B, Lmax, Hq, Hkv, d, chunk_keys=0) -> int:
 
 def prefill(q, k, v, base: float, alpha: float, *, scale: float | None = None, positions=None,
             out=None, out_dtype=None, lse=None, want_lse: bool = False, term_count=None,
-            workspace=None, stream=None, inv_freq=None, pairs: str = "half"):
+            workspace=None, stream=None, inv_freq=None, pairs: str = "half", block_count=None,
+            block_idx=None):
     """Causal windowed prefill.  q [B][N][Hq][d], k/v [B][N][Hkv][d] (bf16 or fp32, pre-RoPE).
+
+    block_count / block_idx (int32 device [B][Hq][ceil(N/64)] and [...][max]): token-level
+    block sparsity on top of the window; each 64-row query block attends its own block and
+    the ascending list of 64-key blocks given for it.
 
     Returns out [B][N][Hq][d] (out_dtype, default q's dtype), or (out, lse [B][Hq][N] fp32)
     when want_lse or an lse buffer is passed.  term_count: optional int64 device tensor of
@@ -258,6 +266,25 @@ def prefill(q, k, v, base: float, alpha: float, *, scale: float | None = None, p
     if workspace is None:
         workspace = torch.empty(max(need, 16), device=q.device, dtype=torch.uint8)
     rope, keep = _rope(d, inv_freq, pairs)
+    if block_count is not None:
+        # token-level block sparsity on top of the window (blocks of 64 tokens)
+        nblk = (N + 63) // 64
+        if positions is not None:
+            raise ValueError("block-sparse prefill uses token indices as positions")
+        for t, n in ((block_count, "block_count"), (block_idx, "block_idx")):
+            _dev(t, n)
+            if t.dtype != torch.int32 or not t.is_contiguous():
+                raise ValueError("%s must be a contiguous int32 device tensor" % n)
+        if tuple(block_count.shape) != (B, Hq, nblk) or block_idx.dim() != 4 \
+                or tuple(block_idx.shape[:3]) != (B, Hq, nblk):
+            raise ValueError("block_count [B][Hq][ceil(N/64)], block_idx [B][Hq][ceil(N/64)][max]")
+        _check(lib().wpa_prefill_sparse(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                        _ptr(block_count), _ptr(block_idx), block_idx.shape[3],
+                                        B, N, Hq, Hkv, d, float(base), rope, float(alpha),
+                                        float(scale) if scale is not None else 0.0,
+                                        _dtype_code(q), _dtype_code(out), _ptr(term_count),
+                                        _ptr(workspace), workspace.numel(), _stream(stream)))
+        return (out, lse) if lse is not None else out
     _check(lib().wpa_prefill_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(positions),
                                 B, N, Hq, Hkv, d, float(base), rope, float(alpha),
                                 float(scale) if scale is not None else 0.0, _dtype_code(q),

@@ -148,7 +148,10 @@ struct Tile {
 // CACHED: the keys and values are the decode caches (K pair-blocked with row stride
 // ldk = Lmax, V blocked by key octets) and sequence b holds kv_len[b] of them; its Nq
 // queries are its last Nq tokens (chunked prefill).  Positions are token indices.
-template <int D, bool F32, bool HASPOS, bool COUNT, bool CACHED>
+// SPARSE: each (sequence, q head, 64-row query block) attends, besides its own block, only
+// the 64-key blocks its ascending list names (token-level block sparsity composed with the
+// window); unlisted keys leave the softmax.  Positions are token indices.
+template <int D, bool F32, bool HASPOS, bool COUNT, bool CACHED, bool SPARSE>
 __global__ __launch_bounds__(64 * (Tile<D>::maxw(HASPOS) + 1))
 __attribute__((amdgpu_waves_per_eu(Tile<D>::waves_per_eu(HASPOS))))
 void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
@@ -182,6 +185,7 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
     // tq0..NK-1.  Row groups start at multiples of 32 tokens, so the first sub-tile a wave
     // visits holds the diagonal of all its rows.  (Plain prefill: NK = NQ = N, tq0 = 0.)
     const int NQ = CACHED ? p.Nq : (int)p.N;
+    const int N_SP = (int)p.N;
     int NK = (int)p.N;
     if constexpr (CACHED) {
         NK = uniform(p.kv_len[b]);                     // in [Nq, Lmax] by contract; clamped
@@ -411,8 +415,11 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
     };
 
     // One key tile from LDS: its 32-key sub-tiles, nearest keys first.
-    auto compute = [&](int kt, const uint16_t* sK, const uint16_t* sV, const int32_t* sPos) {
+    // kmask: bit i set = key block (ks/64 + i) of this tile is in this wave's list (SPARSE)
+    auto compute = [&](int kt, const uint16_t* sK, const uint16_t* sV, const int32_t* sPos,
+                       int kmask) {
         const int ks = kt * BN;
+        constexpr int FULL = (1 << (BN / 64)) - 1;
         auto POSL = [&](int t) -> int { return uniform(HASPOS ? sPos[t - ks] : t); };
 
         // Plain tile: every key precedes every row of the wave (no causal mask), none is past
@@ -422,7 +429,7 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
         // tile's smallest distance is its nearest sub-tile's, so moving plo there is the step
         // that sub-tile would take anyway.
         bool plain = false;
-        if (started && ks + BN - 1 < q0 && ks + BN <= NK) {
+        if (started && ks + BN - 1 < q0 && ks + BN <= NK && (!SPARSE || kmask == FULL)) {
             const int dmin_t = pq_lo - POSL(ks + BN - 1);
             const int dmax_t = pq_hi - POSL(ks);
             while (w_lo < dmin_t) {
@@ -573,13 +580,24 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
 
         // Sub-tiles above the diagonal, or past the last key, come first in the visiting
         // order and are skipped.
-        int sub = NSUB - 1;
+        int sub = NSUB - 1, sub_lo = 0;
         if (!plain) {
             const int a = (q0 + 31 - ks) >> 5, c = (NK - 1 - ks) >> 5;
             sub = a < sub ? a : sub;
             sub = uniform(c < sub ? c : sub);
+            if constexpr (SPARSE) {
+                // sub-tiles 2i, 2i+1 form key block i of the tile; the wave's blocks here are a
+                // contiguous run of them
+                if (kmask == 0) return;
+                int hi = BN / 64 - 1;
+                while (!((kmask >> hi) & 1)) --hi;
+                int lo = 0;
+                while (!((kmask >> lo) & 1)) ++lo;
+                sub = 2 * hi + 1 < sub ? 2 * hi + 1 : sub;
+                sub_lo = 2 * lo;
+            }
         }
-        if (sub < 0) return;
+        if (sub < sub_lo) return;
         // Software pipeline (d=64, plain tiles): the next sub-tile's chain is issued before
         // this one's softmax, so the matrix cores work while the vector unit does; its -m
         // step waits for this sub-tile's vote, which may move m.  (At d=128 the registers for
@@ -593,7 +611,7 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
         while (true) {
             if (!have) T = raw(sub, true);
             f32x16 S = bias(T);
-            have = PIPE && plain && sub > 0;
+            have = PIPE && plain && sub > sub_lo;
             if (have) T = raw(sub - 1, true);
             uint32_t wd[8];
             float psum = 0.f;
@@ -609,7 +627,7 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
             }
             lsum += psum;
             pv(sub, ks + 32 * sub, wd, sV);
-            if (sub == 0) break;
+            if (sub == sub_lo) break;
             --sub;
         }
     };
@@ -618,19 +636,93 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
     // from the other stage; it waits for its own loads before the barrier that hands the
     // stage over, so no compute wave ever has a direct load in flight (the compiler would
     // otherwise hold every LDS read of a compute wave until such loads land).
-    if (producer) {
-        issue(kt_last, 0);
-        __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
-    }
-    for (int kt = kt_last, it = 0; kt >= 0; --kt, ++it) {
-        __syncthreads();          // tile kt is in stage it&1; stage (it+1)&1 is free again
+    if constexpr (!SPARSE) {
         if (producer) {
-            if (kt > 0) {
-                issue(kt - 1, (it & 1) ^ 1);
-                __builtin_amdgcn_s_waitcnt(0x0070);
+            issue(kt_last, 0);
+            __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+        }
+        for (int kt = kt_last, it = 0; kt >= 0; --kt, ++it) {
+            __syncthreads();          // tile kt is in stage it&1; stage (it+1)&1 is free again
+            if (producer) {
+                if (kt > 0) {
+                    issue(kt - 1, (it & 1) ^ 1);
+                    __builtin_amdgcn_s_waitcnt(0x0070);
+                }
+            } else if (wave_ok) {
+                compute(kt, sK2[it & 1], sV2[it & 1], sPos2[it & 1], 0);
             }
-        } else if (wave_ok) {
-            compute(kt, sK2[it & 1], sV2[it & 1], sPos2[it & 1]);
+        }
+    } else {
+        // Every wave follows the lists of all compute waves of the workgroup, lane l holding
+        // compute wave l's: the next block it needs (its own query block first) and a
+        // cursor walking its ascending list downward.  Tiles are visited in decreasing order
+        // and only where some wave needs a block; every wave derives the same sequence.
+        const int nblk = (N_SP + 63) / 64;
+        int nb = -1, cur = -1;
+        const int32_t* lst = p.blk_idx;
+        {
+            const int hin_l = hc * L.Gc + (lane % L.Gc), rg_l = lane / L.Gc;
+            const int q0_l = qs + 32 * rg_l;
+            if (lane < L.Gc * L.R && hin_l < G && q0_l < NK) {
+                const int rb_l = q0_l >> 6;
+                const int64_t li = ((int64_t)b * p.Hq + g * G + hin_l) * nblk + rb_l;
+                int c = p.blk_count[li];
+                c = c < 0 ? 0 : (c > p.blk_max ? p.blk_max : c);
+                lst = p.blk_idx + li * p.blk_max;
+                cur = c - 1;
+                nb = rb_l;
+            }
+        }
+        auto tile_of = [&](int blk) { return blk < 0 ? -1 : (blk * 64) / BN; };
+        auto wave_max = [&](int x) {
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) {
+                const int y = __shfl_xor(x, o);
+                x = y > x ? y : x;
+            }
+            return uniform(x);
+        };
+        // blocks of tile kt this lane's wave needs, as a mask; moves past them
+        auto take = [&](int kt) {
+            const int b0 = kt * BN / 64;
+            int mask = 0;
+            while (nb >= b0) {
+                mask |= 1 << (nb - b0);
+                int nx = -1;
+                while (cur >= 0) {
+                    const int e = lst[cur--];
+                    if (e >= 0 && e < nb) {
+                        nx = e;
+                        break;
+                    }
+                }
+                nb = nx;
+            }
+            return mask;
+        };
+        int kt = wave_max(tile_of(nb));
+        int mask = kt >= 0 ? take(kt) : 0;
+        int kt_next = wave_max(tile_of(nb));
+        if (producer && kt >= 0) {
+            issue(kt, 0);
+            __builtin_amdgcn_s_waitcnt(0x0070);
+        }
+        for (int it = 0; kt >= 0; ++it) {
+            __syncthreads();
+            if (producer) {
+                if (kt_next >= 0) {
+                    issue(kt_next, (it & 1) ^ 1);
+                    __builtin_amdgcn_s_waitcnt(0x0070);
+                }
+            } else if (wave_ok) {
+                compute(kt, sK2[it & 1], sV2[it & 1], sPos2[it & 1],
+                        __builtin_amdgcn_readlane(mask, w));
+            }
+            kt = kt_next;
+            if (kt >= 0) {
+                mask = take(kt);
+                kt_next = wave_max(tile_of(nb));
+            }
         }
     }
 
@@ -682,12 +774,15 @@ hipError_t launch_d(const PrefillParams& p, const Tables& t, hipStream_t s) {
     dim3 grid((unsigned)nblk), block(64 * waves);
     const bool hp = p.pos != nullptr, cn = p.counter != nullptr;
     if (p.kv_len) {
-        if (cn) prefill_kernel<D, F32, false, true, true><<<grid, block, 0, s>>>(p, t, L);
-        else prefill_kernel<D, F32, false, false, true><<<grid, block, 0, s>>>(p, t, L);
-    } else if (hp && cn) prefill_kernel<D, F32, true, true, false><<<grid, block, 0, s>>>(p, t, L);
-    else if (hp) prefill_kernel<D, F32, true, false, false><<<grid, block, 0, s>>>(p, t, L);
-    else if (cn) prefill_kernel<D, F32, false, true, false><<<grid, block, 0, s>>>(p, t, L);
-    else prefill_kernel<D, F32, false, false, false><<<grid, block, 0, s>>>(p, t, L);
+        if (cn) prefill_kernel<D, F32, false, true, true, false><<<grid, block, 0, s>>>(p, t, L);
+        else prefill_kernel<D, F32, false, false, true, false><<<grid, block, 0, s>>>(p, t, L);
+    } else if (p.blk_count) {
+        if (cn) prefill_kernel<D, F32, false, true, false, true><<<grid, block, 0, s>>>(p, t, L);
+        else prefill_kernel<D, F32, false, false, false, true><<<grid, block, 0, s>>>(p, t, L);
+    } else if (hp && cn) prefill_kernel<D, F32, true, true, false, false><<<grid, block, 0, s>>>(p, t, L);
+    else if (hp) prefill_kernel<D, F32, true, false, false, false><<<grid, block, 0, s>>>(p, t, L);
+    else if (cn) prefill_kernel<D, F32, false, true, false, false><<<grid, block, 0, s>>>(p, t, L);
+    else prefill_kernel<D, F32, false, false, false, false><<<grid, block, 0, s>>>(p, t, L);
     return hipGetLastError();
 }
 

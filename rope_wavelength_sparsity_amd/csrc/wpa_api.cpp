@@ -289,11 +289,40 @@ int wpa_prefill_attend(const void* q, void* out, float* lse, const int32_t* posi
                                  scale, dtype, out_dtype, term_count, workspace, ws_bytes, stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+int attend_impl(const void* q, void* out, float* lse, const int32_t* positions, int32_t B,
+                int64_t N, int32_t Hq, int32_t Hkv, int32_t d, double base,
+                const wpa_rope_t* rope, double alpha, float scale, int32_t dtype,
+                int32_t out_dtype, unsigned long long* term_count, const void* workspace,
+                size_t ws_bytes, void* stream, const int32_t* blk_count,
+                const int32_t* blk_idx, int32_t blk_max);
+
+}  // namespace
+
+extern "C" {
+
 int wpa_prefill_attend_ex(const void* q, void* out, float* lse, const int32_t* positions,
                           int32_t B, int64_t N, int32_t Hq, int32_t Hkv, int32_t d, double base,
                           const wpa_rope_t* rope, double alpha, float scale, int32_t dtype,
                           int32_t out_dtype, unsigned long long* term_count,
                           const void* workspace, size_t ws_bytes, void* stream) {
+    return attend_impl(q, out, lse, positions, B, N, Hq, Hkv, d, base, rope, alpha, scale, dtype,
+                       out_dtype, term_count, workspace, ws_bytes, stream, nullptr, nullptr, 0);
+}
+
+}  // extern "C"
+
+namespace {
+
+int attend_impl(const void* q, void* out, float* lse, const int32_t* positions, int32_t B,
+                int64_t N, int32_t Hq, int32_t Hkv, int32_t d, double base,
+                const wpa_rope_t* rope, double alpha, float scale, int32_t dtype,
+                int32_t out_dtype, unsigned long long* term_count, const void* workspace,
+                size_t ws_bytes, void* stream, const int32_t* blk_count,
+                const int32_t* blk_idx, int32_t blk_max) {
     int rc = check_common(d, base, rope, alpha);
     if (rc) return rc;
     rc = check_prefill_shape(N, B, Hkv, dtype, positions, workspace, ws_bytes, d);
@@ -316,10 +345,15 @@ int wpa_prefill_attend_ex(const void* q, void* out, float* lse, const int32_t* p
     pp.pos = positions; pp.counter = term_count; pp.N = N; pp.Np = Np; pp.ldk = Np; pp.B = B; pp.Hq = Hq;
     pp.Hkv = Hkv; pp.d = d; pp.in_f32 = dtype == WPA_FP32; pp.out_f32 = out_dtype == WPA_FP32;
     pp.scale = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)d));
+    pp.blk_count = blk_count; pp.blk_idx = blk_idx; pp.blk_max = blk_max;
     hipError_t e = wpa::launch_prefill(pp, tab, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(WPA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
     return ok();
 }
+
+}  // namespace
+
+extern "C" {
 
 int wpa_prefill(const void* q, const void* k, const void* v, void* out, float* lse,
                 const int32_t* positions, int32_t B, int64_t N, int32_t Hq, int32_t Hkv,
@@ -354,6 +388,35 @@ int wpa_prefill_ex(const void* q, const void* k, const void* v, void* out, float
     if (rc) return rc;
     return wpa_prefill_attend_ex(q, out, lse, positions, B, N, Hq, Hkv, d, base, rope, alpha, scale,
                                  dtype, out_dtype, term_count, workspace, ws_bytes, stream);
+}
+
+int wpa_prefill_sparse(const void* q, const void* k, const void* v, void* out, float* lse,
+                       const int32_t* blk_count, const int32_t* blk_idx, int32_t blk_max,
+                       int32_t B, int64_t N, int32_t Hq, int32_t Hkv, int32_t d, double base,
+                       const wpa_rope_t* rope, double alpha, float scale, int32_t dtype,
+                       int32_t out_dtype, unsigned long long* term_count, void* workspace,
+                       size_t ws_bytes, void* stream) {
+    int rc = check_common(d, base, rope, alpha);
+    if (rc) return rc;
+    if (B < 1 || N < 1 || Hq < 1 || Hkv < 1) return fail(WPA_ERR_INVALID, "B, N, Hq, Hkv must be >= 1");
+    if (Hq % Hkv) return fail(WPA_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+    if (!blk_count || (blk_max > 0 && !blk_idx) || blk_max < 0)
+        return fail(WPA_ERR_INVALID, "block lists: need blk_count, blk_max >= 0 and blk_idx when blk_max > 0");
+    if ((reinterpret_cast<uintptr_t>(blk_count) & 3u) || (reinterpret_cast<uintptr_t>(blk_idx) & 3u))
+        return fail(WPA_ERR_INVALID, "block lists must be 4-byte aligned");
+    if (std::isnan(scale)) return fail(WPA_ERR_INVALID, "scale is NaN");
+    if (out_dtype != WPA_BF16 && out_dtype != WPA_FP32) return fail(WPA_ERR_INVALID, "out_dtype must be WPA_BF16 or WPA_FP32");
+    if (!q || !k || !v || !out) return fail(WPA_ERR_INVALID, "null q, k, v or out");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(WPA_ERR_INVALID, "q, k, v and out must be 16-byte aligned");
+    rc = check_prefill_shape(N, B, Hkv, dtype, nullptr, workspace, ws_bytes, d);
+    if (rc) return rc;
+    rc = wpa_prefill_prepare_ex(k, v, nullptr, B, N, Hkv, d, base, rope, dtype, workspace,
+                                ws_bytes, stream);
+    if (rc) return rc;
+    return attend_impl(q, out, lse, nullptr, B, N, Hq, Hkv, d, base, rope, alpha, scale, dtype,
+                       out_dtype, term_count, workspace, ws_bytes, stream, blk_count,
+                       blk_idx ? blk_idx : blk_count, blk_max);
 }
 
 size_t wpa_kcache_bytes(int32_t B, int64_t Lmax, int32_t Hkv, int32_t d) {
