@@ -256,7 +256,8 @@ int wpa_prefill_cached(const void* q, const void* k_cache, const void* v_cache,
  *              entries outside [0, R) are ignored (R is always visited).  An unsorted list is a
  *              precondition violation (some of its blocks may be skipped).
  *   positions are token indices; other arguments as for wpa_prefill_ex (the workspace is
- *   prepared here).  term_count adds the kept terms of the visited keys.
+ *   prepared here).  term_count adds the kept terms of the visited keys.  N up to 2^21
+ *   (WPA_ERR_UNSUPPORTED above: the lists are held as bitmaps in LDS).
  */
 int wpa_prefill_sparse(const void* q, const void* k, const void* v, void* out, float* lse,
                        const int32_t* blk_count, const int32_t* blk_idx, int32_t blk_max,

@@ -163,6 +163,7 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
     __shared__ __attribute__((aligned(16))) uint16_t sK2[2][NB * BN * 16];
     __shared__ __attribute__((aligned(16))) uint16_t sV2[2][D * BN];
     __shared__ __attribute__((aligned(16))) int32_t sPos2[2][HASPOS ? BN : 1];
+    extern __shared__ uint32_t sBits[];       // SPARSE: block bitmaps (dynamic size)
 
     const int tid = threadIdx.x;
     // wave index through readfirstlane: everything derived from it (head, rows, band
@@ -653,75 +654,57 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
             }
         }
     } else {
-        // Every wave follows the lists of all compute waves of the workgroup, lane l holding
-        // compute wave l's: the next block it needs (its own query block first) and a
-        // cursor walking its ascending list downward.  Tiles are visited in decreasing order
-        // and only where some wave needs a block; every wave derives the same sequence.
-        const int nblk = (N_SP + 63) / 64;
-        int nb = -1, cur = -1;
-        const int32_t* lst = p.blk_idx;
-        {
-            const int hin_l = hc * L.Gc + (lane % L.Gc), rg_l = lane / L.Gc;
-            const int q0_l = qs + 32 * rg_l;
-            if (lane < L.Gc * L.R && hin_l < G && q0_l < NK) {
-                const int rb_l = q0_l >> 6;
-                const int64_t li = ((int64_t)b * p.Hq + g * G + hin_l) * nblk + rb_l;
-                int c = p.blk_count[li];
-                c = c < 0 ? 0 : (c > p.blk_max ? p.blk_max : c);
-                lst = p.blk_idx + li * p.blk_max;
-                cur = c - 1;
-                nb = rb_l;
+        // The lists as bitmaps in LDS: one bit per 64-key block for each compute wave (its own
+        // query block always set) and their union.
+        const int nblk = (N_SP + 63) / 64, words = (nblk + 31) / 32;
+        const int NL = L.Gc * L.R;
+        uint32_t* uni = sBits + NL * words;
+        for (int i = tid; i < (NL + 1) * words; i += blockDim.x) sBits[i] = 0u;
+        __syncthreads();
+        if (!producer && wave_ok) {
+            const int rb = q0 >> 6;
+            uint32_t* mine = sBits + w * words;
+            if (lane == 0) {
+                atomicOr(&mine[rb >> 5], 1u << (rb & 31));
+                atomicOr(&uni[rb >> 5], 1u << (rb & 31));
+            }
+            const int64_t li = ((int64_t)b * p.Hq + hq) * nblk + rb;
+            int c = p.blk_count[li];
+            c = c < 0 ? 0 : (c > p.blk_max ? p.blk_max : c);
+            for (int e = lane; e < c; e += 64) {
+                const int kb = p.blk_idx[li * p.blk_max + e];
+                if (kb >= 0 && kb < rb) {
+                    atomicOr(&mine[kb >> 5], 1u << (kb & 31));
+                    atomicOr(&uni[kb >> 5], 1u << (kb & 31));
+                }
             }
         }
-        auto tile_of = [&](int blk) { return blk < 0 ? -1 : (blk * 64) / BN; };
-        auto wave_max = [&](int x) {
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) {
-                const int y = __shfl_xor(x, o);
-                x = y > x ? y : x;
-            }
-            return uniform(x);
-        };
-        // blocks of tile kt this lane's wave needs, as a mask; moves past them
-        auto take = [&](int kt) {
+        __syncthreads();
+        // this compute wave's blocks of tile kt (tiles start at even blocks: no word straddle)
+        auto wmask = [&](int kt) -> int {
             const int b0 = kt * BN / 64;
-            int mask = 0;
-            while (nb >= b0) {
-                mask |= 1 << (nb - b0);
-                int nx = -1;
-                while (cur >= 0) {
-                    const int e = lst[cur--];
-                    if (e >= 0 && e < nb) {
-                        nx = e;
-                        break;
-                    }
-                }
-                nb = nx;
-            }
-            return mask;
+            return uniform((int)((sBits[w * words + (b0 >> 5)] >> (b0 & 31)) & ((1u << (BN / 64)) - 1u)));
         };
-        int kt = wave_max(tile_of(nb));
-        int mask = kt >= 0 ? take(kt) : 0;
-        int kt_next = wave_max(tile_of(nb));
-        if (producer && kt >= 0) {
-            issue(kt, 0);
+        // Every tile is visited (a loop jumping between needed tiles made the compiler keep
+        // two copies of the accumulators); the producer loads only the needed ones, and a
+        // compute wave returns at once from a tile without its blocks.
+        auto needed = [&](int kt) {
+            const int b0 = kt * BN / 64;
+            return ((uni[b0 >> 5] >> (b0 & 31)) & ((1u << (BN / 64)) - 1u)) != 0u;
+        };
+        if (producer) {
+            if (needed(kt_last)) issue(kt_last, 0);
             __builtin_amdgcn_s_waitcnt(0x0070);
         }
-        for (int it = 0; kt >= 0; ++it) {
+        for (int kt = kt_last, it = 0; kt >= 0; --kt, ++it) {
             __syncthreads();
             if (producer) {
-                if (kt_next >= 0) {
-                    issue(kt_next, (it & 1) ^ 1);
+                if (kt > 0 && needed(kt - 1)) {
+                    issue(kt - 1, (it & 1) ^ 1);
                     __builtin_amdgcn_s_waitcnt(0x0070);
                 }
             } else if (wave_ok) {
-                compute(kt, sK2[it & 1], sV2[it & 1], sPos2[it & 1],
-                        __builtin_amdgcn_readlane(mask, w));
-            }
-            kt = kt_next;
-            if (kt >= 0) {
-                mask = take(kt);
-                kt_next = wave_max(tile_of(nb));
+                compute(kt, sK2[it & 1], sV2[it & 1], sPos2[it & 1], wmask(kt));
             }
         }
     }
@@ -777,8 +760,12 @@ hipError_t launch_d(const PrefillParams& p, const Tables& t, hipStream_t s) {
         if (cn) prefill_kernel<D, F32, false, true, true, false><<<grid, block, 0, s>>>(p, t, L);
         else prefill_kernel<D, F32, false, false, true, false><<<grid, block, 0, s>>>(p, t, L);
     } else if (p.blk_count) {
-        if (cn) prefill_kernel<D, F32, false, true, false, true><<<grid, block, 0, s>>>(p, t, L);
-        else prefill_kernel<D, F32, false, false, false, true><<<grid, block, 0, s>>>(p, t, L);
+        // block bitmaps: one per compute wave and their union
+        const size_t words = (size_t)(((p.N + 63) / 64 + 31) / 32);
+        const size_t bits = (size_t)(L.Gc * L.R + 1) * words * 4;
+        if (bits > 65536) return hipErrorInvalidValue;
+        if (cn) prefill_kernel<D, F32, false, true, false, true><<<grid, block, bits, s>>>(p, t, L);
+        else prefill_kernel<D, F32, false, false, false, true><<<grid, block, bits, s>>>(p, t, L);
     } else if (hp && cn) prefill_kernel<D, F32, true, true, false, false><<<grid, block, 0, s>>>(p, t, L);
     else if (hp) prefill_kernel<D, F32, true, false, false, false><<<grid, block, 0, s>>>(p, t, L);
     else if (cn) prefill_kernel<D, F32, false, true, false, false><<<grid, block, 0, s>>>(p, t, L);

@@ -400,6 +400,7 @@ int wpa_prefill_sparse(const void* q, const void* k, const void* v, void* out, f
     if (rc) return rc;
     if (B < 1 || N < 1 || Hq < 1 || Hkv < 1) return fail(WPA_ERR_INVALID, "B, N, Hq, Hkv must be >= 1");
     if (Hq % Hkv) return fail(WPA_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+    if (N > ((int64_t)1 << 21)) return fail(WPA_ERR_UNSUPPORTED, "block-sparse prefill supports N up to 2^21 tokens");
     if (!blk_count || (blk_max > 0 && !blk_idx) || blk_max < 0)
         return fail(WPA_ERR_INVALID, "block lists: need blk_count, blk_max >= 0 and blk_idx when blk_max > 0");
     if ((reinterpret_cast<uintptr_t>(blk_count) & 3u) || (reinterpret_cast<uintptr_t>(blk_idx) & 3u))
