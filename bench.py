@@ -54,6 +54,10 @@ def _parse():
                          "at N = 32K..1M for the Llama-3.2-3B and Qwen2.5-7B-1M shapes, prefill "
                          "and decode (B=1 and B=16), printed as one JSON line")
     ap.add_argument("--sweep-max", type=int, default=1 << 20, help="largest N of the sweep")
+    ap.add_argument("--extras", action="store_true",
+                    help="instead of the headline line: the paths beside the core one (windowed "
+                         "decode cache, chunked prefill, RoPE variants, block-sparse prefill), "
+                         "printed as one JSON line")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (twice), as the "
                          "reference kernel for scaling FETCH_SIZE/WRITE_SIZE counters")
@@ -298,6 +302,140 @@ def _traffic(kernel_file, workload, alpha):
     return None
 
 
+def _time(fn, reps):
+    """Mean ms of reps calls after one warm-up call (HIP events on the current stream)."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    a, b = _events(2)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def _block_lists(B, H, N, density, seed):
+    """MInference-like block lists (64-token blocks): the first block, the two blocks below the
+    query block, and each earlier block with probability `density`; ascending."""
+    import numpy as np
+    import torch
+    rng = np.random.default_rng(seed)
+    nblk = (N + 63) // 64
+    width = max(3, int(density * nblk) + 8)
+    count = np.zeros((B, H, nblk), np.int32)
+    idx = np.zeros((B, H, nblk, width), np.int32)
+    for b in range(B):
+        for h in range(H):
+            for R in range(nblk):
+                s = {0, R - 1, R - 2} | set(np.nonzero(rng.random(R) < density)[0].tolist())
+                s = sorted(c for c in s if 0 <= c < R)[-width:]
+                count[b, h, R] = len(s)
+                idx[b, h, R, :len(s)] = s
+    return torch.from_numpy(count).cuda(), torch.from_numpy(idx).cuda()
+
+
+def extras(reps):
+    """Measurements of the paths beside the core prefill/decode, one dict per path."""
+    import torch
+    import rope_wavelength_sparsity_amd as wpa
+    import synth
+    res = {}
+    w = synth.WORKLOADS["qwen05b"]
+    q, k, v = synth.workload_inputs(w, device="cuda")
+    ws = torch.empty(wpa.prefill_workspace_bytes(w.B, w.N, w.Hkv, w.d), device="cuda",
+                     dtype=torch.uint8)
+    kept_full, _ = wpa.count_terms(w.d, w.base, 1.0, w.N, 0, w.N)
+    dense_flops = w.B * w.Hq * (4 * kept_full + 2 * w.d * w.N * (w.N + 1) // 2)
+    t_one = _time(lambda: wpa.prefill(q, k, v, w.base, 1.0, workspace=ws), reps)
+
+    # RoPE variants: the same prefill with a Llama-3-style frequency table, interleaved pairs
+    theta = wpa.llama3_inv_freq(w.d, w.base, factor=32.0, low_freq_factor=1.0,
+                                high_freq_factor=4.0, original_max_position=8192)
+    var = {"workload": "qwen05b prefill (prepare + attend), alpha 1", "half_split_ms": t_one}
+    for name, kw in (("llama3_table_ms", dict(inv_freq=theta)),
+                     ("interleaved_ms", dict(pairs="interleaved")),
+                     ("llama3_table_interleaved_ms", dict(inv_freq=theta, pairs="interleaved"))):
+        var[name] = _time(lambda: wpa.prefill(q, k, v, w.base, 1.0, workspace=ws, **kw), reps)
+    kept_t, _ = wpa.count_terms(w.d, w.base, 1.0, w.N, 0, w.N, inv_freq=theta)
+    var["llama3_table_tflops"] = w.B * w.Hq * (4 * kept_t + 2 * w.d * w.N * (w.N + 1) // 2) / (
+        var["llama3_table_ms"] * 1e-3) / 1e12
+    res["rope_variants"] = var
+    _log("extras: rope variants %s" % var)
+
+    # chunked prefill: the same prompt appended and attended in chunks against the decode caches
+    ch = {"workload": "qwen05b prompt of 32768 tokens, alpha 1", "one_shot_ms": t_one,
+          "one_shot_tflops": dense_flops / (t_one * 1e-3) / 1e12}
+    for C in (4096, 8192):
+        cache = wpa.KVCache(w.B, w.N, w.Hkv, w.d, w.base)
+        out = torch.empty_like(q)
+
+        def run():
+            for s in range(0, w.N, C):
+                cache.write(k[:, s:s + C], v[:, s:s + C], s)
+                lens = torch.full((w.B,), s + C, dtype=torch.int32, device="cuda")
+                wpa.prefill_cached(q[:, s:s + C], cache, lens, 1.0, out=out[:, s:s + C])
+        t = _time(run, max(1, reps // 2))
+        ch["chunks_%d_ms" % C] = t
+        ch["chunks_%d_tflops" % C] = dense_flops / (t * 1e-3) / 1e12
+        del cache, out
+    res["chunked_prefill"] = ch
+    _log("extras: chunked %s" % ch)
+
+    # block-sparse prefill on top of the window
+    sp = {"workload": "qwen05b prefill (prepare + attend), alpha 1, 64-token blocks: first block, "
+                      "two local blocks and random earlier blocks"}
+    for dens in (0.3, 0.1):
+        bc, bi = _block_lists(w.B, w.Hq, w.N, dens, 5)
+        t = _time(lambda: wpa.prefill(q, k, v, w.base, 1.0, workspace=ws, block_count=bc,
+                                      block_idx=bi), reps)
+        cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
+        wpa.prefill(q, k, v, w.base, 1.0, workspace=ws, block_count=bc, block_idx=bi,
+                    term_count=cnt)
+        # active flops: 4 per kept term, P*V over the visited keys
+        vis = 0
+        cnt_h = bc.cpu().numpy()
+        for R in range(cnt_h.shape[2]):
+            # keys visited by the rows of block R: own block (causal) + listed blocks
+            vis += int(cnt_h[:, :, R].sum()) * 64 * 64 + w.B * w.Hq * (64 * 65 // 2)
+        flops = 4 * int(cnt.item()) + 2 * w.d * vis
+        sp["density_%g" % dens] = {"ms": t, "vs_dense_window": t / t_one,
+                                   "active_tflops": flops / (t * 1e-3) / 1e12}
+        del bc, bi
+    res["block_sparse_prefill"] = sp
+    _log("extras: block sparse %s" % sp)
+    del q, k, v, ws
+    torch.cuda.empty_cache()
+
+    # windowed decode cache: same step, K cache kept only inside each block's window
+    wd = synth.WORKLOADS["llama3b_decode"]
+    qd, kd, vd, lens = synth.workload_inputs(wd, device="cuda")
+    dec = {"workload": "llama3b_decode, alpha 1"}
+    nbytes = 0
+    for L in lens.cpu().tolist():
+        kp, _ = wpa.count_terms(wd.d, wd.base, 1.0, 1, L - 1, L)
+        nbytes += wd.Hkv * (4 * kp + 2 * wd.d * L)
+    for name, walpha in (("dense_cache", None), ("window_cache", 1.0)):
+        cache = wpa.KVCache(wd.B, wd.N, wd.Hkv, wd.d, wd.base, window_alpha=walpha)
+        for bi_, L in enumerate(lens.cpu().tolist()):        # each sequence up to its length
+            cache.write(kd[bi_:bi_ + 1, :L].contiguous(), vd[bi_:bi_ + 1, :L].contiguous(), 0,
+                        seq=bi_)
+        wsd = torch.empty(max(wpa.decode_workspace_bytes(wd.B, wd.N, wd.Hq, wd.Hkv, wd.d), 16),
+                          device="cuda", dtype=torch.uint8)
+        out = torch.empty_like(qd)
+        t = _time(lambda: wpa.decode(qd, cache, lens, 1.0, out=out, workspace=wsd), reps)
+        dec[name] = {"ms": t, "gbs": nbytes / (t * 1e-3) / 1e9, "k_cache_bytes": cache.k.numel(),
+                     "v_cache_bytes": cache.v.numel()}
+        del cache, wsd, out
+        torch.cuda.empty_cache()
+    dec["kv_bytes_ratio"] = (dec["window_cache"]["k_cache_bytes"] + dec["window_cache"]["v_cache_bytes"]) / (
+        dec["dense_cache"]["k_cache_bytes"] + dec["dense_cache"]["v_cache_bytes"])
+    res["window_decode_cache"] = dec
+    _log("extras: window cache %s" % dec)
+    return res
+
+
 def main():
     args = _parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -311,6 +449,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.sweep:
         print(json.dumps(sweep(args.sweep_max)), flush=True)
+        return
+    if args.extras:
+        print(json.dumps({"extras": extras(max(3, args.steps // 4))}), flush=True)
         return
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib << 20
