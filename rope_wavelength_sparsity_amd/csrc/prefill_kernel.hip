@@ -599,21 +599,14 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
             }
         }
         if (sub < sub_lo) return;
-        // Software pipeline (d=64, plain tiles): the next sub-tile's chain is issued before
-        // this one's softmax, so the matrix cores work while the vector unit does; its -m
-        // step waits for this sub-tile's vote, which may move m.  (At d=128 the registers for
-        // a second score block would cost a wave per SIMD.)  A sub-tile that fails the vote
-        // recomputes its scores: a plain tile's band is fixed, and elsewhere the band still
-        // sits at this sub-tile.
-        constexpr bool PIPE = D == 64;
-        f32x16 T;
-        bool have = false;                      // T holds sub-tile `sub`'s scores already
+        // The -m step of a sub-tile follows the previous sub-tile's vote, which may move m.  A
+        // sub-tile that fails the vote recomputes its scores (the band still sits at it).  (Issuing
+        // the next sub-tile's chain before this one's softmax cost the d=64 kernel 12 spilled
+        // registers and 3%.)
 #pragma unroll 1
         while (true) {
-            if (!have) T = raw(sub, true);
+            const f32x16 T = raw(sub, true);
             f32x16 S = bias(T);
-            have = PIPE && plain && sub > sub_lo;
-            if (have) T = raw(sub - 1, true);
             uint32_t wd[8];
             float psum = 0.f;
             bool redo = !started;
