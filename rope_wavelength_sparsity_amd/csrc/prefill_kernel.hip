@@ -605,6 +605,7 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
         // registers and 3%.)
 #pragma unroll 1
         while (true) {
+            sub = uniform(sub);      // (merged from two branches it would otherwise live in a VGPR)
             const f32x16 T = raw(sub, true);
             f32x16 S = bias(T);
             uint32_t wd[8];
