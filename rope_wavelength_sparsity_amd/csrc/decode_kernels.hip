@@ -5,7 +5,8 @@
 // Work item = (sequence b, kv head g, chunk of `chunk` keys); items past kv_len exit.
 // Each item serves all G q heads of its kv head, so every K/V byte is read once per step.
 // The 4 waves take interleaved 32-key tiles of the chunk, each with its own online-softmax
-// state, merged in LDS at the end.
+// state, merged in LDS at the end.  A wave's next tile is in flight while it computes the
+// current one.
 //
 // Per 32-key tile (one 32x32x16 MFMA row block):
 //   S^T[32 keys x 32 cols] = K'[keys x 16 dims] * Q'^T, one MFMA per active 16-dim pair
@@ -28,6 +29,8 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr float kTau = 8.0f;
+constexpr int kBufWord3 = 0x00020000;   // buffer descriptor word 3 (raw bytes, no format)
+constexpr int kNT = 2;                  // buffer load cache policy: non-temporal
 
 __device__ inline int perm_row(int m) {
     return (m & ~0xC) | ((m & 4) << 1) | ((m & 8) >> 1);
@@ -47,18 +50,20 @@ void decode_partial_kernel(DecodeParams p, Tables tab) {
     __shared__ __attribute__((aligned(16))) uint16_t sQ[32][D];      // pair-blocked, half
     __shared__ float sO[kWaves][GMAX][D + 2];
 
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l32 = lane & 31, h = lane >> 5;
     const int xaddr = (lane ^ 32) << 2;
     const int G = p.Hq / p.Hkv;
     const int chunk = blockIdx.x % p.n_chunks;
     const int bg = blockIdx.x / p.n_chunks;
     const int g = bg % p.Hkv, b = bg / p.Hkv;
     const int Lb = __builtin_amdgcn_readfirstlane(p.kv_len[b]);
-    const int c0 = chunk * p.chunk;
-    if (c0 >= Lb) return;
-    const int c1 = c0 + p.chunk < Lb ? c0 + p.chunk : Lb;
+    const int key_lo = chunk * p.chunk;
+    if (key_lo >= Lb) return;
+    const int key_hi = key_lo + p.chunk < Lb ? key_lo + p.chunk : Lb;
     const int64_t qpos = __builtin_amdgcn_readfirstlane(p.q_pos ? p.q_pos[b] : Lb - 1);
     const float sl2 = p.scale * 1.4426950408889634f;
+    uint64_t cnt = 0;
 
     // rotated q of the G heads (pre-scaled into log2 units), pair-blocked half-precision
     // rows; rows >= G are zero
@@ -101,90 +106,110 @@ void decode_partial_kernel(DecodeParams p, Tables tab) {
 #pragma unroll
     for (int i = 0; i < NDB; ++i) O[i] = f32x16{};
     float m = -INFINITY, lsum = 0.f;
-    uint64_t cnt = 0;
     const int arow = perm_row(l32);                  // key row this lane feeds to the A operand
 
     const char* kbytes = reinterpret_cast<const char*>(kpg);
     const char* vbytes = reinterpret_cast<const char*>(vg);
-    const uint32_t voff0 = (uint32_t)((h * D + l32) * 16);
-    int plo = 0, pfull = 0;                          // band edges, moved incrementally
-    for (int k0 = c0 + 32 * w; k0 < c1; k0 += 32 * kWaves) {
-        const int kmax = k0 + 31 < c1 ? k0 + 31 : c1 - 1;
+    const int koffl = arow * 32 + 16 * h;            // lane offset in a K block's 32 rows
+    const int Wl = lane < P ? tab.W[lane] : INT32_MAX;   // window of pair `lane`
+    const int voffl = (h * D + l32) * 16;            // lane offset in a tile's V octets
+    int plo = 0, pfull = 0;                          // band edges of the current tile
+
+    // Band of the tile at k0: the first pair with W >= its smallest distance (plo) and
+    // with W >= its largest (pfull), i.e. the numbers of pairs with W below them (W is
+    // non-decreasing in the pair index): one ballot over the lane-held table each.
+    auto band = [&](int k0) {
+        const int kmax = k0 + 31 < key_hi ? k0 + 31 : key_hi - 1;
         int64_t dlo, dhi;
         if (qpos >= kmax) { dlo = qpos - kmax; dhi = qpos - k0; }
         else if (qpos <= k0) { dlo = k0 - qpos; dhi = kmax - qpos; }
         else { dlo = 0; dhi = (qpos - k0 > kmax - qpos) ? qpos - k0 : kmax - qpos; }
         const int dl = __builtin_amdgcn_readfirstlane((int)(dlo < INT32_MAX ? dlo : INT32_MAX));
         const int dh = __builtin_amdgcn_readfirstlane((int)(dhi < INT32_MAX ? dhi : INT32_MAX));
-        // first pair with W >= dl (resp. dh); consecutive tiles of a wave move these by a
-        // step or two, so walk from the previous value instead of searching
-        while (plo > 0 && tab.W[plo - 1] >= dl) --plo;
-        while (plo < P && tab.W[plo] < dl) ++plo;
-        while (pfull > 0 && tab.W[pfull - 1] >= dh) --pfull;
-        while (pfull < P && tab.W[pfull] < dh) ++pfull;
-        plo = __builtin_amdgcn_readfirstlane(plo);
-        pfull = __builtin_amdgcn_readfirstlane(pfull);
+        plo = __builtin_popcountll(__ballot(Wl < dl));
+        pfull = __builtin_popcountll(__ballot(Wl < dh));
+    };
+    // Loads of the tile at k0 (band already moved there) through buffer descriptors
+    // whose extent holds only what is wanted: the K blocks below the band's first
+    // active one, the rows past the chunk's last key and a whole tile past the chunk
+    // get extent 0 and read as zero without touching memory.  So every tile issues the
+    // same loads, and those of the next tile can be in flight while this one computes.
+    // The caches are streamed once per step: non-temporal loads (a plain read runs
+    // markedly closer to the HBM peak with them).
+    auto kload = [&](int k0, u32x4 (&ka)[NB]) {
         const int jlo = plo >> 3;
-        const bool tail = k0 + 32 > c1;             // tile runs past the chunk's last key
-
-        // issue every load of the tile before using any: active K blocks (lane = key row
-        // arow, half h) and the V^T operands (lane = dim, half h = key octet); uniform
-        // 64-bit bases with 32-bit lane offsets.  The caches are streamed once per step:
-        // non-temporal loads (a plain read runs markedly closer to the HBM peak with them)
-        const int key = k0 + arow;
-        const int keyc = key < c1 ? key : c1 - 1;
-        u32x4 ka[NB];
+        const int nk = k0 < key_hi ? (key_hi - k0 < 32 ? key_hi - k0 : 32) : 0;
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
-            if (j < jlo) continue;
-            // row of this key in block j: the key itself, or in a ring block (one holding only
-            // the keys inside its largest window) key mod cap, without wrapping in the tile
+            // rows of this tile in block j: from the key itself, or in a ring block (one
+            // holding only the keys inside its largest window) from k0 mod cap; a tile
+            // never wraps (cap is a multiple of 32)
             const int cap = p.kl.cap[j];
             const int r0 = cap < p.Lmax ? (int)((uint32_t)k0 % (uint32_t)cap) : k0;
-            const int64_t koff = (p.kl.off[j] + r0) * 32 + (int64_t)((keyc - k0) * 32 + 16 * h);
-            ka[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbytes + koff));
+            const char* base = kbytes + (p.kl.off[j] + r0) * 32;
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<char*>(base), 0, j >= jlo ? nk * 32 : 0, kBufWord3);
+            ka[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, koffl, 0, kNT));
         }
-        u32x4 va[2][NDB];
+    };
+    // V^T operands of the tile at k0: lane = dim, half h = key octet; the octets past the
+    // cache's end read as zero
+    auto vload = [&](int k0, u32x4 (&va)[2][NDB]) {
         const int64_t oct0 = k0 >> 3;
+        const int64_t nob = k0 < key_hi ? (L8 - oct0 < 4 ? L8 - oct0 : 4) : 0;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<char*>(vbytes + oct0 * (D * 16)), 0, (int)nob * D * 16, kBufWord3);
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            // octet oct0 + 2c + h; the last octet of the cache stands in past its end
-            const int64_t ob = oct0 + 2 * c + 1 < L8 ? oct0 + 2 * c : L8 - 1 - h;
-            const char* vb = vbytes + ob * (D * 16);
+        for (int c = 0; c < 2; ++c)
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
-                va[c][db] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb + voff0 + db * 512));
-        }
+                va[c][db] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                    rs, voffl + (2 * c * D + 32 * db) * 16, 0, kNT));
+    };
 
-        // S^T over the active blocks; pairs not active for this lane's key are zeroed
+    int k0 = key_lo + 32 * w;
+    band(k0);
+    u32x4 ka[NB], va[2][NDB];
+    kload(k0, ka);
+    vload(k0, va);
+    while (k0 < key_hi) {
+        const int pl = plo, pf = pfull, jlo = pl >> 3;   // this tile's band
+        const bool tail = k0 + 32 > key_hi;          // tile runs past the chunk's last key
+        const int key = k0 + arow;
+
+        // S^T over the active blocks; pairs not active for this lane's key are zeroed.
+        // Pairs below pl are dead and pairs from pf on active for every key of the tile;
+        // the key's first active pair fa counts the straddling pairs whose window it
+        // leaves (windows grow with the pair index).
         const int64_t dist = qpos - key >= 0 ? qpos - key : key - qpos;
+        int fa = pl;
+        for (int e = pl; e < pf; ++e) fa += dist > (int64_t)__builtin_amdgcn_readlane(Wl, e) ? 1 : 0;
+        if (p.counter && h == 0 && key < key_hi) cnt += P - fa;
         f32x16 S = f32x16{};
 #pragma unroll
         for (int j = NB - 1; j >= 0; --j) {
             if (j < jlo) continue;
             u32x4 a = ka[j];
-            int on = 8;
-            if (8 * j < pfull) {                      // block holds a straddling pair
-                on = 0;
+            if (8 * j < pf) {                         // block holds a straddling pair
+                const int lead = fa - 8 * j;          // its pairs below fa are zeroed
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const bool e0 = dist <= (int64_t)tab.W[8 * j + 2 * t];
-                    const bool e1 = dist <= (int64_t)tab.W[8 * j + 2 * t + 1];
-                    on += e0 + e1;
-                    a[t] &= (e0 ? 0xffffu : 0u) | (e1 ? 0xffff0000u : 0u);
-                }
+                for (int t = 0; t < 4; ++t)
+                    a[t] &= (2 * t >= lead ? 0xffffu : 0u) | (2 * t + 1 >= lead ? 0xffff0000u : 0u);
             }
-            if (p.counter && h == 0 && key < c1) cnt += on;
             S = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                        __builtin_bit_cast(f16x8, qB[j]), S,
                                                        0, 0, 0);
         }
+        // the next tile's K, into the registers the MFMAs have just read
+        const int kn = k0 + 32 * kWaves;
+        band(kn);
+        kload(kn, ka);
 
         // register r of half h holds key k0 + 16(r/8) + 8h + (r%8) for column l32
         if (tail) {
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                if (k0 + 16 * (r >> 3) + 8 * h + (r & 7) >= c1) S[r] = -INFINITY;
+                if (k0 + 16 * (r >> 3) + 8 * h + (r & 7) >= key_hi) S[r] = -INFINITY;
         }
         float mx = S[0];
 #pragma unroll
@@ -216,20 +241,17 @@ void decode_partial_kernel(DecodeParams p, Tables tab) {
                     const int kb = k0 + 16 * c + 8 * h;
 #pragma unroll
                     for (int t = 0; t < 4; ++t)
-                        a[t] &= (kb + 2 * t < c1 ? 0xffffu : 0u) | (kb + 2 * t + 1 < c1 ? 0xffff0000u : 0u);
+                        a[t] &= (kb + 2 * t < key_hi ? 0xffffu : 0u) | (kb + 2 * t + 1 < key_hi ? 0xffff0000u : 0u);
                 }
                 O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, pb), O[db], 0, 0, 0);
             }
         }
+        // the next tile's V, into the registers the MFMAs have just read
+        vload(kn, va);
+        k0 = kn;
     }
 
-    if (p.counter) {
-        uint64_t tot = cnt;
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) tot += __shfl_xor(tot, o);
-        if (lane == 0 && tot) atomicAdd(p.counter, (unsigned long long)(tot * (uint64_t)G));
-    }
     // this wave's (O^T, m, l) for its columns (q heads) into LDS: lane = column l32,
     // register r of dim block db is dim 32db + 8(r/4) + 4h + (r%4)
     const float l_tot = lsum + xchg32(lsum, xaddr);
@@ -265,6 +287,12 @@ void decode_partial_kernel(DecodeParams p, Tables tab) {
             dst[hh * (D + 2) + D] = M;
             dst[hh * (D + 2) + D + 1] = ls;
         }
+    }
+    if (p.counter) {
+        uint64_t tot = cnt;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) tot += __shfl_xor(tot, o);
+        if (lane == 0 && tot) atomicAdd(p.counter, (unsigned long long)(tot * (uint64_t)G));
     }
 }
 

@@ -457,7 +457,8 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
         // window go back to zero.  Pair windows grow with the pair index, so an element
         // outside pair e's window is outside every earlier one's too and still holds zero:
         // the reset removes exactly pair e's term.  Then the causal mask.  Moves the band to
-        // this sub-tile (sub-tiles come nearest first, so distances only grow).
+        // this sub-tile (sub-tiles come nearest first, so distances only grow) on the first
+        // call for it (`count`), which also counts its kept terms.
         auto raw = [&](int sub, bool count) -> f32x16 {
             const int k0 = ks + 32 * sub;
             const uint16_t* ksub = kl + 32 * sub * 16;            // this lane's K row, this sub-tile
@@ -476,22 +477,26 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
                 });
                 return S;
             }
-            const int k_last = k0 + 31 < NK ? k0 + 31 : NK - 1;
-            const int dmin = pq_lo - POSL(k_last) > 0 ? pq_lo - POSL(k_last) : 0;
-            const int dmax = pq_hi - POSL(k0);
-            while (w_lo < dmin) {
-                ++plo;
-                w_lo = plo < P ? tab.W[plo] : INT32_MAX;
-            }
-            while (w_full < dmax) {
-                ++pfull;
-                w_full = pfull < P ? tab.W[pfull] : INT32_MAX;
+            if (count) {
+                // (a recomputation finds the band already at this sub-tile)
+                const int k_last = k0 + 31 < NK ? k0 + 31 : NK - 1;
+                const int dmin = pq_lo - POSL(k_last) > 0 ? pq_lo - POSL(k_last) : 0;
+                const int dmax = pq_hi - POSL(k0);
+                while (w_lo < dmin) {
+                    ++plo;
+                    w_lo = plo < P ? tab.W[plo] : INT32_MAX;
+                }
+                while (w_full < dmax) {
+                    ++pfull;
+                    w_full = pfull < P ? tab.W[pfull] : INT32_MAX;
+                }
+                const int jn = pfull >> 3;
+                if (pfull != q_key && jn < NB) {
+                    qm = Qf(jn) & lead_mask(pfull - 8 * jn);
+                    q_key = pfull;
+                }
             }
             const int jf = pfull >> 3;
-            if (pfull != q_key && jf < NB) {
-                qm = Qf(jf) & lead_mask(pfull - 8 * jf);
-                q_key = pfull;
-            }
             const bool diag = k0 + 31 > q0;
             // register r of half h holds key k0 + off(r) + 8h, off(r) = 16(r/8) + r%8:
             // causal iff off(r) <= lim
