@@ -288,7 +288,10 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
     int w_lo = tab.W[0], w_full = tab.W[0];  // W at the two edges (INT32_MAX past the end)
     // Block jf = pfull/8 of Q with its leading (not fully active) pairs zeroed, valid for
     // the band edge pfull == q_key; rebuilt only when that edge moves.
-    u32x4 qm = {0u, 0u, 0u, 0u};
+    // kept in LDS (one slot per lane of each compute wave), not in registers
+    __shared__ u32x4 sQm[Tile<D>::maxw(false) > Tile<D>::maxw(true) ? Tile<D>::maxw(false) : Tile<D>::maxw(true)][64];
+    auto set_qm = [&](u32x4 v) { sQm[w][lane] = v; };
+    auto qm = [&]() { return sQm[w][lane]; };
     int q_key = -1;
 
     // Stream key tile kt into `stage` with direct global->LDS loads (one wave instruction
@@ -442,7 +445,7 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
                 w_full = w_lo;                  // first pair active at dmax_t
                 const int jf = pfull >> 3;
                 if (pfull != q_key) {
-                    qm = Qf(jf) & lead_mask(pfull - 8 * jf);
+                    set_qm(Qf(jf) & lead_mask(pfull - 8 * jf));
                     q_key = pfull;
                 }
                 if (COUNT && row_ok) cnt += (uint64_t)(16 * NSUB) * (uint64_t)(P - pfull);
@@ -469,7 +472,7 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
                 dispatch<NB>(pfull >> 3, [&](auto jfc) {
                     constexpr int JF = decltype(jfc)::value;
                     f32x16 T = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                        K(JF), __builtin_bit_cast(f16x8, qm), f32x16{}, 0, 0, 0);
+                        K(JF), __builtin_bit_cast(f16x8, qm()), f32x16{}, 0, 0, 0);
 #pragma unroll
                     for (int j = JF + 1; j < NB; ++j)
                         T = __builtin_amdgcn_mfma_f32_32x32x16_f16(K(j), __builtin_bit_cast(f16x8, Qf(j)), T, 0, 0, 0);
@@ -492,7 +495,7 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
                 }
                 const int jn = pfull >> 3;
                 if (pfull != q_key && jn < NB) {
-                    qm = Qf(jn) & lead_mask(pfull - 8 * jn);
+                    set_qm(Qf(jn) & lead_mask(pfull - 8 * jn));
                     q_key = pfull;
                 }
             }
@@ -537,10 +540,10 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
                     for (int r = 0; r < 16; ++r)
                         if (16 * (r >> 3) + (r & 7) < t) T[r] = 0.f;
                 }
-                if (jf < NB) T = __builtin_amdgcn_mfma_f32_32x32x16_f16(K(jf), __builtin_bit_cast(f16x8, qm), T, 0, 0, 0);
+                if (jf < NB) T = __builtin_amdgcn_mfma_f32_32x32x16_f16(K(jf), __builtin_bit_cast(f16x8, qm()), T, 0, 0, 0);
                 S = upper(T);
             } else if (jf < NB) {
-                S = upper(__builtin_amdgcn_mfma_f32_32x32x16_f16(K(jf), __builtin_bit_cast(f16x8, qm), f32x16{}, 0, 0, 0));
+                S = upper(__builtin_amdgcn_mfma_f32_32x32x16_f16(K(jf), __builtin_bit_cast(f16x8, qm()), f32x16{}, 0, 0, 0));
             } else {
                 S = f32x16{};
             }
