@@ -303,9 +303,10 @@ def _traffic(kernel_file, workload, alpha):
 
 
 def _time(fn, reps):
-    """Mean ms of reps calls after one warm-up call (HIP events on the current stream)."""
+    """Mean ms of reps calls after three warm-up calls (HIP events on the current stream)."""
     import torch
-    fn()
+    for _ in range(3):
+        fn()
     torch.cuda.synchronize()
     a, b = _events(2)
     a.record()
@@ -316,21 +317,33 @@ def _time(fn, reps):
     return a.elapsed_time(b) / reps
 
 
-def _block_lists(B, H, N, density, seed):
-    """MInference-like block lists (64-token blocks): the first block, the two blocks below the
-    query block, and each earlier block with probability `density`; ascending."""
+def _block_lists(B, H, N, density, seed, pattern="random"):
+    """Block lists of 64-token blocks, ascending: the first block and the two blocks below the
+    query block, plus
+      random          each earlier block with probability `density`, drawn anew for every
+                      (head, query block);
+      vertical_slash  per head, a fixed set of key blocks ("vertical" columns, each block with
+                      probability `density`) and 4 fixed diagonal offsets in [3, 64) ("slash"
+                      lines), the same for every query block of the head: the shape of
+                      MInference's vertical-slash index."""
     import numpy as np
     import torch
     rng = np.random.default_rng(seed)
     nblk = (N + 63) // 64
-    width = max(3, int(density * nblk) + 8)
+    width = max(3, int(density * nblk) + 16)
     count = np.zeros((B, H, nblk), np.int32)
     idx = np.zeros((B, H, nblk, width), np.int32)
     for b in range(B):
         for h in range(H):
+            if pattern == "vertical_slash":
+                vert = np.nonzero(rng.random(nblk) < density)[0]
+                slash = rng.integers(3, 64, size=4)
             for R in range(nblk):
-                s = {0, R - 1, R - 2} | set(np.nonzero(rng.random(R) < density)[0].tolist())
-                s = sorted(c for c in s if 0 <= c < R)[-width:]
+                if pattern == "random":
+                    extra = np.nonzero(rng.random(R) < density)[0].tolist()
+                else:
+                    extra = vert[vert < R].tolist() + [R - int(o) for o in slash]
+                s = sorted(c for c in {0, R - 1, R - 2} | set(extra) if 0 <= c < R)[-width:]
                 count[b, h, R] = len(s)
                 idx[b, h, R, :len(s)] = s
     return torch.from_numpy(count).cuda(), torch.from_numpy(idx).cuda()
@@ -385,9 +398,11 @@ def extras(reps):
 
     # block-sparse prefill on top of the window
     sp = {"workload": "qwen05b prefill (prepare + attend), alpha 1, 64-token blocks: first block, "
-                      "two local blocks and random earlier blocks"}
-    for dens in (0.3, 0.1):
-        bc, bi = _block_lists(w.B, w.Hq, w.N, dens, 5)
+                      "two local blocks and earlier blocks, random per (head, query block) or "
+                      "vertical-slash per head"}
+    for pattern, dens in (("random", 0.3), ("random", 0.1), ("vertical_slash", 0.3),
+                          ("vertical_slash", 0.1)):
+        bc, bi = _block_lists(w.B, w.Hq, w.N, dens, 5, pattern)
         t = _time(lambda: wpa.prefill(q, k, v, w.base, 1.0, workspace=ws, block_count=bc,
                                       block_idx=bi), reps)
         cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
@@ -400,8 +415,10 @@ def extras(reps):
             # keys visited by the rows of block R: own block (causal) + listed blocks
             vis += int(cnt_h[:, :, R].sum()) * 64 * 64 + w.B * w.Hq * (64 * 65 // 2)
         flops = 4 * int(cnt.item()) + 2 * w.d * vis
-        sp["density_%g" % dens] = {"ms": t, "vs_dense_window": t / t_one,
-                                   "active_tflops": flops / (t * 1e-3) / 1e12}
+        listed = float(bc.double().mean().item()) / ((w.N + 63) // 64 / 2)
+        sp["%s_%g" % (pattern, dens)] = {"ms": t, "vs_dense_window": t / t_one,
+                                         "listed_fraction": listed,
+                                         "active_tflops": flops / (t * 1e-3) / 1e12}
         del bc, bi
     res["block_sparse_prefill"] = sp
     _log("extras: block sparse %s" % sp)
@@ -451,7 +468,7 @@ def main():
         print(json.dumps(sweep(args.sweep_max)), flush=True)
         return
     if args.extras:
-        print(json.dumps({"extras": extras(max(3, args.steps // 4))}), flush=True)
+        print(json.dumps({"extras": extras(max(5, args.steps // 2))}), flush=True)
         return
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib << 20

@@ -39,6 +39,7 @@
 //   V operand (A of the P*V step): V^T rows (dims) from LDS, key-contiguous, 16-byte
 //     chunks XOR-swizzled by the row index against bank conflicts.
 //   O^T accumulator: lane = query row, so the softmax rescale is a per-lane scalar.
+#include <atomic>
 #include <type_traits>
 
 #include "wpa_device.hpp"
@@ -743,16 +744,60 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
         p.lse[((int64_t)b * p.Hq + hq) * NQ + qi] = (m + log2f(l_tot)) * 0.6931471805599453f;
 }
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+    static std::atomic<int> cus[64];
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    if (dev >= 0 && dev < 64) n = cus[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        if (dev >= 0 && dev < 64) cus[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 template <int D, bool F32>
 hipError_t launch_d(const PrefillParams& p, const Tables& t, hipStream_t s) {
     const int G = p.Hq / p.Hkv;
     const int MAXW = Tile<D>::maxw(p.pos != nullptr);
     Launch L;
-    L.nhc = (G + MAXW - 1) / MAXW;                  // head chunks, as even as possible
-    L.Gc = (G + L.nhc - 1) / L.nhc;
-    L.R = MAXW / L.Gc > 1 ? MAXW / L.Gc : 1;
+    if (p.blk_count) {
+        // Block-sparse: a workgroup takes consecutive row groups of one q head.  Its waves'
+        // lists are then one head's pattern at neighbouring query blocks, which share most
+        // of their key blocks (vertical columns, nearby diagonals), so the union of tiles the
+        // workgroup streams stays close to one list; grouped by heads, the union of several
+        // heads' unrelated lists would approach the dense set.  (Measured on the Qwen-0.5B
+        // shape: vertical-slash lists with 13% of the blocks, 0.36x the dense time against
+        // 0.55x grouped by heads; random lists with 11%, 0.48x against 0.54x.)  The q heads
+        // of a kv head then read the shared K/V tiles separately.
+        L.nhc = G;
+        L.Gc = 1;
+        L.R = MAXW;
+    } else {
+        L.nhc = (G + MAXW - 1) / MAXW;              // head chunks, as even as possible
+        L.Gc = (G + L.nhc - 1) / L.nhc;
+        L.R = MAXW / L.Gc > 1 ? MAXW / L.Gc : 1;
+    }
     // row blocks per sequence (cached: up to 31 extra rows from aligning the first group)
     const int64_t rows = p.kv_len ? (int64_t)p.Nq + 31 : p.N;
+    if (!p.blk_count) {
+        // Few rows (a short prompt, a prefill chunk): fewer row groups per workgroup, then the
+        // q heads of a kv head over more workgroups, until about two workgroups per CU (the
+        // resident count) are launched.  Each split re-reads the kv head's K/V tiles.
+        const int64_t target = 2 * (int64_t)device_cus();
+        auto wgs = [&](int R, int nhc) { return (rows + 32 * R - 1) / (32 * R) * p.B * p.Hkv * nhc; };
+        if (wgs(L.R, L.nhc) < target) {
+            L.R = 1;
+            if (wgs(1, L.nhc) < target) {
+                int nhc = (int)((target + wgs(1, 1) - 1) / wgs(1, 1));
+                nhc = nhc < G ? nhc : G;
+                L.Gc = (G + nhc - 1) / nhc;
+                L.nhc = (G + L.Gc - 1) / L.Gc;
+            }
+        }
+    }
     L.n_rb = (int)((rows + 32 * L.R - 1) / (32 * L.R));
     const int waves = L.Gc * L.R + 1;               // + the producer wave
     const int64_t nblk = (int64_t)L.n_rb * p.B * p.Hkv * L.nhc;
