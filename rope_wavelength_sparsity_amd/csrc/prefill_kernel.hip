@@ -276,13 +276,23 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
     bool started = false;
     const u32x4 ones_blk = h ? u32x4{0u, 0u, 0u, 0u} : u32x4{0x68003c00u, 0u, 0u, 0u};   // (1, 2048)
     u32x4 negm_blk = {0u, 0u, 0u, 0u};
+    // At d=64, when the chain's first block has zeroed leading pairs, the -m step rides in it
+    // instead: slot 0 of that block (pair 8jf: its first dim in half 0, its second in half 1)
+    // holds 2048 resp. 1 in the K operand and -hi resp. -lo in the Q operand (the pair's own
+    // term is then not in this MFMA, which it must not be anyway).  One MFMA less per sub-tile
+    // for two VALU operations: 2.6% faster at d=64, 1.9% slower at d=128 (where the MFMA
+    // stream dominates less), so d=128 keeps the separate step.
+    constexpr bool FOLD = D == 64;
+    const uint32_t kfold = h ? 0x3c00u : 0x6800u;            // 1, 2048 (half)
+    uint32_t qfold = 0u;                                      // -lo, -hi (half)
     auto set_m = [&](float mv) {
         const _Float16 hi = (_Float16)(mv * (1.0f / 2048.0f));
         const _Float16 lo = (_Float16)(mv - 2048.0f * (float)hi);
         m = 2048.0f * (float)hi + (float)lo;
-        const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)-lo) |
-                            ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)-hi) << 16);
-        negm_blk[0] = h ? 0u : w0;
+        const uint32_t nlo = __builtin_bit_cast(uint16_t, (_Float16)-lo);
+        const uint32_t nhi = __builtin_bit_cast(uint16_t, (_Float16)-hi);
+        negm_blk[0] = h ? 0u : (nlo | (nhi << 16));
+        qfold = h ? nlo : nhi;
     };
     uint64_t cnt = 0;
     int plo = 0, pfull = 0, plo_wg = 0;     // running band edges (distances only grow)
@@ -468,12 +478,22 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
             const uint16_t* ksub = kl + 32 * sub * 16;            // this lane's K row, this sub-tile
             auto K = [&](int j) { return *reinterpret_cast<const f16x8*>(ksub + j * BN * 16); };
             f32x16 S;
+            // the first active block's operands, with the -m step folded in when it can be
+            auto first = [&](int j, f32x16 acc) {
+                if constexpr (!FOLD)
+                    return __builtin_amdgcn_mfma_f32_32x32x16_f16(K(j), __builtin_bit_cast(f16x8, qm()), acc, 0, 0, 0);
+                const uint32_t fm = (pfull & 7) ? 0xffffu : 0u;
+                u32x4 kj = __builtin_bit_cast(u32x4, K(j)), qj = qm();
+                kj[0] = (kj[0] & ~fm) | (kfold & fm);
+                qj[0] = (qj[0] & ~fm) | (qfold & fm);
+                return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, kj),
+                                                              __builtin_bit_cast(f16x8, qj), acc, 0, 0, 0);
+            };
             if (plain) {
                 // the tile's block set, unrolled for each first block
                 dispatch<NB>(pfull >> 3, [&](auto jfc) {
                     constexpr int JF = decltype(jfc)::value;
-                    f32x16 T = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                        K(JF), __builtin_bit_cast(f16x8, qm()), f32x16{}, 0, 0, 0);
+                    f32x16 T = first(JF, f32x16{});
 #pragma unroll
                     for (int j = JF + 1; j < NB; ++j)
                         T = __builtin_amdgcn_mfma_f32_32x32x16_f16(K(j), __builtin_bit_cast(f16x8, Qf(j)), T, 0, 0, 0);
@@ -541,10 +561,10 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
                     for (int r = 0; r < 16; ++r)
                         if (16 * (r >> 3) + (r & 7) < t) T[r] = 0.f;
                 }
-                if (jf < NB) T = __builtin_amdgcn_mfma_f32_32x32x16_f16(K(jf), __builtin_bit_cast(f16x8, qm()), T, 0, 0, 0);
+                if (jf < NB) T = first(jf, T);
                 S = upper(T);
             } else if (jf < NB) {
-                S = upper(__builtin_amdgcn_mfma_f32_32x32x16_f16(K(jf), __builtin_bit_cast(f16x8, qm()), f32x16{}, 0, 0, 0));
+                S = upper(first(jf, f32x16{}));
             } else {
                 S = f32x16{};
             }
@@ -616,7 +636,11 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
         while (true) {
             sub = uniform(sub);      // (merged from two branches it would otherwise live in a VGPR)
             const f32x16 T = raw(sub, true);
-            f32x16 S = bias(T);
+            // the -m step, unless the chain's first block carried it
+            const bool folded = FOLD && (pfull & 7) != 0 && (pfull >> 3) < NB;
+            f32x16 S;
+            if (folded) S = T;
+            else S = bias(T);
             uint32_t wd[8];
             float psum = 0.f;
             bool redo = !started;
@@ -625,7 +649,8 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
                 redo = __any(psum > kSumTau);
             }
             if (redo) {
-                f32x16 R = bias(raw(sub, false));
+                f32x16 R = raw(sub, false);
+                if (!folded) R = bias(R);
                 remax(R);
                 psum = probs(R, wd);
             }
