@@ -300,6 +300,46 @@ int wpa_decode_window(const void* q, const void* k_cache, const void* v_cache,
                       int32_t out_dtype, unsigned long long* term_count, int32_t chunk_keys,
                       void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * Paged decode caches (serving with a block table: the ragged-batch path around the decode
+ * step; ATFlash abstract: the window ported into a serving decode kernel).  Keys and values
+ * live in a pool of pages of page_size tokens each; the token range [i*page_size,
+ * (i+1)*page_size) of sequence b is page block_table[b*max_pages + i] of the pool.  The
+ * arithmetic is that of the contiguous caches (same rotation, same layouts inside a page):
+ * a step on a paged cache gives bit-identical results to the same step on a contiguous cache
+ * holding the same tokens with Lmax = max_pages * page_size.
+ *   page_size    a power of two in [32, 65536] (a 32-token tile never straddles pages);
+ *                max_pages * page_size < 2^31.
+ *   k_pool, v_pool  num_pages pages of wpa_kv_page_bytes(Hkv, d, page_size) bytes each,
+ *                16-byte aligned.  K page: [Hkv][d/16][page_size][16] IEEE half (rotated,
+ *                pair-blocked); V page: [Hkv][page_size/8][d][8] bf16.  Caller-owned.
+ *   block_table  int32 device [B][max_pages], entries in [0, num_pages) for every page a
+ *                sequence's tokens reach (others are not read).  Entries outside that range
+ *                break the contract; the kernels clamp them so that no access leaves the pool.
+ *                Pages may be shared or reused by the caller as it sees fit: writes go where
+ *                the table says.
+ *   wpa_kv_page_bytes   bytes of one K page (one V page has the same size); 0 for invalid
+ *                arguments (d not 64 or 128, page_size not a power of two in range).
+ *   wpa_kv_write_paged  as wpa_kv_write_ex for tokens start .. start+n-1 of every sequence
+ *                (start + n <= max_pages * page_size); a partly written V octet keeps its
+ *                other tokens.  For one sequence, pass B = 1 and its block-table row.
+ *   wpa_decode_paged    as wpa_decode_ex on the pools; kv_len[b] in [1, max_pages*page_size]
+ *                (larger values are clamped to it).  Workspace:
+ *                wpa_decode_workspace_bytes(B, max_pages*page_size, Hq, Hkv, d, chunk_keys).
+ */
+size_t wpa_kv_page_bytes(int32_t Hkv, int32_t d, int32_t page_size);
+int wpa_kv_write_paged(const void* k, const void* v, int64_t start, int64_t n, void* k_pool,
+                       void* v_pool, const int32_t* block_table, int32_t num_pages, int32_t B,
+                       int32_t max_pages, int32_t page_size, int32_t Hkv, int32_t d, double base,
+                       const wpa_rope_t* rope, int32_t dtype, void* stream);
+int wpa_decode_paged(const void* q, const void* k_pool, const void* v_pool,
+                     const int32_t* block_table, int32_t num_pages, const int32_t* kv_len,
+                     const int32_t* q_pos, void* out, float* lse, int32_t B, int32_t max_pages,
+                     int32_t page_size, int32_t Hq, int32_t Hkv, int32_t d, double base,
+                     const wpa_rope_t* rope, double alpha, float scale, int32_t dtype,
+                     int32_t out_dtype, unsigned long long* term_count, int32_t chunk_keys,
+                     void* workspace, size_t ws_bytes, void* stream);
+
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char* wpa_last_error(void);
 

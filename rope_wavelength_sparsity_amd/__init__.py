@@ -39,7 +39,8 @@ EXPORTS = ("wpa_count_terms", "wpa_thresholds", "wpa_prefill_workspace_bytes", "
            "wpa_kv_write", "wpa_decode_workspace_bytes", "wpa_decode", "wpa_count_terms_ex",
            "wpa_thresholds_ex", "wpa_prefill_ex", "wpa_prefill_prepare_ex", "wpa_prefill_attend_ex",
            "wpa_kv_write_ex", "wpa_decode_ex", "wpa_prefill_cached", "wpa_kcache_window_bytes",
-           "wpa_kv_write_window", "wpa_decode_window", "wpa_prefill_sparse", "wpa_last_error")
+           "wpa_kv_write_window", "wpa_decode_window", "wpa_prefill_sparse", "wpa_kv_page_bytes",
+           "wpa_kv_write_paged", "wpa_decode_paged", "wpa_last_error")
 
 
 class Rope(ctypes.Structure):
@@ -156,6 +157,14 @@ def lib():
     L.wpa_prefill_sparse.argtypes = [P, P, P, P, P, P, P, I32, I32, I64, I32, I32, I32, D, P, D, F,
                                      I32, I32, P, P, SZ, P]
     L.wpa_prefill_sparse.restype = ctypes.c_int
+    L.wpa_kv_page_bytes.argtypes = [I32, I32, I32]
+    L.wpa_kv_page_bytes.restype = SZ
+    L.wpa_kv_write_paged.argtypes = [P, P, I64, I64, P, P, P, I32, I32, I32, I32, I32, I32, D, P,
+                                     I32, P]
+    L.wpa_kv_write_paged.restype = ctypes.c_int
+    L.wpa_decode_paged.argtypes = [P, P, P, P, I32, P, P, P, P, I32, I32, I32, I32, I32, I32, D, P,
+                                   D, F, I32, I32, P, I32, P, SZ, P]
+    L.wpa_decode_paged.restype = ctypes.c_int
     L.wpa_last_error.argtypes = []
     L.wpa_last_error.restype = ctypes.c_char_p
     _lib = L
@@ -397,14 +406,67 @@ class KVCache:
         return v.permute(0, 1, 2, 4, 3).reshape(self.B, self.Hkv, L8 * 8, self.d)[:, :, :self.Lmax]
 
 
-def decode(q, cache: KVCache, kv_len, alpha: float, *, q_pos=None, scale: float | None = None,
+class PagedKVCache:
+    """Decode caches as a pool of `num_pages` pages of `page_size` tokens (all Hkv kv heads of
+    a page together); a block table int32 device [B][max_pages] maps token range
+    [i*page_size, (i+1)*page_size) of sequence b to page table[b][i].  The table is the
+    caller's: `block_table` here is only a convenience default (set it or pass one per call)."""
+
+    def __init__(self, num_pages, page_size, Hkv, d, base, device="cuda", *, inv_freq=None,
+                 pairs="half", block_table=None):
+        self.num_pages, self.page_size, self.Hkv, self.d = num_pages, page_size, Hkv, d
+        self.base = float(base)
+        self.inv_freq = None if inv_freq is None else np.asarray(inv_freq, dtype=np.float64).copy()
+        self.pairs = pairs
+        _rope(d, self.inv_freq, pairs)                   # validates the description
+        self.page_bytes = lib().wpa_kv_page_bytes(Hkv, d, page_size)
+        if self.page_bytes == 0:
+            raise ValueError("invalid page arguments (d 64 or 128, page_size a power of two >= 32)")
+        self.k = torch.empty(num_pages * self.page_bytes, device=device, dtype=torch.uint8)
+        self.v = torch.empty(num_pages * self.page_bytes, device=device, dtype=torch.uint8)
+        self.window_alpha = None
+        self.block_table = block_table
+
+    def _table(self, block_table):
+        t = self.block_table if block_table is None else block_table
+        if t is None:
+            raise ValueError("no block table")
+        _dev(t, "block_table")
+        if t.dtype != torch.int32 or t.dim() != 2 or not t.is_contiguous():
+            raise ValueError("block_table must be a contiguous int32 [B][max_pages] tensor")
+        return t
+
+    def write(self, k, v, start: int, block_table=None, stream=None):
+        """Append pre-RoPE k, v [B][n][Hkv][d] at token indices start .. start+n-1 of the B
+        sequences whose block-table rows are given (one sequence: its row, as [1][max_pages])."""
+        _dev(k, "k")
+        _dev(v, "v")
+        t = self._table(block_table)
+        if k.shape != v.shape or k.dim() != 4 or k.shape[0] != t.shape[0] or \
+                k.shape[2] != self.Hkv or k.shape[3] != self.d or k.dtype != v.dtype:
+            raise ValueError("k, v must be [B][n][Hkv][d] of one dtype, B = block_table rows")
+        rope, keep = _rope(self.d, self.inv_freq, self.pairs)
+        _check(lib().wpa_kv_write_paged(_ptr(k), _ptr(v), int(start), k.shape[1], _ptr(self.k),
+                                        _ptr(self.v), _ptr(t), self.num_pages, t.shape[0],
+                                        t.shape[1], self.page_size, self.Hkv, self.d, self.base,
+                                        rope, _dtype_code(k), _stream(stream)))
+
+
+def decode(q, cache, kv_len, alpha: float, *, q_pos=None, scale: float | None = None,
            out=None, out_dtype=None, lse=None, want_lse: bool = False, term_count=None,
-           chunk_keys: int = 0, workspace=None, stream=None):
-    """One decode step.  q [B][Hq][d] pre-RoPE; kv_len int32 device [B]."""
+           chunk_keys: int = 0, workspace=None, stream=None, block_table=None):
+    """One decode step.  q [B][Hq][d] pre-RoPE; kv_len int32 device [B]; `cache` a KVCache or
+    a PagedKVCache (with `block_table` [B][max_pages], or the cache's default table)."""
     _dev(q, "q")
     _dev(kv_len, "kv_len")
     B, Hq, d = q.shape
-    if B != cache.B or d != cache.d or kv_len.dtype != torch.int32 or kv_len.numel() != B:
+    paged = isinstance(cache, PagedKVCache)
+    if paged:
+        table = cache._table(block_table)
+        nseq, lmax = table.shape[0], table.shape[1] * cache.page_size
+    else:
+        nseq, lmax = cache.B, cache.Lmax
+    if B != nseq or d != cache.d or kv_len.dtype != torch.int32 or kv_len.numel() != B:
         raise ValueError("q [B][Hq][d] and kv_len int32 [B] must match the cache")
     if q_pos is not None:
         _dev(q_pos, "q_pos")
@@ -415,10 +477,20 @@ def decode(q, cache: KVCache, kv_len, alpha: float, *, q_pos=None, scale: float 
     _dev(out, "out")
     if want_lse and lse is None:
         lse = torch.empty((B, Hq), device=q.device, dtype=torch.float32)
-    need = decode_workspace_bytes(B, cache.Lmax, Hq, cache.Hkv, d, chunk_keys)
+    need = decode_workspace_bytes(B, lmax, Hq, cache.Hkv, d, chunk_keys)
     if workspace is None:
         workspace = torch.empty(max(need, 16), device=q.device, dtype=torch.uint8)
     rope, keep = _rope(d, cache.inv_freq, cache.pairs)
+    if paged:
+        _check(lib().wpa_decode_paged(_ptr(q), _ptr(cache.k), _ptr(cache.v), _ptr(table),
+                                      cache.num_pages, _ptr(kv_len), _ptr(q_pos), _ptr(out),
+                                      _ptr(lse), B, table.shape[1], cache.page_size, Hq,
+                                      cache.Hkv, d, cache.base, rope, float(alpha),
+                                      float(scale) if scale is not None else 0.0,
+                                      _dtype_code(q), _dtype_code(out), _ptr(term_count),
+                                      int(chunk_keys), _ptr(workspace), workspace.numel(),
+                                      _stream(stream)))
+        return (out, lse) if lse is not None else out
     if cache.window_alpha is not None:
         if q_pos is not None:
             raise ValueError("a windowed cache decodes at the newest token (q_pos must be None)")
@@ -444,6 +516,8 @@ def prefill_cached(q, cache: KVCache, kv_len, alpha: float, *, scale: float | No
                    stream=None):
     """Chunked prefill: q [B][Nq][Hq][d] pre-RoPE holds the last Nq tokens of each sequence,
     whose keys and values are already in `cache`; kv_len int32 device [B], each >= Nq."""
+    if isinstance(cache, PagedKVCache):
+        raise ValueError("chunked prefill reads contiguous caches (KVCache)")
     _dev(q, "q")
     _dev(kv_len, "kv_len")
     B, Nq, Hq, d = q.shape

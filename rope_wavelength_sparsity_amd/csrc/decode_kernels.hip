@@ -40,7 +40,7 @@ __device__ inline float xchg32(float v, int xaddr) {
     return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(xaddr, __builtin_bit_cast(int, v)));
 }
 
-template <int D>
+template <int D, bool PAGED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_partial_kernel(DecodeParams p, Tables tab) {
     constexpr int NB = D / 16;
@@ -57,7 +57,8 @@ void decode_partial_kernel(DecodeParams p, Tables tab) {
     const int chunk = blockIdx.x % p.n_chunks;
     const int bg = blockIdx.x / p.n_chunks;
     const int g = bg % p.Hkv, b = bg / p.Hkv;
-    const int Lb = __builtin_amdgcn_readfirstlane(p.kv_len[b]);
+    int Lb = __builtin_amdgcn_readfirstlane(p.kv_len[b]);
+    if constexpr (PAGED) Lb = Lb < p.Lmax ? Lb : (int)p.Lmax;   // the table's reach
     const int key_lo = chunk * p.chunk;
     if (key_lo >= Lb) return;
     const int key_hi = key_lo + p.chunk < Lb ? key_lo + p.chunk : Lb;
@@ -98,9 +99,10 @@ void decode_partial_kernel(DecodeParams p, Tables tab) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) qB[j] = *reinterpret_cast<const u32x4*>(&sQ[l32][16 * j + 8 * h]);
 
-    const uint16_t* kpg = p.kp + ((int64_t)b * p.Hkv + g) * p.kl.head * 16;
+    // (paged: the pools; a tile's page is looked up per tile)
+    const uint16_t* kpg = PAGED ? p.kp : p.kp + ((int64_t)b * p.Hkv + g) * p.kl.head * 16;
     const int64_t L8 = (p.Lmax + 7) / 8;
-    const uint16_t* vg = p.v + ((int64_t)b * p.Hkv + g) * L8 * D * 8;
+    const uint16_t* vg = PAGED ? p.v : p.v + ((int64_t)b * p.Hkv + g) * L8 * D * 8;
 
     f32x16 O[NDB];
 #pragma unroll
@@ -136,9 +138,27 @@ void decode_partial_kernel(DecodeParams p, Tables tab) {
     // same loads, and those of the next tile can be in flight while this one computes.
     // The caches are streamed once per step: non-temporal loads (a plain read runs
     // markedly closer to the HBM peak with them).
-    auto kload = [&](int k0, u32x4 (&ka)[NB]) {
+    // page of the tile at k0 (paged caches; 0 past the chunk, where nothing is read)
+    auto tile_page = [&](int k0) -> int64_t {
+        if constexpr (PAGED) return k0 < key_hi ? page_of(p.pg, b, k0) : 0;
+        else return 0;
+    };
+    auto kload = [&](int k0, int64_t page, u32x4 (&ka)[NB]) {
         const int jlo = plo >> 3;
         const int nk = k0 < key_hi ? (key_hi - k0 < 32 ? key_hi - k0 : 32) : 0;
+        if constexpr (PAGED) {
+            // rows k0 mod page .. +31 of block j of (page, kv head g)
+            const int ps = 1 << p.pg.page_log2;
+            const int64_t row0 = (page * p.Hkv + g) * NB * ps + (k0 & (ps - 1));
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                const char* base = kbytes + (row0 + (int64_t)j * ps) * 32;
+                const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                    const_cast<char*>(base), 0, j >= jlo ? nk * 32 : 0, kBufWord3);
+                ka[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, koffl, 0, kNT));
+            }
+            return;
+        }
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
             // rows of this tile in block j: from the key itself, or in a ring block (one
@@ -154,9 +174,14 @@ void decode_partial_kernel(DecodeParams p, Tables tab) {
     };
     // V^T operands of the tile at k0: lane = dim, half h = key octet; the octets past the
     // cache's end read as zero
-    auto vload = [&](int k0, u32x4 (&va)[2][NDB]) {
-        const int64_t oct0 = k0 >> 3;
-        const int64_t nob = k0 < key_hi ? (L8 - oct0 < 4 ? L8 - oct0 : 4) : 0;
+    auto vload = [&](int k0, int64_t page, u32x4 (&va)[2][NDB]) {
+        int64_t oct0 = k0 >> 3, nob = k0 < key_hi ? (L8 - oct0 < 4 ? L8 - oct0 : 4) : 0;
+        if constexpr (PAGED) {
+            // octet (k0 mod page)/8 of (page, kv head g); a tile never leaves its page
+            const int o_pg = 1 << (p.pg.page_log2 - 3);
+            oct0 = (page * p.Hkv + g) * o_pg + ((k0 >> 3) & (o_pg - 1));
+            nob = k0 < key_hi ? 4 : 0;
+        }
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<char*>(vbytes + oct0 * (D * 16)), 0, (int)nob * D * 16, kBufWord3);
 #pragma unroll
@@ -170,8 +195,9 @@ void decode_partial_kernel(DecodeParams p, Tables tab) {
     int k0 = key_lo + 32 * w;
     band(k0);
     u32x4 ka[NB], va[2][NDB];
-    kload(k0, ka);
-    vload(k0, va);
+    int64_t page = tile_page(k0);
+    kload(k0, page, ka);
+    vload(k0, page, va);
     while (k0 < key_hi) {
         const int pl = plo, pf = pfull, jlo = pl >> 3;   // this tile's band
         const bool tail = k0 + 32 > key_hi;          // tile runs past the chunk's last key
@@ -203,7 +229,8 @@ void decode_partial_kernel(DecodeParams p, Tables tab) {
         // the next tile's K, into the registers the MFMAs have just read
         const int kn = k0 + 32 * kWaves;
         band(kn);
-        kload(kn, ka);
+        page = tile_page(kn);
+        kload(kn, page, ka);
 
         // register r of half h holds key k0 + 16(r/8) + 8h + (r%8) for column l32
         if (tail) {
@@ -248,7 +275,7 @@ void decode_partial_kernel(DecodeParams p, Tables tab) {
             }
         }
         // the next tile's V, into the registers the MFMAs have just read
-        vload(kn, va);
+        vload(kn, page, va);
         k0 = kn;
     }
 
@@ -354,7 +381,8 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
 template <int D>
 hipError_t launch_decode_d(const DecodeParams& p, const Tables& t, hipStream_t s) {
     dim3 grid((unsigned)((int64_t)p.n_chunks * p.B * p.Hkv)), block(64 * kWaves);
-    decode_partial_kernel<D><<<grid, block, 0, s>>>(p, t);
+    if (p.pg.table) decode_partial_kernel<D, true><<<grid, block, 0, s>>>(p, t);
+    else decode_partial_kernel<D, false><<<grid, block, 0, s>>>(p, t);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     dim3 grid2((unsigned)(p.B * p.Hq), D / 32), block2(256);

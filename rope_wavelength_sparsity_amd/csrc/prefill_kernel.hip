@@ -632,9 +632,12 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
         // sub-tile that fails the vote recomputes its scores (the band still sits at it).  (Issuing
         // the next sub-tile's chain before this one's softmax cost the d=64 kernel 12 spilled
         // registers and 3%.)
+        // the sub-tile index as top - i with a loop counter i: both scalar (a decremented index
+        // merged from the two ways of computing its start lived in a vector register)
+        const int sub_top = uniform(sub), n_sub = uniform(sub - sub_lo + 1);
 #pragma unroll 1
-        while (true) {
-            sub = uniform(sub);      // (merged from two branches it would otherwise live in a VGPR)
+        for (int i = 0; i < n_sub; ++i) {
+            sub = sub_top - i;
             const f32x16 T = raw(sub, true);
             // the -m step, unless the chain's first block carried it
             const bool folded = FOLD && (pfull & 7) != 0 && (pfull >> 3) < NB;
@@ -656,8 +659,6 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
             }
             lsum += psum;
             pv(sub, ks + 32 * sub, wd, sV);
-            if (sub == sub_lo) break;
-            --sub;
         }
     };
 

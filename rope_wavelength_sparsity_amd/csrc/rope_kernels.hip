@@ -46,12 +46,20 @@ __global__ __launch_bounds__(256) void rope_keys_kernel(RopeParams p, Tables tab
             cap = p.kl.cap[jj];
         }
     const int64_t tok = p.t0 + t;
-    int64_t krow = tok;
-    if (cap < p.ld) {
-        if (tok + cap < p.t0 + p.n) return;
-        krow = tok % cap;
+    uint16_t* dst;
+    if (p.pg.table) {
+        // paged: row tok mod page of block j of the page holding tok
+        const int64_t page = page_of(p.pg, b, tok);
+        const int64_t ps = (int64_t)1 << p.pg.page_log2;
+        dst = p.kp + (((page * p.Hkv + g) * NB + j) * ps + (tok & (ps - 1))) * 16;
+    } else {
+        int64_t krow = tok;
+        if (cap < p.ld) {
+            if (tok + cap < p.t0 + p.n) return;
+            krow = tok % cap;
+        }
+        dst = p.kp + (((int64_t)b * p.Hkv + g) * p.kl.head + off + krow) * 16;
     }
-    uint16_t* dst = p.kp + (((int64_t)b * p.Hkv + g) * p.kl.head + off + krow) * 16;
     u32x4* d4 = reinterpret_cast<u32x4*>(dst);
     if (t >= p.n) {
         u32x4 z = {0u, 0u, 0u, 0u};
@@ -151,8 +159,16 @@ __global__ __launch_bounds__(256) void v_cache_kernel(RopeParams p) {
     rest /= n_oct;
     const int g = (int)(rest % p.Hkv);
     const int b = (int)(rest / p.Hkv);
-    const int64_t L8 = (p.ld + 7) / 8;
-    uint16_t* dst = p.vout + ((((int64_t)b * p.Hkv + g) * L8 + o) * p.d + e8) * 8;
+    uint16_t* dst;
+    if (p.pg.table) {
+        // paged: octet (8o mod page)/8 of the page holding token 8o
+        const int64_t page = page_of(p.pg, b, 8 * o);
+        const int64_t o_pg = (int64_t)1 << (p.pg.page_log2 - 3);        // octets per page
+        dst = p.vout + (((page * p.Hkv + g) * o_pg + (o & (o_pg - 1))) * p.d + e8) * 8;
+    } else {
+        const int64_t L8 = (p.ld + 7) / 8;
+        dst = p.vout + ((((int64_t)b * p.Hkv + g) * L8 + o) * p.d + e8) * 8;
+    }
     uint16_t cell[8][8];                 // [dim][token in octet]
     const bool partial = o * 8 < p.t0 || o * 8 + 8 > p.t0 + p.n;
     if (partial) {

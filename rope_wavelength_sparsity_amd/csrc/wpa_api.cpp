@@ -443,7 +443,8 @@ namespace {
 
 int kv_write_impl(const void* k, const void* v, int64_t start, int64_t n, void* k_cache,
                   void* v_cache, int32_t B, int64_t Lmax, int32_t Hkv, int32_t d, double base,
-                  const wpa_rope_t* rope, const wpa::KLayout& kl, int32_t dtype, void* stream) {
+                  const wpa_rope_t* rope, const wpa::KLayout& kl, int32_t dtype, void* stream,
+                  const wpa::Paging& pg = wpa::Paging{}) {
     if (B < 1 || Hkv < 1 || Lmax < 1 || n < 1 || start < 0 || start + n > Lmax)
         return fail(WPA_ERR_INVALID, "need B, Hkv, n >= 1 and 0 <= start, start + n <= Lmax");
     if (Lmax >= (int64_t)INT32_MAX) return fail(WPA_ERR_INVALID, "Lmax too large");
@@ -461,6 +462,7 @@ int kv_write_impl(const void* k, const void* v, int64_t start, int64_t n, void* 
     rp.n = n; rp.t0 = start; rp.ld = Lmax; rp.pad_to = 0;
     rp.B = B; rp.Hkv = Hkv; rp.d = d; rp.in_f32 = dtype == WPA_FP32; rp.v_transposed = 0;
     rp.tab = &tab;
+    rp.pg = pg;
     hipError_t e = wpa::launch_rope_relayout(rp, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(WPA_ERR_HIP, "kv write launch: %s", hipGetErrorString(e));
     return ok();
@@ -471,7 +473,7 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache, const i
                 int32_t Hq, int32_t Hkv, int32_t d, double base, const wpa_rope_t* rope,
                 const wpa::KLayout& kl, double alpha, float scale, int32_t dtype, int32_t out_dtype,
                 unsigned long long* term_count, int32_t chunk_keys, void* workspace,
-                size_t ws_bytes, void* stream) {
+                size_t ws_bytes, void* stream, const wpa::Paging& pg = wpa::Paging{}) {
     if (B < 1 || Lmax < 1 || Hq < 1 || Hkv < 1) return fail(WPA_ERR_INVALID, "B, Lmax, Hq, Hkv must be >= 1");
     if (Hq % Hkv) return fail(WPA_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
     if (Hq / Hkv > 16) return fail(WPA_ERR_UNSUPPORTED, "decode supports up to 16 q heads per kv head");
@@ -497,6 +499,7 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache, const i
     dp.partial = static_cast<float*>(workspace); dp.Lmax = Lmax; dp.B = B; dp.Hq = Hq; dp.Hkv = Hkv;
     dp.d = d; dp.in_f32 = dtype == WPA_FP32; dp.out_f32 = out_dtype == WPA_FP32; dp.chunk = ch; dp.n_chunks = (int)((Lmax + ch - 1) / ch);
     dp.scale = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)d));
+    dp.pg = pg;
     hipError_t e = wpa::launch_decode(dp, tab, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(WPA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
     return ok();
@@ -510,9 +513,67 @@ int check_cache_alpha(double cache_alpha) {
     return WPA_OK;
 }
 
+// A page table's description: page_size a power of two in [32, 65536] (a 32-token tile and
+// an 8-token octet never straddle pages), the table's reach max_pages * page_size below 2^31.
+int check_paging(const int32_t* table, int32_t num_pages, int32_t max_pages, int32_t page_size,
+                 wpa::Paging* pg) {
+    if (!table) return fail(WPA_ERR_INVALID, "null block table");
+    if (num_pages < 1 || max_pages < 1) return fail(WPA_ERR_INVALID, "num_pages and max_pages must be >= 1");
+    if (page_size < 32 || page_size > 65536 || (page_size & (page_size - 1)))
+        return fail(WPA_ERR_INVALID, "page_size must be a power of two in [32, 65536] (got %d)", page_size);
+    if ((int64_t)max_pages * page_size >= (int64_t)INT32_MAX)
+        return fail(WPA_ERR_INVALID, "max_pages * page_size must be below 2^31");
+    int lg = 0;
+    while ((1 << lg) < page_size) ++lg;
+    pg->table = table;
+    pg->max_pages = max_pages;
+    pg->page_log2 = lg;
+    pg->num_pages = num_pages;
+    return WPA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t wpa_kv_page_bytes(int32_t Hkv, int32_t d, int32_t page_size) {
+    if (Hkv < 1 || (d != 64 && d != 128) || page_size < 32 || page_size > 65536 ||
+        (page_size & (page_size - 1)))
+        return 0;
+    return (size_t)Hkv * d * page_size * 2;
+}
+
+int wpa_kv_write_paged(const void* k, const void* v, int64_t start, int64_t n, void* k_pool,
+                       void* v_pool, const int32_t* block_table, int32_t num_pages, int32_t B,
+                       int32_t max_pages, int32_t page_size, int32_t Hkv, int32_t d, double base,
+                       const wpa_rope_t* rope, int32_t dtype, void* stream) {
+    int rc = check_common(d, base, rope, 1.0);
+    if (rc) return rc;
+    wpa::Paging pg{};
+    rc = check_paging(block_table, num_pages, max_pages, page_size, &pg);
+    if (rc) return rc;
+    return kv_write_impl(k, v, start, n, k_pool, v_pool, B, (int64_t)max_pages * page_size, Hkv,
+                         d, base, rope, dense_layout(d, (int64_t)max_pages * page_size), dtype,
+                         stream, pg);
+}
+
+int wpa_decode_paged(const void* q, const void* k_pool, const void* v_pool,
+                     const int32_t* block_table, int32_t num_pages, const int32_t* kv_len,
+                     const int32_t* q_pos, void* out, float* lse, int32_t B, int32_t max_pages,
+                     int32_t page_size, int32_t Hq, int32_t Hkv, int32_t d, double base,
+                     const wpa_rope_t* rope, double alpha, float scale, int32_t dtype,
+                     int32_t out_dtype, unsigned long long* term_count, int32_t chunk_keys,
+                     void* workspace, size_t ws_bytes, void* stream) {
+    int rc = check_common(d, base, rope, alpha);
+    if (rc) return rc;
+    wpa::Paging pg{};
+    rc = check_paging(block_table, num_pages, max_pages, page_size, &pg);
+    if (rc) return rc;
+    const int64_t Lmax = (int64_t)max_pages * page_size;
+    return decode_impl(q, k_pool, v_pool, kv_len, q_pos, out, lse, B, Lmax, Hq, Hkv, d, base,
+                       rope, dense_layout(d, Lmax), alpha, scale, dtype, out_dtype, term_count,
+                       chunk_keys, workspace, ws_bytes, stream, pg);
+}
 
 int wpa_kv_write_ex(const void* k, const void* v, int64_t start, int64_t n, void* k_cache,
                     void* v_cache, int32_t B, int64_t Lmax, int32_t Hkv, int32_t d, double base,

@@ -30,6 +30,22 @@ struct KLayout {
     int32_t cap[8];
 };
 
+// Paged caches: the token range [i*page, (i+1)*page) of sequence b lives in page
+// table[b*max_pages + i] of a pool.  A K page is [Hkv][d/16][page][16] half (pair-blocked),
+// a V page [Hkv][page/8][d][8] bf16 (key octets); page is a power of two >= 32, so a 32-token
+// tile and an octet never straddle pages.  table == null: contiguous per-sequence caches.
+struct Paging {
+    const int32_t* table;         // [B][max_pages] device, or null
+    int32_t max_pages, page_log2, num_pages;
+};
+
+// Pool page holding token tok of sequence b (tok < max_pages << page_log2).  Entries outside
+// [0, num_pages) break the caller's contract; they are clamped so that no access leaves the pool.
+__device__ inline int64_t page_of(const Paging& pg, int b, int64_t tok) {
+    const int64_t page = pg.table[(int64_t)b * pg.max_pages + (tok >> pg.page_log2)];
+    return page < 0 ? 0 : (page >= pg.num_pages ? pg.num_pages - 1 : page);
+}
+
 struct RopeParams {
     const void* k;                // [B][n][Hkv][d]
     const void* v;                // [B][n][Hkv][d]
@@ -41,6 +57,7 @@ struct RopeParams {
     int32_t B, Hkv, d, in_f32, v_transposed;
     int32_t interleaved;          // pair i = dims (2i, 2i+1) instead of (i, i+d/2)
     const Tables* tab;            // host pointer; copied into kernel arguments
+    Paging pg;                    // decode cache writes: pages (table null: kl layout)
 };
 
 struct PrefillParams {
@@ -78,6 +95,7 @@ struct DecodeParams {
     int32_t B, Hq, Hkv, d, in_f32, out_f32, chunk, n_chunks;
     int32_t interleaved;          // pair i = dims (2i, 2i+1) instead of (i, i+d/2)
     float scale;
+    Paging pg;                    // pools of pages (table null: kl layout, [B][Hkv][..] V)
 };
 
 hipError_t launch_rope_relayout(const RopeParams& p, hipStream_t s);

@@ -309,3 +309,59 @@ def _decode_window_rc(**kw):
 ])
 def test_decode_window_rejects_bad_arguments(kw, code):
     assert _decode_window_rc(**kw) == code
+
+
+def test_kv_page_bytes():
+    assert wpa.lib().wpa_kv_page_bytes(8, 128, 64) == 8 * 128 * 64 * 2
+    assert wpa.lib().wpa_kv_page_bytes(2, 64, 32) == 2 * 64 * 32 * 2
+    for hkv, d, ps in ((8, 128, 48), (8, 128, 16), (8, 96, 64), (0, 128, 64), (8, 128, 1 << 17)):
+        assert wpa.lib().wpa_kv_page_bytes(hkv, d, ps) == 0
+
+
+def _decode_paged_rc(**kw):
+    a = dict(q=FAKE, kp=FAKE, vp=FAKE, table=FAKE, npages=16, lens=FAKE, qpos=None, out=FAKE,
+             lse=None, B=2, maxp=8, ps=64, Hq=8, Hkv=2, d=128, base=5e5, rope=None, alpha=1.0,
+             scale=0.0, dtype=0, odt=1, cnt=None, chunk=0, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    return wpa.lib().wpa_decode_paged(a["q"], a["kp"], a["vp"], a["table"], a["npages"],
+                                      a["lens"], a["qpos"], a["out"], a["lse"], a["B"], a["maxp"],
+                                      a["ps"], a["Hq"], a["Hkv"], a["d"], a["base"], a["rope"],
+                                      a["alpha"], a["scale"], a["dtype"], a["odt"], a["cnt"],
+                                      a["chunk"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ps=48), wpa.WPA_ERR_INVALID),
+    (dict(ps=16), wpa.WPA_ERR_INVALID),
+    (dict(table=None), wpa.WPA_ERR_INVALID),
+    (dict(npages=0), wpa.WPA_ERR_INVALID),
+    (dict(maxp=0), wpa.WPA_ERR_INVALID),
+    (dict(maxp=1 << 20, ps=4096), wpa.WPA_ERR_INVALID),
+    (dict(d=96), wpa.WPA_ERR_UNSUPPORTED),
+    (dict(Hq=7), wpa.WPA_ERR_INVALID),
+    (dict(lens=None), wpa.WPA_ERR_INVALID),
+    (dict(ws_bytes=64), wpa.WPA_ERR_WORKSPACE),
+])
+def test_decode_paged_rejects_bad_arguments(kw, code):
+    assert _decode_paged_rc(**kw) == code
+
+
+def _kv_write_paged_rc(**kw):
+    a = dict(k=FAKE, v=FAKE, start=0, n=64, kp=FAKE, vp=FAKE, table=FAKE, npages=16, B=2,
+             maxp=8, ps=64, Hkv=2, d=128, base=5e5, rope=None, dtype=0)
+    a.update(kw)
+    return wpa.lib().wpa_kv_write_paged(a["k"], a["v"], a["start"], a["n"], a["kp"], a["vp"],
+                                        a["table"], a["npages"], a["B"], a["maxp"], a["ps"],
+                                        a["Hkv"], a["d"], a["base"], a["rope"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(start=480, n=64), wpa.WPA_ERR_INVALID),      # past 8 pages of 64
+    (dict(n=0), wpa.WPA_ERR_INVALID),
+    (dict(ps=100), wpa.WPA_ERR_INVALID),
+    (dict(table=None), wpa.WPA_ERR_INVALID),
+    (dict(d=80), wpa.WPA_ERR_UNSUPPORTED),
+    (dict(kp=None), wpa.WPA_ERR_INVALID),
+])
+def test_kv_write_paged_rejects_bad_arguments(kw, code):
+    assert _kv_write_paged_rc(**kw) == code
