@@ -450,6 +450,38 @@ def extras(reps):
         dec["dense_cache"]["k_cache_bytes"] + dec["dense_cache"]["v_cache_bytes"])
     res["window_decode_cache"] = dec
     _log("extras: window cache %s" % dec)
+
+    # paged decode cache: each sequence holds only the pages its length needs, shuffled
+    import numpy as np
+    pg = {"workload": "llama3b_decode, alpha 1, pages shuffled over the pool"}
+    for ps in (64, 256):
+        maxp = (wd.N + ps - 1) // ps
+        need = [(L + ps - 1) // ps for L in lens.cpu().tolist()]
+        order = np.random.default_rng(ps).permutation(sum(need))
+        tab = np.zeros((wd.B, maxp), np.int32)
+        at = 0
+        for bi_, n_ in enumerate(need):
+            tab[bi_, :n_] = order[at:at + n_]
+            at += n_
+        table = torch.from_numpy(tab).cuda()
+        cache = wpa.PagedKVCache(sum(need), ps, wd.Hkv, wd.d, wd.base)
+        for bi_, L in enumerate(lens.cpu().tolist()):
+            cache.write(kd[bi_:bi_ + 1, :L].contiguous(), vd[bi_:bi_ + 1, :L].contiguous(), 0,
+                        block_table=table[bi_:bi_ + 1])
+        wsd = torch.empty(max(wpa.decode_workspace_bytes(wd.B, maxp * ps, wd.Hq, wd.Hkv, wd.d), 16),
+                          device="cuda", dtype=torch.uint8)
+        out = torch.empty_like(qd)
+        t = _time(lambda: wpa.decode(qd, cache, lens, 1.0, out=out, workspace=wsd,
+                                     block_table=table), reps)
+        pg["page_%d" % ps] = {"ms": t, "gbs": nbytes / (t * 1e-3) / 1e9,
+                              "kv_bytes": cache.k.numel() + cache.v.numel(),
+                              "kv_bytes_vs_contiguous": (cache.k.numel() + cache.v.numel()) / (
+                                  dec["dense_cache"]["k_cache_bytes"] + dec["dense_cache"]["v_cache_bytes"])}
+        del cache, wsd, out, table
+        torch.cuda.empty_cache()
+    pg["contiguous_ms"] = dec["dense_cache"]["ms"]
+    res["paged_decode_cache"] = pg
+    _log("extras: paged cache %s" % pg)
     return res
 
 
