@@ -326,6 +326,9 @@ int wpa_decode_window(const void* q, const void* k_cache, const void* v_cache,
  *   wpa_decode_paged    as wpa_decode_ex on the pools; kv_len[b] in [1, max_pages*page_size]
  *                (larger values are clamped to it).  Workspace:
  *                wpa_decode_workspace_bytes(B, max_pages*page_size, Hq, Hkv, d, chunk_keys).
+ *   wpa_prefill_paged   as wpa_prefill_cached on the pools (Lmax = max_pages * page_size),
+ *                bit-identical to it on contiguous caches holding the same tokens; needs
+ *                page_size >= 128 (a page holds whole key tiles; WPA_ERR_UNSUPPORTED below).
  */
 size_t wpa_kv_page_bytes(int32_t Hkv, int32_t d, int32_t page_size);
 int wpa_kv_write_paged(const void* k, const void* v, int64_t start, int64_t n, void* k_pool,
@@ -339,6 +342,12 @@ int wpa_decode_paged(const void* q, const void* k_pool, const void* v_pool,
                      const wpa_rope_t* rope, double alpha, float scale, int32_t dtype,
                      int32_t out_dtype, unsigned long long* term_count, int32_t chunk_keys,
                      void* workspace, size_t ws_bytes, void* stream);
+int wpa_prefill_paged(const void* q, const void* k_pool, const void* v_pool,
+                      const int32_t* block_table, int32_t num_pages, const int32_t* kv_len,
+                      void* out, float* lse, int32_t B, int32_t Nq, int32_t max_pages,
+                      int32_t page_size, int32_t Hq, int32_t Hkv, int32_t d, double base,
+                      const wpa_rope_t* rope, double alpha, float scale, int32_t dtype,
+                      int32_t out_dtype, unsigned long long* term_count, void* stream);
 
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char* wpa_last_error(void);

@@ -40,7 +40,7 @@ EXPORTS = ("wpa_count_terms", "wpa_thresholds", "wpa_prefill_workspace_bytes", "
            "wpa_thresholds_ex", "wpa_prefill_ex", "wpa_prefill_prepare_ex", "wpa_prefill_attend_ex",
            "wpa_kv_write_ex", "wpa_decode_ex", "wpa_prefill_cached", "wpa_kcache_window_bytes",
            "wpa_kv_write_window", "wpa_decode_window", "wpa_prefill_sparse", "wpa_kv_page_bytes",
-           "wpa_kv_write_paged", "wpa_decode_paged", "wpa_last_error")
+           "wpa_kv_write_paged", "wpa_decode_paged", "wpa_prefill_paged", "wpa_last_error")
 
 
 class Rope(ctypes.Structure):
@@ -165,6 +165,9 @@ def lib():
     L.wpa_decode_paged.argtypes = [P, P, P, P, I32, P, P, P, P, I32, I32, I32, I32, I32, I32, D, P,
                                    D, F, I32, I32, P, I32, P, SZ, P]
     L.wpa_decode_paged.restype = ctypes.c_int
+    L.wpa_prefill_paged.argtypes = [P, P, P, P, I32, P, P, P, I32, I32, I32, I32, I32, I32, I32, D,
+                                    P, D, F, I32, I32, P, P]
+    L.wpa_prefill_paged.restype = ctypes.c_int
     L.wpa_last_error.argtypes = []
     L.wpa_last_error.restype = ctypes.c_char_p
     _lib = L
@@ -511,17 +514,23 @@ def decode(q, cache, kv_len, alpha: float, *, q_pos=None, scale: float | None = 
     return (out, lse) if lse is not None else out
 
 
-def prefill_cached(q, cache: KVCache, kv_len, alpha: float, *, scale: float | None = None,
+def prefill_cached(q, cache, kv_len, alpha: float, *, scale: float | None = None,
                    out=None, out_dtype=None, lse=None, want_lse: bool = False, term_count=None,
-                   stream=None):
+                   stream=None, block_table=None):
     """Chunked prefill: q [B][Nq][Hq][d] pre-RoPE holds the last Nq tokens of each sequence,
-    whose keys and values are already in `cache`; kv_len int32 device [B], each >= Nq."""
-    if isinstance(cache, PagedKVCache):
-        raise ValueError("chunked prefill reads contiguous caches (KVCache)")
+    whose keys and values are already in `cache` (a KVCache, or a PagedKVCache with pages of
+    at least 128 tokens and `block_table` [B][max_pages] or the cache's default table);
+    kv_len int32 device [B], each >= Nq."""
     _dev(q, "q")
     _dev(kv_len, "kv_len")
     B, Nq, Hq, d = q.shape
-    if B != cache.B or d != cache.d or kv_len.dtype != torch.int32 or kv_len.numel() != B:
+    paged = isinstance(cache, PagedKVCache)
+    if paged:
+        table = cache._table(block_table)
+        nseq = table.shape[0]
+    else:
+        nseq = cache.B
+    if B != nseq or d != cache.d or kv_len.dtype != torch.int32 or kv_len.numel() != B:
         raise ValueError("q [B][Nq][Hq][d] and kv_len int32 [B] must match the cache")
     if cache.window_alpha is not None:
         raise ValueError("chunked prefill needs the dense cache (window_alpha=None)")
@@ -531,11 +540,18 @@ def prefill_cached(q, cache: KVCache, kv_len, alpha: float, *, scale: float | No
     if want_lse and lse is None:
         lse = torch.empty((B, Hq, Nq), device=q.device, dtype=torch.float32)
     rope, keep = _rope(d, cache.inv_freq, cache.pairs)
-    _check(lib().wpa_prefill_cached(_ptr(q), _ptr(cache.k), _ptr(cache.v), _ptr(kv_len),
-                                    _ptr(out), _ptr(lse), B, Nq, cache.Lmax, Hq, cache.Hkv, d,
-                                    cache.base, rope, float(alpha),
-                                    float(scale) if scale is not None else 0.0, _dtype_code(q),
-                                    _dtype_code(out), _ptr(term_count), _stream(stream)))
+    sc = float(scale) if scale is not None else 0.0
+    if paged:
+        _check(lib().wpa_prefill_paged(_ptr(q), _ptr(cache.k), _ptr(cache.v), _ptr(table),
+                                       cache.num_pages, _ptr(kv_len), _ptr(out), _ptr(lse), B, Nq,
+                                       table.shape[1], cache.page_size, Hq, cache.Hkv, d,
+                                       cache.base, rope, float(alpha), sc, _dtype_code(q),
+                                       _dtype_code(out), _ptr(term_count), _stream(stream)))
+    else:
+        _check(lib().wpa_prefill_cached(_ptr(q), _ptr(cache.k), _ptr(cache.v), _ptr(kv_len),
+                                        _ptr(out), _ptr(lse), B, Nq, cache.Lmax, Hq, cache.Hkv, d,
+                                        cache.base, rope, float(alpha), sc, _dtype_code(q),
+                                        _dtype_code(out), _ptr(term_count), _stream(stream)))
     return (out, lse) if lse is not None else out
 
 

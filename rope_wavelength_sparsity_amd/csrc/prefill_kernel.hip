@@ -152,7 +152,7 @@ struct Tile {
 // SPARSE: each (sequence, q head, 64-row query block) attends, besides its own block, only
 // the 64-key blocks its ascending list names (token-level block sparsity composed with the
 // window); unlisted keys leave the softmax.  Positions are token indices.
-template <int D, bool F32, bool HASPOS, bool COUNT, bool CACHED, bool SPARSE>
+template <int D, bool F32, bool HASPOS, bool COUNT, bool CACHED, bool SPARSE, bool PAGED = false>
 __global__ __launch_bounds__(64 * (Tile<D>::maxw(HASPOS) + 1))
 __attribute__((amdgpu_waves_per_eu(Tile<D>::waves_per_eu(HASPOS))))
 void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
@@ -316,6 +316,10 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
         const int jlo = uniform(plo_wg) >> 3;
         const int nK = Tile<D>::KI * (NB - jlo);
         const int nI = nK + Tile<D>::VI + (HASPOS ? Tile<D>::PI : 0);
+        // paged caches: the tile's page (a page holds whole tiles: page_size >= BN)
+        constexpr bool paged = CACHED && PAGED;
+        int64_t tile_page = 0;
+        if constexpr (paged) tile_page = page_of(p.pg, b, ks);
         for (int i = 0; i < nI; ++i) {
             if (i < nK) {
                 // 16-byte chunk `ch` of block j: half (ch & 1) of key ks + ch/2 (past the last
@@ -326,7 +330,13 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
                 if constexpr (CACHED) {
                     int t = ks + (ch >> 1);
                     if (t > NK - 1) t = NK - 1;
-                    src = kpg + ((int64_t)j * ldk + t) * 16 + (ch & 1) * 8;
+                    if constexpr (paged) {
+                        const int ps = 1 << p.pg.page_log2;
+                        src = p.kp + (((tile_page * p.Hkv + g) * NB + j) * ps + (t & (ps - 1))) * 16 +
+                              (ch & 1) * 8;
+                    } else {
+                        src = kpg + ((int64_t)j * ldk + t) * 16 + (ch & 1) * 8;
+                    }
                 } else {
                     src = kpg + ((int64_t)j * ldk + ks) * 16 + ch * 8;
                 }
@@ -342,7 +352,12 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
                     // keys ks+8c .. ks+8c+7 form octet ks/8 + c of the cache
                     int o = ks / 8 + c;
                     if (o > (NK - 1) / 8) o = (NK - 1) / 8;
-                    src = vtg + ((int64_t)o * D + e) * 8;
+                    if constexpr (paged) {
+                        const int opg = 1 << (p.pg.page_log2 - 3);        // octets per page
+                        src = p.vt + (((tile_page * p.Hkv + g) * opg + (o & (opg - 1))) * D + e) * 8;
+                    } else {
+                        src = vtg + ((int64_t)o * D + e) * 8;
+                    }
                 } else {
                     src = vtg + (int64_t)e * p.Np + ks + 8 * c;
                 }
@@ -830,8 +845,13 @@ hipError_t launch_d(const PrefillParams& p, const Tables& t, hipStream_t s) {
     dim3 grid((unsigned)nblk), block(64 * waves);
     const bool hp = p.pos != nullptr, cn = p.counter != nullptr;
     if (p.kv_len) {
-        if (cn) prefill_kernel<D, F32, false, true, true, false><<<grid, block, 0, s>>>(p, t, L);
-        else prefill_kernel<D, F32, false, false, true, false><<<grid, block, 0, s>>>(p, t, L);
+        if (p.pg.table) {
+            if (cn) prefill_kernel<D, F32, false, true, true, false, true><<<grid, block, 0, s>>>(p, t, L);
+            else prefill_kernel<D, F32, false, false, true, false, true><<<grid, block, 0, s>>>(p, t, L);
+        } else {
+            if (cn) prefill_kernel<D, F32, false, true, true, false><<<grid, block, 0, s>>>(p, t, L);
+            else prefill_kernel<D, F32, false, false, true, false><<<grid, block, 0, s>>>(p, t, L);
+        }
     } else if (p.blk_count) {
         // block bitmaps: one per compute wave and their union
         const size_t words = (size_t)(((p.N + 63) / 64 + 31) / 32);

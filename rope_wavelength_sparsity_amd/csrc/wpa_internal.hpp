@@ -78,6 +78,7 @@ struct PrefillParams {
     int32_t B, Hq, Hkv, d, in_f32, out_f32;
     int32_t interleaved;          // pair i = dims (2i, 2i+1) instead of (i, i+d/2)
     float scale;
+    Paging pg;                    // cached prefill on paged caches (kp, vt: the pools)
 };
 
 struct DecodeParams {

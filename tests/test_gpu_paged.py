@@ -144,3 +144,52 @@ def test_paged_rejects_misuse():
     kk = torch.zeros((1, 200, 2, 64), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(RuntimeError):
         paged.write(kk, kk, 0, block_table=table)     # 200 tokens > 2 pages of 64
+
+
+@pytest.mark.parametrize("d,Hq,Hkv,base,page", [(64, 14, 2, 1e6, 128), (128, 24, 8, 5e5, 256)])
+def test_paged_chunked_prefill_matches_contiguous_and_oracle(d, Hq, Hkv, base, page):
+    """Ragged prompts whose last 300 tokens are attended as a chunk against shuffled pages:
+    bit-identical to the same chunk against contiguous caches, and within tolerance of the
+    oracle's rows."""
+    need_gpu()
+    B, Nq = 3, 300
+    lens_h = [Nq, Nq + 777, Nq + 2000]
+    max_pages = (max(lens_h) + page - 1) // page + 1
+    Lmax = max_pages * page
+    q, k, v = synth.prefill_inputs(B, Lmax, Hq, Hkv, d, "bf16", seed=84)
+    table = _table(B, max_pages, B * max_pages + 3, seed=page + 1)
+    dense = wpa.KVCache(B, Lmax, Hkv, d, base)
+    paged = wpa.PagedKVCache(B * max_pages + 3, page, Hkv, d, base, block_table=table)
+    _fill_nan(dense, paged)
+    for b, L in enumerate(lens_h):
+        kk, vv = k[b:b + 1, :L].cuda().contiguous(), v[b:b + 1, :L].cuda().contiguous()
+        dense.write(kk, vv, 0, seq=b)
+        paged.write(kk, vv, 0, block_table=table[b:b + 1])
+    qc = torch.stack([q[b, L - Nq:L] for b, L in enumerate(lens_h)]).contiguous().cuda()
+    kv_len = torch.tensor(lens_h, dtype=torch.int32, device="cuda")
+    cd = torch.zeros(1, dtype=torch.int64, device="cuda")
+    cp = torch.zeros(1, dtype=torch.int64, device="cuda")
+    say("paged chunked prefill", d, page)
+    od, ld = wpa.prefill_cached(qc, dense, kv_len, 1.0, want_lse=True, term_count=cd,
+                                out_dtype=torch.float32)
+    op, lp = wpa.prefill_cached(qc, paged, kv_len, 1.0, want_lse=True, term_count=cp,
+                                out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(od, op) and torch.equal(ld, lp), "paged chunk differs from contiguous"
+    assert int(cd.item()) == int(cp.item())
+    for b, L in enumerate(lens_h):
+        ro, rl, kept = oracle.prefill(synth.to_oracle(q[b:b + 1, :L]), synth.to_oracle(k[b:b + 1, :L]),
+                                      synth.to_oracle(v[b:b + 1, :L]), base, 1.0,
+                                      rows=np.arange(L - Nq, L))
+        check_close(op[b:b + 1].cpu().numpy(), ro, "out[%d]" % b)
+        check_close(lp[b:b + 1].cpu().numpy(), rl, "lse[%d]" % b, LSE_MAX, LSE_MAX)
+
+
+def test_paged_chunked_prefill_needs_big_pages():
+    need_gpu()
+    paged = wpa.PagedKVCache(8, 64, 2, 64, 1e4)
+    table = torch.arange(8, dtype=torch.int32, device="cuda").view(1, 8)
+    q = torch.zeros((1, 16, 4, 64), dtype=torch.bfloat16, device="cuda")
+    lens = torch.full((1,), 64, dtype=torch.int32, device="cuda")
+    with pytest.raises(RuntimeError):
+        wpa.prefill_cached(q, paged, lens, 1.0, block_table=table)

@@ -365,3 +365,26 @@ def _kv_write_paged_rc(**kw):
 ])
 def test_kv_write_paged_rejects_bad_arguments(kw, code):
     assert _kv_write_paged_rc(**kw) == code
+
+
+def _prefill_paged_rc(**kw):
+    a = dict(q=FAKE, kp=FAKE, vp=FAKE, table=FAKE, npages=16, lens=FAKE, out=FAKE, lse=None, B=2,
+             Nq=64, maxp=8, ps=128, Hq=8, Hkv=2, d=128, base=5e5, rope=None, alpha=1.0, scale=0.0,
+             dtype=0, odt=1, cnt=None)
+    a.update(kw)
+    return wpa.lib().wpa_prefill_paged(a["q"], a["kp"], a["vp"], a["table"], a["npages"],
+                                       a["lens"], a["out"], a["lse"], a["B"], a["Nq"], a["maxp"],
+                                       a["ps"], a["Hq"], a["Hkv"], a["d"], a["base"], a["rope"],
+                                       a["alpha"], a["scale"], a["dtype"], a["odt"], a["cnt"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ps=64), wpa.WPA_ERR_UNSUPPORTED),          # a page must hold whole key tiles
+    (dict(ps=96), wpa.WPA_ERR_INVALID),
+    (dict(table=None), wpa.WPA_ERR_INVALID),
+    (dict(Nq=2000), wpa.WPA_ERR_INVALID),             # more rows than the table reaches
+    (dict(d=96), wpa.WPA_ERR_UNSUPPORTED),
+    (dict(lens=None), wpa.WPA_ERR_INVALID),
+])
+def test_prefill_paged_rejects_bad_arguments(kw, code):
+    assert _prefill_paged_rc(**kw) == code
