@@ -246,6 +246,22 @@ int wpa_prefill_cached(const void* q, const void* k_cache, const void* v_cache,
                        int32_t out_dtype, unsigned long long* term_count, void* stream);
 
 /*
+ * Chunked prefill with a query count per sequence (varlen): sequence b's chunk is its last
+ * q_b = cu_q[b+1] - cu_q[b] tokens (0 <= q_b <= max_q, q_b <= kv_len[b]; a sequence with
+ * q_b = 0 is skipped), packed back to back.
+ *   cu_q     [B+1] int32 device, non-decreasing: rows cu_q[b] .. cu_q[b+1]-1 of q and out
+ *   q        [cu_q[B]][Hq][d] pre-RoPE;  out [cu_q[B]][Hq][d];  lse [cu_q[B]][Hq] or NULL
+ *   max_q    an upper bound of every q_b (it sizes the launch; larger counts are clamped)
+ * Each row is bit-identical to the same row of wpa_prefill_cached with Nq = q_b.
+ */
+int wpa_prefill_cached_varlen(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* cu_q, const int32_t* kv_len, void* out, float* lse,
+                              int32_t B, int32_t max_q, int64_t Lmax, int32_t Hq, int32_t Hkv,
+                              int32_t d, double base, const wpa_rope_t* rope, double alpha,
+                              float scale, int32_t dtype, int32_t out_dtype,
+                              unsigned long long* term_count, void* stream);
+
+/*
  * Prefill composed with token-level block sparsity (ATFlash abstract: the window can be
  * applied on top of other sparse attention methods).  Tokens form blocks of 64; the query
  * rows of block R of q head h attend, besides block R itself (always), only the key blocks
@@ -348,6 +364,15 @@ int wpa_prefill_paged(const void* q, const void* k_pool, const void* v_pool,
                       int32_t page_size, int32_t Hq, int32_t Hkv, int32_t d, double base,
                       const wpa_rope_t* rope, double alpha, float scale, int32_t dtype,
                       int32_t out_dtype, unsigned long long* term_count, void* stream);
+/* Varlen chunked prefill on paged caches: wpa_prefill_cached_varlen's arguments with the
+ * pools and block table of wpa_prefill_paged. */
+int wpa_prefill_paged_varlen(const void* q, const void* k_pool, const void* v_pool,
+                             const int32_t* block_table, int32_t num_pages, const int32_t* cu_q,
+                             const int32_t* kv_len, void* out, float* lse, int32_t B,
+                             int32_t max_q, int32_t max_pages, int32_t page_size, int32_t Hq,
+                             int32_t Hkv, int32_t d, double base, const wpa_rope_t* rope,
+                             double alpha, float scale, int32_t dtype, int32_t out_dtype,
+                             unsigned long long* term_count, void* stream);
 
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char* wpa_last_error(void);

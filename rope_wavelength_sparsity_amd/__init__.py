@@ -40,7 +40,8 @@ EXPORTS = ("wpa_count_terms", "wpa_thresholds", "wpa_prefill_workspace_bytes", "
            "wpa_thresholds_ex", "wpa_prefill_ex", "wpa_prefill_prepare_ex", "wpa_prefill_attend_ex",
            "wpa_kv_write_ex", "wpa_decode_ex", "wpa_prefill_cached", "wpa_kcache_window_bytes",
            "wpa_kv_write_window", "wpa_decode_window", "wpa_prefill_sparse", "wpa_kv_page_bytes",
-           "wpa_kv_write_paged", "wpa_decode_paged", "wpa_prefill_paged", "wpa_last_error")
+           "wpa_kv_write_paged", "wpa_decode_paged", "wpa_prefill_paged",
+           "wpa_prefill_cached_varlen", "wpa_prefill_paged_varlen", "wpa_last_error")
 
 
 class Rope(ctypes.Structure):
@@ -168,6 +169,12 @@ def lib():
     L.wpa_prefill_paged.argtypes = [P, P, P, P, I32, P, P, P, I32, I32, I32, I32, I32, I32, I32, D,
                                     P, D, F, I32, I32, P, P]
     L.wpa_prefill_paged.restype = ctypes.c_int
+    L.wpa_prefill_cached_varlen.argtypes = [P, P, P, P, P, P, P, I32, I32, I64, I32, I32, I32, D,
+                                            P, D, F, I32, I32, P, P]
+    L.wpa_prefill_cached_varlen.restype = ctypes.c_int
+    L.wpa_prefill_paged_varlen.argtypes = [P, P, P, P, I32, P, P, P, P, I32, I32, I32, I32, I32,
+                                           I32, I32, D, P, D, F, I32, I32, P, P]
+    L.wpa_prefill_paged_varlen.restype = ctypes.c_int
     L.wpa_last_error.argtypes = []
     L.wpa_last_error.restype = ctypes.c_char_p
     _lib = L
@@ -516,11 +523,17 @@ def decode(q, cache, kv_len, alpha: float, *, q_pos=None, scale: float | None = 
 
 def prefill_cached(q, cache, kv_len, alpha: float, *, scale: float | None = None,
                    out=None, out_dtype=None, lse=None, want_lse: bool = False, term_count=None,
-                   stream=None, block_table=None):
+                   stream=None, block_table=None, cu_q=None, max_q: int | None = None):
     """Chunked prefill: q [B][Nq][Hq][d] pre-RoPE holds the last Nq tokens of each sequence,
     whose keys and values are already in `cache` (a KVCache, or a PagedKVCache with pages of
     at least 128 tokens and `block_table` [B][max_pages] or the cache's default table);
-    kv_len int32 device [B], each >= Nq."""
+    kv_len int32 device [B], each >= Nq.
+    Varlen: with cu_q (int32 device [B+1]) q is [rows][Hq][d], sequence b's chunk being rows
+    cu_q[b] .. cu_q[b+1]-1 (its last tokens), max_q an upper bound of the per-sequence counts;
+    lse is then [rows][Hq]."""
+    if cu_q is not None:
+        return _prefill_varlen(q, cache, kv_len, alpha, cu_q, max_q, scale, out, out_dtype, lse,
+                               want_lse, term_count, stream, block_table)
     _dev(q, "q")
     _dev(kv_len, "kv_len")
     B, Nq, Hq, d = q.shape
@@ -552,6 +565,51 @@ def prefill_cached(q, cache, kv_len, alpha: float, *, scale: float | None = None
                                         _ptr(out), _ptr(lse), B, Nq, cache.Lmax, Hq, cache.Hkv, d,
                                         cache.base, rope, float(alpha), sc, _dtype_code(q),
                                         _dtype_code(out), _ptr(term_count), _stream(stream)))
+    return (out, lse) if lse is not None else out
+
+
+def _prefill_varlen(q, cache, kv_len, alpha, cu_q, max_q, scale, out, out_dtype, lse, want_lse,
+                    term_count, stream, block_table):
+    _dev(q, "q")
+    _dev(kv_len, "kv_len")
+    _dev(cu_q, "cu_q")
+    if q.dim() != 3:
+        raise ValueError("varlen q must be [rows][Hq][d]")
+    rows, Hq, d = q.shape
+    B = kv_len.numel()
+    if cu_q.dtype != torch.int32 or cu_q.numel() != B + 1 or kv_len.dtype != torch.int32:
+        raise ValueError("cu_q int32 [B+1] and kv_len int32 [B]")
+    if max_q is None:
+        raise ValueError("max_q (an upper bound of the per-sequence query counts) is needed")
+    paged = isinstance(cache, PagedKVCache)
+    if paged:
+        table = cache._table(block_table)
+        if table.shape[0] != B:
+            raise ValueError("block_table must have B rows")
+    elif B != cache.B:
+        raise ValueError("kv_len must hold one length per cache sequence")
+    if d != cache.d or cache.window_alpha is not None:
+        raise ValueError("q must match the (dense) cache")
+    if out is None:
+        out = torch.empty(q.shape, device=q.device, dtype=out_dtype or q.dtype)
+    _dev(out, "out")
+    if want_lse and lse is None:
+        lse = torch.empty((rows, Hq), device=q.device, dtype=torch.float32)
+    rope, keep = _rope(d, cache.inv_freq, cache.pairs)
+    sc = float(scale) if scale is not None else 0.0
+    if paged:
+        _check(lib().wpa_prefill_paged_varlen(_ptr(q), _ptr(cache.k), _ptr(cache.v), _ptr(table),
+                                              cache.num_pages, _ptr(cu_q), _ptr(kv_len), _ptr(out),
+                                              _ptr(lse), B, int(max_q), table.shape[1],
+                                              cache.page_size, Hq, cache.Hkv, d, cache.base, rope,
+                                              float(alpha), sc, _dtype_code(q), _dtype_code(out),
+                                              _ptr(term_count), _stream(stream)))
+    else:
+        _check(lib().wpa_prefill_cached_varlen(_ptr(q), _ptr(cache.k), _ptr(cache.v), _ptr(cu_q),
+                                               _ptr(kv_len), _ptr(out), _ptr(lse), B, int(max_q),
+                                               cache.Lmax, Hq, cache.Hkv, d, cache.base, rope,
+                                               float(alpha), sc, _dtype_code(q), _dtype_code(out),
+                                               _ptr(term_count), _stream(stream)))
     return (out, lse) if lse is not None else out
 
 

@@ -186,7 +186,17 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
     // Token geometry: NK keys (tokens 0..NK-1); the NQ rows of q and out are tokens
     // tq0..NK-1.  Row groups start at multiples of 32 tokens, so the first sub-tile a wave
     // visits holds the diagonal of all its rows.  (Plain prefill: NK = NQ = N, tq0 = 0.)
-    const int NQ = CACHED ? p.Nq : (int)p.N;
+    int NQ = CACHED ? p.Nq : (int)p.N;
+    int64_t row0 = (int64_t)b * NQ;                    // first row of this sequence in q / out
+    if constexpr (CACHED) {
+        if (p.cu_q) {
+            // varlen: rows cu_q[b] .. cu_q[b+1]-1 of the packed q / out (at most Nq of them)
+            const int c0 = uniform(p.cu_q[b]), c1 = uniform(p.cu_q[b + 1]);
+            NQ = c1 - c0 < 0 ? 0 : (c1 - c0 > p.Nq ? p.Nq : c1 - c0);
+            row0 = c0;
+            if (NQ == 0) return;
+        }
+    }
     const int N_SP = (int)p.N;
     int NK = (int)p.N;
     if constexpr (CACHED) {
@@ -218,7 +228,7 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
     u32xQ Qv;
     auto Qf = [&](int j) -> u32x4 { return u32x4{Qv[4 * j], Qv[4 * j + 1], Qv[4 * j + 2], Qv[4 * j + 3]}; };
     {
-        const int64_t qb = (((int64_t)b * NQ + qi) * p.Hq + hq) * D;
+        const int64_t qb = ((row0 + qi) * p.Hq + hq) * D;
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
             // pairs 8j..8j+7, one at a time (rolled loop: one sincos instance per block);
@@ -763,7 +773,7 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
     const float l_tot = sum_with_partner(lsum, xaddr);
     if (!row_ok) return;
     const float inv = 1.0f / l_tot;
-    const int64_t ob = (((int64_t)b * NQ + qi) * p.Hq + hq) * D;
+    const int64_t ob = ((row0 + qi) * p.Hq + hq) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -782,7 +792,8 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
         }
     }
     if (p.lse && h == 0)
-        p.lse[((int64_t)b * p.Hq + hq) * NQ + qi] = (m + log2f(l_tot)) * 0.6931471805599453f;
+        p.lse[CACHED && p.cu_q ? (row0 + qi) * p.Hq + hq : ((int64_t)b * p.Hq + hq) * NQ + qi] =
+            (m + log2f(l_tot)) * 0.6931471805599453f;
 }
 
 // Compute units of the current device (cached per device).

@@ -518,7 +518,7 @@ int prefill_cached_impl(const void* q, const void* k_cache, const void* v_cache,
                         int64_t Lmax, int32_t Hq, int32_t Hkv, int32_t d, double base,
                         const wpa_rope_t* rope, double alpha, float scale, int32_t dtype,
                         int32_t out_dtype, unsigned long long* term_count, void* stream,
-                        const wpa::Paging& pg);
+                        const wpa::Paging& pg, const int32_t* cu_q);
 
 // A page table's description: page_size a power of two in [32, 65536] (a 32-token tile and
 // an 8-token octet never straddle pages), the table's reach max_pages * page_size below 2^31.
@@ -665,7 +665,19 @@ int wpa_prefill_cached(const void* q, const void* k_cache, const void* v_cache,
                        int32_t out_dtype, unsigned long long* term_count, void* stream) {
     return prefill_cached_impl(q, k_cache, v_cache, kv_len, out, lse, B, Nq, Lmax, Hq, Hkv, d,
                                base, rope, alpha, scale, dtype, out_dtype, term_count, stream,
-                               wpa::Paging{});
+                               wpa::Paging{}, nullptr);
+}
+
+int wpa_prefill_cached_varlen(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* cu_q, const int32_t* kv_len, void* out, float* lse,
+                              int32_t B, int32_t max_q, int64_t Lmax, int32_t Hq, int32_t Hkv,
+                              int32_t d, double base, const wpa_rope_t* rope, double alpha,
+                              float scale, int32_t dtype, int32_t out_dtype,
+                              unsigned long long* term_count, void* stream) {
+    if (!cu_q || (reinterpret_cast<uintptr_t>(cu_q) & 3u)) return fail(WPA_ERR_INVALID, "cu_q must be a 4-byte aligned device pointer");
+    return prefill_cached_impl(q, k_cache, v_cache, kv_len, out, lse, B, max_q, Lmax, Hq, Hkv, d,
+                               base, rope, alpha, scale, dtype, out_dtype, term_count, stream,
+                               wpa::Paging{}, cu_q);
 }
 
 int wpa_prefill_paged(const void* q, const void* k_pool, const void* v_pool,
@@ -681,7 +693,25 @@ int wpa_prefill_paged(const void* q, const void* k_pool, const void* v_pool,
         return fail(WPA_ERR_UNSUPPORTED, "chunked prefill on paged caches needs page_size >= 128 (got %d)", page_size);
     return prefill_cached_impl(q, k_pool, v_pool, kv_len, out, lse, B, Nq,
                                (int64_t)max_pages * page_size, Hq, Hkv, d, base, rope, alpha,
-                               scale, dtype, out_dtype, term_count, stream, pg);
+                               scale, dtype, out_dtype, term_count, stream, pg, nullptr);
+}
+
+int wpa_prefill_paged_varlen(const void* q, const void* k_pool, const void* v_pool,
+                             const int32_t* block_table, int32_t num_pages, const int32_t* cu_q,
+                             const int32_t* kv_len, void* out, float* lse, int32_t B,
+                             int32_t max_q, int32_t max_pages, int32_t page_size, int32_t Hq,
+                             int32_t Hkv, int32_t d, double base, const wpa_rope_t* rope,
+                             double alpha, float scale, int32_t dtype, int32_t out_dtype,
+                             unsigned long long* term_count, void* stream) {
+    wpa::Paging pg{};
+    int rc = check_paging(block_table, num_pages, max_pages, page_size, &pg);
+    if (rc) return rc;
+    if (page_size < 128)
+        return fail(WPA_ERR_UNSUPPORTED, "chunked prefill on paged caches needs page_size >= 128 (got %d)", page_size);
+    if (!cu_q || (reinterpret_cast<uintptr_t>(cu_q) & 3u)) return fail(WPA_ERR_INVALID, "cu_q must be a 4-byte aligned device pointer");
+    return prefill_cached_impl(q, k_pool, v_pool, kv_len, out, lse, B, max_q,
+                               (int64_t)max_pages * page_size, Hq, Hkv, d, base, rope, alpha,
+                               scale, dtype, out_dtype, term_count, stream, pg, cu_q);
 }
 
 }  // extern "C"
@@ -693,7 +723,7 @@ int prefill_cached_impl(const void* q, const void* k_cache, const void* v_cache,
                         int64_t Lmax, int32_t Hq, int32_t Hkv, int32_t d, double base,
                         const wpa_rope_t* rope, double alpha, float scale, int32_t dtype,
                         int32_t out_dtype, unsigned long long* term_count, void* stream,
-                        const wpa::Paging& pg) {
+                        const wpa::Paging& pg, const int32_t* cu_q) {
     int rc = check_common(d, base, rope, alpha);
     if (rc) return rc;
     if (B < 1 || Nq < 1 || Lmax < 1 || Hq < 1 || Hkv < 1) return fail(WPA_ERR_INVALID, "B, Nq, Lmax, Hq, Hkv must be >= 1");
@@ -719,6 +749,7 @@ int prefill_cached_impl(const void* q, const void* k_cache, const void* v_cache,
     pp.Hkv = Hkv; pp.d = d; pp.in_f32 = dtype == WPA_FP32; pp.out_f32 = out_dtype == WPA_FP32;
     pp.scale = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)d));
     pp.pg = pg;
+    pp.cu_q = cu_q;
     hipError_t e = wpa::launch_prefill(pp, tab, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(WPA_ERR_HIP, "cached prefill launch: %s", hipGetErrorString(e));
     return ok();

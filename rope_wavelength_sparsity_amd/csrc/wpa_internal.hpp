@@ -79,6 +79,8 @@ struct PrefillParams {
     int32_t interleaved;          // pair i = dims (2i, 2i+1) instead of (i, i+d/2)
     float scale;
     Paging pg;                    // cached prefill on paged caches (kp, vt: the pools)
+    const int32_t* cu_q;          // cached prefill, varlen: [B+1] first packed q row of each
+                                  // sequence (q, out [rows][Hq][d], lse [rows][Hq]); else null
 };
 
 struct DecodeParams {

@@ -388,3 +388,14 @@ def _prefill_paged_rc(**kw):
 ])
 def test_prefill_paged_rejects_bad_arguments(kw, code):
     assert _prefill_paged_rc(**kw) == code
+
+
+def test_prefill_varlen_needs_cu_q():
+    rc = wpa.lib().wpa_prefill_cached_varlen(FAKE, FAKE, FAKE, None, FAKE, FAKE, None, 2, 64,
+                                             4096, 8, 2, 128, 5e5, None, 1.0, 0.0, 0, 1, None,
+                                             None)
+    assert rc == wpa.WPA_ERR_INVALID
+    rc = wpa.lib().wpa_prefill_paged_varlen(FAKE, FAKE, FAKE, FAKE, 16, None, FAKE, FAKE, None,
+                                            2, 64, 8, 128, 8, 2, 128, 5e5, None, 1.0, 0.0, 0, 1,
+                                            None, None)
+    assert rc == wpa.WPA_ERR_INVALID
