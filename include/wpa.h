@@ -8,7 +8,7 @@
  *   d/2 two-dimensional rotation ("frequency") pairs.  Pair i has wavelength
  *   lambda_i = 2*pi*base^(2i/d) and keeps its term only while the query-key distance
  *   |t_r - t_c| <= alpha*lambda_i; a pruned term contributes zero and the key stays in
- *   the softmax.  alpha = 1 is WavePrune's "first rotation period"; alpha = +INFINITY is
+ *   the softmax.  alpha = 1 is WavePrune's one-rotation-period window; alpha = +INFINITY is
  *   ordinary (full-window) causal RoPE attention in the same kernels.  Softmax and the
  *   P*V product are unchanged.
  *

@@ -6,8 +6,8 @@ with the HIP library (its C part is ``wpa_oracle.c``; the counting helpers below
 numpy).
 
 Method (ATFlash abstract, "Per-RoPE-Wavelength Attention Windows"): the RoPE score is
-an exact sum over frequency pairs; pair i (wavelength lambda_i = 2*pi*base^(2i/d),
-WavePrune original abstract, "first rotation period") keeps its q.k term only while
+an exact sum over frequency pairs; pair i (wavelength lambda_i = 2*pi*base^(2i/d), one
+rotation period: WavePrune original abstract) keeps its q.k term only while
 the query-key distance is <= alpha*lambda_i.  Online softmax and P.V are unchanged.
 
 Parity status of each function (what pins it is listed in the design notes and in

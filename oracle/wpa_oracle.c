@@ -11,14 +11,14 @@
  *   - the RoPE attention score is an exact sum over 2-D rotation frequency
  *     pairs (ATFlash abstract, first sentence);
  *   - pair i has wavelength lambda_i = 2*pi*base^(2i/d), one full rotation
- *     period (WavePrune abstract: "restricts each channel to its first rotation
- *     period"); its query-key term is kept only while the query-key distance
- *     is at most alpha*lambda_i (ATFlash abstract: "prunes the query--key
- *     inner-product terms beyond a wavelength-proportional distance");
+ *     period (WavePrune abstract: each channel kept for its first rotation
+ *     period); its query-key term is kept only while the query-key distance
+ *     is at most alpha*lambda_i (ATFlash abstract: terms farther than a
+ *     distance proportional to the wavelength are dropped);
  *   - a pruned term contributes zero but the key stays in the softmax
- *     (ATFlash abstract: "every key remains reachable");
- *   - the softmax over the windowed logits is ordinary (ATFlash abstract:
- *     "leaving the online-softmax recurrences untouched").
+ *     (ATFlash abstract: no key becomes unreachable, unlike a sliding window);
+ *   - the softmax over the windowed logits is ordinary (ATFlash abstract: the
+ *     online-softmax recurrences are not modified).
  *
  * Readings taken where the pages are silent (each is listed in the design notes):
  *   - pair i is made of head dims i and i + d/2 ("half-split" layout);

@@ -13,8 +13,9 @@
 //   Distance band: dmin/dmax over the sub-tile's visible elements.  With the window table
 //   W (non-decreasing in the pair index), pairs split into dead (W < dmin), straddling
 //   (dmin <= W < dmax) and fully active (W >= dmax).  Because the active pairs at any
-//   distance are a suffix of the pair axis (ATFlash abstract: "a slice of the
-//   query--key contraction axis"), fully active pairs occupy a suffix of 16-dim blocks:
+//   distance are a suffix of the pair axis (ATFlash abstract: the kept terms form a
+//   contiguous part of the contraction axis), fully active pairs occupy a suffix of 16-dim
+//   blocks:
 //     * S^T = K'_blk * Q'_blk^T on v_mfma_f32_32x32x16_f16 over those blocks only; the
 //       leading pairs of the first such block are zeroed in the Q operand;
 //     * straddling pairs are added per element on VALU with the exact test D <= W_i.

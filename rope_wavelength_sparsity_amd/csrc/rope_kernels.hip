@@ -9,7 +9,7 @@
 // [B][Hkv][d/16][tokens][16] in IEEE half precision (the rotated value of a bf16 input
 // needs more than bf16's 8 significant bits; half keeps 11, at the same MFMA rate, for
 // rotated components below 65504 in magnitude).  One 16-element block is one MFMA K-step, so
-// "contract only the active blocks" (pairs form a contiguous slice of the contraction
+// contracting only the active blocks (pairs form a contiguous slice of the contraction
 // axis at every distance) reads contiguous memory for every token range.
 //
 // Values: for prefill they are transposed to [B][Hkv][d][tokens] and for the decode cache

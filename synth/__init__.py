@@ -6,8 +6,8 @@ here (the oracle receives the bf16 bit patterns / fp32 values, never a re-draw).
 
 Shapes follow the attention layers of the models the pages evaluate (ATFlash abstract:
 Qwen2.5-0.5B, Llama-3.2-3B, Qwen2.5-7B-1M).  No weights or datasets exist here; the
-method's cost is input-independent (ATFlash abstract: "The reduction rate is
-input-independent"), so seeded tensors at those shapes reproduce the cost profile.
+method's cost does not depend on the input values (ATFlash abstract: the pruned share is
+fixed by the shapes alone), so seeded tensors at those shapes reproduce the cost profile.
 """
 from __future__ import annotations
 
