@@ -287,13 +287,11 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
     bool started = false;
     const u32x4 ones_blk = h ? u32x4{0u, 0u, 0u, 0u} : u32x4{0x68003c00u, 0u, 0u, 0u};   // (1, 2048)
     u32x4 negm_blk = {0u, 0u, 0u, 0u};
-    // At d=64, when the chain's first block has zeroed leading pairs, the -m step rides in it
-    // instead: slot 0 of that block (pair 8jf: its first dim in half 0, its second in half 1)
-    // holds 2048 resp. 1 in the K operand and -hi resp. -lo in the Q operand (the pair's own
-    // term is then not in this MFMA, which it must not be anyway).  One MFMA less per sub-tile
-    // for two VALU operations: 2.6% faster at d=64, 1.9% slower at d=128 (where the MFMA
-    // stream dominates less), so d=128 keeps the separate step.
-    constexpr bool FOLD = D == 64;
+    // When the chain's first block has zeroed leading pairs, the -m step rides in it instead:
+    // slot 0 of that block (pair 8jf: its first dim in half 0, its second in half 1) holds 2048
+    // resp. 1 in the K operand and -hi resp. -lo in the Q operand (the pair's own term is then
+    // not in this MFMA, which it must not be anyway).  One MFMA less per sub-tile for two VALU
+    // bit merges: 2.6% faster at d=64, ~1% at d=128.
     const uint32_t kfold = h ? 0x3c00u : 0x6800u;            // 1, 2048 (half)
     uint32_t qfold = 0u;                                      // -lo, -hi (half)
     auto set_m = [&](float mv) {
@@ -506,8 +504,6 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
             f32x16 S;
             // the first active block's operands, with the -m step folded in when it can be
             auto first = [&](int j, f32x16 acc) {
-                if constexpr (!FOLD)
-                    return __builtin_amdgcn_mfma_f32_32x32x16_f16(K(j), __builtin_bit_cast(f16x8, qm()), acc, 0, 0, 0);
                 const uint32_t fm = (pfull & 7) ? 0xffffu : 0u;
                 u32x4 kj = __builtin_bit_cast(u32x4, K(j)), qj = qm();
                 kj[0] = (kj[0] & ~fm) | (kfold & fm);
@@ -666,7 +662,7 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
             sub = sub_top - i;
             const f32x16 T = raw(sub, true);
             // the -m step, unless the chain's first block carried it
-            const bool folded = FOLD && (pfull & 7) != 0 && (pfull >> 3) < NB;
+            const bool folded = (pfull & 7) != 0 && (pfull >> 3) < NB;
             f32x16 S;
             if (folded) S = T;
             else S = bias(T);
