@@ -55,7 +55,7 @@ extern "C" {
 enum {
     WPA_OK = 0,
     WPA_ERR_INVALID = -1,      /* argument out of range, null or misaligned pointer */
-    WPA_ERR_UNSUPPORTED = -2,  /* valid request this build does not implement (e.g. d) */
+    WPA_ERR_UNSUPPORTED = -2,  /* valid request this library does not implement (e.g. d) */
     WPA_ERR_WORKSPACE = -3,    /* workspace smaller than the matching *_bytes() query */
     WPA_ERR_HIP = -4           /* the HIP runtime reported an error while enqueueing */
 };
