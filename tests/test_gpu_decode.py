@@ -144,3 +144,22 @@ def test_decode_full_size_llama_batch():
     ro, _, _ = oracle.decode(synth.to_oracle(q), synth.to_oracle(k), synth.to_oracle(v), lens_h,
                              w.base, 1.0)
     check_close(out.float().cpu().numpy(), ro, "llama decode full size")
+
+
+def test_decode_full_size_qwen7b1m():
+    """The Qwen2.5-7B-1M-shaped decode step: one sequence at the full 1M-token context."""
+    need_gpu()
+    w = synth.WORKLOADS["qwen7b1m_decode"]
+    say("decode full size", w.name)
+    q, k, v, lens = synth.workload_inputs(w, device="cuda")
+    assert int(lens.min()) == w.N
+    cache = wpa.KVCache(w.B, w.N, w.Hkv, w.d, w.base)
+    cache.write(k, v, 0)
+    cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
+    out = wpa.decode(q, cache, lens, 1.0, term_count=cnt, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert int(cnt.item()) == w.B * w.Hq * wpa.count_terms(w.d, w.base, 1.0, 1, w.N - 1, w.N)[0]
+    say("oracle decode full size")
+    ro, _, _ = oracle.decode(synth.to_oracle(q), synth.to_oracle(k), synth.to_oracle(v),
+                             lens.cpu().numpy(), w.base, 1.0)
+    check_close(out.float().cpu().numpy(), ro, "qwen7b1m decode full size")

@@ -164,3 +164,24 @@ def test_full_size_sampled_rows(name, alpha):
                               w.base, alpha, rows=rows)
     check_close(got, ro, "%s sampled rows" % name)
     assert int(cnt.item()) == w.Hq * wpa.count_terms(w.d, w.base, alpha, w.N, 0, w.N)[0]
+
+
+def test_full_size_qwen7b1m_sampled_rows():
+    """The Qwen2.5-7B-1M-shaped prefill at its full 1M tokens, in the launch configuration the
+    sweep times: sampled query rows (first, last and random) against the oracle; exact
+    kept-term count (about 3.4e14 at this size)."""
+    need_gpu()
+    w = synth.WORKLOADS["qwen7b1m"]
+    say("full size", w.name, 1.0)
+    q, k, v = synth.workload_inputs(w, device="cuda")
+    cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
+    out = wpa.prefill(q, k, v, w.base, 1.0, term_count=cnt)
+    torch.cuda.synchronize()
+    rows = synth.sample_rows(w.N, 16, seed=w.seed)
+    got = out[:, torch.as_tensor(rows, device="cuda")].float().cpu().numpy()
+    del out
+    say("oracle rows", len(rows))
+    ro, _, _ = oracle.prefill(synth.to_oracle(q), synth.to_oracle(k), synth.to_oracle(v),
+                              w.base, 1.0, rows=rows)
+    check_close(got, ro, "qwen7b1m sampled rows")
+    assert int(cnt.item()) == w.Hq * wpa.count_terms(w.d, w.base, 1.0, w.N, 0, w.N)[0]
