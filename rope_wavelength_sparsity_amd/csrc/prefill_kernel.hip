@@ -423,13 +423,14 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
         for (int r = 0; r < 16; ++r) S[r] -= shift;
     };
     const int v_row = l32 * BN;                               // V^T row of this lane (db = 0)
-    const int v_x = (h ^ Tile<D>::swz(l32)) << 3;             // its slot swizzle, in elements
+    const uint32_t v_xb = (uint32_t)(h ^ Tile<D>::swz(l32)) << 4;   // its slot swizzle, in bytes
     auto pv = [&](int sub, int k0, const uint32_t (&wd)[8], const uint16_t* sV) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             const u32x4 pb = u32x4{wd[4 * c], wd[4 * c + 1], wd[4 * c + 2], wd[4 * c + 3]};
-            // chunk 4sub + 2c + h of row e sits in slot (4sub + 2c + h) ^ swz(e)
-            const uint16_t* vp = sV + v_row + ((((4 * sub + 2 * c) << 3)) ^ v_x);
+            // chunk 4sub + 2c + h of row e sits in slot (4sub + 2c + h) ^ swz(e): one xor-add
+            const uint16_t* vp = reinterpret_cast<const uint16_t*>(
+                reinterpret_cast<const char*>(sV + v_row) + (((uint32_t)(4 * sub + 2 * c) << 4) ^ v_xb));
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
                 bf16x8 a = *reinterpret_cast<const bf16x8*>(vp + 32 * db * BN);
