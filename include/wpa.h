@@ -249,7 +249,9 @@ int wpa_prefill_cached(const void* q, const void* k_cache, const void* v_cache,
  * Chunked prefill with a query count per sequence (varlen): sequence b's chunk is its last
  * q_b = cu_q[b+1] - cu_q[b] tokens (0 <= q_b <= max_q, q_b <= kv_len[b]; a sequence with
  * q_b = 0 is skipped), packed back to back.
- *   cu_q     [B+1] int32 device, non-decreasing: rows cu_q[b] .. cu_q[b+1]-1 of q and out
+ *   cu_q     [B+1] int32 device, non-decreasing from cu_q[0] >= 0: rows cu_q[b] ..
+ *            cu_q[b+1]-1 of q and out.  Its values are trusted (the library does not read
+ *            device memory on the host): offsets past the end of q/out are the caller's fault.
  *   q        [cu_q[B]][Hq][d] pre-RoPE;  out [cu_q[B]][Hq][d];  lse [cu_q[B]][Hq] or NULL
  *   max_q    an upper bound of every q_b (it sizes the launch; larger counts are clamped)
  * Each row is bit-identical to the same row of wpa_prefill_cached with Nq = q_b.
