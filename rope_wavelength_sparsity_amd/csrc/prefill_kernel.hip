@@ -661,12 +661,17 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
 #pragma unroll 1
         for (int i = 0; i < n_sub; ++i) {
             sub = sub_top - i;
+            // the QK chain at raised wave priority: the SIMD's arbiter then issues each
+            // dependent MFMA as soon as it can, and the other waves' softmax work fills the
+            // gaps (2% faster at both d; raising P*V as well, or the producer, gained less)
+            __builtin_amdgcn_s_setprio(1);
             const f32x16 T = raw(sub, true);
             // the -m step, unless the chain's first block carried it
             const bool folded = (pfull & 7) != 0 && (pfull >> 3) < NB;
             f32x16 S;
             if (folded) S = T;
             else S = bias(T);
+            __builtin_amdgcn_s_setprio(0);
             uint32_t wd[8];
             float psum = 0.f;
             bool redo = !started;
