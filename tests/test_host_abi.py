@@ -399,3 +399,13 @@ def test_prefill_varlen_needs_cu_q():
                                             2, 64, 8, 128, 8, 2, 128, 5e5, None, 1.0, 0.0, 0, 1,
                                             None, None)
     assert rc == wpa.WPA_ERR_INVALID
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without libwpa.so the binding raises: there is no fallback path."""
+    monkeypatch.setattr(wpa, "_lib", None)
+    monkeypatch.setattr(wpa, "LIB_PATH", str(tmp_path / "libwpa.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        wpa.lib()
+    with pytest.raises(RuntimeError, match="not built"):
+        wpa.count_terms(64, 1e4, 1.0, 16, 0, 16)
