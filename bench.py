@@ -1,21 +1,26 @@
 #!/usr/bin/env python3
 """Benchmark of per-RoPE-wavelength windowed attention on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
 
-Headline (`value`): windowed causal prefill of the Qwen2.5-0.5B-shaped layer (B=1, 14 q /
-2 kv heads, d=64, base 1e6, N=32768, alpha=1, bf16 synthetic inputs).  One step = the
-whole prefill path: key rotation/relayout + the attention kernel.  `value` is the
-algorithmic (active-term) TFLOP/s of that step, inputs resident in HBM:
+Headline workload: the Qwen2.5-7B-1M-shaped attention layer (28 q / 4 kv heads, d=128,
+rope base 1e7, alpha=1, bf16 synthetic N(0,1) tensors): a causal prefill of N = 1,048,576
+tokens plus one batch-1 decode step at 1M context.  One step is that whole path:
+key rotation/relayout (prefill_prepare) + windowed attention (prefill_attend) + the decode
+step (decode_partial + decode_combine) against a resident 1M-token cache.  `value` is the
+algorithmic (active-term) prefill TFLOP/s of the step, inputs resident in HBM:
     flops = B*Hq*(4*kept + 2*d*N(N+1)/2)
 where kept (per head) is the exact kept-term count and P*V stays full.
 
 Also reported on the same line:
-  roofline       the attention kernel alone (HIP events around its launch) vs bf16 MFMA peak
-  decode         one decode step of the Llama-3.2-3B-shaped batch (B=16, 24/8 heads, d=128,
-                 kv_len ~ U{8192..131072}), algorithmic KV bytes per second vs HBM peak
-  speedup_vs_full_window   the same kernels with alpha = inf, prefill and decode
-  cpu_baseline   the fp64 CPU oracle on a bounded sample of query rows of the same prefill
+  roofline       the attention kernel alone (HIP events around its launch on the launch
+                 stream) vs the bf16 MFMA peak
+  decode         the step's decode (Qwen2.5-7B-1M shape, L = 1M), algorithmic KV bytes/s
+                 vs the HBM peak; decode_batch: the Llama-3.2-3B-shaped batch (B=16, 24/8
+                 heads, kv_len ~ U{8192..131072}) timed in its own loop
+  speedup_vs_full_window   the same kernels with alpha = inf (fewer prefill repetitions)
+  cpu_baseline   the fp64 CPU oracle on a bounded sample of query rows of the same prefill,
+                 with the full prefill's CPU time extrapolated from it
 """
 from __future__ import annotations
 
@@ -41,9 +46,14 @@ def _parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="qwen05b", help="prefill workload (synth.WORKLOADS)")
+    ap.add_argument("--workload", default="qwen7b1m", help="prefill workload (synth.WORKLOADS)")
     ap.add_argument("--alpha", type=float, default=None, help="override the workload's alpha")
-    ap.add_argument("--decode-workload", default="llama3b_decode")
+    ap.add_argument("--decode-workload", default="qwen7b1m_decode",
+                    help="the decode step inside each timed step")
+    ap.add_argument("--decode-batch-workload", default="llama3b_decode",
+                    help="a second decode workload, timed in its own loop ('' to skip)")
+    ap.add_argument("--full-window-reps", type=int, default=2,
+                    help="timed prefill repetitions of the alpha = inf leg (after one warm-up)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-full-window", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -69,8 +79,53 @@ def _events(n):
     return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
 
 
-def bench_prefill(w, alpha, steps, warmup):
-    """Times `steps` prefill steps (prepare + attend).  Returns dict of timings."""
+def _prefill_flops(w, alpha, N=None):
+    import rope_wavelength_sparsity_amd as wpa
+    n = w.N if N is None else N
+    kept, _ = wpa.count_terms(w.d, w.base, alpha, n, 0, n)
+    return w.B * w.Hq * (4 * kept + 2 * w.d * n * (n + 1) // 2), kept
+
+
+def _decode_bytes(w, alpha, lens_h):
+    """Algorithmic bytes of one decode step: K at 2 bf16-sized values per kept pair, full V
+    rows, q in and out."""
+    import rope_wavelength_sparsity_amd as wpa
+    nbytes = 0
+    for L in lens_h:
+        kept, _ = wpa.count_terms(w.d, w.base, alpha, 1, L - 1, L)
+        nbytes += w.Hkv * (4 * kept + 2 * w.d * L)
+    return nbytes + 2 * 2 * w.B * w.Hq * w.d
+
+
+class DecodeState:
+    """A decode workload's query, lengths and resident KV cache (filled once, untimed)."""
+
+    def __init__(self, w):
+        import torch
+        import rope_wavelength_sparsity_amd as wpa
+        import synth
+        self.w = w
+        q, k, v, lens = synth.workload_inputs(w, device="cuda")
+        self.cache = wpa.KVCache(w.B, w.N, w.Hkv, w.d, w.base)
+        self.cache.write(k, v, 0)
+        del k, v
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        self.q, self.lens = q, lens
+        self.ws = torch.empty(max(wpa.decode_workspace_bytes(w.B, w.N, w.Hq, w.Hkv, w.d), 16),
+                              device="cuda", dtype=torch.uint8)
+        self.out = torch.empty_like(q)
+        self.lens_h = [int(x) for x in lens.cpu().tolist()]
+
+    def step(self, alpha):
+        import rope_wavelength_sparsity_amd as wpa
+        wpa.decode(self.q, self.cache, self.lens, alpha, out=self.out, workspace=self.ws)
+
+
+def bench_step(w, alpha, steps, warmup, dec):
+    """Times `steps` steps of the whole path: prefill_prepare + prefill_attend over the
+    prompt, then the decode step of `dec` (None: prefill only).  HIP events on the launch
+    stream bracket each part of every timed step.  Returns a dict of timings."""
     import torch
     import rope_wavelength_sparsity_amd as wpa
     import synth
@@ -78,84 +133,105 @@ def bench_prefill(w, alpha, steps, warmup):
     ws = torch.empty(wpa.prefill_workspace_bytes(w.B, w.N, w.Hkv, w.d), device="cuda",
                      dtype=torch.uint8)
     out = torch.empty_like(q)
-    ka, kb = _events(steps), _events(steps)
+    ev = [_events(4) for _ in range(steps)]
 
-    def step(i=None):
+    def step(e=None):
+        if e is not None:
+            e[0].record()
         wpa.prefill_prepare(k, v, w.base, workspace=ws)
-        if i is not None:
-            ka[i].record()
+        if e is not None:
+            e[1].record()
         wpa.prefill_attend(q, ws, w.Hkv, w.base, alpha, out=out)
-        if i is not None:
-            kb[i].record()
+        if e is not None:
+            e[2].record()
+        if dec is not None:
+            dec.step(alpha)
+        if e is not None:
+            e[3].record()
 
-    for _ in range(warmup):
+    slow = w.N >= (1 << 18)           # seconds per step: report progress as steps complete
+    for i in range(warmup):
         step()
+        if slow:
+            torch.cuda.synchronize()
+            _log("warm-up step %d/%d done" % (i + 1, warmup))
     torch.cuda.synchronize()
     t0, t1 = _events(2)
     w0 = time.perf_counter()
     t0.record()
     for i in range(steps):
-        step(i)
+        step(ev[i])
+        if slow and i > 0:
+            # step i is queued behind step i-1, so waiting for the end of step i-1 leaves the
+            # GPU busy while the host prints
+            ev[i - 1][3].synchronize()
+            _log("step %d/%d done" % (i, steps))
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    step_ms = t0.elapsed_time(t1) / steps
-    kern_ms = sum(a.elapsed_time(b) for a, b in zip(ka, kb)) / steps
-    kept, _ = wpa.count_terms(w.d, w.base, alpha, w.N, 0, w.N)
-    flops = w.B * w.Hq * (4 * kept + 2 * w.d * w.N * (w.N + 1) // 2)
+    avg = lambda a, b: sum(e[a].elapsed_time(e[b]) for e in ev) / steps
+    flops, kept = _prefill_flops(w, alpha)
+    res = {"step_ms": t0.elapsed_time(t1) / steps, "prepare_ms": avg(0, 1), "attend_ms": avg(1, 2),
+           "decode_ms": avg(2, 3), "wall_s": wall, "flops": flops, "kept_per_head": kept}
     del q, k, v, ws, out
     torch.cuda.empty_cache()
-    return {"step_ms": step_ms, "kernel_ms": kern_ms, "wall_s": wall, "flops": flops,
-            "kept_per_head": kept}
+    return res
 
 
-def bench_decode(w, alpha, steps, warmup):
+def bench_decode(dec, alpha, steps, warmup):
+    """Mean time of `steps` back-to-back decode steps (HIP events) after `warmup`."""
     import torch
-    import rope_wavelength_sparsity_amd as wpa
-    import synth
-    q, k, v, lens = synth.workload_inputs(w, device="cuda")
-    cache = wpa.KVCache(w.B, w.N, w.Hkv, w.d, w.base)
-    cache.write(k, v, 0)
-    del k, v
-    torch.cuda.synchronize()
-    torch.cuda.empty_cache()
-    ws = torch.empty(max(wpa.decode_workspace_bytes(w.B, w.N, w.Hq, w.Hkv, w.d), 16),
-                     device="cuda", dtype=torch.uint8)
-    out = torch.empty_like(q)
     for _ in range(warmup):
-        wpa.decode(q, cache, lens, alpha, out=out, workspace=ws)
+        dec.step(alpha)
     torch.cuda.synchronize()
     t0, t1 = _events(2)
     t0.record()
     for _ in range(steps):
-        wpa.decode(q, cache, lens, alpha, out=out, workspace=ws)
+        dec.step(alpha)
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
-    lens_h = [int(x) for x in lens.cpu().tolist()]
-    nbytes = 0
-    for L in lens_h:
-        kept, _ = wpa.count_terms(w.d, w.base, alpha, 1, L - 1, L)
-        nbytes += w.Hkv * (4 * kept + 2 * w.d * L)
-    nbytes += 2 * 2 * w.B * w.Hq * w.d                 # q in, out
-    del q, cache, ws, out
-    torch.cuda.empty_cache()
-    return {"ms": ms, "bytes": nbytes, "kv_len_mean": sum(lens_h) / len(lens_h)}
+    return {"ms": ms, "bytes": _decode_bytes(dec.w, alpha, dec.lens_h),
+            "kv_len_mean": sum(dec.lens_h) / len(dec.lens_h)}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(w, alpha, target_s):
-    """The fp64 oracle on sampled query rows of the same prefill (all heads)."""
+    """The unmodified fp64 oracle on a bounded sample of query rows (all heads) of the same
+    prefill, on the same input values (drawn on the device, copied to the host).  The rate is
+    algorithmic flops of the sampled rows per second; the full prefill's CPU time is
+    extrapolated from it (labelled as such)."""
     import numpy as np
+    import torch
     import oracle
     import rope_wavelength_sparsity_amd as wpa
     import synth
-    q, k, v = synth.workload_inputs(w, device="cpu")
+    q, k, v = synth.workload_inputs(w, device="cuda")
     qa, ka, va = synth.to_oracle(q), synth.to_oracle(k), synth.to_oracle(v)
+    del q, k, v
+    torch.cuda.empty_cache()
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
 
     def run(rows):
         t = time.perf_counter()
-        oracle.prefill(qa, ka, va, w.base, alpha, rows=rows)
+        oracle.prefill(qa, ka, va, w.base, alpha, rows=rows, nthreads=threads)
         return time.perf_counter() - t
+
+    def row_flops(rows):
+        f = 0
+        for r in rows.tolist():
+            kept, _ = wpa.count_terms(w.d, w.base, alpha, 1, r, r + 1)
+            f += w.B * w.Hq * (4 * kept + 2 * w.d * (r + 1))
+        return f
 
     rng = np.random.default_rng(12345)
     cal = np.sort(rng.integers(0, w.N, 8))
@@ -163,14 +239,13 @@ def cpu_baseline(w, alpha, target_s):
     n = int(max(8, min(4096, 8 * target_s / max(tc, 1e-3))))
     rows = np.sort(rng.integers(0, w.N, n))
     dt = run(rows)
-    flops = 0
-    for r in rows.tolist():
-        kept, _ = wpa.count_terms(w.d, w.base, alpha, 1, r, r + 1)
-        flops += w.B * w.Hq * (4 * kept + 2 * w.d * (r + 1))
-    cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": "%d random query rows x %d heads of %s (N=%d), fp64, %.1f s" % (
-                n, w.Hq, w.name, w.N, dt)}
+    rate = row_flops(rows) / dt
+    full, _ = _prefill_flops(w, alpha)
+    return {"value": rate / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": _cpu_model(),
+            "sample": "%d random query rows x %d heads of %s (N=%d), fp64, %.1f s (%.3f s per row "
+                      "on average, setup included)" % (n, w.Hq, w.name, w.N, dt, dt / n),
+            "full_prefill_s_extrapolated": full / rate}
 
 
 def _log(*a):
@@ -514,65 +589,99 @@ def main():
     w = synth.WORKLOADS[args.workload]
     assert w.kind == "prefill"
     alpha = args.alpha if args.alpha is not None else w.alphas[0]
-    print("# prefill %s alpha=%g" % (w.name, alpha), file=sys.stderr, flush=True)
-    pre = bench_prefill(w, alpha, args.steps, args.warmup)
+    dec = None
+    if not args.no_decode:
+        wd = synth.WORKLOADS[args.decode_workload]
+        _log("decode cache %s" % wd.name)
+        dec = DecodeState(wd)
+    _log("steps of %s alpha=%g%s" % (w.name, alpha, " + decode %s" % dec.w.name if dec else ""))
+    st = bench_step(w, alpha, args.steps, args.warmup, dec)
+    achieved = st["flops"] / (st["attend_ms"] * 1e-3) / 1e12
+    step_desc = "prefill_prepare (key rotation + relayout) + prefill_attend"
+    if dec is not None:
+        step_desc += " + one decode step (decode_partial + decode_combine) of %s" % dec.w.name
     res = {
         "metric": METRIC,
-        "value": pre["flops"] / (pre["step_ms"] * 1e-3) / 1e12,
+        "value": st["flops"] / (st["step_ms"] * 1e-3) / 1e12,
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": pre["step_ms"],
+        "ms_per_step": st["step_ms"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) tensors at the layer's shapes; no weights or datasets)",
-        "config": {"workload": "%s prefill: B=%d N=%d Hq=%d Hkv=%d d=%d base=%g alpha=%g" % (
-            w.name, w.B, w.N, w.Hq, w.Hkv, w.d, w.base, alpha),
-            "step": "prefill_prepare (key rotation + relayout) + prefill_attend",
-            "algorithmic_flops_per_step": pre["flops"],
-            "kept_terms_per_head": pre["kept_per_head"]},
+        "config": {"workload": "%s prefill: B=%d N=%d Hq=%d Hkv=%d d=%d base=%g alpha=%g%s" % (
+            w.name, w.B, w.N, w.Hq, w.Hkv, w.d, w.base, alpha,
+            (" + decode step B=%d L=%d" % (dec.w.B, max(dec.lens_h))) if dec else ""),
+            "step": step_desc,
+            "value_is": "prefill algorithmic flops per step / step time (the decode step adds "
+                        "%.4f ms to each step)" % st["decode_ms"],
+            "algorithmic_flops_per_step": st["flops"],
+            "kept_terms_per_head": st["kept_per_head"],
+            "step_parts_ms": {"prefill_prepare": st["prepare_ms"], "prefill_attend": st["attend_ms"],
+                              "decode": st["decode_ms"]}},
     }
-    achieved = pre["flops"] / (pre["kernel_ms"] * 1e-3) / 1e12
     res["roofline"] = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                        "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                        "traffic": _traffic("prefill_kernel.hip", w.name, alpha),
-                       "kernel": "prefill_kernel (attend)", "kernel_ms": pre["kernel_ms"]}
-    print("# prefill %.3f ms/step, attend %.3f ms, %.1f TFLOP/s" % (
-        pre["step_ms"], pre["kernel_ms"], achieved), file=sys.stderr, flush=True)
+                       "kernel": "prefill_kernel (attend)", "kernel_ms": st["attend_ms"]}
+    _log("step %.1f ms: prepare %.2f ms, attend %.1f ms (%.1f TFLOP/s), decode %.4f ms" % (
+        st["step_ms"], st["prepare_ms"], st["attend_ms"], achieved, st["decode_ms"]))
     speed = {}
-    if not args.no_full_window and not math.isinf(alpha):
-        print("# prefill full window", file=sys.stderr, flush=True)
-        full = bench_prefill(w, math.inf, args.steps, args.warmup)
-        speed["prefill_attend"] = full["kernel_ms"] / pre["kernel_ms"]
-        speed["prefill_step"] = full["step_ms"] / pre["step_ms"]
-        speed["prefill_full_window_kernel_ms"] = full["kernel_ms"]
-        speed["prefill_full_window_tflops_dense"] = full["flops"] / (full["kernel_ms"] * 1e-3) / 1e12
-    if not args.no_decode:
-        wd = synth.WORKLOADS[args.decode_workload]
-        print("# decode %s" % wd.name, file=sys.stderr, flush=True)
-        dec = bench_decode(wd, 1.0, args.steps, args.warmup)
-        gbs = dec["bytes"] / (dec["ms"] * 1e-3) / 1e9
-        res["decode"] = {"workload": "%s: B=%d Lmax=%d Hq=%d Hkv=%d d=%d base=%g alpha=1, "
-                                     "kv_len ~ U{%d..%d} (mean %.0f)" % (
-                                         wd.name, wd.B, wd.N, wd.Hq, wd.Hkv, wd.d, wd.base,
-                                         wd.len_lo, wd.N, dec["kv_len_mean"]),
-                         "value": gbs, "unit": "GB/s", "ms_per_step": dec["ms"],
-                         "algorithmic_bytes": dec["bytes"],
+    if dec is not None:
+        gbs = _decode_bytes(dec.w, alpha, dec.lens_h) / (st["decode_ms"] * 1e-3) / 1e9
+        res["decode"] = {"workload": "%s: B=%d L=%d Hq=%d Hkv=%d d=%d base=%g alpha=%g" % (
+                             dec.w.name, dec.w.B, max(dec.lens_h), dec.w.Hq, dec.w.Hkv, dec.w.d,
+                             dec.w.base, alpha),
+                         "value": gbs, "unit": "GB/s", "ms_per_step": st["decode_ms"],
+                         "timing": "HIP events around the decode launches inside each timed step",
+                         "algorithmic_bytes": _decode_bytes(dec.w, alpha, dec.lens_h),
                          "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
                                       "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
                                       "kernel": "decode_partial + decode_combine"}}
-        print("# decode %.3f ms, %.0f GB/s" % (dec["ms"], gbs), file=sys.stderr, flush=True)
+    if not args.no_full_window and not math.isinf(alpha):
+        _log("full window: %d + 1 steps" % args.full_window_reps)
+        full = bench_step(w, math.inf, args.full_window_reps, 1, dec)
+        speed["prefill_attend"] = full["attend_ms"] / st["attend_ms"]
+        speed["step"] = full["step_ms"] / st["step_ms"]
+        speed["prefill_full_window_attend_ms"] = full["attend_ms"]
+        speed["prefill_full_window_tflops_dense"] = full["flops"] / (full["attend_ms"] * 1e-3) / 1e12
+        speed["prefill_full_window_reps"] = args.full_window_reps
+        if dec is not None:
+            speed["decode"] = full["decode_ms"] / st["decode_ms"]
+            speed["decode_full_window_ms"] = full["decode_ms"]
+        _log("full window attend %.1f ms: speedup %.3f" % (full["attend_ms"], speed["prefill_attend"]))
+    del dec
+    torch.cuda.empty_cache()
+    if not args.no_decode and args.decode_batch_workload:
+        wb = synth.WORKLOADS[args.decode_batch_workload]
+        _log("decode batch %s" % wb.name)
+        db = DecodeState(wb)
+        r = bench_decode(db, alpha, args.steps, args.warmup)
+        gbs = r["bytes"] / (r["ms"] * 1e-3) / 1e9
+        res["decode_batch"] = {"workload": "%s: B=%d Lmax=%d Hq=%d Hkv=%d d=%d base=%g alpha=%g, "
+                                           "kv_len ~ U{%d..%d} (mean %.0f)" % (
+                                               wb.name, wb.B, wb.N, wb.Hq, wb.Hkv, wb.d, wb.base,
+                                               alpha, wb.len_lo, wb.N, r["kv_len_mean"]),
+                               "value": gbs, "unit": "GB/s", "ms_per_step": r["ms"],
+                               "algorithmic_bytes": r["bytes"],
+                               "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
+                                            "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                                            "kernel": "decode_partial + decode_combine"}}
+        _log("decode batch %.3f ms, %.0f GB/s" % (r["ms"], gbs))
         if not args.no_full_window:
-            decf = bench_decode(wd, math.inf, args.steps, args.warmup)
-            speed["decode"] = decf["ms"] / dec["ms"]
-            speed["decode_full_window_ms"] = decf["ms"]
+            rf = bench_decode(db, math.inf, args.steps, args.warmup)
+            speed["decode_batch"] = rf["ms"] / r["ms"]
+            speed["decode_batch_full_window_ms"] = rf["ms"]
+        del db
+        torch.cuda.empty_cache()
     if speed:
         res["speedup_vs_full_window"] = speed
     if not args.no_cpu_baseline:
-        print("# cpu baseline (oracle)", file=sys.stderr, flush=True)
+        _log("cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(w, alpha, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 

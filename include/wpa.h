@@ -63,8 +63,9 @@ enum {
 enum { WPA_BF16 = 0, WPA_FP32 = 1 };
 
 /*
- * Kept-term count, host only, exact (ATFlash abstract: the reduction rate is
- * input-independent with a closed form logarithmic in N).  A term is one pair's
+ * Kept-term count, host only, exact (ATFlash abstract: how many terms the window drops
+ * depends only on the shapes, d, base and alpha, not on the inputs, and the dropped share
+ * grows like log N).  A term is one pair's
  * contribution to one (query, key) score.  Queries sit at positions q_pos0 ..
  * q_pos0+n_q-1, keys at 0 .. n_k-1, key c visible to query r iff c <= r.
  *   *kept  = #{(r, c, i) visible : r - c <= alpha*lambda_i}
@@ -154,7 +155,9 @@ size_t wpa_decode_workspace_bytes(int32_t B, int64_t Lmax, int32_t Hq, int32_t H
  * kernel; far keys read only the pairs still active).
  *   q        [B][Hq][d] pre-RoPE query (dtype)
  *   k_cache, v_cache  written by wpa_kv_write for the same B, Lmax, Hkv, d, base
- *   kv_len   [B] int32 device, each in [1, Lmax]: the query sees keys 0 .. kv_len-1
+ *   kv_len   [B] int32 device: the query sees keys 0 .. kv_len-1.  The kernels clamp each
+ *            value into [0, Lmax] (no access leaves the caches, whatever the buffer holds); a
+ *            sequence whose clamped kv_len is 0 has no keys: its out is 0 and its lse -inf
  *   q_pos    [B] int32 device query positions, or NULL for kv_len-1 (the query's own
  *            token is then the last cached key)
  *   out      [B][Hq][d] (out_dtype);  lse [B][Hq] fp32 or NULL
@@ -162,8 +165,6 @@ size_t wpa_decode_workspace_bytes(int32_t B, int64_t Lmax, int32_t Hq, int32_t H
  *            choice.  The result depends on it only through rounding (probabilities
  *            enter the P*V product as bf16 relative to each split's running maximum).
  *   workspace at least wpa_decode_workspace_bytes(B, Lmax, Hq, Hkv, d, chunk_keys).
- * kv_len values outside [1, Lmax] are a precondition violation (not checked: they live
- * on the device).
  */
 int wpa_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* kv_len,
                const int32_t* q_pos, void* out, float* lse, int32_t B, int64_t Lmax,
@@ -270,12 +271,13 @@ int wpa_prefill_cached_varlen(const void* q, const void* k_cache, const void* v_
  * listed for (b, h, R), with the per-pair window on every listed key; keys of unlisted blocks
  * leave the softmax altogether (unlike pruned terms, which keep the key at logit 0).
  *   blk_count  int32 device [B][Hq][ceil(N/64)]: list lengths (clamped to [0, blk_max])
- *   blk_idx    int32 device [B][Hq][ceil(N/64)][blk_max]: key blocks in ascending order;
- *              entries outside [0, R) are ignored (R is always visited).  An unsorted list is a
- *              precondition violation (some of its blocks may be skipped).
+ *   blk_idx    int32 device [B][Hq][ceil(N/64)][blk_max]: key blocks, in any order;
+ *              duplicates count once, entries outside [0, R) are ignored (R is always visited).
  *   positions are token indices; other arguments as for wpa_prefill_ex (the workspace is
- *   prepared here).  term_count adds the kept terms of the visited keys.  N up to 2^21
- *   (WPA_ERR_UNSUPPORTED above: the lists are held as bitmaps in LDS).
+ *   prepared here).  term_count adds the kept terms of the visited keys.  The lists are held
+ *   as bitmaps in LDS beside the kernel's tiles: N up to 2^21 at d = 64 and up to about
+ *   9.1e5 tokens at d = 128; a longer N is WPA_ERR_UNSUPPORTED (checked before anything is
+ *   enqueued).
  */
 int wpa_prefill_sparse(const void* q, const void* k, const void* v, void* out, float* lse,
                        const int32_t* blk_count, const int32_t* blk_idx, int32_t blk_max,
@@ -341,8 +343,8 @@ int wpa_decode_window(const void* q, const void* k_cache, const void* v_cache,
  *   wpa_kv_write_paged  as wpa_kv_write_ex for tokens start .. start+n-1 of every sequence
  *                (start + n <= max_pages * page_size); a partly written V octet keeps its
  *                other tokens.  For one sequence, pass B = 1 and its block-table row.
- *   wpa_decode_paged    as wpa_decode_ex on the pools; kv_len[b] in [1, max_pages*page_size]
- *                (larger values are clamped to it).  Workspace:
+ *   wpa_decode_paged    as wpa_decode_ex on the pools, kv_len clamped into
+ *                [0, max_pages*page_size] (the table's reach).  Workspace:
  *                wpa_decode_workspace_bytes(B, max_pages*page_size, Hq, Hkv, d, chunk_keys).
  *   wpa_prefill_paged   as wpa_prefill_cached on the pools (Lmax = max_pages * page_size),
  *                bit-identical to it on contiguous caches holding the same tokens; needs

@@ -1,9 +1,10 @@
 """Per-RoPE-wavelength windowed causal attention on MI355X (gfx950).
 
 Thin ctypes binding over ``libwpa.so`` (C ABI in ``include/wpa.h``).  This module only
-marshals arguments: it checks tensor shapes/dtypes/devices, allocates outputs and
-workspace with torch when the caller does not pass them, and forwards raw device
-pointers and the current HIP stream.  Every step of the computation runs in the HIP
+marshals arguments: it checks the shape, dtype, device and contiguity of every tensor it
+is given (inputs and caller-supplied out, lse, workspace, counters, positions), allocates
+outputs and workspace with torch when the caller does not pass them, and forwards raw
+device pointers and the current HIP stream.  Every step of the computation runs in the HIP
 kernels behind the C ABI; there is no CPU or PyTorch fallback.  If the library is not
 built, every entry point raises.
 
@@ -209,6 +210,69 @@ def _dev(t, name):
         raise ValueError("%s must be a contiguous device tensor" % name)
 
 
+def _same_device(t, ref, name):
+    if t.device != ref.device:
+        raise ValueError("%s is on %s, the inputs on %s" % (name, t.device, ref.device))
+
+
+def _out(out, shape, ref, out_dtype):
+    """The output buffer: given (checked: shape, dtype, device, contiguity) or allocated."""
+    if out is None:
+        return torch.empty(tuple(shape), device=ref.device, dtype=out_dtype or ref.dtype)
+    _dev(out, "out")
+    _same_device(out, ref, "out")
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError("out must be %s, got %s" % (tuple(shape), tuple(out.shape)))
+    if out.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("out must be bfloat16 or float32")
+    return out
+
+
+def _lse(lse, want, shape, ref):
+    """The lse buffer: None, allocated when wanted, or a checked float32 [shape] tensor."""
+    if lse is None:
+        return torch.empty(tuple(shape), device=ref.device, dtype=torch.float32) if want else None
+    _dev(lse, "lse")
+    _same_device(lse, ref, "lse")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != tuple(shape):
+        raise ValueError("lse must be float32 %s" % (tuple(shape),))
+    return lse
+
+
+def _workspace(ws, need, ref):
+    """The workspace: given (a contiguous device buffer on the inputs' device, at least
+    `need` bytes; the library re-checks the size) or allocated."""
+    if ws is None:
+        return torch.empty(max(need, 16), device=ref.device, dtype=torch.uint8)
+    _dev(ws, "workspace")
+    _same_device(ws, ref, "workspace")
+    return ws
+
+
+def _ws_bytes(ws):
+    return ws.numel() * ws.element_size()
+
+
+def _counter(term_count, ref):
+    if term_count is None:
+        return None
+    _dev(term_count, "term_count")
+    _same_device(term_count, ref, "term_count")
+    if term_count.dtype != torch.int64 or term_count.numel() < 1:
+        raise ValueError("term_count must be an int64 device tensor of at least one element")
+    return term_count
+
+
+def _int32_vec(t, n, ref, name):
+    if t is None:
+        return None
+    _dev(t, name)
+    _same_device(t, ref, name)
+    if t.dtype != torch.int32 or t.numel() != n:
+        raise ValueError("%s must be int32 with %d elements" % (name, n))
+    return t
+
+
 # ------------------------------------------------------------------------------ host-only
 
 def count_terms(d: int, base: float, alpha: float, n_q: int, q_pos0: int, n_k: int, *,
@@ -270,20 +334,13 @@ def prefill(q, k, v, base: float, alpha: float, *, scale: float | None = None, p
     Hkv = k.shape[2]
     if k.shape[0] != B or k.shape[1] != N or k.shape[3] != d or not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k, v shapes/dtypes disagree")
-    if out is None:
-        out = torch.empty(q.shape, device=q.device, dtype=out_dtype or q.dtype)
-    _dev(out, "out")
-    if want_lse and lse is None:
-        lse = torch.empty((B, Hq, N), device=q.device, dtype=torch.float32)
-    if positions is not None:
-        _dev(positions, "positions")
-        if positions.dtype != torch.int32 or positions.numel() != B * N:
-            raise ValueError("positions must be int32 [B][N]")
-    if term_count is not None and (term_count.dtype != torch.int64 or not term_count.is_cuda):
-        raise ValueError("term_count must be an int64 device tensor")
-    need = prefill_workspace_bytes(B, N, Hkv, d)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), device=q.device, dtype=torch.uint8)
+    _same_device(k, q, "k")
+    _same_device(v, q, "v")
+    out = _out(out, q.shape, q, out_dtype)
+    lse = _lse(lse, want_lse, (B, Hq, N), q)
+    positions = _int32_vec(positions, B * N, q, "positions")
+    term_count = _counter(term_count, q)
+    workspace = _workspace(workspace, prefill_workspace_bytes(B, N, Hkv, d), q)
     rope, keep = _rope(d, inv_freq, pairs)
     if block_count is not None:
         # token-level block sparsity on top of the window (blocks of 64 tokens)
@@ -302,13 +359,13 @@ def prefill(q, k, v, base: float, alpha: float, *, scale: float | None = None, p
                                         B, N, Hq, Hkv, d, float(base), rope, float(alpha),
                                         float(scale) if scale is not None else 0.0,
                                         _dtype_code(q), _dtype_code(out), _ptr(term_count),
-                                        _ptr(workspace), workspace.numel(), _stream(stream)))
+                                        _ptr(workspace), _ws_bytes(workspace), _stream(stream)))
         return (out, lse) if lse is not None else out
     _check(lib().wpa_prefill_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(positions),
                                 B, N, Hq, Hkv, d, float(base), rope, float(alpha),
                                 float(scale) if scale is not None else 0.0, _dtype_code(q),
                                 _dtype_code(out), _ptr(term_count), _ptr(workspace),
-                                workspace.numel(), _stream(stream)))
+                                _ws_bytes(workspace), _stream(stream)))
     return (out, lse) if lse is not None else out
 
 
@@ -320,17 +377,13 @@ def prefill_prepare(k, v, base: float, *, positions=None, workspace=None, stream
     if k.dim() != 4 or k.shape != v.shape or k.dtype != v.dtype:
         raise ValueError("k, v must be [B][N][Hkv][d] of one dtype")
     B, N, Hkv, d = k.shape
-    if positions is not None:
-        _dev(positions, "positions")
-        if positions.dtype != torch.int32 or positions.numel() != B * N:
-            raise ValueError("positions must be int32 [B][N]")
-    need = prefill_workspace_bytes(B, N, Hkv, d)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), device=k.device, dtype=torch.uint8)
+    _same_device(v, k, "v")
+    positions = _int32_vec(positions, B * N, k, "positions")
+    workspace = _workspace(workspace, prefill_workspace_bytes(B, N, Hkv, d), k)
     rope, keep = _rope(d, inv_freq, pairs)
     _check(lib().wpa_prefill_prepare_ex(_ptr(k), _ptr(v), _ptr(positions), B, N, Hkv, d,
                                         float(base), rope, _dtype_code(k), _ptr(workspace),
-                                        workspace.numel(), _stream(stream)))
+                                        _ws_bytes(workspace), _stream(stream)))
     return workspace
 
 
@@ -339,21 +392,21 @@ def prefill_attend(q, workspace, Hkv: int, base: float, alpha: float, *, scale=N
                    term_count=None, stream=None, inv_freq=None, pairs: str = "half"):
     """Second half of prefill: windowed attention of q against a prepared workspace."""
     _dev(q, "q")
+    if q.dim() != 4:
+        raise ValueError("q must be [B][N][Hq][d]")
     _dev(workspace, "workspace")
+    _same_device(workspace, q, "workspace")
     B, N, Hq, d = q.shape
-    if out is None:
-        out = torch.empty(q.shape, device=q.device, dtype=out_dtype or q.dtype)
-    _dev(out, "out")
-    if want_lse and lse is None:
-        lse = torch.empty((B, Hq, N), device=q.device, dtype=torch.float32)
-    if positions is not None:
-        _dev(positions, "positions")
+    out = _out(out, q.shape, q, out_dtype)
+    lse = _lse(lse, want_lse, (B, Hq, N), q)
+    positions = _int32_vec(positions, B * N, q, "positions")
+    term_count = _counter(term_count, q)
     rope, keep = _rope(d, inv_freq, pairs)
     _check(lib().wpa_prefill_attend_ex(_ptr(q), _ptr(out), _ptr(lse), _ptr(positions), B, N, Hq,
                                        Hkv, d, float(base), rope, float(alpha),
                                        float(scale) if scale is not None else 0.0, _dtype_code(q),
                                        _dtype_code(out), _ptr(term_count), _ptr(workspace),
-                                       workspace.numel(), _stream(stream)))
+                                       _ws_bytes(workspace), _stream(stream)))
     return (out, lse) if lse is not None else out
 
 
@@ -469,6 +522,8 @@ def decode(q, cache, kv_len, alpha: float, *, q_pos=None, scale: float | None = 
     a PagedKVCache (with `block_table` [B][max_pages], or the cache's default table)."""
     _dev(q, "q")
     _dev(kv_len, "kv_len")
+    if q.dim() != 3:
+        raise ValueError("q must be [B][Hq][d]")
     B, Hq, d = q.shape
     paged = isinstance(cache, PagedKVCache)
     if paged:
@@ -478,18 +533,13 @@ def decode(q, cache, kv_len, alpha: float, *, q_pos=None, scale: float | None = 
         nseq, lmax = cache.B, cache.Lmax
     if B != nseq or d != cache.d or kv_len.dtype != torch.int32 or kv_len.numel() != B:
         raise ValueError("q [B][Hq][d] and kv_len int32 [B] must match the cache")
-    if q_pos is not None:
-        _dev(q_pos, "q_pos")
-        if q_pos.dtype != torch.int32 or q_pos.numel() != B:
-            raise ValueError("q_pos must be int32 [B]")
-    if out is None:
-        out = torch.empty(q.shape, device=q.device, dtype=out_dtype or q.dtype)
-    _dev(out, "out")
-    if want_lse and lse is None:
-        lse = torch.empty((B, Hq), device=q.device, dtype=torch.float32)
-    need = decode_workspace_bytes(B, lmax, Hq, cache.Hkv, d, chunk_keys)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), device=q.device, dtype=torch.uint8)
+    _same_device(kv_len, q, "kv_len")
+    _same_device(cache.k, q, "the cache")
+    q_pos = _int32_vec(q_pos, B, q, "q_pos")
+    out = _out(out, q.shape, q, out_dtype)
+    lse = _lse(lse, want_lse, (B, Hq), q)
+    term_count = _counter(term_count, q)
+    workspace = _workspace(workspace, decode_workspace_bytes(B, lmax, Hq, cache.Hkv, d, chunk_keys), q)
     rope, keep = _rope(d, cache.inv_freq, cache.pairs)
     if paged:
         _check(lib().wpa_decode_paged(_ptr(q), _ptr(cache.k), _ptr(cache.v), _ptr(table),
@@ -498,7 +548,7 @@ def decode(q, cache, kv_len, alpha: float, *, q_pos=None, scale: float | None = 
                                       cache.Hkv, d, cache.base, rope, float(alpha),
                                       float(scale) if scale is not None else 0.0,
                                       _dtype_code(q), _dtype_code(out), _ptr(term_count),
-                                      int(chunk_keys), _ptr(workspace), workspace.numel(),
+                                      int(chunk_keys), _ptr(workspace), _ws_bytes(workspace),
                                       _stream(stream)))
         return (out, lse) if lse is not None else out
     if cache.window_alpha is not None:
@@ -509,14 +559,14 @@ def decode(q, cache, kv_len, alpha: float, *, q_pos=None, scale: float | None = 
                                        cache.base, rope, cache.window_alpha, float(alpha),
                                        float(scale) if scale is not None else 0.0,
                                        _dtype_code(q), _dtype_code(out), _ptr(term_count),
-                                       int(chunk_keys), _ptr(workspace), workspace.numel(),
+                                       int(chunk_keys), _ptr(workspace), _ws_bytes(workspace),
                                        _stream(stream)))
         return (out, lse) if lse is not None else out
     _check(lib().wpa_decode_ex(_ptr(q), _ptr(cache.k), _ptr(cache.v), _ptr(kv_len), _ptr(q_pos),
                                _ptr(out), _ptr(lse), B, cache.Lmax, Hq, cache.Hkv, d, cache.base,
                                rope, float(alpha), float(scale) if scale is not None else 0.0,
                                _dtype_code(q), _dtype_code(out), _ptr(term_count),
-                               int(chunk_keys), _ptr(workspace), workspace.numel(),
+                               int(chunk_keys), _ptr(workspace), _ws_bytes(workspace),
                                _stream(stream)))
     return (out, lse) if lse is not None else out
 
@@ -536,6 +586,8 @@ def prefill_cached(q, cache, kv_len, alpha: float, *, scale: float | None = None
                                want_lse, term_count, stream, block_table)
     _dev(q, "q")
     _dev(kv_len, "kv_len")
+    if q.dim() != 4:
+        raise ValueError("q must be [B][Nq][Hq][d]")
     B, Nq, Hq, d = q.shape
     paged = isinstance(cache, PagedKVCache)
     if paged:
@@ -547,11 +599,11 @@ def prefill_cached(q, cache, kv_len, alpha: float, *, scale: float | None = None
         raise ValueError("q [B][Nq][Hq][d] and kv_len int32 [B] must match the cache")
     if cache.window_alpha is not None:
         raise ValueError("chunked prefill needs the dense cache (window_alpha=None)")
-    if out is None:
-        out = torch.empty(q.shape, device=q.device, dtype=out_dtype or q.dtype)
-    _dev(out, "out")
-    if want_lse and lse is None:
-        lse = torch.empty((B, Hq, Nq), device=q.device, dtype=torch.float32)
+    _same_device(kv_len, q, "kv_len")
+    _same_device(cache.k, q, "the cache")
+    out = _out(out, q.shape, q, out_dtype)
+    lse = _lse(lse, want_lse, (B, Hq, Nq), q)
+    term_count = _counter(term_count, q)
     rope, keep = _rope(d, cache.inv_freq, cache.pairs)
     sc = float(scale) if scale is not None else 0.0
     if paged:
@@ -590,11 +642,12 @@ def _prefill_varlen(q, cache, kv_len, alpha, cu_q, max_q, scale, out, out_dtype,
         raise ValueError("kv_len must hold one length per cache sequence")
     if d != cache.d or cache.window_alpha is not None:
         raise ValueError("q must match the (dense) cache")
-    if out is None:
-        out = torch.empty(q.shape, device=q.device, dtype=out_dtype or q.dtype)
-    _dev(out, "out")
-    if want_lse and lse is None:
-        lse = torch.empty((rows, Hq), device=q.device, dtype=torch.float32)
+    _same_device(kv_len, q, "kv_len")
+    _same_device(cu_q, q, "cu_q")
+    _same_device(cache.k, q, "the cache")
+    out = _out(out, q.shape, q, out_dtype)
+    lse = _lse(lse, want_lse, (rows, Hq), q)
+    term_count = _counter(term_count, q)
     rope, keep = _rope(d, cache.inv_freq, cache.pairs)
     sc = float(scale) if scale is not None else 0.0
     if paged:

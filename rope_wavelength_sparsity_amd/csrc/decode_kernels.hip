@@ -36,6 +36,12 @@ __device__ inline int perm_row(int m) {
     return (m & ~0xC) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
 
+// A sequence's key count as the kernels use it: kv_len clamped into [0, Lmax].
+__device__ inline int clamp_len(int32_t len, int64_t Lmax) {
+    const int l = __builtin_amdgcn_readfirstlane(len);
+    return l < 0 ? 0 : (l > Lmax ? (int)Lmax : l);
+}
+
 __device__ inline float xchg32(float v, int xaddr) {
     return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(xaddr, __builtin_bit_cast(int, v)));
 }
@@ -57,8 +63,9 @@ void decode_partial_kernel(DecodeParams p, Tables tab) {
     const int chunk = blockIdx.x % p.n_chunks;
     const int bg = blockIdx.x / p.n_chunks;
     const int g = bg % p.Hkv, b = bg / p.Hkv;
-    int Lb = __builtin_amdgcn_readfirstlane(p.kv_len[b]);
-    if constexpr (PAGED) Lb = Lb < p.Lmax ? Lb : (int)p.Lmax;   // the table's reach
+    // kv_len is clamped into [0, Lmax] (the caches' or the block table's reach), so no access
+    // leaves the caches whatever the device holds; a sequence with no keys writes no partial
+    const int Lb = clamp_len(p.kv_len[b], p.Lmax);
     const int key_lo = chunk * p.chunk;
     if (key_lo >= Lb) return;
     const int key_hi = key_lo + p.chunk < Lb ? key_lo + p.chunk : Lb;
@@ -334,8 +341,18 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
     const int b = bh / p.Hq, hq = bh % p.Hq;
     const int G = p.Hq / p.Hkv;
     const int g = hq / G, hh = hq % G;
-    const int64_t Lb = __builtin_amdgcn_readfirstlane(p.kv_len[b]);
-    const int nc = (int)((Lb + p.chunk - 1) / p.chunk);
+    const int64_t Lb = clamp_len(p.kv_len[b], p.Lmax);
+    const int nc = (int)((Lb + p.chunk - 1) / p.chunk);        // <= n_chunks
+    if (nc == 0) {
+        // no keys (kv_len <= 0): nothing to attend to; out = 0, lse = -inf
+        if (tid < 32) {
+            const int64_t oi = ((int64_t)b * p.Hq + hq) * D + slice * 32 + tid;
+            if (p.out_f32) static_cast<float*>(p.out)[oi] = 0.f;
+            else static_cast<uint16_t*>(p.out)[oi] = 0;
+            if (p.lse && slice == 0 && tid == 0) p.lse[(int64_t)b * p.Hq + hq] = -INFINITY;
+        }
+        return;
+    }
     const float* base = p.partial + ((int64_t)(b * p.Hkv + g) * p.n_chunks) * G * (D + 2) + hh * (D + 2);
     const int64_t cstride = (int64_t)G * (D + 2);
 

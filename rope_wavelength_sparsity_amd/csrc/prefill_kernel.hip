@@ -813,6 +813,33 @@ int device_cus() {
     return n;
 }
 
+// Dynamic LDS of a block-sparse launch: one bitmap of ceil(N/64) bits per compute wave (a
+// workgroup takes maxw row groups of one q head) and their union, in 32-bit words.
+template <int D>
+size_t sparse_bitmap_bytes(int64_t N) {
+    const size_t words = (size_t)(((N + 63) / 64 + 31) / 32);
+    return (size_t)(Tile<D>::maxw(false) + 1) * words * 4;
+}
+
+// LDS a block-sparse launch of N tokens needs (the kernel's static arrays plus the bitmaps)
+// and the device's per-workgroup limit.
+template <int D, bool F32>
+hipError_t sparse_lds_d(const PrefillParams& p, size_t* need, size_t* limit) {
+    hipFuncAttributes attr;
+    hipError_t e = p.counter
+        ? hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&prefill_kernel<D, F32, false, true, false, true>))
+        : hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&prefill_kernel<D, F32, false, false, false, true>));
+    if (e != hipSuccess) return e;
+    int dev = 0, lim = 0;
+    e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&lim, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+    if (e != hipSuccess) return e;
+    *need = attr.sharedSizeBytes + sparse_bitmap_bytes<D>(p.N);
+    *limit = (size_t)lim;
+    return hipSuccess;
+}
+
 template <int D, bool F32>
 hipError_t launch_d(const PrefillParams& p, const Tables& t, hipStream_t s) {
     const int G = p.Hq / p.Hkv;
@@ -881,10 +908,9 @@ hipError_t launch_d(const PrefillParams& p, const Tables& t, hipStream_t s) {
             else prefill_kernel<D, F32, false, false, true, false><<<grid, block, 0, s>>>(p, t, L);
         }
     } else if (p.blk_count) {
-        // block bitmaps: one per compute wave and their union
-        const size_t words = (size_t)(((p.N + 63) / 64 + 31) / 32);
-        const size_t bits = (size_t)(L.Gc * L.R + 1) * words * 4;
-        if (bits > 65536) return hipErrorInvalidValue;
+        // block bitmaps: one per compute wave and their union (the caller has checked that
+        // they fit next to the kernel's static LDS: sparse_lds)
+        const size_t bits = sparse_bitmap_bytes<D>(p.N);
         if (cn) prefill_kernel<D, F32, false, true, false, true><<<grid, block, bits, s>>>(p, t, L);
         else prefill_kernel<D, F32, false, false, false, true><<<grid, block, bits, s>>>(p, t, L);
     } else if (hp && cn) prefill_kernel<D, F32, true, true, false, false><<<grid, block, 0, s>>>(p, t, L);
@@ -895,6 +921,11 @@ hipError_t launch_d(const PrefillParams& p, const Tables& t, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t prefill_sparse_lds(const PrefillParams& p, size_t* need, size_t* limit) {
+    if (p.d == 64) return p.in_f32 ? sparse_lds_d<64, true>(p, need, limit) : sparse_lds_d<64, false>(p, need, limit);
+    return p.in_f32 ? sparse_lds_d<128, true>(p, need, limit) : sparse_lds_d<128, false>(p, need, limit);
+}
 
 hipError_t launch_prefill(const PrefillParams& p, const Tables& t, hipStream_t s) {
     if (!p.kv_len && (p.Np % Tile<64>::BN || p.Np % Tile<128>::BN)) return hipErrorInvalidValue;

@@ -412,6 +412,20 @@ int wpa_prefill_sparse(const void* q, const void* k, const void* v, void* out, f
         return fail(WPA_ERR_INVALID, "q, k, v and out must be 16-byte aligned");
     rc = check_prefill_shape(N, B, Hkv, dtype, nullptr, workspace, ws_bytes, d);
     if (rc) return rc;
+    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(WPA_ERR_INVALID, "lse must be 4-byte aligned");
+    if (term_count && (reinterpret_cast<uintptr_t>(term_count) & 7u)) return fail(WPA_ERR_INVALID, "term_count must be 8-byte aligned");
+    {
+        // the lists live in LDS as bitmaps next to the kernel's tiles: check the fit before
+        // anything is enqueued (at d = 128 this bounds N below 2^21)
+        wpa::PrefillParams pp{};
+        pp.d = d; pp.in_f32 = dtype == WPA_FP32; pp.N = N; pp.counter = term_count;
+        size_t need = 0, limit = 0;
+        hipError_t e = wpa::prefill_sparse_lds(pp, &need, &limit);
+        if (e != hipSuccess) return fail(WPA_ERR_HIP, "block-sparse LDS query: %s", hipGetErrorString(e));
+        if (need > limit)
+            return fail(WPA_ERR_UNSUPPORTED, "block-sparse prefill of %lld tokens at d=%d needs %zu bytes of LDS per "
+                        "workgroup (limit %zu)", (long long)N, d, need, limit);
+    }
     rc = wpa_prefill_prepare_ex(k, v, nullptr, B, N, Hkv, d, base, rope, dtype, workspace,
                                 ws_bytes, stream);
     if (rc) return rc;

@@ -103,6 +103,9 @@ struct DecodeParams {
 
 hipError_t launch_rope_relayout(const RopeParams& p, hipStream_t s);
 hipError_t launch_prefill(const PrefillParams& p, const Tables& t, hipStream_t s);
+// LDS bytes a block-sparse prefill launch for p (d, dtype, N, counter) needs, and the
+// device's per-workgroup limit; nothing is enqueued.
+hipError_t prefill_sparse_lds(const PrefillParams& p, size_t* need, size_t* limit);
 hipError_t launch_decode(const DecodeParams& p, const Tables& t, hipStream_t s);
 
 }  // namespace wpa

@@ -409,3 +409,81 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
         wpa.lib()
     with pytest.raises(RuntimeError, match="not built"):
         wpa.count_terms(64, 1e4, 1.0, 16, 0, 16)
+
+
+# ---------------------------------------------------------------- binding argument checks
+# The binding must reject a wrongly shaped or typed caller buffer before any library call.
+# CPU tensors stand in for device tensors here: the device test is relaxed to contiguity.
+
+@pytest.fixture
+def cpu_as_device(monkeypatch):
+    import torch
+
+    def dev(t, name):
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+    monkeypatch.setattr(wpa, "_dev", dev)
+
+    def no_call(*a, **k):
+        raise AssertionError("a rejected call reached the library")
+    for name in ("wpa_prefill_ex", "wpa_prefill_attend_ex", "wpa_prefill_prepare_ex", "wpa_decode_ex",
+                 "wpa_prefill_cached", "wpa_prefill_sparse"):
+        monkeypatch.setattr(wpa.lib(), name, no_call)
+    return torch
+
+
+def _pf(torch, B=1, N=64, Hq=4, Hkv=2, d=64):
+    q = torch.zeros((B, N, Hq, d), dtype=torch.bfloat16)
+    k = torch.zeros((B, N, Hkv, d), dtype=torch.bfloat16)
+    return q, k, k.clone()
+
+
+@pytest.mark.parametrize("case", ["out_shape", "out_dtype", "lse_shape", "lse_dtype", "count_empty",
+                                  "count_dtype", "positions_dtype", "positions_size"])
+def test_binding_rejects_bad_prefill_buffers(cpu_as_device, case):
+    torch = cpu_as_device
+    q, k, v = _pf(torch)
+    kw = {}
+    if case == "out_shape":
+        kw["out"] = torch.empty((1, 64, 4, 32), dtype=torch.bfloat16)
+    elif case == "out_dtype":
+        kw["out"] = torch.empty((1, 64, 4, 64), dtype=torch.float16)
+    elif case == "lse_shape":
+        kw["lse"] = torch.empty((1, 64, 4), dtype=torch.float32)
+    elif case == "lse_dtype":
+        kw["lse"] = torch.empty((1, 4, 64), dtype=torch.bfloat16)
+    elif case == "count_empty":
+        kw["term_count"] = torch.empty((0,), dtype=torch.int64)
+    elif case == "count_dtype":
+        kw["term_count"] = torch.zeros((1,), dtype=torch.int32)
+    elif case == "positions_dtype":
+        kw["positions"] = torch.zeros((1, 64), dtype=torch.int64)
+    elif case == "positions_size":
+        kw["positions"] = torch.zeros((1, 63), dtype=torch.int32)
+    with pytest.raises(ValueError):
+        wpa.prefill(q, k, v, 1e4, 1.0, **kw)
+    ws = torch.empty(wpa.prefill_workspace_bytes(1, 64, 2, 64), dtype=torch.uint8)
+    if case.startswith(("out", "lse", "count", "positions")):
+        with pytest.raises(ValueError):
+            wpa.prefill_attend(q, ws, 2, 1e4, 1.0, **kw)
+
+
+def test_binding_rejects_bad_decode_buffers(cpu_as_device, monkeypatch):
+    torch = cpu_as_device
+
+    class FakeCache:                      # a dense cache's attributes, host memory
+        B, Lmax, Hkv, d, base, inv_freq, pairs, window_alpha = 2, 256, 2, 64, 1e4, None, "half", None
+        k = torch.empty(16, dtype=torch.uint8)
+        v = torch.empty(16, dtype=torch.uint8)
+    q = torch.zeros((2, 4, 64), dtype=torch.bfloat16)
+    lens = torch.full((2,), 100, dtype=torch.int32)
+    bad = [dict(out=torch.empty((2, 4, 32), dtype=torch.bfloat16)),
+           dict(lse=torch.empty((4, 2), dtype=torch.float32)),
+           dict(lse=torch.empty((2, 4), dtype=torch.float64)),
+           dict(term_count=torch.empty((0,), dtype=torch.int64)),
+           dict(q_pos=torch.zeros((3,), dtype=torch.int32))]
+    for kw in bad:
+        with pytest.raises(ValueError):
+            wpa.decode(q, FakeCache(), lens, 1.0, **kw)
+    with pytest.raises(ValueError):                          # q of the wrong rank
+        wpa.decode(q[0], FakeCache(), lens, 1.0)

@@ -8,7 +8,7 @@ Sources:
   ATFlash abstract ("Per-RoPE-Wavelength Attention Windows for Compute/Memory-Efficient
   LLM Inference"): exact decomposition over 2-D rotation pairs; pruning beyond a
   wavelength-proportional distance; every key reachable through low-frequency pairs;
-  closed-form reduction rate logarithmic in N; online softmax untouched.
+  a dropped share fixed by the shapes alone that grows like log N; online softmax untouched.
   WavePrune original abstract ("One period is often enough for RoPE"): alpha=1 is the
   first rotation period.
   "The Heterogeneous Feature of RoPE-based Attention", Explanation: the critical
@@ -170,8 +170,8 @@ def test_two_token_window_edge(tk, alpha_steps, kept_far):
 
 
 def test_shift_invariance():
-    """RoPE scores depend on positions only through differences (WavePrune abstract:
-    'invariant to a common shift of positions'); the window does too."""
+    """RoPE scores depend on positions only through their difference (WavePrune, original
+    abstract); the window, a test on that difference, keeps this property."""
     N = 64
     q, k, v = synth.prefill_inputs(1, N, 2, 2, 32, "fp32", seed=12)
     a = [synth.to_oracle(t) for t in (q, k, v)]
@@ -277,7 +277,8 @@ def test_count_matches_attention_tally():
 
 @pytest.mark.parametrize("d,base", [(128, 5e5), (64, 1e6), (128, 1e7)])
 def test_pruned_fraction_grows_logarithmically(d, base):
-    """ATFlash abstract: the reduction rate has a closed form logarithmic in N.  Once
+    """ATFlash abstract: the dropped share of terms depends on the shapes alone and grows
+    like log N.  Once
     every short-wavelength pair is well inside N, doubling N adds ln 2 / ln base to the
     pruned fraction (pairs are spaced ln(base)*2/d apart in ln(lambda))."""
     slope = math.log(2.0) / math.log(base)
