@@ -54,13 +54,14 @@ def _load():
         build()
         lib = ctypes.CDLL(_LIB)
         P, I, I64, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
-        lib.orc_prefill_ex.argtypes = [P, P, P, I, P, I, I64, I, I, I, D, P, I, D, D, P, I64, P, P,
-                                       P, I]
+        lib.orc_prefill_ex.argtypes = [P, P, P, I, P, I, I64, I, I, I, D, P, I, I, D, D, P, I64, P,
+                                       P, P, I]
         lib.orc_prefill_ex.restype = I
         lib.orc_prefill_sparse.argtypes = [P, P, P, I, I, I64, I, I, I, D, P, I, D, D, P, P, I, I,
                                            P, I64, P, P, P, I]
         lib.orc_prefill_sparse.restype = I
-        lib.orc_decode_ex.argtypes = [P, P, P, I, P, P, I, I64, I, I, I, D, P, I, D, D, P, P, P, I]
+        lib.orc_decode_ex.argtypes = [P, P, P, I, P, P, I, I64, I, I, I, D, P, I, I, D, D, P, P, P,
+                                      I]
         lib.orc_decode_ex.restype = I
         lib.orc_rope_ex.argtypes = [P, I, I64, I, I, P, D, P, I, P]
         lib.orc_rope_ex.restype = None
@@ -98,6 +99,19 @@ def _freq(inv_freq, d):
     return f
 
 
+def _freq_heads(inv_freq, d, Hkv):
+    """(table, number of tables): None; one shared d/2 table; or one row per kv head,
+    [Hkv][d/2] (per-head frequencies)."""
+    if inv_freq is None:
+        return None, 0
+    f = np.ascontiguousarray(inv_freq, dtype=np.float64)
+    if f.ndim == 1:
+        assert f.shape == (d // 2,)
+        return f, 1
+    assert f.shape == (Hkv, d // 2), f.shape
+    return f, Hkv
+
+
 def thresholds(d: int, base: float, alpha: float, inv_freq=None) -> np.ndarray:
     """alpha*lambda_i for i < d/2, in double (may be +inf); lambda_i = 2*pi*base^(2i/d), or
     2*pi/th_i for a given frequency table."""
@@ -120,8 +134,9 @@ def rope(x, pos, base: float, inv_freq=None, layout: str = "half") -> np.ndarray
 def prefill(q, k, v, base: float, alpha: float, scale: float | None = None, pos=None,
             rows=None, nthreads: int = 0, inv_freq=None, layout: str = "half"):
     """Causal windowed prefill.  q [B][N][Hq][d], k/v [B][N][Hkv][d] (same dtype).
-    inv_freq: optional d/2 rotation frequencies (else base^(-2i/d)); layout: "half"
-    (pair i = dims i, i+d/2) or "interleaved" (dims 2i, 2i+1).
+    inv_freq: optional d/2 rotation frequencies (else base^(-2i/d)), or [Hkv][d/2], one row
+    per kv head (its q heads use the same row); layout: "half" (pair i = dims i, i+d/2) or
+    "interleaved" (dims 2i, 2i+1).
 
     Returns (out [B][R][Hq][d], lse [B][Hq][R], kept) in fp64, R = len(rows) or N.
     """
@@ -143,8 +158,9 @@ def prefill(q, k, v, base: float, alpha: float, scale: float | None = None, pos=
     out = np.empty((B, R, Hq, d), dtype=np.float64)
     lse = np.empty((B, Hq, R), dtype=np.float64)
     kept = ctypes.c_int64(0)
+    tab, ntab = _freq_heads(inv_freq, d, Hkv)
     rc = _load().orc_prefill_ex(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(pos), B, N, Hq, Hkv, d,
-                                float(base), _ptr(_freq(inv_freq, d)), LAYOUTS[layout],
+                                float(base), _ptr(tab), ntab, LAYOUTS[layout],
                                 float(alpha), float(scale), _ptr(rows), R,
                                 _ptr(out), _ptr(lse), ctypes.byref(kept), int(nthreads))
     if rc != 0:
@@ -207,8 +223,9 @@ def decode(q, k, v, kv_len, base: float, alpha: float, scale: float | None = Non
     out = np.empty((B, Hq, d), dtype=np.float64)
     lse = np.empty((B, Hq), dtype=np.float64)
     kept = ctypes.c_int64(0)
+    tab, ntab = _freq_heads(inv_freq, d, Hkv)
     rc = _load().orc_decode_ex(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(kv_len), _ptr(q_pos), B, Lmax,
-                               Hq, Hkv, d, float(base), _ptr(_freq(inv_freq, d)), LAYOUTS[layout],
+                               Hq, Hkv, d, float(base), _ptr(tab), ntab, LAYOUTS[layout],
                                float(alpha), float(scale), _ptr(out), _ptr(lse),
                                ctypes.byref(kept), int(nthreads))
     if rc != 0:

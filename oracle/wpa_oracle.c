@@ -39,6 +39,11 @@
  * alpha * ((2.0*M_PI) / th_i); and the interleaved pair layout, pair i = dims
  * (2i, 2i+1), rotated by the same formulas.
  *
+ * Per-head frequencies (AdaRoPE, on the cards page: rotation frequencies chosen per
+ * head): with n_tables = Hkv the table is [Hkv][d/2] and kv head g, with the q heads that
+ * read it (h / (Hq/Hkv) = g), rotates and windows by its own row, lambda_{g,i} =
+ * 2*pi/th_{g,i}.  n_tables = 0 or 1 is the shared table (or base) above.
+ *
  * Inputs are the exact values the GPU consumes (bf16 bit patterns as uint16, or
  * fp32); step 1 upcasts them to double.  All arithmetic is double.
  */
@@ -114,6 +119,51 @@ void orc_rope(const void* x, int dtype, int64_t n_tok, int H, int d,
     orc_rope_ex(x, dtype, n_tok, H, d, pos, base, NULL, 0, out);
 }
 
+/* Step 3 with one frequency table per group of heads: head h of x[n_tok][H][d] rotates by
+ * row h / heads_per_table of tables[][d/2]. */
+static void orc_rope_heads(const void* x, int dtype, int64_t n_tok, int H, int d,
+                           const int64_t* pos, const double* tables, int heads_per_table,
+                           int interleaved, double* out) {
+    int P = d / 2;
+    #pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < n_tok; ++t) {
+        for (int h = 0; h < H; ++h) {
+            const double* th = tables + (int64_t)(h / heads_per_table) * P;
+            int64_t row = (t * H + h) * (int64_t)d;
+            for (int i = 0; i < P; ++i) {
+                int ix = orc_dim_x(i, d, interleaved), iy = orc_dim_y(i, d, interleaved);
+                double a = (double)pos[t] * th[i];
+                double c = cos(a), s = sin(a);
+                double x0 = orc_load(x, dtype, row + ix);
+                double x1 = orc_load(x, dtype, row + iy);
+                out[row + ix] = x0 * c - x1 * s;
+                out[row + iy] = x1 * c + x0 * s;
+            }
+        }
+    }
+}
+
+/* Rotation of n_tok tokens of H heads, by the shared table (n_tables <= 1: inv_freq or
+ * base) or by one row of inv_freq[n_tables][d/2] per group of H / n_tables heads. */
+static void orc_rotate(const void* x, int dtype, int64_t n_tok, int H, int d, const int64_t* pos,
+                       double base, const double* inv_freq, int n_tables, int interleaved,
+                       double* out) {
+    if (n_tables > 1) orc_rope_heads(x, dtype, n_tok, H, d, pos, inv_freq, H / n_tables, interleaved, out);
+    else orc_rope_ex(x, dtype, n_tok, H, d, pos, base, inv_freq, interleaved, out);
+}
+
+/* Window thresholds of every kv head: thr[Hkv][d/2] (a copy of the shared row when
+ * n_tables <= 1). */
+static double* orc_head_thresholds(int d, double base, const double* inv_freq, int n_tables,
+                                   int Hkv, double alpha) {
+    int P = d / 2;
+    double* thr = (double*)malloc(sizeof(double) * P * Hkv);
+    for (int g = 0; g < Hkv; ++g)
+        orc_thresholds_ex(d, base, n_tables > 1 ? inv_freq + (int64_t)g * P : inv_freq, alpha,
+                          thr + (int64_t)g * P);
+    return thr;
+}
+
 /* Steps 4-5 for one query row: windowed logits over visible keys 0..last,
  * ordinary softmax, out = sum p v, lse = log sum exp(logit).
  *   qr  : rotated query [d]          kr : rotated keys [n_k][Hkv][d]
@@ -167,19 +217,19 @@ static int64_t orc_row(const double* qr, int64_t qpos, const double* kr, const i
  */
 int orc_prefill_ex(const void* q, const void* k, const void* v, int dtype, const int32_t* pos,
                    int B, int64_t N, int Hq, int Hkv, int d, double base,
-                   const double* inv_freq, int interleaved, double alpha,
+                   const double* inv_freq, int n_tables, int interleaved, double alpha,
                    double scale, const int64_t* rows, int64_t n_rows,
                    double* out, double* lse, int64_t* kept_out, int nthreads) {
     if (B < 1 || N < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || d < 2 || d % 2 != 0)
         return -1;
+    if (n_tables > 1 && (n_tables != Hkv || !inv_freq)) return -1;
     if (!rows) n_rows = N;
 #ifdef _OPENMP
     if (nthreads > 0) omp_set_num_threads(nthreads);
 #endif
     int G = Hq / Hkv;
     int P = d / 2;
-    double* thr = (double*)malloc(sizeof(double) * P);
-    orc_thresholds_ex(d, base, inv_freq, alpha, thr);
+    double* thr = orc_head_thresholds(d, base, inv_freq, n_tables, Hkv, alpha);
     int64_t* p64 = (int64_t*)malloc(sizeof(int64_t) * N);
     double* kr = (double*)malloc(sizeof(double) * N * Hkv * d);
     double* qr = (double*)malloc(sizeof(double) * n_rows * Hq * d);
@@ -187,8 +237,8 @@ int orc_prefill_ex(const void* q, const void* k, const void* v, int dtype, const
     int64_t kept_total = 0;
     for (int b = 0; b < B; ++b) {
         for (int64_t t = 0; t < N; ++t) p64[t] = pos ? (int64_t)pos[(int64_t)b * N + t] : t;
-        orc_rope_ex((const char*)k + (dtype == ORC_FP32 ? 4 : 2) * (int64_t)b * N * Hkv * d, dtype,
-                    N, Hkv, d, p64, base, inv_freq, interleaved, kr);
+        orc_rotate((const char*)k + (dtype == ORC_FP32 ? 4 : 2) * (int64_t)b * N * Hkv * d, dtype,
+                   N, Hkv, d, p64, base, inv_freq, n_tables, interleaved, kr);
         /* gather the evaluated query rows, then rotate them at their own positions */
         const char* qb = (const char*)q + (dtype == ORC_FP32 ? 4 : 2) * (int64_t)b * N * Hq * d;
         int esz = dtype == ORC_FP32 ? 4 : 2;
@@ -198,7 +248,7 @@ int orc_prefill_ex(const void* q, const void* k, const void* v, int dtype, const
             memcpy(qsel + (size_t)esz * j * Hq * d, qb + (size_t)esz * r * Hq * d, (size_t)esz * Hq * d);
             qp[j] = p64[r];
         }
-        orc_rope_ex(qsel, dtype, n_rows, Hq, d, qp, base, inv_freq, interleaved, qr);
+        orc_rotate(qsel, dtype, n_rows, Hq, d, qp, base, inv_freq, n_tables, interleaved, qr);
         free(qsel);
         const char* vb = (const char*)v + (size_t)esz * b * N * Hkv * d;
         int64_t kept_b = 0;
@@ -212,8 +262,8 @@ int orc_prefill_ex(const void* q, const void* k, const void* v, int dtype, const
                     double* o = out + (((int64_t)b * n_rows + j) * Hq + h) * d;
                     double* l = lse + ((int64_t)b * Hq + h) * n_rows + j;
                     kept_b += orc_row(qr + (j * Hq + h) * (int64_t)d, qp[j], kr, p64, vb, dtype,
-                                      r, Hkv, h / G, d, interleaved, thr, scale, logit, o, l,
-                                      NULL);
+                                      r, Hkv, h / G, d, interleaved, thr + (int64_t)(h / G) * P,
+                                      scale, logit, o, l, NULL);
                 }
             }
             free(logit);
@@ -229,7 +279,7 @@ int orc_prefill(const void* q, const void* k, const void* v, int dtype, const in
                 int B, int64_t N, int Hq, int Hkv, int d, double base, double alpha,
                 double scale, const int64_t* rows, int64_t n_rows,
                 double* out, double* lse, int64_t* kept_out, int nthreads) {
-    return orc_prefill_ex(q, k, v, dtype, pos, B, N, Hq, Hkv, d, base, NULL, 0, alpha, scale,
+    return orc_prefill_ex(q, k, v, dtype, pos, B, N, Hq, Hkv, d, base, NULL, 0, 0, alpha, scale,
                           rows, n_rows, out, lse, kept_out, nthreads);
 }
 
@@ -323,17 +373,17 @@ int orc_prefill_sparse(const void* q, const void* k, const void* v, int dtype, i
  */
 int orc_decode_ex(const void* q, const void* k, const void* v, int dtype, const int32_t* kv_len,
                   const int32_t* q_pos, int B, int64_t Lmax, int Hq, int Hkv, int d, double base,
-                  const double* inv_freq, int interleaved, double alpha, double scale,
+                  const double* inv_freq, int n_tables, int interleaved, double alpha, double scale,
                   double* out, double* lse, int64_t* kept_out, int nthreads) {
     if (B < 1 || Lmax < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || d < 2 || d % 2 != 0)
         return -1;
+    if (n_tables > 1 && (n_tables != Hkv || !inv_freq)) return -1;
 #ifdef _OPENMP
     if (nthreads > 0) omp_set_num_threads(nthreads);
 #endif
     int G = Hq / Hkv, P = d / 2;
     int esz = dtype == ORC_FP32 ? 4 : 2;
-    double* thr = (double*)malloc(sizeof(double) * P);
-    orc_thresholds_ex(d, base, inv_freq, alpha, thr);
+    double* thr = orc_head_thresholds(d, base, inv_freq, n_tables, Hkv, alpha);
     int64_t kept_total = 0;
     for (int b = 0; b < B; ++b) {
         int64_t L = kv_len[b];
@@ -342,11 +392,11 @@ int orc_decode_ex(const void* q, const void* k, const void* v, int dtype, const 
         int64_t* kp = (int64_t*)malloc(sizeof(int64_t) * L);
         for (int64_t c = 0; c < L; ++c) kp[c] = c;
         double* kr = (double*)malloc(sizeof(double) * L * Hkv * d);
-        orc_rope_ex((const char*)k + (size_t)esz * b * Lmax * Hkv * d, dtype, L, Hkv, d, kp, base,
-                    inv_freq, interleaved, kr);
+        orc_rotate((const char*)k + (size_t)esz * b * Lmax * Hkv * d, dtype, L, Hkv, d, kp, base,
+                   inv_freq, n_tables, interleaved, kr);
         double* qr = (double*)malloc(sizeof(double) * Hq * d);
-        orc_rope_ex((const char*)q + (size_t)esz * b * Hq * d, dtype, 1, Hq, d, &qp, base,
-                    inv_freq, interleaved, qr);
+        orc_rotate((const char*)q + (size_t)esz * b * Hq * d, dtype, 1, Hq, d, &qp, base,
+                   inv_freq, n_tables, interleaved, qr);
         const char* vb = (const char*)v + (size_t)esz * b * Lmax * Hkv * d;
         int64_t kept_b = 0;
         #pragma omp parallel reduction(+:kept_b)
@@ -355,8 +405,8 @@ int orc_decode_ex(const void* q, const void* k, const void* v, int dtype, const 
             #pragma omp for schedule(dynamic, 1)
             for (int h = 0; h < Hq; ++h)
                 kept_b += orc_row(qr + (int64_t)h * d, qp, kr, kp, vb, dtype, L - 1, Hkv, h / G, d,
-                                  interleaved, thr, scale, logit, out + ((int64_t)b * Hq + h) * d,
-                                  lse + (int64_t)b * Hq + h, NULL);
+                                  interleaved, thr + (int64_t)(h / G) * P, scale, logit,
+                                  out + ((int64_t)b * Hq + h) * d, lse + (int64_t)b * Hq + h, NULL);
             free(logit);
         }
         kept_total += kept_b;
@@ -370,7 +420,7 @@ int orc_decode_ex(const void* q, const void* k, const void* v, int dtype, const 
 int orc_decode(const void* q, const void* k, const void* v, int dtype, const int32_t* kv_len,
                const int32_t* q_pos, int B, int64_t Lmax, int Hq, int Hkv, int d, double base,
                double alpha, double scale, double* out, double* lse, int64_t* kept_out, int nthreads) {
-    return orc_decode_ex(q, k, v, dtype, kv_len, q_pos, B, Lmax, Hq, Hkv, d, base, NULL, 0, alpha,
+    return orc_decode_ex(q, k, v, dtype, kv_len, q_pos, B, Lmax, Hq, Hkv, d, base, NULL, 0, 0, alpha,
                          scale, out, lse, kept_out, nthreads);
 }
 

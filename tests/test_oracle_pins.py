@@ -538,3 +538,63 @@ def test_block_sparse_empty_lists_are_block_local():
         ref, _, _ = oracle.prefill(synth.to_oracle(q[:, sl]), synth.to_oracle(k[:, sl]),
                                    synth.to_oracle(v[:, sl]), base, 1.0)
         np.testing.assert_allclose(out[:, sl], ref, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------------------
+# Per-head frequency tables (AdaRoPE abstract, on the cards page: each head gets its own
+# rotation frequencies).  One row per kv head; its q heads use the same row.  Pins: the
+# relative complex form per head, the shared-table oracle when all rows are equal, and the
+# count as a sum of single-table enumerations.
+
+def _head_tables(Hkv, d, seed):
+    rng = np.random.default_rng(seed)
+    rows = [np.sort(rng.uniform(0.01, 1.5, d // 2))[::-1] for _ in range(Hkv)]
+    return np.ascontiguousarray(np.stack(rows))
+
+
+@pytest.mark.parametrize("alpha", [0.5, 1.0, math.inf])
+@pytest.mark.parametrize("layout", ["half", "interleaved"])
+def test_per_head_tables_equal_relative_form(alpha, layout):
+    N, Hq, Hkv, d = 37, 6, 2, 16
+    q, k, v = synth.prefill_inputs(1, N, Hq, Hkv, d, "fp32", seed=41)
+    pos = np.cumsum(np.random.default_rng(8).integers(0, 4, N))
+    tabs = _head_tables(Hkv, d, 9)
+    out, lse, kept = oracle.prefill(synth.to_oracle(q), synth.to_oracle(k), synth.to_oracle(v),
+                                    1e4, alpha, pos=pos, inv_freq=tabs, layout=layout)
+    G = Hq // Hkv
+    for h in range(Hq):
+        g = h // G
+        ro, rl = _relative_form_table(_f64(q[0, :, h]), _f64(k[0, :, g]), _f64(v[0, :, g]), pos,
+                                      pos, tabs[g], layout, alpha, 1.0 / math.sqrt(d))
+        np.testing.assert_allclose(out[0, :, h], ro, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[0, h], rl, rtol=0, atol=1e-12)
+
+
+def test_per_head_tables_all_equal_is_shared_table():
+    B, N, Hq, Hkv, d = 2, 45, 4, 2, 32
+    q, k, v = synth.prefill_inputs(B, N, Hq, Hkv, d, "bf16", seed=42)
+    theta = _llama3_table(d, 5e5)
+    a = [synth.to_oracle(t) for t in (q, k, v)]
+    shared = oracle.prefill(*a, 5e5, 1.0, inv_freq=theta)
+    heads = oracle.prefill(*a, 5e5, 1.0, inv_freq=np.stack([theta, theta]))
+    np.testing.assert_array_equal(shared[0], heads[0])
+    np.testing.assert_array_equal(shared[1], heads[1])
+    assert shared[2] == heads[2]
+
+
+def test_per_head_tables_count_and_decode():
+    """Kept terms: the sum over kv heads of (q heads per kv head) x that row's enumeration.
+    Decode with per-head rows equals the last prefill row."""
+    N, Hq, Hkv, d = 50, 6, 3, 16
+    tabs = _head_tables(Hkv, d, 10)
+    q, k, v = synth.prefill_inputs(1, N, Hq, Hkv, d, "fp32", seed=43)
+    a = [synth.to_oracle(t) for t in (q, k, v)]
+    _, _, kept = oracle.prefill(*a, 1e4, 1.0, inv_freq=tabs)
+    G = Hq // Hkv
+    assert kept == sum(G * oracle.count_enumerate(d, 1e4, 1.0, N, 0, N, inv_freq=tabs[g])[0]
+                       for g in range(Hkv))
+    po, pl, _ = oracle.prefill(*a, 1e4, 1.0, inv_freq=tabs, rows=[N - 1])
+    do, dl, _ = oracle.decode(synth.to_oracle(q[:, N - 1]), a[1], a[2], np.array([N]), 1e4, 1.0,
+                              inv_freq=tabs)
+    np.testing.assert_allclose(do, po[:, 0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dl, pl[:, :, 0], rtol=0, atol=1e-12)
