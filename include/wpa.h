@@ -378,6 +378,25 @@ int wpa_prefill_paged_varlen(const void* q, const void* k_pool, const void* v_po
                              double alpha, float scale, int32_t dtype, int32_t out_dtype,
                              unsigned long long* term_count, void* stream);
 
+/*
+ * wpa_decode_ex without a workspace, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation).  Arguments
+ * are those of wpa_decode_ex minus workspace and ws_bytes; results are bit-identical to it
+ * with the same chunk_keys.  The split-KV partials go to a scratch array the library holds
+ * in device memory, 16 MiB per GPU, kept until the process ends: a call whose partials need
+ * more (wpa_decode_workspace_bytes(B, Lmax, Hq, Hkv, d, chunk_keys) > 16 MiB) returns
+ * WPA_ERR_UNSUPPORTED before enqueueing anything.  The call allocates nothing.  Every call on
+ * one GPU uses that GPU's array: calls that may run concurrently on one GPU (different
+ * streams without ordering between them) race on it.  The first call on a device looks up
+ * the array's address on that device (it must be the current device).
+ */
+int wpa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* kv_len, const int32_t* q_pos, void* out, float* lse,
+                       int32_t B, int64_t Lmax, int32_t Hq, int32_t Hkv, int32_t d, double base,
+                       const wpa_rope_t* rope, double alpha, float scale, int32_t dtype,
+                       int32_t out_dtype, unsigned long long* term_count, int32_t chunk_keys,
+                       void* stream);
+
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char* wpa_last_error(void);
 

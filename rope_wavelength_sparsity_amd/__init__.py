@@ -42,7 +42,8 @@ EXPORTS = ("wpa_count_terms", "wpa_thresholds", "wpa_prefill_workspace_bytes", "
            "wpa_kv_write_ex", "wpa_decode_ex", "wpa_prefill_cached", "wpa_kcache_window_bytes",
            "wpa_kv_write_window", "wpa_decode_window", "wpa_prefill_sparse", "wpa_kv_page_bytes",
            "wpa_kv_write_paged", "wpa_decode_paged", "wpa_prefill_paged",
-           "wpa_prefill_cached_varlen", "wpa_prefill_paged_varlen", "wpa_last_error")
+           "wpa_prefill_cached_varlen", "wpa_prefill_paged_varlen", "wpa_decode_noalloc",
+           "wpa_last_error")
 
 
 class Rope(ctypes.Structure):
@@ -176,6 +177,9 @@ def lib():
     L.wpa_prefill_paged_varlen.argtypes = [P, P, P, P, I32, P, P, P, P, I32, I32, I32, I32, I32,
                                            I32, I32, D, P, D, F, I32, I32, P, P]
     L.wpa_prefill_paged_varlen.restype = ctypes.c_int
+    L.wpa_decode_noalloc.argtypes = [P, P, P, P, P, P, P, I32, I64, I32, I32, I32, D, P, D, F, I32,
+                                     I32, P, I32, P]
+    L.wpa_decode_noalloc.restype = ctypes.c_int
     L.wpa_last_error.argtypes = []
     L.wpa_last_error.restype = ctypes.c_char_p
     _lib = L
@@ -568,6 +572,38 @@ def decode(q, cache, kv_len, alpha: float, *, q_pos=None, scale: float | None = 
                                _dtype_code(q), _dtype_code(out), _ptr(term_count),
                                int(chunk_keys), _ptr(workspace), _ws_bytes(workspace),
                                _stream(stream)))
+    return (out, lse) if lse is not None else out
+
+
+def decode_noalloc(q, cache, kv_len, alpha: float, *, out, q_pos=None, scale: float | None = None,
+                   lse=None, term_count=None, chunk_keys: int = 0, stream=None):
+    """decode() on a dense KVCache through the entry point that allocates nothing: the split-KV
+    partials live in the library's per-GPU scratch array (16 MiB).  `out` (and `lse`, if
+    wanted) must be given; calls that may overlap on one GPU race on the scratch array."""
+    _dev(q, "q")
+    _dev(kv_len, "kv_len")
+    if q.dim() != 3:
+        raise ValueError("q must be [B][Hq][d]")
+    B, Hq, d = q.shape
+    if isinstance(cache, PagedKVCache) or cache.window_alpha is not None:
+        raise ValueError("decode_noalloc takes a dense KVCache")
+    if B != cache.B or d != cache.d or kv_len.dtype != torch.int32 or kv_len.numel() != B:
+        raise ValueError("q [B][Hq][d] and kv_len int32 [B] must match the cache")
+    _same_device(kv_len, q, "kv_len")
+    _same_device(cache.k, q, "the cache")
+    if out is None:
+        raise ValueError("decode_noalloc needs a caller-supplied out")
+    out = _out(out, q.shape, q, None)
+    lse = _lse(lse, False, (B, Hq), q)
+    q_pos = _int32_vec(q_pos, B, q, "q_pos")
+    term_count = _counter(term_count, q)
+    rope, keep = _rope(d, cache.inv_freq, cache.pairs)
+    _check(lib().wpa_decode_noalloc(_ptr(q), _ptr(cache.k), _ptr(cache.v), _ptr(kv_len), _ptr(q_pos),
+                                    _ptr(out), _ptr(lse), B, cache.Lmax, Hq, cache.Hkv, d,
+                                    cache.base, rope, float(alpha),
+                                    float(scale) if scale is not None else 0.0, _dtype_code(q),
+                                    _dtype_code(out), _ptr(term_count), int(chunk_keys),
+                                    _stream(stream)))
     return (out, lse) if lse is not None else out
 
 

@@ -20,10 +20,18 @@
 //   permuted (bits 2 and 3 swapped) so the S^T registers are directly the P^T operand of
 //   O^T[32 dims x 32 cols] += V^T[32 dims x 16 keys] * P^T, whose V^T operand is one
 //   16-byte load per lane from the key-octet-blocked V cache.
+#include <atomic>
+
 #include "wpa_device.hpp"
 #include "wpa_internal.hpp"
 
 namespace wpa {
+
+// The no-allocation decode entry point keeps its split-KV partials here instead of in a
+// caller workspace: one copy of this array per GPU, held until the process ends.  Host code
+// must not use the array's name as an address (on the host it is only a stand-in); the
+// device address comes from hipGetSymbolAddress, once per device (decode_scratch below).
+static __device__ __align__(256) float scratch[kDecodeScratchBytes / sizeof(float)];
 
 namespace {
 
@@ -411,6 +419,27 @@ hipError_t launch_decode_d(const DecodeParams& p, const Tables& t, hipStream_t s
 
 hipError_t launch_decode(const DecodeParams& p, const Tables& t, hipStream_t s) {
     return p.d == 64 ? launch_decode_d<64>(p, t, s) : launch_decode_d<128>(p, t, s);
+}
+
+hipError_t decode_scratch(void** ptr) {
+    // device address of `scratch` on the current device, looked up on the first call made
+    // with that device current and kept per device (two threads racing on a first call
+    // both store the same address)
+    constexpr int kMaxDevices = 64;
+    static std::atomic<void*> addr[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void* a = addr[dev].load(std::memory_order_acquire);
+    if (!a) {
+        e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!a) return hipErrorInvalidSymbol;
+        addr[dev].store(a, std::memory_order_release);
+    }
+    *ptr = a;
+    return hipSuccess;
 }
 
 }  // namespace wpa

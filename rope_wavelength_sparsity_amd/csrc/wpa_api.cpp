@@ -487,7 +487,10 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache, const i
                 int32_t Hq, int32_t Hkv, int32_t d, double base, const wpa_rope_t* rope,
                 const wpa::KLayout& kl, double alpha, float scale, int32_t dtype, int32_t out_dtype,
                 unsigned long long* term_count, int32_t chunk_keys, void* workspace,
-                size_t ws_bytes, void* stream, const wpa::Paging& pg = wpa::Paging{}) {
+                size_t ws_bytes, void* stream, const wpa::Paging& pg = wpa::Paging{},
+                bool use_scratch = false) {
+    // use_scratch: the partials go to the library's per-GPU scratch array (workspace and
+    // ws_bytes are ignored)
     if (B < 1 || Lmax < 1 || Hq < 1 || Hkv < 1) return fail(WPA_ERR_INVALID, "B, Lmax, Hq, Hkv must be >= 1");
     if (Hq % Hkv) return fail(WPA_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
     if (Hq / Hkv > 16) return fail(WPA_ERR_UNSUPPORTED, "decode supports up to 16 q heads per kv head");
@@ -496,12 +499,26 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache, const i
     if (out_dtype != WPA_BF16 && out_dtype != WPA_FP32) return fail(WPA_ERR_INVALID, "out_dtype must be WPA_BF16 or WPA_FP32");
     if (std::isnan(scale)) return fail(WPA_ERR_INVALID, "scale is NaN");
     if (chunk_keys < 0 || (chunk_keys % 256)) return fail(WPA_ERR_INVALID, "chunk_keys must be 0 or a positive multiple of 256");
-    if (!q || !k_cache || !v_cache || !kv_len || !out || !workspace) return fail(WPA_ERR_INVALID, "null pointer");
-    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) || !aligned16(workspace))
+    if (!q || !k_cache || !v_cache || !kv_len || !out || (!use_scratch && !workspace))
+        return fail(WPA_ERR_INVALID, "null pointer");
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+        (!use_scratch && !aligned16(workspace)))
         return fail(WPA_ERR_INVALID, "q, caches, out and workspace must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(kv_len) & 3u) || (reinterpret_cast<uintptr_t>(q_pos) & 3u) ||
+        (reinterpret_cast<uintptr_t>(lse) & 3u))
+        return fail(WPA_ERR_INVALID, "kv_len, q_pos and lse must be 4-byte aligned");
     if (term_count && (reinterpret_cast<uintptr_t>(term_count) & 7u)) return fail(WPA_ERR_INVALID, "term_count must be 8-byte aligned");
     const int ch = chunk_keys > 0 ? chunk_keys : default_chunk(B, Lmax, Hkv);
     const size_t need = wpa_decode_workspace_bytes(B, Lmax, Hq, Hkv, d, ch);
+    if (use_scratch) {
+        if (need > wpa::kDecodeScratchBytes)
+            return fail(WPA_ERR_UNSUPPORTED, "decode partials need %zu bytes; the no-allocation entry point "
+                        "holds %zu (use a larger chunk_keys, or wpa_decode_ex with a workspace)", need,
+                        wpa::kDecodeScratchBytes);
+        const hipError_t e = wpa::decode_scratch(&workspace);
+        if (e != hipSuccess) return fail(WPA_ERR_HIP, "scratch address: %s", hipGetErrorString(e));
+        ws_bytes = wpa::kDecodeScratchBytes;
+    }
     if (ws_bytes < need) return fail(WPA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
     wpa::Tables tab;
     make_tables(d, base, rope, alpha, &tab);
@@ -670,6 +687,19 @@ int wpa_decode_ex(const void* q, const void* k_cache, const void* v_cache, const
     return decode_impl(q, k_cache, v_cache, kv_len, q_pos, out, lse, B, Lmax, Hq, Hkv, d, base,
                        rope, dense_layout(d, Lmax), alpha, scale, dtype, out_dtype, term_count,
                        chunk_keys, workspace, ws_bytes, stream);
+}
+
+int wpa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* kv_len, const int32_t* q_pos, void* out, float* lse,
+                       int32_t B, int64_t Lmax, int32_t Hq, int32_t Hkv, int32_t d, double base,
+                       const wpa_rope_t* rope, double alpha, float scale, int32_t dtype,
+                       int32_t out_dtype, unsigned long long* term_count, int32_t chunk_keys,
+                       void* stream) {
+    int rc = check_common(d, base, rope, alpha);
+    if (rc) return rc;
+    return decode_impl(q, k_cache, v_cache, kv_len, q_pos, out, lse, B, Lmax, Hq, Hkv, d, base,
+                       rope, dense_layout(d, Lmax), alpha, scale, dtype, out_dtype, term_count,
+                       chunk_keys, nullptr, 0, stream, wpa::Paging{}, true);
 }
 
 int wpa_prefill_cached(const void* q, const void* k_cache, const void* v_cache,

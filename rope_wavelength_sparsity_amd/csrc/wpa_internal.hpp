@@ -108,4 +108,9 @@ hipError_t launch_prefill(const PrefillParams& p, const Tables& t, hipStream_t s
 hipError_t prefill_sparse_lds(const PrefillParams& p, size_t* need, size_t* limit);
 hipError_t launch_decode(const DecodeParams& p, const Tables& t, hipStream_t s);
 
+// Size of the per-GPU scratch array of the no-allocation decode entry point (its split-KV
+// partials), and its device address on the current device (looked up once per device).
+constexpr size_t kDecodeScratchBytes = (size_t)16 << 20;
+hipError_t decode_scratch(void** ptr);
+
 }  // namespace wpa
