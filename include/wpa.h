@@ -184,8 +184,20 @@ int wpa_decode(const void* q, const void* k_cache, const void* v_cache, const in
  *             stay a suffix of the pair axis), or NULL for theta_i = base^(-2i/d).  With a
  *             table the window test is D <= alpha * ((2.0*M_PI) / theta_i) in IEEE double,
  *             and `base` is not used.  The table is read during the call only.
+ *   head_inv_freq  NULL, or a DEVICE array [Hkv][d/2] of double: one frequency table per kv
+ *             head (AdaRoPE abstract, on the ATFlash cards page: rotation frequencies chosen
+ *             per head).  Kv head g rotates its keys, and the q heads that read it
+ *             (h / (Hq/Hkv) = g) their queries, by row g, and pair i of those heads has the
+ *             window D <= alpha * ((2.0*M_PI) / head_inv_freq[g][i]), evaluated on the device
+ *             in IEEE double (the same decisions as the host's expression).  Each row must be
+ *             finite, > 0 and non-increasing: a precondition (the values live on the device and
+ *             are not checked).  inv_freq must then be NULL and `base` is not used.  Per-head
+ *             tables are taken by wpa_prefill_ex / _prepare_ex / _attend_ex, wpa_kv_write_ex,
+ *             wpa_kv_write_paged, wpa_decode_ex, wpa_decode_paged and wpa_decode_noalloc; the
+ *             other entry points return WPA_ERR_UNSUPPORTED for them, and the host-only count
+ *             and threshold queries take one head's table (as inv_freq) at a time.
  * Every *_ex entry point below is its namesake with this description added; rope = NULL
- * means {WPA_PAIRS_HALF, NULL}.  A table that is not positive and non-increasing is
+ * means {WPA_PAIRS_HALF, NULL, NULL}.  A table that is not positive and non-increasing is
  * WPA_ERR_UNSUPPORTED; an unknown `pairs` value WPA_ERR_INVALID.  The decode caches hold
  * keys rotated by the description given to wpa_kv_write_ex; wpa_decode_ex must be given
  * the same one (q is rotated by it).
@@ -194,7 +206,8 @@ enum { WPA_PAIRS_HALF = 0, WPA_PAIRS_INTERLEAVED = 1 };
 
 typedef struct wpa_rope {
     int32_t pairs;
-    const double* inv_freq;
+    const double* inv_freq;        /* host [d/2], or NULL */
+    const double* head_inv_freq;   /* device [Hkv][d/2], or NULL */
 } wpa_rope_t;
 
 int wpa_count_terms_ex(int32_t d, double base, const wpa_rope_t* rope, double alpha, int64_t n_q,

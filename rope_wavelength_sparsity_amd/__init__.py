@@ -47,23 +47,48 @@ EXPORTS = ("wpa_count_terms", "wpa_thresholds", "wpa_prefill_workspace_bytes", "
 
 
 class Rope(ctypes.Structure):
-    """wpa_rope_t: pair layout and optional host table of rotation frequencies."""
-    _fields_ = [("pairs", ctypes.c_int32), ("inv_freq", ctypes.c_void_p)]
+    """wpa_rope_t: pair layout, optional host table of rotation frequencies, optional device
+    tables of one row per kv head."""
+    _fields_ = [("pairs", ctypes.c_int32), ("inv_freq", ctypes.c_void_p),
+                ("head_inv_freq", ctypes.c_void_p)]
 
 
-def _rope(d, inv_freq, pairs):
-    """(pointer to a wpa_rope_t or None, objects that must outlive the call)."""
+def _ndim(x):
+    return x.dim() if isinstance(x, torch.Tensor) else np.ndim(x)
+
+
+def head_table(tab, d: int, Hkv: int, device):
+    """Per-kv-head rotation frequencies [Hkv][d/2] as a float64 tensor on `device`, checked on
+    the host (each row finite, > 0 and non-increasing, as the kernels require)."""
+    t = torch.as_tensor(tab, dtype=torch.float64)
+    host = t.detach().cpu().numpy()
+    if host.shape != (Hkv, d // 2):
+        raise ValueError("per-head frequency tables must be [Hkv][d/2] = [%d][%d], got %s"
+                         % (Hkv, d // 2, host.shape))
+    if not (np.all(np.isfinite(host)) and np.all(host > 0) and np.all(np.diff(host, axis=1) <= 0)):
+        raise ValueError("each per-head frequency row must be finite, > 0 and non-increasing")
+    return t.to(device).contiguous()
+
+
+def _rope(d, inv_freq, pairs, Hkv=None, device=None):
+    """(pointer to a wpa_rope_t or None, objects that must outlive the call).  inv_freq: None,
+    d/2 shared frequencies, or [Hkv][d/2] per-kv-head rows (uploaded to `device`)."""
     if inv_freq is None and pairs == "half":
         return None, ()
     if pairs not in WPA_PAIRS:
         raise ValueError("pairs must be 'half' or 'interleaved'")
-    tab = None
-    if inv_freq is not None:
+    tab, heads = None, None
+    if inv_freq is not None and _ndim(inv_freq) == 2:
+        if Hkv is None or device is None:
+            raise ValueError("per-head frequency tables are not taken here")
+        heads = head_table(inv_freq, d, Hkv, device)
+    elif inv_freq is not None:
         tab = np.ascontiguousarray(np.asarray(inv_freq, dtype=np.float64))
         if tab.shape != (d // 2,):
             raise ValueError("inv_freq must hold d/2 = %d frequencies" % (d // 2))
-    r = Rope(WPA_PAIRS[pairs], None if tab is None else tab.ctypes.data)
-    return ctypes.byref(r), (r, tab)
+    r = Rope(WPA_PAIRS[pairs], None if tab is None else tab.ctypes.data,
+             None if heads is None else heads.data_ptr())
+    return ctypes.byref(r), (r, tab, heads)
 
 
 def default_inv_freq(d: int, base: float) -> np.ndarray:
@@ -289,6 +314,18 @@ def count_terms(d: int, base: float, alpha: float, n_q: int, q_pos0: int, n_k: i
     return kept.value, total.value
 
 
+def count_terms_heads(d: int, alpha: float, n_q: int, q_pos0: int, n_k: int, head_inv_freq,
+                      q_per_kv: int):
+    """(kept, total) terms summed over the q heads of one sequence with per-kv-head frequency
+    rows [Hkv][d/2]: each row counted by the closed form and weighted by its q heads."""
+    kept = total = 0
+    for row in np.asarray(torch.as_tensor(head_inv_freq, dtype=torch.float64).cpu()):
+        k, t = count_terms(d, 2.0, alpha, n_q, q_pos0, n_k, inv_freq=row)
+        kept += q_per_kv * k
+        total += q_per_kv * t
+    return kept, total
+
+
 def thresholds(d: int, base: float, alpha: float, *, inv_freq=None, pairs: str = "half"):
     """Integer window table W_i = floor(alpha * lambda_i) (INT32_MAX if unbounded), with
     lambda_i = 2*pi*base^(2i/d) or 2*pi/inv_freq[i]."""
@@ -345,7 +382,7 @@ def prefill(q, k, v, base: float, alpha: float, *, scale: float | None = None, p
     positions = _int32_vec(positions, B * N, q, "positions")
     term_count = _counter(term_count, q)
     workspace = _workspace(workspace, prefill_workspace_bytes(B, N, Hkv, d), q)
-    rope, keep = _rope(d, inv_freq, pairs)
+    rope, keep = _rope(d, inv_freq, pairs, Hkv, q.device)
     if block_count is not None:
         # token-level block sparsity on top of the window (blocks of 64 tokens)
         nblk = (N + 63) // 64
@@ -384,7 +421,7 @@ def prefill_prepare(k, v, base: float, *, positions=None, workspace=None, stream
     _same_device(v, k, "v")
     positions = _int32_vec(positions, B * N, k, "positions")
     workspace = _workspace(workspace, prefill_workspace_bytes(B, N, Hkv, d), k)
-    rope, keep = _rope(d, inv_freq, pairs)
+    rope, keep = _rope(d, inv_freq, pairs, Hkv, k.device)
     _check(lib().wpa_prefill_prepare_ex(_ptr(k), _ptr(v), _ptr(positions), B, N, Hkv, d,
                                         float(base), rope, _dtype_code(k), _ptr(workspace),
                                         _ws_bytes(workspace), _stream(stream)))
@@ -405,13 +442,23 @@ def prefill_attend(q, workspace, Hkv: int, base: float, alpha: float, *, scale=N
     lse = _lse(lse, want_lse, (B, Hq, N), q)
     positions = _int32_vec(positions, B * N, q, "positions")
     term_count = _counter(term_count, q)
-    rope, keep = _rope(d, inv_freq, pairs)
+    rope, keep = _rope(d, inv_freq, pairs, Hkv, q.device)
     _check(lib().wpa_prefill_attend_ex(_ptr(q), _ptr(out), _ptr(lse), _ptr(positions), B, N, Hq,
                                        Hkv, d, float(base), rope, float(alpha),
                                        float(scale) if scale is not None else 0.0, _dtype_code(q),
                                        _dtype_code(out), _ptr(term_count), _ptr(workspace),
                                        _ws_bytes(workspace), _stream(stream)))
     return (out, lse) if lse is not None else out
+
+
+def _own_table(inv_freq, d, Hkv, device):
+    """A cache's copy of its frequency description: None, a host d/2 table, or the per-kv-head
+    rows as a checked float64 device tensor."""
+    if inv_freq is None:
+        return None
+    if _ndim(inv_freq) == 2:
+        return head_table(inv_freq, d, Hkv, device)
+    return np.asarray(inv_freq, dtype=np.float64).copy()
 
 
 class KVCache:
@@ -426,9 +473,10 @@ class KVCache:
     def __init__(self, B, Lmax, Hkv, d, base, device="cuda", *, inv_freq=None, pairs="half",
                  window_alpha=None):
         self.B, self.Lmax, self.Hkv, self.d, self.base = B, Lmax, Hkv, d, float(base)
-        self.inv_freq = None if inv_freq is None else np.asarray(inv_freq, dtype=np.float64).copy()
+        self.inv_freq = _own_table(inv_freq, d, Hkv, device)
         self.pairs = pairs
-        rope, keep = _rope(d, self.inv_freq, pairs)    # validates the description
+        self._rope = _rope(d, self.inv_freq, pairs, Hkv, device)   # validates the description
+        rope = self._rope[0]
         self.window_alpha = None if window_alpha is None else float(window_alpha)
         if self.window_alpha is None:
             self.k_seq_bytes = kcache_bytes(1, Lmax, Hkv, d)
@@ -455,7 +503,7 @@ class KVCache:
                 raise ValueError("seq out of range")
             kc += seq * self.k_seq_bytes
             vc += seq * vcache_bytes(1, self.Lmax, self.Hkv, self.d)
-        rope, keep = _rope(self.d, self.inv_freq, self.pairs)
+        rope = self._rope[0]
         if self.window_alpha is None:
             _check(lib().wpa_kv_write_ex(_ptr(k), _ptr(v), int(start), k.shape[1], kc, vc, nb,
                                          self.Lmax, self.Hkv, self.d, self.base, rope,
@@ -483,9 +531,9 @@ class PagedKVCache:
                  pairs="half", block_table=None):
         self.num_pages, self.page_size, self.Hkv, self.d = num_pages, page_size, Hkv, d
         self.base = float(base)
-        self.inv_freq = None if inv_freq is None else np.asarray(inv_freq, dtype=np.float64).copy()
+        self.inv_freq = _own_table(inv_freq, d, Hkv, device)
         self.pairs = pairs
-        _rope(d, self.inv_freq, pairs)                   # validates the description
+        self._rope = _rope(d, self.inv_freq, pairs, Hkv, device)   # validates the description
         self.page_bytes = lib().wpa_kv_page_bytes(Hkv, d, page_size)
         if self.page_bytes == 0:
             raise ValueError("invalid page arguments (d 64 or 128, page_size a power of two >= 32)")
@@ -512,7 +560,7 @@ class PagedKVCache:
         if k.shape != v.shape or k.dim() != 4 or k.shape[0] != t.shape[0] or \
                 k.shape[2] != self.Hkv or k.shape[3] != self.d or k.dtype != v.dtype:
             raise ValueError("k, v must be [B][n][Hkv][d] of one dtype, B = block_table rows")
-        rope, keep = _rope(self.d, self.inv_freq, self.pairs)
+        rope = self._rope[0]
         _check(lib().wpa_kv_write_paged(_ptr(k), _ptr(v), int(start), k.shape[1], _ptr(self.k),
                                         _ptr(self.v), _ptr(t), self.num_pages, t.shape[0],
                                         t.shape[1], self.page_size, self.Hkv, self.d, self.base,
@@ -544,7 +592,7 @@ def decode(q, cache, kv_len, alpha: float, *, q_pos=None, scale: float | None = 
     lse = _lse(lse, want_lse, (B, Hq), q)
     term_count = _counter(term_count, q)
     workspace = _workspace(workspace, decode_workspace_bytes(B, lmax, Hq, cache.Hkv, d, chunk_keys), q)
-    rope, keep = _rope(d, cache.inv_freq, cache.pairs)
+    rope = cache._rope[0]
     if paged:
         _check(lib().wpa_decode_paged(_ptr(q), _ptr(cache.k), _ptr(cache.v), _ptr(table),
                                       cache.num_pages, _ptr(kv_len), _ptr(q_pos), _ptr(out),
@@ -597,7 +645,7 @@ def decode_noalloc(q, cache, kv_len, alpha: float, *, out, q_pos=None, scale: fl
     lse = _lse(lse, False, (B, Hq), q)
     q_pos = _int32_vec(q_pos, B, q, "q_pos")
     term_count = _counter(term_count, q)
-    rope, keep = _rope(d, cache.inv_freq, cache.pairs)
+    rope = cache._rope[0]
     _check(lib().wpa_decode_noalloc(_ptr(q), _ptr(cache.k), _ptr(cache.v), _ptr(kv_len), _ptr(q_pos),
                                     _ptr(out), _ptr(lse), B, cache.Lmax, Hq, cache.Hkv, d,
                                     cache.base, rope, float(alpha),
@@ -640,7 +688,7 @@ def prefill_cached(q, cache, kv_len, alpha: float, *, scale: float | None = None
     out = _out(out, q.shape, q, out_dtype)
     lse = _lse(lse, want_lse, (B, Hq, Nq), q)
     term_count = _counter(term_count, q)
-    rope, keep = _rope(d, cache.inv_freq, cache.pairs)
+    rope = cache._rope[0]
     sc = float(scale) if scale is not None else 0.0
     if paged:
         _check(lib().wpa_prefill_paged(_ptr(q), _ptr(cache.k), _ptr(cache.v), _ptr(table),
@@ -684,7 +732,7 @@ def _prefill_varlen(q, cache, kv_len, alpha, cu_q, max_q, scale, out, out_dtype,
     out = _out(out, q.shape, q, out_dtype)
     lse = _lse(lse, want_lse, (rows, Hq), q)
     term_count = _counter(term_count, q)
-    rope, keep = _rope(d, cache.inv_freq, cache.pairs)
+    rope = cache._rope[0]
     sc = float(scale) if scale is not None else 0.0
     if paged:
         _check(lib().wpa_prefill_paged_varlen(_ptr(q), _ptr(cache.k), _ptr(cache.v), _ptr(table),

@@ -101,7 +101,7 @@ void decode_partial_kernel(DecodeParams p, Tables tab) {
                 y = bf16_bits_to_f32(static_cast<const uint16_t*>(p.q)[iy]);
             }
             float sn, cs;
-            rope_sincos(qpos, tab.theta[pr], &sn, &cs);
+            rope_sincos(qpos, p.head_theta ? p.head_theta[(int64_t)g * P + pr] : tab.theta[pr], &sn, &cs);
             xo = (x * cs - y * sn) * sl2;
             yo = (y * cs + x * sn) * sl2;
         }
@@ -128,7 +128,10 @@ void decode_partial_kernel(DecodeParams p, Tables tab) {
     const char* kbytes = reinterpret_cast<const char*>(kpg);
     const char* vbytes = reinterpret_cast<const char*>(vg);
     const int koffl = arow * 32 + 16 * h;            // lane offset in a K block's 32 rows
-    const int Wl = lane < P ? tab.W[lane] : INT32_MAX;   // window of pair `lane`
+    // window of pair `lane` (per-head tables: from kv head g's frequency)
+    const int Wl = lane >= P ? INT32_MAX
+                 : (p.head_theta ? window_from_theta(p.alpha, p.head_theta[(int64_t)g * P + lane])
+                                 : tab.W[lane]);
     const int voffl = (h * D + l32) * 16;            // lane offset in a tile's V octets
     int plo = 0, pfull = 0;                          // band edges of the current tile
 

@@ -153,7 +153,10 @@ struct Tile {
 // SPARSE: each (sequence, q head, 64-row query block) attends, besides its own block, only
 // the 64-key blocks its ascending list names (token-level block sparsity composed with the
 // window); unlisted keys leave the softmax.  Positions are token indices.
-template <int D, bool F32, bool HASPOS, bool COUNT, bool CACHED, bool SPARSE, bool PAGED = false>
+// HEADS: one rotation-frequency table per kv head (p.head_theta [Hkv][d/2], device); the
+// workgroup's window table is computed from its kv head's row at start.
+template <int D, bool F32, bool HASPOS, bool COUNT, bool CACHED, bool SPARSE, bool PAGED = false,
+          bool HEADS = false>
 __global__ __launch_bounds__(64 * (Tile<D>::maxw(HASPOS) + 1))
 __attribute__((amdgpu_waves_per_eu(Tile<D>::waves_per_eu(HASPOS))))
 void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
@@ -180,6 +183,21 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
     const int hc = u % L.nhc;
     const int g = (u / L.nhc) % p.Hkv;
     const int b = u / (L.nhc * p.Hkv);
+    // Window and rotation tables: the launch's (kernel arguments), or with per-head tables the
+    // row of kv head g, its windows computed here once per workgroup (into LDS)
+    __shared__ int32_t sWh[HEADS ? D / 2 : 1];
+    if constexpr (HEADS) {
+        if (tid < D / 2) sWh[tid] = window_from_theta(p.alpha, p.head_theta[(int64_t)g * (D / 2) + tid]);
+        __syncthreads();
+    }
+    auto Wt = [&](int i) -> int {
+        if constexpr (HEADS) return uniform(sWh[i]);
+        else return tab.W[i];
+    };
+    auto TH = [&](int i) -> double {
+        if constexpr (HEADS) return p.head_theta[(int64_t)g * (D / 2) + i];
+        else return tab.theta[i];
+    };
     const int hin = hc * L.Gc + (w % L.Gc);
     const int rg = w / L.Gc;
     const bool head_ok = hin < G;
@@ -250,7 +268,7 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
                     y = bf16_bits_to_f32(static_cast<const uint16_t*>(p.q)[iy]);
                 }
                 float sn, cs;
-                rope_sincos(pq, tab.theta[8 * j + e], &sn, &cs);
+                rope_sincos(pq, TH(8 * j + e), &sn, &cs);
                 const float rot = h ? (y * cs + x * sn) : (x * cs - y * sn);
                 const uint32_t bits = f32_to_f16_bits(rot * sl2);
                 acc[0] = (acc[0] >> 16) | (acc[1] << 16);
@@ -305,7 +323,7 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
     };
     uint64_t cnt = 0;
     int plo = 0, pfull = 0, plo_wg = 0;     // running band edges (distances only grow)
-    int w_lo = tab.W[0], w_full = tab.W[0];  // W at the two edges (INT32_MAX past the end)
+    int w_lo = Wt(0), w_full = Wt(0);  // W at the two edges (INT32_MAX past the end)
     // Block jf = pfull/8 of Q with its leading (not fully active) pairs zeroed, valid for
     // the band edge pfull == q_key; rebuilt only when that edge moves.
     // kept in LDS (one slot per lane of each compute wave), not in registers
@@ -321,7 +339,7 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
         const int ks = kt * BN;
         const int kend = (ks + BN < NK ? ks + BN : NK) - 1;
         const int dmin_wg = uniform(pq_wg - POS(kend) > 0 ? pq_wg - POS(kend) : 0);
-        while (plo_wg < P && tab.W[plo_wg] < dmin_wg) ++plo_wg;
+        while (plo_wg < P && Wt(plo_wg) < dmin_wg) ++plo_wg;
         const int jlo = uniform(plo_wg) >> 3;
         const int nK = Tile<D>::KI * (NB - jlo);
         const int nI = nK + Tile<D>::VI + (HASPOS ? Tile<D>::PI : 0);
@@ -474,7 +492,7 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
             const int dmax_t = pq_hi - POSL(ks);
             while (w_lo < dmin_t) {
                 ++plo;
-                w_lo = plo < P ? tab.W[plo] : INT32_MAX;
+                w_lo = plo < P ? Wt(plo) : INT32_MAX;
             }
             if (w_lo >= dmax_t && plo < P) {
                 pfull = plo;                    // no W in [dmin_t, dmax_t): plo is also the
@@ -531,11 +549,11 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
                 const int dmax = pq_hi - POSL(k0);
                 while (w_lo < dmin) {
                     ++plo;
-                    w_lo = plo < P ? tab.W[plo] : INT32_MAX;
+                    w_lo = plo < P ? Wt(plo) : INT32_MAX;
                 }
                 while (w_full < dmax) {
                     ++pfull;
-                    w_full = pfull < P ? tab.W[pfull] : INT32_MAX;
+                    w_full = pfull < P ? Wt(pfull) : INT32_MAX;
                 }
                 const int jn = pfull >> 3;
                 if (pfull != q_key && jn < NB) {
@@ -558,10 +576,10 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
                             const int kk = 32 * sub + key_of_reg(r, h);
-                            cnt += (16 * (r >> 3) + (r & 7) <= lim && pq - sPos[kk] <= tab.W[e]) ? 1 : 0;
+                            cnt += (16 * (r >> 3) + (r & 7) <= lim && pq - sPos[kk] <= Wt(e)) ? 1 : 0;
                         }
                     } else {
-                        const int c = n_off_le(lim) - n_off_le(lim - tab.W[e] - 1);
+                        const int c = n_off_le(lim) - n_off_le(lim - Wt(e) - 1);
                         cnt += c > 0 ? c : 0;
                     }
                 }
@@ -579,7 +597,7 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
                 for (int e = plo; e < pfull; ++e) {
                     const u32x4 qe = Qf(e >> 3) & pair_mask(e & 7);
                     T = __builtin_amdgcn_mfma_f32_32x32x16_f16(K(e >> 3), __builtin_bit_cast(f16x8, qe), T, 0, 0, 0);
-                    const int t = lim - tab.W[e];              // inside iff off(r) >= t
+                    const int t = lim - Wt(e);              // inside iff off(r) >= t
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
                         if (16 * (r >> 3) + (r & 7) < t) T[r] = 0.f;
@@ -609,7 +627,7 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
                             const int sh = (e & 1) * 16;
                             const float fqx = f16_bits_to_f32((sel4(qx, e >> 1) >> sh) & 0xffffu);
                             const float fqy = f16_bits_to_f32((sel4(qy, e >> 1) >> sh) & 0xffffu);
-                            const int Wi = tab.W[8 * j + e];
+                            const int Wi = Wt(8 * j + e);
 #pragma unroll
                             for (int r = 0; r < 16; ++r) {
                                 const int kk = 32 * sub + key_of_reg(r, h);
@@ -913,6 +931,12 @@ hipError_t launch_d(const PrefillParams& p, const Tables& t, hipStream_t s) {
         const size_t bits = sparse_bitmap_bytes<D>(p.N);
         if (cn) prefill_kernel<D, F32, false, true, false, true><<<grid, block, bits, s>>>(p, t, L);
         else prefill_kernel<D, F32, false, false, false, true><<<grid, block, bits, s>>>(p, t, L);
+    } else if (p.head_theta) {
+        // per-head rotation frequencies (one-shot prefill only)
+        if (hp && cn) prefill_kernel<D, F32, true, true, false, false, false, true><<<grid, block, 0, s>>>(p, t, L);
+        else if (hp) prefill_kernel<D, F32, true, false, false, false, false, true><<<grid, block, 0, s>>>(p, t, L);
+        else if (cn) prefill_kernel<D, F32, false, true, false, false, false, true><<<grid, block, 0, s>>>(p, t, L);
+        else prefill_kernel<D, F32, false, false, false, false, false, true><<<grid, block, 0, s>>>(p, t, L);
     } else if (hp && cn) prefill_kernel<D, F32, true, true, false, false><<<grid, block, 0, s>>>(p, t, L);
     else if (hp) prefill_kernel<D, F32, true, false, false, false><<<grid, block, 0, s>>>(p, t, L);
     else if (cn) prefill_kernel<D, F32, false, true, false, false><<<grid, block, 0, s>>>(p, t, L);

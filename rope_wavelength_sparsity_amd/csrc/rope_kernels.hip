@@ -86,12 +86,15 @@ __global__ __launch_bounds__(256) void rope_keys_kernel(RopeParams p, Tables tab
         load8<F32>(p.k, row + P + 8 * j, y);
     }
     const int64_t pos = p.pos ? (int64_t)p.pos[(int64_t)b * p.n + t] : p.t0 + t;
+    // rotation frequencies: the shared table, or kv head g's row of the per-head tables
+    const double* hth = p.head_theta ? p.head_theta + (int64_t)g * P : nullptr;
+    auto TH = [&](int i) { return hth ? hth[i] : tab.theta[i]; };
     uint32_t ox[4], oy[4];
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
         float s0, c0, s1, c1;
-        rope_sincos(pos, tab.theta[8 * j + e], &s0, &c0);
-        rope_sincos(pos, tab.theta[8 * j + e + 1], &s1, &c1);
+        rope_sincos(pos, TH(8 * j + e), &s0, &c0);
+        rope_sincos(pos, TH(8 * j + e + 1), &s1, &c1);
         float x0 = round_bf16(x[e]), y0 = round_bf16(y[e]);
         float x1 = round_bf16(x[e + 1]), y1 = round_bf16(y[e + 1]);
         ox[e / 2] = pack_f16x2(x0 * c0 - y0 * s0, x1 * c1 - y1 * s1);

@@ -40,6 +40,7 @@ double window_value(int d, double base, const double* inv_freq, double alpha, in
 }
 
 const double* freq_table(const wpa_rope_t* rope) { return rope ? rope->inv_freq : nullptr; }
+const double* head_tables(const wpa_rope_t* rope) { return rope ? rope->head_inv_freq : nullptr; }
 int interleaved(const wpa_rope_t* rope) { return rope && rope->pairs == WPA_PAIRS_INTERLEAVED; }
 
 // The RoPE description: a known pair layout; a frequency table positive, finite and
@@ -47,6 +48,13 @@ int interleaved(const wpa_rope_t* rope) { return rope && rope->pairs == WPA_PAIR
 int check_rope(int32_t d, double base, const wpa_rope_t* rope) {
     if (rope && rope->pairs != WPA_PAIRS_HALF && rope->pairs != WPA_PAIRS_INTERLEAVED)
         return fail(WPA_ERR_INVALID, "rope pairs must be WPA_PAIRS_HALF or WPA_PAIRS_INTERLEAVED");
+    if (head_tables(rope)) {
+        // per-kv-head tables live on the device: their values are the caller's contract
+        if (freq_table(rope)) return fail(WPA_ERR_INVALID, "give inv_freq or head_inv_freq, not both");
+        if (reinterpret_cast<uintptr_t>(head_tables(rope)) & 7u)
+            return fail(WPA_ERR_INVALID, "head_inv_freq must be 8-byte aligned");
+        return WPA_OK;
+    }
     const double* f = freq_table(rope);
     if (!f) {
         if (!(base > 1.0) || !std::isfinite(base)) return fail(WPA_ERR_INVALID, "rope base must be finite and > 1");
@@ -65,6 +73,14 @@ int check_rope(int32_t d, double base, const wpa_rope_t* rope) {
 int32_t window_int(double t) {
     if (!(t < (double)INT32_MAX)) return INT32_MAX;
     return (int32_t)std::floor(t);
+}
+
+// Paths that take one table for all heads only (their windows or cache layouts are fixed
+// on the host, or their kernels read the launch's table).
+int no_head_tables(const wpa_rope_t* rope, const char* what) {
+    if (head_tables(rope))
+        return fail(WPA_ERR_UNSUPPORTED, "%s takes no per-head frequency tables", what);
+    return WPA_OK;
 }
 
 int check_common(int32_t d, double base, const wpa_rope_t* rope, double alpha) {
@@ -185,7 +201,9 @@ const char* wpa_last_error(void) { return g_err; }
 
 int wpa_thresholds_ex(int32_t d, double base, const wpa_rope_t* rope, double alpha, int32_t* W) {
     if (d < 2 || d > 128 || (d & 1)) return fail(WPA_ERR_INVALID, "d must be even and in [2, 128]");
-    const int rc = check_rope(d, base, rope);
+    int rc = check_rope(d, base, rope);
+    if (rc) return rc;
+    rc = no_head_tables(rope, "wpa_thresholds_ex (host only: pass one head's table as inv_freq)");
     if (rc) return rc;
     if (!(alpha >= 0.0)) return fail(WPA_ERR_INVALID, "alpha must be >= 0");
     if (!W) return fail(WPA_ERR_INVALID, "W is null");
@@ -205,7 +223,9 @@ int wpa_count_terms(int32_t d, double base, double alpha, int64_t n_q, int64_t q
 int wpa_count_terms_ex(int32_t d, double base, const wpa_rope_t* rope, double alpha, int64_t n_q,
                        int64_t q_pos0, int64_t n_k, int64_t* kept, int64_t* total) {
     if (d < 2 || (d & 1)) return fail(WPA_ERR_INVALID, "d must be even and >= 2");
-    const int rc = check_rope(d, base, rope);
+    int rc = check_rope(d, base, rope);
+    if (rc) return rc;
+    rc = no_head_tables(rope, "wpa_count_terms_ex (host only: count each head with its table as inv_freq)");
     if (rc) return rc;
     if (!(alpha >= 0.0)) return fail(WPA_ERR_INVALID, "alpha must be >= 0");
     if (n_q < 0 || n_k < 0 || q_pos0 < 0) return fail(WPA_ERR_INVALID, "negative count or position");
@@ -274,6 +294,7 @@ int wpa_prefill_prepare_ex(const void* k, const void* v, const int32_t* position
     rp.n = N; rp.t0 = 0; rp.ld = Np; rp.pad_to = Np; rp.kl = dense_layout(d, Np);
     rp.B = B; rp.Hkv = Hkv; rp.d = d; rp.in_f32 = dtype == WPA_FP32; rp.v_transposed = 1;
     rp.interleaved = interleaved(rope);
+    rp.head_theta = head_tables(rope);
     rp.tab = &tab;
     hipError_t e = wpa::launch_rope_relayout(rp, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(WPA_ERR_HIP, "rope relayout launch: %s", hipGetErrorString(e));
@@ -346,6 +367,8 @@ int attend_impl(const void* q, void* out, float* lse, const int32_t* positions, 
     pp.Hkv = Hkv; pp.d = d; pp.in_f32 = dtype == WPA_FP32; pp.out_f32 = out_dtype == WPA_FP32;
     pp.scale = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)d));
     pp.blk_count = blk_count; pp.blk_idx = blk_idx; pp.blk_max = blk_max;
+    pp.head_theta = head_tables(rope);
+    pp.alpha = alpha;
     hipError_t e = wpa::launch_prefill(pp, tab, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(WPA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
     return ok();
@@ -400,6 +423,8 @@ int wpa_prefill_sparse(const void* q, const void* k, const void* v, void* out, f
     if (rc) return rc;
     if (B < 1 || N < 1 || Hq < 1 || Hkv < 1) return fail(WPA_ERR_INVALID, "B, N, Hq, Hkv must be >= 1");
     if (Hq % Hkv) return fail(WPA_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+    rc = no_head_tables(rope, "wpa_prefill_sparse");
+    if (rc) return rc;
     if (N > ((int64_t)1 << 21)) return fail(WPA_ERR_UNSUPPORTED, "block-sparse prefill supports N up to 2^21 tokens");
     if (!blk_count || (blk_max > 0 && !blk_idx) || blk_max < 0)
         return fail(WPA_ERR_INVALID, "block lists: need blk_count, blk_max >= 0 and blk_idx when blk_max > 0");
@@ -477,6 +502,7 @@ int kv_write_impl(const void* k, const void* v, int64_t start, int64_t n, void* 
     rp.B = B; rp.Hkv = Hkv; rp.d = d; rp.in_f32 = dtype == WPA_FP32; rp.v_transposed = 0;
     rp.tab = &tab;
     rp.pg = pg;
+    rp.head_theta = head_tables(rope);
     hipError_t e = wpa::launch_rope_relayout(rp, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(WPA_ERR_HIP, "kv write launch: %s", hipGetErrorString(e));
     return ok();
@@ -531,6 +557,8 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache, const i
     dp.d = d; dp.in_f32 = dtype == WPA_FP32; dp.out_f32 = out_dtype == WPA_FP32; dp.chunk = ch; dp.n_chunks = (int)((Lmax + ch - 1) / ch);
     dp.scale = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)d));
     dp.pg = pg;
+    dp.head_theta = head_tables(rope);
+    dp.alpha = alpha;
     hipError_t e = wpa::launch_decode(dp, tab, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(WPA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
     return ok();
@@ -626,6 +654,7 @@ size_t wpa_kcache_window_bytes(int32_t B, int64_t Lmax, int32_t Hkv, int32_t d, 
                                const wpa_rope_t* rope, double cache_alpha) {
     if (B < 1 || Lmax < 1 || Hkv < 1 || Lmax >= (int64_t)INT32_MAX) return 0;
     if (check_common(d, base, rope, 1.0) || check_cache_alpha(cache_alpha)) return 0;
+    if (no_head_tables(rope, "a windowed cache")) return 0;
     return (size_t)B * Hkv * window_layout(d, Lmax, base, rope, cache_alpha).head * 32;
 }
 
@@ -636,6 +665,8 @@ int wpa_kv_write_window(const void* k, const void* v, int64_t start, int64_t n, 
     int rc = check_common(d, base, rope, 1.0);
     if (rc) return rc;
     rc = check_cache_alpha(cache_alpha);
+    if (rc) return rc;
+    rc = no_head_tables(rope, "wpa_kv_write_window");
     if (rc) return rc;
     return kv_write_impl(k, v, start, n, k_cache, v_cache, B, Lmax, Hkv, d, base, rope,
                          window_layout(d, Lmax, base, rope, cache_alpha), dtype, stream);
@@ -650,6 +681,8 @@ int wpa_decode_window(const void* q, const void* k_cache, const void* v_cache,
     int rc = check_common(d, base, rope, alpha);
     if (rc) return rc;
     rc = check_cache_alpha(cache_alpha);
+    if (rc) return rc;
+    rc = no_head_tables(rope, "wpa_decode_window");
     if (rc) return rc;
     if (alpha > cache_alpha)
         return fail(WPA_ERR_INVALID, "alpha (%g) exceeds the cache's window alpha (%g)", alpha, cache_alpha);
@@ -769,6 +802,8 @@ int prefill_cached_impl(const void* q, const void* k_cache, const void* v_cache,
                         int32_t out_dtype, unsigned long long* term_count, void* stream,
                         const wpa::Paging& pg, const int32_t* cu_q) {
     int rc = check_common(d, base, rope, alpha);
+    if (rc) return rc;
+    rc = no_head_tables(rope, "chunked prefill");
     if (rc) return rc;
     if (B < 1 || Nq < 1 || Lmax < 1 || Hq < 1 || Hkv < 1) return fail(WPA_ERR_INVALID, "B, Nq, Lmax, Hq, Hkv must be >= 1");
     if (Nq > Lmax) return fail(WPA_ERR_INVALID, "Nq (%d) exceeds Lmax (%lld)", Nq, (long long)Lmax);

@@ -97,6 +97,15 @@ __device__ inline float wave_sum(float v) {
     return v;
 }
 
+// Window of a pair with rotation frequency theta: floor(alpha * (2*pi / theta)) in IEEE
+// double, or INT32_MAX when that is not below INT32_MAX (an unbounded window; also a NaN).
+// The same expression and rounding as the host's table, so per-head tables computed here give
+// the decisions the host would.
+__device__ inline int window_from_theta(double alpha, double theta) {
+    const double t = alpha * ((2.0 * M_PI) / theta);
+    return t < (double)INT32_MAX ? (int)floor(t) : INT32_MAX;
+}
+
 // First index i in [0, P) with W[i] >= x (W non-decreasing), or P.  Uniform across the
 // wave; W lives in kernel arguments.
 __device__ inline int first_at_least(const int32_t* W, int P, int64_t x) {

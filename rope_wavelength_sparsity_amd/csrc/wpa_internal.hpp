@@ -58,6 +58,7 @@ struct RopeParams {
     int32_t interleaved;          // pair i = dims (2i, 2i+1) instead of (i, i+d/2)
     const Tables* tab;            // host pointer; copied into kernel arguments
     Paging pg;                    // decode cache writes: pages (table null: kl layout)
+    const double* head_theta;     // [Hkv][d/2] device: per-kv-head frequencies, or null (tab)
 };
 
 struct PrefillParams {
@@ -81,6 +82,8 @@ struct PrefillParams {
     Paging pg;                    // cached prefill on paged caches (kp, vt: the pools)
     const int32_t* cu_q;          // cached prefill, varlen: [B+1] first packed q row of each
                                   // sequence (q, out [rows][Hq][d], lse [rows][Hq]); else null
+    const double* head_theta;     // [Hkv][d/2] device: per-kv-head frequencies (windows are
+    double alpha;                 // computed from them and alpha in the kernel), or null (tab)
 };
 
 struct DecodeParams {
@@ -99,6 +102,8 @@ struct DecodeParams {
     int32_t interleaved;          // pair i = dims (2i, 2i+1) instead of (i, i+d/2)
     float scale;
     Paging pg;                    // pools of pages (table null: kl layout, [B][Hkv][..] V)
+    const double* head_theta;     // [Hkv][d/2] device: per-kv-head frequencies, or null (tab)
+    double alpha;
 };
 
 hipError_t launch_rope_relayout(const RopeParams& p, hipStream_t s);

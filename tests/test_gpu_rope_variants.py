@@ -105,3 +105,143 @@ def test_decode_variants_match_oracle(table, pairs, alpha):
     closed = sum(wpa.count_terms(d, base, alpha, 1, int(L) - 1, int(L), inv_freq=theta)[0]
                  for L in lens.tolist())
     assert int(cnt.item()) == kept == Hq * closed
+
+
+# ------------------------------------------------------------------ per-kv-head tables
+# One rotation-frequency row per kv head (its q heads use the same row): the rows here are
+# RoPE tables of different bases and Llama-3-style scalings, so every kv head has its own
+# windows.
+
+def _head_rows(Hkv, d):
+    rows = []
+    for g in range(Hkv):
+        base = (1e4, 5e5, 1e6, 1e7)[g % 4]
+        t = wpa.default_inv_freq(d, base)
+        if g % 2:
+            t = wpa.llama3_inv_freq(d, base, factor=8.0 * (g + 1), low_freq_factor=1.0,
+                                    high_freq_factor=4.0, original_max_position=4096)
+        rows.append(t)
+    return np.stack(rows)
+
+
+def _head_count(d, alpha, N, rows, G):
+    return wpa.count_terms_heads(d, alpha, N, 0, N, rows, G)[0]
+
+
+@pytest.mark.parametrize("alpha", [1.0, 2.0])
+@pytest.mark.parametrize("pairs", ["half", "interleaved"])
+@pytest.mark.parametrize("shape", [
+    (1, 700, 14, 2, 64),               # Qwen2.5-0.5B heads
+    (2, 400, 24, 8, 128),              # Llama-3.2-3B heads
+])
+def test_prefill_per_head_tables_match_oracle(shape, pairs, alpha):
+    need_gpu()
+    B, N, Hq, Hkv, d = shape
+    rows = _head_rows(Hkv, d)
+    q, k, v = synth.prefill_inputs(B, N, Hq, Hkv, d, "bf16", seed=60 + N)
+    say("prefill per-head tables", shape, pairs, alpha)
+    cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
+    out, lse = wpa.prefill(q.cuda(), k.cuda(), v.cuda(), 1e4, alpha, want_lse=True,
+                           term_count=cnt, out_dtype=torch.float32, inv_freq=rows, pairs=pairs)
+    torch.cuda.synchronize()
+    ro, rl, kept = oracle.prefill(as_bf16_for_oracle(q), as_bf16_for_oracle(k),
+                                  as_bf16_for_oracle(v), 1e4, alpha, inv_freq=rows, layout=pairs)
+    check_close(out.cpu().numpy(), ro, "out")
+    check_close(lse.cpu().numpy(), rl, "lse", LSE_MAX, LSE_MAX)
+    assert int(cnt.item()) == kept == B * _head_count(d, alpha, N, rows, Hq // Hkv)
+
+
+def test_prefill_per_head_tables_with_positions():
+    """Explicit (gapped) positions with per-head rows, at d = 128 and d = 64."""
+    need_gpu()
+    for (B, N, Hq, Hkv, d) in ((1, 600, 8, 4, 128), (2, 500, 6, 2, 64)):
+        rows = _head_rows(Hkv, d)
+        q, k, v = synth.prefill_inputs(B, N, Hq, Hkv, d, "bf16", seed=61)
+        pos = (np.cumsum(np.random.default_rng(9).integers(0, 30, (B, N)), axis=1) + 77).astype(np.int32)
+        say("per-head tables, positions", d)
+        cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
+        out, lse = wpa.prefill(q.cuda(), k.cuda(), v.cuda(), 1e4, 1.0, want_lse=True,
+                               term_count=cnt, out_dtype=torch.float32, inv_freq=rows,
+                               positions=torch.from_numpy(pos).cuda())
+        torch.cuda.synchronize()
+        ro, rl, kept = oracle.prefill(as_bf16_for_oracle(q), as_bf16_for_oracle(k),
+                                      as_bf16_for_oracle(v), 1e4, 1.0, pos=pos, inv_freq=rows)
+        check_close(out.cpu().numpy(), ro, "out d=%d" % d)
+        check_close(lse.cpu().numpy(), rl, "lse", LSE_MAX, LSE_MAX)
+        assert int(cnt.item()) == kept
+
+
+def test_per_head_tables_equal_rows_is_bitwise_shared_table():
+    need_gpu()
+    B, N, Hq, Hkv, d, base = 1, 900, 24, 8, 128, 5e5
+    theta = _table("llama3", d, base)
+    q, k, v = synth.prefill_inputs(B, N, Hq, Hkv, d, "bf16", seed=62)
+    say("per-head rows all equal")
+    a = wpa.prefill(q.cuda(), k.cuda(), v.cuda(), base, 1.0, inv_freq=theta, out_dtype=torch.float32)
+    b = wpa.prefill(q.cuda(), k.cuda(), v.cuda(), base, 1.0, inv_freq=np.stack([theta] * Hkv),
+                    out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_decode_per_head_tables_match_oracle():
+    """The decode step and the cache write with per-head rows (contiguous and paged caches)."""
+    need_gpu()
+    B, Lmax, Hq, Hkv, d = 4, 3000, 24, 8, 128
+    rows = _head_rows(Hkv, d)
+    q, k, v, lens = synth.decode_inputs(B, Lmax, Hq, Hkv, d, "bf16", seed=63, len_lo=500)
+    say("decode per-head tables")
+    cache = wpa.KVCache(B, Lmax, Hkv, d, 1e4, inv_freq=rows)
+    cache.write(k.cuda(), v.cuda(), 0)
+    cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
+    out, lse = wpa.decode(q.cuda(), cache, lens.cuda(), 1.0, want_lse=True, term_count=cnt,
+                          out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ro, rl, kept = oracle.decode(synth.to_oracle(q), synth.to_oracle(k), synth.to_oracle(v),
+                                 lens.numpy(), 1e4, 1.0, inv_freq=rows)
+    check_close(out.cpu().numpy(), ro, "out")
+    check_close(lse.cpu().numpy(), rl, "lse", LSE_MAX, LSE_MAX)
+    assert int(cnt.item()) == kept == sum(
+        wpa.count_terms_heads(d, 1.0, 1, int(L) - 1, int(L), rows, Hq // Hkv)[0] for L in lens)
+    # the same tokens in a paged pool give the same bits
+    ps, maxp = 256, (Lmax + 255) // 256
+    table = torch.arange(B * maxp, dtype=torch.int32).flip(0).reshape(B, maxp).contiguous().cuda()
+    paged = wpa.PagedKVCache(B * maxp, ps, Hkv, d, 1e4, inv_freq=rows)
+    paged.write(k.cuda(), v.cuda(), 0, block_table=table)
+    op = wpa.decode(q.cuda(), paged, lens.cuda(), 1.0, out_dtype=torch.float32, block_table=table)
+    torch.cuda.synchronize()
+    assert torch.equal(op.cpu(), out.cpu())
+
+
+def test_per_head_tables_unsupported_paths():
+    need_gpu()
+    rows = _head_rows(2, 64)
+    cache = wpa.KVCache(1, 256, 2, 64, 1e4, inv_freq=rows)
+    q = torch.zeros((1, 32, 4, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(wpa.WpaError) as e:
+        wpa.prefill_cached(q, cache, torch.full((1,), 64, dtype=torch.int32, device="cuda"), 1.0)
+    assert e.value.code == wpa.WPA_ERR_UNSUPPORTED
+    with pytest.raises(ValueError):              # the windowed cache's size query refuses
+        wpa.KVCache(1, 256, 2, 64, 1e4, inv_freq=rows, window_alpha=1.0)
+
+
+def test_full_size_llama3b_per_head_tables():
+    """The Llama-3.2-3B-shaped prefill at its full 131072 tokens with a distinct frequency row
+    per kv head, in the bench's launch configuration: sampled rows against the oracle, exact
+    count (per head, summed)."""
+    need_gpu()
+    w = synth.WORKLOADS["llama3b"]
+    rows = _head_rows(w.Hkv, w.d)
+    say("full size llama3b per-head tables")
+    q, k, v = synth.workload_inputs(w, device="cuda")
+    cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
+    out = wpa.prefill(q, k, v, w.base, 1.0, term_count=cnt, out_dtype=torch.float32, inv_freq=rows)
+    torch.cuda.synchronize()
+    srows = synth.sample_rows(w.N, 24, seed=w.seed)
+    got = out[:, torch.as_tensor(srows, device="cuda")].cpu().numpy()
+    del out
+    say("oracle rows", len(srows))
+    ro, _, _ = oracle.prefill(synth.to_oracle(q), synth.to_oracle(k), synth.to_oracle(v), w.base, 1.0,
+                              rows=srows, inv_freq=rows)
+    check_close(got, ro, "llama3b per-head sampled rows")
+    assert int(cnt.item()) == _head_count(w.d, 1.0, w.N, rows, w.Hq // w.Hkv)

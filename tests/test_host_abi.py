@@ -487,3 +487,32 @@ def test_binding_rejects_bad_decode_buffers(cpu_as_device, monkeypatch):
             wpa.decode(q, FakeCache(), lens, 1.0, **kw)
     with pytest.raises(ValueError):                          # q of the wrong rank
         wpa.decode(q[0], FakeCache(), lens, 1.0)
+
+
+def test_per_head_tables_are_validated_on_the_host():
+    """The binding checks per-kv-head rows before uploading them; the C ABI refuses per-head
+    tables where it does not take them, and both inv_freq and head_inv_freq at once."""
+    import torch
+    d, Hkv = 64, 2
+    good = np.stack([wpa.default_inv_freq(d, 1e4), wpa.default_inv_freq(d, 1e6)])
+    for bad in (good[:, ::-1].copy(), -good, good[:1]):
+        with pytest.raises(ValueError):
+            wpa.head_table(bad, d, Hkv, "cpu")
+    assert wpa.head_table(good, d, Hkv, "cpu").dtype == torch.float64
+    # host-only queries take one row at a time
+    kept, total = wpa.count_terms_heads(d, 1.0, 300, 0, 300, good, 3)
+    assert kept == 3 * (wpa.count_terms(d, 1e4, 1.0, 300, 0, 300)[0] +
+                        wpa.count_terms(d, 1e6, 1.0, 300, 0, 300)[0])
+    r = wpa.Rope(0, None, ctypes.c_void_p(1 << 20).value)
+    W = (ctypes.c_int32 * (d // 2))()
+    assert wpa.lib().wpa_thresholds_ex(d, 1e4, ctypes.byref(r), 1.0, W) == wpa.WPA_ERR_UNSUPPORTED
+    r2 = wpa.Rope(0, good[0].ctypes.data, ctypes.c_void_p(1 << 20).value)
+    assert _prefill_ex_rc(ctypes.byref(r2)) == wpa.WPA_ERR_INVALID
+    r3 = wpa.Rope(0, None, ctypes.c_void_p((1 << 20) + 4).value)
+    assert _prefill_ex_rc(ctypes.byref(r3)) == wpa.WPA_ERR_INVALID
+
+
+def _prefill_ex_rc(rope):
+    L = wpa.lib()
+    return L.wpa_prefill_ex(FAKE, FAKE, FAKE, FAKE, None, None, 1, 128, 4, 2, 64, 1e4, rope, 1.0, 0.0,
+                            0, 0, None, FAKE, 1 << 30, None)
