@@ -60,6 +60,9 @@ def _load():
         lib.orc_prefill_sparse.argtypes = [P, P, P, I, I, I64, I, I, I, D, P, I, D, D, P, P, I, I,
                                            P, I64, P, P, P, I]
         lib.orc_prefill_sparse.restype = I
+        lib.orc_prefill_backward_ex.argtypes = [P, P, P, P, I, P, I, I64, I, I, I, D, P, I, I, D, D,
+                                                P, I64, P, I64, P, P, P, I]
+        lib.orc_prefill_backward_ex.restype = I
         lib.orc_decode_ex.argtypes = [P, P, P, I, P, P, I, I64, I, I, I, D, P, I, I, D, D, P, P, P,
                                       I]
         lib.orc_decode_ex.restype = I
@@ -166,6 +169,45 @@ def prefill(q, k, v, base: float, alpha: float, scale: float | None = None, pos=
     if rc != 0:
         raise ValueError("orc_prefill rejected its arguments")
     return out, lse, kept.value
+
+
+def prefill_backward(q, k, v, dout, base: float, alpha: float, scale: float | None = None,
+                     pos=None, rows=None, keys=None, nthreads: int = 0, inv_freq=None,
+                     layout: str = "half"):
+    """Gradients of the windowed causal prefill for dout = dL/dout [B][N][Hq][d] (same dtype as
+    q, k, v): dq at query rows `rows`, dk and dv at key rows `keys` (None: all).  Returns
+    (dq [B][R][Hq][d], dk [B][K][Hkv][d], dv [B][K][Hkv][d]) in fp64, with respect to the
+    pre-RoPE q and k."""
+    q, dt = _as_input(q)
+    k, dk_ = _as_input(k)
+    v, dv_ = _as_input(v)
+    g, dg = _as_input(dout)
+    assert dt == dk_ == dv_ == dg
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    assert g.shape == q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if pos is not None:
+        pos = np.ascontiguousarray(pos, dtype=np.int32).reshape(B, N)
+    R, K = N, N
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        R = rows.shape[0]
+    if keys is not None:
+        keys = np.ascontiguousarray(keys, dtype=np.int64)
+        K = keys.shape[0]
+    dq = np.empty((B, R, Hq, d), dtype=np.float64)
+    dk = np.empty((B, K, Hkv, d), dtype=np.float64)
+    dv = np.empty((B, K, Hkv, d), dtype=np.float64)
+    tab, ntab = _freq_heads(inv_freq, d, Hkv)
+    rc = _load().orc_prefill_backward_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), dt, _ptr(pos), B, N,
+                                         Hq, Hkv, d, float(base), _ptr(tab), ntab, LAYOUTS[layout],
+                                         float(alpha), float(scale), _ptr(rows), R, _ptr(keys), K,
+                                         _ptr(dq), _ptr(dk), _ptr(dv), int(nthreads))
+    if rc != 0:
+        raise ValueError("orc_prefill_backward rejected its arguments")
+    return dq, dk, dv
 
 
 def prefill_sparse(q, k, v, base: float, alpha: float, count, idx, blk: int = 64,

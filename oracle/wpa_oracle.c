@@ -425,6 +425,183 @@ int orc_decode(const void* q, const void* k, const void* v, int dtype, const int
 }
 
 /*
+ * Backward of the windowed causal prefill (WavePrune, What the paper found: models trained
+ * with the window from scratch; training needs these gradients).  Given dout = dL/dout for a
+ * scalar loss L, the chain rule through the forward above, step by step:
+ *   P_rc    = softmax over visible c of the windowed logits l_rc (recomputed, fp64)
+ *   dv_c   += P_rc dout_r                                  (every q head of kv head g)
+ *   dP_rc   = dout_r . v_c
+ *   D_r     = sum_c P_rc dP_rc                             (= dout_r . out_r)
+ *   dl_rc   = P_rc (dP_rc - D_r)
+ *   dq'_r  += scale * dl_rc * [pair of x kept at r-c] * k'_c[x]     (rotated coordinates)
+ *   dk'_c  += scale * dl_rc * [pair of x kept at r-c] * q'_r[x]
+ *   dq_r    = R(t_r)^T dq'_r,  dk_c = R(t_c)^T dk'_c      (rotation by minus the angle)
+ * Only the gradients asked for are formed: dq at query rows rows[n_rows], dk and dv at key
+ * rows keys[n_keys] (NULL: all N).  Inputs as for orc_prefill_ex; dout [B][N][Hq][d] in the
+ * same dtype.  Outputs (double): dq [B][n_rows][Hq][d], dk and dv [B][n_keys][Hkv][d].
+ */
+int orc_prefill_backward_ex(const void* q, const void* k, const void* v, const void* dout,
+                            int dtype, const int32_t* pos, int B, int64_t N, int Hq, int Hkv,
+                            int d, double base, const double* inv_freq, int n_tables,
+                            int interleaved, double alpha, double scale, const int64_t* rows,
+                            int64_t n_rows, const int64_t* keys, int64_t n_keys, double* dq,
+                            double* dk, double* dv, int nthreads) {
+    if (B < 1 || N < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || d < 2 || d % 2 != 0 || d > 256)
+        return -1;
+    if (n_tables > 1 && (n_tables != Hkv || !inv_freq)) return -1;
+    if (!rows) n_rows = N;
+    if (!keys) n_keys = N;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#endif
+    int G = Hq / Hkv, P = d / 2;
+    int esz = dtype == ORC_FP32 ? 4 : 2;
+    double* thr = orc_head_thresholds(d, base, inv_freq, n_tables, Hkv, alpha);
+    int64_t* p64 = (int64_t*)malloc(sizeof(int64_t) * N);
+    double* kr = (double*)malloc(sizeof(double) * N * Hkv * d);
+    double* qr = (double*)malloc(sizeof(double) * N * Hq * d);
+    double* lse = (double*)malloc(sizeof(double) * N * Hq);
+    double* Dr = (double*)malloc(sizeof(double) * N * Hq);
+    unsigned char* need = (unsigned char*)malloc((size_t)N);
+    for (int b = 0; b < B; ++b) {
+        for (int64_t t = 0; t < N; ++t) p64[t] = pos ? (int64_t)pos[(int64_t)b * N + t] : t;
+        const char* qb = (const char*)q + (size_t)esz * b * N * Hq * d;
+        const char* kb = (const char*)k + (size_t)esz * b * N * Hkv * d;
+        const char* vb = (const char*)v + (size_t)esz * b * N * Hkv * d;
+        const char* ob = (const char*)dout + (size_t)esz * b * N * Hq * d;
+        orc_rotate(kb, dtype, N, Hkv, d, p64, base, inv_freq, n_tables, interleaved, kr);
+        orc_rotate(qb, dtype, N, Hq, d, p64, base, inv_freq, n_tables, interleaved, qr);
+        /* rows whose softmax statistics are needed: the dq rows, and every row at or after
+         * the first dk/dv key (those rows see it) */
+        int64_t kmin = N;
+        for (int64_t j = 0; j < n_keys; ++j) {
+            int64_t c = keys ? keys[j] : j;
+            if (c < kmin) kmin = c;
+        }
+        for (int64_t r = 0; r < N; ++r) need[r] = r >= kmin;
+        for (int64_t j = 0; j < n_rows; ++j) need[rows ? rows[j] : j] = 1;
+        /* forward statistics of the needed rows: lse_r and D_r = dout_r . out_r */
+        #pragma omp parallel
+        {
+            double* logit = (double*)malloc(sizeof(double) * N);
+            double* o = (double*)malloc(sizeof(double) * d);
+            #pragma omp for schedule(dynamic, 1) collapse(2)
+            for (int64_t r = 0; r < N; ++r) {
+                for (int h = 0; h < Hq; ++h) {
+                    if (!need[r]) continue;
+                    double l;
+                    orc_row(qr + (r * Hq + h) * (int64_t)d, p64[r], kr, p64, vb, dtype, r, Hkv,
+                            h / G, d, interleaved, thr + (int64_t)(h / G) * P, scale, logit, o, &l,
+                            NULL);
+                    double dd = 0.0;
+                    for (int e = 0; e < d; ++e) dd += orc_load(ob, dtype, (r * Hq + h) * (int64_t)d + e) * o[e];
+                    lse[r * Hq + h] = l;
+                    Dr[r * Hq + h] = dd;
+                }
+            }
+            free(logit);
+            free(o);
+        }
+        /* dq at the requested rows */
+        #pragma omp parallel for schedule(dynamic, 1) collapse(2)
+        for (int64_t j = 0; j < n_rows; ++j) {
+            for (int h = 0; h < Hq; ++h) {
+                int64_t r = rows ? rows[j] : j;
+                int g = h / G;
+                const double* th = thr + (int64_t)g * P;
+                const double* qv = qr + (r * Hq + h) * (int64_t)d;
+                double acc[256];
+                for (int e = 0; e < d; ++e) acc[e] = 0.0;
+                for (int64_t c = 0; c <= r; ++c) {
+                    const double* kv = kr + (c * Hkv + g) * (int64_t)d;
+                    double dist = fabs((double)(p64[r] - p64[c]));
+                    double s = 0.0, dp = 0.0;
+                    for (int i = 0; i < P; ++i) {
+                        if (dist <= th[i]) {
+                            int ix = orc_dim_x(i, d, interleaved), iy = orc_dim_y(i, d, interleaved);
+                            s += qv[ix] * kv[ix] + qv[iy] * kv[iy];
+                        }
+                    }
+                    double pr = exp(scale * s - lse[r * Hq + h]);
+                    for (int e = 0; e < d; ++e)
+                        dp += orc_load(ob, dtype, (r * Hq + h) * (int64_t)d + e) *
+                              orc_load(vb, dtype, (c * Hkv + g) * (int64_t)d + e);
+                    double dl = pr * (dp - Dr[r * Hq + h]);
+                    for (int i = 0; i < P; ++i) {
+                        if (dist <= th[i]) {
+                            int ix = orc_dim_x(i, d, interleaved), iy = orc_dim_y(i, d, interleaved);
+                            acc[ix] += scale * dl * kv[ix];
+                            acc[iy] += scale * dl * kv[iy];
+                        }
+                    }
+                }
+                /* back to pre-RoPE coordinates: R(t_r)^T */
+                double* out = dq + (((int64_t)b * n_rows + j) * Hq + h) * d;
+                for (int i = 0; i < P; ++i) {
+                    double th_i = n_tables > 1 ? inv_freq[(int64_t)g * P + i]
+                                               : (inv_freq ? inv_freq[i] : pow(base, -(2.0 * i) / (double)d));
+                    double a = (double)p64[r] * th_i, cs = cos(a), sn = sin(a);
+                    int ix = orc_dim_x(i, d, interleaved), iy = orc_dim_y(i, d, interleaved);
+                    out[ix] = acc[ix] * cs + acc[iy] * sn;
+                    out[iy] = -acc[ix] * sn + acc[iy] * cs;
+                }
+            }
+        }
+        /* dk, dv at the requested keys: every row r >= c of every q head of kv head g */
+        #pragma omp parallel for schedule(dynamic, 1) collapse(2)
+        for (int64_t j = 0; j < n_keys; ++j) {
+            for (int g = 0; g < Hkv; ++g) {
+                int64_t c = keys ? keys[j] : j;
+                const double* th = thr + (int64_t)g * P;
+                const double* kv = kr + (c * Hkv + g) * (int64_t)d;
+                double acck[256], accv[256];
+                for (int e = 0; e < d; ++e) acck[e] = accv[e] = 0.0;
+                for (int h = g * G; h < (g + 1) * G; ++h) {
+                    for (int64_t r = c; r < N; ++r) {
+                        const double* qv = qr + (r * Hq + h) * (int64_t)d;
+                        double dist = fabs((double)(p64[r] - p64[c]));
+                        double s = 0.0, dp = 0.0;
+                        for (int i = 0; i < P; ++i) {
+                            if (dist <= th[i]) {
+                                int ix = orc_dim_x(i, d, interleaved), iy = orc_dim_y(i, d, interleaved);
+                                s += qv[ix] * kv[ix] + qv[iy] * kv[iy];
+                            }
+                        }
+                        double pr = exp(scale * s - lse[r * Hq + h]);
+                        for (int e = 0; e < d; ++e) {
+                            double go = orc_load(ob, dtype, (r * Hq + h) * (int64_t)d + e);
+                            accv[e] += pr * go;
+                            dp += go * orc_load(vb, dtype, (c * Hkv + g) * (int64_t)d + e);
+                        }
+                        double dl = pr * (dp - Dr[r * Hq + h]);
+                        for (int i = 0; i < P; ++i) {
+                            if (dist <= th[i]) {
+                                int ix = orc_dim_x(i, d, interleaved), iy = orc_dim_y(i, d, interleaved);
+                                acck[ix] += scale * dl * qv[ix];
+                                acck[iy] += scale * dl * qv[iy];
+                            }
+                        }
+                    }
+                }
+                double* ok = dk + (((int64_t)b * n_keys + j) * Hkv + g) * d;
+                double* ov = dv + (((int64_t)b * n_keys + j) * Hkv + g) * d;
+                for (int e = 0; e < d; ++e) ov[e] = accv[e];
+                for (int i = 0; i < P; ++i) {
+                    double th_i = n_tables > 1 ? inv_freq[(int64_t)g * P + i]
+                                               : (inv_freq ? inv_freq[i] : pow(base, -(2.0 * i) / (double)d));
+                    double a = (double)p64[c] * th_i, cs = cos(a), sn = sin(a);
+                    int ix = orc_dim_x(i, d, interleaved), iy = orc_dim_y(i, d, interleaved);
+                    ok[ix] = acck[ix] * cs + acck[iy] * sn;
+                    ok[iy] = -acck[ix] * sn + acck[iy] * cs;
+                }
+            }
+        }
+    }
+    free(thr); free(p64); free(kr); free(qr); free(lse); free(Dr); free(need);
+    return 0;
+}
+
+/*
  * Kept-term count by enumeration (no closed form): queries at token indices
  * q_idx0 .. q_idx0+n_q-1 with positions equal to their indices, keys 0..n_k-1,
  * key c visible to query r iff c <= r; counts (r, c, i) with |r-c| <= alpha*lambda_i.

@@ -598,3 +598,121 @@ def test_per_head_tables_count_and_decode():
                               inv_freq=tabs)
     np.testing.assert_allclose(do, po[:, 0], rtol=0, atol=1e-12)
     np.testing.assert_allclose(dl, pl[:, :, 0], rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------------------
+# Backward (WavePrune, What the paper found: training with the window).  Pins: torch
+# autograd, in fp64 on the CPU, through the relative complex form (no rotation of q or k, no
+# back-rotation: an independent route to the pre-RoPE gradients), and central finite
+# differences of the pinned forward.
+
+def _torch_relative_loss(q, k, v, dout, pos, theta, alpha, scale, layout="half"):
+    """sum(out * dout) of windowed attention written with the relative form of each pair's
+    term, q [N][Hq][d], k, v [N][Hkv][d] (torch fp64, requires_grad on q, k, v)."""
+    N, Hq, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    dx, dy = _dims(d, layout)
+    th = torch.as_tensor(theta, dtype=torch.float64)
+    tpos = torch.as_tensor(np.asarray(pos), dtype=torch.float64)
+    dt = tpos[:, None] - tpos[None, :]
+    keep = (dt.abs()[..., None] <= alpha * (2.0 * math.pi / th)).to(torch.float64)
+    rot = torch.exp(1j * dt[..., None] * th)
+    causal = torch.arange(N)[None, :] <= torch.arange(N)[:, None]
+    loss = 0.0
+    for h in range(Hq):
+        g = h // G
+        zq = torch.complex(q[:, h, dx], q[:, h, dy])
+        zk = torch.complex(k[:, g, dx], k[:, g, dy])
+        terms = torch.real(zq[:, None, :] * torch.conj(zk[None, :, :]) * rot)
+        logits = scale * (terms * keep).sum(-1)
+        logits = logits.masked_fill(~causal, float("-inf"))
+        out = torch.softmax(logits, dim=-1) @ v[:, g]
+        loss = loss + (out * dout[:, h]).sum()
+    return loss
+
+
+@pytest.mark.parametrize("alpha", [0.5, 1.0, 2.0, math.inf])
+@pytest.mark.parametrize("positions", ["default", "gapped"])
+def test_backward_equals_autograd_of_relative_form(alpha, positions):
+    N, Hq, Hkv, d, base = 33, 4, 2, 16, 100.0
+    q, k, v = synth.prefill_inputs(1, N, Hq, Hkv, d, "fp32", seed=71)
+    g = torch.randn((1, N, Hq, d), generator=torch.Generator().manual_seed(72))
+    pos = np.arange(N) if positions == "default" else \
+        np.cumsum(np.random.default_rng(11).integers(0, 7, N))
+    dq, dk, dv = oracle.prefill_backward(synth.to_oracle(q), synth.to_oracle(k), synth.to_oracle(v),
+                                         synth.to_oracle(g), base, alpha, pos=pos)
+    theta = base ** (-np.arange(d // 2) * 2.0 / d)
+    tq, tk, tv = (torch.from_numpy(_f64(t[0])).requires_grad_() for t in (q, k, v))
+    loss = _torch_relative_loss(tq, tk, tv, torch.from_numpy(_f64(g[0])), pos, theta, alpha,
+                                1.0 / math.sqrt(d))
+    loss.backward()
+    np.testing.assert_allclose(dq[0], tq.grad.numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dk[0], tk.grad.numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dv[0], tv.grad.numpy(), rtol=0, atol=1e-11)
+
+
+def test_backward_equals_autograd_per_head_tables_interleaved():
+    N, Hq, Hkv, d = 25, 4, 2, 16
+    q, k, v = synth.prefill_inputs(1, N, Hq, Hkv, d, "fp32", seed=73)
+    g = torch.randn((1, N, Hq, d), generator=torch.Generator().manual_seed(74))
+    tabs = _head_tables(Hkv, d, 12)
+    pos = np.arange(N)
+    dq, dk, dv = oracle.prefill_backward(synth.to_oracle(q), synth.to_oracle(k), synth.to_oracle(v),
+                                         synth.to_oracle(g), 1e4, 1.0, inv_freq=tabs,
+                                         layout="interleaved")
+    G = Hq // Hkv
+    for gg in range(Hkv):
+        hs = slice(gg * G, (gg + 1) * G)
+        tq = torch.from_numpy(_f64(q[0, :, hs])).requires_grad_()
+        tk = torch.from_numpy(_f64(k[0, :, gg:gg + 1])).requires_grad_()
+        tv = torch.from_numpy(_f64(v[0, :, gg:gg + 1])).requires_grad_()
+        loss = _torch_relative_loss(tq, tk, tv, torch.from_numpy(_f64(g[0, :, hs])), pos, tabs[gg],
+                                    1.0, 1.0 / math.sqrt(d), layout="interleaved")
+        loss.backward()
+        np.testing.assert_allclose(dq[0, :, hs], tq.grad.numpy(), rtol=0, atol=1e-11)
+        np.testing.assert_allclose(dk[0, :, gg:gg + 1], tk.grad.numpy(), rtol=0, atol=1e-11)
+        np.testing.assert_allclose(dv[0, :, gg:gg + 1], tv.grad.numpy(), rtol=0, atol=1e-11)
+
+
+def test_backward_equals_finite_differences_of_forward():
+    """Central differences of sum(out * dout) through the (pinned) forward, on fp32 inputs: the
+    step applied is the exact fp32 difference, so the quotient is accurate to O(eps^2)."""
+    N, Hq, Hkv, d, base, alpha = 14, 2, 1, 8, 30.0, 1.0
+    q, k, v = synth.prefill_inputs(1, N, Hq, Hkv, d, "fp32", seed=75)
+    g = torch.randn((1, N, Hq, d), generator=torch.Generator().manual_seed(76))
+    ga = synth.to_oracle(g).astype(np.float64)
+    dq, dk, dv = oracle.prefill_backward(synth.to_oracle(q), synth.to_oracle(k), synth.to_oracle(v),
+                                         synth.to_oracle(g), base, alpha)
+    arrs = [synth.to_oracle(t).copy() for t in (q, k, v)]
+
+    def loss(a):
+        out, _, _ = oracle.prefill(*a, base, alpha)
+        return float((out * ga).sum())
+
+    rng = np.random.default_rng(13)
+    for which, grad in ((0, dq), (1, dk), (2, dv)):
+        for _ in range(12):
+            idx = tuple(int(rng.integers(0, s)) for s in arrs[which].shape)
+            x0 = arrs[which][idx]
+            hi, lo = np.float32(x0 + 1e-2), np.float32(x0 - 1e-2)
+            arrs[which][idx] = hi
+            lp = loss(arrs)
+            arrs[which][idx] = lo
+            lm = loss(arrs)
+            arrs[which][idx] = x0
+            fd = (lp - lm) / (float(hi) - float(lo))
+            assert abs(fd - grad[idx]) <= 2e-5 * max(1.0, abs(grad[idx])), (which, idx, fd, grad[idx])
+
+
+def test_backward_row_and_key_subsets_equal_full():
+    N, Hq, Hkv, d = 40, 6, 2, 32
+    q, k, v = synth.prefill_inputs(2, N, Hq, Hkv, d, "bf16", seed=77)
+    g = synth.prefill_inputs(2, N, Hq, Hkv, d, "bf16", seed=78)[0]
+    a = [synth.to_oracle(t) for t in (q, k, v, g)]
+    full = oracle.prefill_backward(*a, 1e4, 1.0)
+    rows, keys = np.array([0, 7, 39]), np.array([3, 38, 39])
+    part = oracle.prefill_backward(*a, 1e4, 1.0, rows=rows, keys=keys)
+    np.testing.assert_array_equal(part[0], full[0][:, rows])
+    np.testing.assert_array_equal(part[1], full[1][:, keys])
+    np.testing.assert_array_equal(part[2], full[2][:, keys])
