@@ -392,6 +392,33 @@ int wpa_prefill_paged_varlen(const void* q, const void* k_pool, const void* v_po
                              unsigned long long* term_count, void* stream);
 
 /*
+ * Backward of the causal windowed prefill, for training with the window (WavePrune, "What the
+ * paper found": models trained from scratch with each pair's term limited to its first
+ * rotation period).  Given the forward's inputs q, k, v (pre-RoPE, bf16, [B][N][H][d]), its
+ * output `out` [B][N][Hq][d] (out_dtype) and `lse` [B][Hq][N] (fp32, natural log, as
+ * wpa_prefill writes them), and dout = dL/dout [B][N][Hq][d] (bf16), writes the gradients of
+ * L with respect to the pre-RoPE q, k and v:
+ *   dq [B][N][Hq][d], dk and dv [B][N][Hkv][d] (grad_dtype: WPA_BF16 or WPA_FP32)
+ * with P recomputed under the same window, dl = P (dout.v - dout.out), dq' = scale sum_c dl k'
+ * and dk' = scale sum_r dl q' restricted to the pairs kept at each distance, and dq, dk the
+ * rotated gradients rotated back by minus their position's angle.  Positions are token indices
+ * (the one-shot prefill's default).  Rotated q and k are rounded to IEEE half, dl to half and P
+ * to bf16 for the MFMA products, which accumulate in fp32.  rope: pair layout and one shared
+ * frequency table (per-head tables: WPA_ERR_UNSUPPORTED).  dtype must be WPA_BF16
+ * (WPA_ERR_UNSUPPORTED otherwise).  workspace: 256-byte aligned, at least
+ * wpa_prefill_backward_workspace_bytes(B, N, Hq, Hkv, d) bytes (it holds the rotated and
+ * transposed operands and per-q-head dk/dv partials).
+ */
+size_t wpa_prefill_backward_workspace_bytes(int32_t B, int64_t N, int32_t Hq, int32_t Hkv,
+                                            int32_t d);
+int wpa_prefill_backward(const void* q, const void* k, const void* v, const void* out,
+                         const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                         int32_t B, int64_t N, int32_t Hq, int32_t Hkv, int32_t d, double base,
+                         const wpa_rope_t* rope, double alpha, float scale, int32_t dtype,
+                         int32_t out_dtype, int32_t grad_dtype, void* workspace, size_t ws_bytes,
+                         void* stream);
+
+/*
  * wpa_decode_ex without a workspace, for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid allocation).  Arguments
  * are those of wpa_decode_ex minus workspace and ws_bytes; results are bit-identical to it

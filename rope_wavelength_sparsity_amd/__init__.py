@@ -43,7 +43,7 @@ EXPORTS = ("wpa_count_terms", "wpa_thresholds", "wpa_prefill_workspace_bytes", "
            "wpa_kv_write_window", "wpa_decode_window", "wpa_prefill_sparse", "wpa_kv_page_bytes",
            "wpa_kv_write_paged", "wpa_decode_paged", "wpa_prefill_paged",
            "wpa_prefill_cached_varlen", "wpa_prefill_paged_varlen", "wpa_decode_noalloc",
-           "wpa_last_error")
+           "wpa_prefill_backward_workspace_bytes", "wpa_prefill_backward", "wpa_last_error")
 
 
 class Rope(ctypes.Structure):
@@ -205,6 +205,11 @@ def lib():
     L.wpa_decode_noalloc.argtypes = [P, P, P, P, P, P, P, I32, I64, I32, I32, I32, D, P, D, F, I32,
                                      I32, P, I32, P]
     L.wpa_decode_noalloc.restype = ctypes.c_int
+    L.wpa_prefill_backward_workspace_bytes.argtypes = [I32, I64, I32, I32, I32]
+    L.wpa_prefill_backward_workspace_bytes.restype = SZ
+    L.wpa_prefill_backward.argtypes = [P, P, P, P, P, P, P, P, P, I32, I64, I32, I32, I32, D, P, D, F,
+                                       I32, I32, I32, P, SZ, P]
+    L.wpa_prefill_backward.restype = ctypes.c_int
     L.wpa_last_error.argtypes = []
     L.wpa_last_error.restype = ctypes.c_char_p
     _lib = L
@@ -408,6 +413,48 @@ def prefill(q, k, v, base: float, alpha: float, *, scale: float | None = None, p
                                 _dtype_code(out), _ptr(term_count), _ptr(workspace),
                                 _ws_bytes(workspace), _stream(stream)))
     return (out, lse) if lse is not None else out
+
+
+def prefill_backward_workspace_bytes(B, N, Hq, Hkv, d) -> int:
+    return lib().wpa_prefill_backward_workspace_bytes(B, N, Hq, Hkv, d)
+
+
+def prefill_backward(q, k, v, out, lse, dout, base: float, alpha: float, *, scale=None,
+                     grad_dtype=None, dq=None, dk=None, dv=None, workspace=None, stream=None,
+                     inv_freq=None, pairs: str = "half"):
+    """Gradients (dq, dk, dv) of the windowed causal prefill with respect to the pre-RoPE q, k
+    and v, for dout = dL/dout.  q, k, v, dout bf16 ([B][N][Hq|Hkv][d]); out and lse are the
+    forward's (prefill(..., want_lse=True)); positions are token indices.  grad_dtype:
+    torch.float32 (default) or torch.bfloat16."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout"), (lse, "lse")):
+        _dev(t, n)
+        _same_device(t, q, n)
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
+        raise ValueError("q [B][N][Hq][d], k, v [B][N][Hkv][d] expected")
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if k.shape[0] != B or k.shape[1] != N or k.shape[3] != d:
+        raise ValueError("q, k, v shapes disagree")
+    if not (q.dtype == k.dtype == v.dtype == dout.dtype == torch.bfloat16):
+        raise ValueError("the backward takes bf16 q, k, v and dout")
+    if tuple(out.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape):
+        raise ValueError("out and dout must be shaped like q")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, N):
+        raise ValueError("lse must be float32 [B][Hq][N]")
+    gdt = grad_dtype or torch.float32
+    dq = _out(dq, q.shape, q, gdt)
+    dk = _out(dk, k.shape, q, gdt)
+    dv = _out(dv, v.shape, q, gdt)
+    if not (dq.dtype == dk.dtype == dv.dtype):
+        raise ValueError("dq, dk, dv must share one dtype")
+    workspace = _workspace(workspace, prefill_backward_workspace_bytes(B, N, Hq, Hkv, d), q)
+    rope, keep = _rope(d, inv_freq, pairs, Hkv, q.device)
+    _check(lib().wpa_prefill_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout),
+                                      _ptr(dq), _ptr(dk), _ptr(dv), B, N, Hq, Hkv, d, float(base),
+                                      rope, float(alpha), float(scale) if scale is not None else 0.0,
+                                      WPA_BF16, _dtype_code(out), _dtype_code(dq), _ptr(workspace),
+                                      _ws_bytes(workspace), _stream(stream)))
+    return dq, dk, dv
 
 
 def prefill_prepare(k, v, base: float, *, positions=None, workspace=None, stream=None,

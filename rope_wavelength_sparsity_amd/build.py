@@ -16,7 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libwpa.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["wpa_api.cpp", "rope_kernels.hip", "prefill_kernel.hip", "decode_kernels.hip"]
+SOURCES = ["wpa_api.cpp", "rope_kernels.hip", "prefill_kernel.hip", "decode_kernels.hip",
+           "backward_kernels.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

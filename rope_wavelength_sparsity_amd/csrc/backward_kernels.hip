@@ -1,0 +1,569 @@
+// Backward of the causal prefill with a per-RoPE-wavelength window, on gfx950 MFMA
+// (WavePrune, What the paper found: models trained with the window need its gradients).
+//
+// For dout = dL/dout, with P the windowed softmax of the forward (recomputed from the
+// forward's lse), per q head and per visible (row r, key c):
+//   dP_rc = dout_r . v_c,   D_r = dout_r . out_r,   dl_rc = P_rc (dP_rc - D_r)
+//   dv_c  = sum_r P_rc dout_r
+//   dq'_r = scale * sum_c dl_rc [pair of x kept at r-c] k'_c[x]    (rotated coordinates)
+//   dk'_c = scale * sum_r dl_rc [pair of x kept at r-c] q'_r[x]
+// and dq, dk are dq', dk' rotated back by minus the RoPE angle.  The window keeps a pair's
+// term only inside its distance, so in the dq and dk contractions each 32x32 block uses the
+// same band plan as the forward: dims of dead pairs are skipped, fully active pairs are one
+// MFMA per 16-dim block, and each pair whose window edge falls inside the block is one MFMA
+// with dl masked to the elements inside its window.
+//
+// Kernels
+//   bwd_prep_k: rotated keys, pair-blocked K' [B][Hkv][d/16][Np][16] and transposed K'^T
+//               [B][Hkv][d][Np] (pair-block element order), IEEE half.
+//   bwd_prep_q: rotated queries Q' (times scale*log2 e) pair-blocked, Q'^T (unscaled)
+//               transposed, dout^T [B][Hq][d][Np] bf16, lse*log2 e and D per row.
+//   bwd_dq:     one wave per (sequence, q head, 32 query rows): S^T, P^T, dP^T, dl^T over the
+//               causal key blocks, dq'^T on MFMA; epilogue rotates back and writes dq.
+//   bwd_dkdv:   one wave per (sequence, q head, 32 keys): S, P, dP, dl over the causal row
+//               blocks, dv^T and dk'^T on MFMA, written per q head to a workspace.
+//   bwd_reduce: sums the q heads of each kv head, rotates dk' back, writes dk and dv.
+// Waves take a short and a long row (or key) range in turn, so causal work balances.
+//
+// MFMA layouts (32x32x16): A row m / B column n in lane m%32 / n%32, the 16-deep contraction
+// split 8+8 between lane halves; C element (8(r/4) + 4(l/32) + r%4, l%32) in register r of
+// lane l.  A-operand rows are permuted (bits 2 and 3 swapped) wherever the result feeds a
+// contraction over that index, so that C registers 0-7 / 8-15 of lane half h hold indices
+// 8h..8h+7 / 16+8h..16+8h+7: exactly the B operand of the next MFMA.
+#include "wpa_device.hpp"
+#include "wpa_internal.hpp"
+
+namespace wpa {
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ inline int perm_row(int m) {
+    return (m & ~0xC) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+// Index (row or key) held by C register r of lane half h when the A rows were permuted.
+__device__ inline int idx_of_reg(int r, int h) {
+    return 16 * (r >> 3) + 8 * h + (r & 7);
+}
+
+__device__ inline int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// The element e of an 8-pair block alone (both halves), as a mask on the packed block.
+__device__ inline u32x4 pair_mask(int e) {
+    u32x4 q;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+        q[t] = (e >> 1) == t ? ((e & 1) ? 0xffff0000u : 0xffffu) : 0u;
+    return q;
+}
+
+// Leading nz pairs of an 8-pair block zeroed, as a mask on the packed block.
+__device__ inline u32x4 lead_mask(int nz) {
+    u32x4 q;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+        q[t] = ((2 * t >= nz) ? 0xffffu : 0u) | ((2 * t + 1 >= nz) ? 0xffff0000u : 0u);
+    return q;
+}
+
+__device__ inline u32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+__device__ inline f32x16 mfma_h(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+__device__ inline f32x16 mfma_b(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Registers 8s..8s+7 of a C block as a packed 16-deep operand (f16 or bf16).
+template <bool BF>
+__device__ inline u32x4 pack8(const f32x16& c, int s) {
+    u32x4 o;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+        o[t] = BF ? pack_bf16x2(c[8 * s + 2 * t], c[8 * s + 2 * t + 1])
+                  : pack_f16x2(c[8 * s + 2 * t], c[8 * s + 2 * t + 1]);
+    return o;
+}
+
+// Pair of the row x (pair-block element order, x = 16j + e) of a 32-row block db.
+__device__ inline int pair_of_x(int db, int x) { return 8 * (2 * db + (x >> 4)) + (x & 7); }
+
+// Work index i of n (ordered by growing length) as the wave's two ranges: i and n-1-i take
+// turns, so every wave holds one short and one long range.
+__device__ inline int paired(int i, int n, int half) { return half ? n - 1 - i : i; }
+
+// ---------------------------------------------------------------------------- prep kernels
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_k_kernel(BwdParams p, Tables tab) {
+    constexpr int P = D / 2, NB = D / 16;
+    const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t total = (int64_t)p.B * p.Hkv * p.Np;
+    if (id >= total) return;
+    const int64_t t = id % p.Np;
+    const int64_t bg = id / p.Np;
+    uint16_t* ks = p.ks + bg * NB * p.Np * 16;
+    uint16_t* kt = p.kt + bg * D * p.Np;
+    if (t >= p.N) {
+        for (int j = 0; j < NB; ++j) {
+            u32x4* d4 = reinterpret_cast<u32x4*>(ks + ((int64_t)j * p.Np + t) * 16);
+            d4[0] = u32x4{0u, 0u, 0u, 0u};
+            d4[1] = u32x4{0u, 0u, 0u, 0u};
+        }
+        for (int x = 0; x < D; ++x) kt[x * p.Np + t] = 0;
+        return;
+    }
+    const int g = (int)(bg % p.Hkv), b = (int)(bg / p.Hkv);
+    const uint16_t* kr = static_cast<const uint16_t*>(p.k) + (((int64_t)b * p.N + t) * p.Hkv + g) * D;
+    for (int j = 0; j < NB; ++j) {
+        uint16_t el[16];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int i = 8 * j + e;
+            const int ix = p.interleaved ? 2 * i : i, iy = p.interleaved ? 2 * i + 1 : i + P;
+            const float x = bf16_bits_to_f32(kr[ix]), y = bf16_bits_to_f32(kr[iy]);
+            float sn, cs;
+            rope_sincos(t, tab.theta[i], &sn, &cs);
+            el[e] = f32_to_f16_bits(x * cs - y * sn);
+            el[8 + e] = f32_to_f16_bits(y * cs + x * sn);
+        }
+        u32x4 w0, w1;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            w0[q] = (uint32_t)el[2 * q] | ((uint32_t)el[2 * q + 1] << 16);
+            w1[q] = (uint32_t)el[8 + 2 * q] | ((uint32_t)el[8 + 2 * q + 1] << 16);
+        }
+        u32x4* d4 = reinterpret_cast<u32x4*>(ks + ((int64_t)j * p.Np + t) * 16);
+        d4[0] = w0;
+        d4[1] = w1;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) kt[(int64_t)(16 * j + e) * p.Np + t] = el[e];
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_q_kernel(BwdParams p, Tables tab) {
+    constexpr int P = D / 2, NB = D / 16;
+    const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t total = (int64_t)p.B * p.Hq * p.Np;
+    if (id >= total) return;
+    const int64_t t = id % p.Np;
+    const int64_t bh = id / p.Np;
+    uint16_t* qs = p.qs + bh * NB * p.Np * 16;
+    uint16_t* qt = p.qt + bh * D * p.Np;
+    uint16_t* dot = p.dot + bh * D * p.Np;
+    if (t >= p.N) {
+        for (int j = 0; j < NB; ++j) {
+            u32x4* d4 = reinterpret_cast<u32x4*>(qs + ((int64_t)j * p.Np + t) * 16);
+            d4[0] = u32x4{0u, 0u, 0u, 0u};
+            d4[1] = u32x4{0u, 0u, 0u, 0u};
+        }
+        for (int x = 0; x < D; ++x) {
+            qt[x * p.Np + t] = 0;
+            dot[x * p.Np + t] = 0;
+        }
+        p.lse2[bh * p.Np + t] = INFINITY;      // rows past the end: P = 0
+        p.Dr[bh * p.Np + t] = 0.f;
+        return;
+    }
+    const int h = (int)(bh % p.Hq), b = (int)(bh / p.Hq);
+    const int64_t row = (((int64_t)b * p.N + t) * p.Hq + h) * D;
+    const uint16_t* qr = static_cast<const uint16_t*>(p.q) + row;
+    const float sl2 = p.scale * kLog2e;
+    for (int j = 0; j < NB; ++j) {
+        uint16_t es[16], eu[16];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int i = 8 * j + e;
+            const int ix = p.interleaved ? 2 * i : i, iy = p.interleaved ? 2 * i + 1 : i + P;
+            const float x = bf16_bits_to_f32(qr[ix]), y = bf16_bits_to_f32(qr[iy]);
+            float sn, cs;
+            rope_sincos(t, tab.theta[i], &sn, &cs);
+            const float rx = x * cs - y * sn, ry = y * cs + x * sn;
+            es[e] = f32_to_f16_bits(rx * sl2);
+            es[8 + e] = f32_to_f16_bits(ry * sl2);
+            eu[e] = f32_to_f16_bits(rx);
+            eu[8 + e] = f32_to_f16_bits(ry);
+        }
+        u32x4 w0, w1;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            w0[q] = (uint32_t)es[2 * q] | ((uint32_t)es[2 * q + 1] << 16);
+            w1[q] = (uint32_t)es[8 + 2 * q] | ((uint32_t)es[8 + 2 * q + 1] << 16);
+        }
+        u32x4* d4 = reinterpret_cast<u32x4*>(qs + ((int64_t)j * p.Np + t) * 16);
+        d4[0] = w0;
+        d4[1] = w1;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) qt[(int64_t)(16 * j + e) * p.Np + t] = eu[e];
+    }
+    // dout^T (natural dim order) and D = dout . out
+    const uint16_t* gr = static_cast<const uint16_t*>(p.dout) + row;
+    float dd = 0.f;
+    for (int x = 0; x < D; ++x) {
+        const uint16_t gb = gr[x];
+        dot[x * p.Np + t] = gb;
+        const float o = p.out_f32 ? static_cast<const float*>(p.out)[row + x]
+                                  : bf16_bits_to_f32(static_cast<const uint16_t*>(p.out)[row + x]);
+        dd += bf16_bits_to_f32(gb) * o;
+    }
+    p.Dr[bh * p.Np + t] = dd;
+    p.lse2[bh * p.Np + t] = p.lse[((int64_t)b * p.Hq + h) * p.N + t] * kLog2e;
+}
+
+// ---------------------------------------------------------------------------- dq
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void bwd_dq_kernel(BwdParams p, Tables tab) {
+    constexpr int NB = D / 16, NDB = D / 32, P = D / 2;
+    const int lane = threadIdx.x & 63, l32 = lane & 31, h = lane >> 5;
+    const int wave = uniform((int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)));
+    const int nrg = (int)((p.N + 31) / 32);
+    const int npair = (nrg + 1) / 2;                    // waves per (sequence, q head)
+    const int bh = wave / npair;
+    if (bh >= p.B * p.Hq) return;
+    const int hq = bh % p.Hq, b = bh / p.Hq;
+    const int g = hq / (p.Hq / p.Hkv);
+    const int wi = wave % npair;
+    const uint16_t* ksg = p.ks + ((int64_t)b * p.Hkv + g) * NB * p.Np * 16;
+    const uint16_t* ktg = p.kt + ((int64_t)b * p.Hkv + g) * D * p.Np;
+    const uint16_t* qsh = p.qs + (int64_t)bh * NB * p.Np * 16;
+    const float sc = p.scale;
+
+    for (int half = 0; half < 2; ++half) {
+        const int rg = paired(wi, nrg, half);
+        if (half == 1 && rg == wi) break;               // odd count: the middle group once
+        const int r0 = 32 * rg;
+        const int row = r0 + l32;
+        const bool row_ok = row < p.N;
+        const int rowc = row_ok ? row : (int)p.N - 1;
+        // B operands held for the row group: Q' (scaled) and dout, lane = row
+        u32x4 Qb[NB], Gb[NB];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            Qb[j] = ld16(qsh + ((int64_t)j * p.Np + row) * 16 + 8 * h);
+            Gb[j] = ld16(static_cast<const uint16_t*>(p.dout) +
+                         (((int64_t)b * p.N + rowc) * p.Hq + hq) * D + 16 * j + 8 * h);
+        }
+        const float lse2 = p.lse2[(int64_t)bh * p.Np + row];
+        const float Dv = p.Dr[(int64_t)bh * p.Np + row];
+        f32x16 acc[NDB];
+#pragma unroll
+        for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
+        int plo = 0, pfull = 0;                         // band edges, distances only grow
+        for (int kb = rg; kb >= 0; --kb) {
+            const int c0 = 32 * kb;
+            const int dmin = uniform(r0 - (c0 + 31) > 0 ? r0 - (c0 + 31) : 0);
+            const int dmax = uniform(r0 + 31 - c0);
+            while (plo < P && tab.W[plo] < dmin) ++plo;
+            while (pfull < P && tab.W[pfull] < dmax) ++pfull;
+            if (pfull < plo) pfull = plo;
+            const int arow = c0 + perm_row(l32);        // key this lane feeds to A
+            auto K = [&](int j) { return ld16(ksg + ((int64_t)j * p.Np + arow) * 16 + 8 * h); };
+            // S^T (log2 units): straddling pairs one by one, then the fully active blocks
+            f32x16 S = f32x16{};
+            // register r of half h holds key c0 + idx(r); distance = row - key
+            for (int e = plo; e < pfull; ++e) {
+                S = mfma_h(K(e >> 3), Qb[e >> 3] & pair_mask(e & 7), S);
+                const int We = tab.W[e];
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (row - (c0 + idx_of_reg(r, h)) > We) S[r] = 0.f;
+            }
+            const int jf = pfull >> 3;
+            for (int j = jf; j < NB; ++j) {
+                const u32x4 qb = j == jf ? (Qb[j] & lead_mask(pfull - 8 * jf)) : Qb[j];
+                S = mfma_h(K(j), qb, S);
+            }
+            // P^T, dP^T, dl^T (lane = row; register = key)
+            f32x16 Pt;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = c0 + idx_of_reg(r, h);
+                Pt[r] = (key <= row && row_ok) ? __builtin_amdgcn_exp2f(S[r] - lse2) : 0.f;
+            }
+            f32x16 dPt = f32x16{};
+            const int vkey = arow < p.N ? arow : (int)p.N - 1;
+            const uint16_t* vr = static_cast<const uint16_t*>(p.v) + (((int64_t)b * p.N + vkey) * p.Hkv + g) * D;
+#pragma unroll
+            for (int j = 0; j < NB; ++j) dPt = mfma_b(ld16(vr + 16 * j + 8 * h), Gb[j], dPt);
+            f32x16 dl;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dl[r] = Pt[r] * (dPt[r] - Dv);
+            // dq'^T += K'^T dl^T over the fully active pairs' dims ...
+            const u32x4 dlb[2] = {pack8<false>(dl, 0), pack8<false>(dl, 1)};
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                if (2 * db + 1 < jf) continue;              // every dim of this block dead or straddling
+                const bool on = pair_of_x(db, l32) >= pfull;
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    u32x4 a = ld16(ktg + (int64_t)(32 * db + l32) * p.Np + c0 + 16 * s + 8 * h);
+                    if (!on) a = u32x4{0u, 0u, 0u, 0u};
+                    acc[db] = mfma_h(a, dlb[s], acc[db]);
+                }
+            }
+            // ... and each straddling pair with dl masked to its window
+            for (int e = plo; e < pfull; ++e) {
+                const int We = tab.W[e];
+                f32x16 m;
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    m[r] = (row - (c0 + idx_of_reg(r, h)) <= We) ? dl[r] : 0.f;
+                const int db = e >> 4;
+                const bool on = pair_of_x(db, l32) == e;
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    u32x4 a = ld16(ktg + (int64_t)(32 * db + l32) * p.Np + c0 + 16 * s + 8 * h);
+                    if (!on) a = u32x4{0u, 0u, 0u, 0u};
+                    // (db is wave-uniform: select the accumulator without indexing)
+#pragma unroll
+                    for (int dd = 0; dd < NDB; ++dd)
+                        if (dd == db) acc[dd] = mfma_h(a, pack8<false>(m, s), acc[dd]);
+                }
+            }
+        }
+        // epilogue: scale, rotate back at the row's position, write dq (lane = row)
+        if (row_ok) {
+            const int64_t ob = (((int64_t)b * p.N + row) * p.Hq + hq) * D;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    if ((r >> 2) & 1) continue;             // y-components: with their x
+                    const int xl = 8 * (r >> 2) + 4 * h + (r & 3);
+                    const int i = 8 * (2 * db + (xl >> 4)) + (xl & 7);
+                    float sn, cs;
+                    rope_sincos(row, tab.theta[i], &sn, &cs);
+                    const float gx = acc[db][r] * sc, gy = acc[db][r + 4] * sc;
+                    const float ox = gx * cs + gy * sn, oy = gy * cs - gx * sn;
+                    const int ix = p.interleaved ? 2 * i : i, iy = p.interleaved ? 2 * i + 1 : i + P;
+                    if (p.grad_f32) {
+                        static_cast<float*>(p.dq)[ob + ix] = ox;
+                        static_cast<float*>(p.dq)[ob + iy] = oy;
+                    } else {
+                        static_cast<uint16_t*>(p.dq)[ob + ix] = f32_to_bf16_bits(ox);
+                        static_cast<uint16_t*>(p.dq)[ob + iy] = f32_to_bf16_bits(oy);
+                    }
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------- dk, dv
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void bwd_dkdv_kernel(BwdParams p, Tables tab) {
+    constexpr int NB = D / 16, NDB = D / 32, P = D / 2;
+    const int lane = threadIdx.x & 63, l32 = lane & 31, h = lane >> 5;
+    const int wave = uniform((int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)));
+    const int nkg = (int)((p.N + 31) / 32);
+    const int npair = (nkg + 1) / 2;
+    const int bh = wave / npair;
+    if (bh >= p.B * p.Hq) return;
+    const int hq = bh % p.Hq, b = bh / p.Hq;
+    const int g = hq / (p.Hq / p.Hkv);
+    const int wi = wave % npair;
+    const uint16_t* ksg = p.ks + ((int64_t)b * p.Hkv + g) * NB * p.Np * 16;
+    const uint16_t* qsh = p.qs + (int64_t)bh * NB * p.Np * 16;
+    const uint16_t* qth = p.qt + (int64_t)bh * D * p.Np;
+    const uint16_t* doth = p.dot + (int64_t)bh * D * p.Np;
+    const float* lse2h = p.lse2 + (int64_t)bh * p.Np;
+    const float* Drh = p.Dr + (int64_t)bh * p.Np;
+
+    for (int half = 0; half < 2; ++half) {
+        // key groups with the most rows first: index 0 is the first key group
+        const int kg = paired(wi, nkg, half);
+        if (half == 1 && kg == wi) break;
+        const int c0 = 32 * kg;
+        const int key = c0 + l32;
+        const int keyc = key < p.N ? key : (int)p.N - 1;
+        const uint16_t* vr = static_cast<const uint16_t*>(p.v) + (((int64_t)b * p.N + keyc) * p.Hkv + g) * D;
+        f32x16 dK[NDB], dV[NDB];
+#pragma unroll
+        for (int i = 0; i < NDB; ++i) {
+            dK[i] = f32x16{};
+            dV[i] = f32x16{};
+        }
+        int plo = 0, pfull = 0;
+        for (int rb = kg; 32 * rb < p.N; ++rb) {
+            const int r0 = 32 * rb;
+            const int dmin = uniform(r0 - (c0 + 31) > 0 ? r0 - (c0 + 31) : 0);
+            const int dmax = uniform(r0 + 31 - c0);
+            while (plo < P && tab.W[plo] < dmin) ++plo;
+            while (pfull < P && tab.W[pfull] < dmax) ++pfull;
+            if (pfull < plo) pfull = plo;
+            const int arow = r0 + perm_row(l32);         // row this lane feeds to A
+            auto Q = [&](int j) { return ld16(qsh + ((int64_t)j * p.Np + arow) * 16 + 8 * h); };
+            auto Kb = [&](int j) { return ld16(ksg + ((int64_t)j * p.Np + key) * 16 + 8 * h); };
+            // S (log2 units): register r of half h holds row r0 + idx(r); distance = row - key
+            f32x16 S = f32x16{};
+            for (int e = plo; e < pfull; ++e) {
+                S = mfma_h(Q(e >> 3), Kb(e >> 3) & pair_mask(e & 7), S);
+                const int We = tab.W[e];
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if ((r0 + idx_of_reg(r, h)) - key > We) S[r] = 0.f;
+            }
+            const int jf = pfull >> 3;
+            for (int j = jf; j < NB; ++j) {
+                const u32x4 kb = j == jf ? (Kb(j) & lead_mask(pfull - 8 * jf)) : Kb(j);
+                S = mfma_h(Q(j), kb, S);
+            }
+            // lse and D of this lane's 16 rows: rows r0 + 8h + 0..7 and r0 + 16 + 8h + 0..7
+            const f32x4* l4 = reinterpret_cast<const f32x4*>(lse2h + r0 + 8 * h);
+            const f32x4* d4 = reinterpret_cast<const f32x4*>(Drh + r0 + 8 * h);
+            const f32x4 la = l4[0], lb = l4[1], lc = l4[4], ld = l4[5];
+            const f32x4 da = d4[0], dbv = d4[1], dc = d4[4], dd = d4[5];
+            auto lse_r = [&](int r) { const f32x4& v = r < 4 ? la : (r < 8 ? lb : (r < 12 ? lc : ld)); return v[r & 3]; };
+            auto D_r = [&](int r) { const f32x4& v = r < 4 ? da : (r < 8 ? dbv : (r < 12 ? dc : dd)); return v[r & 3]; };
+            f32x16 Pm;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = r0 + idx_of_reg(r, h);
+                Pm[r] = key <= row ? __builtin_amdgcn_exp2f(S[r] - lse_r(r)) : 0.f;
+            }
+            // dP = dout V^T (A = dout rows, permuted)
+            f32x16 dP = f32x16{};
+            const int grow = arow < p.N ? arow : (int)p.N - 1;
+            const uint16_t* gr = static_cast<const uint16_t*>(p.dout) + (((int64_t)b * p.N + grow) * p.Hq + hq) * D;
+#pragma unroll
+            for (int j = 0; j < NB; ++j) dP = mfma_b(ld16(gr + 16 * j + 8 * h), ld16(vr + 16 * j + 8 * h), dP);
+            f32x16 dl;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dl[r] = Pm[r] * (dP[r] - D_r(r));
+            // dv^T += dout^T P ; dk'^T += Q'^T dl (fully active pairs' dims, then straddling).
+            // P enters the dv product as two bf16 parts, P = hi + lo: a key's dv sums the
+            // probabilities of every row of every q head of its kv head (an early key's reaches
+            // ~10 and more), where one bf16 rounding of P alone would cost ~2e-2 max-abs.
+            f32x16 Plo;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) Plo[r] = Pm[r] - round_bf16(Pm[r]);
+            const u32x4 pb[2] = {pack8<true>(Pm, 0), pack8<true>(Pm, 1)};
+            const u32x4 pl[2] = {pack8<true>(Plo, 0), pack8<true>(Plo, 1)};
+            const u32x4 dlb[2] = {pack8<false>(dl, 0), pack8<false>(dl, 1)};
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    const u32x4 a = ld16(doth + (int64_t)(32 * db + l32) * p.Np + r0 + 16 * s + 8 * h);
+                    dV[db] = mfma_b(a, pb[s], dV[db]);
+                    dV[db] = mfma_b(a, pl[s], dV[db]);
+                }
+                if (2 * db + 1 < jf) continue;
+                const bool on = pair_of_x(db, l32) >= pfull;
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    u32x4 a = ld16(qth + (int64_t)(32 * db + l32) * p.Np + r0 + 16 * s + 8 * h);
+                    if (!on) a = u32x4{0u, 0u, 0u, 0u};
+                    dK[db] = mfma_h(a, dlb[s], dK[db]);
+                }
+            }
+            for (int e = plo; e < pfull; ++e) {
+                const int We = tab.W[e];
+                f32x16 m;
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    m[r] = ((r0 + idx_of_reg(r, h)) - key <= We) ? dl[r] : 0.f;
+                const int db = e >> 4;
+                const bool on = pair_of_x(db, l32) == e;
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    u32x4 a = ld16(qth + (int64_t)(32 * db + l32) * p.Np + r0 + 16 * s + 8 * h);
+                    if (!on) a = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+                    for (int dd2 = 0; dd2 < NDB; ++dd2)
+                        if (dd2 == db) dK[dd2] = mfma_h(a, pack8<false>(m, s), dK[dd2]);
+                }
+            }
+        }
+        // this q head's dk'^T (unscaled, pair-block order) and dv^T for the lane's key, as
+        // fp32 partials [B][Hq][Np][d]; register r of half h holds x = 32db + 8(r/4) + 4h + r%4
+        float* kp = p.dkp + ((int64_t)bh * p.Np + key) * D;
+        float* vp = p.dvp + ((int64_t)bh * p.Np + key) * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int x = 32 * db + 8 * q4 + 4 * h;
+                *reinterpret_cast<f32x4*>(kp + x) = f32x4{dK[db][4 * q4], dK[db][4 * q4 + 1], dK[db][4 * q4 + 2], dK[db][4 * q4 + 3]};
+                *reinterpret_cast<f32x4*>(vp + x) = f32x4{dV[db][4 * q4], dV[db][4 * q4 + 1], dV[db][4 * q4 + 2], dV[db][4 * q4 + 3]};
+            }
+        }
+    }
+}
+
+// dk, dv of every kv head: the sum over its q heads' partials; dk' scaled and rotated back.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdParams p, Tables tab) {
+    constexpr int P = D / 2;
+    const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t total = (int64_t)p.B * p.Hkv * p.N * P;
+    if (id >= total) return;
+    const int i = (int)(id % P);
+    int64_t rest = id / P;
+    const int64_t t = rest % p.N;
+    rest /= p.N;
+    const int g = (int)(rest % p.Hkv), b = (int)(rest / p.Hkv);
+    const int G = p.Hq / p.Hkv;
+    const int xk = 16 * (i >> 3) + (i & 7), yk = xk + 8;     // pair i in pair-block order
+    const int ix = p.interleaved ? 2 * i : i, iy = p.interleaved ? 2 * i + 1 : i + P;
+    float kx = 0.f, ky = 0.f, vx = 0.f, vy = 0.f;
+    for (int hh = 0; hh < G; ++hh) {
+        const int64_t base = (((int64_t)b * p.Hq + g * G + hh) * p.Np + t) * D;
+        kx += p.dkp[base + xk];
+        ky += p.dkp[base + yk];
+        vx += p.dvp[base + ix];
+        vy += p.dvp[base + iy];
+    }
+    float sn, cs;
+    rope_sincos(t, tab.theta[i], &sn, &cs);
+    kx *= p.scale;
+    ky *= p.scale;
+    const float ox = kx * cs + ky * sn, oy = ky * cs - kx * sn;
+    const int64_t ob = (((int64_t)b * p.N + t) * p.Hkv + g) * D;
+    if (p.grad_f32) {
+        static_cast<float*>(p.dk)[ob + ix] = ox;
+        static_cast<float*>(p.dk)[ob + iy] = oy;
+        static_cast<float*>(p.dv)[ob + ix] = vx;
+        static_cast<float*>(p.dv)[ob + iy] = vy;
+    } else {
+        static_cast<uint16_t*>(p.dk)[ob + ix] = f32_to_bf16_bits(ox);
+        static_cast<uint16_t*>(p.dk)[ob + iy] = f32_to_bf16_bits(oy);
+        static_cast<uint16_t*>(p.dv)[ob + ix] = f32_to_bf16_bits(vx);
+        static_cast<uint16_t*>(p.dv)[ob + iy] = f32_to_bf16_bits(vy);
+    }
+}
+
+template <int D>
+hipError_t launch_bwd_d(const BwdParams& p, const Tables& t, hipStream_t s) {
+    const dim3 blk(256);
+    const int64_t nk = (int64_t)p.B * p.Hkv * p.Np, nq = (int64_t)p.B * p.Hq * p.Np;
+    bwd_prep_k_kernel<D><<<dim3((unsigned)((nk + 255) / 256)), blk, 0, s>>>(p, t);
+    bwd_prep_q_kernel<D><<<dim3((unsigned)((nq + 255) / 256)), blk, 0, s>>>(p, t);
+    const int64_t ngroups = (p.N + 31) / 32;
+    const int64_t waves = (int64_t)p.B * p.Hq * ((ngroups + 1) / 2);
+    const dim3 grid((unsigned)((waves + 3) / 4));
+    bwd_dq_kernel<D><<<grid, blk, 0, s>>>(p, t);
+    bwd_dkdv_kernel<D><<<grid, blk, 0, s>>>(p, t);
+    const int64_t nr = (int64_t)p.B * p.Hkv * p.N * (D / 2);
+    bwd_reduce_kernel<D><<<dim3((unsigned)((nr + 255) / 256)), blk, 0, s>>>(p, t);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_backward(const BwdParams& p, const Tables& t, hipStream_t s) {
+    return p.d == 64 ? launch_bwd_d<64>(p, t, s) : launch_bwd_d<128>(p, t, s);
+}
+
+}  // namespace wpa

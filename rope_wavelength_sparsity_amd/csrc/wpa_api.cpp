@@ -459,6 +459,82 @@ int wpa_prefill_sparse(const void* q, const void* k, const void* v, void* out, f
                        blk_idx ? blk_idx : blk_count, blk_max);
 }
 
+// Workspace of the prefill backward: its regions, in order, each 256-byte aligned.
+struct BwdLayout {
+    size_t off[9];
+    size_t total;
+};
+
+BwdLayout bwd_layout(int32_t B, int64_t N, int32_t Hq, int32_t Hkv, int32_t d) {
+    const int64_t Np = round_up(N, wpa::kTileKeys);
+    const size_t kvh = (size_t)B * Hkv * Np * d, qh = (size_t)B * Hq * Np * d, rows = (size_t)B * Hq * Np;
+    const size_t sz[9] = {kvh * 2, kvh * 2, qh * 2, qh * 2, qh * 2, rows * 4, rows * 4, qh * 4, qh * 4};
+    BwdLayout L{};
+    size_t at = 0;
+    for (int i = 0; i < 9; ++i) {
+        L.off[i] = at;
+        at += (sz[i] + 255) / 256 * 256;
+    }
+    L.total = at;
+    return L;
+}
+
+size_t wpa_prefill_backward_workspace_bytes(int32_t B, int64_t N, int32_t Hq, int32_t Hkv, int32_t d) {
+    if (B < 1 || N < 1 || Hq < 1 || Hkv < 1 || d < 1) return 0;
+    return bwd_layout(B, N, Hq, Hkv, d).total;
+}
+
+int wpa_prefill_backward(const void* q, const void* k, const void* v, const void* out,
+                         const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                         int32_t B, int64_t N, int32_t Hq, int32_t Hkv, int32_t d, double base,
+                         const wpa_rope_t* rope, double alpha, float scale, int32_t dtype,
+                         int32_t out_dtype, int32_t grad_dtype, void* workspace, size_t ws_bytes,
+                         void* stream) {
+    int rc = check_common(d, base, rope, alpha);
+    if (rc) return rc;
+    rc = no_head_tables(rope, "wpa_prefill_backward");
+    if (rc) return rc;
+    if (B < 1 || N < 1 || Hq < 1 || Hkv < 1) return fail(WPA_ERR_INVALID, "B, N, Hq, Hkv must be >= 1");
+    if (Hq % Hkv) return fail(WPA_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+    if (N >= (int64_t)INT32_MAX - wpa::kTileKeys) return fail(WPA_ERR_INVALID, "N too large");
+    if (dtype != WPA_BF16) return fail(WPA_ERR_UNSUPPORTED, "the backward takes bf16 q, k, v and dout");
+    if (out_dtype != WPA_BF16 && out_dtype != WPA_FP32) return fail(WPA_ERR_INVALID, "out_dtype must be WPA_BF16 or WPA_FP32");
+    if (grad_dtype != WPA_BF16 && grad_dtype != WPA_FP32) return fail(WPA_ERR_INVALID, "grad_dtype must be WPA_BF16 or WPA_FP32");
+    if (std::isnan(scale)) return fail(WPA_ERR_INVALID, "scale is NaN");
+    if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv || !workspace)
+        return fail(WPA_ERR_INVALID, "null pointer");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) ||
+        !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace) ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return fail(WPA_ERR_INVALID, "tensors must be 16-byte aligned and the workspace 256-byte aligned");
+    if (reinterpret_cast<uintptr_t>(lse) & 3u) return fail(WPA_ERR_INVALID, "lse must be 4-byte aligned");
+    const BwdLayout L = bwd_layout(B, N, Hq, Hkv, d);
+    if (ws_bytes < L.total) return fail(WPA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
+    wpa::Tables tab;
+    make_tables(d, base, rope, alpha, &tab);
+    char* w = static_cast<char*>(workspace);
+    wpa::BwdParams bp{};
+    bp.q = q; bp.k = k; bp.v = v; bp.out = out; bp.lse = lse; bp.dout = dout;
+    bp.dq = dq; bp.dk = dk; bp.dv = dv;
+    bp.ks = reinterpret_cast<uint16_t*>(w + L.off[0]);
+    bp.kt = reinterpret_cast<uint16_t*>(w + L.off[1]);
+    bp.qs = reinterpret_cast<uint16_t*>(w + L.off[2]);
+    bp.qt = reinterpret_cast<uint16_t*>(w + L.off[3]);
+    bp.dot = reinterpret_cast<uint16_t*>(w + L.off[4]);
+    bp.lse2 = reinterpret_cast<float*>(w + L.off[5]);
+    bp.Dr = reinterpret_cast<float*>(w + L.off[6]);
+    bp.dkp = reinterpret_cast<float*>(w + L.off[7]);
+    bp.dvp = reinterpret_cast<float*>(w + L.off[8]);
+    bp.N = N; bp.Np = round_up(N, wpa::kTileKeys);
+    bp.B = B; bp.Hq = Hq; bp.Hkv = Hkv; bp.d = d;
+    bp.out_f32 = out_dtype == WPA_FP32; bp.grad_f32 = grad_dtype == WPA_FP32;
+    bp.interleaved = interleaved(rope);
+    bp.scale = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)d));
+    hipError_t e = wpa::launch_backward(bp, tab, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(WPA_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
 size_t wpa_kcache_bytes(int32_t B, int64_t Lmax, int32_t Hkv, int32_t d) {
     if (B < 1 || Lmax < 1 || Hkv < 1 || d < 1) return 0;
     return (size_t)B * Hkv * Lmax * d * 2;

@@ -106,7 +106,36 @@ struct DecodeParams {
     double alpha;
 };
 
+// Backward of the one-shot prefill (positions = token indices).  Inputs q, k, v, dout bf16
+// ([B][N][H][d]), out (forward output, out_f32 ? fp32 : bf16), lse [B][Hq][N] fp32; outputs
+// dq, dk, dv (grad_f32 ? fp32 : bf16) in the inputs' layouts.  Workspace regions (device):
+struct BwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* out;
+    const float* lse;
+    const void* dout;
+    void* dq;
+    void* dk;
+    void* dv;
+    uint16_t* ks;                 // rotated K' pair-blocked [B][Hkv][d/16][Np][16] half
+    uint16_t* kt;                 // rotated K'^T [B][Hkv][d][Np] half (pair-block row order)
+    uint16_t* qs;                 // rotated Q' * scale*log2 e, pair-blocked [B][Hq][d/16][Np][16]
+    uint16_t* qt;                 // rotated Q'^T (unscaled) [B][Hq][d][Np] half
+    uint16_t* dot;                // dout^T [B][Hq][d][Np] bf16
+    float* lse2;                  // lse * log2 e [B][Hq][Np] (+inf past N)
+    float* Dr;                    // dout . out [B][Hq][Np]
+    float* dkp;                   // per-q-head dk'^T partials [B][Hq][Np][d] (pair-block order)
+    float* dvp;                   // per-q-head dv partials [B][Hq][Np][d]
+    int64_t N, Np;
+    int32_t B, Hq, Hkv, d, out_f32, grad_f32;
+    int32_t interleaved;
+    float scale;
+};
+
 hipError_t launch_rope_relayout(const RopeParams& p, hipStream_t s);
+hipError_t launch_backward(const BwdParams& p, const Tables& t, hipStream_t s);
 hipError_t launch_prefill(const PrefillParams& p, const Tables& t, hipStream_t s);
 // LDS bytes a block-sparse prefill launch for p (d, dtype, N, counter) needs, and the
 // device's per-workgroup limit; nothing is enqueued.
