@@ -68,6 +68,10 @@ def _parse():
                     help="instead of the headline line: the paths beside the core one (windowed "
                          "decode cache, chunked prefill, RoPE variants, block-sparse prefill), "
                          "printed as one JSON line")
+    ap.add_argument("--backward", action="store_true",
+                    help="instead of the headline line: the prefill backward (dq, dk, dv) at the "
+                         "Qwen2.5-0.5B (32K) and Llama-3.2-3B (128K) shapes, alpha 1 and inf, "
+                         "printed as one JSON line")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (twice), as the "
                          "reference kernel for scaling FETCH_SIZE/WRITE_SIZE counters")
@@ -246,6 +250,65 @@ def cpu_baseline(w, alpha, target_s):
             "sample": "%d random query rows x %d heads of %s (N=%d), fp64, %.1f s (%.3f s per row "
                       "on average, setup included)" % (n, w.Hq, w.name, w.N, dt, dt / n),
             "full_prefill_s_extrapolated": full / rate}
+
+
+def backward_flops(w, alpha, N=None):
+    """Algorithmic flops of the backward per call: per q head, the recomputed scores, dq' and
+    dk' over the kept terms (4 flops each) and dP and dv over every visible (row, key) pair
+    (2d flops each): 12*kept + 4*d*N(N+1)/2."""
+    import rope_wavelength_sparsity_amd as wpa
+    n = w.N if N is None else N
+    kept, _ = wpa.count_terms(w.d, w.base, alpha, n, 0, n)
+    return w.B * w.Hq * (12 * kept + 4 * w.d * n * (n + 1) // 2)
+
+
+def bench_backward(names, reps):
+    """wpa_prefill_backward timed with HIP events (mean of reps after one warm-up), alpha 1
+    and alpha = inf, at each named prefill workload."""
+    import torch
+    import rope_wavelength_sparsity_amd as wpa
+    import synth
+    rows = []
+    for name in names:
+        w = synth.WORKLOADS[name]
+        q, k, v = synth.workload_inputs(w, device="cuda")
+        g = torch.Generator(device="cuda")
+        g.manual_seed(w.seed + 100)
+        dout = torch.randn(q.shape, generator=g, device="cuda").to(torch.bfloat16)
+        ws = torch.empty(wpa.prefill_backward_workspace_bytes(w.B, w.N, w.Hq, w.Hkv, w.d),
+                         device="cuda", dtype=torch.uint8)
+        dq = torch.empty(q.shape, device="cuda", dtype=torch.float32)
+        dk = torch.empty(k.shape, device="cuda", dtype=torch.float32)
+        dv = torch.empty(v.shape, device="cuda", dtype=torch.float32)
+        r = {"workload": "%s: B=%d N=%d Hq=%d Hkv=%d d=%d base=%g" % (name, w.B, w.N, w.Hq, w.Hkv,
+                                                                       w.d, w.base)}
+        for alpha in (1.0, math.inf):
+            out, lse = wpa.prefill(q, k, v, w.base, alpha, want_lse=True)
+            run = lambda: wpa.prefill_backward(q, k, v, out, lse, dout, w.base, alpha, dq=dq, dk=dk,
+                                               dv=dv, workspace=ws)
+            run()
+            torch.cuda.synchronize()
+            a, b = _events(2)
+            a.record()
+            for _ in range(reps):
+                run()
+            b.record()
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b) / reps
+            fl = backward_flops(w, alpha)
+            key = "alpha_1" if alpha == 1.0 else "alpha_inf"
+            r[key] = {"ms": ms, "flops": fl, "tflops": fl / (ms * 1e-3) / 1e12,
+                      "frac_of_bf16_peak": fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+            _log("backward %s alpha=%g: %.2f ms, %.1f TFLOP/s" % (name, alpha, ms, r[key]["tflops"]))
+            del out, lse
+        r["speedup_vs_full_window"] = r["alpha_inf"]["ms"] / r["alpha_1"]["ms"]
+        rows.append(r)
+        del q, k, v, dout, ws, dq, dk, dv
+        torch.cuda.empty_cache()
+    return {"backward": rows, "timing": "HIP events, mean of %d calls after one warm-up; one call "
+            "= prep + dq + dk/dv + reduce kernels" % reps,
+            "flops": "per q head 12*kept + 4*d*N(N+1)/2 (scores, dq', dk' over kept terms; dP, dv "
+                     "over visible pairs)"}
 
 
 def _log(*a):
@@ -576,6 +639,9 @@ def main():
         return
     if args.extras:
         print(json.dumps({"extras": extras(max(5, args.steps // 2))}), flush=True)
+        return
+    if args.backward:
+        print(json.dumps(bench_backward(("qwen05b", "llama3b"), max(2, args.steps // 4))), flush=True)
         return
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib << 20
