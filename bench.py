@@ -521,16 +521,23 @@ def extras(reps):
     for C in (4096, 8192):
         cache = wpa.KVCache(w.B, w.N, w.Hkv, w.d, w.base)
         out = torch.empty_like(q)
-
-        def run():
-            for s in range(0, w.N, C):
-                cache.write(k[:, s:s + C], v[:, s:s + C], s)
-                lens = torch.full((w.B,), s + C, dtype=torch.int32, device="cuda")
-                wpa.prefill_cached(q[:, s:s + C], cache, lens, 1.0, out=out[:, s:s + C])
-        t = _time(run, max(1, reps // 2))
-        ch["chunks_%d_ms" % C] = t
-        ch["chunks_%d_tflops" % C] = dense_flops / (t * 1e-3) / 1e12
-        del cache, out
+        lens = [torch.full((w.B,), s + C, dtype=torch.int32, device="cuda")
+                for s in range(0, w.N, C)]
+        # key splits as the launch chooses them (their workspace allocated once), and none
+        ns_bytes = wpa.prefill_cached_workspace_bytes(w.B, C, w.Hq, w.Hkv, w.d, 0)
+        wsc = torch.empty(max(ns_bytes, 16), dtype=torch.uint8, device="cuda")
+        ch["chunks_%d_key_splits" % C] = ns_bytes // (w.B * C * w.Hq * (w.d + 1) * 4) or 1
+        for tag, sp in (("", 0), ("_no_key_splits", 1)):
+            def run():
+                for i, s in enumerate(range(0, w.N, C)):
+                    cache.write(k[:, s:s + C], v[:, s:s + C], s)
+                    wpa.prefill_cached(q[:, s:s + C], cache, lens[i], 1.0, out=out[:, s:s + C],
+                                       splits=sp, workspace=wsc if sp != 1 else None)
+            t = _time(run, max(1, reps // 2))
+            ch["chunks_%d%s_ms" % (C, tag)] = t
+            ch["chunks_%d%s_tflops" % (C, tag)] = dense_flops / (t * 1e-3) / 1e12
+        ch["chunks_%d_over_one_shot" % C] = ch["chunks_%d_ms" % C] / t_one
+        del cache, out, wsc
     res["chunked_prefill"] = ch
     _log("extras: chunked %s" % ch)
 

@@ -83,8 +83,9 @@ int wpa_count_terms(int32_t d, double base, double alpha, int64_t n_q, int64_t q
  */
 int wpa_thresholds(int32_t d, double base, double alpha, int32_t* W);
 
-/* Workspace bytes wpa_prefill needs: the rotated, pair-blocked K and the transposed V
- * of all B*Hkv heads, padded to 128 tokens (2 * B*Hkv*roundup(N,128)*d*2 bytes). */
+/* Workspace bytes wpa_prefill needs: the rotated, pair-blocked K and V blocked by key
+ * octets (the decode caches' layouts) of all B*Hkv heads, padded to 128 tokens
+ * (2 * B*Hkv*roundup(N,128)*d*2 bytes). */
 size_t wpa_prefill_workspace_bytes(int32_t B, int64_t N, int32_t Hkv, int32_t d);
 
 /*
@@ -111,7 +112,7 @@ int wpa_prefill(const void* q, const void* k, const void* v, void* out, float* l
  * keys and values for several query launches.  wpa_prefill(...) is exactly
  * wpa_prefill_prepare(...) followed by wpa_prefill_attend(...) on the same stream.
  *   prepare: rotate k at its positions into the workspace (pair-blocked half) and store v
- *            transposed there; q is not read.
+ *            there by key octets (bf16, zero past token N); q is not read.
  *   attend:  the windowed attention of q against a workspace prepared for the same
  *            B, N, Hkv, d, base, positions (the workspace is only read).
  * Arguments have the meaning given for wpa_prefill.
@@ -390,6 +391,43 @@ int wpa_prefill_paged_varlen(const void* q, const void* k_pool, const void* v_po
                              int32_t Hkv, int32_t d, double base, const wpa_rope_t* rope,
                              double alpha, float scale, int32_t dtype, int32_t out_dtype,
                              unsigned long long* term_count, void* stream);
+
+/*
+ * Chunked prefill with key splits (the operation of wpa_prefill_cached: WavePrune original,
+ * the pair-wise window; ATFlash abstract: one window test per pair and distance).  A short
+ * chunk has too few row blocks to fill the GPU; here the key tiles each row block attends to
+ * are divided among up to `splits` workgroups, each of which writes its rows' output over its
+ * own share of the keys, normalised by its own softmax sum, and that sum's log; a second
+ * kernel merges the shares with weights exp(share's lse - row lse).  Rows whose keys fit one
+ * 128-key tile are written directly.  The result is the same attention up to fp32 rounding
+ * order (the merge adds one fp32 rescale per share).
+ *   One entry point for the four cached forms:
+ *   block_table  NULL: dense caches (k_cache, v_cache, Lmax as for wpa_prefill_cached);
+ *                else paged pools (num_pages, page_size as for wpa_prefill_paged, with
+ *                Lmax = max_pages * page_size, a multiple of page_size; page_size >= 128).
+ *   cu_q         NULL: Nq queries per sequence (out [B][Nq][Hq][d], lse [B][Hq][Nq]); else the
+ *                varlen packing of wpa_prefill_cached_varlen with max_q = Nq.
+ *   splits       0: the launch chooses (about two workgroups per compute unit on the current
+ *                device, at most 16, within the workspace's room; with no room for two, or no
+ *                workspace, it launches as wpa_prefill_cached does); 1: no key splits; 2..16:
+ *                exactly that many (a workspace of at least
+ *                wpa_prefill_cached_workspace_bytes(..., splits) bytes, else WPA_ERR_INVALID).
+ *   workspace    device, 16-byte aligned, caller-owned, ws_bytes long (NULL with 0: none);
+ *                overwritten.  Calls that overlap in time must not share it.
+ *   Other arguments, their layouts and errors as for wpa_prefill_cached.
+ * wpa_prefill_cached_workspace_bytes: bytes for `splits` splits (0: the count the launch
+ * would choose on the current device) of B sequences of Nq queries: splits * B * Nq * Hq *
+ * (d + 1) * 4, and 0 when no split is taken or for invalid arguments.
+ */
+size_t wpa_prefill_cached_workspace_bytes(int32_t B, int32_t Nq, int32_t Hq, int32_t Hkv,
+                                          int32_t d, int32_t splits);
+int wpa_prefill_cached_ex(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_table, int32_t num_pages, int32_t page_size,
+                          const int32_t* cu_q, const int32_t* kv_len, void* out, float* lse,
+                          int32_t B, int32_t Nq, int64_t Lmax, int32_t Hq, int32_t Hkv, int32_t d,
+                          double base, const wpa_rope_t* rope, double alpha, float scale,
+                          int32_t dtype, int32_t out_dtype, unsigned long long* term_count,
+                          int32_t splits, void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * Backward of the causal windowed prefill, for training with the window (WavePrune, "What the

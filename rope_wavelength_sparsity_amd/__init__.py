@@ -43,7 +43,8 @@ EXPORTS = ("wpa_count_terms", "wpa_thresholds", "wpa_prefill_workspace_bytes", "
            "wpa_kv_write_window", "wpa_decode_window", "wpa_prefill_sparse", "wpa_kv_page_bytes",
            "wpa_kv_write_paged", "wpa_decode_paged", "wpa_prefill_paged",
            "wpa_prefill_cached_varlen", "wpa_prefill_paged_varlen", "wpa_decode_noalloc",
-           "wpa_prefill_backward_workspace_bytes", "wpa_prefill_backward", "wpa_last_error")
+           "wpa_prefill_backward_workspace_bytes", "wpa_prefill_backward",
+           "wpa_prefill_cached_workspace_bytes", "wpa_prefill_cached_ex", "wpa_last_error")
 
 
 class Rope(ctypes.Structure):
@@ -210,6 +211,11 @@ def lib():
     L.wpa_prefill_backward.argtypes = [P, P, P, P, P, P, P, P, P, I32, I64, I32, I32, I32, D, P, D, F,
                                        I32, I32, I32, P, SZ, P]
     L.wpa_prefill_backward.restype = ctypes.c_int
+    L.wpa_prefill_cached_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32]
+    L.wpa_prefill_cached_workspace_bytes.restype = SZ
+    L.wpa_prefill_cached_ex.argtypes = [P, P, P, P, I32, I32, P, P, P, P, I32, I32, I64, I32, I32,
+                                        I32, D, P, D, F, I32, I32, P, I32, P, SZ, P]
+    L.wpa_prefill_cached_ex.restype = ctypes.c_int
     L.wpa_last_error.argtypes = []
     L.wpa_last_error.restype = ctypes.c_char_p
     _lib = L
@@ -702,19 +708,31 @@ def decode_noalloc(q, cache, kv_len, alpha: float, *, out, q_pos=None, scale: fl
     return (out, lse) if lse is not None else out
 
 
+def prefill_cached_workspace_bytes(B: int, Nq: int, Hq: int, Hkv: int, d: int,
+                                   splits: int = 0) -> int:
+    """Workspace bytes of a chunked prefill with `splits` key splits (0: the launch's own
+    choice on the current device); 0 when no split is taken."""
+    return int(lib().wpa_prefill_cached_workspace_bytes(int(B), int(Nq), int(Hq), int(Hkv), int(d),
+                                                        int(splits)))
+
+
 def prefill_cached(q, cache, kv_len, alpha: float, *, scale: float | None = None,
                    out=None, out_dtype=None, lse=None, want_lse: bool = False, term_count=None,
-                   stream=None, block_table=None, cu_q=None, max_q: int | None = None):
+                   stream=None, block_table=None, cu_q=None, max_q: int | None = None,
+                   splits: int = 0, workspace=None):
     """Chunked prefill: q [B][Nq][Hq][d] pre-RoPE holds the last Nq tokens of each sequence,
     whose keys and values are already in `cache` (a KVCache, or a PagedKVCache with pages of
     at least 128 tokens and `block_table` [B][max_pages] or the cache's default table);
     kv_len int32 device [B], each >= Nq.
     Varlen: with cu_q (int32 device [B+1]) q is [rows][Hq][d], sequence b's chunk being rows
     cu_q[b] .. cu_q[b+1]-1 (its last tokens), max_q an upper bound of the per-sequence counts;
-    lse is then [rows][Hq]."""
+    lse is then [rows][Hq].
+    splits: key splits of each row block's key tiles (0: chosen by the launch, 1: none, 2..16:
+    that many); their partials live in `workspace` (uint8 device tensor, at least
+    prefill_cached_workspace_bytes(...) long), allocated here when not given."""
     if cu_q is not None:
         return _prefill_varlen(q, cache, kv_len, alpha, cu_q, max_q, scale, out, out_dtype, lse,
-                               want_lse, term_count, stream, block_table)
+                               want_lse, term_count, stream, block_table, splits, workspace)
     _dev(q, "q")
     _dev(kv_len, "kv_len")
     if q.dim() != 4:
@@ -735,24 +753,55 @@ def prefill_cached(q, cache, kv_len, alpha: float, *, scale: float | None = None
     out = _out(out, q.shape, q, out_dtype)
     lse = _lse(lse, want_lse, (B, Hq, Nq), q)
     term_count = _counter(term_count, q)
-    rope = cache._rope[0]
-    sc = float(scale) if scale is not None else 0.0
-    if paged:
-        _check(lib().wpa_prefill_paged(_ptr(q), _ptr(cache.k), _ptr(cache.v), _ptr(table),
-                                       cache.num_pages, _ptr(kv_len), _ptr(out), _ptr(lse), B, Nq,
-                                       table.shape[1], cache.page_size, Hq, cache.Hkv, d,
-                                       cache.base, rope, float(alpha), sc, _dtype_code(q),
-                                       _dtype_code(out), _ptr(term_count), _stream(stream)))
-    else:
-        _check(lib().wpa_prefill_cached(_ptr(q), _ptr(cache.k), _ptr(cache.v), _ptr(kv_len),
-                                        _ptr(out), _ptr(lse), B, Nq, cache.Lmax, Hq, cache.Hkv, d,
-                                        cache.base, rope, float(alpha), sc, _dtype_code(q),
-                                        _dtype_code(out), _ptr(term_count), _stream(stream)))
+    _cached_ex(q, cache, table if paged else None, None, kv_len, out, lse, B, Nq, Hq, d, alpha,
+               scale, term_count, splits, workspace, stream)
     return (out, lse) if lse is not None else out
 
 
+def _cached_ex(q, cache, table, cu_q, kv_len, out, lse, B, Nq, Hq, d, alpha, scale, term_count,
+               splits, workspace, stream):
+    """wpa_prefill_cached_ex on a dense or paged cache (table), fixed or varlen (cu_q)."""
+    splits = int(splits)
+    if not 0 <= splits <= 16:
+        raise ValueError("splits must be in [0, 16]")
+    need = prefill_cached_workspace_bytes(B, Nq, Hq, cache.Hkv, d, splits) if splits != 1 else 0
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device) if need else None
+    else:
+        _dev(workspace, "workspace")
+        _same_device(workspace, q, "workspace")
+        if splits > 1 and workspace.numel() * workspace.element_size() < need:
+            raise ValueError("workspace needs %d bytes for %d splits" % (need, splits))
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if table is not None:
+        nt, Lmax, ps = cache.num_pages, table.shape[1] * cache.page_size, cache.page_size
+    else:
+        nt, Lmax, ps = 0, cache.Lmax, 0
+    sc = float(scale) if scale is not None else 0.0
+    if splits == 1:
+        # no key splits: the four plain entry points
+        args = (_ptr(out), _ptr(lse), B, Nq)
+        tail = (Hq, cache.Hkv, d, cache.base, cache._rope[0], float(alpha), sc, _dtype_code(q),
+                _dtype_code(out), _ptr(term_count), _stream(stream))
+        kv = (_ptr(cu_q), _ptr(kv_len)) if cu_q is not None else (_ptr(kv_len),)
+        fn = {(False, False): lib().wpa_prefill_cached, (False, True): lib().wpa_prefill_cached_varlen,
+              (True, False): lib().wpa_prefill_paged, (True, True): lib().wpa_prefill_paged_varlen}
+        f = fn[(table is not None, cu_q is not None)]
+        if table is not None:
+            _check(f(_ptr(q), _ptr(cache.k), _ptr(cache.v), _ptr(table), nt, *kv, *args,
+                     table.shape[1], ps, *tail))
+        else:
+            _check(f(_ptr(q), _ptr(cache.k), _ptr(cache.v), *kv, *args, Lmax, *tail))
+        return
+    _check(lib().wpa_prefill_cached_ex(_ptr(q), _ptr(cache.k), _ptr(cache.v), _ptr(table), nt, ps,
+                                       _ptr(cu_q), _ptr(kv_len), _ptr(out), _ptr(lse), B, Nq, Lmax,
+                                       Hq, cache.Hkv, d, cache.base, cache._rope[0], float(alpha),
+                                       sc, _dtype_code(q), _dtype_code(out), _ptr(term_count),
+                                       splits, _ptr(workspace), ws_bytes, _stream(stream)))
+
+
 def _prefill_varlen(q, cache, kv_len, alpha, cu_q, max_q, scale, out, out_dtype, lse, want_lse,
-                    term_count, stream, block_table):
+                    term_count, stream, block_table, splits, workspace):
     _dev(q, "q")
     _dev(kv_len, "kv_len")
     _dev(cu_q, "cu_q")
@@ -779,21 +828,8 @@ def _prefill_varlen(q, cache, kv_len, alpha, cu_q, max_q, scale, out, out_dtype,
     out = _out(out, q.shape, q, out_dtype)
     lse = _lse(lse, want_lse, (rows, Hq), q)
     term_count = _counter(term_count, q)
-    rope = cache._rope[0]
-    sc = float(scale) if scale is not None else 0.0
-    if paged:
-        _check(lib().wpa_prefill_paged_varlen(_ptr(q), _ptr(cache.k), _ptr(cache.v), _ptr(table),
-                                              cache.num_pages, _ptr(cu_q), _ptr(kv_len), _ptr(out),
-                                              _ptr(lse), B, int(max_q), table.shape[1],
-                                              cache.page_size, Hq, cache.Hkv, d, cache.base, rope,
-                                              float(alpha), sc, _dtype_code(q), _dtype_code(out),
-                                              _ptr(term_count), _stream(stream)))
-    else:
-        _check(lib().wpa_prefill_cached_varlen(_ptr(q), _ptr(cache.k), _ptr(cache.v), _ptr(cu_q),
-                                               _ptr(kv_len), _ptr(out), _ptr(lse), B, int(max_q),
-                                               cache.Lmax, Hq, cache.Hkv, d, cache.base, rope,
-                                               float(alpha), sc, _dtype_code(q), _dtype_code(out),
-                                               _ptr(term_count), _stream(stream)))
+    _cached_ex(q, cache, table if paged else None, cu_q, kv_len, out, lse, B, int(max_q), Hq, d,
+               alpha, scale, term_count, splits, workspace, stream)
     return (out, lse) if lse is not None else out
 
 

@@ -37,8 +37,10 @@
 //     register r of half h holds key 16(r/8) + 8h + (r%8).  Registers 8c..8c+7 are then
 //     exactly the 8 keys that half h must supply as the B operand of the P*V step over
 //     keys 16c..16c+15, and the P^T operand needs no data movement.
-//   V operand (A of the P*V step): V^T rows (dims) from LDS, key-contiguous, 16-byte
-//     chunks XOR-swizzled by the row index against bank conflicts.
+//   V operand (A of the P*V step): 16 bytes per lane, the 8 keys of one key octet for one
+//     dim.  A tile's values sit in LDS as in memory, by key octets ([BN/8][d][8]: lane l of
+//     half h reads dim l%32 of octet 2c+h, 512 contiguous bytes per half, conflict-free),
+//     so a tile is one contiguous block to copy from the workspace or the decode cache.
 //   O^T accumulator: lane = query row, so the softmax rescale is a per-lane scalar.
 #include <atomic>
 #include <type_traits>
@@ -119,6 +121,7 @@ __device__ inline void dispatch(int v, F&& f) {
 
 struct Launch {
     int Gc, R, nhc, n_rb;
+    int ns;        // CACHED: key splits per row block (1: none; >1: partials in p.part)
 };
 
 template <int D>
@@ -126,25 +129,14 @@ struct Tile {
     static constexpr int BN = 128;                  // keys per tile (d=128: 64 was 5% slower)
     static constexpr int NSUB = BN / 32;
     static constexpr int KI = BN * 32 / 1024;       // wave loads per K block
-    static constexpr int VI = D * BN * 2 / 1024;    // wave loads for V^T
+    static constexpr int VI = D * BN * 2 / 1024;    // wave loads for V (1 KB each)
     static constexpr int PI = BN * 4 / 256;         // wave loads for positions
-    static constexpr int CPR = BN / 8;              // 16-byte chunks per V^T row
-    static constexpr int RPI = 64 / CPR;            // V^T rows per wave load
     // Compute waves per workgroup (plus one producer wave) and the waves per SIMD the
     // register budget must allow.  d=64 fits 128 VGPRs: 4 waves per SIMD, two 8-wave
     // workgroups per CU (64 KB of LDS each).  d=128 fits 168: 3 per SIMD, one 12-wave
     // workgroup per CU; with explicit positions (more registers) 2 per SIMD, 8 waves.
     static constexpr int maxw(bool haspos) { return D == 64 || haspos ? 7 : 11; }
     static constexpr int waves_per_eu(bool haspos) { return D == 64 ? 4 : (haspos ? 2 : 3); }
-    // Slot swizzle of V^T row e (16-byte chunks).  The P*V read has lane l fetch row
-    // e = l%32 (+32db): any 8 consecutive rows, and any 16, must land on distinct
-    // (bank-group) slots.  Rows of 128 keys are 256 bytes (16 slots): e mod 16.  (Rows of 64
-    // keys, 128 bytes, two per 256-byte bank window, would take e mod 8 with bit 0 flipped
-    // for rows 8..15 of each 16.)
-    __device__ static int swz(int e) {
-        if constexpr (BN == 128) return e & 15;
-        else return (e & 7) ^ ((e >> 3) & 1);
-    }
 };
 
 // CACHED: the keys and values are the decode caches (K pair-blocked with row stride
@@ -179,7 +171,10 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
     const int G = p.Hq / p.Hkv;
     const int U = p.B * p.Hkv * L.nhc;
     const int u = blockIdx.x % U;
-    const int rb = L.n_rb - 1 - (int)(blockIdx.x / U);     // longest rows first
+    // workgroup order: row blocks longest first, then their key splits, then (sequence, kv
+    // head, head chunk)
+    const int split = CACHED ? (int)(blockIdx.x / U) % L.ns : 0;
+    const int rb = L.n_rb - 1 - (int)(blockIdx.x / U) / (CACHED ? L.ns : 1);
     const int hc = u % L.nhc;
     const int g = (u / L.nhc) % p.Hkv;
     const int b = u / (L.nhc * p.Hkv);
@@ -225,6 +220,23 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
     const int tq0 = NK - NQ;
     const int qs = (CACHED ? (tq0 & ~31) : 0) + rb * 32 * L.R;
     if (CACHED && qs >= NK) return;                    // this sequence has fewer rows
+    const int row_end = (qs + 32 * L.R < NK ? qs + 32 * L.R : NK) - 1;
+    // Key tiles 0 .. kt_last reach this workgroup's rows.  With key splits, split s of the row
+    // block takes tiles [T s / ns, T (s+1) / ns) of those T and writes its share for the
+    // combine: its rows' output normalised by their own sum over its keys, and m + log2 of
+    // that sum.  A row block whose tiles all fall to one split (T = 1) writes its rows directly.
+    int kt_last = row_end / BN, kt_lo = 0;
+    bool partial = false;
+    if constexpr (CACHED) {
+        if (L.ns > 1) {
+            const int T = kt_last + 1;
+            kt_lo = (int)((int64_t)T * split / L.ns);
+            const int hi = (int)((int64_t)T * (split + 1) / L.ns);
+            if (kt_lo >= hi) return;                   // an empty split (T < ns)
+            kt_last = hi - 1;
+            partial = T > 1;
+        }
+    }
     const int q0 = qs + 32 * rg;
     const bool producer = w == L.Gc * L.R;                 // the extra, loading wave
     const bool wave_ok = !producer && head_ok && q0 < NK && (!CACHED || q0 + 31 >= tq0);
@@ -283,11 +295,9 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
 
     const int64_t ldk = CACHED ? p.ldk : p.Np;            // key row stride of kp
     const uint16_t* kpg = p.kp + ((int64_t)b * p.Hkv + g) * NB * ldk * 16;
-    // V^T [d][Np] per head (plain) or the key-octet cache [ceil(Lmax/8)][d][8] (CACHED)
+    // V by key octets: [Np/8][d][8] per head (plain) or the cache [ceil(Lmax/8)][d][8]
     const uint16_t* vtg = p.vt + ((int64_t)b * p.Hkv + g) * D *
                                      (CACHED ? (p.ldk + 7) / 8 * 8 : p.Np);
-    const int row_end = (qs + 32 * L.R < NK ? qs + 32 * L.R : NK) - 1;
-    const int kt_last = row_end / BN;
     const int pq_wg = POS(qs < NK ? qs : NK - 1);
     const int pq_lo = POS(q0 < NK ? q0 : NK - 1);
     const int pq_hi = POS(q0 + 31 < NK ? q0 + 31 : NK - 1);
@@ -370,14 +380,14 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
                 __builtin_amdgcn_global_load_lds(src, (lds_ptr)&sK2[stage][j * BN * 16 + part * 512],
                                                  16, 0, 0);
             } else if (i < nK + Tile<D>::VI) {
-                // V^T rows e; the 16-byte chunk c of row e sits in slot c ^ swz(e)
+                // the tile's octets as one block: 16-byte piece 64r + lane is dim e of
+                // octet c (past the last key of a cache, its last octet stands in: those
+                // keys are masked)
                 const int r = i - nK;
-                const int e = r * Tile<D>::RPI + lane / Tile<D>::CPR;
-                const int c = (lane % Tile<D>::CPR) ^ Tile<D>::swz(e);
+                const int pc = 64 * r + lane, c = pc / D, e = pc % D;
+                int o = ks / 8 + c;
                 const uint16_t* src;
                 if constexpr (CACHED) {
-                    // keys ks+8c .. ks+8c+7 form octet ks/8 + c of the cache
-                    int o = ks / 8 + c;
                     if (o > (NK - 1) / 8) o = (NK - 1) / 8;
                     if constexpr (paged) {
                         const int opg = 1 << (p.pg.page_log2 - 3);        // octets per page
@@ -386,15 +396,36 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
                         src = vtg + ((int64_t)o * D + e) * 8;
                     }
                 } else {
-                    src = vtg + (int64_t)e * p.Np + ks + 8 * c;
+                    src = vtg + ((int64_t)o * D + e) * 8;
                 }
-                __builtin_amdgcn_global_load_lds(src, (lds_ptr)&sV2[stage][r * Tile<D>::RPI * BN],
-                                                 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(src, (lds_ptr)&sV2[stage][r * 512], 16, 0, 0);
             } else if (HASPOS) {
                 const int pi = i - nK - Tile<D>::VI;
                 const int t = ks + 64 * pi + lane;
                 const int32_t* src = posb + (t < NK ? t : NK - 1);
                 __builtin_amdgcn_global_load_lds(src, (lds_ptr)&sPos2[stage][64 * pi], 4, 0, 0);
+            }
+        }
+        if constexpr (CACHED) {
+            // The tile past the last key (only the one holding key NK-1): once its loads have
+            // landed, its V slots of keys >= NK (cache slots never written, or other data) are
+            // set to zero, so that their zero probabilities give zero terms in P*V.
+            if (ks + BN > NK) {
+                __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+                const int first = NK - ks;             // first key slot to clear, in [1, BN)
+                const int co = first >> 3, j0 = first & 7;
+                for (int pc = co * D + lane; pc < (BN / 8) * D; pc += 64) {
+                    u32x4* cell = reinterpret_cast<u32x4*>(&sV2[stage][pc * 8]);
+                    if (pc / D > co || j0 == 0) {
+                        *cell = u32x4{0u, 0u, 0u, 0u};
+                    } else {
+                        u32x4 x = *cell;
+#pragma unroll
+                        for (int t = 0; t < 4; ++t)
+                            x[t] &= (2 * t < j0 ? 0xffffu : 0u) | (2 * t + 1 < j0 ? 0xffff0000u : 0u);
+                        *cell = x;
+                    }
+                }
             }
         }
     };
@@ -440,28 +471,16 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) S[r] -= shift;
     };
-    const int v_row = l32 * BN;                               // V^T row of this lane (db = 0)
-    const uint32_t v_xb = (uint32_t)(h ^ Tile<D>::swz(l32)) << 4;   // its slot swizzle, in bytes
-    auto pv = [&](int sub, int k0, const uint32_t (&wd)[8], const uint16_t* sV) {
+    const int v_lane = (h * D + l32) * 8;                    // dim l32 of octet h (db = 0, c = 0)
+    auto pv = [&](int sub, const uint32_t (&wd)[8], const uint16_t* sV) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             const u32x4 pb = u32x4{wd[4 * c], wd[4 * c + 1], wd[4 * c + 2], wd[4 * c + 3]};
-            // chunk 4sub + 2c + h of row e sits in slot (4sub + 2c + h) ^ swz(e): one xor-add
-            const uint16_t* vp = reinterpret_cast<const uint16_t*>(
-                reinterpret_cast<const char*>(sV + v_row) + (((uint32_t)(4 * sub + 2 * c) << 4) ^ v_xb));
+            // keys 16(2sub + c) + 8h .. +7: octet 4sub + 2c + h of the tile
+            const uint16_t* vp = sV + v_lane + (4 * sub + 2 * c) * D * 8;
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                bf16x8 a = *reinterpret_cast<const bf16x8*>(vp + 32 * db * BN);
-                if (CACHED && k0 + 32 > NK) {
-                    // cache slots past the last key: zero them (their p is 0, but the slots
-                    // may hold anything)
-                    u32x4 av = __builtin_bit_cast(u32x4, a);
-                    const int kb = k0 + 16 * c + 8 * h;
-#pragma unroll
-                    for (int t = 0; t < 4; ++t)
-                        av[t] &= (kb + 2 * t < NK ? 0xffffu : 0u) | (kb + 2 * t + 1 < NK ? 0xffff0000u : 0u);
-                    a = __builtin_bit_cast(bf16x8, av);
-                }
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(vp + 32 * db * 8);
                 O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     a, __builtin_bit_cast(bf16x8, pb), O[db], 0, 0, 0);
             }
@@ -704,7 +723,7 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
                 psum = probs(R, wd);
             }
             lsum += psum;
-            pv(sub, ks + 32 * sub, wd, sV);
+            pv(sub, wd, sV);
         }
     };
 
@@ -717,10 +736,10 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
             issue(kt_last, 0);
             __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
         }
-        for (int kt = kt_last, it = 0; kt >= 0; --kt, ++it) {
+        for (int kt = kt_last, it = 0; kt >= kt_lo; --kt, ++it) {
             __syncthreads();          // tile kt is in stage it&1; stage (it+1)&1 is free again
             if (producer) {
-                if (kt > 0) {
+                if (kt > kt_lo) {
                     issue(kt - 1, (it & 1) ^ 1);
                     __builtin_amdgcn_s_waitcnt(0x0070);
                 }
@@ -793,6 +812,26 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
     if (!wave_ok) return;
     const float l_tot = sum_with_partner(lsum, xaddr);
     if (!row_ok) return;
+    if (CACHED && partial) {
+        // this split's share: rows with no key in its range hold sum 0 (output 0, log2-sum
+        // -inf); the partials of split s sit at [s][b*Nq + qi][hq]
+        const int64_t pr = ((int64_t)split * p.B * p.Nq + (int64_t)b * p.Nq + qi) * p.Hq + hq;
+        const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+        float* po = p.part + pr * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+            for (int grp = 0; grp < 4; ++grp) {
+                const int dim = 32 * db + 8 * grp + 4 * h;
+                *reinterpret_cast<f32x4*>(po + dim) =
+                    f32x4{O[db][4 * grp] * inv, O[db][4 * grp + 1] * inv, O[db][4 * grp + 2] * inv,
+                          O[db][4 * grp + 3] * inv};
+            }
+        }
+        if (h == 0)
+            p.part[(int64_t)L.ns * p.B * p.Nq * p.Hq * D + pr] = l_tot > 0.f ? m + log2f(l_tot) : -INFINITY;
+        return;
+    }
     const float inv = 1.0f / l_tot;
     const int64_t ob = ((row0 + qi) * p.Hq + hq) * D;
 #pragma unroll
@@ -815,6 +854,68 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
     if (p.lse && h == 0)
         p.lse[CACHED && p.cu_q ? (row0 + qi) * p.Hq + hq : ((int64_t)b * p.Hq + hq) * NQ + qi] =
             (m + log2f(l_tot)) * 0.6931471805599453f;
+}
+
+// Merge of the key splits of a cached prefill: each (row, q head) of a row block with more
+// than one key tile takes the splits that hold tiles of its row block (the same partition
+// as the attention kernel's), weighs each by 2^(its log2-sum - their max), and writes the
+// normalised sum and the natural-log lse.  D/4 threads per (row, head), 4 dims each.
+template <int D>
+__global__ __launch_bounds__(256) void split_combine(PrefillParams p, int R, int ns) {
+    constexpr int BN = Tile<D>::BN, TPR = D / 4;
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t pr = gid / TPR;                          // (b*Nq + qi)*Hq + hq
+    const int c = (int)(gid % TPR);
+    const int64_t npr = (int64_t)p.B * p.Nq * p.Hq;
+    if (pr >= npr) return;
+    const int hq = (int)(pr % p.Hq);
+    const int64_t bq = pr / p.Hq;
+    const int b = (int)(bq / p.Nq), qi = (int)(bq % p.Nq);
+    // the sequence's geometry, as the attention kernel derives it
+    int NQ = p.Nq;
+    int64_t row0 = (int64_t)b * p.Nq;
+    if (p.cu_q) {
+        const int c0 = p.cu_q[b], c1 = p.cu_q[b + 1];
+        NQ = c1 - c0 < 0 ? 0 : (c1 - c0 > p.Nq ? p.Nq : c1 - c0);
+        row0 = c0;
+    }
+    if (qi >= NQ) return;
+    int NK = p.kv_len[b];
+    NK = NK < NQ ? NQ : (NK > (int)p.N ? (int)p.N : NK);
+    const int tq0 = NK - NQ, qrow = tq0 + qi, base = tq0 & ~31;
+    const int qs = base + (qrow - base) / (32 * R) * (32 * R);
+    const int row_end = (qs + 32 * R < NK ? qs + 32 * R : NK) - 1;
+    const int T = row_end / BN + 1;
+    if (T == 1) return;                                    // written by its only split
+    const int64_t sstride = npr;                           // (row, head) pairs per split
+    const float* lse2 = p.part + (int64_t)ns * npr * D;
+    float mx = -INFINITY;
+    for (int sp = 0; sp < ns; ++sp) {
+        if ((int64_t)T * sp / ns >= (int64_t)T * (sp + 1) / ns) continue;   // empty split
+        mx = fmaxf(mx, lse2[sp * sstride + pr]);
+    }
+    float wsum = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < ns; ++sp) {
+        if ((int64_t)T * sp / ns >= (int64_t)T * (sp + 1) / ns) continue;
+        const float l2 = lse2[sp * sstride + pr];
+        if (l2 == -INFINITY) continue;                     // no key of this split reaches the row
+        const float wgt = exp2f(l2 - mx);
+        wsum += wgt;
+        acc += wgt * *reinterpret_cast<const f32x4*>(p.part + (sp * sstride + pr) * D + 4 * c);
+    }
+    const float inv = 1.0f / wsum;
+    const int64_t ob = ((row0 + qi) * p.Hq + hq) * D + 4 * c;
+    if (p.out_f32) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + ob) = acc * inv;
+    } else {
+        uint32_t* dst = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p.out) + ob);
+        dst[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+        dst[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+    }
+    if (p.lse && c == 0)
+        p.lse[p.cu_q ? (row0 + qi) * p.Hq + hq : ((int64_t)b * p.Hq + hq) * NQ + qi] =
+            (mx + log2f(wsum)) * 0.6931471805599453f;
 }
 
 // Compute units of the current device (cached per device).
@@ -858,11 +959,14 @@ hipError_t sparse_lds_d(const PrefillParams& p, size_t* need, size_t* limit) {
     return hipSuccess;
 }
 
-template <int D, bool F32>
-hipError_t launch_d(const PrefillParams& p, const Tables& t, hipStream_t s) {
+// Workgroup layout of a launch: q heads per wave group, row groups per workgroup, head
+// chunks, key splits.
+template <int D>
+Launch plan_launch(const PrefillParams& p) {
     const int G = p.Hq / p.Hkv;
     const int MAXW = Tile<D>::maxw(p.pos != nullptr);
     Launch L;
+    L.ns = 1;
     if (p.blk_count) {
         // Block-sparse: a workgroup takes consecutive row groups of one q head.  Its waves'
         // lists are then one head's pattern at neighbouring query blocks, which share most
@@ -897,24 +1001,48 @@ hipError_t launch_d(const PrefillParams& p, const Tables& t, hipStream_t s) {
         L.Gc = (G + L.nhc - 1) / L.nhc;
         L.R = mw / L.Gc > 1 ? mw / L.Gc : 1;
     }
+    // Cached prefill with a workspace: the key tiles of each row block shared among key
+    // splits.  Asked for: exactly that many (within the workspace's room).
+    const bool ksplit = p.kv_len && p.part && p.max_splits > 1;
+    if (ksplit && p.splits > 0) {
+        L.ns = p.splits < p.max_splits ? p.splits : p.max_splits;
+        return L;
+    }
     if (!rows_grouped) {
-        // Few rows (a short prompt, a prefill chunk): fewer row groups per workgroup, then the
-        // q heads of a kv head over more workgroups, until about two workgroups per CU (the
-        // resident count) are launched.  Each split re-reads the kv head's K/V tiles.
+        // Few rows (a short prompt, a prefill chunk): fewer row groups per workgroup, then
+        // more workgroups until about two per CU (the resident count) are launched: with a
+        // workspace, by splitting each row block's key tiles (each split reads its own share
+        // of the K/V tiles once, and every workgroup keeps all the q heads of its chunk);
+        // without one, by spreading the q heads of a kv head over several workgroups (each
+        // re-reads the kv head's K/V tiles).  (8 chunks of 4096 of the Qwen-0.5B shape: a
+        // 4096-row chunk has 128 row groups per kv head, two key splits give 512 workgroups.)
         const int64_t target = 2 * (int64_t)device_cus();
         if (wgs(L.R, L.nhc) < target) {
             L.R = 1;
-            if (wgs(1, L.nhc) < target) {
-                int nhc = (int)((target + wgs(1, 1) - 1) / wgs(1, 1));
-                nhc = nhc < G ? nhc : G;
-                L.Gc = (G + nhc - 1) / nhc;
-                L.nhc = (G + L.Gc - 1) / L.Gc;
+            const int64_t w1 = wgs(1, L.nhc);
+            if (w1 < target) {
+                if (ksplit) {
+                    const int64_t ns = (target + w1 - 1) / w1;
+                    L.ns = (int)(ns < p.max_splits ? ns : p.max_splits);
+                } else {
+                    int nhc = (int)((target + wgs(1, 1) - 1) / wgs(1, 1));
+                    nhc = nhc < G ? nhc : G;
+                    L.Gc = (G + nhc - 1) / nhc;
+                    L.nhc = (G + L.Gc - 1) / L.Gc;
+                }
             }
         }
     }
+    return L;
+}
+
+template <int D, bool F32>
+hipError_t launch_d(const PrefillParams& p, const Tables& t, hipStream_t s) {
+    Launch L = plan_launch<D>(p);
+    const int64_t rows = p.kv_len ? (int64_t)p.Nq + 31 : p.N;
     L.n_rb = (int)((rows + 32 * L.R - 1) / (32 * L.R));
     const int waves = L.Gc * L.R + 1;               // + the producer wave
-    const int64_t nblk = (int64_t)L.n_rb * p.B * p.Hkv * L.nhc;
+    const int64_t nblk = (int64_t)L.n_rb * L.ns * p.B * p.Hkv * L.nhc;
     dim3 grid((unsigned)nblk), block(64 * waves);
     const bool hp = p.pos != nullptr, cn = p.counter != nullptr;
     if (p.kv_len) {
@@ -924,6 +1052,12 @@ hipError_t launch_d(const PrefillParams& p, const Tables& t, hipStream_t s) {
         } else {
             if (cn) prefill_kernel<D, F32, false, true, true, false><<<grid, block, 0, s>>>(p, t, L);
             else prefill_kernel<D, F32, false, false, true, false><<<grid, block, 0, s>>>(p, t, L);
+        }
+        if (L.ns > 1) {
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            const int64_t thr = (int64_t)p.B * p.Nq * p.Hq * (D / 4);
+            split_combine<D><<<dim3((unsigned)((thr + 255) / 256)), dim3(256), 0, s>>>(p, L.R, L.ns);
         }
     } else if (p.blk_count) {
         // block bitmaps: one per compute wave and their union (the caller has checked that
@@ -949,6 +1083,10 @@ hipError_t launch_d(const PrefillParams& p, const Tables& t, hipStream_t s) {
 hipError_t prefill_sparse_lds(const PrefillParams& p, size_t* need, size_t* limit) {
     if (p.d == 64) return p.in_f32 ? sparse_lds_d<64, true>(p, need, limit) : sparse_lds_d<64, false>(p, need, limit);
     return p.in_f32 ? sparse_lds_d<128, true>(p, need, limit) : sparse_lds_d<128, false>(p, need, limit);
+}
+
+int prefill_key_splits(const PrefillParams& p) {
+    return p.d == 64 ? plan_launch<64>(p).ns : plan_launch<128>(p).ns;
 }
 
 hipError_t launch_prefill(const PrefillParams& p, const Tables& t, hipStream_t s) {

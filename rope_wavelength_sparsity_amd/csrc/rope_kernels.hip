@@ -12,9 +12,9 @@
 // contracting only the active blocks (pairs form a contiguous slice of the contraction
 // axis at every distance) reads contiguous memory for every token range.
 //
-// Values: for prefill they are transposed to [B][Hkv][d][tokens] and for the decode cache
-// blocked by key octets, [B][Hkv][tokens/8][d][8]: in both, the P*V matrix product (a
-// contraction over keys) reads key-contiguous MFMA operands.
+// Values, for prefill and for the decode cache alike, are blocked by key octets,
+// [B][Hkv][tokens/8][d][8]: the P*V matrix product (a contraction over keys) then reads
+// key-contiguous 16-byte MFMA operands, and a tile of keys is one contiguous block.
 #include "wpa_device.hpp"
 #include "wpa_internal.hpp"
 
@@ -104,9 +104,11 @@ __global__ __launch_bounds__(256) void rope_keys_kernel(RopeParams p, Tables tab
     d4[1] = u32x4{oy[0], oy[1], oy[2], oy[3]};
 }
 
-// V transpose for prefill: one block = 64 tokens x d dims of one (b, kv head).
+// V for prefill, by key octets [B][Hkv][ntok/8][d][8] bf16, zero past the last token:
+// one block = 64 tokens (8 octets) x d dims of one (b, kv head), staged through LDS so that
+// both the token-row reads and the octet writes are contiguous.
 template <bool F32, int D>
-__global__ __launch_bounds__(256) void v_transpose_kernel(RopeParams p) {
+__global__ __launch_bounds__(256) void v_octets_kernel(RopeParams p) {
     __shared__ uint16_t tile[64][D + 2];
     const int64_t ntok = p.pad_to > p.n ? p.pad_to : p.n;
     const int64_t ntiles = (ntok + 63) / 64;
@@ -129,16 +131,17 @@ __global__ __launch_bounds__(256) void v_transpose_kernel(RopeParams p) {
         for (int i = 0; i < 8; ++i) tile[tt][e8 + i] = f32_to_bf16_bits(x[i]);
     }
     __syncthreads();
-    // store: each thread 8 consecutive tokens of one dim
+    // store: each thread the 8 tokens of one octet for one dim; consecutive threads write
+    // consecutive 16-byte pieces (dims of one octet, then the next octet)
     for (int c = threadIdx.x; c < D * 8; c += blockDim.x) {
-        const int e = c / 8, t8 = (c % 8) * 8;
+        const int oc = c / D, e = c % D, t8 = 8 * oc;
         const int64_t t = t0 + t8;
         if (t >= ntok) continue;
         uint32_t w[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             w[i] = (uint32_t)tile[t8 + 2 * i][e] | ((uint32_t)tile[t8 + 2 * i + 1][e] << 16);
-        uint16_t* dst = p.vout + (((int64_t)b * p.Hkv + g) * D + e) * p.ld + p.t0 + t;
+        uint16_t* dst = p.vout + ((((int64_t)b * p.Hkv + g) * (p.ld / 8) + (p.t0 + t) / 8) * D + e) * 8;
         *reinterpret_cast<u32x4*>(dst) = u32x4{w[0], w[1], w[2], w[3]};
     }
 }
@@ -213,15 +216,15 @@ hipError_t launch_rope_relayout(const RopeParams& p, hipStream_t s) {
         rope_keys_kernel<true><<<dim3((unsigned)((nk + 255) / 256)), blk, 0, s>>>(p, *p.tab);
     else
         rope_keys_kernel<false><<<dim3((unsigned)((nk + 255) / 256)), blk, 0, s>>>(p, *p.tab);
-    if (p.v_transposed) {
+    if (p.v_prefill) {
         const int64_t nt = (ntok + 63) / 64;
         dim3 grid((unsigned)(nt * p.B * p.Hkv));
         if (p.d == 64) {
-            if (p.in_f32) v_transpose_kernel<true, 64><<<grid, blk, 0, s>>>(p);
-            else v_transpose_kernel<false, 64><<<grid, blk, 0, s>>>(p);
+            if (p.in_f32) v_octets_kernel<true, 64><<<grid, blk, 0, s>>>(p);
+            else v_octets_kernel<false, 64><<<grid, blk, 0, s>>>(p);
         } else {
-            if (p.in_f32) v_transpose_kernel<true, 128><<<grid, blk, 0, s>>>(p);
-            else v_transpose_kernel<false, 128><<<grid, blk, 0, s>>>(p);
+            if (p.in_f32) v_octets_kernel<true, 128><<<grid, blk, 0, s>>>(p);
+            else v_octets_kernel<false, 128><<<grid, blk, 0, s>>>(p);
         }
     } else {
         const int64_t n_oct = (p.t0 + p.n - 1) / 8 - p.t0 / 8 + 1;

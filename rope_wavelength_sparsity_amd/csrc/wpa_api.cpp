@@ -292,7 +292,7 @@ int wpa_prefill_prepare_ex(const void* k, const void* v, const int32_t* position
     wpa::RopeParams rp{};
     rp.k = k; rp.v = v; rp.pos = positions; rp.kp = kp; rp.vout = kp + (size_t)B * Hkv * Np * d;
     rp.n = N; rp.t0 = 0; rp.ld = Np; rp.pad_to = Np; rp.kl = dense_layout(d, Np);
-    rp.B = B; rp.Hkv = Hkv; rp.d = d; rp.in_f32 = dtype == WPA_FP32; rp.v_transposed = 1;
+    rp.B = B; rp.Hkv = Hkv; rp.d = d; rp.in_f32 = dtype == WPA_FP32; rp.v_prefill = 1;
     rp.interleaved = interleaved(rope);
     rp.head_theta = head_tables(rope);
     rp.tab = &tab;
@@ -575,7 +575,7 @@ int kv_write_impl(const void* k, const void* v, int64_t start, int64_t n, void* 
     rp.kp = static_cast<uint16_t*>(k_cache); rp.vout = static_cast<uint16_t*>(v_cache);
     rp.kl = kl;
     rp.n = n; rp.t0 = start; rp.ld = Lmax; rp.pad_to = 0;
-    rp.B = B; rp.Hkv = Hkv; rp.d = d; rp.in_f32 = dtype == WPA_FP32; rp.v_transposed = 0;
+    rp.B = B; rp.Hkv = Hkv; rp.d = d; rp.in_f32 = dtype == WPA_FP32; rp.v_prefill = 0;
     rp.tab = &tab;
     rp.pg = pg;
     rp.head_theta = head_tables(rope);
@@ -640,6 +640,11 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache, const i
     return ok();
 }
 
+// Room of one key split of a cached prefill (outputs and log2-sums of every row and q head).
+size_t split_bytes(int32_t B, int32_t Nq, int32_t Hq, int32_t d) {
+    return (size_t)B * (size_t)Nq * (size_t)Hq * (size_t)(d + 1) * sizeof(float);
+}
+
 // cache_alpha of a windowed cache: finite (a full window keeps every key: use the dense
 // cache), >= 0
 int check_cache_alpha(double cache_alpha) {
@@ -653,7 +658,8 @@ int prefill_cached_impl(const void* q, const void* k_cache, const void* v_cache,
                         int64_t Lmax, int32_t Hq, int32_t Hkv, int32_t d, double base,
                         const wpa_rope_t* rope, double alpha, float scale, int32_t dtype,
                         int32_t out_dtype, unsigned long long* term_count, void* stream,
-                        const wpa::Paging& pg, const int32_t* cu_q);
+                        const wpa::Paging& pg, const int32_t* cu_q, int32_t splits = 1,
+                        void* workspace = nullptr, size_t ws_bytes = 0);
 
 // A page table's description: page_size a power of two in [32, 65536] (a 32-token tile and
 // an 8-token octet never straddle pages), the table's reach max_pages * page_size below 2^31.
@@ -867,6 +873,47 @@ int wpa_prefill_paged_varlen(const void* q, const void* k_pool, const void* v_po
                                scale, dtype, out_dtype, term_count, stream, pg, cu_q);
 }
 
+size_t wpa_prefill_cached_workspace_bytes(int32_t B, int32_t Nq, int32_t Hq, int32_t Hkv,
+                                          int32_t d, int32_t splits) {
+    if (B < 1 || Nq < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || (d != 64 && d != 128) || splits < 0 ||
+        splits > wpa::kMaxKeySplits || splits == 1)
+        return 0;
+    int ns = splits;
+    if (ns == 0) {
+        // the launch's own choice on the current device, with room for every split
+        wpa::PrefillParams pp{};
+        static const int32_t marker = 0;
+        pp.kv_len = &marker;             // a cached launch (never read here)
+        pp.part = reinterpret_cast<float*>(16);
+        pp.max_splits = wpa::kMaxKeySplits;
+        pp.Nq = Nq; pp.B = B; pp.Hq = Hq; pp.Hkv = Hkv; pp.d = d;
+        ns = wpa::prefill_key_splits(pp);
+    }
+    return ns > 1 ? (size_t)ns * split_bytes(B, Nq, Hq, d) : 0;
+}
+
+int wpa_prefill_cached_ex(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_table, int32_t num_pages, int32_t page_size,
+                          const int32_t* cu_q, const int32_t* kv_len, void* out, float* lse,
+                          int32_t B, int32_t Nq, int64_t Lmax, int32_t Hq, int32_t Hkv, int32_t d,
+                          double base, const wpa_rope_t* rope, double alpha, float scale,
+                          int32_t dtype, int32_t out_dtype, unsigned long long* term_count,
+                          int32_t splits, void* workspace, size_t ws_bytes, void* stream) {
+    if (cu_q && (reinterpret_cast<uintptr_t>(cu_q) & 3u)) return fail(WPA_ERR_INVALID, "cu_q must be 4-byte aligned");
+    wpa::Paging pg{};
+    if (block_table) {
+        if (page_size < 1 || Lmax % page_size || Lmax / page_size > INT32_MAX)
+            return fail(WPA_ERR_INVALID, "Lmax (%lld) must be a multiple of page_size (%d)", (long long)Lmax, page_size);
+        int rc = check_paging(block_table, num_pages, (int32_t)(Lmax / page_size), page_size, &pg);
+        if (rc) return rc;
+        if (page_size < 128)
+            return fail(WPA_ERR_UNSUPPORTED, "chunked prefill on paged caches needs page_size >= 128 (got %d)", page_size);
+    }
+    return prefill_cached_impl(q, k_cache, v_cache, kv_len, out, lse, B, Nq, Lmax, Hq, Hkv, d,
+                               base, rope, alpha, scale, dtype, out_dtype, term_count, stream, pg,
+                               cu_q, splits, workspace, ws_bytes);
+}
+
 }  // extern "C"
 
 namespace {
@@ -876,7 +923,8 @@ int prefill_cached_impl(const void* q, const void* k_cache, const void* v_cache,
                         int64_t Lmax, int32_t Hq, int32_t Hkv, int32_t d, double base,
                         const wpa_rope_t* rope, double alpha, float scale, int32_t dtype,
                         int32_t out_dtype, unsigned long long* term_count, void* stream,
-                        const wpa::Paging& pg, const int32_t* cu_q) {
+                        const wpa::Paging& pg, const int32_t* cu_q, int32_t splits,
+                        void* workspace, size_t ws_bytes) {
     int rc = check_common(d, base, rope, alpha);
     if (rc) return rc;
     rc = no_head_tables(rope, "chunked prefill");
@@ -905,6 +953,22 @@ int prefill_cached_impl(const void* q, const void* k_cache, const void* v_cache,
     pp.scale = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)d));
     pp.pg = pg;
     pp.cu_q = cu_q;
+    if (splits < 0 || splits > wpa::kMaxKeySplits)
+        return fail(WPA_ERR_INVALID, "splits must be in [0, %d] (got %d)", wpa::kMaxKeySplits, splits);
+    if (splits != 1 && workspace) {
+        if (!aligned16(workspace)) return fail(WPA_ERR_INVALID, "workspace must be 16-byte aligned");
+        // the splits the workspace has room for
+        const size_t per = split_bytes(B, Nq, Hq, d);
+        const size_t fit = ws_bytes / per;
+        pp.part = static_cast<float*>(workspace);
+        pp.max_splits = (int32_t)(fit < (size_t)wpa::kMaxKeySplits ? fit : (size_t)wpa::kMaxKeySplits);
+        pp.splits = splits;
+        if (splits > 1 && pp.max_splits < splits)
+            return fail(WPA_ERR_INVALID, "workspace of %zu bytes holds %d key splits, %d asked for",
+                        ws_bytes, pp.max_splits, splits);
+    } else if (splits > 1) {
+        return fail(WPA_ERR_INVALID, "%d key splits need a workspace", splits);
+    }
     hipError_t e = wpa::launch_prefill(pp, tab, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(WPA_ERR_HIP, "cached prefill launch: %s", hipGetErrorString(e));
     return ok();

@@ -16,10 +16,10 @@ struct Tables {
     double theta[kMaxPairs];      // rotation frequency of pair i (base^(-2i/d), or a table)
 };
 
-// Rotate keys into the pair-blocked layout [B][Hkv][d/16][ld][16] (bf16) and, for
-// prefill, write V transposed to [B][Hkv][d][ld]; for the decode cache, V is copied to
-// [B][Hkv][ld][d].  Tokens t0 .. t0+n-1 of the destination receive source rows 0 .. n-1;
-// tokens n .. pad_to-1 (prefill only) are zero-filled.
+// Rotate keys into the pair-blocked layout [B][Hkv][d/16][ld][16] (IEEE half) and write V
+// by key octets, [B][Hkv][ceil(ld/8)][d][8] (bf16), for the prefill workspace and the decode
+// cache alike.  Tokens t0 .. t0+n-1 of the destination receive source rows 0 .. n-1; tokens
+// n .. pad_to-1 (prefill only) are zero-filled.
 // Rows of the pair-blocked K layout of one (sequence, kv head): block j holds cap[j] rows
 // starting at row off[j].  A block with fewer rows than the tokens it serves is a ring:
 // token t sits in row t mod cap[j] (cap[j] a multiple of 32, so a 32-token tile starting at a
@@ -51,10 +51,12 @@ struct RopeParams {
     const void* v;                // [B][n][Hkv][d]
     const int32_t* pos;           // [B][n] or null (positions t0 + row)
     uint16_t* kp;                 // pair-blocked rotated keys, rows as in kl
-    uint16_t* vout;               // transposed (prefill) or row-major (cache) values
+    uint16_t* vout;               // values by key octets [B][Hkv][ld/8][d][8]
     KLayout kl;
     int64_t n, t0, ld, pad_to;
-    int32_t B, Hkv, d, in_f32, v_transposed;
+    int32_t B, Hkv, d, in_f32;
+    int32_t v_prefill;            // the prefill workspace (all of it written, zero past n)
+                                  // rather than a cache write (other tokens kept)
     int32_t interleaved;          // pair i = dims (2i, 2i+1) instead of (i, i+d/2)
     const Tables* tab;            // host pointer; copied into kernel arguments
     Paging pg;                    // decode cache writes: pages (table null: kl layout)
@@ -64,7 +66,8 @@ struct RopeParams {
 struct PrefillParams {
     const void* q;                // [B][N][Hq][d]  (cached: [B][Nq][Hq][d])
     const uint16_t* kp;           // [B][Hkv][d/16][ldk][16]
-    const uint16_t* vt;           // [B][Hkv][d][Np]  (cached: V cache [B][Hkv][ceil(ldk/8)][d][8])
+    const uint16_t* vt;           // V by key octets [B][Hkv][Np/8][d][8]  (cached: the V cache
+                                  // [B][Hkv][ceil(ldk/8)][d][8])
     const int32_t* kv_len;        // cached (chunked) prefill: [B] keys per sequence; else null
     int64_t ldk;                  // key row stride of kp: Np, or Lmax of the caches
     int32_t Nq;                   // cached: queries per sequence (its last Nq tokens)
@@ -84,7 +87,15 @@ struct PrefillParams {
                                   // sequence (q, out [rows][Hq][d], lse [rows][Hq]); else null
     const double* head_theta;     // [Hkv][d/2] device: per-kv-head frequencies (windows are
     double alpha;                 // computed from them and alpha in the kernel), or null (tab)
+    // cached prefill: key splits (the row blocks' key tiles shared among up to max_splits
+    // workgroups, their partials merged by a combine kernel) when part is set and
+    // max_splits > 1; splits > 0 asks for exactly that many (capped), 0 lets the launch choose
+    float* part;                  // [ns][B*Nq][Hq][d] outputs, then [ns][B*Nq][Hq] log2-sums
+    int32_t max_splits, splits;
 };
+
+// Most key splits of one cached prefill launch.
+constexpr int kMaxKeySplits = 16;
 
 struct DecodeParams {
     const void* q;                // [B][Hq][d]
@@ -137,6 +148,9 @@ struct BwdParams {
 hipError_t launch_rope_relayout(const RopeParams& p, hipStream_t s);
 hipError_t launch_backward(const BwdParams& p, const Tables& t, hipStream_t s);
 hipError_t launch_prefill(const PrefillParams& p, const Tables& t, hipStream_t s);
+// Key splits a cached prefill launch with these shapes would take on the current device
+// (p.max_splits, p.splits as for the launch; 1: none).
+int prefill_key_splits(const PrefillParams& p);
 // LDS bytes a block-sparse prefill launch for p (d, dtype, N, counter) needs, and the
 // device's per-workgroup limit; nothing is enqueued.
 hipError_t prefill_sparse_lds(const PrefillParams& p, size_t* need, size_t* limit);

@@ -1,6 +1,8 @@
 """GPU parity of chunked prefill against the decode caches (ragged batches: each sequence
 has its own cached prefix) with the fp64 oracle: a chunk's rows are rows kv_len-Nq ..
-kv_len-1 of a causal windowed prefill over the sequence's first kv_len tokens."""
+kv_len-1 of a causal windowed prefill over the sequence's first kv_len tokens.  With key
+splits (each row block's key tiles shared among several workgroups, their partials merged by
+a second kernel) the rows are the same attention up to fp32 rounding order: the same bar."""
 import math
 
 import numpy as np
@@ -24,7 +26,8 @@ def _poisoned_cache(B, Lmax, Hkv, d, base, **rope):
     return cache
 
 
-def _run_ragged(B, Nq, prefix, Hq, Hkv, d, base, alpha, dtype="bf16", seed=0, rope=None):
+def _run_ragged(B, Nq, prefix, Hq, Hkv, d, base, alpha, dtype="bf16", seed=0, rope=None,
+                splits=0):
     rope = rope or {}
     lens = [Nq + p for p in prefix]
     Lmax = max(lens) + 13
@@ -37,7 +40,7 @@ def _run_ragged(B, Nq, prefix, Hq, Hkv, d, base, alpha, dtype="bf16", seed=0, ro
     kv_len = torch.tensor(lens, dtype=torch.int32, device="cuda")
     cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
     out, lse = wpa.prefill_cached(qc.cuda(), cache, kv_len, alpha, want_lse=True, term_count=cnt,
-                                  out_dtype=torch.float32)
+                                  out_dtype=torch.float32, splits=splits)
     torch.cuda.synchronize()
     kept_all = 0
     for b, L in enumerate(lens):
@@ -53,19 +56,47 @@ def _run_ragged(B, Nq, prefix, Hq, Hkv, d, base, alpha, dtype="bf16", seed=0, ro
     assert int(cnt.item()) == kept_all
 
 
+@pytest.mark.parametrize("splits", [1, 0])
 @pytest.mark.parametrize("alpha", [1.0, 2.0, math.inf])
 @pytest.mark.parametrize("Nq", [1, 77, 300])
 @pytest.mark.parametrize("shape", [
     (14, 2, 64, 1e6),          # Qwen2.5-0.5B heads
     (24, 8, 128, 5e5),         # Llama-3.2-3B heads
 ])
-def test_chunked_prefill_ragged_matches_oracle(shape, Nq, alpha):
+def test_chunked_prefill_ragged_matches_oracle(shape, Nq, alpha, splits):
     """Three sequences with prefixes 0, 517 and 1290 tokens (chunk starts off the 32-token
-    grid), Nq not a multiple of 32, cache slots past each length poisoned with NaN."""
+    grid), Nq not a multiple of 32, cache slots past each length poisoned with NaN; no key
+    splits (the plain entry point) and the launch's own choice (here the most: few rows)."""
     need_gpu()
     Hq, Hkv, d, base = shape
-    say("chunked ragged", shape, Nq, alpha)
-    _run_ragged(3, Nq, [0, 517, 1290], Hq, Hkv, d, base, alpha, seed=Nq + d)
+    say("chunked ragged", shape, Nq, alpha, "splits", splits)
+    _run_ragged(3, Nq, [0, 517, 1290], Hq, Hkv, d, base, alpha, seed=Nq + d, splits=splits)
+
+
+@pytest.mark.parametrize("splits", [2, 3, 5, 16])
+@pytest.mark.parametrize("shape", [(14, 2, 64, 1e6), (24, 8, 128, 5e5), (16, 16, 64, 1e4)])
+def test_key_split_counts_match_oracle(shape, splits):
+    """Explicit split counts, from two to more splits than a row block has key tiles (empty
+    splits), over prefixes that put row blocks across tile edges; one q head per kv head
+    takes the several-row-groups-per-workgroup layout."""
+    need_gpu()
+    Hq, Hkv, d, base = shape
+    say("key splits", shape, splits)
+    _run_ragged(3, 200, [0, 400, 1700], Hq, Hkv, d, base, 1.0, seed=splits + d, splits=splits)
+
+
+def test_key_splits_need_room():
+    need_gpu()
+    cache = wpa.KVCache(1, 512, 2, 64, 1e4)
+    q = torch.zeros((1, 64, 14, 64), dtype=torch.bfloat16, device="cuda")
+    lens = torch.full((1,), 512, dtype=torch.int32, device="cuda")
+    need = wpa.prefill_cached_workspace_bytes(1, 64, 14, 2, 64, 4)
+    assert need == 4 * 64 * 14 * 65 * 4
+    small = torch.empty(need - 16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError):
+        wpa.prefill_cached(q, cache, lens, 1.0, splits=4, workspace=small)
+    with pytest.raises(ValueError):
+        wpa.prefill_cached(q, cache, lens, 1.0, splits=17)
 
 
 def test_chunked_prefill_fp32_queries_and_variant():
@@ -94,7 +125,7 @@ def test_prompt_in_chunks_equals_one_shot_oracle(d, Hq, Hkv, base):
         cache.write(k[:, s:s + n].cuda().contiguous(), v[:, s:s + n].cuda().contiguous(), s)
         kv_len = torch.tensor([s + n], dtype=torch.int32, device="cuda")
         outs.append(wpa.prefill_cached(q[:, s:s + n].cuda().contiguous(), cache, kv_len, alpha,
-                                       out_dtype=torch.float32))
+                                       out_dtype=torch.float32))       # (key splits: automatic)
         s += n
     torch.cuda.synchronize()
     got = torch.cat(outs, dim=1).cpu().numpy()
@@ -123,3 +154,29 @@ def test_chunk_after_long_prefix_sampled_rows():
                               1.0, rows=rows + P)
     check_close(out[:, rows].cpu().numpy(), ro, "sampled rows")
     assert int(cnt.item()) == Hq * wpa.count_terms(d, base, 1.0, Nq, P, L)[0]
+
+
+def test_qwen05b_chunk_schedule_key_splits_sampled():
+    """The Qwen2.5-0.5B prompt of 32768 tokens in 8 chunks of 4096 (append K/V, then attend,
+    key splits chosen by the launch), sampled rows of every chunk against the oracle, and
+    the kept-term count of the whole schedule against the closed form."""
+    need_gpu()
+    w = synth.WORKLOADS["qwen05b"]
+    q, k, v = synth.workload_inputs(w, device="cuda")
+    cache = wpa.KVCache(w.B, w.N, w.Hkv, w.d, w.base)
+    out = torch.empty_like(q, dtype=torch.float32)
+    cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
+    C = 4096
+    for s in range(0, w.N, C):
+        cache.write(k[:, s:s + C], v[:, s:s + C], s)
+        lens = torch.full((w.B,), s + C, dtype=torch.int32, device="cuda")
+        wpa.prefill_cached(q[:, s:s + C], cache, lens, 1.0, out=out[:, s:s + C], term_count=cnt)
+    torch.cuda.synchronize()
+    say("qwen05b chunk schedule: oracle rows")
+    rows = np.unique(np.concatenate([synth.sample_rows(w.N, 12, seed=w.seed),
+                                     np.arange(0, w.N, C), np.arange(C - 1, w.N, C)]))
+    got = out[:, torch.as_tensor(rows, device="cuda")].cpu().numpy()
+    ro, _, _ = oracle.prefill(synth.to_oracle(q), synth.to_oracle(k), synth.to_oracle(v), w.base,
+                              1.0, rows=rows)
+    check_close(got, ro, "chunk schedule sampled rows")
+    assert int(cnt.item()) == w.Hq * wpa.count_terms(w.d, w.base, 1.0, w.N, 0, w.N)[0]

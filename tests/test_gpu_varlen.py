@@ -1,7 +1,8 @@
 """GPU parity of varlen chunked prefill (a query count per sequence, rows packed back to back):
-every row bit-identical to the same row of a per-sequence chunked prefill with that count, on
-contiguous and on paged caches, and within tolerance of the fp64 oracle; sequences with no
-rows, one row, rows not a multiple of 32, and a whole-prompt chunk."""
+without key splits every row bit-identical to the same row of a per-sequence chunked prefill
+with that count; with or without them, paged caches bit-identical to contiguous ones and every
+row within tolerance of the fp64 oracle; sequences with no rows, one row, rows not a multiple
+of 32, and a whole-prompt chunk."""
 import numpy as np
 import pytest
 import torch
@@ -14,8 +15,9 @@ from gpu_util import LSE_MAX, as_bf16_for_oracle as exact, check_close, need_gpu
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("splits", [1, 0, 3])
 @pytest.mark.parametrize("d,Hq,Hkv,base", [(64, 14, 2, 1e6), (128, 24, 8, 5e5)])
-def test_varlen_chunks_match_per_sequence_and_oracle(d, Hq, Hkv, base):
+def test_varlen_chunks_match_per_sequence_and_oracle(d, Hq, Hkv, base, splits):
     need_gpu()
     qn = [0, 1, 77, 300, 256]                       # query rows per sequence
     kv = [50, 1000, 2000, 300, 1500]                # tokens in the cache, each >= its rows
@@ -40,12 +42,13 @@ def test_varlen_chunks_match_per_sequence_and_oracle(d, Hq, Hkv, base):
     cu_q = torch.from_numpy(cu).cuda()
     kv_len = torch.tensor(kv, dtype=torch.int32, device="cuda")
     cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
-    say("varlen contiguous", d)
+    say("varlen contiguous", d, "splits", splits)
     out, lse = wpa.prefill_cached(qp, cache, kv_len, 1.0, cu_q=cu_q, max_q=max(qn),
-                                  want_lse=True, term_count=cnt, out_dtype=torch.float32)
+                                  want_lse=True, term_count=cnt, out_dtype=torch.float32,
+                                  splits=splits)
     say("varlen paged", d)
     outp, lsep = wpa.prefill_cached(qp, paged, kv_len, 1.0, cu_q=cu_q, max_q=max(qn),
-                                    want_lse=True, out_dtype=torch.float32)
+                                    want_lse=True, out_dtype=torch.float32, splits=splits)
     torch.cuda.synchronize()
     assert torch.equal(out, outp) and torch.equal(lse, lsep), "paged varlen differs"
     kept_all = 0
@@ -53,14 +56,15 @@ def test_varlen_chunks_match_per_sequence_and_oracle(d, Hq, Hkv, base):
         if qn[b] == 0:
             continue
         r0, r1, L = cu[b], cu[b + 1], kv[b]
-        one = wpa.KVCache(1, Lmax, Hkv, d, base)
-        one.write(k[b:b + 1, :L].cuda().contiguous(), v[b:b + 1, :L].cuda().contiguous(), 0)
-        ro1, rl1 = wpa.prefill_cached(qp[r0:r1].unsqueeze(0).contiguous(), one,
-                                      kv_len[b:b + 1].contiguous(), 1.0, want_lse=True,
-                                      out_dtype=torch.float32)
-        torch.cuda.synchronize()
-        assert torch.equal(out[r0:r1], ro1[0]), "varlen rows of sequence %d differ" % b
-        assert torch.equal(lse[r0:r1].transpose(0, 1), rl1[0]), "varlen lse of sequence %d" % b
+        if splits == 1:
+            one = wpa.KVCache(1, Lmax, Hkv, d, base)
+            one.write(k[b:b + 1, :L].cuda().contiguous(), v[b:b + 1, :L].cuda().contiguous(), 0)
+            ro1, rl1 = wpa.prefill_cached(qp[r0:r1].unsqueeze(0).contiguous(), one,
+                                          kv_len[b:b + 1].contiguous(), 1.0, want_lse=True,
+                                          out_dtype=torch.float32, splits=1)
+            torch.cuda.synchronize()
+            assert torch.equal(out[r0:r1], ro1[0]), "varlen rows of sequence %d differ" % b
+            assert torch.equal(lse[r0:r1].transpose(0, 1), rl1[0]), "varlen lse of sequence %d" % b
         ro, rl, kept = oracle.prefill(exact(q[b:b + 1, :L]), exact(k[b:b + 1, :L]),
                                       exact(v[b:b + 1, :L]), base, 1.0,
                                       rows=np.arange(L - qn[b], L))

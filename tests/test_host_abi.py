@@ -168,6 +168,54 @@ def test_prefill_cached_rejects_bad_arguments(kw, code):
     assert wpa.lib().wpa_last_error().decode() != ""
 
 
+def _cached_ex_rc(**kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, table=None, npages=0, psize=0, cu=None, lens=FAKE,
+             out=FAKE, lse=None, B=2, Nq=64, Lmax=4096, Hq=8, Hkv=2, d=128, base=5e5, rope=None,
+             alpha=1.0, scale=0.0, dtype=0, odt=1, cnt=None, splits=4, ws=FAKE,
+             ws_bytes=1 << 30)
+    a.update(kw)
+    return wpa.lib().wpa_prefill_cached_ex(
+        a["q"], a["kc"], a["vc"], a["table"], a["npages"], a["psize"], a["cu"], a["lens"],
+        a["out"], a["lse"], a["B"], a["Nq"], a["Lmax"], a["Hq"], a["Hkv"], a["d"], a["base"],
+        a["rope"], a["alpha"], a["scale"], a["dtype"], a["odt"], a["cnt"], a["splits"], a["ws"],
+        a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(splits=-1), wpa.WPA_ERR_INVALID),
+    (dict(splits=17), wpa.WPA_ERR_INVALID),
+    (dict(splits=2, ws=None, ws_bytes=0), wpa.WPA_ERR_INVALID),          # splits need room
+    (dict(splits=4, ws_bytes=3 * 2 * 64 * 8 * 129 * 4), wpa.WPA_ERR_INVALID),   # room for 3
+    (dict(ws=ctypes.c_void_p((1 << 20) + 4)), wpa.WPA_ERR_INVALID),      # misaligned workspace
+    (dict(cu=ctypes.c_void_p((1 << 20) + 2)), wpa.WPA_ERR_INVALID),      # misaligned cu_q
+    (dict(table=FAKE, npages=16, psize=64), wpa.WPA_ERR_UNSUPPORTED),    # pages below 128
+    (dict(table=FAKE, npages=16, psize=384), wpa.WPA_ERR_INVALID),       # not a power of two
+    (dict(table=FAKE, npages=16, psize=256, Lmax=4000), wpa.WPA_ERR_INVALID),
+    (dict(d=96), wpa.WPA_ERR_UNSUPPORTED),
+    (dict(Nq=5000), wpa.WPA_ERR_INVALID),
+    (dict(rope=None, alpha=float("nan")), wpa.WPA_ERR_INVALID),
+])
+def test_prefill_cached_ex_rejects_bad_arguments(kw, code):
+    assert _cached_ex_rc(**kw) == code
+    assert wpa.lib().wpa_last_error().decode() != ""
+
+
+def test_prefill_cached_workspace_bytes():
+    f = wpa.lib().wpa_prefill_cached_workspace_bytes
+    # explicit counts: splits * B * Nq * Hq * (d + 1) floats
+    assert f(2, 64, 8, 2, 128, 4) == 4 * 2 * 64 * 8 * 129 * 4
+    assert f(1, 4096, 14, 2, 64, 2) == 2 * 4096 * 14 * 65 * 4
+    assert f(1, 64, 8, 2, 128, 1) == 0            # no splits, no room
+    for bad in ((0, 64, 8, 2, 128, 2), (1, 64, 8, 3, 128, 2), (1, 64, 8, 2, 96, 2),
+                (1, 64, 8, 2, 128, 17), (1, 64, 8, 2, 128, -1)):
+        assert f(*bad) == 0
+    # the launch's own choice: a multiple of one split's room, at most 16 of them
+    per = 1 * 4096 * 14 * 65 * 4
+    auto = f(1, 4096, 14, 2, 64, 0)
+    assert auto % per == 0 and auto // per in range(0, 17)
+    assert f(1, 1 << 20, 28, 4, 128, 0) == 0      # rows enough to fill the GPU: no splits
+
+
 def test_kv_write_rejects_out_of_range():
     L = wpa.lib()
     rc = L.wpa_kv_write(FAKE, FAKE, 4000, 200, FAKE, FAKE, 1, 4096, 2, 64, 1e4, 0, None)
@@ -427,7 +475,7 @@ def cpu_as_device(monkeypatch):
     def no_call(*a, **k):
         raise AssertionError("a rejected call reached the library")
     for name in ("wpa_prefill_ex", "wpa_prefill_attend_ex", "wpa_prefill_prepare_ex", "wpa_decode_ex",
-                 "wpa_prefill_cached", "wpa_prefill_sparse"):
+                 "wpa_prefill_cached", "wpa_prefill_sparse", "wpa_prefill_cached_ex"):
         monkeypatch.setattr(wpa.lib(), name, no_call)
     return torch
 
