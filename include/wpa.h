@@ -478,6 +478,26 @@ int wpa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char* wpa_last_error(void);
 
+/*
+ * Debug mode, for finding a caller's mistakes; off by default.  It starts on when the
+ * environment variable WPA_DEBUG is set to anything but "0" when first consulted;
+ * wpa_set_debug(1) / (0) switches it for the process, and wpa_set_debug(-1) only reports the
+ * state.  Returns the previous state (0 or 1).
+ * In debug mode every entry point that enqueues work also, before enqueueing anything:
+ *   - checks that each device buffer it will read or write lies inside one allocation of
+ *     the HIP runtime with at least the bytes the call needs from that pointer;
+ *   - reads back, after the stream drains, the device-resident values the kernels otherwise
+ *     trust, and checks them.  Those are positions (non-negative, non-decreasing per
+ *     sequence), per-head frequency tables (finite, > 0, non-increasing), chunked prefill's
+ *     kv_len (in [q_b, Lmax]) and cu_q (non-decreasing from >= 0, q_b <= max_q), and every
+ *     block-table entry a call will use (in [0, num_pages));
+ *   - returns WPA_ERR_INVALID with a message naming the buffer or value, enqueueing nothing.
+ * After enqueueing, it waits for the stream and returns WPA_ERR_HIP if a kernel failed,
+ * so that a fault is reported by the call that caused it.  Debug mode synchronises, and so
+ * it is slow; results are bit-identical to normal mode.
+ */
+int wpa_set_debug(int32_t on);
+
 #ifdef __cplusplus
 }
 #endif

@@ -44,7 +44,8 @@ EXPORTS = ("wpa_count_terms", "wpa_thresholds", "wpa_prefill_workspace_bytes", "
            "wpa_kv_write_paged", "wpa_decode_paged", "wpa_prefill_paged",
            "wpa_prefill_cached_varlen", "wpa_prefill_paged_varlen", "wpa_decode_noalloc",
            "wpa_prefill_backward_workspace_bytes", "wpa_prefill_backward",
-           "wpa_prefill_cached_workspace_bytes", "wpa_prefill_cached_ex", "wpa_last_error")
+           "wpa_prefill_cached_workspace_bytes", "wpa_prefill_cached_ex", "wpa_set_debug",
+           "wpa_last_error")
 
 
 class Rope(ctypes.Structure):
@@ -216,6 +217,8 @@ def lib():
     L.wpa_prefill_cached_ex.argtypes = [P, P, P, P, I32, I32, P, P, P, P, I32, I32, I64, I32, I32,
                                         I32, D, P, D, F, I32, I32, P, I32, P, SZ, P]
     L.wpa_prefill_cached_ex.restype = ctypes.c_int
+    L.wpa_set_debug.argtypes = [I32]
+    L.wpa_set_debug.restype = ctypes.c_int
     L.wpa_last_error.argtypes = []
     L.wpa_last_error.restype = ctypes.c_char_p
     _lib = L
@@ -706,6 +709,12 @@ def decode_noalloc(q, cache, kv_len, alpha: float, *, out, q_pos=None, scale: fl
                                     _dtype_code(out), _ptr(term_count), int(chunk_keys),
                                     _stream(stream)))
     return (out, lse) if lse is not None else out
+
+
+def set_debug(on) -> bool:
+    """Switch the library's debug mode (buffer-extent and device-value checks, a wait after
+    every launch); None only reports it.  Returns the previous state."""
+    return bool(lib().wpa_set_debug(-1 if on is None else int(bool(on))))
 
 
 def prefill_cached_workspace_bytes(B: int, Nq: int, Hq: int, Hkv: int, d: int,

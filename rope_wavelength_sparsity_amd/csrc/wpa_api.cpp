@@ -4,11 +4,14 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
+#include <vector>
 
 #include "wpa_internal.hpp"
 
@@ -26,6 +29,136 @@ int fail(int code, const char* fmt, ...) {
 
 int ok() {
     g_err[0] = 0;
+    return WPA_OK;
+}
+
+// ---- Debug mode: WPA_DEBUG set in the environment (to anything but "0"), or wpa_set_debug(1).
+// An entry point then also checks, before it enqueues anything, that every device buffer it
+// will touch lies inside one allocation of at least the bytes it needs, and that the
+// preconditions on device-resident values hold (read back to the host after the stream
+// drains); after enqueueing it waits for the stream and reports a failure there as
+// WPA_ERR_HIP from the call that caused it.  All of this is host code around the launches.
+std::atomic<int> g_debug{-1};
+
+bool debug_on() {
+    int v = g_debug.load(std::memory_order_relaxed);
+    if (v < 0) {
+        const char* e = std::getenv("WPA_DEBUG");
+        v = (e && *e && std::strcmp(e, "0") != 0) ? 1 : 0;
+        g_debug.store(v, std::memory_order_relaxed);
+    }
+    return v == 1;
+}
+
+size_t esize(int32_t dtype) { return dtype == WPA_FP32 ? 4 : 2; }
+
+// [p, p + bytes) inside one allocation the HIP runtime knows (device, or pinned host memory)
+int dbg_extent(const void* p, size_t bytes, const char* name) {
+    if (!p || bytes == 0) return WPA_OK;
+    hipDeviceptr_t base = nullptr;
+    size_t size = 0;
+    if (hipMemGetAddressRange(&base, &size, const_cast<void*>(p)) != hipSuccess || !base) {
+        (void)hipGetLastError();
+        return fail(WPA_ERR_INVALID, "debug: %s (%p) is not inside an allocation of the HIP runtime",
+                    name, p);
+    }
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p), b0 = reinterpret_cast<uintptr_t>(base);
+    if (a + bytes > b0 + size)
+        return fail(WPA_ERR_INVALID, "debug: %s needs %zu bytes from %p, but its allocation ends %zu "
+                    "bytes after it", name, bytes, p, (size_t)(b0 + size - a));
+    return WPA_OK;
+}
+
+// copy n device values to the host once the stream has drained (after dbg_extent)
+template <typename T>
+int dbg_fetch(const T* p, size_t n, std::vector<T>* h, void* stream, const char* name) {
+    h->assign(n, T{});
+    if (!p || n == 0) return WPA_OK;
+    hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+    if (e == hipSuccess) e = hipMemcpy(h->data(), p, n * sizeof(T), hipMemcpyDeviceToHost);
+    if (e != hipSuccess)
+        return fail(WPA_ERR_HIP, "debug: reading %s back: %s", name, hipGetErrorString(e));
+    return WPA_OK;
+}
+
+// wait for the stream; a device-side failure becomes this call's error
+int dbg_finish(void* stream, const char* what) {
+    const hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(WPA_ERR_HIP, "debug: %s failed on the device: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+// Debug checks of values the kernels trust: positions non-decreasing in [0, 2^31) per
+// sequence; per-head rotation frequencies finite, > 0 and non-increasing per row.
+int dbg_positions(const int32_t* pos, int32_t B, int64_t N, void* stream) {
+    if (!pos) return WPA_OK;
+    int rc = dbg_extent(pos, (size_t)B * N * 4, "positions");
+    if (rc) return rc;
+    std::vector<int32_t> h;
+    rc = dbg_fetch(pos, (size_t)B * N, &h, stream, "positions");
+    if (rc) return rc;
+    for (int32_t b = 0; b < B; ++b)
+        for (int64_t t = 0; t < N; ++t) {
+            const int32_t x = h[(size_t)b * N + t];
+            if (x < 0) return fail(WPA_ERR_INVALID, "debug: positions[%d][%lld] = %d is negative", b, (long long)t, x);
+            if (t > 0 && x < h[(size_t)b * N + t - 1])
+                return fail(WPA_ERR_INVALID, "debug: positions of sequence %d decrease at %lld", b, (long long)t);
+        }
+    return WPA_OK;
+}
+
+int dbg_head_tables(const wpa_rope_t* rope, int32_t Hkv, int32_t d, void* stream) {
+    const double* t = rope ? rope->head_inv_freq : nullptr;
+    if (!t) return WPA_OK;
+    int rc = dbg_extent(t, (size_t)Hkv * (d / 2) * sizeof(double), "head_inv_freq");
+    if (rc) return rc;
+    std::vector<double> h;
+    rc = dbg_fetch(t, (size_t)Hkv * (d / 2), &h, stream, "head_inv_freq");
+    if (rc) return rc;
+    for (int32_t g = 0; g < Hkv; ++g)
+        for (int i = 0; i < d / 2; ++i) {
+            const double x = h[(size_t)g * (d / 2) + i];
+            if (!(x > 0.0) || !std::isfinite(x) || (i > 0 && x > h[(size_t)g * (d / 2) + i - 1]))
+                return fail(WPA_ERR_INVALID, "debug: head_inv_freq[%d][%d] = %g (rows must be finite, "
+                            "> 0 and non-increasing)", g, i, x);
+        }
+    return WPA_OK;
+}
+
+// page-table entries of the pages that tokens [t0, t1) of sequence b reach
+int dbg_pages(const std::vector<int32_t>& table, int32_t b, int32_t max_pages, int32_t page_log2,
+              int32_t num_pages, int64_t t0, int64_t t1) {
+    if (t1 <= t0) return WPA_OK;
+    for (int64_t i = t0 >> page_log2; i <= (t1 - 1) >> page_log2; ++i) {
+        const int32_t pg = table[(size_t)b * max_pages + i];
+        if (pg < 0 || pg >= num_pages)
+            return fail(WPA_ERR_INVALID, "debug: block_table[%d][%lld] = %d is outside [0, %d)", b,
+                        (long long)i, pg, num_pages);
+    }
+    return WPA_OK;
+}
+
+// The decode caches (K in layout kl, V by key octets) or the page pools and, for the latter,
+// the table entries of the pages that tokens [t0[b], t1[b]) of each sequence reach.
+int dbg_caches(const void* kc, const void* vc, int32_t B, int64_t Lmax, int32_t Hkv, int32_t d,
+               const wpa::KLayout& kl, const wpa::Paging& pg, const std::vector<int64_t>& t0,
+               const std::vector<int64_t>& t1, void* stream) {
+    int rc;
+    if (!pg.table) {
+        if ((rc = dbg_extent(kc, (size_t)B * Hkv * kl.head * 32, "k_cache")) ||
+            (rc = dbg_extent(vc, (size_t)B * Hkv * ((Lmax + 7) / 8) * 8 * d * 2, "v_cache")))
+            return rc;
+        return WPA_OK;
+    }
+    const size_t page = (size_t)Hkv * d * ((size_t)1 << pg.page_log2) * 2;
+    if ((rc = dbg_extent(kc, page * pg.num_pages, "k_pool")) ||
+        (rc = dbg_extent(vc, page * pg.num_pages, "v_pool")) ||
+        (rc = dbg_extent(pg.table, (size_t)B * pg.max_pages * 4, "block_table")))
+        return rc;
+    std::vector<int32_t> table;
+    if ((rc = dbg_fetch(pg.table, (size_t)B * pg.max_pages, &table, stream, "block_table"))) return rc;
+    for (int32_t b = 0; b < B; ++b)
+        if ((rc = dbg_pages(table, b, pg.max_pages, pg.page_log2, pg.num_pages, t0[b], t1[b]))) return rc;
     return WPA_OK;
 }
 
@@ -199,6 +332,12 @@ extern "C" {
 
 const char* wpa_last_error(void) { return g_err; }
 
+int wpa_set_debug(int32_t on) {
+    const int was = debug_on() ? 1 : 0;
+    if (on >= 0) g_debug.store(on ? 1 : 0, std::memory_order_relaxed);
+    return was;
+}
+
 int wpa_thresholds_ex(int32_t d, double base, const wpa_rope_t* rope, double alpha, int32_t* W) {
     if (d < 2 || d > 128 || (d & 1)) return fail(WPA_ERR_INVALID, "d must be even and in [2, 128]");
     int rc = check_rope(d, base, rope);
@@ -296,8 +435,16 @@ int wpa_prefill_prepare_ex(const void* k, const void* v, const int32_t* position
     rp.interleaved = interleaved(rope);
     rp.head_theta = head_tables(rope);
     rp.tab = &tab;
+    if (debug_on()) {
+        const size_t kv = (size_t)B * N * Hkv * d * esize(dtype);
+        if ((rc = dbg_extent(k, kv, "k")) || (rc = dbg_extent(v, kv, "v")) ||
+            (rc = dbg_extent(workspace, wpa_prefill_workspace_bytes(B, N, Hkv, d), "workspace")) ||
+            (rc = dbg_positions(positions, B, N, stream)) || (rc = dbg_head_tables(rope, Hkv, d, stream)))
+            return rc;
+    }
     hipError_t e = wpa::launch_rope_relayout(rp, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(WPA_ERR_HIP, "rope relayout launch: %s", hipGetErrorString(e));
+    if (debug_on()) return dbg_finish(stream, "prefill prepare");
     return ok();
 }
 
@@ -369,8 +516,21 @@ int attend_impl(const void* q, void* out, float* lse, const int32_t* positions, 
     pp.blk_count = blk_count; pp.blk_idx = blk_idx; pp.blk_max = blk_max;
     pp.head_theta = head_tables(rope);
     pp.alpha = alpha;
+    if (debug_on()) {
+        const size_t qo = (size_t)B * N * Hq * d, nblk = (size_t)((N + 63) / 64);
+        if ((rc = dbg_extent(q, qo * esize(dtype), "q")) ||
+            (rc = dbg_extent(out, qo * esize(out_dtype), "out")) ||
+            (rc = dbg_extent(lse, (size_t)B * Hq * N * 4, "lse")) ||
+            (rc = dbg_extent(term_count, 8, "term_count")) ||
+            (rc = dbg_extent(workspace, wpa_prefill_workspace_bytes(B, N, Hkv, d), "workspace")) ||
+            (rc = dbg_extent(blk_count, (size_t)B * Hq * nblk * 4, "blk_count")) ||
+            (rc = dbg_extent(blk_idx, (size_t)B * Hq * nblk * (blk_max > 0 ? blk_max : 0) * 4, "blk_idx")) ||
+            (rc = dbg_positions(positions, B, N, stream)) || (rc = dbg_head_tables(rope, Hkv, d, stream)))
+            return rc;
+    }
     hipError_t e = wpa::launch_prefill(pp, tab, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(WPA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+    if (debug_on()) return dbg_finish(stream, "prefill attend");
     return ok();
 }
 
@@ -530,8 +690,18 @@ int wpa_prefill_backward(const void* q, const void* k, const void* v, const void
     bp.out_f32 = out_dtype == WPA_FP32; bp.grad_f32 = grad_dtype == WPA_FP32;
     bp.interleaved = interleaved(rope);
     bp.scale = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)d));
+    if (debug_on()) {
+        const size_t nq = (size_t)B * N * Hq * d, nk = (size_t)B * N * Hkv * d, eg = esize(grad_dtype);
+        if ((rc = dbg_extent(q, nq * 2, "q")) || (rc = dbg_extent(k, nk * 2, "k")) ||
+            (rc = dbg_extent(v, nk * 2, "v")) || (rc = dbg_extent(out, nq * esize(out_dtype), "out")) ||
+            (rc = dbg_extent(lse, (size_t)B * Hq * N * 4, "lse")) || (rc = dbg_extent(dout, nq * 2, "dout")) ||
+            (rc = dbg_extent(dq, nq * eg, "dq")) || (rc = dbg_extent(dk, nk * eg, "dk")) ||
+            (rc = dbg_extent(dv, nk * eg, "dv")) || (rc = dbg_extent(workspace, L.total, "workspace")))
+            return rc;
+    }
     hipError_t e = wpa::launch_backward(bp, tab, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(WPA_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
+    if (debug_on()) return dbg_finish(stream, "prefill backward");
     return ok();
 }
 
@@ -579,8 +749,18 @@ int kv_write_impl(const void* k, const void* v, int64_t start, int64_t n, void* 
     rp.tab = &tab;
     rp.pg = pg;
     rp.head_theta = head_tables(rope);
+    if (debug_on()) {
+        const size_t src = (size_t)B * n * Hkv * d * esize(dtype);
+        int rc;
+        if ((rc = dbg_extent(k, src, "k")) || (rc = dbg_extent(v, src, "v")) ||
+            (rc = dbg_caches(k_cache, v_cache, B, Lmax, Hkv, d, kl, pg, std::vector<int64_t>(B, start),
+                             std::vector<int64_t>(B, start + n), stream)) ||
+            (rc = dbg_head_tables(rope, Hkv, d, stream)))
+            return rc;
+    }
     hipError_t e = wpa::launch_rope_relayout(rp, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(WPA_ERR_HIP, "kv write launch: %s", hipGetErrorString(e));
+    if (debug_on()) return dbg_finish(stream, "kv write");
     return ok();
 }
 
@@ -635,8 +815,28 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache, const i
     dp.pg = pg;
     dp.head_theta = head_tables(rope);
     dp.alpha = alpha;
+    if (debug_on()) {
+        // (kv_len values are clamped by the kernels: not a precondition, but the pages the
+        // clamped lengths reach must be in the pool)
+        const size_t qo = (size_t)B * Hq * d;
+        std::vector<int32_t> len;
+        int rc;
+        if ((rc = dbg_extent(q, qo * esize(dtype), "q")) || (rc = dbg_extent(out, qo * esize(out_dtype), "out")) ||
+            (rc = dbg_extent(lse, (size_t)B * Hq * 4, "lse")) || (rc = dbg_extent(term_count, 8, "term_count")) ||
+            (rc = dbg_extent(kv_len, (size_t)B * 4, "kv_len")) || (rc = dbg_extent(q_pos, (size_t)B * 4, "q_pos")) ||
+            (!use_scratch && (rc = dbg_extent(workspace, need, "workspace"))) ||
+            (rc = dbg_fetch(kv_len, (size_t)B, &len, stream, "kv_len")) ||
+            (rc = dbg_head_tables(rope, Hkv, d, stream)))
+            return rc;
+        std::vector<int64_t> t1(B);
+        for (int32_t b = 0; b < B; ++b) t1[b] = len[b] < 0 ? 0 : (len[b] > Lmax ? Lmax : len[b]);
+        if ((rc = dbg_caches(k_cache, v_cache, B, Lmax, Hkv, d, kl, pg, std::vector<int64_t>(B, 0), t1,
+                             stream)))
+            return rc;
+    }
     hipError_t e = wpa::launch_decode(dp, tab, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(WPA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+    if (debug_on()) return dbg_finish(stream, "decode");
     return ok();
 }
 
@@ -969,8 +1169,38 @@ int prefill_cached_impl(const void* q, const void* k_cache, const void* v_cache,
     } else if (splits > 1) {
         return fail(WPA_ERR_INVALID, "%d key splits need a workspace", splits);
     }
+    if (debug_on()) {
+        // kv_len[b] in [q_b, Lmax]; cu_q non-decreasing from >= 0 with q_b <= Nq
+        std::vector<int32_t> len, cu;
+        if ((rc = dbg_extent(kv_len, (size_t)B * 4, "kv_len")) ||
+            (rc = dbg_extent(cu_q, (size_t)(B + 1) * 4, "cu_q")) ||
+            (rc = dbg_fetch(kv_len, (size_t)B, &len, stream, "kv_len")) ||
+            (rc = dbg_fetch(cu_q, cu_q ? (size_t)B + 1 : 0, &cu, stream, "cu_q")))
+            return rc;
+        if (cu_q && cu[0] < 0) return fail(WPA_ERR_INVALID, "debug: cu_q[0] = %d is negative", cu[0]);
+        std::vector<int64_t> t1(B);
+        for (int32_t b = 0; b < B; ++b) {
+            const int64_t qb = cu_q ? (int64_t)cu[b + 1] - cu[b] : Nq;
+            if (qb < 0 || qb > Nq)
+                return fail(WPA_ERR_INVALID, "debug: sequence %d has %lld queries (allowed 0 .. %d)", b,
+                            (long long)qb, Nq);
+            if (len[b] < qb || len[b] > Lmax)
+                return fail(WPA_ERR_INVALID, "debug: kv_len[%d] = %d is outside [%lld, %lld]", b, len[b],
+                            (long long)qb, (long long)Lmax);
+            t1[b] = len[b];
+        }
+        const size_t rows = cu_q ? (size_t)cu[B] : (size_t)B * Nq;
+        if ((rc = dbg_extent(q, rows * Hq * d * esize(dtype), "q")) ||
+            (rc = dbg_extent(out, rows * Hq * d * esize(out_dtype), "out")) ||
+            (rc = dbg_extent(lse, rows * Hq * 4, "lse")) || (rc = dbg_extent(term_count, 8, "term_count")) ||
+            (rc = dbg_extent(pp.part ? workspace : nullptr, ws_bytes, "workspace")) ||
+            (rc = dbg_caches(k_cache, v_cache, B, Lmax, Hkv, d, dense_layout(d, Lmax), pg,
+                             std::vector<int64_t>(B, 0), t1, stream)))
+            return rc;
+    }
     hipError_t e = wpa::launch_prefill(pp, tab, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(WPA_ERR_HIP, "cached prefill launch: %s", hipGetErrorString(e));
+    if (debug_on()) return dbg_finish(stream, "cached prefill");
     return ok();
 }
 

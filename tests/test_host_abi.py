@@ -564,3 +564,46 @@ def _prefill_ex_rc(rope):
     L = wpa.lib()
     return L.wpa_prefill_ex(FAKE, FAKE, FAKE, FAKE, None, None, 1, 128, 4, 2, 64, 1e4, rope, 1.0, 0.0,
                             0, 0, None, FAKE, 1 << 30, None)
+
+
+# ---------------------------------------------------------------- debug mode (host side)
+
+def test_debug_mode_switch():
+    L = wpa.lib()
+    was = L.wpa_set_debug(-1)
+    try:
+        assert L.wpa_set_debug(1) == was
+        assert L.wpa_set_debug(-1) == 1 and wpa.set_debug(None) is True
+        assert L.wpa_set_debug(0) == 1
+        assert L.wpa_set_debug(-1) == 0
+    finally:
+        L.wpa_set_debug(was)
+
+
+@pytest.mark.parametrize("value,on", [("1", 1), ("yes", 1), ("0", 0), ("", 0)])
+def test_debug_mode_from_environment(value, on):
+    import subprocess
+    import sys
+    code = "import ctypes, sys; print(ctypes.CDLL(sys.argv[1]).wpa_set_debug(-1))"
+    env = dict(os.environ, WPA_DEBUG=value)
+    r = subprocess.run([sys.executable, "-c", code, wpa.LIB_PATH], env=env, capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip() == str(on)
+
+
+def test_debug_mode_checks_after_argument_checks():
+    """Argument errors keep their codes in debug mode; arguments that pass them meet the
+    buffer checks, which reject a pointer outside every allocation before any launch."""
+    L = wpa.lib()
+    was = L.wpa_set_debug(1)
+    try:
+        assert _cached_rc(d=96) == wpa.WPA_ERR_UNSUPPORTED
+        assert _cached_rc(Nq=5000) == wpa.WPA_ERR_INVALID
+        assert "debug" not in L.wpa_last_error().decode()
+        assert _cached_rc() == wpa.WPA_ERR_INVALID
+        assert L.wpa_last_error().decode().startswith("debug: kv_len")
+        assert _cached_ex_rc(splits=0) == wpa.WPA_ERR_INVALID
+        assert L.wpa_last_error().decode().startswith("debug:")
+    finally:
+        L.wpa_set_debug(was)
