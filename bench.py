@@ -72,6 +72,11 @@ def _parse():
                     help="instead of the headline line: the prefill backward (dq, dk, dv) at the "
                          "Qwen2.5-0.5B (32K) and Llama-3.2-3B (128K) shapes, alpha 1 and inf, "
                          "printed as one JSON line")
+    ap.add_argument("--cpu-table", action="store_true",
+                    help="instead of the headline line: the fp64 oracle timed on this host's cores "
+                         "for each workload (full runs of tiny and qwen05b, sampled rows of the "
+                         "larger prefills with the full time extrapolated, full decode steps), "
+                         "printed as one JSON line")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (twice), as the "
                          "reference kernel for scaling FETCH_SIZE/WRITE_SIZE counters")
@@ -487,6 +492,78 @@ def _block_lists(B, H, N, density, seed, pattern="random"):
     return torch.from_numpy(count).cuda(), torch.from_numpy(idx).cuda()
 
 
+def cpu_table():
+    """The unmodified fp64 oracle on this host's cores for each workload, on the inputs the
+    GPU runs use (drawn on the device, copied to the host): the tiny and Qwen2.5-0.5B prefills
+    in full (the latter in slices of 4096 query rows, timed and summed), 128 / 64 sampled rows
+    of the Llama-3.2-3B / Qwen2.5-7B-1M prefills with the full time extrapolated from them,
+    and one full decode step of each decode workload."""
+    import numpy as np
+    import torch
+    import oracle
+    import rope_wavelength_sparsity_amd as wpa
+    import synth
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    res = {"cpu_model": _cpu_model(), "threads": threads, "rows": []}
+
+    def host(w):
+        ins = synth.workload_inputs(w, device="cuda")
+        out = tuple(synth.to_oracle(t) if t.dtype != torch.int32 else t.cpu().numpy() for t in ins)
+        del ins
+        torch.cuda.empty_cache()
+        return out
+
+    def row_flops(w, alpha, rows):
+        f = 0
+        for r in rows.tolist():
+            kept, _ = wpa.count_terms(w.d, w.base, alpha, 1, r, r + 1)
+            f += w.B * w.Hq * (4 * kept + 2 * w.d * (r + 1))
+        return f
+
+    for name, sample in (("tiny", 0), ("qwen05b", 0), ("llama3b", 128), ("qwen7b1m", 64)):
+        w = synth.WORKLOADS[name]
+        alpha = 1.0
+        qa, ka, va = host(w)
+        if sample == 0:
+            dt = 0.0
+            for r0 in range(0, w.N, 4096):
+                rows = np.arange(r0, min(w.N, r0 + 4096))
+                t = time.perf_counter()
+                oracle.prefill(qa, ka, va, w.base, alpha, rows=rows, nthreads=threads)
+                dt += time.perf_counter() - t
+                _log("cpu table: %s rows %d..%d, %.1f s so far" % (name, r0, rows[-1], dt))
+            flops, _ = _prefill_flops(w, alpha)
+            res["rows"].append({"workload": name, "kind": "prefill", "alpha": alpha, "run": "full",
+                                "wall_s": dt, "gflops_fp64": flops / dt / 1e9})
+        else:
+            rows = synth.sample_rows(w.N, sample, seed=w.seed)
+            t = time.perf_counter()
+            oracle.prefill(qa, ka, va, w.base, alpha, rows=rows, nthreads=threads)
+            dt = time.perf_counter() - t
+            rate = row_flops(w, alpha, rows) / dt
+            flops, _ = _prefill_flops(w, alpha)
+            res["rows"].append({"workload": name, "kind": "prefill", "alpha": alpha,
+                                "run": "%d sampled rows (first, last, random)" % len(rows),
+                                "sample_s": dt, "s_per_row": dt / len(rows),
+                                "gflops_fp64": rate / 1e9,
+                                "full_s_extrapolated": flops / rate})
+            _log("cpu table: %s %d rows in %.1f s" % (name, len(rows), dt))
+        del qa, ka, va
+    for name in ("llama3b_decode", "qwen7b1m_decode"):
+        w = synth.WORKLOADS[name]
+        qa, ka, va, lens = host(w)
+        t = time.perf_counter()
+        oracle.decode(qa, ka, va, lens, w.base, 1.0, nthreads=threads)
+        dt = time.perf_counter() - t
+        nbytes = _decode_bytes(w, 1.0, lens.tolist())
+        res["rows"].append({"workload": name, "kind": "decode", "alpha": 1.0,
+                            "run": "one full step (B=%d)" % w.B, "wall_s": dt,
+                            "algorithmic_gbs": nbytes / dt / 1e9})
+        _log("cpu table: %s step in %.2f s" % (name, dt))
+        del qa, ka, va
+    return res
+
+
 def extras(reps):
     """Measurements of the paths beside the core prefill/decode, one dict per path."""
     import torch
@@ -649,6 +726,9 @@ def main():
         return
     if args.backward:
         print(json.dumps(bench_backward(("qwen05b", "llama3b"), max(2, args.steps // 4))), flush=True)
+        return
+    if args.cpu_table:
+        print(json.dumps({"cpu_oracle_table": cpu_table()}), flush=True)
         return
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib << 20

@@ -14,16 +14,19 @@
 // with dl masked to the elements inside its window.
 //
 // Kernels
-//   bwd_prep_k: rotated keys, pair-blocked K' [B][Hkv][d/16][Np][16] and transposed K'^T
-//               [B][Hkv][d][Np] (pair-block element order), IEEE half.
+//   bwd_prep_k: rotated keys, pair-blocked K' [B][Hkv][d/16][Np][16] and K'^T by key octets
+//               [B][Hkv][Np/8][d][8] (pair-block element order), IEEE half; V blocked by 16
+//               dims [B][Hkv][d/16][Np][16] bf16.
 //   bwd_prep_q: rotated queries Q' (times scale*log2 e) pair-blocked, Q'^T (unscaled)
 //               transposed, dout^T [B][Hq][d][Np] bf16, lse*log2 e and D per row.
-//   bwd_dq:     one wave per (sequence, q head, 32 query rows): S^T, P^T, dP^T, dl^T over the
-//               causal key blocks, dq'^T on MFMA; epilogue rotates back and writes dq.
+//   bwd_dq:     a workgroup per (sequence, kv head, row block): each compute wave takes one q
+//               head's 32 query rows; S^T, P^T, dP^T, dl^T over the causal key tiles streamed
+//               through LDS, dq'^T on MFMA; epilogue rotates back and writes dq.
 //   bwd_dkdv:   one wave per (sequence, q head, 32 keys): S, P, dP, dl over the causal row
 //               blocks, dv^T and dk'^T on MFMA, written per q head to a workspace.
 //   bwd_reduce: sums the q heads of each kv head, rotates dk' back, writes dk and dv.
-// Waves take a short and a long row (or key) range in turn, so causal work balances.
+// dk/dv waves take a short and a long key range in turn, so causal work balances; dq
+// workgroups are ordered longest rows first.
 //
 // MFMA layouts (32x32x16): A row m / B column n in lane m%32 / n%32, the 16-deep contraction
 // split 8+8 between lane halves; C element (8(r/4) + 4(l/32) + r%4, l%32) in register r of
@@ -38,6 +41,14 @@ namespace wpa {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// Workgroup layout of the dq kernel: q heads per wave group, row groups per workgroup, head
+// chunks per kv head, row blocks per sequence.
+struct BwdLaunch {
+    int Gc, R, nhc, n_rb;
+};
 
 __device__ inline int perm_row(int m) {
     return (m & ~0xC) | ((m & 4) << 1) | ((m & 8) >> 1);
@@ -109,18 +120,30 @@ __global__ __launch_bounds__(256) void bwd_prep_k_kernel(BwdParams p, Tables tab
     const int64_t t = id % p.Np;
     const int64_t bg = id / p.Np;
     uint16_t* ks = p.ks + bg * NB * p.Np * 16;
-    uint16_t* kt = p.kt + bg * D * p.Np;
+    uint16_t* vb = p.vb + bg * NB * p.Np * 16;
+    // K'^T by key octets: element (x, t) at ((t/8) D + x) 8 + t%8
+    uint16_t* kt = p.kt + bg * D * p.Np + (t >> 3) * D * 8 + (t & 7);
     if (t >= p.N) {
         for (int j = 0; j < NB; ++j) {
             u32x4* d4 = reinterpret_cast<u32x4*>(ks + ((int64_t)j * p.Np + t) * 16);
             d4[0] = u32x4{0u, 0u, 0u, 0u};
             d4[1] = u32x4{0u, 0u, 0u, 0u};
+            u32x4* v4 = reinterpret_cast<u32x4*>(vb + ((int64_t)j * p.Np + t) * 16);
+            v4[0] = u32x4{0u, 0u, 0u, 0u};
+            v4[1] = u32x4{0u, 0u, 0u, 0u};
         }
-        for (int x = 0; x < D; ++x) kt[x * p.Np + t] = 0;
+        for (int x = 0; x < D; ++x) kt[x * 8] = 0;
         return;
     }
     const int g = (int)(bg % p.Hkv), b = (int)(bg / p.Hkv);
     const uint16_t* kr = static_cast<const uint16_t*>(p.k) + (((int64_t)b * p.N + t) * p.Hkv + g) * D;
+    const uint16_t* vr = static_cast<const uint16_t*>(p.v) + (((int64_t)b * p.N + t) * p.Hkv + g) * D;
+    for (int j = 0; j < NB; ++j) {
+        const u32x4* s4 = reinterpret_cast<const u32x4*>(vr + 16 * j);
+        u32x4* v4 = reinterpret_cast<u32x4*>(vb + ((int64_t)j * p.Np + t) * 16);
+        v4[0] = s4[0];
+        v4[1] = s4[1];
+    }
     for (int j = 0; j < NB; ++j) {
         uint16_t el[16];
 #pragma unroll
@@ -143,7 +166,7 @@ __global__ __launch_bounds__(256) void bwd_prep_k_kernel(BwdParams p, Tables tab
         d4[0] = w0;
         d4[1] = w1;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) kt[(int64_t)(16 * j + e) * p.Np + t] = el[e];
+        for (int e = 0; e < 16; ++e) kt[(16 * j + e) * 8] = el[e];
     }
 }
 
@@ -219,57 +242,101 @@ __global__ __launch_bounds__(256) void bwd_prep_q_kernel(BwdParams p, Tables tab
 
 // ---------------------------------------------------------------------------- dq
 
+// dq: a workgroup takes Gc q heads x R row groups (32 rows each) of one kv head and streams
+// that kv head's key tiles through LDS: K' (pair-blocked), V (blocked by 16 dims) and K'^T
+// (by key octets), each one contiguous copy per tile, loaded by an extra producer wave into a
+// two-stage ring.  Every K/V byte then leaves memory once per workgroup.
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
-void bwd_dq_kernel(BwdParams p, Tables tab) {
-    constexpr int NB = D / 16, NDB = D / 32, P = D / 2;
-    const int lane = threadIdx.x & 63, l32 = lane & 31, h = lane >> 5;
-    const int wave = uniform((int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)));
-    const int nrg = (int)((p.N + 31) / 32);
-    const int npair = (nrg + 1) / 2;                    // waves per (sequence, q head)
-    const int bh = wave / npair;
-    if (bh >= p.B * p.Hq) return;
-    const int hq = bh % p.Hq, b = bh / p.Hq;
-    const int g = hq / (p.Hq / p.Hkv);
-    const int wi = wave % npair;
-    const uint16_t* ksg = p.ks + ((int64_t)b * p.Hkv + g) * NB * p.Np * 16;
-    const uint16_t* ktg = p.kt + ((int64_t)b * p.Hkv + g) * D * p.Np;
-    const uint16_t* qsh = p.qs + (int64_t)bh * NB * p.Np * 16;
+struct DqTile {
+    static constexpr int BN = D == 64 ? 128 : 64;       // keys per tile (3 BN d 2 bytes a stage)
+    static constexpr int NSUB = BN / 32;
+    static constexpr int MAXW = 7;                      // compute waves per workgroup
+};
+
+template <int D>
+__global__ __launch_bounds__(64 * (DqTile<D>::MAXW + 1)) __attribute__((amdgpu_waves_per_eu(2)))
+void bwd_dq_kernel(BwdParams p, Tables tab, BwdLaunch L) {
+    constexpr int NB = D / 16, NDB = D / 32, P = D / 2, BN = DqTile<D>::BN, NSUB = DqTile<D>::NSUB;
+    __shared__ __attribute__((aligned(16))) uint16_t sK[2][NB * BN * 16];
+    __shared__ __attribute__((aligned(16))) uint16_t sV[2][NB * BN * 16];
+    __shared__ __attribute__((aligned(16))) uint16_t sT[2][BN * D];
+    const int tid = threadIdx.x;
+    const int w = uniform(tid >> 6);
+    const int lane = tid & 63, l32 = lane & 31, h = lane >> 5;
+    const int G = p.Hq / p.Hkv;
+    const int U = p.B * p.Hkv * L.nhc;
+    const int u = blockIdx.x % U;
+    const int rb = L.n_rb - 1 - (int)(blockIdx.x / U);     // longest rows first
+    const int hc = u % L.nhc, g = (u / L.nhc) % p.Hkv, b = u / (L.nhc * p.Hkv);
+    const int hin = hc * L.Gc + (w % L.Gc), rg = w / L.Gc;
+    const bool producer = w == L.Gc * L.R;
+    const int qs0 = rb * 32 * L.R;
+    const int q0 = qs0 + 32 * rg;
+    const bool wave_ok = !producer && hin < G && q0 < p.N;
+    const int hq = g * G + (hin < G ? hin : 0);
+    const int bh = b * p.Hq + hq;
+    const int row_end = (qs0 + 32 * L.R < p.N ? qs0 + 32 * L.R : (int)p.N) - 1;
+    const int kt_last = row_end / BN;
+    const int64_t kvh = (int64_t)b * p.Hkv + g;
+    const uint16_t* ksg = p.ks + kvh * NB * p.Np * 16;
+    const uint16_t* vbg = p.vb + kvh * NB * p.Np * 16;
+    const uint16_t* ktg = p.kt + kvh * D * p.Np;
     const float sc = p.scale;
 
-    for (int half = 0; half < 2; ++half) {
-        const int rg = paired(wi, nrg, half);
-        if (half == 1 && rg == wi) break;               // odd count: the middle group once
-        const int r0 = 32 * rg;
-        const int row = r0 + l32;
-        const bool row_ok = row < p.N;
-        const int rowc = row_ok ? row : (int)p.N - 1;
-        // B operands held for the row group: Q' (scaled) and dout, lane = row
-        u32x4 Qb[NB], Gb[NB];
+    // tile kt into stage st: K' and V block j are BN rows of 32 bytes (BN/32 wave loads of
+    // 1 KB each); the K'^T octets of the tile are BN*D*2 contiguous bytes
+    auto issue = [&](int kt, int st) {
+        const int64_t k0 = (int64_t)kt * BN;
+        for (int j = 0; j < NB; ++j)
+            for (int part = 0; part < BN / 32; ++part) {
+                const int64_t off = ((int64_t)j * p.Np + k0 + 32 * part) * 16 + lane * 8;
+                __builtin_amdgcn_global_load_lds(ksg + off, (lds_ptr)&sK[st][(j * BN + 32 * part) * 16], 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(vbg + off, (lds_ptr)&sV[st][(j * BN + 32 * part) * 16], 16, 0, 0);
+            }
+        for (int i = 0; i < BN * D * 2 / 1024; ++i)
+            __builtin_amdgcn_global_load_lds(ktg + k0 * D + (i * 64 + lane) * 8, (lds_ptr)&sT[st][i * 512],
+                                             16, 0, 0);
+    };
+
+    // this wave's rows (lane = row): Q' (scaled) and dout as B operands, lse2 and D
+    const int row = q0 + l32;
+    const bool row_ok = wave_ok && row < p.N;
+    const int rowc = row < p.N ? row : (int)p.N - 1;
+    u32x4 Qb[NB], Gb[NB];
+    float lse2 = 0.f, Dv = 0.f;
+    f32x16 acc[NDB];
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
+    if (wave_ok) {
+        const uint16_t* qsh = p.qs + (int64_t)bh * NB * p.Np * 16;
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
             Qb[j] = ld16(qsh + ((int64_t)j * p.Np + row) * 16 + 8 * h);
             Gb[j] = ld16(static_cast<const uint16_t*>(p.dout) +
                          (((int64_t)b * p.N + rowc) * p.Hq + hq) * D + 16 * j + 8 * h);
         }
-        const float lse2 = p.lse2[(int64_t)bh * p.Np + row];
-        const float Dv = p.Dr[(int64_t)bh * p.Np + row];
-        f32x16 acc[NDB];
-#pragma unroll
-        for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
-        int plo = 0, pfull = 0;                         // band edges, distances only grow
-        for (int kb = rg; kb >= 0; --kb) {
-            const int c0 = 32 * kb;
-            const int dmin = uniform(r0 - (c0 + 31) > 0 ? r0 - (c0 + 31) : 0);
-            const int dmax = uniform(r0 + 31 - c0);
+        lse2 = p.lse2[(int64_t)bh * p.Np + row];
+        Dv = p.Dr[(int64_t)bh * p.Np + row];
+    }
+    int plo = 0, pfull = 0;                             // band edges, distances only grow
+
+    auto compute = [&](int kt, const uint16_t* cK, const uint16_t* cV, const uint16_t* cT) {
+        for (int sub = NSUB - 1; sub >= 0; --sub) {
+            const int c0 = kt * BN + 32 * sub;
+            if (c0 > q0 + 31) continue;                 // above every row of the wave
+            const int dmin = uniform(q0 - (c0 + 31) > 0 ? q0 - (c0 + 31) : 0);
+            const int dmax = uniform(q0 + 31 - c0);
             while (plo < P && tab.W[plo] < dmin) ++plo;
             while (pfull < P && tab.W[pfull] < dmax) ++pfull;
             if (pfull < plo) pfull = plo;
-            const int arow = c0 + perm_row(l32);        // key this lane feeds to A
-            auto K = [&](int j) { return ld16(ksg + ((int64_t)j * p.Np + arow) * 16 + 8 * h); };
-            // S^T (log2 units): straddling pairs one by one, then the fully active blocks
-            f32x16 S = f32x16{};
+            const int krow = 32 * sub + perm_row(l32);  // key (in the tile) this lane feeds to A
+            auto K = [&](int j) { return ld16(cK + (j * BN + krow) * 16 + 8 * h); };
+            auto V = [&](int j) { return ld16(cV + (j * BN + krow) * 16 + 8 * h); };
+            // K'^T rows x, keys 16s + 8h .. +7 of the sub-tile: octet 4 sub + 2 s + h
+            auto T = [&](int db, int s2) { return ld16(cT + ((4 * sub + 2 * s2 + h) * D + 32 * db + l32) * 8); };
+            // S^T (log2 units): straddling pairs one by one, then the fully active blocks;
             // register r of half h holds key c0 + idx(r); distance = row - key
+            f32x16 S = f32x16{};
             for (int e = plo; e < pfull; ++e) {
                 S = mfma_h(K(e >> 3), Qb[e >> 3] & pair_mask(e & 7), S);
                 const int We = tab.W[e];
@@ -290,10 +357,8 @@ void bwd_dq_kernel(BwdParams p, Tables tab) {
                 Pt[r] = (key <= row && row_ok) ? __builtin_amdgcn_exp2f(S[r] - lse2) : 0.f;
             }
             f32x16 dPt = f32x16{};
-            const int vkey = arow < p.N ? arow : (int)p.N - 1;
-            const uint16_t* vr = static_cast<const uint16_t*>(p.v) + (((int64_t)b * p.N + vkey) * p.Hkv + g) * D;
 #pragma unroll
-            for (int j = 0; j < NB; ++j) dPt = mfma_b(ld16(vr + 16 * j + 8 * h), Gb[j], dPt);
+            for (int j = 0; j < NB; ++j) dPt = mfma_b(V(j), Gb[j], dPt);
             f32x16 dl;
 #pragma unroll
             for (int r = 0; r < 16; ++r) dl[r] = Pt[r] * (dPt[r] - Dv);
@@ -301,13 +366,13 @@ void bwd_dq_kernel(BwdParams p, Tables tab) {
             const u32x4 dlb[2] = {pack8<false>(dl, 0), pack8<false>(dl, 1)};
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                if (2 * db + 1 < jf) continue;              // every dim of this block dead or straddling
+                if (2 * db + 1 < jf) continue;          // every dim of this block dead or straddling
                 const bool on = pair_of_x(db, l32) >= pfull;
 #pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    u32x4 a = ld16(ktg + (int64_t)(32 * db + l32) * p.Np + c0 + 16 * s + 8 * h);
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    u32x4 a = T(db, s2);
                     if (!on) a = u32x4{0u, 0u, 0u, 0u};
-                    acc[db] = mfma_h(a, dlb[s], acc[db]);
+                    acc[db] = mfma_h(a, dlb[s2], acc[db]);
                 }
             }
             // ... and each straddling pair with dl masked to its window
@@ -320,38 +385,57 @@ void bwd_dq_kernel(BwdParams p, Tables tab) {
                 const int db = e >> 4;
                 const bool on = pair_of_x(db, l32) == e;
 #pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    u32x4 a = ld16(ktg + (int64_t)(32 * db + l32) * p.Np + c0 + 16 * s + 8 * h);
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    u32x4 a = T(db, s2);
                     if (!on) a = u32x4{0u, 0u, 0u, 0u};
                     // (db is wave-uniform: select the accumulator without indexing)
 #pragma unroll
                     for (int dd = 0; dd < NDB; ++dd)
-                        if (dd == db) acc[dd] = mfma_h(a, pack8<false>(m, s), acc[dd]);
+                        if (dd == db) acc[dd] = mfma_h(a, pack8<false>(m, s2), acc[dd]);
                 }
             }
         }
-        // epilogue: scale, rotate back at the row's position, write dq (lane = row)
-        if (row_ok) {
-            const int64_t ob = (((int64_t)b * p.N + row) * p.Hq + hq) * D;
+    };
+
+    // The producer streams tile kt-1 into one stage while the others compute tile kt from
+    // the other; it waits for its own loads before the barrier that hands the stage over.
+    if (producer) {
+        issue(kt_last, 0);
+        __builtin_amdgcn_s_waitcnt(0x0070);             // vmcnt(0) lgkmcnt(0)
+    }
+    for (int kt = kt_last, it = 0; kt >= 0; --kt, ++it) {
+        __syncthreads();
+        if (producer) {
+            if (kt > 0) {
+                issue(kt - 1, (it & 1) ^ 1);
+                __builtin_amdgcn_s_waitcnt(0x0070);
+            }
+        } else if (wave_ok) {
+            compute(kt, sK[it & 1], sV[it & 1], sT[it & 1]);
+        }
+    }
+
+    // epilogue: scale, rotate back at the row's position, write dq (lane = row)
+    if (row_ok) {
+        const int64_t ob = (((int64_t)b * p.N + row) * p.Hq + hq) * D;
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
+        for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    if ((r >> 2) & 1) continue;             // y-components: with their x
-                    const int xl = 8 * (r >> 2) + 4 * h + (r & 3);
-                    const int i = 8 * (2 * db + (xl >> 4)) + (xl & 7);
-                    float sn, cs;
-                    rope_sincos(row, tab.theta[i], &sn, &cs);
-                    const float gx = acc[db][r] * sc, gy = acc[db][r + 4] * sc;
-                    const float ox = gx * cs + gy * sn, oy = gy * cs - gx * sn;
-                    const int ix = p.interleaved ? 2 * i : i, iy = p.interleaved ? 2 * i + 1 : i + P;
-                    if (p.grad_f32) {
-                        static_cast<float*>(p.dq)[ob + ix] = ox;
-                        static_cast<float*>(p.dq)[ob + iy] = oy;
-                    } else {
-                        static_cast<uint16_t*>(p.dq)[ob + ix] = f32_to_bf16_bits(ox);
-                        static_cast<uint16_t*>(p.dq)[ob + iy] = f32_to_bf16_bits(oy);
-                    }
+            for (int r = 0; r < 16; ++r) {
+                if ((r >> 2) & 1) continue;             // y-components: with their x
+                const int xl = 8 * (r >> 2) + 4 * h + (r & 3);
+                const int i = 8 * (2 * db + (xl >> 4)) + (xl & 7);
+                float sn, cs;
+                rope_sincos(row, tab.theta[i], &sn, &cs);
+                const float gx = acc[db][r] * sc, gy = acc[db][r + 4] * sc;
+                const float ox = gx * cs + gy * sn, oy = gy * cs - gx * sn;
+                const int ix = p.interleaved ? 2 * i : i, iy = p.interleaved ? 2 * i + 1 : i + P;
+                if (p.grad_f32) {
+                    static_cast<float*>(p.dq)[ob + ix] = ox;
+                    static_cast<float*>(p.dq)[ob + iy] = oy;
+                } else {
+                    static_cast<uint16_t*>(p.dq)[ob + ix] = f32_to_bf16_bits(ox);
+                    static_cast<uint16_t*>(p.dq)[ob + iy] = f32_to_bf16_bits(oy);
                 }
             }
         }
@@ -551,9 +635,17 @@ hipError_t launch_bwd_d(const BwdParams& p, const Tables& t, hipStream_t s) {
     bwd_prep_k_kernel<D><<<dim3((unsigned)((nk + 255) / 256)), blk, 0, s>>>(p, t);
     bwd_prep_q_kernel<D><<<dim3((unsigned)((nq + 255) / 256)), blk, 0, s>>>(p, t);
     const int64_t ngroups = (p.N + 31) / 32;
+    // dq: Gc q heads x R row groups of one kv head per workgroup (plus the producer wave)
+    const int G = p.Hq / p.Hkv, MW = DqTile<D>::MAXW;
+    BwdLaunch L;
+    L.nhc = (G + MW - 1) / MW;
+    L.Gc = (G + L.nhc - 1) / L.nhc;
+    L.R = MW / L.Gc > 1 ? MW / L.Gc : 1;
+    L.n_rb = (int)((ngroups + L.R - 1) / L.R);
+    const dim3 gq((unsigned)((int64_t)L.n_rb * p.B * p.Hkv * L.nhc)), bq(64 * (L.Gc * L.R + 1));
+    bwd_dq_kernel<D><<<gq, bq, 0, s>>>(p, t, L);
     const int64_t waves = (int64_t)p.B * p.Hq * ((ngroups + 1) / 2);
     const dim3 grid((unsigned)((waves + 3) / 4));
-    bwd_dq_kernel<D><<<grid, blk, 0, s>>>(p, t);
     bwd_dkdv_kernel<D><<<grid, blk, 0, s>>>(p, t);
     const int64_t nr = (int64_t)p.B * p.Hkv * p.N * (D / 2);
     bwd_reduce_kernel<D><<<dim3((unsigned)((nr + 255) / 256)), blk, 0, s>>>(p, t);

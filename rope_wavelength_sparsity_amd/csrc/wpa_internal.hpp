@@ -131,7 +131,9 @@ struct BwdParams {
     void* dk;
     void* dv;
     uint16_t* ks;                 // rotated K' pair-blocked [B][Hkv][d/16][Np][16] half
-    uint16_t* kt;                 // rotated K'^T [B][Hkv][d][Np] half (pair-block row order)
+    uint16_t* kt;                 // rotated K'^T by key octets [B][Hkv][Np/8][d][8] half (pair-block
+                                  // element order within a key's d)
+    uint16_t* vb;                 // V blocked by 16 dims [B][Hkv][d/16][Np][16] bf16
     uint16_t* qs;                 // rotated Q' * scale*log2 e, pair-blocked [B][Hq][d/16][Np][16]
     uint16_t* qt;                 // rotated Q'^T (unscaled) [B][Hq][d][Np] half
     uint16_t* dot;                // dout^T [B][Hq][d][Np] bf16
