@@ -17,16 +17,18 @@
 //   bwd_prep_k: rotated keys, pair-blocked K' [B][Hkv][d/16][Np][16] and K'^T by key octets
 //               [B][Hkv][Np/8][d][8] (pair-block element order), IEEE half; V blocked by 16
 //               dims [B][Hkv][d/16][Np][16] bf16.
-//   bwd_prep_q: rotated queries Q' (times scale*log2 e) pair-blocked, Q'^T (unscaled)
-//               transposed, dout^T [B][Hq][d][Np] bf16, lse*log2 e and D per row.
+//   bwd_prep_q: rotated queries Q' (times scale*log2 e) pair-blocked, Q'^T (unscaled) by row
+//               octets, dout blocked by 16 dims and by row octets (bf16), lse*log2 e and D
+//               per row.
 //   bwd_dq:     a workgroup per (sequence, kv head, row block): each compute wave takes one q
 //               head's 32 query rows; S^T, P^T, dP^T, dl^T over the causal key tiles streamed
 //               through LDS, dq'^T on MFMA; epilogue rotates back and writes dq.
-//   bwd_dkdv:   one wave per (sequence, q head, 32 keys): S, P, dP, dl over the causal row
-//               blocks, dv^T and dk'^T on MFMA, written per q head to a workspace.
+//   bwd_dkdv:   a workgroup per (sequence, q head, key block): each compute wave takes 32
+//               keys; S, P, dP, dl over the causal row tiles streamed through LDS, dv^T and
+//               dk'^T on MFMA, written per q head to a workspace.
 //   bwd_reduce: sums the q heads of each kv head, rotates dk' back, writes dk and dv.
-// dk/dv waves take a short and a long key range in turn, so causal work balances; dq
-// workgroups are ordered longest rows first.
+// Workgroups are ordered longest ranges first (dq: the last row blocks; dk, dv: the first
+// key blocks), so that short ones fill the tail.
 //
 // MFMA layouts (32x32x16): A row m / B column n in lane m%32 / n%32, the 16-deep contraction
 // split 8+8 between lane halves; C element (8(r/4) + 4(l/32) + r%4, l%32) in register r of
@@ -179,17 +181,22 @@ __global__ __launch_bounds__(256) void bwd_prep_q_kernel(BwdParams p, Tables tab
     const int64_t t = id % p.Np;
     const int64_t bh = id / p.Np;
     uint16_t* qs = p.qs + bh * NB * p.Np * 16;
-    uint16_t* qt = p.qt + bh * D * p.Np;
-    uint16_t* dot = p.dot + bh * D * p.Np;
+    uint16_t* dob = p.dob + bh * NB * p.Np * 16;
+    // Q'^T and dout^T by row octets: element (x, t) at ((t/8) D + x) 8 + t%8
+    uint16_t* qt = p.qt + bh * D * p.Np + (t >> 3) * D * 8 + (t & 7);
+    uint16_t* dot = p.dot + bh * D * p.Np + (t >> 3) * D * 8 + (t & 7);
     if (t >= p.N) {
         for (int j = 0; j < NB; ++j) {
             u32x4* d4 = reinterpret_cast<u32x4*>(qs + ((int64_t)j * p.Np + t) * 16);
             d4[0] = u32x4{0u, 0u, 0u, 0u};
             d4[1] = u32x4{0u, 0u, 0u, 0u};
+            u32x4* g4 = reinterpret_cast<u32x4*>(dob + ((int64_t)j * p.Np + t) * 16);
+            g4[0] = u32x4{0u, 0u, 0u, 0u};
+            g4[1] = u32x4{0u, 0u, 0u, 0u};
         }
         for (int x = 0; x < D; ++x) {
-            qt[x * p.Np + t] = 0;
-            dot[x * p.Np + t] = 0;
+            qt[x * 8] = 0;
+            dot[x * 8] = 0;
         }
         p.lse2[bh * p.Np + t] = INFINITY;      // rows past the end: P = 0
         p.Dr[bh * p.Np + t] = 0.f;
@@ -224,14 +231,20 @@ __global__ __launch_bounds__(256) void bwd_prep_q_kernel(BwdParams p, Tables tab
         d4[0] = w0;
         d4[1] = w1;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) qt[(int64_t)(16 * j + e) * p.Np + t] = eu[e];
+        for (int e = 0; e < 16; ++e) qt[(16 * j + e) * 8] = eu[e];
     }
-    // dout^T (natural dim order) and D = dout . out
+    // dout blocked and by row octets (natural dim order), and D = dout . out
     const uint16_t* gr = static_cast<const uint16_t*>(p.dout) + row;
+    for (int j = 0; j < NB; ++j) {
+        const u32x4* s4 = reinterpret_cast<const u32x4*>(gr + 16 * j);
+        u32x4* g4 = reinterpret_cast<u32x4*>(dob + ((int64_t)j * p.Np + t) * 16);
+        g4[0] = s4[0];
+        g4[1] = s4[1];
+    }
     float dd = 0.f;
     for (int x = 0; x < D; ++x) {
         const uint16_t gb = gr[x];
-        dot[x * p.Np + t] = gb;
+        dot[x * 8] = gb;
         const float o = p.out_f32 ? static_cast<const float*>(p.out)[row + x]
                                   : bf16_bits_to_f32(static_cast<const uint16_t*>(p.out)[row + x]);
         dd += bf16_bits_to_f32(gb) * o;
@@ -444,55 +457,121 @@ void bwd_dq_kernel(BwdParams p, Tables tab, BwdLaunch L) {
 
 // ---------------------------------------------------------------------------- dk, dv
 
+// dk, dv: a workgroup takes R key groups (32 keys each) of one q head and streams that q
+// head's row tiles through LDS: Q' (pair-blocked, scaled), dout (blocked by 16 dims), Q'^T
+// and dout^T (by row octets), and the rows' lse and D; the producer wave fills a two-stage
+// ring.  Each compute wave keeps its keys' K' and V as B operands and its dk'^T, dv^T
+// accumulators in registers, and writes them per q head to the workspace.
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
-void bwd_dkdv_kernel(BwdParams p, Tables tab) {
-    constexpr int NB = D / 16, NDB = D / 32, P = D / 2;
-    const int lane = threadIdx.x & 63, l32 = lane & 31, h = lane >> 5;
-    const int wave = uniform((int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)));
-    const int nkg = (int)((p.N + 31) / 32);
-    const int npair = (nkg + 1) / 2;
-    const int bh = wave / npair;
-    if (bh >= p.B * p.Hq) return;
+struct DkTile {
+    static constexpr int BM = D == 64 ? 128 : 64;       // rows per tile (4 BM d 2 + 8 BM bytes a stage)
+    static constexpr int NSUB = BM / 32;
+    static constexpr int MAXW = 7;                      // compute waves per workgroup
+};
+
+template <int D>
+__global__ __launch_bounds__(64 * (DkTile<D>::MAXW + 1)) __attribute__((amdgpu_waves_per_eu(2)))
+void bwd_dkdv_kernel(BwdParams p, Tables tab, int R) {
+    constexpr int NB = D / 16, NDB = D / 32, P = D / 2, BM = DkTile<D>::BM, NSUB = DkTile<D>::NSUB;
+    __shared__ __attribute__((aligned(16))) uint16_t sQ[2][NB * BM * 16];
+    __shared__ __attribute__((aligned(16))) uint16_t sG[2][NB * BM * 16];
+    __shared__ __attribute__((aligned(16))) uint16_t sQt[2][BM * D];
+    __shared__ __attribute__((aligned(16))) uint16_t sGt[2][BM * D];
+    __shared__ __attribute__((aligned(16))) float sL[2][2 * BM];     // lse2, then D, of the rows
+    const int tid = threadIdx.x;
+    const int w = uniform(tid >> 6);
+    const int lane = tid & 63, l32 = lane & 31, h = lane >> 5;
+    const int U = p.B * p.Hq;
+    const int bh = blockIdx.x % U;
+    const int kbk = (int)(blockIdx.x / U);              // key blocks with the most rows first
     const int hq = bh % p.Hq, b = bh / p.Hq;
     const int g = hq / (p.Hq / p.Hkv);
-    const int wi = wave % npair;
-    const uint16_t* ksg = p.ks + ((int64_t)b * p.Hkv + g) * NB * p.Np * 16;
+    const bool producer = w == R;
+    const int c0 = 32 * (kbk * R + w);                  // this wave's first key
+    const bool wave_ok = !producer && c0 < p.N;
+    const int key = c0 + l32;
+    const int keyc = key < p.N ? key : (int)p.N - 1;
+    const int nrt = (int)((p.N + BM - 1) / BM);
+    const int rt_first = (32 * kbk * R) / BM;           // the tile holding the first key's row
     const uint16_t* qsh = p.qs + (int64_t)bh * NB * p.Np * 16;
+    const uint16_t* gbh = p.dob + (int64_t)bh * NB * p.Np * 16;
     const uint16_t* qth = p.qt + (int64_t)bh * D * p.Np;
-    const uint16_t* doth = p.dot + (int64_t)bh * D * p.Np;
+    const uint16_t* gth = p.dot + (int64_t)bh * D * p.Np;
     const float* lse2h = p.lse2 + (int64_t)bh * p.Np;
     const float* Drh = p.Dr + (int64_t)bh * p.Np;
 
-    for (int half = 0; half < 2; ++half) {
-        // key groups with the most rows first: index 0 is the first key group
-        const int kg = paired(wi, nkg, half);
-        if (half == 1 && kg == wi) break;
-        const int c0 = 32 * kg;
-        const int key = c0 + l32;
-        const int keyc = key < p.N ? key : (int)p.N - 1;
-        const uint16_t* vr = static_cast<const uint16_t*>(p.v) + (((int64_t)b * p.N + keyc) * p.Hkv + g) * D;
-        f32x16 dK[NDB], dV[NDB];
-#pragma unroll
-        for (int i = 0; i < NDB; ++i) {
-            dK[i] = f32x16{};
-            dV[i] = f32x16{};
+    // row tile rt into stage st: Q' and dout block j are BM rows of 32 bytes (BM/32 wave loads
+    // of 1 KB), the octet arrays BM*D*2 contiguous bytes, lse2 and D BM floats each
+    auto issue = [&](int rt, int st) {
+        const int64_t r0 = (int64_t)rt * BM;
+        for (int j = 0; j < NB; ++j)
+            for (int part = 0; part < BM / 32; ++part) {
+                const int64_t off = ((int64_t)j * p.Np + r0 + 32 * part) * 16 + lane * 8;
+                __builtin_amdgcn_global_load_lds(qsh + off, (lds_ptr)&sQ[st][(j * BM + 32 * part) * 16], 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(gbh + off, (lds_ptr)&sG[st][(j * BM + 32 * part) * 16], 16, 0, 0);
+            }
+        for (int i = 0; i < BM * D * 2 / 1024; ++i) {
+            const int64_t off = r0 * D + (i * 64 + lane) * 8;
+            __builtin_amdgcn_global_load_lds(qth + off, (lds_ptr)&sQt[st][i * 512], 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(gth + off, (lds_ptr)&sGt[st][i * 512], 16, 0, 0);
         }
-        int plo = 0, pfull = 0;
-        for (int rb = kg; 32 * rb < p.N; ++rb) {
-            const int r0 = 32 * rb;
+        for (int i = 0; i < BM / 64; ++i) {
+            __builtin_amdgcn_global_load_lds(lse2h + r0 + 64 * i + lane, (lds_ptr)&sL[st][64 * i], 4, 0, 0);
+            __builtin_amdgcn_global_load_lds(Drh + r0 + 64 * i + lane, (lds_ptr)&sL[st][BM + 64 * i], 4, 0, 0);
+        }
+    };
+
+    // this wave's keys (lane = key): K' and V, the B operands of S and dP.  V is read again from
+    // the workspace (L2) each sub-tile, its loads issued ahead of the products; so is K' at
+    // d = 128, where holding it next to the dk'^T, dv^T accumulators spills (measured: 923 ms
+    // against 1001 ms for the Llama-3.2-3B shape at 128K); at d = 64 it is held (14.3 against
+    // 13.3 ms for the Qwen2.5-0.5B shape at 32K).
+    constexpr bool HOLDK = D == 64;
+    u32x4 Kh[HOLDK ? NB : 1];
+    f32x16 dK[NDB], dV[NDB];
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) {
+        dK[i] = f32x16{};
+        dV[i] = f32x16{};
+    }
+    const int64_t kvh = (int64_t)b * p.Hkv + g;
+    const uint16_t* kkey = p.ks + (kvh * NB * p.Np + key) * 16 + 8 * h;
+    const uint16_t* vkey = p.vb + (kvh * NB * p.Np + key) * 16 + 8 * h;
+    if constexpr (HOLDK) {
+        if (wave_ok) {
+#pragma unroll
+            for (int j = 0; j < NB; ++j) Kh[j] = ld16(kkey + (int64_t)j * p.Np * 16);
+        }
+    }
+    int plo = 0, pfull = 0;                             // band edges, distances only grow
+
+    auto compute = [&](int rt, const uint16_t* cQ, const uint16_t* cG, const uint16_t* cQt,
+                       const uint16_t* cGt, const float* cL) {
+        for (int sub = 0; sub < NSUB; ++sub) {
+            const int r0 = rt * BM + 32 * sub;
+            if (r0 + 31 < c0 || r0 >= p.N) continue;    // rows before every key, or past the end
             const int dmin = uniform(r0 - (c0 + 31) > 0 ? r0 - (c0 + 31) : 0);
             const int dmax = uniform(r0 + 31 - c0);
             while (plo < P && tab.W[plo] < dmin) ++plo;
             while (pfull < P && tab.W[pfull] < dmax) ++pfull;
             if (pfull < plo) pfull = plo;
-            const int arow = r0 + perm_row(l32);         // row this lane feeds to A
-            auto Q = [&](int j) { return ld16(qsh + ((int64_t)j * p.Np + arow) * 16 + 8 * h); };
-            auto Kb = [&](int j) { return ld16(ksg + ((int64_t)j * p.Np + key) * 16 + 8 * h); };
+            const int arow = 32 * sub + perm_row(l32);  // row (in the tile) this lane feeds to A
+            u32x4 Kb[NB], Vb[NB];
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                if constexpr (HOLDK) Kb[j] = Kh[j];
+                else Kb[j] = ld16(kkey + (int64_t)j * p.Np * 16);
+                Vb[j] = ld16(vkey + (int64_t)j * p.Np * 16);
+            }
+            auto Q = [&](int j) { return ld16(cQ + (j * BM + arow) * 16 + 8 * h); };
+            auto Gr = [&](int j) { return ld16(cG + (j * BM + arow) * 16 + 8 * h); };
+            // x^T rows x, rows 16s + 8h .. +7 of the sub-tile: octet 4 sub + 2 s + h
+            auto QT = [&](int db, int s2) { return ld16(cQt + ((4 * sub + 2 * s2 + h) * D + 32 * db + l32) * 8); };
+            auto GT = [&](int db, int s2) { return ld16(cGt + ((4 * sub + 2 * s2 + h) * D + 32 * db + l32) * 8); };
             // S (log2 units): register r of half h holds row r0 + idx(r); distance = row - key
             f32x16 S = f32x16{};
             for (int e = plo; e < pfull; ++e) {
-                S = mfma_h(Q(e >> 3), Kb(e >> 3) & pair_mask(e & 7), S);
+                S = mfma_h(Q(e >> 3), Kb[e >> 3] & pair_mask(e & 7), S);
                 const int We = tab.W[e];
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
@@ -500,12 +579,12 @@ void bwd_dkdv_kernel(BwdParams p, Tables tab) {
             }
             const int jf = pfull >> 3;
             for (int j = jf; j < NB; ++j) {
-                const u32x4 kb = j == jf ? (Kb(j) & lead_mask(pfull - 8 * jf)) : Kb(j);
+                const u32x4 kb = j == jf ? (Kb[j] & lead_mask(pfull - 8 * jf)) : Kb[j];
                 S = mfma_h(Q(j), kb, S);
             }
-            // lse and D of this lane's 16 rows: rows r0 + 8h + 0..7 and r0 + 16 + 8h + 0..7
-            const f32x4* l4 = reinterpret_cast<const f32x4*>(lse2h + r0 + 8 * h);
-            const f32x4* d4 = reinterpret_cast<const f32x4*>(Drh + r0 + 8 * h);
+            // lse and D of this lane's 16 rows: 32 sub + 8h + 0..7 and 32 sub + 16 + 8h + 0..7
+            const f32x4* l4 = reinterpret_cast<const f32x4*>(cL + 32 * sub + 8 * h);
+            const f32x4* d4 = reinterpret_cast<const f32x4*>(cL + BM + 32 * sub + 8 * h);
             const f32x4 la = l4[0], lb = l4[1], lc = l4[4], ld = l4[5];
             const f32x4 da = d4[0], dbv = d4[1], dc = d4[4], dd = d4[5];
             auto lse_r = [&](int r) { const f32x4& v = r < 4 ? la : (r < 8 ? lb : (r < 12 ? lc : ld)); return v[r & 3]; };
@@ -518,10 +597,8 @@ void bwd_dkdv_kernel(BwdParams p, Tables tab) {
             }
             // dP = dout V^T (A = dout rows, permuted)
             f32x16 dP = f32x16{};
-            const int grow = arow < p.N ? arow : (int)p.N - 1;
-            const uint16_t* gr = static_cast<const uint16_t*>(p.dout) + (((int64_t)b * p.N + grow) * p.Hq + hq) * D;
 #pragma unroll
-            for (int j = 0; j < NB; ++j) dP = mfma_b(ld16(gr + 16 * j + 8 * h), ld16(vr + 16 * j + 8 * h), dP);
+            for (int j = 0; j < NB; ++j) dP = mfma_b(Gr(j), Vb[j], dP);
             f32x16 dl;
 #pragma unroll
             for (int r = 0; r < 16; ++r) dl[r] = Pm[r] * (dP[r] - D_r(r));
@@ -538,18 +615,18 @@ void bwd_dkdv_kernel(BwdParams p, Tables tab) {
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    const u32x4 a = ld16(doth + (int64_t)(32 * db + l32) * p.Np + r0 + 16 * s + 8 * h);
-                    dV[db] = mfma_b(a, pb[s], dV[db]);
-                    dV[db] = mfma_b(a, pl[s], dV[db]);
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const u32x4 a = GT(db, s2);
+                    dV[db] = mfma_b(a, pb[s2], dV[db]);
+                    dV[db] = mfma_b(a, pl[s2], dV[db]);
                 }
                 if (2 * db + 1 < jf) continue;
                 const bool on = pair_of_x(db, l32) >= pfull;
 #pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    u32x4 a = ld16(qth + (int64_t)(32 * db + l32) * p.Np + r0 + 16 * s + 8 * h);
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    u32x4 a = QT(db, s2);
                     if (!on) a = u32x4{0u, 0u, 0u, 0u};
-                    dK[db] = mfma_h(a, dlb[s], dK[db]);
+                    dK[db] = mfma_h(a, dlb[s2], dK[db]);
                 }
             }
             for (int e = plo; e < pfull; ++e) {
@@ -561,27 +638,44 @@ void bwd_dkdv_kernel(BwdParams p, Tables tab) {
                 const int db = e >> 4;
                 const bool on = pair_of_x(db, l32) == e;
 #pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    u32x4 a = ld16(qth + (int64_t)(32 * db + l32) * p.Np + r0 + 16 * s + 8 * h);
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    u32x4 a = QT(db, s2);
                     if (!on) a = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
                     for (int dd2 = 0; dd2 < NDB; ++dd2)
-                        if (dd2 == db) dK[dd2] = mfma_h(a, pack8<false>(m, s), dK[dd2]);
+                        if (dd2 == db) dK[dd2] = mfma_h(a, pack8<false>(m, s2), dK[dd2]);
                 }
             }
         }
-        // this q head's dk'^T (unscaled, pair-block order) and dv^T for the lane's key, as
-        // fp32 partials [B][Hq][Np][d]; register r of half h holds x = 32db + 8(r/4) + 4h + r%4
-        float* kp = p.dkp + ((int64_t)bh * p.Np + key) * D;
-        float* vp = p.dvp + ((int64_t)bh * p.Np + key) * D;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int x = 32 * db + 8 * q4 + 4 * h;
-                *reinterpret_cast<f32x4*>(kp + x) = f32x4{dK[db][4 * q4], dK[db][4 * q4 + 1], dK[db][4 * q4 + 2], dK[db][4 * q4 + 3]};
-                *reinterpret_cast<f32x4*>(vp + x) = f32x4{dV[db][4 * q4], dV[db][4 * q4 + 1], dV[db][4 * q4 + 2], dV[db][4 * q4 + 3]};
+    };
+
+    if (producer) {
+        issue(rt_first, 0);
+        __builtin_amdgcn_s_waitcnt(0x0070);             // vmcnt(0) lgkmcnt(0)
+    }
+    for (int rt = rt_first, it = 0; rt < nrt; ++rt, ++it) {
+        __syncthreads();
+        if (producer) {
+            if (rt + 1 < nrt) {
+                issue(rt + 1, (it & 1) ^ 1);
+                __builtin_amdgcn_s_waitcnt(0x0070);
             }
+        } else if (wave_ok) {
+            compute(rt, sQ[it & 1], sG[it & 1], sQt[it & 1], sGt[it & 1], sL[it & 1]);
+        }
+    }
+    if (!wave_ok) return;
+    // this q head's dk'^T (unscaled, pair-block order) and dv^T for the lane's key, as fp32
+    // partials [B][Hq][Np][d]; register r of half h holds x = 32db + 8(r/4) + 4h + r%4
+    float* kp = p.dkp + ((int64_t)bh * p.Np + key) * D;
+    float* vp = p.dvp + ((int64_t)bh * p.Np + key) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const int x = 32 * db + 8 * q4 + 4 * h;
+            *reinterpret_cast<f32x4*>(kp + x) = f32x4{dK[db][4 * q4], dK[db][4 * q4 + 1], dK[db][4 * q4 + 2], dK[db][4 * q4 + 3]};
+            *reinterpret_cast<f32x4*>(vp + x) = f32x4{dV[db][4 * q4], dV[db][4 * q4 + 1], dV[db][4 * q4 + 2], dV[db][4 * q4 + 3]};
         }
     }
 }
@@ -644,9 +738,10 @@ hipError_t launch_bwd_d(const BwdParams& p, const Tables& t, hipStream_t s) {
     L.n_rb = (int)((ngroups + L.R - 1) / L.R);
     const dim3 gq((unsigned)((int64_t)L.n_rb * p.B * p.Hkv * L.nhc)), bq(64 * (L.Gc * L.R + 1));
     bwd_dq_kernel<D><<<gq, bq, 0, s>>>(p, t, L);
-    const int64_t waves = (int64_t)p.B * p.Hq * ((ngroups + 1) / 2);
-    const dim3 grid((unsigned)((waves + 3) / 4));
-    bwd_dkdv_kernel<D><<<grid, blk, 0, s>>>(p, t);
+    // dk, dv: R key groups of one q head per workgroup (plus the producer wave)
+    const int RK = DkTile<D>::MAXW;
+    const int64_t nkb = (ngroups + RK - 1) / RK;
+    bwd_dkdv_kernel<D><<<dim3((unsigned)(nkb * p.B * p.Hq)), dim3(64 * (RK + 1)), 0, s>>>(p, t, RK);
     const int64_t nr = (int64_t)p.B * p.Hkv * p.N * (D / 2);
     bwd_reduce_kernel<D><<<dim3((unsigned)((nr + 255) / 256)), blk, 0, s>>>(p, t);
     return hipGetLastError();

@@ -621,18 +621,18 @@ int wpa_prefill_sparse(const void* q, const void* k, const void* v, void* out, f
 
 // Workspace of the prefill backward: its regions, in order, each 256-byte aligned.
 struct BwdLayout {
-    size_t off[10];
+    size_t off[11];
     size_t total;
 };
 
 BwdLayout bwd_layout(int32_t B, int64_t N, int32_t Hq, int32_t Hkv, int32_t d) {
     const int64_t Np = round_up(N, wpa::kTileKeys);
     const size_t kvh = (size_t)B * Hkv * Np * d, qh = (size_t)B * Hq * Np * d, rows = (size_t)B * Hq * Np;
-    const size_t sz[10] = {kvh * 2, kvh * 2, qh * 2, qh * 2, qh * 2, rows * 4, rows * 4, qh * 4, qh * 4,
-                           kvh * 2};
+    const size_t sz[11] = {kvh * 2, kvh * 2, qh * 2, qh * 2, qh * 2, rows * 4, rows * 4, qh * 4, qh * 4,
+                           kvh * 2, qh * 2};
     BwdLayout L{};
     size_t at = 0;
-    for (int i = 0; i < 10; ++i) {
+    for (int i = 0; i < 11; ++i) {
         L.off[i] = at;
         at += (sz[i] + 255) / 256 * 256;
     }
@@ -687,6 +687,7 @@ int wpa_prefill_backward(const void* q, const void* k, const void* v, const void
     bp.dkp = reinterpret_cast<float*>(w + L.off[7]);
     bp.dvp = reinterpret_cast<float*>(w + L.off[8]);
     bp.vb = reinterpret_cast<uint16_t*>(w + L.off[9]);
+    bp.dob = reinterpret_cast<uint16_t*>(w + L.off[10]);
     bp.N = N; bp.Np = round_up(N, wpa::kTileKeys);
     bp.B = B; bp.Hq = Hq; bp.Hkv = Hkv; bp.d = d;
     bp.out_f32 = out_dtype == WPA_FP32; bp.grad_f32 = grad_dtype == WPA_FP32;

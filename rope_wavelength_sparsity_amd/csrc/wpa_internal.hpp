@@ -135,8 +135,9 @@ struct BwdParams {
                                   // element order within a key's d)
     uint16_t* vb;                 // V blocked by 16 dims [B][Hkv][d/16][Np][16] bf16
     uint16_t* qs;                 // rotated Q' * scale*log2 e, pair-blocked [B][Hq][d/16][Np][16]
-    uint16_t* qt;                 // rotated Q'^T (unscaled) [B][Hq][d][Np] half
-    uint16_t* dot;                // dout^T [B][Hq][d][Np] bf16
+    uint16_t* qt;                 // rotated Q'^T (unscaled) by row octets [B][Hq][Np/8][d][8] half
+    uint16_t* dot;                // dout^T by row octets [B][Hq][Np/8][d][8] bf16
+    uint16_t* dob;                // dout blocked by 16 dims [B][Hq][d/16][Np][16] bf16
     float* lse2;                  // lse * log2 e [B][Hq][Np] (+inf past N)
     float* Dr;                    // dout . out [B][Hq][Np]
     float* dkp;                   // per-q-head dk'^T partials [B][Hq][Np][d] (pair-block order)
