@@ -297,18 +297,30 @@ void bwd_dq_kernel(BwdParams p, Tables tab, BwdLaunch L) {
     const float sc = p.scale;
 
     // tile kt into stage st: K' and V block j are BN rows of 32 bytes (BN/32 wave loads of
-    // 1 KB each); the K'^T octets of the tile are BN*D*2 contiguous bytes
+    // 1 KB each); the K'^T octets of the tile are BN*D*2 contiguous bytes.  Pair blocks below
+    // jlo, dead for every row of the workgroup at the tile's smallest distance, are not
+    // loaded: no wave reads K' there, and their K'^T dims enter the dq product only as the
+    // zeroed operand of inactive dims.  (A K'^T wave load holds 64 dims of one octet.)
+    // (the producer's band edge lives in LDS: a register would be held by every wave)
+    __shared__ int s_plo;
     auto issue = [&](int kt, int st) {
         const int64_t k0 = (int64_t)kt * BN;
+        const int dmin = uniform(qs0 - (int)(k0 + BN - 1) > 0 ? qs0 - (int)(k0 + BN - 1) : 0);
+        int plo_wg = kt == kt_last ? 0 : uniform(s_plo);
+        while (plo_wg < P && tab.W[plo_wg] < dmin) ++plo_wg;
+        s_plo = plo_wg;
+        const int jlo = plo_wg >> 3;
         for (int j = 0; j < NB; ++j)
             for (int part = 0; part < BN / 32; ++part) {
                 const int64_t off = ((int64_t)j * p.Np + k0 + 32 * part) * 16 + lane * 8;
-                __builtin_amdgcn_global_load_lds(ksg + off, (lds_ptr)&sK[st][(j * BN + 32 * part) * 16], 16, 0, 0);
+                if (j >= jlo)
+                    __builtin_amdgcn_global_load_lds(ksg + off, (lds_ptr)&sK[st][(j * BN + 32 * part) * 16], 16, 0, 0);
                 __builtin_amdgcn_global_load_lds(vbg + off, (lds_ptr)&sV[st][(j * BN + 32 * part) * 16], 16, 0, 0);
             }
         for (int i = 0; i < BN * D * 2 / 1024; ++i)
-            __builtin_amdgcn_global_load_lds(ktg + k0 * D + (i * 64 + lane) * 8, (lds_ptr)&sT[st][i * 512],
-                                             16, 0, 0);
+            if (64 * (i % (D / 64)) + 63 >= 16 * jlo)
+                __builtin_amdgcn_global_load_lds(ktg + k0 * D + (i * 64 + lane) * 8, (lds_ptr)&sT[st][i * 512],
+                                                 16, 0, 0);
     };
 
     // this wave's rows (lane = row): Q' (scaled) and dout as B operands, lse2 and D
@@ -502,12 +514,23 @@ void bwd_dkdv_kernel(BwdParams p, Tables tab, int R) {
 
     // row tile rt into stage st: Q' and dout block j are BM rows of 32 bytes (BM/32 wave loads
     // of 1 KB), the octet arrays BM*D*2 contiguous bytes, lse2 and D BM floats each
+    // (pair blocks below jlo, dead for every key of the workgroup at the tile's smallest
+    // distance: Q' and the Q'^T dims of whole dead wave loads are not loaded, as in dq)
+    // (the producer's band edge lives in LDS: a register would be held by every wave)
+    __shared__ int s_plo;
     auto issue = [&](int rt, int st) {
         const int64_t r0 = (int64_t)rt * BM;
+        const int kend_wg = 32 * (kbk * R + R) - 1;     // the workgroup's last key
+        const int dmin = uniform((int)r0 - kend_wg > 0 ? (int)r0 - kend_wg : 0);
+        int plo_wg = rt == rt_first ? 0 : uniform(s_plo);
+        while (plo_wg < P && tab.W[plo_wg] < dmin) ++plo_wg;
+        s_plo = plo_wg;
+        const int jlo = plo_wg >> 3;
         for (int j = 0; j < NB; ++j)
             for (int part = 0; part < BM / 32; ++part) {
                 const int64_t off = ((int64_t)j * p.Np + r0 + 32 * part) * 16 + lane * 8;
-                __builtin_amdgcn_global_load_lds(qsh + off, (lds_ptr)&sQ[st][(j * BM + 32 * part) * 16], 16, 0, 0);
+                if (j >= jlo)
+                    __builtin_amdgcn_global_load_lds(qsh + off, (lds_ptr)&sQ[st][(j * BM + 32 * part) * 16], 16, 0, 0);
                 __builtin_amdgcn_global_load_lds(gbh + off, (lds_ptr)&sG[st][(j * BM + 32 * part) * 16], 16, 0, 0);
             }
         for (int i = 0; i < BM * D * 2 / 1024; ++i) {
