@@ -44,8 +44,8 @@ PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
 def _parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="qwen7b1m", help="prefill workload (synth.WORKLOADS)")
     ap.add_argument("--alpha", type=float, default=None, help="override the workload's alpha")
     ap.add_argument("--decode-workload", default="qwen7b1m_decode",

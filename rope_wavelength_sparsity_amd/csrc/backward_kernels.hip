@@ -476,7 +476,7 @@ void bwd_dq_kernel(BwdParams p, Tables tab, BwdLaunch L) {
 // accumulators in registers, and writes them per q head to the workspace.
 template <int D>
 struct DkTile {
-    static constexpr int BM = D == 64 ? 128 : 64;       // rows per tile (4 BM d 2 + 8 BM bytes a stage)
+    static constexpr int BM = D == 64 ? 128 : 32;       // rows per tile (4 BM d 2 + 8 BM bytes a stage)
     static constexpr int NSUB = BM / 32;
     static constexpr int MAXW = 7;                      // compute waves per workgroup
 };
@@ -490,6 +490,11 @@ void bwd_dkdv_kernel(BwdParams p, Tables tab, int R) {
     __shared__ __attribute__((aligned(16))) uint16_t sQt[2][BM * D];
     __shared__ __attribute__((aligned(16))) uint16_t sGt[2][BM * D];
     __shared__ __attribute__((aligned(16))) float sL[2][2 * BM];     // lse2, then D, of the rows
+    // d = 128: each compute wave's keys' K' (pair-blocked, 32 rows of 32 bytes per block), the B
+    // operand of S, copied once into LDS (held in registers it spills; read from L2 per
+    // sub-tile its latency stalls the S chain)
+    constexpr bool KLDS = D == 128;
+    __shared__ __attribute__((aligned(16))) uint16_t sKw[KLDS ? DkTile<D>::MAXW : 1][KLDS ? NB * 32 * 16 : 8];
     const int tid = threadIdx.x;
     const int w = uniform(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, h = lane >> 5;
@@ -538,9 +543,16 @@ void bwd_dkdv_kernel(BwdParams p, Tables tab, int R) {
             __builtin_amdgcn_global_load_lds(qth + off, (lds_ptr)&sQt[st][i * 512], 16, 0, 0);
             __builtin_amdgcn_global_load_lds(gth + off, (lds_ptr)&sGt[st][i * 512], 16, 0, 0);
         }
-        for (int i = 0; i < BM / 64; ++i) {
-            __builtin_amdgcn_global_load_lds(lse2h + r0 + 64 * i + lane, (lds_ptr)&sL[st][64 * i], 4, 0, 0);
-            __builtin_amdgcn_global_load_lds(Drh + r0 + 64 * i + lane, (lds_ptr)&sL[st][BM + 64 * i], 4, 0, 0);
+        if constexpr (BM >= 64) {
+            for (int i = 0; i < BM / 64; ++i) {
+                __builtin_amdgcn_global_load_lds(lse2h + r0 + 64 * i + lane, (lds_ptr)&sL[st][64 * i], 4, 0, 0);
+                __builtin_amdgcn_global_load_lds(Drh + r0 + 64 * i + lane, (lds_ptr)&sL[st][BM + 64 * i], 4, 0, 0);
+            }
+        } else {
+            // 32 rows: lanes 0-31 bring lse2, lanes 32-63 D, in one load
+            static_assert(BM == 32, "row statistics of a 32-row tile fill one wave load");
+            const float* src = lane < 32 ? lse2h + r0 + lane : Drh + r0 + (lane - 32);
+            __builtin_amdgcn_global_load_lds(src, (lds_ptr)&sL[st][0], 4, 0, 0);
         }
     };
 
@@ -551,6 +563,7 @@ void bwd_dkdv_kernel(BwdParams p, Tables tab, int R) {
     // 13.3 ms for the Qwen2.5-0.5B shape at 32K).
     constexpr bool HOLDK = D == 64;
     u32x4 Kh[HOLDK ? NB : 1];
+    static_assert(HOLDK != KLDS, "K' is held in registers at d = 64 and in LDS at d = 128");
     f32x16 dK[NDB], dV[NDB];
 #pragma unroll
     for (int i = 0; i < NDB; ++i) {
@@ -564,6 +577,17 @@ void bwd_dkdv_kernel(BwdParams p, Tables tab, int R) {
         if (wave_ok) {
 #pragma unroll
             for (int j = 0; j < NB; ++j) Kh[j] = ld16(kkey + (int64_t)j * p.Np * 16);
+        }
+    }
+    if constexpr (KLDS) {
+        // block j's 32 rows are 1 KB of the workspace: one direct load per block, landed before
+        // the tile loop (so no compute wave has a direct load in flight inside it)
+        if (wave_ok) {
+            const uint16_t* k0 = p.ks + (kvh * NB * p.Np + c0) * 16;
+            for (int j = 0; j < NB; ++j)
+                __builtin_amdgcn_global_load_lds(k0 + (int64_t)j * p.Np * 16 + lane * 8,
+                                                 (lds_ptr)&sKw[w][j * 512], 16, 0, 0);
+            __builtin_amdgcn_s_waitcnt(0x0070);
         }
     }
     int plo = 0, pfull = 0;                             // band edges, distances only grow
@@ -583,7 +607,7 @@ void bwd_dkdv_kernel(BwdParams p, Tables tab, int R) {
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
                 if constexpr (HOLDK) Kb[j] = Kh[j];
-                else Kb[j] = ld16(kkey + (int64_t)j * p.Np * 16);
+                else Kb[j] = ld16(&sKw[w][(j * 32 + l32) * 16 + 8 * h]);
                 Vb[j] = ld16(vkey + (int64_t)j * p.Np * 16);
             }
             auto Q = [&](int j) { return ld16(cQ + (j * BM + arow) * 16 + 8 * h); };
