@@ -478,7 +478,8 @@ template <int D>
 struct DkTile {
     static constexpr int BM = D == 64 ? 128 : 32;       // rows per tile (4 BM d 2 + 8 BM bytes a stage)
     static constexpr int NSUB = BM / 32;
-    static constexpr int MAXW = 7;                      // compute waves per workgroup
+    static constexpr int MAXW = D == 64 ? 7 : 5;        // compute waves per workgroup (d = 128: LDS
+                                                        // holds each wave's K' and V)
 };
 
 template <int D>
@@ -495,6 +496,7 @@ void bwd_dkdv_kernel(BwdParams p, Tables tab, int R) {
     // sub-tile its latency stalls the S chain)
     constexpr bool KLDS = D == 128;
     __shared__ __attribute__((aligned(16))) uint16_t sKw[KLDS ? DkTile<D>::MAXW : 1][KLDS ? NB * 32 * 16 : 8];
+    __shared__ __attribute__((aligned(16))) uint16_t sVw[KLDS ? DkTile<D>::MAXW : 1][KLDS ? NB * 32 * 16 : 8];
     const int tid = threadIdx.x;
     const int w = uniform(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, h = lane >> 5;
@@ -584,9 +586,13 @@ void bwd_dkdv_kernel(BwdParams p, Tables tab, int R) {
         // the tile loop (so no compute wave has a direct load in flight inside it)
         if (wave_ok) {
             const uint16_t* k0 = p.ks + (kvh * NB * p.Np + c0) * 16;
-            for (int j = 0; j < NB; ++j)
+            const uint16_t* v0 = p.vb + (kvh * NB * p.Np + c0) * 16;
+            for (int j = 0; j < NB; ++j) {
                 __builtin_amdgcn_global_load_lds(k0 + (int64_t)j * p.Np * 16 + lane * 8,
                                                  (lds_ptr)&sKw[w][j * 512], 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(v0 + (int64_t)j * p.Np * 16 + lane * 8,
+                                                 (lds_ptr)&sVw[w][j * 512], 16, 0, 0);
+            }
             __builtin_amdgcn_s_waitcnt(0x0070);
         }
     }
@@ -606,9 +612,13 @@ void bwd_dkdv_kernel(BwdParams p, Tables tab, int R) {
             u32x4 Kb[NB], Vb[NB];
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
-                if constexpr (HOLDK) Kb[j] = Kh[j];
-                else Kb[j] = ld16(&sKw[w][(j * 32 + l32) * 16 + 8 * h]);
-                Vb[j] = ld16(vkey + (int64_t)j * p.Np * 16);
+                if constexpr (HOLDK) {
+                    Kb[j] = Kh[j];
+                    Vb[j] = ld16(vkey + (int64_t)j * p.Np * 16);
+                } else {
+                    Kb[j] = ld16(&sKw[w][(j * 32 + l32) * 16 + 8 * h]);
+                    Vb[j] = ld16(&sVw[w][(j * 32 + l32) * 16 + 8 * h]);
+                }
             }
             auto Q = [&](int j) { return ld16(cQ + (j * BM + arow) * 16 + 8 * h); };
             auto Gr = [&](int j) { return ld16(cG + (j * BM + arow) * 16 + 8 * h); };
