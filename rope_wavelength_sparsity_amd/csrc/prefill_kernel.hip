@@ -357,6 +357,32 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
         constexpr bool paged = CACHED && PAGED;
         int64_t tile_page = 0;
         if constexpr (paged) tile_page = page_of(p.pg, b, ks);
+        if constexpr (!CACHED) {
+            // One-shot prefill: block j of the tile is KI contiguous 1 KB pieces and V is one
+            // contiguous run of VI pieces, so each copy is a scalar base plus constant offsets
+            // (the per-load address arithmetic ran on the scalar unit every compute wave of the
+            // CU shares).
+            const uint16_t* kb = kpg + ((int64_t)jlo * ldk + ks) * 16 + lane * 8;
+            for (int j = jlo; j < NB; ++j, kb += ldk * 16) {
+#pragma unroll
+                for (int part = 0; part < Tile<D>::KI; ++part)
+                    __builtin_amdgcn_global_load_lds(kb + part * 512,
+                                                     (lds_ptr)&sK2[stage][j * BN * 16 + part * 512], 16, 0, 0);
+            }
+            const uint16_t* vb = vtg + (int64_t)ks * D + lane * 8;
+#pragma unroll
+            for (int r = 0; r < Tile<D>::VI; ++r)
+                __builtin_amdgcn_global_load_lds(vb + r * 512, (lds_ptr)&sV2[stage][r * 512], 16, 0, 0);
+            if constexpr (HASPOS) {
+#pragma unroll
+                for (int pi = 0; pi < Tile<D>::PI; ++pi) {
+                    const int t = ks + 64 * pi + lane;
+                    __builtin_amdgcn_global_load_lds(posb + (t < NK ? t : NK - 1),
+                                                     (lds_ptr)&sPos2[stage][64 * pi], 4, 0, 0);
+                }
+            }
+            return;
+        }
         for (int i = 0; i < nI; ++i) {
             if (i < nK) {
                 // 16-byte chunk `ch` of block j: half (ch & 1) of key ks + ch/2 (past the last
