@@ -52,7 +52,7 @@ namespace wpa {
 
 namespace {
 
-constexpr float kSumTau = 256.0f;  // lazy rescale: a half-row's probabilities may sum to 2^8
+constexpr float kSumTau = 512.0f;  // lazy rescale: a row's probabilities may sum to 2^9
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
@@ -458,20 +458,29 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
 
     // Softmax step and P*V of one sub-tile (keys k0 .. k0+31, `sub` within its tile):
     // probabilities relative to the running max m, packed to bf16 as P*V takes them, and
-    // their sum over this half's 16 keys (two per v_dot2).
-    // m moves only when the probabilities would grow past 2^8: every probability is at most
-    // the half-row sum, so a wave-wide vote on that sum replaces a max over the scores.  The
+    // the row's sum of them over all 32 keys, on every lane of the row.
+    // The sum comes from two 16x16x32 MFMAs that take the packed probabilities as their B
+    // operand unchanged: there lane 32h + l32 holds query l32 % 16 + 16 (l32 / 16) in K
+    // group 2h + l32 / 16, and the constant A operand `rsel` (ones in rows 0 and 8 over K
+    // groups 0 and 2, in rows 4 and 12 over groups 1 and 3, zeros elsewhere) adds both
+    // halves' groups of each query into the output row whose register 0 that query's lanes
+    // hold.  (Eight dependent v_dot2 per sub-tile, half-row sums, were 8% slower in a
+    // model of this loop.)
+    // m moves only when the probabilities would grow past 2^9: every probability is at most
+    // the row sum, so a wave-wide vote on that sum replaces a max over the scores.  The
     // rare sub-tile that fails it (and the first one, which sets m) recomputes its scores
     // and takes the row max.
+    const uint32_t rsel_w = (((lane & 3) == 0) && ((((lane >> 2) ^ (lane >> 4)) & 1) == 0)) ? 0x3f803f80u : 0u;
+    const bf16x8 rsel = __builtin_bit_cast(bf16x8, u32x4{rsel_w, rsel_w, rsel_w, rsel_w});
     auto probs = [&](const f32x16& S, uint32_t (&wd)[8]) -> float {
-        float ps = 0.f;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
+        for (int t = 0; t < 8; ++t)
             wd[t] = pack_bf16x2(__builtin_amdgcn_exp2f(S[2 * t]), __builtin_amdgcn_exp2f(S[2 * t + 1]));
-            ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wd[t]),
-                                                 __builtin_bit_cast(bf16x2, 0x3f803f80u), ps, false);
-        }
-        return ps;
+        f32x4 R = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            rsel, __builtin_bit_cast(bf16x8, u32x4{wd[0], wd[1], wd[2], wd[3]}), f32x4{}, 0, 0, 0);
+        R = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            rsel, __builtin_bit_cast(bf16x8, u32x4{wd[4], wd[5], wd[6], wd[7]}), R, 0, 0, 0);
+        return R[0];
     };
     // scores S (relative to m; absolute before the first sub-tile) -> new m, O and the row
     // sum rescaled, S made relative to the new m
@@ -836,7 +845,7 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
         if (lane == 0 && wave_ok && tot) atomicAdd(p.counter, (unsigned long long)tot);
     }
     if (!wave_ok) return;
-    const float l_tot = sum_with_partner(lsum, xaddr);
+    const float l_tot = lsum;                  // the whole row's sum on both lanes of the row
     if (!row_ok) return;
     if (CACHED && partial) {
         // this split's share: rows with no key in its range hold sum 0 (output 0, log2-sum
