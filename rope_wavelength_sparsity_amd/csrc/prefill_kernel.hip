@@ -23,10 +23,10 @@
 //   forward along the pair axis: they are tracked with running indices, not searched.
 //   Scores are in log2 units (scale*log2 e is folded into Q), and the chain starts from
 //   -m, the running row max, supplied by one more MFMA step, so the MFMA yields the
-//   exponent of exp2 directly.  m only moves when a sub-tile exceeds it by more than 2^8
-//   (a wave-wide vote on per-lane maxima; the row max across lane halves is formed only
+//   exponent of exp2 directly.  m only moves when a sub-tile's probabilities would sum past
+//   2^9 (a wave-wide vote on the row sums; the row max across lane halves is formed only
 //   then), which leaves the result exact.  Then causal mask, exp2, the row sum of the
-//   bf16 probabilities (two per v_dot2) and O^T += V^T P^T on MFMA.
+//   bf16 probabilities (two small MFMAs) and O^T += V^T P^T on MFMA.
 //
 // Register layouts (32x32x16 MFMA: A row m and B column n live in lane m%32 / n%32, the
 // 16-deep contraction is split 8+8 between lane halves; C element (row 8(r/4)+4(l/32)+r%4,
@@ -77,10 +77,6 @@ __device__ inline uint32_t partner32(uint32_t v, int xaddr) {
 
 __device__ inline float max_with_partner(float v, int xaddr) {
     return fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(xaddr, __builtin_bit_cast(int, v))));
-}
-
-__device__ inline float sum_with_partner(float v, int xaddr) {
-    return v + __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(xaddr, __builtin_bit_cast(int, v)));
 }
 
 __device__ inline int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
