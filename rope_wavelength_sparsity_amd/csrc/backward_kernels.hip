@@ -370,16 +370,26 @@ void bwd_dq_kernel(BwdParams p, Tables tab, BwdLaunch L) {
                     if (row - (c0 + idx_of_reg(r, h)) > We) S[r] = 0.f;
             }
             const int jf = pfull >> 3;
-            for (int j = jf; j < NB; ++j) {
+            // unrolled over the blocks with a uniform test each: a block index known at compile
+            // time keeps Qb in place (a run-time index into it became indexed register moves)
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                if (j < jf) continue;
                 const u32x4 qb = j == jf ? (Qb[j] & lead_mask(pfull - 8 * jf)) : Qb[j];
                 S = mfma_h(K(j), qb, S);
             }
-            // P^T, dP^T, dl^T (lane = row; register = key)
+            // P^T, dP^T, dl^T (lane = row; register = key).  Only a sub-tile that crosses the
+            // diagonal needs the causal test; rows past the end hold lse2 = +inf (P = 0).
             f32x16 Pt;
+            if (c0 + 31 > q0) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = c0 + idx_of_reg(r, h);
-                Pt[r] = (key <= row && row_ok) ? __builtin_amdgcn_exp2f(S[r] - lse2) : 0.f;
+                for (int r = 0; r < 16; ++r) {
+                    const int key = c0 + idx_of_reg(r, h);
+                    Pt[r] = key <= row ? __builtin_amdgcn_exp2f(S[r] - lse2) : 0.f;
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) Pt[r] = __builtin_amdgcn_exp2f(S[r] - lse2);
             }
             f32x16 dPt = f32x16{};
 #pragma unroll
@@ -387,17 +397,23 @@ void bwd_dq_kernel(BwdParams p, Tables tab, BwdLaunch L) {
             f32x16 dl;
 #pragma unroll
             for (int r = 0; r < 16; ++r) dl[r] = Pt[r] * (dPt[r] - Dv);
-            // dq'^T += K'^T dl^T over the fully active pairs' dims ...
+            // dq'^T += K'^T dl^T over the fully active pairs' dims (block db holds pairs 16db ..
+            // 16db + 15: only the block holding the band edge has inactive dims to zero) ...
             const u32x4 dlb[2] = {pack8<false>(dl, 0), pack8<false>(dl, 1)};
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                if (2 * db + 1 < jf) continue;          // every dim of this block dead or straddling
-                const bool on = pair_of_x(db, l32) >= pfull;
+                if (16 * db + 15 < pfull) continue;     // every dim of this block dead or straddling
+                if (16 * db >= pfull) {
 #pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    u32x4 a = T(db, s2);
-                    if (!on) a = u32x4{0u, 0u, 0u, 0u};
-                    acc[db] = mfma_h(a, dlb[s2], acc[db]);
+                    for (int s2 = 0; s2 < 2; ++s2) acc[db] = mfma_h(T(db, s2), dlb[s2], acc[db]);
+                } else {
+                    const bool on = pair_of_x(db, l32) >= pfull;
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2) {
+                        u32x4 a = T(db, s2);
+                        if (!on) a = u32x4{0u, 0u, 0u, 0u};
+                        acc[db] = mfma_h(a, dlb[s2], acc[db]);
+                    }
                 }
             }
             // ... and each straddling pair with dl masked to its window
@@ -635,7 +651,10 @@ void bwd_dkdv_kernel(BwdParams p, Tables tab, int R) {
                     if ((r0 + idx_of_reg(r, h)) - key > We) S[r] = 0.f;
             }
             const int jf = pfull >> 3;
-            for (int j = jf; j < NB; ++j) {
+            // unrolled over the blocks with a uniform test each (Kb indexed at compile time)
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                if (j < jf) continue;
                 const u32x4 kb = j == jf ? (Kb[j] & lead_mask(pfull - 8 * jf)) : Kb[j];
                 S = mfma_h(Q(j), kb, S);
             }
@@ -646,11 +665,18 @@ void bwd_dkdv_kernel(BwdParams p, Tables tab, int R) {
             const f32x4 da = d4[0], dbv = d4[1], dc = d4[4], dd = d4[5];
             auto lse_r = [&](int r) { const f32x4& v = r < 4 ? la : (r < 8 ? lb : (r < 12 ? lc : ld)); return v[r & 3]; };
             auto D_r = [&](int r) { const f32x4& v = r < 4 ? da : (r < 8 ? dbv : (r < 12 ? dc : dd)); return v[r & 3]; };
+            // only a sub-tile that crosses the diagonal needs the causal test; rows past the
+            // end hold lse2 = +inf (P = 0)
             f32x16 Pm;
+            if (r0 < c0 + 31) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = r0 + idx_of_reg(r, h);
-                Pm[r] = key <= row ? __builtin_amdgcn_exp2f(S[r] - lse_r(r)) : 0.f;
+                for (int r = 0; r < 16; ++r) {
+                    const int row = r0 + idx_of_reg(r, h);
+                    Pm[r] = key <= row ? __builtin_amdgcn_exp2f(S[r] - lse_r(r)) : 0.f;
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) Pm[r] = __builtin_amdgcn_exp2f(S[r] - lse_r(r));
             }
             // dP = dout V^T (A = dout rows, permuted)
             f32x16 dP = f32x16{};
@@ -677,13 +703,18 @@ void bwd_dkdv_kernel(BwdParams p, Tables tab, int R) {
                     dV[db] = mfma_b(a, pb[s2], dV[db]);
                     dV[db] = mfma_b(a, pl[s2], dV[db]);
                 }
-                if (2 * db + 1 < jf) continue;
-                const bool on = pair_of_x(db, l32) >= pfull;
+                if (16 * db + 15 < pfull) continue;     // every dim dead or straddling
+                if (16 * db >= pfull) {                 // every dim active
 #pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    u32x4 a = QT(db, s2);
-                    if (!on) a = u32x4{0u, 0u, 0u, 0u};
-                    dK[db] = mfma_h(a, dlb[s2], dK[db]);
+                    for (int s2 = 0; s2 < 2; ++s2) dK[db] = mfma_h(QT(db, s2), dlb[s2], dK[db]);
+                } else {
+                    const bool on = pair_of_x(db, l32) >= pfull;
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2) {
+                        u32x4 a = QT(db, s2);
+                        if (!on) a = u32x4{0u, 0u, 0u, 0u};
+                        dK[db] = mfma_h(a, dlb[s2], dK[db]);
+                    }
                 }
             }
             for (int e = plo; e < pfull; ++e) {
