@@ -359,6 +359,11 @@ void bwd_dq_kernel(BwdParams p, Tables tab, BwdLaunch L) {
             auto V = [&](int j) { return ld16(cV + (j * BN + krow) * 16 + 8 * h); };
             // K'^T rows x, keys 16s + 8h .. +7 of the sub-tile: octet 4 sub + 2 s + h
             auto T = [&](int db, int s2) { return ld16(cT + ((4 * sub + 2 * s2 + h) * D + 32 * db + l32) * 8); };
+            // dP^T = V dout^T first: it does not wait on the scores, so its operand reads and
+            // MFMAs overlap the score chain's
+            f32x16 dPt = f32x16{};
+#pragma unroll
+            for (int j = 0; j < NB; ++j) dPt = mfma_b(V(j), Gb[j], dPt);
             // S^T (log2 units): straddling pairs one by one, then the fully active blocks;
             // register r of half h holds key c0 + idx(r); distance = row - key
             f32x16 S = f32x16{};
@@ -391,9 +396,6 @@ void bwd_dq_kernel(BwdParams p, Tables tab, BwdLaunch L) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) Pt[r] = __builtin_amdgcn_exp2f(S[r] - lse2);
             }
-            f32x16 dPt = f32x16{};
-#pragma unroll
-            for (int j = 0; j < NB; ++j) dPt = mfma_b(V(j), Gb[j], dPt);
             f32x16 dl;
 #pragma unroll
             for (int r = 0; r < 16; ++r) dl[r] = Pt[r] * (dPt[r] - Dv);
@@ -641,6 +643,10 @@ void bwd_dkdv_kernel(BwdParams p, Tables tab, int R) {
             // x^T rows x, rows 16s + 8h .. +7 of the sub-tile: octet 4 sub + 2 s + h
             auto QT = [&](int db, int s2) { return ld16(cQt + ((4 * sub + 2 * s2 + h) * D + 32 * db + l32) * 8); };
             auto GT = [&](int db, int s2) { return ld16(cGt + ((4 * sub + 2 * s2 + h) * D + 32 * db + l32) * 8); };
+            // dP = dout V^T (A = dout rows, permuted), first: it does not wait on the scores
+            f32x16 dP = f32x16{};
+#pragma unroll
+            for (int j = 0; j < NB; ++j) dP = mfma_b(Gr(j), Vb[j], dP);
             // S (log2 units): register r of half h holds row r0 + idx(r); distance = row - key
             f32x16 S = f32x16{};
             for (int e = plo; e < pfull; ++e) {
@@ -678,10 +684,6 @@ void bwd_dkdv_kernel(BwdParams p, Tables tab, int R) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) Pm[r] = __builtin_amdgcn_exp2f(S[r] - lse_r(r));
             }
-            // dP = dout V^T (A = dout rows, permuted)
-            f32x16 dP = f32x16{};
-#pragma unroll
-            for (int j = 0; j < NB; ++j) dP = mfma_b(Gr(j), Vb[j], dP);
             f32x16 dl;
 #pragma unroll
             for (int r = 0; r < 16; ++r) dl[r] = Pm[r] * (dP[r] - D_r(r));
