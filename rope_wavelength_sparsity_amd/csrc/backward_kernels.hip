@@ -383,6 +383,13 @@ void bwd_dq_kernel(BwdParams p, Tables tab, BwdLaunch L) {
                 const u32x4 qb = j == jf ? (Qb[j] & lead_mask(pfull - 8 * jf)) : Qb[j];
                 S = mfma_h(K(j), qb, S);
             }
+            // the dq product's K'^T operands of the upper dim blocks (the ones long distances
+            // keep), read before the exponentials so that their latency passes under them
+            u32x4 Tpre[NDB / 2][2];
+#pragma unroll
+            for (int i = 0; i < NDB / 2; ++i)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) Tpre[i][s2] = T(NDB / 2 + i, s2);
             // P^T, dP^T, dl^T (lane = row; register = key).  Only a sub-tile that crosses the
             // diagonal needs the causal test; rows past the end hold lse2 = +inf (P = 0).
             f32x16 Pt;
@@ -405,14 +412,15 @@ void bwd_dq_kernel(BwdParams p, Tables tab, BwdLaunch L) {
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
                 if (16 * db + 15 < pfull) continue;     // every dim of this block dead or straddling
+                auto Top = [&](int s2) { return db >= NDB / 2 ? Tpre[db - NDB / 2][s2] : T(db, s2); };
                 if (16 * db >= pfull) {
 #pragma unroll
-                    for (int s2 = 0; s2 < 2; ++s2) acc[db] = mfma_h(T(db, s2), dlb[s2], acc[db]);
+                    for (int s2 = 0; s2 < 2; ++s2) acc[db] = mfma_h(Top(s2), dlb[s2], acc[db]);
                 } else {
                     const bool on = pair_of_x(db, l32) >= pfull;
 #pragma unroll
                     for (int s2 = 0; s2 < 2; ++s2) {
-                        u32x4 a = T(db, s2);
+                        u32x4 a = Top(s2);
                         if (!on) a = u32x4{0u, 0u, 0u, 0u};
                         acc[db] = mfma_h(a, dlb[s2], acc[db]);
                     }
