@@ -500,29 +500,38 @@ void bwd_dq_kernel(BwdParams p, Tables tab, BwdLaunch L) {
 // and dout^T (by row octets), and the rows' lse and D; the producer wave fills a two-stage
 // ring.  Each compute wave keeps its keys' K' and V as B operands and its dk'^T, dv^T
 // accumulators in registers, and writes them per q head to the workspace.
-template <int D>
+template <int D, int PASS>
 struct DkTile {
-    static constexpr int BM = D == 64 ? 128 : 32;       // rows per tile (4 BM d 2 + 8 BM bytes a stage)
+    // PASS 0: dk and dv in one kernel (d = 64).  d = 128 takes two passes, 1: dv only, 2: dk
+    // only; each carries half the accumulators and half the row tiles' arrays, so more waves
+    // fit in a CU's registers and LDS than the 5 of one combined kernel.
+    static constexpr int BM = D == 64 ? 128 : 32;       // rows per tile
     static constexpr int NSUB = BM / 32;
-    static constexpr int MAXW = D == 64 ? 7 : 5;        // compute waves per workgroup (d = 128: LDS
-                                                        // holds each wave's K' and V)
+    static constexpr int MAXW = D == 64 ? 7 : (PASS == 1 ? 11 : 7);   // compute waves per workgroup
+    static constexpr int WPE = PASS == 1 ? 3 : 2;                      // waves per SIMD to fit
 };
 
-template <int D>
-__global__ __launch_bounds__(64 * (DkTile<D>::MAXW + 1)) __attribute__((amdgpu_waves_per_eu(2)))
+template <int D, int PASS>
+__global__ __launch_bounds__(64 * (DkTile<D, PASS>::MAXW + 1))
+__attribute__((amdgpu_waves_per_eu(DkTile<D, PASS>::WPE)))
 void bwd_dkdv_kernel(BwdParams p, Tables tab, int R) {
-    constexpr int NB = D / 16, NDB = D / 32, P = D / 2, BM = DkTile<D>::BM, NSUB = DkTile<D>::NSUB;
+    constexpr int NB = D / 16, NDB = D / 32, P = D / 2, BM = DkTile<D, PASS>::BM;
+    constexpr int NSUB = DkTile<D, PASS>::NSUB, MAXW = DkTile<D, PASS>::MAXW;
+    constexpr bool DO_DV = PASS != 2, DO_DK = PASS != 1;
+    // the row tiles' arrays a pass reads (one that does not read an array declares a stub)
     __shared__ __attribute__((aligned(16))) uint16_t sQ[2][NB * BM * 16];
-    __shared__ __attribute__((aligned(16))) uint16_t sG[2][NB * BM * 16];
-    __shared__ __attribute__((aligned(16))) uint16_t sQt[2][BM * D];
-    __shared__ __attribute__((aligned(16))) uint16_t sGt[2][BM * D];
+    __shared__ __attribute__((aligned(16))) uint16_t sG[2][DO_DK ? NB * BM * 16 : 8];
+    __shared__ __attribute__((aligned(16))) uint16_t sQt[2][DO_DK ? BM * D : 8];
+    __shared__ __attribute__((aligned(16))) uint16_t sGt[2][DO_DV ? BM * D : 8];
     __shared__ __attribute__((aligned(16))) float sL[2][2 * BM];     // lse2, then D, of the rows
     // d = 128: each compute wave's keys' K' (pair-blocked, 32 rows of 32 bytes per block), the B
     // operand of S, copied once into LDS (held in registers it spills; read from L2 per
-    // sub-tile its latency stalls the S chain)
+    // sub-tile its latency stalls the S chain).  V, the B operand of dP, sits in LDS too when
+    // one kernel does both products, in registers in the dk pass, and is not read by the dv pass.
     constexpr bool KLDS = D == 128;
-    __shared__ __attribute__((aligned(16))) uint16_t sKw[KLDS ? DkTile<D>::MAXW : 1][KLDS ? NB * 32 * 16 : 8];
-    __shared__ __attribute__((aligned(16))) uint16_t sVw[KLDS ? DkTile<D>::MAXW : 1][KLDS ? NB * 32 * 16 : 8];
+    constexpr bool VLDS = D == 128 && PASS == 0, VHOLD = D == 128 && PASS == 2;
+    __shared__ __attribute__((aligned(16))) uint16_t sKw[KLDS ? MAXW : 1][KLDS ? NB * 32 * 16 : 8];
+    __shared__ __attribute__((aligned(16))) uint16_t sVw[VLDS ? MAXW : 1][VLDS ? NB * 32 * 16 : 8];
     const int tid = threadIdx.x;
     const int w = uniform(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, h = lane >> 5;
@@ -564,12 +573,15 @@ void bwd_dkdv_kernel(BwdParams p, Tables tab, int R) {
                 const int64_t off = ((int64_t)j * p.Np + r0 + 32 * part) * 16 + lane * 8;
                 if (j >= jlo)
                     __builtin_amdgcn_global_load_lds(qsh + off, (lds_ptr)&sQ[st][(j * BM + 32 * part) * 16], 16, 0, 0);
-                __builtin_amdgcn_global_load_lds(gbh + off, (lds_ptr)&sG[st][(j * BM + 32 * part) * 16], 16, 0, 0);
+                if constexpr (DO_DK)
+                    __builtin_amdgcn_global_load_lds(gbh + off, (lds_ptr)&sG[st][(j * BM + 32 * part) * 16], 16, 0, 0);
             }
         for (int i = 0; i < BM * D * 2 / 1024; ++i) {
             const int64_t off = r0 * D + (i * 64 + lane) * 8;
-            __builtin_amdgcn_global_load_lds(qth + off, (lds_ptr)&sQt[st][i * 512], 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(gth + off, (lds_ptr)&sGt[st][i * 512], 16, 0, 0);
+            if constexpr (DO_DK)
+                __builtin_amdgcn_global_load_lds(qth + off, (lds_ptr)&sQt[st][i * 512], 16, 0, 0);
+            if constexpr (DO_DV)
+                __builtin_amdgcn_global_load_lds(gth + off, (lds_ptr)&sGt[st][i * 512], 16, 0, 0);
         }
         if constexpr (BM >= 64) {
             for (int i = 0; i < BM / 64; ++i) {
@@ -591,6 +603,7 @@ void bwd_dkdv_kernel(BwdParams p, Tables tab, int R) {
     // 13.3 ms for the Qwen2.5-0.5B shape at 32K).
     constexpr bool HOLDK = D == 64;
     u32x4 Kh[HOLDK ? NB : 1];
+    u32x4 Vh[VHOLD ? NB : 1];
     static_assert(HOLDK != KLDS, "K' is held in registers at d = 64 and in LDS at d = 128");
     f32x16 dK[NDB], dV[NDB];
 #pragma unroll
@@ -607,6 +620,12 @@ void bwd_dkdv_kernel(BwdParams p, Tables tab, int R) {
             for (int j = 0; j < NB; ++j) Kh[j] = ld16(kkey + (int64_t)j * p.Np * 16);
         }
     }
+    if constexpr (VHOLD) {
+        if (wave_ok) {
+#pragma unroll
+            for (int j = 0; j < NB; ++j) Vh[j] = ld16(vkey + (int64_t)j * p.Np * 16);
+        }
+    }
     if constexpr (KLDS) {
         // block j's 32 rows are 1 KB of the workspace: one direct load per block, landed before
         // the tile loop (so no compute wave has a direct load in flight inside it)
@@ -616,8 +635,9 @@ void bwd_dkdv_kernel(BwdParams p, Tables tab, int R) {
             for (int j = 0; j < NB; ++j) {
                 __builtin_amdgcn_global_load_lds(k0 + (int64_t)j * p.Np * 16 + lane * 8,
                                                  (lds_ptr)&sKw[w][j * 512], 16, 0, 0);
-                __builtin_amdgcn_global_load_lds(v0 + (int64_t)j * p.Np * 16 + lane * 8,
-                                                 (lds_ptr)&sVw[w][j * 512], 16, 0, 0);
+                if constexpr (VLDS)
+                    __builtin_amdgcn_global_load_lds(v0 + (int64_t)j * p.Np * 16 + lane * 8,
+                                                     (lds_ptr)&sVw[w][j * 512], 16, 0, 0);
             }
             __builtin_amdgcn_s_waitcnt(0x0070);
         }
@@ -643,7 +663,9 @@ void bwd_dkdv_kernel(BwdParams p, Tables tab, int R) {
                     Vb[j] = ld16(vkey + (int64_t)j * p.Np * 16);
                 } else {
                     Kb[j] = ld16(&sKw[w][(j * 32 + l32) * 16 + 8 * h]);
-                    Vb[j] = ld16(&sVw[w][(j * 32 + l32) * 16 + 8 * h]);
+                    if constexpr (VLDS) Vb[j] = ld16(&sVw[w][(j * 32 + l32) * 16 + 8 * h]);
+                    else if constexpr (VHOLD) Vb[j] = Vh[j];
+                    else Vb[j] = u32x4{0u, 0u, 0u, 0u};       // the dv pass has no dP
                 }
             }
             auto Q = [&](int j) { return ld16(cQ + (j * BM + arow) * 16 + 8 * h); };
@@ -653,8 +675,10 @@ void bwd_dkdv_kernel(BwdParams p, Tables tab, int R) {
             auto GT = [&](int db, int s2) { return ld16(cGt + ((4 * sub + 2 * s2 + h) * D + 32 * db + l32) * 8); };
             // dP = dout V^T (A = dout rows, permuted), first: it does not wait on the scores
             f32x16 dP = f32x16{};
+            if constexpr (DO_DK) {
 #pragma unroll
-            for (int j = 0; j < NB; ++j) dP = mfma_b(Gr(j), Vb[j], dP);
+                for (int j = 0; j < NB; ++j) dP = mfma_b(Gr(j), Vb[j], dP);
+            }
             // S (log2 units): register r of half h holds row r0 + idx(r); distance = row - key
             f32x16 S = f32x16{};
             for (int e = plo; e < pfull; ++e) {
@@ -692,56 +716,65 @@ void bwd_dkdv_kernel(BwdParams p, Tables tab, int R) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) Pm[r] = __builtin_amdgcn_exp2f(S[r] - lse_r(r));
             }
-            f32x16 dl;
+            f32x16 dl = f32x16{};
+            if constexpr (DO_DK) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) dl[r] = Pm[r] * (dP[r] - D_r(r));
+                for (int r = 0; r < 16; ++r) dl[r] = Pm[r] * (dP[r] - D_r(r));
+            }
             // dv^T += dout^T P ; dk'^T += Q'^T dl (fully active pairs' dims, then straddling).
             // P enters the dv product as two bf16 parts, P = hi + lo: a key's dv sums the
             // probabilities of every row of every q head of its kv head (an early key's reaches
             // ~10 and more), where one bf16 rounding of P alone would cost ~2e-2 max-abs.
-            f32x16 Plo;
+            if constexpr (DO_DV) {
+                f32x16 Plo;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) Plo[r] = Pm[r] - round_bf16(Pm[r]);
-            const u32x4 pb[2] = {pack8<true>(Pm, 0), pack8<true>(Pm, 1)};
-            const u32x4 pl[2] = {pack8<true>(Plo, 0), pack8<true>(Plo, 1)};
-            const u32x4 dlb[2] = {pack8<false>(dl, 0), pack8<false>(dl, 1)};
+                for (int r = 0; r < 16; ++r) Plo[r] = Pm[r] - round_bf16(Pm[r]);
+                const u32x4 pb[2] = {pack8<true>(Pm, 0), pack8<true>(Pm, 1)};
+                const u32x4 pl[2] = {pack8<true>(Plo, 0), pack8<true>(Plo, 1)};
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
+                for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    const u32x4 a = GT(db, s2);
-                    dV[db] = mfma_b(a, pb[s2], dV[db]);
-                    dV[db] = mfma_b(a, pl[s2], dV[db]);
+                    for (int s2 = 0; s2 < 2; ++s2) {
+                        const u32x4 a = GT(db, s2);
+                        dV[db] = mfma_b(a, pb[s2], dV[db]);
+                        dV[db] = mfma_b(a, pl[s2], dV[db]);
+                    }
                 }
-                if (16 * db + 15 < pfull) continue;     // every dim dead or straddling
-                if (16 * db >= pfull) {                 // every dim active
+            }
+            if constexpr (DO_DK) {
+                const u32x4 dlb[2] = {pack8<false>(dl, 0), pack8<false>(dl, 1)};
 #pragma unroll
-                    for (int s2 = 0; s2 < 2; ++s2) dK[db] = mfma_h(QT(db, s2), dlb[s2], dK[db]);
-                } else {
-                    const bool on = pair_of_x(db, l32) >= pfull;
+                for (int db = 0; db < NDB; ++db) {
+                    if (16 * db + 15 < pfull) continue;     // every dim dead or straddling
+                    if (16 * db >= pfull) {                 // every dim active
+#pragma unroll
+                        for (int s2 = 0; s2 < 2; ++s2) dK[db] = mfma_h(QT(db, s2), dlb[s2], dK[db]);
+                    } else {
+                        const bool on = pair_of_x(db, l32) >= pfull;
+#pragma unroll
+                        for (int s2 = 0; s2 < 2; ++s2) {
+                            u32x4 a = QT(db, s2);
+                            if (!on) a = u32x4{0u, 0u, 0u, 0u};
+                            dK[db] = mfma_h(a, dlb[s2], dK[db]);
+                        }
+                    }
+                }
+                for (int e = plo; e < pfull; ++e) {
+                    const int We = tab.W[e];
+                    f32x16 m;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        m[r] = ((r0 + idx_of_reg(r, h)) - key <= We) ? dl[r] : 0.f;
+                    const int db = e >> 4;
+                    const bool on = pair_of_x(db, l32) == e;
 #pragma unroll
                     for (int s2 = 0; s2 < 2; ++s2) {
                         u32x4 a = QT(db, s2);
                         if (!on) a = u32x4{0u, 0u, 0u, 0u};
-                        dK[db] = mfma_h(a, dlb[s2], dK[db]);
+#pragma unroll
+                        for (int dd2 = 0; dd2 < NDB; ++dd2)
+                            if (dd2 == db) dK[dd2] = mfma_h(a, pack8<false>(m, s2), dK[dd2]);
                     }
-                }
-            }
-            for (int e = plo; e < pfull; ++e) {
-                const int We = tab.W[e];
-                f32x16 m;
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    m[r] = ((r0 + idx_of_reg(r, h)) - key <= We) ? dl[r] : 0.f;
-                const int db = e >> 4;
-                const bool on = pair_of_x(db, l32) == e;
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    u32x4 a = QT(db, s2);
-                    if (!on) a = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-                    for (int dd2 = 0; dd2 < NDB; ++dd2)
-                        if (dd2 == db) dK[dd2] = mfma_h(a, pack8<false>(m, s2), dK[dd2]);
                 }
             }
         }
@@ -772,8 +805,10 @@ void bwd_dkdv_kernel(BwdParams p, Tables tab, int R) {
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
             const int x = 32 * db + 8 * q4 + 4 * h;
-            *reinterpret_cast<f32x4*>(kp + x) = f32x4{dK[db][4 * q4], dK[db][4 * q4 + 1], dK[db][4 * q4 + 2], dK[db][4 * q4 + 3]};
-            *reinterpret_cast<f32x4*>(vp + x) = f32x4{dV[db][4 * q4], dV[db][4 * q4 + 1], dV[db][4 * q4 + 2], dV[db][4 * q4 + 3]};
+            if constexpr (DO_DK)
+                *reinterpret_cast<f32x4*>(kp + x) = f32x4{dK[db][4 * q4], dK[db][4 * q4 + 1], dK[db][4 * q4 + 2], dK[db][4 * q4 + 3]};
+            if constexpr (DO_DV)
+                *reinterpret_cast<f32x4*>(vp + x) = f32x4{dV[db][4 * q4], dV[db][4 * q4 + 1], dV[db][4 * q4 + 2], dV[db][4 * q4 + 3]};
         }
     }
 }
@@ -836,10 +871,20 @@ hipError_t launch_bwd_d(const BwdParams& p, const Tables& t, hipStream_t s) {
     L.n_rb = (int)((ngroups + L.R - 1) / L.R);
     const dim3 gq((unsigned)((int64_t)L.n_rb * p.B * p.Hkv * L.nhc)), bq(64 * (L.Gc * L.R + 1));
     bwd_dq_kernel<D><<<gq, bq, 0, s>>>(p, t, L);
-    // dk, dv: R key groups of one q head per workgroup (plus the producer wave)
-    const int RK = DkTile<D>::MAXW;
-    const int64_t nkb = (ngroups + RK - 1) / RK;
-    bwd_dkdv_kernel<D><<<dim3((unsigned)(nkb * p.B * p.Hq)), dim3(64 * (RK + 1)), 0, s>>>(p, t, RK);
+    // dk, dv: R key groups of one q head per workgroup (plus the producer wave); at d = 128 a
+    // dv pass, then a dk pass
+    auto dkdv = [&](auto pass) {
+        constexpr int PASS = decltype(pass)::value;
+        const int RK = DkTile<D, PASS>::MAXW;
+        const int64_t nkb = (ngroups + RK - 1) / RK;
+        bwd_dkdv_kernel<D, PASS><<<dim3((unsigned)(nkb * p.B * p.Hq)), dim3(64 * (RK + 1)), 0, s>>>(p, t, RK);
+    };
+    if constexpr (D == 64) {
+        dkdv(std::integral_constant<int, 0>{});
+    } else {
+        dkdv(std::integral_constant<int, 1>{});
+        dkdv(std::integral_constant<int, 2>{});
+    }
     const int64_t nr = (int64_t)p.B * p.Hkv * p.N * (D / 2);
     bwd_reduce_kernel<D><<<dim3((unsigned)((nr + 255) / 256)), blk, 0, s>>>(p, t);
     return hipGetLastError();
