@@ -505,7 +505,7 @@ struct DkTile {
     // PASS 0: dk and dv in one kernel (d = 64).  d = 128 takes two passes, 1: dv only, 2: dk
     // only; each carries half the accumulators and half the row tiles' arrays, so more waves
     // fit in a CU's registers and LDS than the 5 of one combined kernel.
-    static constexpr int BM = D == 64 ? 128 : (PASS == 1 ? 64 : 32);   // rows per tile
+    static constexpr int BM = D == 64 ? 128 : 64;       // rows per tile
     static constexpr int NSUB = BM / 32;
     static constexpr int MAXW = D == 64 ? 7 : (PASS == 1 ? 11 : 7);   // compute waves per workgroup
     static constexpr int WPE = PASS == 1 ? 3 : 2;                      // waves per SIMD to fit
