@@ -256,6 +256,48 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
     auto Qf = [&](int j) -> u32x4 { return u32x4{Qv[4 * j], Qv[4 * j + 1], Qv[4 * j + 2], Qv[4 * j + 3]}; };
     {
         const int64_t qb = ((row0 + qi) * p.Hq + hq) * D;
+        // the row's components as bf16 bits, first components (xw) and second components (yw)
+        // of all pairs, packed two to a word: 16-byte loads issued for every block up front
+        // (per-element loads inside the rotation loop made a chain of dependent round trips,
+        // the fixed cost of every launch)
+        u32x4 xw[NB], yw[NB];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            if constexpr (F32) {
+                float a[8], c[8];
+                // pairs 8j..8j+7: (i, i+P) half-split, (2i, 2i+1) interleaved
+                load8<true>(p.q, p.interleaved ? qb + 16 * j : qb + 8 * j, a);
+                load8<true>(p.q, p.interleaved ? qb + 16 * j + 8 : qb + P + 8 * j, c);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    if (p.interleaved) {
+                        const float* e = t < 2 ? a + 4 * t : c + 4 * (t - 2);
+                        xw[j][t] = f32_to_bf16_bits(e[0]) | ((uint32_t)f32_to_bf16_bits(e[2]) << 16);
+                        yw[j][t] = f32_to_bf16_bits(e[1]) | ((uint32_t)f32_to_bf16_bits(e[3]) << 16);
+                    } else {
+                        xw[j][t] = f32_to_bf16_bits(a[2 * t]) | ((uint32_t)f32_to_bf16_bits(a[2 * t + 1]) << 16);
+                        yw[j][t] = f32_to_bf16_bits(c[2 * t]) | ((uint32_t)f32_to_bf16_bits(c[2 * t + 1]) << 16);
+                    }
+                }
+            } else {
+                const uint16_t* qh = static_cast<const uint16_t*>(p.q);
+                const u32x4 a = *reinterpret_cast<const u32x4*>(qh + (p.interleaved ? qb + 16 * j : qb + 8 * j));
+                const u32x4 c = *reinterpret_cast<const u32x4*>(qh + (p.interleaved ? qb + 16 * j + 8 : qb + P + 8 * j));
+                if (p.interleaved) {
+                    // word t of a (c) holds pair 8j+t (8j+4+t) as (x, y)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const uint32_t lo = t < 2 ? a[2 * t] : c[2 * t - 4];
+                        const uint32_t hi = t < 2 ? a[2 * t + 1] : c[2 * t - 3];
+                        xw[j][t] = (lo & 0xffffu) | (hi << 16);
+                        yw[j][t] = (lo >> 16) | (hi & 0xffff0000u);
+                    }
+                } else {
+                    xw[j] = a;
+                    yw[j] = c;
+                }
+            }
+        }
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
             // pairs 8j..8j+7, one at a time (rolled loop: one sincos instance per block);
@@ -264,17 +306,9 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
             u32x4 acc = {0u, 0u, 0u, 0u};
 #pragma unroll 1
             for (int e = 0; e < 8; ++e) {
-                // the two dims of pair 8j+e: (i, i+P) half-split, (2i, 2i+1) interleaved
-                const int64_t ix = p.interleaved ? qb + 2 * (8 * j + e) : qb + 8 * j + e;
-                const int64_t iy = p.interleaved ? ix + 1 : ix + P;
-                float x, y;
-                if constexpr (F32) {
-                    x = round_bf16(static_cast<const float*>(p.q)[ix]);
-                    y = round_bf16(static_cast<const float*>(p.q)[iy]);
-                } else {
-                    x = bf16_bits_to_f32(static_cast<const uint16_t*>(p.q)[ix]);
-                    y = bf16_bits_to_f32(static_cast<const uint16_t*>(p.q)[iy]);
-                }
+                const int sh = (e & 1) * 16;
+                const float x = bf16_bits_to_f32((sel4(xw[j], e >> 1) >> sh) & 0xffffu);
+                const float y = bf16_bits_to_f32((sel4(yw[j], e >> 1) >> sh) & 0xffffu);
                 float sn, cs;
                 rope_sincos(pq, TH(8 * j + e), &sn, &cs);
                 const float rot = h ? (y * cs + x * sn) : (x * cs - y * sn);
