@@ -162,9 +162,14 @@ size_t wpa_decode_workspace_bytes(int32_t B, int64_t Lmax, int32_t Hq, int32_t H
  *   q_pos    [B] int32 device query positions, or NULL for kv_len-1 (the query's own
  *            token is then the last cached key)
  *   out      [B][Hq][d] (out_dtype);  lse [B][Hq] fp32 or NULL
- *   chunk_keys  keys per split-KV work item: a multiple of 256, or 0 for the library's
- *            choice.  The result depends on it only through rounding (probabilities
- *            enter the P*V product as bf16 relative to each split's running maximum).
+ *   chunk_keys  keys per split-KV work item: a multiple of 256 (item c then takes keys
+ *            c*chunk_keys .. (c+1)*chunk_keys-1), or 0 for the library's choice: as many
+ *            items as ceil(Lmax / C) for a chunk length C it picks, each taking the keys in a
+ *            range of distances from the sequence's last key that streams the same cache
+ *            bytes (near keys read more of K, so their ranges are shorter).  The result
+ *            depends on the split only through rounding (probabilities enter the P*V product
+ *            as bf16 relative to each split's running maximum); calls with the same split
+ *            (the same d, window table, chunk_keys and ceil(Lmax / chunk)) give the same bits.
  *   workspace at least wpa_decode_workspace_bytes(B, Lmax, Hq, Hkv, d, chunk_keys).
  */
 int wpa_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* kv_len,

@@ -54,6 +54,75 @@ __device__ inline float xchg32(float v, int xaddr) {
     return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(xaddr, __builtin_bit_cast(int, v)));
 }
 
+// Byte-balanced split of a sequence's keys (the library's default).  A key at distance x
+// from the sequence's last key streams its V row (2d bytes) and the K blocks still active at
+// that distance, block j while x <= Wb[j], the window of its last pair (32 bytes each).  In
+// units of 32 bytes the keys at distances below x stream
+//     F(x) = x*d/16 + sum_j min(x, Wb[j] + 1),
+// non-decreasing with slope in [d/16, d/8].  Over the span S = n*chunk of the launch's n chunks,
+// chunk c takes the distances [dl_c, dl_{c+1}), dl_c the smallest x with F(x)*n >= c*F(S), i.e.
+// chunks of equal bytes, and as keys the range [K_{c+1}, K_c) with K_0 = L and K_c = max(0,
+// (L - dl_c) rounded down to 32) (tiles start on 32-key boundaries, as ring caches and pages
+// need).  The split depends only on the window table and (n, chunk), so caches of different
+// Lmax with the same chunk grid split alike.  Every chunk spans more than chunk/2 - 1 >= 127
+// distances, so the non-empty chunks of a sequence of L keys are the first
+// 1 + #{c >= 1 : dl_c <= L - 32}.
+template <int NB>
+struct ByteSplit {
+    int64_t wb[NB];
+    int64_t Ftot, n, S;
+    int D;
+    __device__ int64_t F(int64_t x) const {
+        int64_t f = x * (D / 16);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) f += x < wb[j] + 1 ? x : wb[j] + 1;
+        return f;
+    }
+    // dl_c for c in [1, n): the smallest x in [0, S] with F(x)*n >= c*Ftot
+    __device__ int64_t bound(int64_t c) const {
+        int64_t lo = 0, hi = S;
+        const int64_t want = c * Ftot;
+        while (lo < hi) {
+            const int64_t mid = (lo + hi) >> 1;
+            if (F(mid) * n >= want) hi = mid;
+            else lo = mid + 1;
+        }
+        return lo;
+    }
+    // K_c of a sequence of L keys (c in [0, n])
+    __device__ int64_t key_bound(int64_t c, int64_t L) const {
+        if (c == 0) return L;
+        if (c >= n) return 0;
+        const int64_t k = (L - bound(c)) & ~(int64_t)31;
+        return k > 0 ? k : 0;
+    }
+    // number of non-empty chunks of a sequence of L keys
+    __device__ int chunks_used(int64_t L) const {
+        if (L <= 0) return 0;
+        if (L < 32) return 1;
+        const int64_t k = F(L - 32) * n / Ftot;       // #{c >= 1 : dl_c <= L - 32}, before the cap
+        return 1 + (int)(k < n - 1 ? k : n - 1);
+    }
+};
+
+// The split of kv head g: Wb[j] from the shared table or kv head g's frequencies.
+template <int D>
+__device__ inline ByteSplit<D / 16> byte_split(const DecodeParams& p, const Tables& tab, int g) {
+    constexpr int NB = D / 16, P = D / 2;
+    ByteSplit<NB> s;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+        const int w = p.head_theta ? window_from_theta(p.alpha, p.head_theta[(int64_t)g * P + 8 * j + 7])
+                                   : tab.W[8 * j + 7];
+        s.wb[j] = w;
+    }
+    s.D = D;
+    s.n = p.n_chunks;
+    s.S = (int64_t)p.n_chunks * p.chunk;
+    s.Ftot = s.F(s.S);
+    return s;
+}
+
 template <int D, bool PAGED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_partial_kernel(DecodeParams p, Tables tab) {
@@ -74,9 +143,16 @@ void decode_partial_kernel(DecodeParams p, Tables tab) {
     // kv_len is clamped into [0, Lmax] (the caches' or the block table's reach), so no access
     // leaves the caches whatever the device holds; a sequence with no keys writes no partial
     const int Lb = clamp_len(p.kv_len[b], p.Lmax);
-    const int key_lo = chunk * p.chunk;
-    if (key_lo >= Lb) return;
-    const int key_hi = key_lo + p.chunk < Lb ? key_lo + p.chunk : Lb;
+    int key_lo, key_hi;
+    if (p.balanced) {
+        const ByteSplit<NB> bs = byte_split<D>(p, tab, g);
+        key_hi = __builtin_amdgcn_readfirstlane((int)bs.key_bound(chunk, Lb));
+        key_lo = __builtin_amdgcn_readfirstlane((int)bs.key_bound(chunk + 1, Lb));
+    } else {
+        key_lo = chunk * p.chunk;
+        key_hi = key_lo + p.chunk < Lb ? key_lo + p.chunk : Lb;
+    }
+    if (key_lo >= key_hi) return;
     const int64_t qpos = __builtin_amdgcn_readfirstlane(p.q_pos ? p.q_pos[b] : Lb - 1);
     const float sl2 = p.scale * 1.4426950408889634f;
     uint64_t cnt = 0;
@@ -344,7 +420,7 @@ void decode_partial_kernel(DecodeParams p, Tables tab) {
 // out[b][hq] = merge over the chunks c < ceil(kv_len/chunk) of the partials.
 // Block = 256 threads = 8 chunk groups x 32 dims; grid = (B*Hq) x (D/32).
 template <int D>
-__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p, Tables tab) {
     __shared__ float red[256];
     __shared__ float sacc[8][33];
     const int tid = threadIdx.x;
@@ -353,7 +429,8 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
     const int G = p.Hq / p.Hkv;
     const int g = hq / G, hh = hq % G;
     const int64_t Lb = clamp_len(p.kv_len[b], p.Lmax);
-    const int nc = (int)((Lb + p.chunk - 1) / p.chunk);        // <= n_chunks
+    const int nc = p.balanced ? byte_split<D>(p, tab, g).chunks_used(Lb)
+                              : (int)((Lb + p.chunk - 1) / p.chunk);        // <= n_chunks
     if (nc == 0) {
         // no keys (kv_len <= 0): nothing to attend to; out = 0, lse = -inf
         if (tid < 32) {
@@ -414,7 +491,7 @@ hipError_t launch_decode_d(const DecodeParams& p, const Tables& t, hipStream_t s
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     dim3 grid2((unsigned)(p.B * p.Hq), D / 32), block2(256);
-    decode_combine_kernel<D><<<grid2, block2, 0, s>>>(p);
+    decode_combine_kernel<D><<<grid2, block2, 0, s>>>(p, t);
     return hipGetLastError();
 }
 

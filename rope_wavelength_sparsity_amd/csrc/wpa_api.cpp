@@ -814,6 +814,7 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache, const i
     dp.kv_len = kv_len; dp.q_pos = q_pos; dp.out = out; dp.lse = lse; dp.counter = term_count;
     dp.partial = static_cast<float*>(workspace); dp.Lmax = Lmax; dp.B = B; dp.Hq = Hq; dp.Hkv = Hkv;
     dp.d = d; dp.in_f32 = dtype == WPA_FP32; dp.out_f32 = out_dtype == WPA_FP32; dp.chunk = ch; dp.n_chunks = (int)((Lmax + ch - 1) / ch);
+    dp.balanced = chunk_keys == 0;
     dp.scale = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)d));
     dp.pg = pg;
     dp.head_theta = head_tables(rope);

@@ -110,6 +110,8 @@ struct DecodeParams {
     float* partial;               // [B][Hkv][n_chunks][G][d+2]
     int64_t Lmax;
     int32_t B, Hq, Hkv, d, in_f32, out_f32, chunk, n_chunks;
+    int32_t balanced;             // 1: chunks of equal streamed bytes, counted from the last key
+                                  // (n_chunks of them); 0: chunk c = keys [c*chunk, (c+1)*chunk)
     int32_t interleaved;          // pair i = dims (2i, 2i+1) instead of (i, i+d/2)
     float scale;
     Paging pg;                    // pools of pages (table null: kl layout, [B][Hkv][..] V)
