@@ -78,6 +78,33 @@ def test_decode_matches_oracle(shape, alpha):
     assert int(cnt.item()) == kept == expect
 
 
+@pytest.mark.parametrize("alpha", [0.0, 1.0, math.inf])
+def test_decode_split_edges(alpha):
+    """The library's split-KV items take ranges of distance from each sequence's last key
+    that stream equal cache bytes, rounded to 32 keys.  Lengths below, at and just past 32
+    keys, around the 256-key chunk grid and just below Lmax, against the oracle (outputs,
+    LSE, counts), and against the uniform split of explicit chunk_keys (rounding only)."""
+    need_gpu()
+    Lmax, Hq, Hkv, d, base = 2600, 14, 2, 128, 1e4
+    lens_l = [1, 5, 31, 32, 33, 63, 255, 256, 257, 511, 1025, 2047, 2599, 2600]
+    B = len(lens_l)
+    q, k, v, _ = synth.decode_inputs(B, Lmax, Hq, Hkv, d, "bf16", seed=91, len_lo=1)
+    lens = torch.tensor(lens_l, dtype=torch.int32)
+    say("decode split edges", alpha)
+    cache = _cache_from(k, v, base)
+    cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
+    out, lse = wpa.decode(q.cuda(), cache, lens.cuda(), alpha, want_lse=True, term_count=cnt,
+                          out_dtype=torch.float32)
+    uni = wpa.decode(q.cuda(), cache, lens.cuda(), alpha, chunk_keys=256, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ro, rl, kept = oracle.decode(synth.to_oracle(q), synth.to_oracle(k), synth.to_oracle(v),
+                                 lens.numpy(), base, alpha)
+    check_close(out.cpu().numpy(), ro, "decode out")
+    check_close(lse.cpu().numpy(), rl, "decode lse", LSE_MAX, LSE_MAX)
+    assert int(cnt.item()) == kept
+    assert (out.cpu() - uni.cpu()).abs().max() <= 2e-3
+
+
 def test_decode_explicit_query_position():
     need_gpu()
     B, Lmax, Hq, Hkv, d, base = 2, 400, 8, 2, 128, 1e4
