@@ -366,8 +366,8 @@ int wpa_decode_window(const void* q, const void* k_cache, const void* v_cache,
  *                [0, max_pages*page_size] (the table's reach).  Workspace:
  *                wpa_decode_workspace_bytes(B, max_pages*page_size, Hq, Hkv, d, chunk_keys).
  *   wpa_prefill_paged   as wpa_prefill_cached on the pools (Lmax = max_pages * page_size),
- *                bit-identical to it on contiguous caches holding the same tokens; needs
- *                page_size >= 128 (a page holds whole key tiles; WPA_ERR_UNSUPPORTED below).
+ *                bit-identical to it on contiguous caches holding the same tokens, for every
+ *                page_size the pools accept (a 128-key tile spans up to 4 pages of 32).
  */
 size_t wpa_kv_page_bytes(int32_t Hkv, int32_t d, int32_t page_size);
 int wpa_kv_write_paged(const void* k, const void* v, int64_t start, int64_t n, void* k_pool,
@@ -409,7 +409,7 @@ int wpa_prefill_paged_varlen(const void* q, const void* k_pool, const void* v_po
  *   One entry point for the four cached forms:
  *   block_table  NULL: dense caches (k_cache, v_cache, Lmax as for wpa_prefill_cached);
  *                else paged pools (num_pages, page_size as for wpa_prefill_paged, with
- *                Lmax = max_pages * page_size, a multiple of page_size; page_size >= 128).
+ *                Lmax = max_pages * page_size, a multiple of page_size).
  *   cu_q         NULL: Nq queries per sequence (out [B][Nq][Hq][d], lse [B][Hq][Nq]); else the
  *                varlen packing of wpa_prefill_cached_varlen with max_q = Nq.
  *   splits       0: the launch chooses (about two workgroups per compute unit on the current

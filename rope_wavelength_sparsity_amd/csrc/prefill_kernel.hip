@@ -383,10 +383,34 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
         const int jlo = uniform(plo_wg) >> 3;
         const int nK = Tile<D>::KI * (NB - jlo);
         const int nI = nK + Tile<D>::VI + (HASPOS ? Tile<D>::PI : 0);
-        // paged caches: the tile's page (a page holds whole tiles: page_size >= BN)
+        // paged caches: the tile's page when a page holds whole tiles (page_size >= BN), else
+        // the pages of its BN / page_size page slots (at most 4: pages hold >= 32 tokens), read
+        // as scalars before any copy is issued (their loads do not queue behind the copies)
         constexpr bool paged = CACHED && PAGED;
         int64_t tile_page = 0;
-        if constexpr (paged) tile_page = page_of(p.pg, b, ks);
+        int64_t spg[BN / 32] = {};
+        bool small_pages = false;
+        if constexpr (paged) {
+            small_pages = (1 << p.pg.page_log2) < BN;
+            if (!small_pages) {
+                tile_page = page_of(p.pg, b, ks);
+            } else {
+#pragma unroll
+                for (int i = 0; i < BN / 32; ++i) {
+                    const int t = ks + (i << p.pg.page_log2);
+                    spg[i] = (t < ks + BN) ? page_of(p.pg, b, t < NK ? t : NK - 1) : 0;
+                }
+            }
+        }
+        // page of token t of this tile (t in [ks, ks + BN))
+        auto page_at = [&](int t) -> int64_t {
+            if (!small_pages) return tile_page;
+            const int slot = (t - ks) >> p.pg.page_log2;
+            int64_t pg_ = spg[0];
+#pragma unroll
+            for (int i = 1; i < BN / 32; ++i) pg_ = slot == i ? spg[i] : pg_;
+            return pg_;
+        };
         if constexpr (!CACHED) {
             // One-shot prefill: block j of the tile is KI contiguous 1 KB pieces and V is one
             // contiguous run of VI pieces, so each copy is a scalar base plus constant offsets
@@ -425,7 +449,7 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
                     if (t > NK - 1) t = NK - 1;
                     if constexpr (paged) {
                         const int ps = 1 << p.pg.page_log2;
-                        src = p.kp + (((tile_page * p.Hkv + g) * NB + j) * ps + (t & (ps - 1))) * 16 +
+                        src = p.kp + (((page_at(t) * p.Hkv + g) * NB + j) * ps + (t & (ps - 1))) * 16 +
                               (ch & 1) * 8;
                     } else {
                         src = kpg + ((int64_t)j * ldk + t) * 16 + (ch & 1) * 8;
@@ -447,7 +471,7 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
                     if (o > (NK - 1) / 8) o = (NK - 1) / 8;
                     if constexpr (paged) {
                         const int opg = 1 << (p.pg.page_log2 - 3);        // octets per page
-                        src = p.vt + (((tile_page * p.Hkv + g) * opg + (o & (opg - 1))) * D + e) * 8;
+                        src = p.vt + (((page_at(8 * o) * p.Hkv + g) * opg + (o & (opg - 1))) * D + e) * 8;
                     } else {
                         src = vtg + ((int64_t)o * D + e) * 8;
                     }

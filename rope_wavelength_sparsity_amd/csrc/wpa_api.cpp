@@ -1052,8 +1052,6 @@ int wpa_prefill_paged(const void* q, const void* k_pool, const void* v_pool,
     wpa::Paging pg{};
     int rc = check_paging(block_table, num_pages, max_pages, page_size, &pg);
     if (rc) return rc;
-    if (page_size < 128)
-        return fail(WPA_ERR_UNSUPPORTED, "chunked prefill on paged caches needs page_size >= 128 (got %d)", page_size);
     return prefill_cached_impl(q, k_pool, v_pool, kv_len, out, lse, B, Nq,
                                (int64_t)max_pages * page_size, Hq, Hkv, d, base, rope, alpha,
                                scale, dtype, out_dtype, term_count, stream, pg, nullptr);
@@ -1069,8 +1067,6 @@ int wpa_prefill_paged_varlen(const void* q, const void* k_pool, const void* v_po
     wpa::Paging pg{};
     int rc = check_paging(block_table, num_pages, max_pages, page_size, &pg);
     if (rc) return rc;
-    if (page_size < 128)
-        return fail(WPA_ERR_UNSUPPORTED, "chunked prefill on paged caches needs page_size >= 128 (got %d)", page_size);
     if (!cu_q || (reinterpret_cast<uintptr_t>(cu_q) & 3u)) return fail(WPA_ERR_INVALID, "cu_q must be a 4-byte aligned device pointer");
     return prefill_cached_impl(q, k_pool, v_pool, kv_len, out, lse, B, max_q,
                                (int64_t)max_pages * page_size, Hq, Hkv, d, base, rope, alpha,
@@ -1110,8 +1106,6 @@ int wpa_prefill_cached_ex(const void* q, const void* k_cache, const void* v_cach
             return fail(WPA_ERR_INVALID, "Lmax (%lld) must be a multiple of page_size (%d)", (long long)Lmax, page_size);
         int rc = check_paging(block_table, num_pages, (int32_t)(Lmax / page_size), page_size, &pg);
         if (rc) return rc;
-        if (page_size < 128)
-            return fail(WPA_ERR_UNSUPPORTED, "chunked prefill on paged caches needs page_size >= 128 (got %d)", page_size);
     }
     return prefill_cached_impl(q, k_cache, v_cache, kv_len, out, lse, B, Nq, Lmax, Hq, Hkv, d,
                                base, rope, alpha, scale, dtype, out_dtype, term_count, stream, pg,

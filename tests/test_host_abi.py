@@ -188,7 +188,7 @@ def _cached_ex_rc(**kw):
     (dict(splits=4, ws_bytes=3 * 2 * 64 * 8 * 129 * 4), wpa.WPA_ERR_INVALID),   # room for 3
     (dict(ws=ctypes.c_void_p((1 << 20) + 4)), wpa.WPA_ERR_INVALID),      # misaligned workspace
     (dict(cu=ctypes.c_void_p((1 << 20) + 2)), wpa.WPA_ERR_INVALID),      # misaligned cu_q
-    (dict(table=FAKE, npages=16, psize=64), wpa.WPA_ERR_UNSUPPORTED),    # pages below 128
+    (dict(table=FAKE, npages=16, psize=16), wpa.WPA_ERR_INVALID),        # pages below 32
     (dict(table=FAKE, npages=16, psize=384), wpa.WPA_ERR_INVALID),       # not a power of two
     (dict(table=FAKE, npages=16, psize=256, Lmax=4000), wpa.WPA_ERR_INVALID),
     (dict(d=96), wpa.WPA_ERR_UNSUPPORTED),
@@ -427,7 +427,7 @@ def _prefill_paged_rc(**kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(ps=64), wpa.WPA_ERR_UNSUPPORTED),          # a page must hold whole key tiles
+    (dict(ps=16), wpa.WPA_ERR_INVALID),              # a page must hold a 32-key tile
     (dict(ps=96), wpa.WPA_ERR_INVALID),
     (dict(table=None), wpa.WPA_ERR_INVALID),
     (dict(Nq=2000), wpa.WPA_ERR_INVALID),             # more rows than the table reaches
