@@ -375,6 +375,23 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
     // Stream key tile kt into `stage` with direct global->LDS loads (one wave instruction
     // fills 1 KB of LDS: lane l's bytes land at base + size*l).  Only the pair blocks that
     // can be active anywhere in the tile (from the workgroup's smallest distance) are read.
+    // Paged caches: the page-table entries of the next tile to copy, read one tile ahead (a
+    // lookup right before the copies made a dependent round trip per tile).
+    int32_t pgs[BN / 32] = {};
+    auto fetch_pages = [&](int kt) {
+        if constexpr (CACHED && PAGED) {
+            const int ks = kt * BN, lg = p.pg.page_log2;
+            if ((1 << lg) >= BN) {
+                pgs[0] = uniform((int)page_of(p.pg, b, ks));
+            } else {
+#pragma unroll
+                for (int i = 0; i < BN / 32; ++i) {
+                    const int t = ks + (i << lg);
+                    pgs[i] = (t < ks + BN) ? uniform((int)page_of(p.pg, b, t < NK ? t : NK - 1)) : 0;
+                }
+            }
+        }
+    };
     auto issue = [&](int kt, int stage) {
         const int ks = kt * BN;
         const int kend = (ks + BN < NK ? ks + BN : NK) - 1;
@@ -384,31 +401,17 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
         const int nK = Tile<D>::KI * (NB - jlo);
         const int nI = nK + Tile<D>::VI + (HASPOS ? Tile<D>::PI : 0);
         // paged caches: the tile's page when a page holds whole tiles (page_size >= BN), else
-        // the pages of its BN / page_size page slots (at most 4: pages hold >= 32 tokens), read
-        // as scalars before any copy is issued (their loads do not queue behind the copies)
+        // the pages of its BN / page_size page slots (at most 4: pages hold >= 32 tokens),
+        // fetched by the previous call (fetch_pages) while its copies were in flight
         constexpr bool paged = CACHED && PAGED;
-        int64_t tile_page = 0;
-        int64_t spg[BN / 32] = {};
-        bool small_pages = false;
-        if constexpr (paged) {
-            small_pages = (1 << p.pg.page_log2) < BN;
-            if (!small_pages) {
-                tile_page = page_of(p.pg, b, ks);
-            } else {
-#pragma unroll
-                for (int i = 0; i < BN / 32; ++i) {
-                    const int t = ks + (i << p.pg.page_log2);
-                    spg[i] = (t < ks + BN) ? page_of(p.pg, b, t < NK ? t : NK - 1) : 0;
-                }
-            }
-        }
+        const bool small_pages = paged && (1 << p.pg.page_log2) < BN;
         // page of token t of this tile (t in [ks, ks + BN))
         auto page_at = [&](int t) -> int64_t {
-            if (!small_pages) return tile_page;
+            if (!small_pages) return pgs[0];
             const int slot = (t - ks) >> p.pg.page_log2;
-            int64_t pg_ = spg[0];
+            int32_t pg_ = pgs[0];
 #pragma unroll
-            for (int i = 1; i < BN / 32; ++i) pg_ = slot == i ? spg[i] : pg_;
+            for (int i = 1; i < BN / 32; ++i) pg_ = slot == i ? pgs[i] : pg_;
             return pg_;
         };
         if constexpr (!CACHED) {
@@ -507,6 +510,8 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
                     }
                 }
             }
+            // the next tile's pages (tiles go kt_last down to kt_lo)
+            if (kt > kt_lo) fetch_pages(kt - 1);
         }
     };
 
@@ -822,6 +827,7 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
     // otherwise hold every LDS read of a compute wave until such loads land).
     if constexpr (!SPARSE) {
         if (producer) {
+            fetch_pages(kt_last);
             issue(kt_last, 0);
             __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
         }
