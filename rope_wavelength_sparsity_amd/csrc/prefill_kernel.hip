@@ -440,6 +440,44 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
             }
             return;
         }
+        if constexpr (CACHED) {
+            if (ks + BN <= NK) {
+                // a tile with no key past the last: 32-token K pieces and V pieces (one octet, or
+                // half of one at d=128) each lie in one page, so every copy is a scalar base plus
+                // the lane's 16 bytes, as in the one-shot prefill
+                const int lg = p.pg.page_log2, ps = 1 << lg;
+                for (int j = jlo; j < NB; ++j) {
+#pragma unroll
+                    for (int part = 0; part < Tile<D>::KI; ++part) {
+                        const uint16_t* kb;
+                        if constexpr (paged) {
+                            const int64_t pg_ = small_pages ? pgs[(part * 32) >> lg] : pgs[0];
+                            kb = p.kp + (((pg_ * p.Hkv + g) * NB + j) * ps + ((ks + part * 32) & (ps - 1))) * 16;
+                        } else {
+                            kb = kpg + ((int64_t)j * ldk + ks + part * 32) * 16;
+                        }
+                        __builtin_amdgcn_global_load_lds(kb + lane * 8,
+                                                         (lds_ptr)&sK2[stage][j * BN * 16 + part * 512], 16, 0, 0);
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < Tile<D>::VI; ++r) {
+                    const int c = 64 * r / D;                 // the piece's octet in the tile
+                    const uint16_t* vb;
+                    if constexpr (paged) {
+                        const int opg = ps >> 3;
+                        const int64_t pg_ = small_pages ? pgs[(8 * c) >> lg] : pgs[0];
+                        vb = p.vt + (((pg_ * p.Hkv + g) * opg + ((ks / 8 + c) & (opg - 1))) * D) * 8 +
+                             (64 * r - c * D) * 8;
+                    } else {
+                        vb = vtg + (int64_t)(ks / 8) * D * 8 + 64 * r * 8;
+                    }
+                    __builtin_amdgcn_global_load_lds(vb + lane * 8, (lds_ptr)&sV2[stage][r * 512], 16, 0, 0);
+                }
+                if (kt > kt_lo) fetch_pages(kt - 1);
+                return;
+            }
+        }
         for (int i = 0; i < nI; ++i) {
             if (i < nK) {
                 // 16-byte chunk `ch` of block j: half (ch & 1) of key ks + ch/2 (past the last
