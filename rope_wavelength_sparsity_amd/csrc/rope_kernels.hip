@@ -20,13 +20,13 @@
 
 namespace wpa {
 
+// Thread id of the key rotation: one (sequence, kv head, pair block, token).
 template <bool F32>
-__global__ __launch_bounds__(256) void rope_keys_kernel(RopeParams p, Tables tab) {
+__device__ inline void rope_keys_item(const RopeParams& p, const Tables& tab, int64_t id) {
     const int NB = p.d / 16;
     const int P = p.d / 2;
     const int64_t ntok = p.pad_to > p.n ? p.pad_to : p.n;
     const int64_t total = (int64_t)p.B * p.Hkv * NB * ntok;
-    int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (id >= total) return;
     const int64_t t = id % ntok;
     int64_t rest = id / ntok;
@@ -104,6 +104,11 @@ __global__ __launch_bounds__(256) void rope_keys_kernel(RopeParams p, Tables tab
     d4[1] = u32x4{oy[0], oy[1], oy[2], oy[3]};
 }
 
+template <bool F32>
+__global__ __launch_bounds__(256) void rope_keys_kernel(RopeParams p, Tables tab) {
+    rope_keys_item<F32>(p, tab, (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
+}
+
 // V for prefill, by key octets [B][Hkv][ntok/8][d][8] bf16, zero past the last token:
 // one block = 64 tokens (8 octets) x d dims of one (b, kv head), staged through LDS so that
 // both the token-row reads and the octet writes are contiguous.
@@ -152,12 +157,11 @@ __global__ __launch_bounds__(256) void v_octets_kernel(RopeParams p) {
 // handles one (sequence, kv head, octet, 8 dims): an 8x8 transpose in registers; tokens of a
 // partially written octet keep their previous cache contents.
 template <bool F32>
-__global__ __launch_bounds__(256) void v_cache_kernel(RopeParams p) {
+__device__ inline void v_cache_item(const RopeParams& p, int64_t id) {
     const int d8 = p.d / 8;
     const int64_t o_first = p.t0 / 8, o_last = (p.t0 + p.n - 1) / 8;
     const int64_t n_oct = o_last - o_first + 1;
     const int64_t total = (int64_t)p.B * p.Hkv * n_oct * d8;
-    int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (id >= total) return;
     const int e8 = (int)(id % d8) * 8;
     int64_t rest = id / d8;
@@ -207,16 +211,34 @@ __global__ __launch_bounds__(256) void v_cache_kernel(RopeParams p) {
     }
 }
 
+// A cache append in one launch: the first k_blocks workgroups rotate keys, the rest write V
+// (one launch instead of two: the appends of a chunked prefill are small, so the second
+// launch was about half of their cost).
+template <bool F32>
+__global__ __launch_bounds__(256) void kv_cache_kernel(RopeParams p, Tables tab, unsigned k_blocks) {
+    if (blockIdx.x < k_blocks) rope_keys_item<F32>(p, tab, (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
+    else v_cache_item<F32>(p, (int64_t)(blockIdx.x - k_blocks) * blockDim.x + threadIdx.x);
+}
+
 hipError_t launch_rope_relayout(const RopeParams& p, hipStream_t s) {
     const int NB = p.d / 16;
     const int64_t ntok = p.pad_to > p.n ? p.pad_to : p.n;
     const int64_t nk = (int64_t)p.B * p.Hkv * NB * ntok;
     dim3 blk(256);
+    const unsigned kb = (unsigned)((nk + 255) / 256);
+    if (!p.v_prefill) {
+        const int64_t n_oct = (p.t0 + p.n - 1) / 8 - p.t0 / 8 + 1;
+        const int64_t nv = (int64_t)p.B * p.Hkv * n_oct * (p.d / 8);
+        dim3 grid(kb + (unsigned)((nv + 255) / 256));
+        if (p.in_f32) kv_cache_kernel<true><<<grid, blk, 0, s>>>(p, *p.tab, kb);
+        else kv_cache_kernel<false><<<grid, blk, 0, s>>>(p, *p.tab, kb);
+        return hipGetLastError();
+    }
     if (p.in_f32)
-        rope_keys_kernel<true><<<dim3((unsigned)((nk + 255) / 256)), blk, 0, s>>>(p, *p.tab);
+        rope_keys_kernel<true><<<dim3(kb), blk, 0, s>>>(p, *p.tab);
     else
-        rope_keys_kernel<false><<<dim3((unsigned)((nk + 255) / 256)), blk, 0, s>>>(p, *p.tab);
-    if (p.v_prefill) {
+        rope_keys_kernel<false><<<dim3(kb), blk, 0, s>>>(p, *p.tab);
+    {
         const int64_t nt = (ntok + 63) / 64;
         dim3 grid((unsigned)(nt * p.B * p.Hkv));
         if (p.d == 64) {
@@ -226,12 +248,6 @@ hipError_t launch_rope_relayout(const RopeParams& p, hipStream_t s) {
             if (p.in_f32) v_octets_kernel<true, 128><<<grid, blk, 0, s>>>(p);
             else v_octets_kernel<false, 128><<<grid, blk, 0, s>>>(p);
         }
-    } else {
-        const int64_t n_oct = (p.t0 + p.n - 1) / 8 - p.t0 / 8 + 1;
-        const int64_t nv = (int64_t)p.B * p.Hkv * n_oct * (p.d / 8);
-        dim3 grid((unsigned)((nv + 255) / 256));
-        if (p.in_f32) v_cache_kernel<true><<<grid, blk, 0, s>>>(p);
-        else v_cache_kernel<false><<<grid, blk, 0, s>>>(p);
     }
     return hipGetLastError();
 }
