@@ -199,9 +199,11 @@ int wpa_decode(const void* q, const void* k_cache, const void* v_cache, const in
  *             finite, > 0 and non-increasing: a precondition (the values live on the device and
  *             are not checked).  inv_freq must then be NULL and `base` is not used.  Per-head
  *             tables are taken by wpa_prefill_ex / _prepare_ex / _attend_ex, wpa_kv_write_ex,
- *             wpa_kv_write_paged, wpa_decode_ex, wpa_decode_paged and wpa_decode_noalloc; the
- *             other entry points return WPA_ERR_UNSUPPORTED for them, and the host-only count
- *             and threshold queries take one head's table (as inv_freq) at a time.
+ *             wpa_kv_write_paged, wpa_decode_ex, wpa_decode_paged, wpa_decode_noalloc and the
+ *             chunked prefills (wpa_prefill_cached, _varlen, wpa_prefill_paged, _varlen,
+ *             wpa_prefill_cached_ex: the caches written with the same rows); the other entry
+ *             points return WPA_ERR_UNSUPPORTED for them, and the host-only count and threshold
+ *             queries take one head's table (as inv_freq) at a time.
  * Every *_ex entry point below is its namesake with this description added; rope = NULL
  * means {WPA_PAIRS_HALF, NULL, NULL}.  A table that is not positive and non-increasing is
  * WPA_ERR_UNSUPPORTED; an unknown `pairs` value WPA_ERR_INVALID.  The decode caches hold

@@ -730,8 +730,9 @@ def prefill_cached(q, cache, kv_len, alpha: float, *, scale: float | None = None
                    stream=None, block_table=None, cu_q=None, max_q: int | None = None,
                    splits: int = 0, workspace=None):
     """Chunked prefill: q [B][Nq][Hq][d] pre-RoPE holds the last Nq tokens of each sequence,
-    whose keys and values are already in `cache` (a KVCache, or a PagedKVCache with pages of
-    at least 128 tokens and `block_table` [B][max_pages] or the cache's default table);
+    whose keys and values are already in `cache` (a KVCache, or a PagedKVCache with
+    `block_table` [B][max_pages] or the cache's default table; per-kv-head frequency tables
+    as the cache was made with);
     kv_len int32 device [B], each >= Nq.
     Varlen: with cu_q (int32 device [B+1]) q is [rows][Hq][d], sequence b's chunk being rows
     cu_q[b] .. cu_q[b+1]-1 (its last tokens), max_q an upper bound of the per-sequence counts;

@@ -1179,11 +1179,17 @@ hipError_t launch_d(const PrefillParams& p, const Tables& t, hipStream_t s) {
     dim3 grid((unsigned)nblk), block(64 * waves);
     const bool hp = p.pos != nullptr, cn = p.counter != nullptr;
     if (p.kv_len) {
+        // (per-kv-head frequency tables: the HEADS instances, windows computed per workgroup)
+        const bool hd = p.head_theta != nullptr;
         if (p.pg.table) {
-            if (cn) prefill_kernel<D, F32, false, true, true, false, true><<<grid, block, 0, s>>>(p, t, L);
+            if (hd && cn) prefill_kernel<D, F32, false, true, true, false, true, true><<<grid, block, 0, s>>>(p, t, L);
+            else if (hd) prefill_kernel<D, F32, false, false, true, false, true, true><<<grid, block, 0, s>>>(p, t, L);
+            else if (cn) prefill_kernel<D, F32, false, true, true, false, true><<<grid, block, 0, s>>>(p, t, L);
             else prefill_kernel<D, F32, false, false, true, false, true><<<grid, block, 0, s>>>(p, t, L);
         } else {
-            if (cn) prefill_kernel<D, F32, false, true, true, false><<<grid, block, 0, s>>>(p, t, L);
+            if (hd && cn) prefill_kernel<D, F32, false, true, true, false, false, true><<<grid, block, 0, s>>>(p, t, L);
+            else if (hd) prefill_kernel<D, F32, false, false, true, false, false, true><<<grid, block, 0, s>>>(p, t, L);
+            else if (cn) prefill_kernel<D, F32, false, true, true, false><<<grid, block, 0, s>>>(p, t, L);
             else prefill_kernel<D, F32, false, false, true, false><<<grid, block, 0, s>>>(p, t, L);
         }
         if (L.ns > 1) {

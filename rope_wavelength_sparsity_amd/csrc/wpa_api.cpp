@@ -1125,8 +1125,6 @@ int prefill_cached_impl(const void* q, const void* k_cache, const void* v_cache,
                         void* workspace, size_t ws_bytes) {
     int rc = check_common(d, base, rope, alpha);
     if (rc) return rc;
-    rc = no_head_tables(rope, "chunked prefill");
-    if (rc) return rc;
     if (B < 1 || Nq < 1 || Lmax < 1 || Hq < 1 || Hkv < 1) return fail(WPA_ERR_INVALID, "B, Nq, Lmax, Hq, Hkv must be >= 1");
     if (Nq > Lmax) return fail(WPA_ERR_INVALID, "Nq (%d) exceeds Lmax (%lld)", Nq, (long long)Lmax);
     if (Hq % Hkv) return fail(WPA_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
@@ -1151,6 +1149,8 @@ int prefill_cached_impl(const void* q, const void* k_cache, const void* v_cache,
     pp.scale = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)d));
     pp.pg = pg;
     pp.cu_q = cu_q;
+    pp.head_theta = head_tables(rope);
+    pp.alpha = alpha;                  // (per-head tables: windows computed on the device)
     if (splits < 0 || splits > wpa::kMaxKeySplits)
         return fail(WPA_ERR_INVALID, "splits must be in [0, %d] (got %d)", wpa::kMaxKeySplits, splits);
     if (splits != 1 && workspace) {
@@ -1173,7 +1173,8 @@ int prefill_cached_impl(const void* q, const void* k_cache, const void* v_cache,
         if ((rc = dbg_extent(kv_len, (size_t)B * 4, "kv_len")) ||
             (rc = dbg_extent(cu_q, (size_t)(B + 1) * 4, "cu_q")) ||
             (rc = dbg_fetch(kv_len, (size_t)B, &len, stream, "kv_len")) ||
-            (rc = dbg_fetch(cu_q, cu_q ? (size_t)B + 1 : 0, &cu, stream, "cu_q")))
+            (rc = dbg_fetch(cu_q, cu_q ? (size_t)B + 1 : 0, &cu, stream, "cu_q")) ||
+            (rc = dbg_head_tables(rope, Hkv, d, stream)))
             return rc;
         if (cu_q && cu[0] < 0) return fail(WPA_ERR_INVALID, "debug: cu_q[0] = %d is negative", cu[0]);
         std::vector<int64_t> t1(B);

@@ -216,13 +216,51 @@ def test_decode_per_head_tables_match_oracle():
 def test_per_head_tables_unsupported_paths():
     need_gpu()
     rows = _head_rows(2, 64)
-    cache = wpa.KVCache(1, 256, 2, 64, 1e4, inv_freq=rows)
-    q = torch.zeros((1, 32, 4, 64), dtype=torch.bfloat16, device="cuda")
-    with pytest.raises(wpa.WpaError) as e:
-        wpa.prefill_cached(q, cache, torch.full((1,), 64, dtype=torch.int32, device="cuda"), 1.0)
-    assert e.value.code == wpa.WPA_ERR_UNSUPPORTED
     with pytest.raises(ValueError):              # the windowed cache's size query refuses
         wpa.KVCache(1, 256, 2, 64, 1e4, inv_freq=rows, window_alpha=1.0)
+
+
+@pytest.mark.parametrize("d,Hq,Hkv", [(64, 14, 2), (128, 24, 8)])
+def test_chunked_prefill_per_head_tables(d, Hq, Hkv):
+    """Chunked prefill against caches written with a distinct frequency row per kv head: the
+    last 300 tokens of two ragged prompts, automatic key splits on the dense cache, the same on
+    a paged pool of 64-token pages (bit-identical), no splits (rounding only), against the
+    oracle's rows with the same tables (outputs, LSE, counts)."""
+    need_gpu()
+    rows = _head_rows(Hkv, d)
+    B, Nq, page = 2, 300, 64
+    lens_h = [Nq + 500, Nq + 1700]
+    Lmax = 2048
+    q, k, v = synth.prefill_inputs(B, Lmax, Hq, Hkv, d, "bf16", seed=71)
+    max_pages = Lmax // page
+    table = torch.from_numpy(np.random.default_rng(3).permutation(B * max_pages).astype(np.int32)
+                             .reshape(B, max_pages)).cuda()
+    cache = wpa.KVCache(B, Lmax, Hkv, d, 1e4, inv_freq=rows)
+    paged = wpa.PagedKVCache(B * max_pages, page, Hkv, d, 1e4, inv_freq=rows, block_table=table)
+    for b, L in enumerate(lens_h):
+        kk, vv = k[b:b + 1, :L].cuda().contiguous(), v[b:b + 1, :L].cuda().contiguous()
+        cache.write(kk, vv, 0, seq=b)
+        paged.write(kk, vv, 0, block_table=table[b:b + 1])
+    qc = torch.stack([q[b, L - Nq:L] for b, L in enumerate(lens_h)]).contiguous().cuda()
+    kv_len = torch.tensor(lens_h, dtype=torch.int32, device="cuda")
+    say("chunked prefill per-head tables", d)
+    cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
+    od, ld = wpa.prefill_cached(qc, cache, kv_len, 1.0, want_lse=True, term_count=cnt,
+                                out_dtype=torch.float32)
+    op, lp = wpa.prefill_cached(qc, paged, kv_len, 1.0, want_lse=True, out_dtype=torch.float32)
+    o1 = wpa.prefill_cached(qc, cache, kv_len, 1.0, out_dtype=torch.float32, splits=1)
+    torch.cuda.synchronize()
+    assert torch.equal(od, op) and torch.equal(ld, lp), "paged chunk differs from contiguous"
+    assert (od - o1).abs().max() <= 2e-3
+    kept_all = 0
+    for b, L in enumerate(lens_h):
+        ro, rl, kept = oracle.prefill(as_bf16_for_oracle(q[b:b + 1, :L]), as_bf16_for_oracle(k[b:b + 1, :L]),
+                                      as_bf16_for_oracle(v[b:b + 1, :L]), 1e4, 1.0,
+                                      rows=np.arange(L - Nq, L), inv_freq=rows)
+        check_close(od[b:b + 1].cpu().numpy(), ro, "out[%d]" % b)
+        check_close(ld[b:b + 1].cpu().numpy(), rl, "lse[%d]" % b, LSE_MAX, LSE_MAX)
+        kept_all += kept
+    assert int(cnt.item()) == kept_all
 
 
 def test_full_size_llama3b_per_head_tables():
