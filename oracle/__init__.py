@@ -57,7 +57,7 @@ def _load():
         lib.orc_prefill_ex.argtypes = [P, P, P, I, P, I, I64, I, I, I, D, P, I, I, D, D, P, I64, P,
                                        P, P, I]
         lib.orc_prefill_ex.restype = I
-        lib.orc_prefill_sparse.argtypes = [P, P, P, I, I, I64, I, I, I, D, P, I, D, D, P, P, I, I,
+        lib.orc_prefill_sparse.argtypes = [P, P, P, I, I, I64, I, I, I, D, P, I, I, D, D, P, P, I, I,
                                            P, I64, P, P, P, I]
         lib.orc_prefill_sparse.restype = I
         lib.orc_prefill_backward_ex.argtypes = [P, P, P, P, I, P, I, I64, I, I, I, D, P, I, I, D, D,
@@ -238,8 +238,9 @@ def prefill_sparse(q, k, v, base: float, alpha: float, count, idx, blk: int = 64
     out = np.empty((B, R, Hq, d), dtype=np.float64)
     lse = np.empty((B, Hq, R), dtype=np.float64)
     kept = ctypes.c_int64(0)
+    tabs, ntab = _freq_heads(inv_freq, d, Hkv)
     rc = _load().orc_prefill_sparse(_ptr(q), _ptr(k), _ptr(v), dt, B, N, Hq, Hkv, d, float(base),
-                                    _ptr(_freq(inv_freq, d)), LAYOUTS[layout], float(alpha),
+                                    _ptr(tabs), ntab, LAYOUTS[layout], float(alpha),
                                     float(scale), _ptr(count), _ptr(idx), idx.shape[3], blk,
                                     _ptr(rows), R, _ptr(out), _ptr(lse), ctypes.byref(kept),
                                     int(nthreads))

@@ -291,10 +291,11 @@ int orc_prefill(const void* q, const void* k, const void* v, int dtype, const in
  * idx[b][h][R][0 .. max_blocks).  Keys outside the listed blocks leave the softmax
  * altogether; the listed ones get the windowed logits of orc_prefill_ex.
  *   count int32 [B][Hq][nblk], idx int32 [B][Hq][nblk][max_blocks], nblk = ceil(N / blk).
- * Positions are token indices.  Other arguments and outputs as for orc_prefill_ex.
+ * Positions are token indices.  Other arguments (inv_freq with n_tables: one shared table,
+ * or one row per kv head) and outputs as for orc_prefill_ex.
  */
 int orc_prefill_sparse(const void* q, const void* k, const void* v, int dtype, int B, int64_t N,
-                       int Hq, int Hkv, int d, double base, const double* inv_freq,
+                       int Hq, int Hkv, int d, double base, const double* inv_freq, int n_tables,
                        int interleaved, double alpha, double scale, const int32_t* count,
                        const int32_t* idx, int max_blocks, int blk, const int64_t* rows,
                        int64_t n_rows, double* out, double* lse, int64_t* kept_out,
@@ -302,6 +303,7 @@ int orc_prefill_sparse(const void* q, const void* k, const void* v, int dtype, i
     if (B < 1 || N < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || d < 2 || d % 2 != 0 || blk < 1 ||
         max_blocks < 0 || !count || (max_blocks > 0 && !idx))
         return -1;
+    if (n_tables > 1 && (n_tables != Hkv || !inv_freq)) return -1;
     if (!rows) n_rows = N;
 #ifdef _OPENMP
     if (nthreads > 0) omp_set_num_threads(nthreads);
@@ -309,8 +311,7 @@ int orc_prefill_sparse(const void* q, const void* k, const void* v, int dtype, i
     int G = Hq / Hkv, P = d / 2;
     int esz = dtype == ORC_FP32 ? 4 : 2;
     int64_t nblk = (N + blk - 1) / blk;
-    double* thr = (double*)malloc(sizeof(double) * P);
-    orc_thresholds_ex(d, base, inv_freq, alpha, thr);
+    double* thr = orc_head_thresholds(d, base, inv_freq, n_tables, Hkv, alpha);
     int64_t* p64 = (int64_t*)malloc(sizeof(int64_t) * N);
     for (int64_t t = 0; t < N; ++t) p64[t] = t;
     double* kr = (double*)malloc(sizeof(double) * N * Hkv * d);
@@ -318,8 +319,8 @@ int orc_prefill_sparse(const void* q, const void* k, const void* v, int dtype, i
     int64_t* qp = (int64_t*)malloc(sizeof(int64_t) * n_rows);
     int64_t kept_total = 0;
     for (int b = 0; b < B; ++b) {
-        orc_rope_ex((const char*)k + (size_t)esz * b * N * Hkv * d, dtype, N, Hkv, d, p64, base,
-                    inv_freq, interleaved, kr);
+        orc_rotate((const char*)k + (size_t)esz * b * N * Hkv * d, dtype, N, Hkv, d, p64, base,
+                   inv_freq, n_tables, interleaved, kr);
         const char* qb = (const char*)q + (size_t)esz * b * N * Hq * d;
         char* qsel = (char*)malloc((size_t)esz * n_rows * Hq * d);
         for (int64_t j = 0; j < n_rows; ++j) {
@@ -327,7 +328,7 @@ int orc_prefill_sparse(const void* q, const void* k, const void* v, int dtype, i
             memcpy(qsel + (size_t)esz * j * Hq * d, qb + (size_t)esz * r * Hq * d, (size_t)esz * Hq * d);
             qp[j] = r;
         }
-        orc_rope_ex(qsel, dtype, n_rows, Hq, d, qp, base, inv_freq, interleaved, qr);
+        orc_rotate(qsel, dtype, n_rows, Hq, d, qp, base, inv_freq, n_tables, interleaved, qr);
         free(qsel);
         const char* vb = (const char*)v + (size_t)esz * b * N * Hkv * d;
         int64_t kept_b = 0;
@@ -352,7 +353,8 @@ int orc_prefill_sparse(const void* q, const void* k, const void* v, int dtype, i
                     double* o = out + (((int64_t)b * n_rows + j) * Hq + h) * d;
                     double* l = lse + ((int64_t)b * Hq + h) * n_rows + j;
                     kept_b += orc_row(qr + (j * Hq + h) * (int64_t)d, qp[j], kr, p64, vb, dtype,
-                                      r, Hkv, h / G, d, interleaved, thr, scale, logit, o, l, vis);
+                                      r, Hkv, h / G, d, interleaved, thr + (int64_t)(h / G) * P,
+                                      scale, logit, o, l, vis);
                 }
             }
             free(logit);

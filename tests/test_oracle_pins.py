@@ -399,9 +399,10 @@ def test_full_window_variant_equals_library_sdpa(layout):
     assert kept == B * Hq * (d // 2) * N * (N + 1) // 2
 
 
-def _relative_form_table(q, k, v, qpos, kpos, theta, layout, alpha, scale):
+def _relative_form_table(q, k, v, qpos, kpos, theta, layout, alpha, scale, visible=None):
     """The relative complex form with a frequency table: Term_i = Re(zq_i conj(zk_i)
-    exp(1j*(tq - tk)*theta_i)), kept iff |tq - tk| <= alpha*2*pi/theta_i."""
+    exp(1j*(tq - tk)*theta_i)), kept iff |tq - tk| <= alpha*2*pi/theta_i; an optional boolean
+    visible [Nq][Nk] removes keys from the softmax."""
     dx, dy = _dims(q.shape[-1], layout)
     zq = q[:, dx] + 1j * q[:, dy]
     zk = k[:, dx] + 1j * k[:, dy]
@@ -410,7 +411,10 @@ def _relative_form_table(q, k, v, qpos, kpos, theta, layout, alpha, scale):
     keep = np.abs(dt)[..., None] <= alpha * (2.0 * np.pi / theta)
     logits = scale * np.where(keep, terms, 0.0).sum(-1)
     Nq, Nk = logits.shape
-    logits = np.where(np.arange(Nk)[None, :] <= np.arange(Nq)[:, None], logits, -np.inf)
+    causal = np.arange(Nk)[None, :] <= np.arange(Nq)[:, None]
+    if visible is not None:
+        causal = causal & visible
+    logits = np.where(causal, logits, -np.inf)
     return scipy.special.softmax(logits, axis=-1) @ v, scipy.special.logsumexp(logits, axis=-1)
 
 
@@ -580,6 +584,57 @@ def test_per_head_tables_all_equal_is_shared_table():
     np.testing.assert_array_equal(shared[0], heads[0])
     np.testing.assert_array_equal(shared[1], heads[1])
     assert shared[2] == heads[2]
+
+
+@pytest.mark.parametrize("alpha", [0.5, 1.0, math.inf])
+def test_block_sparse_per_head_tables_equal_relative_form_with_mask(alpha):
+    """Block sparsity with one frequency row per kv head: each q head against the relative
+    complex form with its kv head's row and the list mask written from the rule; the kept
+    count as a tally over visible pairs with each head's windows."""
+    B, N, Hq, Hkv, d, blk = 2, 45, 4, 2, 16, 8
+    q, k, v = synth.prefill_inputs(B, N, Hq, Hkv, d, "fp32", seed=91)
+    tabs = _head_tables(Hkv, d, 92)
+    nblk = (N + blk - 1) // blk
+    count, idx = _random_lists(B, Hq, nblk, 4, seed=93)
+    out, lse, kept = oracle.prefill_sparse(synth.to_oracle(q), synth.to_oracle(k),
+                                           synth.to_oracle(v), 1e4, alpha, count, idx, blk=blk,
+                                           inv_freq=tabs)
+    vis = _visible(N, blk, count, idx)
+    pos = np.arange(N)
+    G = Hq // Hkv
+    tally = 0
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            ro, rl = _relative_form_table(_f64(q[b, :, h]), _f64(k[b, :, g]), _f64(v[b, :, g]), pos,
+                                          pos, tabs[g], "half", alpha, 1.0 / math.sqrt(d),
+                                          visible=vis[b, h])
+            np.testing.assert_allclose(out[b, :, h], ro, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(lse[b, h], rl, rtol=0, atol=1e-12)
+            dist = pos[:, None] - pos[None, :]
+            lam = 2.0 * np.pi / tabs[g]
+            tally += int(((np.abs(dist)[..., None] <= alpha * lam) & vis[b, h][..., None]).sum())
+    assert kept == tally
+
+
+def test_block_sparse_per_head_tables_every_block_is_dense():
+    """With every block listed, per-head block sparsity is the per-head causal prefill, bit for
+    bit; with all rows equal it is the shared-table block sparsity, bit for bit."""
+    B, N, Hq, Hkv, d, blk = 1, 70, 4, 2, 32, 16
+    q, k, v = synth.prefill_inputs(B, N, Hq, Hkv, d, "bf16", seed=94)
+    a = [synth.to_oracle(t) for t in (q, k, v)]
+    tabs = _head_tables(Hkv, d, 95)
+    nblk = (N + blk - 1) // blk
+    count = np.full((B, Hq, nblk), nblk, np.int32)
+    idx = np.broadcast_to(np.arange(nblk, dtype=np.int32), (B, Hq, nblk, nblk)).copy()
+    o1, l1, k1 = oracle.prefill(*a, 1e4, 1.0, inv_freq=tabs)
+    o2, l2, k2 = oracle.prefill_sparse(*a, 1e4, 1.0, count, idx, blk=blk, inv_freq=tabs)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2) and k1 == k2
+    c2, i2 = _random_lists(B, Hq, nblk, 3, seed=96)
+    eq = np.stack([tabs[0], tabs[0]])
+    s1 = oracle.prefill_sparse(*a, 1e4, 1.0, c2, i2, blk=blk, inv_freq=tabs[0])
+    s2 = oracle.prefill_sparse(*a, 1e4, 1.0, c2, i2, blk=blk, inv_freq=eq)
+    assert np.array_equal(s1[0], s2[0]) and np.array_equal(s1[1], s2[1]) and s1[2] == s2[2]
 
 
 def test_per_head_tables_count_and_decode():
