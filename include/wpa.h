@@ -201,8 +201,8 @@ int wpa_decode(const void* q, const void* k_cache, const void* v_cache, const in
  *             tables are taken by wpa_prefill_ex / _prepare_ex / _attend_ex, wpa_kv_write_ex,
  *             wpa_kv_write_paged, wpa_decode_ex, wpa_decode_paged, wpa_decode_noalloc and the
  *             chunked prefills (wpa_prefill_cached, _varlen, wpa_prefill_paged, _varlen,
- *             wpa_prefill_cached_ex: the caches written with the same rows); the other entry
- *             points return WPA_ERR_UNSUPPORTED for them, and the host-only count and threshold
+ *             wpa_prefill_cached_ex: the caches written with the same rows) and
+ *             wpa_prefill_sparse; the other entry points return WPA_ERR_UNSUPPORTED for them, and the host-only count and threshold
  *             queries take one head's table (as inv_freq) at a time.
  * Every *_ex entry point below is its namesake with this description added; rope = NULL
  * means {WPA_PAIRS_HALF, NULL, NULL}.  A table that is not positive and non-increasing is

@@ -1078,9 +1078,12 @@ size_t sparse_bitmap_bytes(int64_t N) {
 template <int D, bool F32>
 hipError_t sparse_lds_d(const PrefillParams& p, size_t* need, size_t* limit) {
     hipFuncAttributes attr;
+    const bool hd = p.head_theta != nullptr;
     hipError_t e = p.counter
-        ? hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&prefill_kernel<D, F32, false, true, false, true>))
-        : hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&prefill_kernel<D, F32, false, false, false, true>));
+        ? (hd ? hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&prefill_kernel<D, F32, false, true, false, true, false, true>))
+              : hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&prefill_kernel<D, F32, false, true, false, true>)))
+        : (hd ? hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&prefill_kernel<D, F32, false, false, false, true, false, true>))
+              : hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&prefill_kernel<D, F32, false, false, false, true>)));
     if (e != hipSuccess) return e;
     int dev = 0, lim = 0;
     e = hipGetDevice(&dev);
@@ -1202,7 +1205,10 @@ hipError_t launch_d(const PrefillParams& p, const Tables& t, hipStream_t s) {
         // block bitmaps: one per compute wave and their union (the caller has checked that
         // they fit next to the kernel's static LDS: sparse_lds)
         const size_t bits = sparse_bitmap_bytes<D>(p.N);
-        if (cn) prefill_kernel<D, F32, false, true, false, true><<<grid, block, bits, s>>>(p, t, L);
+        const bool hd = p.head_theta != nullptr;        // per-kv-head frequency tables
+        if (hd && cn) prefill_kernel<D, F32, false, true, false, true, false, true><<<grid, block, bits, s>>>(p, t, L);
+        else if (hd) prefill_kernel<D, F32, false, false, false, true, false, true><<<grid, block, bits, s>>>(p, t, L);
+        else if (cn) prefill_kernel<D, F32, false, true, false, true><<<grid, block, bits, s>>>(p, t, L);
         else prefill_kernel<D, F32, false, false, false, true><<<grid, block, bits, s>>>(p, t, L);
     } else if (p.head_theta) {
         // per-head rotation frequencies (one-shot prefill only)

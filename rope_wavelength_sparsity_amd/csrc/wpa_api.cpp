@@ -583,8 +583,6 @@ int wpa_prefill_sparse(const void* q, const void* k, const void* v, void* out, f
     if (rc) return rc;
     if (B < 1 || N < 1 || Hq < 1 || Hkv < 1) return fail(WPA_ERR_INVALID, "B, N, Hq, Hkv must be >= 1");
     if (Hq % Hkv) return fail(WPA_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
-    rc = no_head_tables(rope, "wpa_prefill_sparse");
-    if (rc) return rc;
     if (N > ((int64_t)1 << 21)) return fail(WPA_ERR_UNSUPPORTED, "block-sparse prefill supports N up to 2^21 tokens");
     if (!blk_count || (blk_max > 0 && !blk_idx) || blk_max < 0)
         return fail(WPA_ERR_INVALID, "block lists: need blk_count, blk_max >= 0 and blk_idx when blk_max > 0");
@@ -604,6 +602,7 @@ int wpa_prefill_sparse(const void* q, const void* k, const void* v, void* out, f
         // anything is enqueued (at d = 128 this bounds N below 2^21)
         wpa::PrefillParams pp{};
         pp.d = d; pp.in_f32 = dtype == WPA_FP32; pp.N = N; pp.counter = term_count;
+        pp.head_theta = head_tables(rope);
         size_t need = 0, limit = 0;
         hipError_t e = wpa::prefill_sparse_lds(pp, &need, &limit);
         if (e != hipSuccess) return fail(WPA_ERR_HIP, "block-sparse LDS query: %s", hipGetErrorString(e));

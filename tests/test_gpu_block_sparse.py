@@ -70,6 +70,36 @@ def test_block_sparse_matches_oracle(shape, alpha):
     assert cnt == kept
 
 
+@pytest.mark.parametrize("shape", [(1, 700, 14, 2, 64), (2, 650, 24, 8, 128)])
+def test_block_sparse_per_head_tables_match_oracle(shape):
+    """Block sparsity with one frequency row per kv head (different bases, Llama-3 scaling on
+    odd heads): outputs, LSE and counts against the oracle with the same rows."""
+    need_gpu()
+    B, N, Hq, Hkv, d = shape
+    rows = []
+    for g in range(Hkv):
+        t = wpa.default_inv_freq(d, (1e4, 5e5, 1e6, 1e7)[g % 4])
+        if g % 2:
+            t = wpa.llama3_inv_freq(d, (1e4, 5e5, 1e6, 1e7)[g % 4], factor=8.0 * (g + 1),
+                                    low_freq_factor=1.0, high_freq_factor=4.0,
+                                    original_max_position=4096)
+        rows.append(t)
+    rows = np.stack(rows)
+    q, k, v = synth.prefill_inputs(B, N, Hq, Hkv, d, "bf16", seed=97 + d)
+    count, idx = _lists(B, Hq, N, 0.3, seed=98)
+    say("block sparse per-head tables", shape)
+    cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
+    out, lse = wpa.prefill(q.cuda(), k.cuda(), v.cuda(), 1e4, 1.0, want_lse=True, term_count=cnt,
+                           out_dtype=torch.float32, block_count=torch.from_numpy(count).cuda(),
+                           block_idx=torch.from_numpy(idx).cuda(), inv_freq=rows)
+    torch.cuda.synchronize()
+    ro, rl, kept = oracle.prefill_sparse(exact(q), exact(k), exact(v), 1e4, 1.0, count, idx,
+                                         inv_freq=rows)
+    check_close(out.cpu().numpy(), ro, "out")
+    check_close(lse.cpu().numpy(), rl, "lse", LSE_MAX, LSE_MAX)
+    assert int(cnt.item()) == kept
+
+
 def test_block_sparse_lists_with_junk_and_truncation():
     """Duplicates, entries at or past the query block, -1, and lists longer than the
     width (truncated by count) are absorbed as the rule says."""
