@@ -528,6 +528,54 @@ def test_block_sparse_with_every_block_is_dense():
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2) and k1 == k2
 
 
+def _expand_lists(count, idx, f, N, fine):
+    """Lists over blocks of f*fine tokens as lists over blocks of `fine`: each listed coarse
+    block becomes its f fine blocks, and each fine query block also lists the earlier fine
+    blocks of its own coarse block."""
+    B, H, nc = count.shape
+    nf = (N + fine - 1) // fine
+    cf = np.zeros((B, H, nf), np.int32)
+    rows = [[[[] for _ in range(nf)] for _ in range(H)] for _ in range(B)]
+    for b in range(B):
+        for h in range(H):
+            for Rf in range(nf):
+                R = Rf // f
+                got = [int(x) for x in idx[b, h, R, :max(0, min(int(count[b, h, R]), idx.shape[3]))]]
+                lst = [c * f + j for c in got if 0 <= c < R for j in range(f)]
+                lst += list(range(R * f, Rf))
+                rows[b][h][Rf] = lst
+                cf[b, h, Rf] = len(lst)
+    m = max(1, int(cf.max()))
+    xf = np.zeros((B, H, nf, m), np.int32)
+    for b in range(B):
+        for h in range(H):
+            for Rf in range(nf):
+                xf[b, h, Rf, :cf[b, h, Rf]] = rows[b][h][Rf]
+    return cf, xf
+
+
+@pytest.mark.parametrize("f", [2, 4])
+def test_block_sparse_coarse_blocks_equal_expanded_fine_lists(f):
+    """A list over blocks of f*8 tokens is the same attention as the list of their 8-token
+    blocks (plus the earlier 8-token blocks of the row's own coarse block), bit for bit."""
+    B, N, Hq, Hkv, d, base, fine = 1, 77, 2, 1, 16, 100.0, 8
+    q, k, v = synth.prefill_inputs(B, N, Hq, Hkv, d, "bf16", seed=85)
+    a = [synth.to_oracle(t) for t in (q, k, v)]
+    nc = (N + f * fine - 1) // (f * fine)
+    count, idx = _random_lists(B, Hq, nc, 3, seed=86)
+    cf, xf = _expand_lists(count, idx, f, N, fine)
+    o1, l1, k1 = oracle.prefill_sparse(*a, base, 1.0, count, idx, blk=f * fine)
+    o2, l2, k2 = oracle.prefill_sparse(*a, base, 1.0, cf, xf, blk=fine)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2) and k1 == k2
+    # dropping one coarse block's expansion changes the result (the pin sees the lists)
+    R = next(R for R in range(nc) for e in range(min(int(count[0, 0, R]), 3))
+             if 0 <= idx[0, 0, R, e] < R)
+    cf2 = cf.copy()
+    cf2[0, 0, R * f:(R + 1) * f] = 0
+    o4, _, _ = oracle.prefill_sparse(*a, base, 1.0, cf2, xf, blk=fine)
+    assert not np.array_equal(o1, o4)
+
+
 def test_block_sparse_empty_lists_are_block_local():
     """With no listed blocks every row sees only its own block: the same rows as a plain
     prefill of that block alone (positions shifted, which RoPE attention does not see)."""
