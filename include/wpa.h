@@ -308,6 +308,22 @@ int wpa_prefill_sparse(const void* q, const void* k, const void* v, void* out, f
                        size_t ws_bytes, void* stream);
 
 /*
+ * wpa_prefill_sparse with another block size (the token-level methods the window is composed
+ * with index blocks of their own size; ATFlash abstract, as above).  Tokens form blocks of
+ * `block` tokens, a power of two from 64 to 1024 (else WPA_ERR_INVALID); the rule, the lists and
+ * every other argument are as above with 64 replaced by `block`:
+ *   blk_count  int32 device [B][Hq][ceil(N/block)];  blk_idx [B][Hq][ceil(N/block)][blk_max]
+ * The same LDS bound on N applies (the lists are held at 64-token granularity).
+ * wpa_prefill_sparse is this call with block = 64.
+ */
+int wpa_prefill_sparse_ex(const void* q, const void* k, const void* v, void* out, float* lse,
+                          const int32_t* blk_count, const int32_t* blk_idx, int32_t blk_max,
+                          int32_t block, int32_t B, int64_t N, int32_t Hq, int32_t Hkv, int32_t d,
+                          double base, const wpa_rope_t* rope, double alpha, float scale,
+                          int32_t dtype, int32_t out_dtype, unsigned long long* term_count,
+                          void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * Windowed decode cache (K-dim eviction).  In decode the query is the newest token, so the
  * distance to a given key only grows: once it exceeds the window of every pair of a 16-dim
  * pair block, that block of that key is never read again (WavePrune original abstract:

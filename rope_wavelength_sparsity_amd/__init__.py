@@ -45,7 +45,7 @@ EXPORTS = ("wpa_count_terms", "wpa_thresholds", "wpa_prefill_workspace_bytes", "
            "wpa_prefill_cached_varlen", "wpa_prefill_paged_varlen", "wpa_decode_noalloc",
            "wpa_prefill_backward_workspace_bytes", "wpa_prefill_backward",
            "wpa_prefill_cached_workspace_bytes", "wpa_prefill_cached_ex", "wpa_set_debug",
-           "wpa_last_error")
+           "wpa_last_error", "wpa_prefill_sparse_ex")
 
 
 class Rope(ctypes.Structure):
@@ -187,6 +187,9 @@ def lib():
     L.wpa_prefill_sparse.argtypes = [P, P, P, P, P, P, P, I32, I32, I64, I32, I32, I32, D, P, D, F,
                                      I32, I32, P, P, SZ, P]
     L.wpa_prefill_sparse.restype = ctypes.c_int
+    L.wpa_prefill_sparse_ex.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I64, I32, I32, I32, D,
+                                        P, D, F, I32, I32, P, P, SZ, P]
+    L.wpa_prefill_sparse_ex.restype = ctypes.c_int
     L.wpa_kv_page_bytes.argtypes = [I32, I32, I32]
     L.wpa_kv_page_bytes.restype = SZ
     L.wpa_kv_write_paged.argtypes = [P, P, I64, I64, P, P, P, I32, I32, I32, I32, I32, I32, D, P,
@@ -370,12 +373,12 @@ def decode_workspace_bytes(B, Lmax, Hq, Hkv, d, chunk_keys=0) -> int:
 def prefill(q, k, v, base: float, alpha: float, *, scale: float | None = None, positions=None,
             out=None, out_dtype=None, lse=None, want_lse: bool = False, term_count=None,
             workspace=None, stream=None, inv_freq=None, pairs: str = "half", block_count=None,
-            block_idx=None):
+            block_idx=None, block: int = 64):
     """Causal windowed prefill.  q [B][N][Hq][d], k/v [B][N][Hkv][d] (bf16 or fp32, pre-RoPE).
 
-    block_count / block_idx (int32 device [B][Hq][ceil(N/64)] and [...][max]): token-level
-    block sparsity on top of the window; each 64-row query block attends its own block and
-    the ascending list of 64-key blocks given for it.
+    block_count / block_idx (int32 device [B][Hq][ceil(N/block)] and [...][max]): token-level
+    block sparsity on top of the window; each query block of `block` rows (a power of two,
+    64 .. 1024) attends its own block and the key blocks listed for it.
 
     Returns out [B][N][Hq][d] (out_dtype, default q's dtype), or (out, lse [B][Hq][N] fp32)
     when want_lse or an lse buffer is passed.  term_count: optional int64 device tensor of
@@ -398,8 +401,11 @@ def prefill(q, k, v, base: float, alpha: float, *, scale: float | None = None, p
     workspace = _workspace(workspace, prefill_workspace_bytes(B, N, Hkv, d), q)
     rope, keep = _rope(d, inv_freq, pairs, Hkv, q.device)
     if block_count is not None:
-        # token-level block sparsity on top of the window (blocks of 64 tokens)
-        nblk = (N + 63) // 64
+        # token-level block sparsity on top of the window (blocks of `block` tokens)
+        block = int(block)
+        if block < 64 or block > 1024 or block & (block - 1):
+            raise ValueError("block must be a power of two from 64 to 1024")
+        nblk = (N + block - 1) // block
         if positions is not None:
             raise ValueError("block-sparse prefill uses token indices as positions")
         for t, n in ((block_count, "block_count"), (block_idx, "block_idx")):
@@ -408,13 +414,13 @@ def prefill(q, k, v, base: float, alpha: float, *, scale: float | None = None, p
                 raise ValueError("%s must be a contiguous int32 device tensor" % n)
         if tuple(block_count.shape) != (B, Hq, nblk) or block_idx.dim() != 4 \
                 or tuple(block_idx.shape[:3]) != (B, Hq, nblk):
-            raise ValueError("block_count [B][Hq][ceil(N/64)], block_idx [B][Hq][ceil(N/64)][max]")
-        _check(lib().wpa_prefill_sparse(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
-                                        _ptr(block_count), _ptr(block_idx), block_idx.shape[3],
-                                        B, N, Hq, Hkv, d, float(base), rope, float(alpha),
-                                        float(scale) if scale is not None else 0.0,
-                                        _dtype_code(q), _dtype_code(out), _ptr(term_count),
-                                        _ptr(workspace), _ws_bytes(workspace), _stream(stream)))
+            raise ValueError("block_count [B][Hq][ceil(N/block)], block_idx [B][Hq][ceil(N/block)][max]")
+        _check(lib().wpa_prefill_sparse_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                           _ptr(block_count), _ptr(block_idx), block_idx.shape[3],
+                                           block, B, N, Hq, Hkv, d, float(base), rope,
+                                           float(alpha), float(scale) if scale is not None else 0.0,
+                                           _dtype_code(q), _dtype_code(out), _ptr(term_count),
+                                           _ptr(workspace), _ws_bytes(workspace), _stream(stream)))
         return (out, lse) if lse is not None else out
     _check(lib().wpa_prefill_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(positions),
                                 B, N, Hq, Hkv, d, float(base), rope, float(alpha),

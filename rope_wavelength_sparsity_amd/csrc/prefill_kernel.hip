@@ -881,28 +881,33 @@ void prefill_kernel(PrefillParams p, Tables tab, Launch L) {
             }
         }
     } else {
-        // The lists as bitmaps in LDS: one bit per 64-key block for each compute wave (its own
-        // query block always set) and their union.
+        // The lists as bitmaps in LDS: one bit per 64-key block for each compute wave and their
+        // union.  A list block of 64 << s keys sets 1 << s consecutive bits (aligned, so never
+        // across a word); the wave's own list block is always set up to its own 64-key block.
         const int nblk = (N_SP + 63) / 64, words = (nblk + 31) / 32;
         const int NL = L.Gc * L.R;
         uint32_t* uni = sBits + NL * words;
         for (int i = tid; i < (NL + 1) * words; i += blockDim.x) sBits[i] = 0u;
         __syncthreads();
         if (!producer && wave_ok) {
-            const int rb = q0 >> 6;
+            const int s = p.blk_log2 - 6;
+            const int rb = q0 >> 6, R = q0 >> p.blk_log2;
+            const int nlb = (N_SP + (1 << p.blk_log2) - 1) >> p.blk_log2;
             uint32_t* mine = sBits + w * words;
-            if (lane == 0) {
-                atomicOr(&mine[rb >> 5], 1u << (rb & 31));
-                atomicOr(&uni[rb >> 5], 1u << (rb & 31));
+            for (int t = (R << s) + lane; t <= rb; t += 64) {
+                atomicOr(&mine[t >> 5], 1u << (t & 31));
+                atomicOr(&uni[t >> 5], 1u << (t & 31));
             }
-            const int64_t li = ((int64_t)b * p.Hq + hq) * nblk + rb;
+            const uint32_t run = (1u << (1 << s)) - 1u;        // s <= 4
+            const int64_t li = ((int64_t)b * p.Hq + hq) * nlb + R;
             int c = p.blk_count[li];
             c = c < 0 ? 0 : (c > p.blk_max ? p.blk_max : c);
             for (int e = lane; e < c; e += 64) {
                 const int kb = p.blk_idx[li * p.blk_max + e];
-                if (kb >= 0 && kb < rb) {
-                    atomicOr(&mine[kb >> 5], 1u << (kb & 31));
-                    atomicOr(&uni[kb >> 5], 1u << (kb & 31));
+                if (kb >= 0 && kb < R) {
+                    const int t = kb << s;
+                    atomicOr(&mine[t >> 5], run << (t & 31));
+                    atomicOr(&uni[t >> 5], run << (t & 31));
                 }
             }
         }

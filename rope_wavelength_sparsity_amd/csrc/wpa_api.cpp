@@ -466,7 +466,7 @@ int attend_impl(const void* q, void* out, float* lse, const int32_t* positions, 
                 const wpa_rope_t* rope, double alpha, float scale, int32_t dtype,
                 int32_t out_dtype, unsigned long long* term_count, const void* workspace,
                 size_t ws_bytes, void* stream, const int32_t* blk_count,
-                const int32_t* blk_idx, int32_t blk_max);
+                const int32_t* blk_idx, int32_t blk_max, int32_t blk_log2 = 6);
 
 }  // namespace
 
@@ -490,7 +490,7 @@ int attend_impl(const void* q, void* out, float* lse, const int32_t* positions, 
                 const wpa_rope_t* rope, double alpha, float scale, int32_t dtype,
                 int32_t out_dtype, unsigned long long* term_count, const void* workspace,
                 size_t ws_bytes, void* stream, const int32_t* blk_count,
-                const int32_t* blk_idx, int32_t blk_max) {
+                const int32_t* blk_idx, int32_t blk_max, int32_t blk_log2) {
     int rc = check_common(d, base, rope, alpha);
     if (rc) return rc;
     rc = check_prefill_shape(N, B, Hkv, dtype, positions, workspace, ws_bytes, d);
@@ -513,11 +513,11 @@ int attend_impl(const void* q, void* out, float* lse, const int32_t* positions, 
     pp.pos = positions; pp.counter = term_count; pp.N = N; pp.Np = Np; pp.ldk = Np; pp.B = B; pp.Hq = Hq;
     pp.Hkv = Hkv; pp.d = d; pp.in_f32 = dtype == WPA_FP32; pp.out_f32 = out_dtype == WPA_FP32;
     pp.scale = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)d));
-    pp.blk_count = blk_count; pp.blk_idx = blk_idx; pp.blk_max = blk_max;
+    pp.blk_count = blk_count; pp.blk_idx = blk_idx; pp.blk_max = blk_max; pp.blk_log2 = blk_log2;
     pp.head_theta = head_tables(rope);
     pp.alpha = alpha;
     if (debug_on()) {
-        const size_t qo = (size_t)B * N * Hq * d, nblk = (size_t)((N + 63) / 64);
+        const size_t qo = (size_t)B * N * Hq * d, nblk = (size_t)((N + (1 << blk_log2) - 1) >> blk_log2);
         if ((rc = dbg_extent(q, qo * esize(dtype), "q")) ||
             (rc = dbg_extent(out, qo * esize(out_dtype), "out")) ||
             (rc = dbg_extent(lse, (size_t)B * Hq * N * 4, "lse")) ||
@@ -579,8 +579,22 @@ int wpa_prefill_sparse(const void* q, const void* k, const void* v, void* out, f
                        const wpa_rope_t* rope, double alpha, float scale, int32_t dtype,
                        int32_t out_dtype, unsigned long long* term_count, void* workspace,
                        size_t ws_bytes, void* stream) {
+    return wpa_prefill_sparse_ex(q, k, v, out, lse, blk_count, blk_idx, blk_max, 64, B, N, Hq,
+                                 Hkv, d, base, rope, alpha, scale, dtype, out_dtype, term_count,
+                                 workspace, ws_bytes, stream);
+}
+
+int wpa_prefill_sparse_ex(const void* q, const void* k, const void* v, void* out, float* lse,
+                          const int32_t* blk_count, const int32_t* blk_idx, int32_t blk_max,
+                          int32_t block, int32_t B, int64_t N, int32_t Hq, int32_t Hkv, int32_t d,
+                          double base, const wpa_rope_t* rope, double alpha, float scale,
+                          int32_t dtype, int32_t out_dtype, unsigned long long* term_count,
+                          void* workspace, size_t ws_bytes, void* stream) {
     int rc = check_common(d, base, rope, alpha);
     if (rc) return rc;
+    if (block < 64 || block > 1024 || (block & (block - 1)))
+        return fail(WPA_ERR_INVALID, "block must be a power of two from 64 to 1024 (got %d)", block);
+    const int32_t blk_log2 = __builtin_ctz((unsigned)block);
     if (B < 1 || N < 1 || Hq < 1 || Hkv < 1) return fail(WPA_ERR_INVALID, "B, N, Hq, Hkv must be >= 1");
     if (Hq % Hkv) return fail(WPA_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
     if (N > ((int64_t)1 << 21)) return fail(WPA_ERR_UNSUPPORTED, "block-sparse prefill supports N up to 2^21 tokens");
@@ -615,7 +629,7 @@ int wpa_prefill_sparse(const void* q, const void* k, const void* v, void* out, f
     if (rc) return rc;
     return attend_impl(q, out, lse, nullptr, B, N, Hq, Hkv, d, base, rope, alpha, scale, dtype,
                        out_dtype, term_count, workspace, ws_bytes, stream, blk_count,
-                       blk_idx ? blk_idx : blk_count, blk_max);
+                       blk_idx ? blk_idx : blk_count, blk_max, blk_log2);
 }
 
 // Workspace of the prefill backward: its regions, in order, each 256-byte aligned.

@@ -71,9 +71,10 @@ struct PrefillParams {
     const int32_t* kv_len;        // cached (chunked) prefill: [B] keys per sequence; else null
     int64_t ldk;                  // key row stride of kp: Np, or Lmax of the caches
     int32_t Nq;                   // cached: queries per sequence (its last Nq tokens)
-    const int32_t* blk_count;     // block-sparse: [B][Hq][ceil(N/64)] list lengths; else null
-    const int32_t* blk_idx;       // block-sparse: [B][Hq][ceil(N/64)][blk_max] ascending blocks
+    const int32_t* blk_count;     // block-sparse: [B][Hq][ceil(N/blk)] list lengths; else null
+    const int32_t* blk_idx;       // block-sparse: [B][Hq][ceil(N/blk)][blk_max] key blocks
     int32_t blk_max;
+    int32_t blk_log2;             // block-sparse: log2 of the block size blk (6 .. 10)
     void* out;                    // [B][N][Hq][d]
     float* lse;                   // [B][Hq][N] or null
     const int32_t* pos;           // [B][N] or null

@@ -15,12 +15,12 @@ from gpu_util import LSE_MAX, as_bf16_for_oracle as exact, check_close, need_gpu
 pytestmark = pytest.mark.gpu
 
 
-def _lists(B, H, N, density, seed, width=None, junk=False):
+def _lists(B, H, N, density, seed, width=None, junk=False, blk=64):
     """MInference-like lists: the first block (attention sink), the two blocks below the
     query block (local), and random earlier blocks with the given density; ascending.
     junk adds duplicates and entries outside [0, R) (ignored by the rule)."""
     rng = np.random.default_rng(seed)
-    nblk = (N + 63) // 64
+    nblk = (N + blk - 1) // blk
     lists = [[[None] * nblk for _ in range(H)] for _ in range(B)]
     for b in range(B):
         for h in range(H):
@@ -42,14 +42,14 @@ def _lists(B, H, N, density, seed, width=None, junk=False):
     return count, idx
 
 
-def _run(q, k, v, base, alpha, count, idx, rows=None):
+def _run(q, k, v, base, alpha, count, idx, rows=None, blk=64):
     cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
     out, lse = wpa.prefill(q.cuda(), k.cuda(), v.cuda(), base, alpha, want_lse=True, term_count=cnt,
                            out_dtype=torch.float32, block_count=torch.from_numpy(count).cuda(),
-                           block_idx=torch.from_numpy(idx).cuda())
+                           block_idx=torch.from_numpy(idx).cuda(), block=blk)
     torch.cuda.synchronize()
     ro, rl, kept = oracle.prefill_sparse(exact(q), exact(k), exact(v), base, alpha, count, idx,
-                                         rows=rows)
+                                         rows=rows, blk=blk)
     return out, lse, int(cnt.item()), ro, rl, kept
 
 
@@ -170,3 +170,47 @@ def test_block_sparse_long_sampled_rows():
     torch.cuda.synchronize()
     _, _, kept = oracle.prefill_sparse(exact(q1), exact(k1), exact(v1), base, 1.0, c1, i1)
     assert int(cnt1.item()) == kept
+
+
+def _expand(count, idx, f, N):
+    """Lists over blocks of 64*f tokens as lists of 64-token blocks: a listed block becomes
+    its f 64-token blocks, and each 64-row block also lists the earlier 64-token blocks of its
+    own coarse block."""
+    B, H, _ = count.shape
+    nf = (N + 63) // 64
+    rows = [[[sorted({c * f + j for c in idx[b, h, R // f, :min(max(int(count[b, h, R // f]), 0),
+                                                                 idx.shape[3])]
+                      if 0 <= c < R // f for j in range(f)} | set(range((R // f) * f, R)))
+              for R in range(nf)] for h in range(H)] for b in range(B)]
+    m = max(1, max(len(x) for bl in rows for hl in bl for x in hl))
+    cf = np.zeros((B, H, nf), np.int32)
+    xf = np.zeros((B, H, nf, m), np.int32)
+    for b in range(B):
+        for h in range(H):
+            for R in range(nf):
+                cf[b, h, R] = len(rows[b][h][R])
+                xf[b, h, R, :cf[b, h, R]] = rows[b][h][R]
+    return cf, xf
+
+
+@pytest.mark.parametrize("blk,N", [(128, 1300), (256, 1300), (1024, 2500)])
+@pytest.mark.parametrize("d,Hq,Hkv,base", [(64, 14, 2, 1e6), (128, 24, 8, 5e5)])
+def test_block_sparse_other_block_sizes(blk, N, d, Hq, Hkv, base):
+    """Blocks of 128, 256 and 1024 tokens (N not a multiple of the block): outputs, LSE and
+    counts against the oracle at that block size, and bit-identical to the 64-token call on
+    the expanded lists (the same visited keys)."""
+    need_gpu()
+    q, k, v = synth.prefill_inputs(1, N, Hq, Hkv, d, "bf16", seed=95 + d)
+    count, idx = _lists(1, Hq, N, 0.3, seed=96, junk=True, blk=blk)
+    say("block sparse blocks of", blk, "d", d)
+    out, lse, cnt, ro, rl, kept = _run(q, k, v, base, 1.0, count, idx, blk=blk)
+    check_close(out.cpu().numpy(), ro, "out")
+    check_close(lse.cpu().numpy(), rl, "lse", LSE_MAX, LSE_MAX)
+    assert cnt == kept
+    cf, xf = _expand(count, idx, blk // 64, N)
+    c64 = torch.zeros(1, dtype=torch.int64, device="cuda")
+    o64, l64 = wpa.prefill(q.cuda(), k.cuda(), v.cuda(), base, 1.0, want_lse=True, term_count=c64,
+                           out_dtype=torch.float32, block_count=torch.from_numpy(cf).cuda(),
+                           block_idx=torch.from_numpy(xf).cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(out, o64) and torch.equal(lse, l64) and int(c64.item()) == cnt

@@ -475,7 +475,8 @@ def cpu_as_device(monkeypatch):
     def no_call(*a, **k):
         raise AssertionError("a rejected call reached the library")
     for name in ("wpa_prefill_ex", "wpa_prefill_attend_ex", "wpa_prefill_prepare_ex", "wpa_decode_ex",
-                 "wpa_prefill_cached", "wpa_prefill_sparse", "wpa_prefill_cached_ex"):
+                 "wpa_prefill_cached", "wpa_prefill_sparse", "wpa_prefill_cached_ex",
+                 "wpa_prefill_sparse_ex"):
         monkeypatch.setattr(wpa.lib(), name, no_call)
     return torch
 
@@ -607,3 +608,48 @@ def test_debug_mode_checks_after_argument_checks():
         assert L.wpa_last_error().decode().startswith("debug:")
     finally:
         L.wpa_set_debug(was)
+
+
+def _sparse_ex_rc(block, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, cnt_l=FAKE, idx=FAKE, bmax=4, B=1, N=4096,
+             Hq=4, Hkv=2, d=64, base=1e4, alpha=1.0, scale=0.0, dtype=0, odt=0, cnt=None, ws=FAKE,
+             ws_bytes=1 << 30)
+    a.update(kw)
+    return wpa.lib().wpa_prefill_sparse_ex(a["q"], a["k"], a["v"], a["out"], a["lse"], a["cnt_l"],
+                                           a["idx"], a["bmax"], block, a["B"], a["N"], a["Hq"],
+                                           a["Hkv"], a["d"], a["base"], None, a["alpha"], a["scale"],
+                                           a["dtype"], a["odt"], a["cnt"], a["ws"], a["ws_bytes"],
+                                           None)
+
+
+@pytest.mark.parametrize("block", [0, 32, 96, 100, 2048, -64])
+def test_sparse_block_size_is_checked_first(block):
+    """Block sizes that are not a power of two from 64 to 1024 are refused before anything
+    is enqueued, with the reason in the error text."""
+    assert _sparse_ex_rc(block) == wpa.WPA_ERR_INVALID
+    assert "block must be" in wpa.lib().wpa_last_error().decode()
+
+
+def test_sparse_lists_rejected_like_the_64_block_entry():
+    """The other argument checks of the block-size entry run for every block size."""
+    for block in (64, 128, 1024):
+        assert _sparse_ex_rc(block, cnt_l=None) == wpa.WPA_ERR_INVALID
+        assert _sparse_ex_rc(block, bmax=-1) == wpa.WPA_ERR_INVALID
+        assert _sparse_ex_rc(block, Hq=3) == wpa.WPA_ERR_INVALID
+        assert _sparse_ex_rc(block, N=(1 << 21) + 1) == wpa.WPA_ERR_UNSUPPORTED
+
+
+def test_binding_checks_sparse_block_and_list_shapes(cpu_as_device, monkeypatch):
+    torch = cpu_as_device
+    monkeypatch.setattr(wpa, "_stream", lambda s: None)
+    q, k, v = _pf(torch, N=512)
+    for block, nblk, ok in ((128, 4, True), (128, 8, False), (256, 2, True), (96, 6, False),
+                            (2048, 1, False)):
+        cnt = torch.zeros((1, 4, nblk), dtype=torch.int32)
+        idx = torch.zeros((1, 4, nblk, 2), dtype=torch.int32)
+        if ok:                      # shapes accepted: the call reaches the (stubbed) library
+            with pytest.raises(AssertionError):
+                wpa.prefill(q, k, v, 1e4, 1.0, block_count=cnt, block_idx=idx, block=block)
+        else:
+            with pytest.raises(ValueError):
+                wpa.prefill(q, k, v, 1e4, 1.0, block_count=cnt, block_idx=idx, block=block)
