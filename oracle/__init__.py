@@ -57,7 +57,7 @@ def _load():
         lib.orc_prefill_ex.argtypes = [P, P, P, I, P, I, I64, I, I, I, D, P, I, I, D, D, P, I64, P,
                                        P, P, I]
         lib.orc_prefill_ex.restype = I
-        lib.orc_prefill_sparse.argtypes = [P, P, P, I, I, I64, I, I, I, D, P, I, I, D, D, P, P, I, I,
+        lib.orc_prefill_sparse.argtypes = [P, P, P, I, P, I, I64, I, I, I, D, P, I, I, D, D, P, P, I, I,
                                            P, I64, P, P, P, I]
         lib.orc_prefill_sparse.restype = I
         lib.orc_prefill_backward_ex.argtypes = [P, P, P, P, I, P, I, I64, I, I, I, D, P, I, I, D, D,
@@ -212,11 +212,12 @@ def prefill_backward(q, k, v, dout, base: float, alpha: float, scale: float | No
 
 def prefill_sparse(q, k, v, base: float, alpha: float, count, idx, blk: int = 64,
                    scale: float | None = None, rows=None, nthreads: int = 0, inv_freq=None,
-                   layout: str = "half"):
+                   layout: str = "half", pos=None):
     """Causal windowed prefill restricted to listed key blocks: with R = r // blk, row r of
     head h attends key c <= r iff c // blk == R or c // blk is among the first
-    count[b][h][R] entries of idx[b][h][R]; other keys leave the softmax.  Positions are
-    token indices.  count int32 [B][Hq][nblk], idx int32 [B][Hq][nblk][max_blocks].
+    count[b][h][R] entries of idx[b][h][R]; other keys leave the softmax.  Blocks are by
+    token index; pos ([B][N] int, default token indices) are the RoPE positions, as in
+    prefill().  count int32 [B][Hq][nblk], idx int32 [B][Hq][nblk][max_blocks].
     Returns (out [B][R][Hq][d], lse [B][Hq][R], kept) in fp64 like prefill()."""
     q, dt = _as_input(q)
     k, dk = _as_input(k)
@@ -239,7 +240,10 @@ def prefill_sparse(q, k, v, base: float, alpha: float, count, idx, blk: int = 64
     lse = np.empty((B, Hq, R), dtype=np.float64)
     kept = ctypes.c_int64(0)
     tabs, ntab = _freq_heads(inv_freq, d, Hkv)
-    rc = _load().orc_prefill_sparse(_ptr(q), _ptr(k), _ptr(v), dt, B, N, Hq, Hkv, d, float(base),
+    if pos is not None:
+        pos = np.ascontiguousarray(pos, dtype=np.int32).reshape(B, N)
+    rc = _load().orc_prefill_sparse(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(pos), B, N, Hq, Hkv, d,
+                                    float(base),
                                     _ptr(tabs), ntab, LAYOUTS[layout], float(alpha),
                                     float(scale), _ptr(count), _ptr(idx), idx.shape[3], blk,
                                     _ptr(rows), R, _ptr(out), _ptr(lse), ctypes.byref(kept),

@@ -291,10 +291,12 @@ int orc_prefill(const void* q, const void* k, const void* v, int dtype, const in
  * idx[b][h][R][0 .. max_blocks).  Keys outside the listed blocks leave the softmax
  * altogether; the listed ones get the windowed logits of orc_prefill_ex.
  *   count int32 [B][Hq][nblk], idx int32 [B][Hq][nblk][max_blocks], nblk = ceil(N / blk).
- * Positions are token indices.  Other arguments (inv_freq with n_tables: one shared table,
- * or one row per kv head) and outputs as for orc_prefill_ex.
+ * Blocks are formed by token index; the rotation and the window take the positions pos
+ * ([B][N], NULL = token indices), as in orc_prefill_ex.  Other arguments (inv_freq with
+ * n_tables: one shared table, or one row per kv head) and outputs as for orc_prefill_ex.
  */
-int orc_prefill_sparse(const void* q, const void* k, const void* v, int dtype, int B, int64_t N,
+int orc_prefill_sparse(const void* q, const void* k, const void* v, int dtype, const int32_t* pos,
+                       int B, int64_t N,
                        int Hq, int Hkv, int d, double base, const double* inv_freq, int n_tables,
                        int interleaved, double alpha, double scale, const int32_t* count,
                        const int32_t* idx, int max_blocks, int blk, const int64_t* rows,
@@ -313,12 +315,12 @@ int orc_prefill_sparse(const void* q, const void* k, const void* v, int dtype, i
     int64_t nblk = (N + blk - 1) / blk;
     double* thr = orc_head_thresholds(d, base, inv_freq, n_tables, Hkv, alpha);
     int64_t* p64 = (int64_t*)malloc(sizeof(int64_t) * N);
-    for (int64_t t = 0; t < N; ++t) p64[t] = t;
     double* kr = (double*)malloc(sizeof(double) * N * Hkv * d);
     double* qr = (double*)malloc(sizeof(double) * n_rows * Hq * d);
     int64_t* qp = (int64_t*)malloc(sizeof(int64_t) * n_rows);
     int64_t kept_total = 0;
     for (int b = 0; b < B; ++b) {
+        for (int64_t t = 0; t < N; ++t) p64[t] = pos ? (int64_t)pos[(int64_t)b * N + t] : t;
         orc_rotate((const char*)k + (size_t)esz * b * N * Hkv * d, dtype, N, Hkv, d, p64, base,
                    inv_freq, n_tables, interleaved, kr);
         const char* qb = (const char*)q + (size_t)esz * b * N * Hq * d;
@@ -326,7 +328,7 @@ int orc_prefill_sparse(const void* q, const void* k, const void* v, int dtype, i
         for (int64_t j = 0; j < n_rows; ++j) {
             int64_t r = rows ? rows[j] : j;
             memcpy(qsel + (size_t)esz * j * Hq * d, qb + (size_t)esz * r * Hq * d, (size_t)esz * Hq * d);
-            qp[j] = r;
+            qp[j] = p64[r];
         }
         orc_rotate(qsel, dtype, n_rows, Hq, d, qp, base, inv_freq, n_tables, interleaved, qr);
         free(qsel);

@@ -515,6 +515,54 @@ def test_block_sparse_equals_relative_form_with_mask(alpha):
     assert kept == tally
 
 
+@pytest.mark.parametrize("positions", ["gapped", "nonmonotone"])
+def test_block_sparse_with_positions_equals_relative_form_with_mask(positions):
+    """Blocks by token index, rotation and window at explicit positions: each head against
+    the complex relative form at those positions with the block mask, and a brute-force
+    tally of the kept terms."""
+    B, N, Hq, Hkv, d, base, blk, alpha = 1, 45, 2, 1, 16, 100.0, 8, 1.0
+    q, k, v = synth.prefill_inputs(B, N, Hq, Hkv, d, "fp32", seed=87)
+    rng = np.random.default_rng(88)
+    if positions == "gapped":
+        pos = np.cumsum(rng.integers(1, 9, N)) + 3
+    else:
+        pos = rng.integers(0, 200, N)
+    nblk = (N + blk - 1) // blk
+    count, idx = _random_lists(B, Hq, nblk, 4, seed=89)
+    out, lse, kept = oracle.prefill_sparse(synth.to_oracle(q), synth.to_oracle(k),
+                                           synth.to_oracle(v), base, alpha, count, idx, blk=blk,
+                                           pos=pos[None])
+    vis = _visible(N, blk, count, idx)
+    lam = 2.0 * np.pi * np.power(base, np.arange(d // 2) * 2.0 / d)
+    tally = 0
+    for h in range(Hq):
+        ro, rl = _relative_form(_f64(q[0, :, h]), _f64(k[0, :, 0]), _f64(v[0, :, 0]), pos, pos,
+                                base, alpha, 1.0 / math.sqrt(d), visible=vis[0, h])
+        np.testing.assert_allclose(out[0, :, h], ro, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[0, h], rl, rtol=0, atol=1e-12)
+        dist = pos[:, None] - pos[None, :]
+        tally += int(((np.abs(dist)[..., None] <= alpha * lam) & vis[0, h][..., None]
+                      & np.tri(N, dtype=bool)[..., None]).sum())
+    assert kept == tally
+
+
+def test_block_sparse_with_positions_and_every_block_is_the_dense_prefill():
+    """Listing every block at explicit positions is the plain prefill at those positions,
+    bit for bit (and differs from the same call at token indices)."""
+    B, N, Hq, Hkv, d, base, blk = 2, 70, 2, 1, 32, 1e4, 16
+    q, k, v = synth.prefill_inputs(B, N, Hq, Hkv, d, "bf16", seed=90)
+    a = [synth.to_oracle(t) for t in (q, k, v)]
+    pos = np.cumsum(np.random.default_rng(91).integers(1, 40, (B, N)), axis=1).astype(np.int32)
+    nblk = (N + blk - 1) // blk
+    count = np.full((B, Hq, nblk), nblk, np.int32)
+    idx = np.broadcast_to(np.arange(nblk, dtype=np.int32), (B, Hq, nblk, nblk)).copy()
+    o1, l1, k1 = oracle.prefill(*a, base, 1.0, pos=pos)
+    o2, l2, k2 = oracle.prefill_sparse(*a, base, 1.0, count, idx, blk=blk, pos=pos)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2) and k1 == k2
+    o3, _, k3 = oracle.prefill_sparse(*a, base, 1.0, count, idx, blk=blk)
+    assert not np.array_equal(o1, o3) and k3 != k1
+
+
 def test_block_sparse_with_every_block_is_dense():
     """Listing every block is the plain causal prefill, bit for bit."""
     B, N, Hq, Hkv, d, base, blk = 1, 70, 3, 1, 32, 1e4, 16
