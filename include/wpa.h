@@ -324,6 +324,25 @@ int wpa_prefill_sparse_ex(const void* q, const void* k, const void* v, void* out
                           void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * wpa_prefill_sparse_ex at explicit positions (ATFlash abstract: the window is applied on top
+ * of token-level block methods, and RoPE rotates each token by its position).  The blocks and
+ * the causal rule stay those of token indices: row r attends key c <= r iff c // block is r's
+ * own block or is listed for it.  The rotation of q and k and the window compare positions:
+ *   positions  int32 device [B][N], non-negative and non-decreasing within each sequence
+ *              (repeats allowed), below 2^31 - 1; not null (WPA_ERR_INVALID).
+ * Every other argument, the LDS bound on N and the error behaviour are those of
+ * wpa_prefill_sparse_ex.  Per-kv-head frequency tables (rope->head_inv_freq) are not taken
+ * here: WPA_ERR_UNSUPPORTED, before anything is enqueued.
+ */
+int wpa_prefill_sparse_pos(const void* q, const void* k, const void* v, void* out, float* lse,
+                           const int32_t* blk_count, const int32_t* blk_idx, int32_t blk_max,
+                           int32_t block, const int32_t* positions, int32_t B, int64_t N,
+                           int32_t Hq, int32_t Hkv, int32_t d, double base, const wpa_rope_t* rope,
+                           double alpha, float scale, int32_t dtype, int32_t out_dtype,
+                           unsigned long long* term_count, void* workspace, size_t ws_bytes,
+                           void* stream);
+
+/*
  * Windowed decode cache (K-dim eviction).  In decode the query is the newest token, so the
  * distance to a given key only grows: once it exceeds the window of every pair of a 16-dim
  * pair block, that block of that key is never read again (WavePrune original abstract:

@@ -45,7 +45,7 @@ EXPORTS = ("wpa_count_terms", "wpa_thresholds", "wpa_prefill_workspace_bytes", "
            "wpa_prefill_cached_varlen", "wpa_prefill_paged_varlen", "wpa_decode_noalloc",
            "wpa_prefill_backward_workspace_bytes", "wpa_prefill_backward",
            "wpa_prefill_cached_workspace_bytes", "wpa_prefill_cached_ex", "wpa_set_debug",
-           "wpa_last_error", "wpa_prefill_sparse_ex")
+           "wpa_last_error", "wpa_prefill_sparse_ex", "wpa_prefill_sparse_pos")
 
 
 class Rope(ctypes.Structure):
@@ -190,6 +190,9 @@ def lib():
     L.wpa_prefill_sparse_ex.argtypes = [P, P, P, P, P, P, P, I32, I32, I32, I64, I32, I32, I32, D,
                                         P, D, F, I32, I32, P, P, SZ, P]
     L.wpa_prefill_sparse_ex.restype = ctypes.c_int
+    L.wpa_prefill_sparse_pos.argtypes = [P, P, P, P, P, P, P, I32, I32, P, I32, I64, I32, I32, I32,
+                                         D, P, D, F, I32, I32, P, P, ctypes.c_size_t, P]
+    L.wpa_prefill_sparse_pos.restype = ctypes.c_int
     L.wpa_kv_page_bytes.argtypes = [I32, I32, I32]
     L.wpa_kv_page_bytes.restype = SZ
     L.wpa_kv_write_paged.argtypes = [P, P, I64, I64, P, P, P, I32, I32, I32, I32, I32, I32, D, P,
@@ -378,7 +381,8 @@ def prefill(q, k, v, base: float, alpha: float, *, scale: float | None = None, p
 
     block_count / block_idx (int32 device [B][Hq][ceil(N/block)] and [...][max]): token-level
     block sparsity on top of the window; each query block of `block` rows (a power of two,
-    64 .. 1024) attends its own block and the key blocks listed for it.
+    64 .. 1024) attends its own block and the key blocks listed for it.  Blocks are by token
+    index; with positions, the rotation and the window use the positions.
 
     Returns out [B][N][Hq][d] (out_dtype, default q's dtype), or (out, lse [B][Hq][N] fp32)
     when want_lse or an lse buffer is passed.  term_count: optional int64 device tensor of
@@ -406,8 +410,8 @@ def prefill(q, k, v, base: float, alpha: float, *, scale: float | None = None, p
         if block < 64 or block > 1024 or block & (block - 1):
             raise ValueError("block must be a power of two from 64 to 1024")
         nblk = (N + block - 1) // block
-        if positions is not None:
-            raise ValueError("block-sparse prefill uses token indices as positions")
+        if positions is not None and inv_freq is not None and _ndim(inv_freq) == 2:
+            raise ValueError("block-sparse prefill at explicit positions takes one frequency table")
         for t, n in ((block_count, "block_count"), (block_idx, "block_idx")):
             _dev(t, n)
             if t.dtype != torch.int32 or not t.is_contiguous():
@@ -415,6 +419,17 @@ def prefill(q, k, v, base: float, alpha: float, *, scale: float | None = None, p
         if tuple(block_count.shape) != (B, Hq, nblk) or block_idx.dim() != 4 \
                 or tuple(block_idx.shape[:3]) != (B, Hq, nblk):
             raise ValueError("block_count [B][Hq][ceil(N/block)], block_idx [B][Hq][ceil(N/block)][max]")
+        if positions is not None:
+            # blocks by token index; rotation and window at the positions
+            _check(lib().wpa_prefill_sparse_pos(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                                _ptr(block_count), _ptr(block_idx),
+                                                block_idx.shape[3], block, _ptr(positions), B, N,
+                                                Hq, Hkv, d, float(base), rope, float(alpha),
+                                                float(scale) if scale is not None else 0.0,
+                                                _dtype_code(q), _dtype_code(out), _ptr(term_count),
+                                                _ptr(workspace), _ws_bytes(workspace),
+                                                _stream(stream)))
+            return (out, lse) if lse is not None else out
         _check(lib().wpa_prefill_sparse_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                                            _ptr(block_count), _ptr(block_idx), block_idx.shape[3],
                                            block, B, N, Hq, Hkv, d, float(base), rope,

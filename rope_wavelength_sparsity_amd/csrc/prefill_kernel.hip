@@ -140,7 +140,8 @@ struct Tile {
 // queries are its last Nq tokens (chunked prefill).  Positions are token indices.
 // SPARSE: each (sequence, q head, 64-row query block) attends, besides its own block, only
 // the 64-key blocks its ascending list names (token-level block sparsity composed with the
-// window); unlisted keys leave the softmax.  Positions are token indices.
+// window); unlisted keys leave the softmax.  Blocks are by token index; with HASPOS the
+// rotation and the window use the explicit positions.
 // HEADS: one rotation-frequency table per kv head (p.head_theta [Hkv][d/2], device); the
 // workgroup's window table is computed from its kv head's row at start.
 template <int D, bool F32, bool HASPOS, bool COUNT, bool CACHED, bool SPARSE, bool PAGED = false,
@@ -1073,9 +1074,9 @@ int device_cus() {
 // Dynamic LDS of a block-sparse launch: one bitmap of ceil(N/64) bits per compute wave (a
 // workgroup takes maxw row groups of one q head) and their union, in 32-bit words.
 template <int D>
-size_t sparse_bitmap_bytes(int64_t N) {
+size_t sparse_bitmap_bytes(int64_t N, bool haspos) {
     const size_t words = (size_t)(((N + 63) / 64 + 31) / 32);
-    return (size_t)(Tile<D>::maxw(false) + 1) * words * 4;
+    return (size_t)(Tile<D>::maxw(haspos) + 1) * words * 4;
 }
 
 // LDS a block-sparse launch of N tokens needs (the kernel's static arrays plus the bitmaps)
@@ -1084,7 +1085,11 @@ template <int D, bool F32>
 hipError_t sparse_lds_d(const PrefillParams& p, size_t* need, size_t* limit) {
     hipFuncAttributes attr;
     const bool hd = p.head_theta != nullptr;
-    hipError_t e = p.counter
+    // explicit positions (never with per-head tables here): the instances with a position tile
+    hipError_t e = p.pos
+        ? (p.counter ? hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&prefill_kernel<D, F32, true, true, false, true>))
+                     : hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&prefill_kernel<D, F32, true, false, false, true>)))
+        : p.counter
         ? (hd ? hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&prefill_kernel<D, F32, false, true, false, true, false, true>))
               : hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&prefill_kernel<D, F32, false, true, false, true>)))
         : (hd ? hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&prefill_kernel<D, F32, false, false, false, true, false, true>))
@@ -1095,7 +1100,7 @@ hipError_t sparse_lds_d(const PrefillParams& p, size_t* need, size_t* limit) {
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&lim, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
     if (e != hipSuccess) return e;
-    *need = attr.sharedSizeBytes + sparse_bitmap_bytes<D>(p.N);
+    *need = attr.sharedSizeBytes + sparse_bitmap_bytes<D>(p.N, p.pos != nullptr);
     *limit = (size_t)lim;
     return hipSuccess;
 }
@@ -1209,9 +1214,13 @@ hipError_t launch_d(const PrefillParams& p, const Tables& t, hipStream_t s) {
     } else if (p.blk_count) {
         // block bitmaps: one per compute wave and their union (the caller has checked that
         // they fit next to the kernel's static LDS: sparse_lds)
-        const size_t bits = sparse_bitmap_bytes<D>(p.N);
+        const size_t bits = sparse_bitmap_bytes<D>(p.N, hp);
         const bool hd = p.head_theta != nullptr;        // per-kv-head frequency tables
-        if (hd && cn) prefill_kernel<D, F32, false, true, false, true, false, true><<<grid, block, bits, s>>>(p, t, L);
+        // explicit positions: blocks stay token-index blocks, distances come from the
+        // position tile (the caller rejects positions with per-head tables here)
+        if (hp && cn) prefill_kernel<D, F32, true, true, false, true><<<grid, block, bits, s>>>(p, t, L);
+        else if (hp) prefill_kernel<D, F32, true, false, false, true><<<grid, block, bits, s>>>(p, t, L);
+        else if (hd && cn) prefill_kernel<D, F32, false, true, false, true, false, true><<<grid, block, bits, s>>>(p, t, L);
         else if (hd) prefill_kernel<D, F32, false, false, false, true, false, true><<<grid, block, bits, s>>>(p, t, L);
         else if (cn) prefill_kernel<D, F32, false, true, false, true><<<grid, block, bits, s>>>(p, t, L);
         else prefill_kernel<D, F32, false, false, false, true><<<grid, block, bits, s>>>(p, t, L);

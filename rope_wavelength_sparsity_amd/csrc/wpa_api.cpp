@@ -584,14 +584,19 @@ int wpa_prefill_sparse(const void* q, const void* k, const void* v, void* out, f
                                  workspace, ws_bytes, stream);
 }
 
-int wpa_prefill_sparse_ex(const void* q, const void* k, const void* v, void* out, float* lse,
-                          const int32_t* blk_count, const int32_t* blk_idx, int32_t blk_max,
-                          int32_t block, int32_t B, int64_t N, int32_t Hq, int32_t Hkv, int32_t d,
-                          double base, const wpa_rope_t* rope, double alpha, float scale,
-                          int32_t dtype, int32_t out_dtype, unsigned long long* term_count,
-                          void* workspace, size_t ws_bytes, void* stream) {
+// Block-sparse prefill, at token indices (positions null) or at explicit positions.  The
+// blocks are always token-index blocks; the positions only move the rotation and the window.
+static int sparse_impl(const void* q, const void* k, const void* v, void* out, float* lse,
+                       const int32_t* blk_count, const int32_t* blk_idx, int32_t blk_max,
+                       int32_t block, const int32_t* positions, int32_t B, int64_t N, int32_t Hq,
+                       int32_t Hkv, int32_t d, double base, const wpa_rope_t* rope, double alpha,
+                       float scale, int32_t dtype, int32_t out_dtype,
+                       unsigned long long* term_count, void* workspace, size_t ws_bytes,
+                       void* stream) {
     int rc = check_common(d, base, rope, alpha);
     if (rc) return rc;
+    if (positions && head_tables(rope))
+        return fail(WPA_ERR_UNSUPPORTED, "block-sparse prefill at explicit positions takes one frequency table for all heads");
     if (block < 64 || block > 1024 || (block & (block - 1)))
         return fail(WPA_ERR_INVALID, "block must be a power of two from 64 to 1024 (got %d)", block);
     const int32_t blk_log2 = __builtin_ctz((unsigned)block);
@@ -607,7 +612,7 @@ int wpa_prefill_sparse_ex(const void* q, const void* k, const void* v, void* out
     if (!q || !k || !v || !out) return fail(WPA_ERR_INVALID, "null q, k, v or out");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
         return fail(WPA_ERR_INVALID, "q, k, v and out must be 16-byte aligned");
-    rc = check_prefill_shape(N, B, Hkv, dtype, nullptr, workspace, ws_bytes, d);
+    rc = check_prefill_shape(N, B, Hkv, dtype, positions, workspace, ws_bytes, d);
     if (rc) return rc;
     if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(WPA_ERR_INVALID, "lse must be 4-byte aligned");
     if (term_count && (reinterpret_cast<uintptr_t>(term_count) & 7u)) return fail(WPA_ERR_INVALID, "term_count must be 8-byte aligned");
@@ -616,7 +621,7 @@ int wpa_prefill_sparse_ex(const void* q, const void* k, const void* v, void* out
         // anything is enqueued (at d = 128 this bounds N below 2^21)
         wpa::PrefillParams pp{};
         pp.d = d; pp.in_f32 = dtype == WPA_FP32; pp.N = N; pp.counter = term_count;
-        pp.head_theta = head_tables(rope);
+        pp.head_theta = head_tables(rope); pp.pos = positions;
         size_t need = 0, limit = 0;
         hipError_t e = wpa::prefill_sparse_lds(pp, &need, &limit);
         if (e != hipSuccess) return fail(WPA_ERR_HIP, "block-sparse LDS query: %s", hipGetErrorString(e));
@@ -624,12 +629,36 @@ int wpa_prefill_sparse_ex(const void* q, const void* k, const void* v, void* out
             return fail(WPA_ERR_UNSUPPORTED, "block-sparse prefill of %lld tokens at d=%d needs %zu bytes of LDS per "
                         "workgroup (limit %zu)", (long long)N, d, need, limit);
     }
-    rc = wpa_prefill_prepare_ex(k, v, nullptr, B, N, Hkv, d, base, rope, dtype, workspace,
+    rc = wpa_prefill_prepare_ex(k, v, positions, B, N, Hkv, d, base, rope, dtype, workspace,
                                 ws_bytes, stream);
     if (rc) return rc;
-    return attend_impl(q, out, lse, nullptr, B, N, Hq, Hkv, d, base, rope, alpha, scale, dtype,
+    return attend_impl(q, out, lse, positions, B, N, Hq, Hkv, d, base, rope, alpha, scale, dtype,
                        out_dtype, term_count, workspace, ws_bytes, stream, blk_count,
                        blk_idx ? blk_idx : blk_count, blk_max, blk_log2);
+}
+
+int wpa_prefill_sparse_ex(const void* q, const void* k, const void* v, void* out, float* lse,
+                          const int32_t* blk_count, const int32_t* blk_idx, int32_t blk_max,
+                          int32_t block, int32_t B, int64_t N, int32_t Hq, int32_t Hkv, int32_t d,
+                          double base, const wpa_rope_t* rope, double alpha, float scale,
+                          int32_t dtype, int32_t out_dtype, unsigned long long* term_count,
+                          void* workspace, size_t ws_bytes, void* stream) {
+    return sparse_impl(q, k, v, out, lse, blk_count, blk_idx, blk_max, block, nullptr, B, N, Hq,
+                       Hkv, d, base, rope, alpha, scale, dtype, out_dtype, term_count, workspace,
+                       ws_bytes, stream);
+}
+
+int wpa_prefill_sparse_pos(const void* q, const void* k, const void* v, void* out, float* lse,
+                           const int32_t* blk_count, const int32_t* blk_idx, int32_t blk_max,
+                           int32_t block, const int32_t* positions, int32_t B, int64_t N,
+                           int32_t Hq, int32_t Hkv, int32_t d, double base, const wpa_rope_t* rope,
+                           double alpha, float scale, int32_t dtype, int32_t out_dtype,
+                           unsigned long long* term_count, void* workspace, size_t ws_bytes,
+                           void* stream) {
+    if (!positions) return fail(WPA_ERR_INVALID, "null positions (use wpa_prefill_sparse_ex for token indices)");
+    return sparse_impl(q, k, v, out, lse, blk_count, blk_idx, blk_max, block, positions, B, N, Hq,
+                       Hkv, d, base, rope, alpha, scale, dtype, out_dtype, term_count, workspace,
+                       ws_bytes, stream);
 }
 
 // Workspace of the prefill backward: its regions, in order, each 256-byte aligned.

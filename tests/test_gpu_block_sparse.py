@@ -214,3 +214,65 @@ def test_block_sparse_other_block_sizes(blk, N, d, Hq, Hkv, base):
                            block_idx=torch.from_numpy(xf).cuda())
     torch.cuda.synchronize()
     assert torch.equal(out, o64) and torch.equal(lse, l64) and int(c64.item()) == cnt
+
+
+def _positions(B, N, kind, seed):
+    rng = np.random.default_rng(seed)
+    if kind == "gapped":
+        pos = np.cumsum(rng.integers(0, 40, (B, N)), axis=1) + 1000
+    elif kind == "repeated":
+        pos = np.cumsum(rng.integers(0, 2, (B, N)), axis=1)
+    else:                                   # near the top of the int32 range
+        pos = (2 ** 31 - 2 - N) + np.arange(N)[None, :].repeat(B, 0)
+    return np.ascontiguousarray(pos, dtype=np.int32)
+
+
+@pytest.mark.parametrize("kind", ["gapped", "repeated", "high"])
+@pytest.mark.parametrize("blk", [64, 256])
+@pytest.mark.parametrize("d,Hq,Hkv,base", [(64, 14, 2, 1e6), (128, 24, 8, 5e5)])
+def test_block_sparse_at_explicit_positions(kind, blk, d, Hq, Hkv, base):
+    """Block sparsity at explicit positions (blocks by token index; rotation and window at the
+    positions): outputs, LSE and kept-term counts against the oracle given the same
+    positions, with junk entries in the lists and N not a multiple of the block."""
+    need_gpu()
+    B, N = 2, 1100
+    q, k, v = synth.prefill_inputs(B, N, Hq, Hkv, d, "bf16", seed=97 + d)
+    count, idx = _lists(B, Hq, N, 0.3, seed=98, junk=True, blk=blk)
+    pos = _positions(B, N, kind, seed=99)
+    say("block sparse at positions", kind, "blk", blk, "d", d)
+    cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
+    out, lse = wpa.prefill(q.cuda(), k.cuda(), v.cuda(), base, 1.0, want_lse=True, term_count=cnt,
+                           out_dtype=torch.float32, positions=torch.from_numpy(pos).cuda(),
+                           block_count=torch.from_numpy(count).cuda(),
+                           block_idx=torch.from_numpy(idx).cuda(), block=blk)
+    torch.cuda.synchronize()
+    ro, rl, kept = oracle.prefill_sparse(exact(q), exact(k), exact(v), base, 1.0, count, idx,
+                                         blk=blk, pos=pos)
+    check_close(out.cpu().numpy(), ro, "out")
+    check_close(lse.cpu().numpy(), rl, "lse", LSE_MAX, LSE_MAX)
+    assert int(cnt.item()) == kept
+
+
+def test_block_sparse_positions_every_block_equals_dense_at_positions():
+    """With every earlier block listed, the sparse call at positions visits the keys of the
+    dense prefill at the same positions: the two agree within the oracle bar, with the same
+    kept-term count (different kernel instances, so not bit for bit)."""
+    need_gpu()
+    B, N, Hq, Hkv, d, base = 1, 900, 14, 2, 64, 1e6
+    q, k, v = synth.prefill_inputs(B, N, Hq, Hkv, d, "bf16", seed=101)
+    pos = torch.from_numpy(_positions(B, N, "gapped", seed=102)).cuda()
+    nblk = (N + 63) // 64
+    count = np.tile(np.arange(nblk, dtype=np.int32), (B, Hq, 1))
+    idx = np.tile(np.arange(max(nblk, 1), dtype=np.int32), (B, Hq, nblk, 1))
+    c1 = torch.zeros(1, dtype=torch.int64, device="cuda")
+    c2 = torch.zeros(1, dtype=torch.int64, device="cuda")
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    o1, l1 = wpa.prefill(qd, kd, vd, base, 1.0, want_lse=True, term_count=c1, positions=pos,
+                         out_dtype=torch.float32, block_count=torch.from_numpy(count).cuda(),
+                         block_idx=torch.from_numpy(idx).cuda())
+    o2, l2 = wpa.prefill(qd, kd, vd, base, 1.0, want_lse=True, term_count=c2, positions=pos,
+                         out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    check_close(o1.cpu().numpy(), o2.cpu().numpy().astype(np.float64), "out")
+    check_close(l1.cpu().numpy(), l2.cpu().numpy().astype(np.float64), "lse", LSE_MAX, LSE_MAX)
+    assert int(c1.item()) == int(c2.item())

@@ -476,7 +476,7 @@ def cpu_as_device(monkeypatch):
         raise AssertionError("a rejected call reached the library")
     for name in ("wpa_prefill_ex", "wpa_prefill_attend_ex", "wpa_prefill_prepare_ex", "wpa_decode_ex",
                  "wpa_prefill_cached", "wpa_prefill_sparse", "wpa_prefill_cached_ex",
-                 "wpa_prefill_sparse_ex"):
+                 "wpa_prefill_sparse_ex", "wpa_prefill_sparse_pos"):
         monkeypatch.setattr(wpa.lib(), name, no_call)
     return torch
 
@@ -653,3 +653,32 @@ def test_binding_checks_sparse_block_and_list_shapes(cpu_as_device, monkeypatch)
         else:
             with pytest.raises(ValueError):
                 wpa.prefill(q, k, v, 1e4, 1.0, block_count=cnt, block_idx=idx, block=block)
+
+
+def _sparse_pos_rc(pos, rope=None, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, cnt_l=FAKE, idx=FAKE, bmax=4, B=1, N=4096,
+             Hq=4, Hkv=2, d=64, base=1e4, alpha=1.0, scale=0.0, dtype=0, odt=0, cnt=None, ws=FAKE,
+             ws_bytes=1 << 30, block=64)
+    a.update(kw)
+    return wpa.lib().wpa_prefill_sparse_pos(a["q"], a["k"], a["v"], a["out"], a["lse"], a["cnt_l"],
+                                            a["idx"], a["bmax"], a["block"], pos, a["B"], a["N"],
+                                            a["Hq"], a["Hkv"], a["d"], a["base"], rope, a["alpha"],
+                                            a["scale"], a["dtype"], a["odt"], a["cnt"], a["ws"],
+                                            a["ws_bytes"], None)
+
+
+def test_sparse_at_positions_host_checks():
+    """The positions entry refuses a null or misaligned positions pointer, per-head tables,
+    and every argument the token-index entry refuses, before anything is enqueued."""
+    L = wpa.lib()
+    assert _sparse_pos_rc(None) == wpa.WPA_ERR_INVALID
+    assert "positions" in L.wpa_last_error().decode()
+    assert _sparse_pos_rc(ctypes.c_void_p((1 << 20) + 2)) == wpa.WPA_ERR_INVALID
+    assert "positions" in L.wpa_last_error().decode()
+    assert _sparse_pos_rc(FAKE, block=96) == wpa.WPA_ERR_INVALID
+    assert _sparse_pos_rc(FAKE, cnt_l=None) == wpa.WPA_ERR_INVALID
+    assert _sparse_pos_rc(FAKE, Hq=3) == wpa.WPA_ERR_INVALID
+    assert _sparse_pos_rc(FAKE, N=(1 << 21) + 1) == wpa.WPA_ERR_UNSUPPORTED
+    heads = wpa.Rope(wpa.WPA_PAIRS["half"], None, 1 << 20)
+    assert _sparse_pos_rc(FAKE, rope=ctypes.byref(heads)) == wpa.WPA_ERR_UNSUPPORTED
+    assert "frequency table" in L.wpa_last_error().decode()
