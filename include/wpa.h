@@ -331,8 +331,7 @@ int wpa_prefill_sparse_ex(const void* q, const void* k, const void* v, void* out
  *   positions  int32 device [B][N], non-negative and non-decreasing within each sequence
  *              (repeats allowed), below 2^31 - 1; not null (WPA_ERR_INVALID).
  * Every other argument, the LDS bound on N and the error behaviour are those of
- * wpa_prefill_sparse_ex.  Per-kv-head frequency tables (rope->head_inv_freq) are not taken
- * here: WPA_ERR_UNSUPPORTED, before anything is enqueued.
+ * wpa_prefill_sparse_ex, per-kv-head frequency tables (rope->head_inv_freq) included.
  */
 int wpa_prefill_sparse_pos(const void* q, const void* k, const void* v, void* out, float* lse,
                            const int32_t* blk_count, const int32_t* blk_idx, int32_t blk_max,

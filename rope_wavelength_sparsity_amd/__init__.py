@@ -410,8 +410,6 @@ def prefill(q, k, v, base: float, alpha: float, *, scale: float | None = None, p
         if block < 64 or block > 1024 or block & (block - 1):
             raise ValueError("block must be a power of two from 64 to 1024")
         nblk = (N + block - 1) // block
-        if positions is not None and inv_freq is not None and _ndim(inv_freq) == 2:
-            raise ValueError("block-sparse prefill at explicit positions takes one frequency table")
         for t, n in ((block_count, "block_count"), (block_idx, "block_idx")):
             _dev(t, n)
             if t.dtype != torch.int32 or not t.is_contiguous():

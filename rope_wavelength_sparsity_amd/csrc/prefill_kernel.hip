@@ -1085,10 +1085,13 @@ template <int D, bool F32>
 hipError_t sparse_lds_d(const PrefillParams& p, size_t* need, size_t* limit) {
     hipFuncAttributes attr;
     const bool hd = p.head_theta != nullptr;
-    // explicit positions (never with per-head tables here): the instances with a position tile
+    // explicit positions: the instances with a position tile
     hipError_t e = p.pos
-        ? (p.counter ? hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&prefill_kernel<D, F32, true, true, false, true>))
-                     : hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&prefill_kernel<D, F32, true, false, false, true>)))
+        ? (p.counter
+               ? (hd ? hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&prefill_kernel<D, F32, true, true, false, true, false, true>))
+                     : hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&prefill_kernel<D, F32, true, true, false, true>)))
+               : (hd ? hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&prefill_kernel<D, F32, true, false, false, true, false, true>))
+                     : hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&prefill_kernel<D, F32, true, false, false, true>))))
         : p.counter
         ? (hd ? hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&prefill_kernel<D, F32, false, true, false, true, false, true>))
               : hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&prefill_kernel<D, F32, false, true, false, true>)))
@@ -1217,8 +1220,10 @@ hipError_t launch_d(const PrefillParams& p, const Tables& t, hipStream_t s) {
         const size_t bits = sparse_bitmap_bytes<D>(p.N, hp);
         const bool hd = p.head_theta != nullptr;        // per-kv-head frequency tables
         // explicit positions: blocks stay token-index blocks, distances come from the
-        // position tile (the caller rejects positions with per-head tables here)
-        if (hp && cn) prefill_kernel<D, F32, true, true, false, true><<<grid, block, bits, s>>>(p, t, L);
+        // position tile
+        if (hp && hd && cn) prefill_kernel<D, F32, true, true, false, true, false, true><<<grid, block, bits, s>>>(p, t, L);
+        else if (hp && hd) prefill_kernel<D, F32, true, false, false, true, false, true><<<grid, block, bits, s>>>(p, t, L);
+        else if (hp && cn) prefill_kernel<D, F32, true, true, false, true><<<grid, block, bits, s>>>(p, t, L);
         else if (hp) prefill_kernel<D, F32, true, false, false, true><<<grid, block, bits, s>>>(p, t, L);
         else if (hd && cn) prefill_kernel<D, F32, false, true, false, true, false, true><<<grid, block, bits, s>>>(p, t, L);
         else if (hd) prefill_kernel<D, F32, false, false, false, true, false, true><<<grid, block, bits, s>>>(p, t, L);

@@ -595,8 +595,6 @@ static int sparse_impl(const void* q, const void* k, const void* v, void* out, f
                        void* stream) {
     int rc = check_common(d, base, rope, alpha);
     if (rc) return rc;
-    if (positions && head_tables(rope))
-        return fail(WPA_ERR_UNSUPPORTED, "block-sparse prefill at explicit positions takes one frequency table for all heads");
     if (block < 64 || block > 1024 || (block & (block - 1)))
         return fail(WPA_ERR_INVALID, "block must be a power of two from 64 to 1024 (got %d)", block);
     const int32_t blk_log2 = __builtin_ctz((unsigned)block);

@@ -70,10 +70,12 @@ def test_block_sparse_matches_oracle(shape, alpha):
     assert cnt == kept
 
 
+@pytest.mark.parametrize("at_pos", [False, True])
 @pytest.mark.parametrize("shape", [(1, 700, 14, 2, 64), (2, 650, 24, 8, 128)])
-def test_block_sparse_per_head_tables_match_oracle(shape):
+def test_block_sparse_per_head_tables_match_oracle(shape, at_pos):
     """Block sparsity with one frequency row per kv head (different bases, Llama-3 scaling on
-    odd heads): outputs, LSE and counts against the oracle with the same rows."""
+    odd heads), at token indices and at gapped explicit positions: outputs, LSE and counts
+    against the oracle with the same rows and positions."""
     need_gpu()
     B, N, Hq, Hkv, d = shape
     rows = []
@@ -87,14 +89,16 @@ def test_block_sparse_per_head_tables_match_oracle(shape):
     rows = np.stack(rows)
     q, k, v = synth.prefill_inputs(B, N, Hq, Hkv, d, "bf16", seed=97 + d)
     count, idx = _lists(B, Hq, N, 0.3, seed=98)
-    say("block sparse per-head tables", shape)
+    pos = _positions(B, N, "gapped", seed=100) if at_pos else None
+    say("block sparse per-head tables", shape, "positions" if at_pos else "")
     cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
     out, lse = wpa.prefill(q.cuda(), k.cuda(), v.cuda(), 1e4, 1.0, want_lse=True, term_count=cnt,
                            out_dtype=torch.float32, block_count=torch.from_numpy(count).cuda(),
-                           block_idx=torch.from_numpy(idx).cuda(), inv_freq=rows)
+                           block_idx=torch.from_numpy(idx).cuda(), inv_freq=rows,
+                           positions=None if pos is None else torch.from_numpy(pos).cuda())
     torch.cuda.synchronize()
     ro, rl, kept = oracle.prefill_sparse(exact(q), exact(k), exact(v), 1e4, 1.0, count, idx,
-                                         inv_freq=rows)
+                                         inv_freq=rows, pos=pos)
     check_close(out.cpu().numpy(), ro, "out")
     check_close(lse.cpu().numpy(), rl, "lse", LSE_MAX, LSE_MAX)
     assert int(cnt.item()) == kept

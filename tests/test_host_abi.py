@@ -668,8 +668,8 @@ def _sparse_pos_rc(pos, rope=None, **kw):
 
 
 def test_sparse_at_positions_host_checks():
-    """The positions entry refuses a null or misaligned positions pointer, per-head tables,
-    and every argument the token-index entry refuses, before anything is enqueued."""
+    """The positions entry refuses a null or misaligned positions pointer and every argument
+    the token-index entry refuses, before anything is enqueued."""
     L = wpa.lib()
     assert _sparse_pos_rc(None) == wpa.WPA_ERR_INVALID
     assert "positions" in L.wpa_last_error().decode()
@@ -679,6 +679,3 @@ def test_sparse_at_positions_host_checks():
     assert _sparse_pos_rc(FAKE, cnt_l=None) == wpa.WPA_ERR_INVALID
     assert _sparse_pos_rc(FAKE, Hq=3) == wpa.WPA_ERR_INVALID
     assert _sparse_pos_rc(FAKE, N=(1 << 21) + 1) == wpa.WPA_ERR_UNSUPPORTED
-    heads = wpa.Rope(wpa.WPA_PAIRS["half"], None, 1 << 20)
-    assert _sparse_pos_rc(FAKE, rope=ctypes.byref(heads)) == wpa.WPA_ERR_UNSUPPORTED
-    assert "frequency table" in L.wpa_last_error().decode()
